@@ -1,0 +1,181 @@
+"""Seeded synthetic inputs for the scaled low-precision GEMM.
+
+This module is shared by the tests (which hand the same arrays to the CPU
+oracle and to the HIP library) and by the benchmark.  It draws random
+numbers and quantises them into the input formats; it holds none of the
+GEMM's own arithmetic (no decode-and-accumulate, no epilogue).
+
+Recipe per workload (seed = 101..105 for the five workloads; every tensor
+draws from ``numpy.random.default_rng([seed, tensor_id, rot])`` with
+tensor_id A=0, B=1, scale_A=2, scale_B=3, bias=4 and ``rot`` the index of a
+rotating input set):
+
+  i8_small   INT8 M=256 N=256 K=512: A, B uniform integers in [-127, 127];
+             scale_A, scale_B uniform in [1e-3, 1e-2] (fp32); bias bf16 of N(0,1).
+  f8_ptpc    FP8 e4m3 M=4096 N=2112 K=7168: A, B ~ N(0,1) (fp32); per row
+             s = amax/448 (fp32), codes = e4m3(x/s) rounded to nearest even;
+             no bias.
+  mxfp8      MX e4m3 M=16384 N=7168 K=2048: A, B ~ N(0,1); shared exponent
+             X = floor(log2(block amax)) - 8 per 1x32 block of A and per 32x32
+             block of B (scales [M,K/32] and [N/32,K/32]); codes e4m3(x*2^-X)
+             rounded to nearest even and saturated at 448; no bias.
+  mxfp4      MX e2m1 M=N=K=8192: as mxfp8 with X = floor(log2(amax)) - 2,
+             1x32 blocks for A and B (scales [M,K/32] and [N,K/32]); two codes
+             per byte, even k in the low nibble; no bias.
+  i8_qkv     INT8 M=30000 N=21504 K=5376 with bias, values as i8_small.
+
+The recipes follow the workloads named for this GEMM (INT8 rowwise as in
+comfy-kitchen PR #174's 30000x21504x5376 projection; per-token FP8 and MXFP8
+as in ROCm/mori PR #806; MXFP4 8192^3 as in ROCm/FlyDSL PR #990).  All
+inputs are synthetic.
+"""
+import hashlib
+
+import numpy as np
+
+# name -> (kind, M, N, K, seed, has_bias, fmt, b_rows_per_scale)
+WORKLOADS = {
+    "i8_small": ("i8", 256, 256, 512, 101, True, None, None),
+    "f8_ptpc": ("f8", 4096, 2112, 7168, 102, False, None, None),
+    "mxfp8": ("mx", 16384, 7168, 2048, 103, False, "e4m3", 32),
+    "mxfp4": ("mx", 8192, 8192, 8192, 104, False, "e2m1", 1),
+    "i8_qkv": ("i8", 30000, 21504, 5376, 105, True, None, None),
+}
+ORDER = ["i8_small", "f8_ptpc", "mxfp8", "mxfp4", "i8_qkv"]
+
+E4M3_MAX = 448.0
+E2M1_MAX = 6.0
+
+
+def rng(seed, tensor_id, rot=0):
+    return np.random.default_rng([seed, tensor_id, rot])
+
+
+# ------------------------------------------------------------ quantisers
+
+def _e4m3_grid():
+    """Non-negative finite e4m3fn magnitudes, indexed by code 0..126, as
+    torch decodes them (a library cast, not this project's decoder)."""
+    import torch
+    codes = torch.arange(127, dtype=torch.uint8)
+    return codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+# OCP MX v1.0 FP4 E2M1 magnitudes in code order 0..7.
+_E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+_grid_cache = {}
+
+
+def _grid(fmt):
+    if fmt not in _grid_cache:
+        _grid_cache[fmt] = _e4m3_grid() if fmt == "e4m3" else _E2M1_GRID
+    return _grid_cache[fmt]
+
+
+def quantise(x, fmt):
+    """Round x to the nearest representable value of fmt (ties to the even
+    code), saturating at the largest finite magnitude.  Returns codes (uint8;
+    for e2m1 one 4-bit code per element, not yet packed)."""
+    grid = _grid(fmt)
+    x = np.asarray(x, dtype=np.float64)
+    ax = np.minimum(np.abs(x), grid[-1])
+    hi = np.searchsorted(grid, ax, side="left")          # grid[hi] >= ax
+    hi = np.minimum(hi, len(grid) - 1)
+    lo = np.maximum(hi - 1, 0)
+    dlo = ax - grid[lo]
+    dhi = grid[hi] - ax
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    sign_bit = 0x80 if fmt == "e4m3" else 0x8
+    neg = np.signbit(x) & (code != 0)
+    return np.where(neg, code | sign_bit, code).astype(np.uint8)
+
+
+def pack_e2m1(codes):
+    """[R, K] 4-bit codes -> [R, K/2] bytes, element k even in the low nibble."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    return (codes[:, 0::2] & 15) | ((codes[:, 1::2] & 15) << 4)
+
+
+def floor_log2(x):
+    """floor(log2(x)) for x > 0, exact (from frexp, not a float log)."""
+    _, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return e.astype(np.int64) - 1
+
+
+def mx_quantise(x, fmt, block_rows):
+    """MX-quantise x [R, K] (K % 32 == 0) with one ue8m0 scale per
+    block_rows x 32 block.  Returns (codes [R, K] uint8, scales
+    [ceil(R/block_rows), K/32] uint8)."""
+    emax = 8 if fmt == "e4m3" else 2
+    R, K = x.shape
+    Rb = -(-R // block_rows)
+    pad = Rb * block_rows - R
+    xp = np.pad(np.abs(x), ((0, pad), (0, 0))) if pad else np.abs(x)
+    amax = xp.reshape(Rb, block_rows, K // 32, 32).max(axis=(1, 3))
+    X = np.where(amax > 0, floor_log2(np.where(amax > 0, amax, 1.0)) - emax, -127)
+    code = np.clip(X + 127, 0, 254).astype(np.uint8)
+    Xe = code.astype(np.int64) - 127
+    Xfull = np.repeat(np.repeat(Xe, block_rows, axis=0)[:R], 32, axis=1)
+    y = np.ldexp(np.asarray(x, dtype=np.float64), -Xfull)
+    return quantise(y, fmt), code
+
+
+def bf16_bits(x):
+    """float values -> bfloat16 bit patterns via torch's own cast."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+# ------------------------------------------------------------ workloads
+
+def make(name, rot=0, M=None, N=None, K=None, bias=None, seed=None):
+    """Build one workload's inputs (numpy, host memory).  Shape overrides keep
+    the recipe and seed.  Returns a dict with kind, fmt, M, N, K, A, B,
+    scale_a, scale_b, bias (uint16 bf16 bits or None), b_rows_per_scale."""
+    kind, M0, N0, K0, seed0, bias0, fmt, brows = WORKLOADS[name]
+    M = M0 if M is None else M
+    N = N0 if N is None else N
+    K = K0 if K is None else K
+    seed = seed0 if seed is None else seed
+    has_bias = bias0 if bias is None else bias
+    d = dict(name=name, kind=kind, fmt=fmt, M=M, N=N, K=K, b_rows_per_scale=brows,
+             seed=seed, rot=rot)
+    if kind == "i8":
+        d["A"] = rng(seed, 0, rot).integers(-127, 128, size=(M, K), dtype=np.int8)
+        d["B"] = rng(seed, 1, rot).integers(-127, 128, size=(N, K), dtype=np.int8)
+        d["scale_a"] = rng(seed, 2, rot).uniform(1e-3, 1e-2, size=M).astype(np.float32)
+        d["scale_b"] = rng(seed, 3, rot).uniform(1e-3, 1e-2, size=N).astype(np.float32)
+    elif kind == "f8":
+        for tid, rows, key in ((0, M, "A"), (1, N, "B")):
+            x = rng(seed, tid, rot).standard_normal(size=(rows, K), dtype=np.float32)
+            amax = np.abs(x).max(axis=1)
+            s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+            s = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+            d[key] = quantise(x / s[:, None], "e4m3")
+            d["scale_a" if key == "A" else "scale_b"] = s
+    elif kind == "mx":
+        xa = rng(seed, 0, rot).standard_normal(size=(M, K), dtype=np.float32)
+        ca, sa = mx_quantise(xa, fmt, 1)
+        del xa
+        xb = rng(seed, 1, rot).standard_normal(size=(N, K), dtype=np.float32)
+        cb, sb = mx_quantise(xb, fmt, brows)
+        del xb
+        if fmt == "e2m1":
+            ca, cb = pack_e2m1(ca), pack_e2m1(cb)
+        d.update(A=ca, B=cb, scale_a=sa, scale_b=sb)
+    else:
+        raise ValueError(name)
+    d["bias"] = (bf16_bits(rng(seed, 4, rot).standard_normal(size=N).astype(np.float32))
+                 if has_bias else None)
+    return d
+
+
+def digest(d):
+    """sha256 over the input bytes, for the benchmark report."""
+    h = hashlib.sha256()
+    for key in ("A", "B", "scale_a", "scale_b", "bias"):
+        if d.get(key) is not None:
+            h.update(np.ascontiguousarray(d[key]).tobytes())
+    return h.hexdigest()

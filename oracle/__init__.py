@@ -1,0 +1,184 @@
+"""CPU oracle for the scaled low-precision GEMM (test infrastructure only).
+
+Loads ``liboracle.so`` built from ``qgemm_oracle.c`` (plain C, OpenMP, fp64
+accumulation, fixed-order binary32 epilogue).  Only the tests, the smoke
+check and the benchmark's CPU-baseline leg import this package; the product
+library never does.  It shares no code with the HIP path: inputs arrive as
+numpy arrays and results leave as numpy arrays.
+
+Functions follow the definitions in ``qgemm_oracle.c``:
+  i8_rowwise   -- INT8, rowwise fp32 scales (comfy-kitchen PR #174 "Optimize
+                  HIP WMMA INT8 GEMM ...": Summary, Validation).
+  f8_pertoken  -- FP8 e4m3 per-token / per-channel (ROCm/mori PR #806,
+                  Measured: "ptpc").
+  mx           -- MX e4m3 / e2m1 with ue8m0 per 32 K elements (ROCm/mori PR
+                  #806, What; ROCm/FlyDSL PR #990).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_SRC = os.path.join(_HERE, "qgemm_oracle.c")
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+MX_E4M3 = 0
+MX_E2M1 = 1
+
+
+def build(force=True):
+    """Compile liboracle.so with gcc (no fast-math, no FP contraction)."""
+    import subprocess
+    cmd = ["gcc", "-O3", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", "-Wall", "-o", _LIB_PATH + ".tmp", _SRC, "-lm"]
+    if force or not os.path.exists(_LIB_PATH):
+        subprocess.check_call(cmd)
+        os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.orc_dec_e4m3.restype = ctypes.c_double
+    lib.orc_dec_e4m3.argtypes = [ctypes.c_uint8]
+    lib.orc_dec_e2m1.restype = ctypes.c_double
+    lib.orc_dec_e2m1.argtypes = [ctypes.c_uint8]
+    lib.orc_dec_ue8m0.restype = ctypes.c_double
+    lib.orc_dec_ue8m0.argtypes = [ctypes.c_uint8]
+    lib.orc_bf16_rne.restype = ctypes.c_uint16
+    lib.orc_bf16_rne.argtypes = [ctypes.c_float]
+    lib.orc_num_threads.restype = ctypes.c_int
+    for name in ("orc_dec_e4m3_array", "orc_dec_e2m1_array", "orc_dec_ue8m0_array",
+                 "orc_bf16_rne_array"):
+        getattr(lib, name).restype = None
+        getattr(lib, name).argtypes = [_P, _P, _I64]
+    lib.orc_i8_rowwise.restype = ctypes.c_int
+    lib.orc_i8_rowwise.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _P, _I64, _P,
+                                   _I64, _I64, _I64]
+    lib.orc_f8_pertoken.restype = None
+    lib.orc_f8_pertoken.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _P, _I64, _P, _P,
+                                    _I64, _I64, _I64]
+    lib.orc_mx.restype = ctypes.c_int
+    lib.orc_mx.argtypes = [ctypes.c_int, _P, _I64, _P, _I64, _P, _P, ctypes.c_int, _P,
+                           _P, _I64, _P, _P, _I64, _I64, _I64]
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads():
+    return _load().orc_num_threads()
+
+
+def dec_e4m3(codes):
+    codes = _c(codes, np.uint8)
+    out = np.empty(codes.shape, np.float64)
+    _load().orc_dec_e4m3_array(_ptr(codes), _ptr(out), codes.size)
+    return out
+
+
+def dec_e2m1(nibbles):
+    nibbles = _c(nibbles, np.uint8)
+    out = np.empty(nibbles.shape, np.float64)
+    _load().orc_dec_e2m1_array(_ptr(nibbles), _ptr(out), nibbles.size)
+    return out
+
+
+def dec_ue8m0(codes):
+    codes = _c(codes, np.uint8)
+    out = np.empty(codes.shape, np.float64)
+    _load().orc_dec_ue8m0_array(_ptr(codes), _ptr(out), codes.size)
+    return out
+
+
+def bf16_rne(x):
+    """binary32 values -> bfloat16 bit patterns (uint16), round-nearest-even."""
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    _load().orc_bf16_rne_array(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def i8_rowwise(A, B, scale_a, scale_b, bias=None):
+    """INT8 rowwise GEMM.  A [M,K] int8, B [N,K] int8, scale_a [M] / scale_b [N]
+    float32, bias [N] bf16 bits (uint16) or None.
+    Returns (C bf16 bits uint16 [M,N], acc int32 [M,N])."""
+    A = _c(A, np.int8)
+    B = _c(B, np.int8)
+    M, K = A.shape
+    N = B.shape[0]
+    assert B.shape[1] == K
+    sa = _c(scale_a, np.float32)
+    sb = _c(scale_b, np.float32)
+    bias = _c(bias, np.uint16)
+    assert sa.shape == (M,) and sb.shape == (N,)
+    C = np.empty((M, N), np.uint16)
+    acc = np.empty((M, N), np.int32)
+    rc = _load().orc_i8_rowwise(_ptr(A), K, _ptr(B), K, _ptr(sa), _ptr(sb), _ptr(bias),
+                                _ptr(C), N, _ptr(acc), M, N, K)
+    if rc != 0:
+        raise OverflowError("int32 accumulator out of range")
+    return C, acc
+
+
+def f8_pertoken(A, B, scale_a, scale_b, bias=None):
+    """FP8 e4m3 per-token/per-channel GEMM.  A [M,K], B [N,K] uint8 e4m3 codes.
+    Returns (C uint16 [M,N], acc float64 [M,N], absdot float64 [M,N])."""
+    A = _c(A, np.uint8)
+    B = _c(B, np.uint8)
+    M, K = A.shape
+    N = B.shape[0]
+    assert B.shape[1] == K
+    sa = _c(scale_a, np.float32)
+    sb = _c(scale_b, np.float32)
+    bias = _c(bias, np.uint16)
+    assert sa.shape == (M,) and sb.shape == (N,)
+    C = np.empty((M, N), np.uint16)
+    acc = np.empty((M, N), np.float64)
+    absdot = np.empty((M, N), np.float64)
+    _load().orc_f8_pertoken(_ptr(A), K, _ptr(B), K, _ptr(sa), _ptr(sb), _ptr(bias),
+                            _ptr(C), N, _ptr(acc), _ptr(absdot), M, N, K)
+    return C, acc, absdot
+
+
+def mx(fmt, A, B, scale_a, scale_b, b_rows_per_scale, K, bias=None):
+    """MX GEMM.  fmt MX_E4M3 (A [M,K], B [N,K] bytes) or MX_E2M1 (A [M,K/2],
+    B [N,K/2] bytes, element k in the low nibble when k is even).  scale_a
+    [M,K/32] ue8m0, scale_b [N or ceil(N/32), K/32] ue8m0.
+    Returns (C uint16 [M,N], acc float64 [M,N], absdot float64 [M,N])."""
+    A = _c(A, np.uint8)
+    B = _c(B, np.uint8)
+    M, N = A.shape[0], B.shape[0]
+    row_bytes = K if fmt == MX_E4M3 else K // 2
+    assert A.shape[1] == row_bytes and B.shape[1] == row_bytes and K % 32 == 0
+    sa = _c(scale_a, np.uint8)
+    sb = _c(scale_b, np.uint8)
+    assert sa.shape == (M, K // 32)
+    assert sb.shape == ((N + b_rows_per_scale - 1) // b_rows_per_scale, K // 32)
+    bias = _c(bias, np.uint16)
+    C = np.empty((M, N), np.uint16)
+    acc = np.empty((M, N), np.float64)
+    absdot = np.empty((M, N), np.float64)
+    rc = _load().orc_mx(fmt, _ptr(A), row_bytes, _ptr(B), row_bytes, _ptr(sa), _ptr(sb),
+                        b_rows_per_scale, _ptr(bias), _ptr(C), N, _ptr(acc), _ptr(absdot),
+                        M, N, K)
+    if rc != 0:
+        raise ValueError("bad MX format or B-scale layout")
+    return C, acc, absdot

@@ -1,0 +1,287 @@
+/*
+ * qgemm_oracle.c -- plain CPU oracle for the scaled low-precision GEMM
+ *
+ *     C = bf16( scale_A (.) scale_B (.) (A . B^T) + bias )
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links or calls
+ * this file; only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg load it.  It shares no header, table or helper with the HIP path.
+ *
+ * Sources, by page title and section:
+ *  - "Optimize HIP WMMA INT8 GEMM staging, epilogue, and deep-K tiling"
+ *    (comfy-kitchen PR #174): Summary (rowwise scales and bias; signed zero
+ *    kept without bias), Validation (int8 results exact), Update "rebased
+ *    onto v0.2.40" (association pinned to (acc*sa)*sb).
+ *  - "perf(gemm-ar): mxfp8 with row-major scales staged through LDS"
+ *    (ROCm/mori PR #806): What (32-wide ue8m0 scales; A scales [M,K/32], B
+ *    scales [N/32,K/32] uint8 row-major), Measured (per-token/per-channel
+ *    "ptpc" FP8).
+ *  - "[fp4_gemm_4wave] MXFP4 GEMM perf optimize" (ROCm/FlyDSL PR #990):
+ *    MXFP4 = e2m1 elements with one ue8m0 scale per 1x32 K block.
+ * The pages name e4m3 / e2m1 / ue8m0 without giving their bits; the reading
+ * taken is the OCP 8-bit floating point (E4M3FN) and OCP Microscaling v1.0
+ * definitions of those names.
+ *
+ * Arithmetic: integers accumulate exactly (int64, checked to fit int32, the
+ * accumulator the INT8 page specifies); e4m3 / e2m1 / ue8m0 are decoded
+ * exactly to double and accumulated in double (every sum here is exact for
+ * these formats up to the bounds stated per function); the epilogue is a
+ * fixed sequence of IEEE binary32 operations, each rounded to nearest even,
+ * subnormals kept, no fused multiply-add (built with -ffp-contract=off), and
+ * a final round-to-nearest-even to bfloat16.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- formats */
+
+/* E4M3FN: sign, 4-bit exponent (bias 7), 3-bit mantissa; exponent field 0
+ * is subnormal (m * 2^-9); S.1111.111 is NaN; there is no infinity, and the
+ * largest finite magnitude is 1.75 * 2^8 = 448. */
+double orc_dec_e4m3(uint8_t code)
+{
+    int s = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return s ? -NAN : NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp((double)(8 + m), e - 10);
+    return s ? -v : v;
+}
+
+/* E2M1: sign, 2-bit exponent (bias 1), 1-bit mantissa; exponent field 0 is
+ * subnormal (m * 0.5); every code is finite, largest magnitude 6. */
+double orc_dec_e2m1(uint8_t nibble)
+{
+    int s = (nibble >> 3) & 1, e = (nibble >> 1) & 3, m = nibble & 1;
+    double v = (e == 0) ? 0.5 * m : ldexp((double)(2 + m), e - 2);
+    return s ? -v : v;
+}
+
+/* E8M0 (unsigned, exponent only, bias 127): code c is 2^(c-127), 255 is NaN. */
+double orc_dec_ue8m0(uint8_t code)
+{
+    if (code == 255)
+        return NAN;
+    return ldexp(1.0, (int)code - 127);
+}
+
+/* bfloat16 bits -> binary32 (exact: bf16 is the upper half of binary32). */
+float orc_bf16_to_f32(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* binary32 -> bfloat16, round to nearest, ties to even; NaN stays NaN (quiet,
+ * sign kept); overflow rounds to infinity as IEEE rounding does. */
+uint16_t orc_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------ INT8 */
+
+/* INT8 rowwise GEMM.  A [M,K] int8 (row stride lda), B [N,K] int8 (row
+ * stride ldb), scale_a [M] and scale_b [N] binary32, bias [N] bf16 bits or
+ * NULL, C [M,ldc] bf16 bits.  acc (optional, [M,N] dense) receives the int32
+ * accumulator.  Returns 0, or -1 if an accumulator leaves the int32 range
+ * (impossible for K <= 131071).
+ *
+ * Per output: acc = sum_k A[m,k]*B[n,k] exactly; f = (float)acc;
+ * f = f*sa[m]; f = f*sb[n]; if bias: f = f + bias[n]; C = bf16_rne(f).
+ * Without bias nothing is added, so a -0 product stays -0. */
+int orc_i8_rowwise(const int8_t *A, int64_t lda, const int8_t *B, int64_t ldb,
+                   const float *scale_a, const float *scale_b, const uint16_t *bias,
+                   uint16_t *C, int64_t ldc, int32_t *acc,
+                   int64_t M, int64_t N, int64_t K)
+{
+    int bad = 0;
+#pragma omp parallel for collapse(2) schedule(static) reduction(| : bad)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            const int8_t *a = A + m * lda;
+            const int8_t *b = B + n * ldb;
+            int64_t s = 0;
+            for (int64_t k = 0; k < K; ++k)
+                s += (int32_t)a[k] * (int32_t)b[k];
+            if (s > INT32_MAX || s < INT32_MIN)
+                bad = 1;
+            int32_t s32 = (int32_t)s;
+            if (acc)
+                acc[m * N + n] = s32;
+            float f = (float)s32;
+            f = f * scale_a[m];
+            f = f * scale_b[n];
+            if (bias)
+                f = f + orc_bf16_to_f32(bias[n]);
+            C[m * ldc + n] = orc_bf16_rne(f);
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------ FP8 */
+
+/* FP8 e4m3 per-token (row of A) / per-channel (row of B) GEMM.  A [M,K] and
+ * B [N,K] e4m3 codes, scale_a [M] / scale_b [N] binary32, bias as above.
+ * acc (optional [M,N]) receives the double accumulator; absdot (optional
+ * [M,N]) receives |sa[m]*sb[n]| * sum_k |a_k*b_k|, the scale of the error
+ * bound.
+ *
+ * Every e4m3 value is an integer multiple of 2^-9 of magnitude at most
+ * 448 = 229376 * 2^-9, so each product is a multiple of 2^-18 below 2^35.7
+ * and a sum of K <= 131072 such products stays below 2^53 * 2^-18: the
+ * double sum is exact, whatever its order.
+ *
+ * Per output: f = (float)acc; f = f*sa[m]; f = f*sb[n]; [f = f + bias[n]];
+ * C = bf16_rne(f). */
+void orc_f8_pertoken(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                     const float *scale_a, const float *scale_b, const uint16_t *bias,
+                     uint16_t *C, int64_t ldc, double *acc, double *absdot,
+                     int64_t M, int64_t N, int64_t K)
+{
+    double lut[256];
+    for (int c = 0; c < 256; ++c)
+        lut[c] = orc_dec_e4m3((uint8_t)c);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            const uint8_t *a = A + m * lda;
+            const uint8_t *b = B + n * ldb;
+            double s = 0.0, t = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double p = lut[a[k]] * lut[b[k]];
+                s += p;
+                t += fabs(p);
+            }
+            if (acc)
+                acc[m * N + n] = s;
+            if (absdot)
+                absdot[m * N + n] = fabs((double)scale_a[m] * (double)scale_b[n]) * t;
+            float f = (float)s;
+            f = f * scale_a[m];
+            f = f * scale_b[n];
+            if (bias)
+                f = f + orc_bf16_to_f32(bias[n]);
+            C[m * ldc + n] = orc_bf16_rne(f);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------- MX */
+
+/* MX GEMM: fmt 0 = e4m3 elements (one byte each), fmt 1 = e2m1 elements (two
+ * per byte, element k in the low nibble of byte k/2 when k is even, in the
+ * high nibble when k is odd).  lda / ldb are row strides in BYTES.
+ * scale_a: ue8m0 codes [M, K/32] row-major (row stride K/32).
+ * scale_b: ue8m0 codes, b_rows_per_scale = 1 -> [N, K/32] (one scale per row
+ * of B and K block), = 32 -> [ceil(N/32), K/32] (one scale per 32 rows of B
+ * and K block).  bias / C as above; acc / absdot as for FP8, here over the
+ * scaled values (absdot = sum_k |A~[m,k] * B~[n,k]|).
+ *
+ * A~[m,k] = dec(A[m,k]) * 2^(SA[m,k/32]-127) and likewise B~; each is exact in
+ * double (a power-of-two multiple of a short integer).  acc = sum_k A~ B~ in
+ * double; with the power-of-two scales the terms of one row pair differ only
+ * by the spread of their scale exponents, and for spreads within the bound
+ * the tests check (an exact integer recomputation) the sum is exact.
+ *
+ * Per output: f = (float)acc; [f = f + bias[n]]; C = bf16_rne(f).
+ * Returns 0, or -1 for an unknown fmt / b_rows_per_scale. */
+int orc_mx(int fmt, const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+           const uint8_t *scale_a, const uint8_t *scale_b, int b_rows_per_scale,
+           const uint16_t *bias, uint16_t *C, int64_t ldc, double *acc, double *absdot,
+           int64_t M, int64_t N, int64_t K)
+{
+    if ((fmt != 0 && fmt != 1) || (b_rows_per_scale != 1 && b_rows_per_scale != 32))
+        return -1;
+    const int64_t KB = K / 32;
+    double lut8[256], lut4[16], lut_s[256];
+    for (int c = 0; c < 256; ++c) {
+        lut8[c] = orc_dec_e4m3((uint8_t)c);
+        lut_s[c] = orc_dec_ue8m0((uint8_t)c);
+    }
+    for (int c = 0; c < 16; ++c)
+        lut4[c] = orc_dec_e2m1((uint8_t)c);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            const uint8_t *sarow = scale_a + m * KB;
+            const uint8_t *sbrow = scale_b + (n / b_rows_per_scale) * KB;
+            double s = 0.0, t = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double a, b;
+                if (fmt == 0) {
+                    a = lut8[A[m * lda + k]];
+                    b = lut8[B[n * ldb + k]];
+                } else {
+                    uint8_t ab = A[m * lda + k / 2], bb = B[n * ldb + k / 2];
+                    a = lut4[(k & 1) ? (ab >> 4) : (ab & 15)];
+                    b = lut4[(k & 1) ? (bb >> 4) : (bb & 15)];
+                }
+                a *= lut_s[sarow[k / 32]];
+                b *= lut_s[sbrow[k / 32]];
+                double p = a * b;
+                s += p;
+                t += fabs(p);
+            }
+            if (acc)
+                acc[m * N + n] = s;
+            if (absdot)
+                absdot[m * N + n] = t;
+            float f = (float)s;
+            if (bias)
+                f = f + orc_bf16_to_f32(bias[n]);
+            C[m * ldc + n] = orc_bf16_rne(f);
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------- array forms for tests */
+
+void orc_dec_e4m3_array(const uint8_t *codes, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_dec_e4m3(codes[i]);
+}
+
+void orc_dec_e2m1_array(const uint8_t *nibbles, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_dec_e2m1(nibbles[i]);
+}
+
+void orc_dec_ue8m0_array(const uint8_t *codes, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_dec_ue8m0(codes[i]);
+}
+
+void orc_bf16_rne_array(const float *in, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_bf16_rne(in[i]);
+}
