@@ -1,0 +1,202 @@
+"""Benchmark of the scaled low-precision GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one call of the GEMM (argument checks, tile choice, one kernel:
+tile schedule, HBM->LDS staging, MFMA K loop, fused scale/bias epilogue) on
+one batch of seeded synthetic inputs already resident in HBM.  The default
+workload is the INT8 rowwise projection M=30000 N=21504 K=5376 with bias;
+--workload picks another (i8_small, f8_ptpc, mxfp8, mxfp4, i8_qkv).
+
+Prints one JSON line: effective TOPS/TFLOPS = 2MNK / t, the roofline of the
+kernel (achieved over the dense MFMA peak of its dtype, from HIP events on
+the launch stream), and the CPU oracle timed on a bounded sample of the same
+workload on this host.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective TFLOPS/TOPS (2MNK/t) per dtype; % of MI355X dense MFMA peak"
+# MI355X dense matrix-core peaks (TOPS / TFLOPS)
+PEAK = {"i8": 5000.0, "f8": 5000.0, "e4m3": 5000.0, "e2m1": 10100.0}
+# The pages' number for the INT8 30000x21504x5376 workload: 209.9 TOPS, on a
+# different GPU (RX 9070 XT); context only.
+PAGES_I8_QKV_TOPS = 209.9
+# Rotating input sets so operands are not served from the 256 MB MALL.
+ROT = {"i8_small": 1, "f8_ptpc": 8, "mxfp8": 2, "mxfp4": 3, "i8_qkv": 2}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dtype_of(d):
+    return d["kind"] if d["kind"] != "mx" else d["fmt"]
+
+
+def unit_of(d):
+    return "TOPS" if d["kind"] == "i8" else "TFLOPS"
+
+
+class Launcher:
+    """Binds one workload's device buffers to a direct C-ABI call (the
+    binding's argument checks are done once, outside the timed loop)."""
+
+    def __init__(self, d, sets, out, stream):
+        import block_scaled_precision_02_amd as q
+        self.L = q.lib()
+        self.d = d
+        self.sets = sets
+        self.out = out
+        self.stream = ctypes.c_void_p(stream)
+        N = d["N"]
+        self.ldc = out.stride(0)
+        self.args = []
+        for s in sets:
+            bias = None if s["bias"] is None else s["bias"].data_ptr()
+            if d["kind"] == "i8":
+                a = (s["A"].data_ptr(), s["A"].stride(0), s["B"].data_ptr(), s["B"].stride(0),
+                     s["scale_a"].data_ptr(), s["scale_b"].data_ptr(), bias, out.data_ptr(),
+                     self.ldc, d["M"], N, d["K"], self.stream)
+                self.args.append((self.L.qgemm_i8_rowwise, a))
+            elif d["kind"] == "f8":
+                a = (s["A"].data_ptr(), s["A"].stride(0), s["B"].data_ptr(), s["B"].stride(0),
+                     s["scale_a"].data_ptr(), s["scale_b"].data_ptr(), bias, out.data_ptr(),
+                     self.ldc, d["M"], N, d["K"], self.stream)
+                self.args.append((self.L.qgemm_f8_pertoken, a))
+            else:
+                fmt = 0 if d["fmt"] == "e4m3" else 1
+                a = (fmt, s["A"].data_ptr(), s["A"].stride(0), s["B"].data_ptr(), s["B"].stride(0),
+                     s["scale_a"].data_ptr(), s["scale_b"].data_ptr(), d["b_rows_per_scale"], bias,
+                     out.data_ptr(), self.ldc, d["M"], N, d["K"], self.stream)
+                self.args.append((self.L.qgemm_mx, a))
+
+    def __call__(self, i):
+        fn, a = self.args[i % len(self.args)]
+        st = fn(*a)
+        if st != 0:
+            raise RuntimeError(self.L.qgemm_last_error().decode())
+
+
+def upload(d):
+    import torch
+    t = {}
+    for k in ("A", "B", "scale_a", "scale_b"):
+        t[k] = torch.from_numpy(np.ascontiguousarray(d[k])).cuda()
+    t["bias"] = None if d["bias"] is None else torch.from_numpy(d["bias"].view(np.int16)).cuda()
+    return t
+
+
+def cpu_baseline(d, target_s):
+    """The oracle, as it is, on whole rows of the same workload: a few rows
+    first to calibrate, then enough rows for about target_s seconds."""
+    import oracle
+    from tests import parity
+    rows = np.arange(min(2, d["M"]))
+    t0 = time.perf_counter()
+    parity.oracle_run(d, rows=rows)
+    t1 = time.perf_counter() - t0
+    per_row = max(t1 / len(rows), 1e-6)
+    n = int(min(d["M"], max(len(rows), target_s / per_row)))
+    rows = np.linspace(0, d["M"] - 1, n).astype(np.int64)
+    t0 = time.perf_counter()
+    parity.oracle_run(d, rows=rows)
+    t = time.perf_counter() - t0
+    ops = 2.0 * n * d["N"] * d["K"]
+    return {"value": round(ops / t / 1e12, 6), "unit": unit_of(d), "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n} of {d['M']} rows of A (all {d['N']} columns, K={d['K']}), {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="i8_qkv")
+    ap.add_argument("--rot", type=int, default=None, help="rotating input sets")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this GEMM library has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_scaled_precision_02_amd import inputs
+    import block_scaled_precision_02_amd as q
+
+    torch.cuda.set_device(0)
+    name = args.workload
+    R = args.rot or ROT[name]
+    log(f"[bench] generating {name} x{R}")
+    d0 = inputs.make(name)
+    sets = [upload(d0)]
+    for r in range(1, R):
+        sets.append(upload(inputs.make(name, rot=r)))
+    M, N, K = d0["M"], d0["N"], d0["K"]
+    out = torch.empty((M, N + (-N) % 8), dtype=torch.bfloat16, device="cuda")[:, :N]
+    stream = torch.cuda.current_stream()
+    run = Launcher(d0, sets, out, stream.cuda_stream)
+    tile = q.select_tile({"i8": 0, "f8": 1, "e4m3": 2, "e2m1": 3}[dtype_of(d0)], M, N, K)
+
+    log(f"[bench] warmup {args.warmup}")
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        run(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    flops = 2.0 * M * N * K
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    peak = PEAK[dtype_of(d0)]
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": unit_of(d0),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / PAGES_I8_QKV_TOPS, 4) if name == "i8_qkv" else None,
+        "dtype": {"i8": "int8", "f8": "e4m3", "e4m3": "mxfp8-e4m3", "e2m1": "mxfp4-e2m1"}[dtype_of(d0)],
+        "data": "synthetic",
+        "config": {"workload": f"{name} M={M} N={N} K={K}" + (" bias" if d0["bias"] is not None else ""),
+                   "tile": q.tile_rows(tile), "rotating_sets": R, "pct_of_peak": round(100 * value / peak, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": unit_of(d0), "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel_ms": round(kernel_ms, 6)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(d0, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

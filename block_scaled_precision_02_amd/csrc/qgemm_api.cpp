@@ -1,0 +1,369 @@
+// qgemm_api.cpp -- the C ABI: argument checks, cached device check, tile
+// table, launch.
+//
+// Boundary conventions follow the caller-owned-output GEMMs of ROCm/aiter PR
+// #6262 (Technical Details: out= checked for shape, dtype and device before
+// use; the review's request to refuse unsupported layouts) and the tile
+// policy of comfy-kitchen PR #174 (Summary: a cached host-side device
+// property query picks the tile; an unknown device never reaches a kernel).
+// Unlike aiter's A4W4 path, C is exactly [M, N]: edge tiles are masked rather
+// than padded to whole 32-row tiles.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/qgemm.h"
+#include "qgemm_launch.hpp"
+
+using namespace qgemm;
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local int g_forced_tile = -1;
+
+qgemm_status fail(qgemm_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+qgemm_status fail(qgemm_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = std::string(qgemm_status_string(st)) + ": " + buf;
+    return st;
+}
+
+constexpr int64_t I8_K_MAX = 131071;   // K * 128 * 128 < 2^31
+constexpr int64_t LD_LIMIT = (int64_t)1 << 31;
+
+bool aligned(const void *p, unsigned a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// ------------------------------------------------------------ device check
+// gfx950 or nothing.  The answer per device is cached after the first query.
+constexpr int MAX_DEV = 64;
+std::once_flag g_dev_once[MAX_DEV];
+int g_dev_ok[MAX_DEV];
+
+bool is_gfx950(const char *name)
+{
+    return strncmp(name, "gfx950", 6) == 0 && (name[6] == 0 || name[6] == ':');
+}
+
+qgemm_status check_device()
+{
+    // Test hook: a fake architecture name that is not gfx950 is refused
+    // before any HIP call is made.
+    const char *fake = getenv("QGEMM_FAKE_ARCH");
+    if (fake && *fake && !is_gfx950(fake))
+        return fail(QGEMM_ERR_UNSUPPORTED_DEVICE, "device reports %s, not gfx950", fake);
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(QGEMM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= MAX_DEV)
+        return fail(QGEMM_ERR_UNSUPPORTED_DEVICE, "device index %d out of range", dev);
+    std::call_once(g_dev_once[dev], [dev]() {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            g_dev_ok[dev] = -1;
+            return;
+        }
+        g_dev_ok[dev] = is_gfx950(prop.gcnArchName) ? 1 : 0;
+    });
+    if (g_dev_ok[dev] == 1)
+        return QGEMM_OK;
+    if (g_dev_ok[dev] < 0)
+        return fail(QGEMM_ERR_HIP, "hipGetDeviceProperties failed for device %d", dev);
+    return fail(QGEMM_ERR_UNSUPPORTED_DEVICE, "device %d is not gfx950", dev);
+}
+
+// ------------------------------------------------------------ tile table
+// Rows are checked in order; the first whose bounds hold picks the tile.
+// A miss falls through to the default rule.  256x256 is the throughput tile
+// (one workgroup per CU, 256 accumulators per lane in AGPRs); 128x128 keeps
+// more workgroups in flight when the 256x256 grid would leave CUs idle.
+struct TileRow {
+    int path;          // -1: any path
+    int64_t max_tiles; // the 256x256 grid has at most this many tiles
+    int tile;
+};
+const TileRow TILE_TABLE[] = {
+    {-1, 128, 1},   // under half the 256 CUs busy with the big tile
+};
+constexpr int DEFAULT_TILE = 0;
+
+int select_tile_impl(int path, int64_t M, int64_t N)
+{
+    const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+    for (const TileRow &r : TILE_TABLE)
+        if ((r.path < 0 || r.path == path) && big <= r.max_tiles)
+            return r.tile;
+    return DEFAULT_TILE;
+}
+
+// ------------------------------------------------------------ common checks
+struct Shape {
+    int64_t M, N, K;
+};
+
+qgemm_status check_shape(Shape s, bool is_i8)
+{
+    if (s.M < 0 || s.N < 0 || s.K <= 0)
+        return fail(QGEMM_ERR_BAD_SHAPE, "M=%lld N=%lld K=%lld: need M>=0, N>=0, K>0", (long long)s.M,
+                    (long long)s.N, (long long)s.K);
+    if (s.K % 32)
+        return fail(QGEMM_ERR_BAD_SHAPE, "K=%lld is not a multiple of 32", (long long)s.K);
+    if (s.M >= LD_LIMIT || s.N >= LD_LIMIT || s.K >= LD_LIMIT)
+        return fail(QGEMM_ERR_BAD_SHAPE, "M, N and K must stay below 2^31");
+    if (is_i8 && s.K > I8_K_MAX)
+        return fail(QGEMM_ERR_BAD_SHAPE, "K=%lld exceeds %lld (int32 accumulator range)", (long long)s.K,
+                    (long long)I8_K_MAX);
+    return QGEMM_OK;
+}
+
+qgemm_status check_operand(const char *name, const void *p, int64_t ld, int64_t row_bytes)
+{
+    if (!p)
+        return fail(QGEMM_ERR_NULL_POINTER, "%s is NULL", name);
+    if (!aligned(p, 16))
+        return fail(QGEMM_ERR_BAD_LAYOUT, "%s is not 16-byte aligned", name);
+    if (ld < row_bytes)
+        return fail(QGEMM_ERR_BAD_LAYOUT, "ld%s=%lld bytes is below the row (%lld bytes)", name, (long long)ld,
+                    (long long)row_bytes);
+    if (ld % 16)
+        return fail(QGEMM_ERR_BAD_LAYOUT, "ld%s=%lld is not a multiple of 16 bytes", name, (long long)ld);
+    if (ld * 256 >= LD_LIMIT)
+        return fail(QGEMM_ERR_BAD_LAYOUT, "ld%s=%lld bytes: 256 rows exceed 2^31 bytes", name, (long long)ld);
+    return QGEMM_OK;
+}
+
+qgemm_status check_output(const void *C, int64_t ldc, int64_t N, int esz)
+{
+    if (!C)
+        return fail(QGEMM_ERR_NULL_POINTER, "C is NULL");
+    if (!aligned(C, 16))
+        return fail(QGEMM_ERR_BAD_LAYOUT, "C is not 16-byte aligned");
+    if (ldc < N)
+        return fail(QGEMM_ERR_BAD_LAYOUT, "ldc=%lld is below N=%lld", (long long)ldc, (long long)N);
+    if (ldc % 8)
+        return fail(QGEMM_ERR_BAD_LAYOUT, "ldc=%lld is not a multiple of 8", (long long)ldc);
+    if (ldc * esz * 256 >= LD_LIMIT)
+        return fail(QGEMM_ERR_BAD_LAYOUT, "ldc=%lld: 256 rows exceed 2^31 bytes", (long long)ldc);
+    return QGEMM_OK;
+}
+
+qgemm_status check_fp32_scales(const float *sa, const float *sb)
+{
+    if (!sa)
+        return fail(QGEMM_ERR_NULL_POINTER, "scale_a is NULL");
+    if (!sb)
+        return fail(QGEMM_ERR_NULL_POINTER, "scale_b is NULL");
+    if (!aligned(sa, 4) || !aligned(sb, 4))
+        return fail(QGEMM_ERR_BAD_LAYOUT, "fp32 scales must be 4-byte aligned");
+    return QGEMM_OK;
+}
+
+qgemm_status check_bias(const uint16_t *bias)
+{
+    if (bias && !aligned(bias, 2))
+        return fail(QGEMM_ERR_BAD_LAYOUT, "bias is not 2-byte aligned");
+    return QGEMM_OK;
+}
+
+#define TRY(x)                                  \
+    do {                                        \
+        qgemm_status st_ = (x);                 \
+        if (st_ != QGEMM_OK)                    \
+            return st_;                         \
+    } while (0)
+
+Params base_params(const void *A, int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc, Shape s,
+                   int64_t kbytes, int tile)
+{
+    Params p;
+    memset(&p, 0, sizeof p);
+    p.A = (const uint8_t *)A;
+    p.B = (const uint8_t *)B;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.C = C;
+    p.ldc = ldc;
+    p.M = (int)s.M;
+    p.N = (int)s.N;
+    p.K = (int)s.K;
+    p.kbytes = (int)kbytes;
+    p.ksteps = (int)((kbytes + KSTEP_BYTES - 1) / KSTEP_BYTES);
+    p.kblocks = (int)(s.K / 32);
+    const int edge = tile_edge(tile);
+    p.tiles_m = (int)((s.M + edge - 1) / edge);
+    p.tiles_n = (int)((s.N + edge - 1) / edge);
+    p.group_m = 8;
+    return p;
+}
+
+qgemm_status check_grid(const Params &p)
+{
+    if ((int64_t)p.tiles_m * p.tiles_n >= LD_LIMIT)
+        return fail(QGEMM_ERR_BAD_SHAPE, "grid of %d x %d tiles is too large", p.tiles_m, p.tiles_n);
+    return QGEMM_OK;
+}
+
+qgemm_status finish(hipError_t e)
+{
+    if (e != hipSuccess)
+        return fail(QGEMM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+    return QGEMM_OK;
+}
+
+int pick_tile(int path, Shape s)
+{
+    return g_forced_tile >= 0 ? g_forced_tile : select_tile_impl(path, s.M, s.N);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qgemm_status_string(qgemm_status st)
+{
+    switch (st) {
+    case QGEMM_OK: return "QGEMM_OK";
+    case QGEMM_ERR_NULL_POINTER: return "QGEMM_ERR_NULL_POINTER";
+    case QGEMM_ERR_BAD_SHAPE: return "QGEMM_ERR_BAD_SHAPE";
+    case QGEMM_ERR_BAD_LAYOUT: return "QGEMM_ERR_BAD_LAYOUT";
+    case QGEMM_ERR_BAD_FORMAT: return "QGEMM_ERR_BAD_FORMAT";
+    case QGEMM_ERR_UNSUPPORTED_DEVICE: return "QGEMM_ERR_UNSUPPORTED_DEVICE";
+    case QGEMM_ERR_HIP: return "QGEMM_ERR_HIP";
+    }
+    return "QGEMM_UNKNOWN_STATUS";
+}
+
+const char *qgemm_last_error(void) { return g_last_error.c_str(); }
+
+int qgemm_select_tile(int path, int64_t M, int64_t N, int64_t K)
+{
+    (void)K;
+    if (path < 0 || path > 3)
+        return -1;
+    return select_tile_impl(path, M, N);
+}
+
+int qgemm_tile_rows(int tile) { return (tile >= 0 && tile < NUM_TILES) ? tile_edge(tile) : 0; }
+
+int qgemm_force_tile(int tile)
+{
+    if (tile < -1 || tile >= NUM_TILES)
+        return -2;
+    const int prev = g_forced_tile;
+    g_forced_tile = tile;
+    return prev;
+}
+
+static qgemm_status i8_common(const int8_t *A, int64_t lda, const int8_t *B, int64_t ldb, const float *sa,
+                              const float *sb, const uint16_t *bias, void *C, int64_t ldc, Shape s, void *stream,
+                              int out)
+{
+    TRY(check_shape(s, true));
+    if (s.M == 0 || s.N == 0)
+        return QGEMM_OK;
+    TRY(check_operand("A", A, lda, s.K));
+    TRY(check_operand("B", B, ldb, s.K));
+    if (out == OUT_BF16) {
+        TRY(check_fp32_scales(sa, sb));
+        TRY(check_bias(bias));
+    }
+    TRY(check_output(C, ldc, s.N, out == OUT_I32 ? 4 : 2));
+    TRY(check_device());
+    const int tile = pick_tile(0, s);
+    Params p = base_params(A, lda, B, ldb, C, ldc, s, s.K, tile);
+    TRY(check_grid(p));
+    p.scale_a = sa;
+    p.scale_b = sb;
+    p.bias = bias;
+    return finish(launch_i8(tile, bias != nullptr, out, p, (hipStream_t)stream));
+}
+
+qgemm_status qgemm_i8_rowwise(const int8_t *A, int64_t lda, const int8_t *B, int64_t ldb, const float *scale_a,
+                              const float *scale_b, const uint16_t *bias, uint16_t *C, int64_t ldc, int64_t M,
+                              int64_t N, int64_t K, void *stream)
+{
+    return i8_common(A, lda, B, ldb, scale_a, scale_b, bias, C, ldc, Shape{M, N, K}, stream, OUT_BF16);
+}
+
+qgemm_status qgemm_i8_acc_i32(const int8_t *A, int64_t lda, const int8_t *B, int64_t ldb, int32_t *C,
+                              int64_t ldc, int64_t M, int64_t N, int64_t K, void *stream)
+{
+    return i8_common(A, lda, B, ldb, nullptr, nullptr, nullptr, C, ldc, Shape{M, N, K}, stream, OUT_I32);
+}
+
+qgemm_status qgemm_f8_pertoken(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb, const float *scale_a,
+                               const float *scale_b, const uint16_t *bias, uint16_t *C, int64_t ldc, int64_t M,
+                               int64_t N, int64_t K, void *stream)
+{
+    const Shape s{M, N, K};
+    TRY(check_shape(s, false));
+    if (M == 0 || N == 0)
+        return QGEMM_OK;
+    TRY(check_operand("A", A, lda, K));
+    TRY(check_operand("B", B, ldb, K));
+    TRY(check_fp32_scales(scale_a, scale_b));
+    TRY(check_bias(bias));
+    TRY(check_output(C, ldc, N, 2));
+    TRY(check_device());
+    const int tile = pick_tile(1, s);
+    Params p = base_params(A, lda, B, ldb, C, ldc, s, K, tile);
+    TRY(check_grid(p));
+    p.scale_a = scale_a;
+    p.scale_b = scale_b;
+    p.bias = bias;
+    return finish(launch_f8(tile, bias != nullptr, p, (hipStream_t)stream));
+}
+
+qgemm_status qgemm_mx(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const void *B, int64_t ldb_bytes,
+                      const uint8_t *scale_a, const uint8_t *scale_b, qgemm_mx_bscale b_layout,
+                      const uint16_t *bias, uint16_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                      void *stream)
+{
+    const Shape s{M, N, K};
+    if (fmt != QGEMM_MX_E4M3 && fmt != QGEMM_MX_E2M1)
+        return fail(QGEMM_ERR_BAD_FORMAT, "unknown MX element format %d", (int)fmt);
+    if (b_layout != QGEMM_MX_BSCALE_1x32 && b_layout != QGEMM_MX_BSCALE_32x32)
+        return fail(QGEMM_ERR_BAD_FORMAT, "unknown B-scale layout %d", (int)b_layout);
+    TRY(check_shape(s, false));
+    if (M == 0 || N == 0)
+        return QGEMM_OK;
+    const int64_t row_bytes = (fmt == QGEMM_MX_E4M3) ? K : K / 2;
+    TRY(check_operand("A", A, lda_bytes, row_bytes));
+    TRY(check_operand("B", B, ldb_bytes, row_bytes));
+    if (!scale_a)
+        return fail(QGEMM_ERR_NULL_POINTER, "scale_a is NULL");
+    if (!scale_b)
+        return fail(QGEMM_ERR_NULL_POINTER, "scale_b is NULL");
+    TRY(check_bias(bias));
+    TRY(check_output(C, ldc, N, 2));
+    TRY(check_device());
+    const int path = (fmt == QGEMM_MX_E4M3) ? 2 : 3;
+    const int tile = pick_tile(path, s);
+    Params p = base_params(A, lda_bytes, B, ldb_bytes, C, ldc, s, row_bytes, tile);
+    TRY(check_grid(p));
+    p.mx_sa = scale_a;
+    p.mx_sb = scale_b;
+    p.bias = bias;
+    // Scale words load whole when every lane's bytes of a K step are aligned:
+    // e2m1 takes 4 bytes per lane half (K/32 % 4 == 0), e4m3 takes 2 (K/32 even),
+    // and the scale arrays themselves start aligned.
+    const int wb = (fmt == QGEMM_MX_E2M1) ? 4 : 2;
+    const bool svec = ((K / 32) % wb == 0) && aligned(scale_a, wb) && aligned(scale_b, wb);
+    const int brows = (int)b_layout;
+    if (fmt == QGEMM_MX_E4M3)
+        return finish(launch_mx8(tile, bias != nullptr, brows, svec, p, (hipStream_t)stream));
+    return finish(launch_mx4(tile, bias != nullptr, brows, svec, p, (hipStream_t)stream));
+}
+
+}  // extern "C"

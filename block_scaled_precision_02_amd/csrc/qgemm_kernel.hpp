@@ -1,0 +1,490 @@
+// qgemm_kernel.hpp -- gfx950 kernels for the scaled low-precision GEMM
+//
+//     C[m,n] = bf16( sa[m] * sb[n] * sum_k A[m,k] B[n,k] + bias[n] )
+//
+// One template covers the three element paths (the rowwise INT8 GEMM of
+// comfy-kitchen PR #174 "Optimize HIP WMMA INT8 GEMM staging, epilogue, and
+// deep-K tiling"; the per-token FP8 and 32-wide ue8m0 MXFP8 GEMMs of ROCm/mori
+// PR #806 "perf(gemm-ar): mxfp8 with row-major scales staged through LDS";
+// the MXFP4 GEMM of ROCm/FlyDSL PR #990 "[fp4_gemm_4wave] MXFP4 GEMM perf
+// optimize").  Written for CDNA4 only:
+//
+//  * 256 threads = 4 wave64s in a 2x2 grid; a wave owns a (TM*32) x (TN*32)
+//    block of C held in 32x32 MFMA accumulators (TM*TN*16 per lane, so the
+//    256x256 tile keeps 256 accumulator registers per lane, which the
+//    compiler places in AGPRs).
+//  * K advances 128 bytes per step for every element type (128 int8 or e4m3
+//    elements, 256 e2m1 elements); each step of A and B is staged HBM ->
+//    VGPR -> LDS into one of two LDS buffers, 16-byte chunks XOR-swizzled by
+//    row so that the fragment reads of 32 consecutive rows hit distinct banks.
+//    Global loads are raw buffer loads whose range check zero-fills rows past
+//    M / N; the K tail is zero-filled by pushing its offset out of range in
+//    the per-lane VGPR offset (never through soffset, which the range check
+//    ignores -- the point made in ROCm/mori PR #806's review thread).
+//  * One barrier per K step: step k+1 is written to the idle LDS buffer and
+//    step k+2's global loads are issued before the MFMAs of step k start.
+//  * MX scales (ue8m0) travel with the operand prefetch straight into VGPRs
+//    and feed v_mfma_scale_f32_32x32x64_f8f6f4 as its per-lane scale operand;
+//    op_sel picks the byte for each K sub-step.
+//  * The MFMA computes C^T (B is the instruction's first operand) so that
+//    every lane ends with runs of 4 consecutive n for one m: the epilogue
+//    writes 8-byte bf16 vectors.
+//  * Epilogue: fixed-order binary32, (float)acc * sa * sb + bias, no
+//    contraction (the library is built with -ffp-contract=off), bias add
+//    skipped entirely when there is no bias so -0 survives, then RNE to bf16
+//    (v_cvt_pk_bf16_f32).  Full tiles store without per-element masks.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <type_traits>
+
+namespace qgemm {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+enum Path { PATH_I8 = 0, PATH_F8 = 1, PATH_MX8 = 2, PATH_MX4 = 3 };
+enum OutKind { OUT_BF16 = 0, OUT_I32 = 1 };
+
+// Kernel arguments (one struct, passed by value).
+struct Params {
+    const uint8_t *A, *B;          // operand rows, K contiguous
+    int64_t lda, ldb;              // row strides in bytes
+    const float *scale_a;          // [M] (INT8 / FP8)
+    const float *scale_b;          // [N] (INT8 / FP8)
+    const uint8_t *mx_sa;          // ue8m0 [M, K/32]      (MX)
+    const uint8_t *mx_sb;          // ue8m0 [N or N/32, K/32] (MX)
+    const uint16_t *bias;          // [N] bf16 bits or null
+    void *C;                       // [M, ldc] bf16 bits (or int32 for OUT_I32)
+    int64_t ldc;                   // elements
+    int M, N, K;                   // K in elements
+    int kbytes;                    // bytes of one operand row
+    int ksteps;                    // ceil(kbytes / 128)
+    int kblocks;                   // K / 32 (MX scale row length in bytes)
+    int tiles_m, tiles_n;
+    int group_m;                   // tile rows per group in the launch order
+};
+
+constexpr int KSTEP_BYTES = 128;
+constexpr int CHUNKS = KSTEP_BYTES / 16;   // 16-byte chunks per staged row
+constexpr unsigned OOB = 0x80000000u;      // offset beyond every range check
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>());
+        static_for<I + 1, N>(f);
+    }
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    // 0x00020000: raw buffer, 32-bit data format, range-checked against bytes.
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, unsigned off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// LDS barrier: every LDS write of this wave has landed, then all waves meet.
+// Outstanding global loads stay in flight.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Position of 16-byte chunk c of staged row r inside an LDS tile of rows of
+// 128 bytes.  Rows r..r+7 place the same logical chunk in 8 different slots.
+__device__ __forceinline__ int lds_off(int r, int c)
+{
+    return r * KSTEP_BYTES + ((c ^ (r & 7)) << 4);
+}
+
+// Workgroup -> output tile.  Workgroups are handed to the 8 XCDs round-robin;
+// renumber so each XCD gets a contiguous run of the grouped order (tiles
+// that share A and B panels then share that XCD's L2), then walk the tiles
+// in groups of group_m tile rows.
+__device__ __forceinline__ void tile_of(const Params &p, int &tm, int &tn)
+{
+    const int G = p.tiles_m * p.tiles_n;
+    const int i = blockIdx.x;
+    const int xcd = i & 7, local = i >> 3;
+    const int per = G >> 3, rem = G & 7;
+    const int pid = xcd * per + (xcd < rem ? xcd : rem) + local;
+    const int width = p.group_m * p.tiles_n;
+    const int group = pid / width;
+    const int first_m = group * p.group_m;
+    const int gsz = min(p.tiles_m - first_m, p.group_m);
+    const int in = pid - group * width;
+    tm = first_m + in % gsz;
+    tn = in / gsz;
+}
+
+template <int PATH> struct PathTraits;
+template <> struct PathTraits<PATH_I8> { static constexpr int NSUB = 4; using Frag = i32x4; };
+template <> struct PathTraits<PATH_F8> { static constexpr int NSUB = 2; using Frag = i32x8; };
+template <> struct PathTraits<PATH_MX8> { static constexpr int NSUB = 2; using Frag = i32x8; };
+template <> struct PathTraits<PATH_MX4> { static constexpr int NSUB = 4; using Frag = i32x8; };
+
+// Fragment of one 32-row MFMA operand for K sub-step S, read from a staged
+// tile.  Lane (h = lane/32, row = lane%32):
+//   INT8  v_mfma_i32_32x32x32_i8: 16 bytes, chunk 2S+h.
+//   e4m3  v_mfma_*_32x32x64_f8f6f4: 32 bytes; the instruction forms its
+//         first 32-element K block from VGPRs 0-3 of both lane halves and its
+//         second from VGPRs 4-7, so VGPRs 0-3 take chunk 2S+h (block S of the
+//         step) and VGPRs 4-7 take chunk 4+2S+h (block 2+S).
+//   e2m1  16 bytes = one whole 32-element block per lane: chunk 4h+S (block
+//         4h+S of the step's eight); VGPRs 4-7 are unused.
+// A and B use the same map, so the products pair up; the scale operand of a
+// lane belongs to the block its lane half holds (see scale words below).
+template <int PATH, int S>
+__device__ __forceinline__ typename PathTraits<PATH>::Frag
+load_frag(const uint8_t *tile, int row, int h)
+{
+    typename PathTraits<PATH>::Frag f;
+    if constexpr (PATH == PATH_I8) {
+        f = *(const i32x4 *)(tile + lds_off(row, 2 * S + h));
+    } else if constexpr (PATH == PATH_MX4) {
+        i32x4 lo = *(const i32x4 *)(tile + lds_off(row, 4 * h + S));
+        f = i32x8{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+    } else {
+        i32x4 lo = *(const i32x4 *)(tile + lds_off(row, 2 * S + h));
+        i32x4 hi = *(const i32x4 *)(tile + lds_off(row, 4 + 2 * S + h));
+        f = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    return f;
+}
+
+template <int PATH> struct AccT { using T = f32x16; };
+template <> struct AccT<PATH_I8> { using T = i32x16; };
+
+// acc += B-fragment x A-fragment (the MFMA sees B as its M side: C^T).
+template <int PATH, int S>
+__device__ __forceinline__ void mfma(typename AccT<PATH>::T &acc,
+                                     const typename PathTraits<PATH>::Frag &fb,
+                                     const typename PathTraits<PATH>::Frag &fa,
+                                     unsigned sc_b, unsigned sc_a)
+{
+    if constexpr (PATH == PATH_I8) {
+        acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb, fa, acc, 0, 0, 0);
+    } else if constexpr (PATH == PATH_F8) {
+        // scale operands 0 with op_sel 0: the unscaled f8f6f4 encoding.
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, acc, 0, 0, 0, 0, 0, 0);
+    } else if constexpr (PATH == PATH_MX8) {
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, acc, 0, 0, S, (int)sc_b, S, (int)sc_a);
+    } else {
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, acc, 4, 4, S, (int)sc_b, S, (int)sc_a);
+    }
+}
+
+// ue8m0 scale word for one lane and one K step.  The lane half h needs the
+// blocks its fragments hold in sub-steps 0..NSUB-1, packed so that byte S is
+// sub-step S's scale:
+//   e2m1: blocks 4h..4h+3 of the step  -> 4 consecutive bytes
+//   e4m3: blocks 2h, 2h+1 of the step  -> 2 consecutive bytes
+// SVEC: the bytes are read with one aligned load (scale rows are whole
+// dwords / halfwords); otherwise byte by byte.  Blocks at or past K/32 read
+// as 0 (their data is zero as well).
+template <int PATH, bool SVEC>
+__device__ __forceinline__ unsigned load_scale_word(__amdgpu_buffer_rsrc_t r, int row_off, int kt,
+                                                    int h, int kblocks)
+{
+    constexpr int NB = (PATH == PATH_MX4) ? 8 : 4;   // blocks per K step
+    constexpr int NL = (PATH == PATH_MX4) ? 4 : 2;   // blocks per lane half
+    const int b0 = kt * NB + h * NL;
+    if constexpr (SVEC) {
+        const unsigned off = (b0 < kblocks) ? (unsigned)(row_off + b0) : OOB;
+        if constexpr (NL == 4)
+            return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+        else
+            return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+    } else {
+        unsigned w = 0;
+#pragma unroll
+        for (int q = 0; q < NL; ++q) {
+            const unsigned off = (b0 + q < kblocks) ? (unsigned)(row_off + b0 + q) : OOB;
+            w |= (unsigned)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0) << (8 * q);
+        }
+        return w;
+    }
+}
+
+__device__ __forceinline__ unsigned pack_bf16(float x, float y)
+{
+    bf16x2 v;
+    v[0] = (__bf16)x;
+    v[1] = (__bf16)y;
+    return __builtin_bit_cast(unsigned, v);
+}
+
+template <int PATH, int TM, int TN, bool BIAS, int BROWS, bool SVEC, int OUT>
+__global__ void __launch_bounds__(256, 1) qgemm_kernel(const Params p)
+{
+    constexpr int BM = 2 * TM * 32, BN = 2 * TN * 32;
+    constexpr int NSUB = PathTraits<PATH>::NSUB;
+    constexpr int CA = BM * CHUNKS / 256;   // A chunks staged per thread per step
+    constexpr int CB = BN * CHUNKS / 256;
+    constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4);
+    using Frag = typename PathTraits<PATH>::Frag;
+    using Acc = typename AccT<PATH>::T;
+
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + BN) * KSTEP_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5, r32 = lane & 31;
+
+    int tm, tn;
+    tile_of(p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int rows_a = min(BM, p.M - m0), rows_b = min(BN, p.N - n0);
+
+    // Operand ranges: rows past M / N and everything after the last valid
+    // row's K bytes are out of range and read as zero.
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * p.lda,
+                                                (uint32_t)((rows_a - 1) * p.lda + p.kbytes));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + (int64_t)n0 * p.ldb,
+                                                (uint32_t)((rows_b - 1) * p.ldb + p.kbytes));
+
+    // Staging map: thread tid copies chunk tid%8 of rows tid/8 + 32*i.
+    const int st_row = tid >> 3, st_c = tid & 7;
+    u32x4 ga[CA], gb[CB];
+
+    // MX scale ranges and per-lane row offsets.
+    __amdgpu_buffer_rsrc_t rsa, rsb;
+    int sa_off[TM], sb_off[TN];
+    unsigned sa_next[TM], sb_next[TN], sa_cur[TM], sb_cur[TN];
+    if constexpr (MX) {
+        rsa = make_rsrc(p.mx_sa + (int64_t)m0 * p.kblocks, (uint32_t)(rows_a * p.kblocks));
+        if constexpr (BROWS == 1) {
+            rsb = make_rsrc(p.mx_sb + (int64_t)n0 * p.kblocks, (uint32_t)(rows_b * p.kblocks));
+        } else {
+            rsb = make_rsrc(p.mx_sb + (int64_t)(n0 / 32) * p.kblocks,
+                            (uint32_t)(((rows_b + 31) / 32) * p.kblocks));
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            sa_off[i] = (wm * TM * 32 + i * 32 + r32) * p.kblocks;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            sb_off[j] = (BROWS == 1 ? (wn * TN * 32 + j * 32 + r32) : (wn * TN + j)) * p.kblocks;
+    }
+
+    auto load_step = [&](int kt) {
+        const int kb = kt * KSTEP_BYTES + st_c * 16;
+        const bool kin = kb < p.kbytes;
+#pragma unroll
+        for (int i = 0; i < CA; ++i)
+            ga[i] = ld16(ra, kin ? (unsigned)((st_row + 32 * i) * p.lda + kb) : OOB);
+#pragma unroll
+        for (int i = 0; i < CB; ++i)
+            gb[i] = ld16(rb, kin ? (unsigned)((st_row + 32 * i) * p.ldb + kb) : OOB);
+        if constexpr (MX) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                sa_next[i] = load_scale_word<PATH, SVEC>(rsa, sa_off[i], kt, h, p.kblocks);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                sb_next[j] = load_scale_word<PATH, SVEC>(rsb, sb_off[j], kt, h, p.kblocks);
+        }
+    };
+    auto store_step = [&](int buf) {
+        uint8_t *ta = &lds[buf][0];
+        uint8_t *tb = &lds[buf][BM * KSTEP_BYTES];
+#pragma unroll
+        for (int i = 0; i < CA; ++i)
+            *(u32x4 *)(ta + lds_off(st_row + 32 * i, st_c)) = ga[i];
+#pragma unroll
+        for (int i = 0; i < CB; ++i)
+            *(u32x4 *)(tb + lds_off(st_row + 32 * i, st_c)) = gb[i];
+    };
+
+    Acc acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = Acc{};
+
+    // Prologue: step 0 into LDS buffer 0, step 1 into registers.
+    load_step(0);
+    store_step(0);
+    if constexpr (MX) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) sa_cur[i] = sa_next[i];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) sb_cur[j] = sb_next[j];
+    }
+    if (p.ksteps > 1)
+        load_step(1);
+    lds_barrier();
+
+    const int arow = wm * TM * 32 + r32;
+    const int brow = wn * TN * 32 + r32;
+
+    for (int kt = 0; kt < p.ksteps; ++kt) {
+        const int cur = kt & 1;
+        unsigned sa_step[TM], sb_step[TN];
+        if constexpr (MX) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) sa_step[i] = sa_cur[i];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) sb_step[j] = sb_cur[j];
+        }
+        if (kt + 1 < p.ksteps) {
+            // Step kt+1 has had a whole step to arrive: park it in the idle
+            // buffer (last read before the previous barrier), then start
+            // fetching step kt+2.
+            store_step(cur ^ 1);
+            if constexpr (MX) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i) sa_cur[i] = sa_next[i];
+#pragma unroll
+                for (int j = 0; j < TN; ++j) sb_cur[j] = sb_next[j];
+            }
+            if (kt + 2 < p.ksteps)
+                load_step(kt + 2);
+        }
+        const uint8_t *ta = &lds[cur][0];
+        const uint8_t *tb = &lds[cur][BM * KSTEP_BYTES];
+        static_for<0, NSUB>([&](auto sc) {
+            constexpr int S = decltype(sc)::value;
+            Frag fa[TM], fb[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                fa[i] = load_frag<PATH, S>(ta, arow + 32 * i, h);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                fb[j] = load_frag<PATH, S>(tb, brow + 32 * j, h);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int jj = 0; jj < TN; ++jj) {
+                    const int j = (i & 1) ? (TN - 1 - jj) : jj;   // serpentine: reuse fb[j]
+                    mfma<PATH, S>(acc[i][j], fb[j], fa[i], MX ? sb_step[j] : 0u, MX ? sa_step[i] : 0u);
+                }
+        });
+        lds_barrier();
+    }
+
+    // ---------------------------------------------------------- epilogue
+    // Lane holds, for tile (i, j): m = m0 + arow + 32i, and for g = 0..3 the
+    // four consecutive n = n0 + wn*TN*32 + 32j + 8g + 4h + {0..3} in
+    // acc[i][j][4g..4g+3].  Every access goes through a range-checked buffer
+    // descriptor: loads past M / N read 0, stores past them are dropped, so
+    // the only difference between a full tile and an edge tile is that the
+    // edge tile stores element by element (columns past N inside a row of
+    // ldc must not be touched).
+    constexpr int ESZ = (OUT == OUT_I32) ? 4 : 2;
+    const bool full = (rows_a == BM) && (rows_b == BN);
+    const int nloc_base = wn * TN * 32 + 4 * h;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc((const uint8_t *)p.C + (int64_t)m0 * p.ldc * ESZ,
+                                                (uint32_t)((int64_t)rows_a * p.ldc * ESZ));
+    const unsigned col0 = (unsigned)(n0 * ESZ);
+    __amdgpu_buffer_rsrc_t rsb_e, rbias;
+    if constexpr (OUT == OUT_BF16 && !MX)
+        rsb_e = make_rsrc(p.scale_b + n0, (uint32_t)(rows_b * 4));
+    if constexpr (BIAS)
+        rbias = make_rsrc(p.bias + n0, (uint32_t)(rows_b * 2));
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int mloc = arow + 32 * i;
+        const bool mok = mloc < rows_a;
+        float sa = 0.f;
+        if constexpr (OUT == OUT_BF16 && !MX) {
+            if (mok)
+                sa = p.scale_a[m0 + mloc];
+        }
+        const unsigned rowoff = (unsigned)((int64_t)mloc * p.ldc * ESZ);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int nloc = nloc_base + 32 * j + 8 * g;
+                const unsigned off = rowoff + col0 + (unsigned)(nloc * ESZ);
+                if constexpr (OUT == OUT_I32) {
+                    const i32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1],
+                                     acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                    if (full) {
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rc, off, 0, 0);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            __builtin_amdgcn_raw_buffer_store_b32(
+                                (unsigned)v[r], rc, (nloc + r < rows_b) ? off + 4 * r : OOB, 0, 0);
+                    }
+                } else {
+                    // Per-column scale and bias: one vector load in a full tile;
+                    // element loads at an edge (a vector load that runs past the
+                    // range returns zeros for all of its elements).
+                    float f[4];
+                    unsigned sbw[4], bbw[4];
+                    if (full) {
+                        if constexpr (!MX) {
+                            const u32x4 t = ld16(rsb_e, (unsigned)(nloc * 4));
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) sbw[r] = t[r];
+                        }
+                        if constexpr (BIAS) {
+                            const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(rbias, (unsigned)(nloc * 2), 0, 0);
+                            const unsigned t0 = t[0], t1 = t[1];
+                            bbw[0] = t0 << 16;
+                            bbw[1] = t0 & 0xffff0000u;
+                            bbw[2] = t1 << 16;
+                            bbw[3] = t1 & 0xffff0000u;
+                        }
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const bool in = nloc + r < rows_b;
+                            if constexpr (!MX)
+                                sbw[r] = __builtin_amdgcn_raw_buffer_load_b32(
+                                    rsb_e, in ? (unsigned)((nloc + r) * 4) : OOB, 0, 0);
+                            if constexpr (BIAS)
+                                bbw[r] = (unsigned)__builtin_amdgcn_raw_buffer_load_b16(
+                                             rbias, in ? (unsigned)((nloc + r) * 2) : OOB, 0, 0) << 16;
+                        }
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float x;
+                        if constexpr (PATH == PATH_I8)
+                            x = (float)acc[i][j][4 * g + r];
+                        else
+                            x = acc[i][j][4 * g + r];
+                        // (scalars only under bit_cast: clang's bit_cast of an
+                        // ext_vector element reads element 0)
+                        if constexpr (!MX) {
+                            x = x * sa;
+                            x = x * __builtin_bit_cast(float, sbw[r]);
+                        }
+                        if constexpr (BIAS)
+                            x = x + __builtin_bit_cast(float, bbw[r]);
+                        f[r] = x;
+                    }
+                    const u32x2 v = {pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3])};
+                    if (full) {
+                        __builtin_amdgcn_raw_buffer_store_b64(v, rc, off, 0, 0);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            __builtin_amdgcn_raw_buffer_store_b16(
+                                (unsigned short)(v[r >> 1] >> (16 * (r & 1))), rc,
+                                (nloc + r < rows_b) ? off + 2 * r : OOB, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace qgemm

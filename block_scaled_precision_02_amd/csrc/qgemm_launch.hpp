@@ -1,0 +1,37 @@
+// qgemm_launch.hpp -- host-side launch of one kernel variant.
+#pragma once
+#include <hip/hip_runtime.h>
+#include "qgemm_kernel.hpp"
+
+namespace qgemm {
+
+// Tile ids of the host table: 0 -> 256x256 (2x2 waves of 128x128),
+// 1 -> 128x128 (2x2 waves of 64x64).
+constexpr int NUM_TILES = 2;
+__host__ __device__ constexpr int tile_edge(int tile) { return tile == 0 ? 256 : 128; }
+
+template <int PATH, int TM, int TN, bool BIAS, int BROWS, bool SVEC, int OUT>
+hipError_t launch_variant(const Params &p, hipStream_t s)
+{
+    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(256);
+    hipLaunchKernelGGL((qgemm_kernel<PATH, TM, TN, BIAS, BROWS, SVEC, OUT>), grid, block, 0, s, p);
+    return hipGetLastError();
+}
+
+template <int PATH, bool BIAS, int BROWS, bool SVEC, int OUT>
+hipError_t launch_tile(int tile, const Params &p, hipStream_t s)
+{
+    switch (tile) {
+    case 0: return launch_variant<PATH, 4, 4, BIAS, BROWS, SVEC, OUT>(p, s);
+    case 1: return launch_variant<PATH, 2, 2, BIAS, BROWS, SVEC, OUT>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// Per-path entry points, one translation unit each.
+hipError_t launch_i8(int tile, bool bias, int out, const Params &p, hipStream_t s);
+hipError_t launch_f8(int tile, bool bias, const Params &p, hipStream_t s);
+hipError_t launch_mx8(int tile, bool bias, int brows, bool svec, const Params &p, hipStream_t s);
+hipError_t launch_mx4(int tile, bool bias, int brows, bool svec, const Params &p, hipStream_t s);
+
+}  // namespace qgemm

@@ -1,0 +1,159 @@
+/*
+ * qgemm.h -- C ABI of the MI355X (gfx950) scaled low-precision GEMM library
+ *
+ *     C = bf16( scale_A (.) scale_B (.) (A . B^T) + bias )
+ *
+ * in three element paths:
+ *   qgemm_i8_rowwise   int8 A and B, int32 accumulation, fp32 per-row scale of
+ *                      A and per-row scale of B ("rowwise"), optional bf16
+ *                      bias, bf16 out.  Defined by comfy-kitchen PR #174
+ *                      "Optimize HIP WMMA INT8 GEMM staging, epilogue, and
+ *                      deep-K tiling": Summary (rowwise scales and bias,
+ *                      no-bias signed zero), Validation (exact int8 results),
+ *                      Update "rebased onto v0.2.40" (epilogue association
+ *                      (acc*sa)*sb).
+ *   qgemm_f8_pertoken  e4m3 A and B with fp32 per-token (row of A) and
+ *                      per-channel (row of B) scales, the "ptpc" GEMM of
+ *                      ROCm/mori PR #806 "perf(gemm-ar): mxfp8 with row-major
+ *                      scales staged through LDS", commit message table.
+ *   qgemm_mx           MX: e4m3 or e2m1 elements with one ue8m0 scale per 32
+ *                      elements along K; A scales [M, K/32] and B scales
+ *                      [N/32, K/32] as uint8 row-major ("mxfp8_raw", ROCm/mori
+ *                      PR #806, What) or [N, K/32] (the 1x32 FP4 scales of
+ *                      ROCm/FlyDSL PR #990 "[fp4_gemm_4wave] MXFP4 GEMM perf
+ *                      optimize").
+ *
+ * Numerics (all paths): the product is accumulated exactly (int32) for int8
+ * and in fp32 by the matrix cores for e4m3 / e2m1; the epilogue is, per
+ * output, in binary32 with round-to-nearest-even and no fused operations:
+ *     f = (float)acc;  f = f * scale_a[m];  f = f * scale_b[n];   (int8, fp8)
+ *     if (bias) f = f + bias[n];
+ *     C[m,n] = bf16_round_nearest_even(f)
+ * Without bias nothing is added, so a negative-zero product stays -0.
+ *
+ * Conventions shared by every entry point:
+ *  - Every pointer is device memory of the current HIP device, owned by the
+ *    caller.  The library keeps no pointer after the call returns and
+ *    allocates no device memory.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    device's default stream).  The call returns once the kernel is queued.
+ *  - Arguments are validated on the host before anything is enqueued: on any
+ *    non-OK status nothing has been launched and C is untouched.  The text of
+ *    the last failure on the calling thread is qgemm_last_error().
+ *  - M == 0 or N == 0 is a no-op that returns QGEMM_OK once M, N and K pass
+ *    the shape checks (pointers may then be NULL).  K must be a positive
+ *    multiple of 32 (the MX block size) and at most 131071 for int8 (the
+ *    int32 accumulator cannot overflow below that).
+ *  - Only C[0..M) x [0..N) is written; the rest of each ldc-long row is left
+ *    alone.  C must not alias any input.
+ *  - Alignment: A, B, C 16-byte aligned; lda, ldb (bytes) multiples of 16 and
+ *    at least the bytes of one row; ldc (elements) a multiple of 8 and >= N;
+ *    scale_a / scale_b (fp32) 4-byte aligned; bias 2-byte aligned; MX scale
+ *    arrays have no alignment requirement.  256 * lda and 256 * ldb must stay
+ *    below 2^31 bytes.
+ *  - The device must be gfx950; anything else returns
+ *    QGEMM_ERR_UNSUPPORTED_DEVICE.  There is no fallback path.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QGEMM_OK = 0,
+    QGEMM_ERR_NULL_POINTER = 1,       /* a required pointer is NULL (bias may be)      */
+    QGEMM_ERR_BAD_SHAPE = 2,          /* M<0, N<0, K<=0, K%32, int8 K>131071, M or N
+                                         >= 2^31                                       */
+    QGEMM_ERR_BAD_LAYOUT = 3,         /* stride below the row, stride or pointer
+                                         misaligned, 256*ld beyond 2^31 bytes         */
+    QGEMM_ERR_BAD_FORMAT = 4,         /* unknown MX element format or B-scale layout  */
+    QGEMM_ERR_UNSUPPORTED_DEVICE = 5, /* current device is not gfx950                 */
+    QGEMM_ERR_HIP = 6                 /* HIP reported an error; see qgemm_last_error  */
+} qgemm_status;
+
+/* MX element format, the same for A and B. */
+typedef enum {
+    QGEMM_MX_E4M3 = 0, /* OCP E4M3FN, one byte per element                          */
+    QGEMM_MX_E2M1 = 1  /* OCP E2M1, two per byte: element k (k even) in bits 3:0 of
+                          byte k/2, element k+1 in bits 7:4                         */
+} qgemm_mx_fmt;
+
+/* Rows of B that share one ue8m0 scale per 32-element K block. */
+typedef enum {
+    QGEMM_MX_BSCALE_1x32 = 1,  /* scale_b is [N, K/32]            */
+    QGEMM_MX_BSCALE_32x32 = 32 /* scale_b is [ceil(N/32), K/32]   */
+} qgemm_mx_bscale;
+
+/* INT8 rowwise GEMM.
+ *   A        [M, K] int8, row stride lda bytes
+ *   B        [N, K] int8, row stride ldb bytes
+ *   scale_a  [M] fp32, scale_b [N] fp32 (any finite values, sign kept)
+ *   bias     [N] bf16 bit patterns, or NULL for no bias
+ *   C        [M, ldc] bf16 bit patterns (output)
+ * acc[m,n] = sum_k A[m,k]*B[n,k] in int32, exact; then the epilogue above. */
+qgemm_status qgemm_i8_rowwise(const int8_t *A, int64_t lda, const int8_t *B, int64_t ldb,
+                              const float *scale_a, const float *scale_b, const uint16_t *bias,
+                              uint16_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                              void *stream);
+
+/* The INT8 product alone: C[m,n] = sum_k A[m,k]*B[n,k] as int32 (the
+ * accumulator qgemm_i8_rowwise applies its epilogue to), C [M, ldc] int32.
+ * Same operand conventions as qgemm_i8_rowwise. */
+qgemm_status qgemm_i8_acc_i32(const int8_t *A, int64_t lda, const int8_t *B, int64_t ldb,
+                              int32_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                              void *stream);
+
+/* FP8 e4m3 per-token / per-channel GEMM.
+ *   A        [M, K] e4m3fn codes, row stride lda bytes
+ *   B        [N, K] e4m3fn codes, row stride ldb bytes
+ *   scale_a  [M] fp32 per token, scale_b [N] fp32 per channel
+ *   bias, C  as for qgemm_i8_rowwise
+ * acc[m,n] = sum_k e4m3(A[m,k]) * e4m3(B[n,k]) in fp32 (matrix cores); then
+ * the epilogue above.  NaN codes propagate. */
+qgemm_status qgemm_f8_pertoken(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                               const float *scale_a, const float *scale_b, const uint16_t *bias,
+                               uint16_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                               void *stream);
+
+/* MX GEMM (block-scaled e4m3 or e2m1).
+ *   A        [M, K] elements of fmt, row stride lda_bytes (K or K/2 bytes of data)
+ *   B        [N, K] elements of fmt, row stride ldb_bytes
+ *   scale_a  ue8m0 [M, K/32], row-major, row stride K/32 bytes
+ *   scale_b  ue8m0 [N, K/32] (b_layout 1x32) or [ceil(N/32), K/32] (32x32)
+ *   bias, C  as for qgemm_i8_rowwise
+ * A~[m,k] = fmt(A[m,k]) * 2^(scale_a[m,k/32]-127), B~ likewise with the scale
+ * of row n (1x32) or n/32 (32x32); acc = sum_k A~ B~ in fp32 (matrix cores);
+ * then f = acc, [+ bias], bf16 round-nearest-even.  Scale code 255 is NaN. */
+qgemm_status qgemm_mx(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const void *B,
+                      int64_t ldb_bytes, const uint8_t *scale_a, const uint8_t *scale_b,
+                      qgemm_mx_bscale b_layout, const uint16_t *bias, uint16_t *C, int64_t ldc,
+                      int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Text of the last non-OK status returned on the calling thread ("" if none). */
+const char *qgemm_last_error(void);
+
+/* Fixed name of a status code, e.g. "QGEMM_ERR_BAD_SHAPE". */
+const char *qgemm_status_string(qgemm_status status);
+
+/* Tile variant the host-side table picks for a problem (pure host logic, no
+ * HIP call).  path: 0 int8, 1 fp8, 2 MX e4m3, 3 MX e2m1.  Returns the tile id
+ * (0: 256x256, 1: 128x128), or -1 for a bad path. */
+int qgemm_select_tile(int path, int64_t M, int64_t N, int64_t K);
+
+/* Block edge (rows of A = rows of B) of a tile id, or 0 for an unknown id. */
+int qgemm_tile_rows(int tile);
+
+/* Force a tile id for later calls on the calling thread (benchmarks and the
+ * variant-equivalence tests); -1 restores the table.  Returns the previous
+ * value, or -2 (and changes nothing) for an unknown id. */
+int qgemm_force_tile(int tile);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

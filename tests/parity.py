@@ -1,0 +1,116 @@
+"""Shared helpers for the GPU parity tests: run the library and the oracle on
+the same inputs and compare them.
+
+Bars (from the GEMM's definition):
+  INT8      bit-exact bf16 output (and int32 accumulator)
+  FP8 / MX  per element |gpu - oracle| <= 1e-2 * sum_k |a_k b_k| (scaled)
+            + 1 bf16 ulp of the oracle's value, and cosine >= 0.99999 over
+            all compared outputs.
+"""
+import numpy as np
+import torch
+
+import block_scaled_precision_02_amd as q
+import oracle
+
+TOL_REL = 1e-2
+COS_MIN = 0.99999
+
+
+def bf16_to_f64(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bf16_ulp(ref_f64):
+    """1 ulp of a bf16 value: 2^(floor(log2|r|)-7) for normal r, 2^-133 for
+    zero and subnormals (bf16 keeps 7 fraction bits, emin = -126)."""
+    a = np.abs(ref_f64)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    ulp = np.exp2(e - 7)
+    return np.where(a >= 2.0 ** -126, ulp, 2.0 ** -133)
+
+
+def check_tolerance(got_bits, ref_bits, absdot, what=""):
+    g = bf16_to_f64(got_bits)
+    r = bf16_to_f64(ref_bits)
+    bound = TOL_REL * absdot + bf16_ulp(r)
+    nan_ref = np.isnan(r)
+    assert np.array_equal(np.isnan(g), nan_ref), f"{what}: NaN pattern differs"
+    err = np.abs(g - r)
+    err[nan_ref] = 0
+    bad = err > bound
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside the bound; first "
+                             + ", ".join(f"{tuple(i)} gpu={g[tuple(i)]} ref={r[tuple(i)]} "
+                                         f"bound={bound[tuple(i)]}" for i in idx))
+    gg, rr = g[~nan_ref], r[~nan_ref]
+    den = np.linalg.norm(gg) * np.linalg.norm(rr)
+    cos = float(gg @ rr / den) if den > 0 else 1.0
+    assert cos >= COS_MIN or (np.array_equal(gg, rr)), f"{what}: cosine {cos}"
+    return float((err / np.where(bound > 0, bound, 1)).max()), cos
+
+
+def dev(x, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.cuda()
+
+
+def bits(t):
+    """bf16 / uint16 tensor on the GPU -> numpy uint16."""
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def gpu_run(d, out=None, stream=None):
+    """Run the library on workload dict d (from inputs.make).  Returns the
+    output tensor (bf16)."""
+    bias = None if d["bias"] is None else dev(d["bias"].view(np.int16))
+    if d["kind"] == "i8":
+        return q.qgemm_i8_rowwise(dev(d["A"]), dev(d["B"]), dev(d["scale_a"]), dev(d["scale_b"]),
+                                  bias, out=out, stream=stream)
+    if d["kind"] == "f8":
+        return q.qgemm_f8_pertoken(dev(d["A"]), dev(d["B"]), dev(d["scale_a"]),
+                                   dev(d["scale_b"]), bias, out=out, stream=stream)
+    fmt = q.QGEMM_MX_E4M3 if d["fmt"] == "e4m3" else q.QGEMM_MX_E2M1
+    return q.qgemm_mx(fmt, dev(d["A"]), dev(d["B"]), dev(d["scale_a"]), dev(d["scale_b"]),
+                      d["b_rows_per_scale"], bias, out=out, stream=stream)
+
+
+def oracle_run(d, rows=None, cols=None):
+    """Oracle on workload d, optionally on a subset of rows of A / rows of B.
+    Returns (C bits, absdot or None, int32 acc or None)."""
+    A, sa = d["A"], d["scale_a"]
+    B, sb, bias = d["B"], d["scale_b"], d["bias"]
+    if rows is not None:
+        A, sa = A[rows], sa[rows]
+    if cols is not None:
+        if d["kind"] == "mx" and d["b_rows_per_scale"] == 32:
+            sb = np.repeat(sb, 32, axis=0)[:d["N"]][cols]
+            brows = 1
+        else:
+            sb = sb[cols]
+        B = B[cols]
+        bias = None if bias is None else bias[cols]
+    if d["kind"] == "i8":
+        C, acc = oracle.i8_rowwise(A, B, sa, sb, bias)
+        return C, None, acc
+    if d["kind"] == "f8":
+        C, _, absdot = oracle.f8_pertoken(A, B, sa, sb, bias)
+        return C, absdot, None
+    fmt = oracle.MX_E4M3 if d["fmt"] == "e4m3" else oracle.MX_E2M1
+    brows = d["b_rows_per_scale"] if cols is None else 1
+    C, _, absdot = oracle.mx(fmt, A, B, sa, sb, brows, d["K"], bias)
+    return C, absdot, None
+
+
+def compare(d, got_bits, ref_bits, absdot, what):
+    if d["kind"] == "i8":
+        if not np.array_equal(got_bits, ref_bits):
+            bad = np.argwhere(got_bits != ref_bits)
+            i = tuple(bad[0])
+            raise AssertionError(f"{what}: {len(bad)} of {got_bits.size} outputs differ; first at "
+                                 f"{i}: gpu={got_bits[i]:#06x} oracle={ref_bits[i]:#06x}")
+        return 0.0, 1.0
+    return check_tolerance(got_bits, ref_bits, absdot, what)

@@ -1,0 +1,238 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded
+inputs, through the C ABI (the ctypes binding).
+
+INT8 bit-exact (bf16 output and int32 accumulator); FP8 / MX within
+1e-2 * sum|a b| + 1 bf16 ulp per element with cosine >= 0.99999.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+from block_scaled_precision_02_amd import inputs  # noqa: E402
+import block_scaled_precision_02_amd as q  # noqa: E402
+
+from tests import parity  # noqa: E402
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _gpu_only():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    q.force_tile(-1)
+    yield
+    q.force_tile(-1)
+
+
+def _full_check(d, what, tile=None):
+    _say(f"[parity] {what} M={d['M']} N={d['N']} K={d['K']} tile={tile}")
+    if tile is not None:
+        q.force_tile(tile)
+    out = parity.gpu_run(d)
+    torch.cuda.synchronize()
+    got = parity.bits(out)
+    ref, absdot, _ = parity.oracle_run(d)
+    return parity.compare(d, got, ref, absdot, what)
+
+
+# ------------------------------------------------------------------ INT8
+
+@pytest.mark.parametrize("bias", [True, False])
+@pytest.mark.parametrize("tile", [0, 1])
+def test_i8_small_workload(bias, tile):
+    d = inputs.make("i8_small", bias=bias)
+    _full_check(d, f"i8_small bias={bias}", tile)
+
+
+def test_i8_accumulator_exact():
+    d = inputs.make("i8_small")
+    A, B = parity.dev(d["A"]), parity.dev(d["B"])
+    for tile in (0, 1):
+        q.force_tile(tile)
+        acc = q.qgemm_i8_acc_i32(A, B)
+        torch.cuda.synchronize()
+        _, _, ref = parity.oracle_run(d)
+        assert np.array_equal(acc.cpu().numpy(), ref), f"tile {tile}"
+    # extreme values: all -128 x -128 over a deep K
+    K = 8192
+    A = torch.full((3, K), -128, dtype=torch.int8, device="cuda")
+    acc = q.qgemm_i8_acc_i32(A, A)
+    assert (acc.cpu().numpy() == K * 16384).all()
+
+
+def test_i8_signed_zero_and_subnormals():
+    """No-bias epilogue keeps -0 (comfy-kitchen PR #174, Summary) and fp32
+    subnormals; the same rows with a +0 bias give +0."""
+    d = inputs.make("i8_small", bias=False)
+    A, sa, sb = d["A"].copy(), d["scale_a"].copy(), d["scale_b"].copy()
+    A[0:8] = 0
+    sa[0:8] = -np.abs(sa[0:8])
+    # rows 8..15: acc = -1 exactly in column 0, scales push it below fp32's range
+    A[8:16] = 0
+    A[8:16, 0] = -1
+    B = d["B"].copy()
+    B[0] = 0
+    B[0, 0] = 1
+    sa[8:16] = np.float32(2.0 ** -100)
+    sb[0] = np.float32(2.0 ** -50)
+    # row 16: acc = +1 in column 1 with 2^-100 * 2^-30 = 2^-130 (fp32 subnormal)
+    A[16] = 0
+    A[16, 1] = 1
+    B[1] = 0
+    B[1, 1] = 1
+    sa[16] = np.float32(2.0 ** -100)
+    sb[1] = np.float32(2.0 ** -30)
+    d2 = dict(d, A=A, B=B, scale_a=sa, scale_b=sb)
+    out = parity.bits(parity.gpu_run(d2))
+    ref, _, _ = parity.oracle_run(d2)
+    assert np.array_equal(out, ref)
+    assert (out[0:8] == 0x8000).all()
+    assert (out[8:16, 0] == 0x8000).all()
+    assert out[16, 1] == 0x0008
+    d3 = dict(d2, bias=np.zeros(d["N"], np.uint16))
+    out3 = parity.bits(parity.gpu_run(d3))
+    assert (out3[0:8] == 0).all() and (out3[8:16, 0] == 0).all()
+
+
+EDGE_SHAPES = [(1, 1, 32), (17, 31, 64), (48, 33, 96), (100, 2112, 256), (255, 256, 512),
+               (256, 255, 640), (257, 300, 1280), (1000, 129, 2048)]
+
+
+@pytest.mark.parametrize("M,N,K", EDGE_SHAPES)
+def test_i8_edges_canaries(M, N, K):
+    """Ragged shapes, NaN-filled output with canary columns (ldc > N) and a
+    canary row block: nothing outside [0,M) x [0,N) may change."""
+    d = inputs.make("i8_small", M=M, N=N, K=K)
+    ldc = N + (-N) % 8 + 8
+    buf = torch.full((M + 3, ldc), float("nan"), dtype=torch.bfloat16, device="cuda")
+    before = parity.bits(buf)
+    out = buf[:M, :N]
+    parity.gpu_run(d, out=out)
+    after = parity.bits(buf)
+    ref, _, _ = parity.oracle_run(d)
+    parity.compare(d, after[:M, :N], ref, None, f"i8 {M}x{N}x{K}")
+    assert np.array_equal(after[:M, N:], before[:M, N:]), "wrote past N"
+    assert np.array_equal(after[M:], before[M:]), "wrote past M"
+
+
+def test_i8_empty_is_noop():
+    A = torch.zeros((0, 64), dtype=torch.int8, device="cuda")
+    B = torch.zeros((5, 64), dtype=torch.int8, device="cuda")
+    out = q.qgemm_i8_rowwise(A, B, torch.zeros(0, device="cuda"), torch.ones(5, device="cuda"))
+    assert out.shape == (0, 5)
+
+
+# ------------------------------------------------------------------ FP8
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 512), (17, 33, 96), (300, 2112, 1024)])
+@pytest.mark.parametrize("bias", [False, True])
+def test_f8_small(M, N, K, bias):
+    d = inputs.make("f8_ptpc", M=M, N=N, K=K, bias=bias)
+    _full_check(d, f"f8 {M}x{N}x{K} bias={bias}")
+
+
+# ------------------------------------------------------------------ MX
+
+@pytest.mark.parametrize("name", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 512), (33, 70, 96), (300, 520, 1024),
+                                   (129, 64, 160)])
+@pytest.mark.parametrize("bias", [False, True])
+def test_mx_small(name, M, N, K, bias):
+    d = inputs.make(name, M=M, N=N, K=K, bias=bias)
+    _full_check(d, f"{name} {M}x{N}x{K} bias={bias}")
+
+
+@pytest.mark.parametrize("name", ["mxfp8", "mxfp4"])
+def test_mx_other_b_layout(name):
+    """mxfp8 with 1x32 B scales and mxfp4 with 32x32 B scales."""
+    rng = np.random.default_rng(77)
+    d = inputs.make(name, M=130, N=96, K=512)
+    fmt = d["fmt"]
+    brows = 1 if d["b_rows_per_scale"] == 32 else 32
+    xb = rng.standard_normal((96, 512)).astype(np.float32)
+    cb, sb = inputs.mx_quantise(xb, fmt, brows)
+    if fmt == "e2m1":
+        cb = inputs.pack_e2m1(cb)
+    d2 = dict(d, B=cb, scale_b=sb, b_rows_per_scale=brows)
+    _full_check(d2, f"{name} B-scale rows {brows}")
+
+
+@pytest.mark.parametrize("name", ["mxfp8", "mxfp4"])
+def test_mx_random_scales_repeated(name):
+    """Random per-block scales (a stale or misrouted scale shows at once),
+    output NaN-filled before each of 12 launches; every launch must match the
+    oracle and equal the first bit for bit."""
+    rng = np.random.default_rng(5)
+    d = inputs.make(name, M=512, N=512, K=1280)
+    d = dict(d, scale_a=rng.integers(118, 136, d["scale_a"].shape, dtype=np.uint8),
+             scale_b=rng.integers(118, 136, d["scale_b"].shape, dtype=np.uint8))
+    ref, absdot, _ = parity.oracle_run(d)
+    first = None
+    out = torch.empty((512, 512), dtype=torch.bfloat16, device="cuda")
+    for it in range(12):
+        out.fill_(float("nan"))
+        parity.gpu_run(d, out=out)
+        got = parity.bits(out)
+        if first is None:
+            parity.compare(d, got, ref, absdot, f"{name} launch 0")
+            first = got
+        else:
+            assert np.array_equal(got, first), f"launch {it} differs"
+
+
+# ------------------------------------------------------------------ variants
+
+@pytest.mark.parametrize("name", ["i8_small", "f8_ptpc", "mxfp8", "mxfp4"])
+def test_tile_variants_identical(name):
+    """Each output's accumulation chain is the same sequence of MFMAs in every
+    tile variant, so the variants agree bit for bit."""
+    d = inputs.make(name, M=300, N=280, K=512)
+    outs = []
+    for tile in (0, 1):
+        q.force_tile(tile)
+        outs.append(parity.bits(parity.gpu_run(d)))
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_non_default_stream():
+    d = inputs.make("mxfp4", M=256, N=512, K=512)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = parity.gpu_run(d, stream=s)
+    s.synchronize()
+    ref, absdot, _ = parity.oracle_run(d)
+    parity.compare(d, parity.bits(out), ref, absdot, "side stream")
+
+
+# ------------------------------------------------------------------ full sizes
+
+def _sample_rows(M, n, rng):
+    tail = np.arange(max(0, M - 8), M)
+    head = np.arange(0, min(8, M))
+    mid = rng.choice(M, size=max(0, n - len(head) - len(tail)), replace=False)
+    return np.unique(np.concatenate([head, mid, tail]))
+
+
+@pytest.mark.parametrize("name", ["f8_ptpc", "mxfp8", "mxfp4", "i8_qkv"])
+def test_full_workload_sampled(name):
+    """The workload at its full size, launched as the benchmark launches it;
+    the oracle checks a sample of whole output rows (first, last -- inside
+    the partial tile when M is not a tile multiple -- and random ones)."""
+    d = inputs.make(name)
+    _say(f"[parity] full {name} M={d['M']} N={d['N']} K={d['K']}")
+    out = parity.gpu_run(d)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    rows = _sample_rows(d["M"], 24, rng)
+    got = parity.bits(out[torch.from_numpy(rows).cuda()])
+    ref, absdot, _ = parity.oracle_run(d, rows=rows)
+    worst, cos = parity.compare(d, got, ref, absdot, f"full {name}")
+    _say(f"[parity] full {name}: worst err/bound {worst:.3g} cos {cos:.8f}")
