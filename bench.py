@@ -126,6 +126,10 @@ def main():
     ap.add_argument("--rot", type=int, default=None, help="rotating input sets")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tile", type=int, default=-1, help="force a tile id (-1: the table's choice)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead: time a plain device copy of this many bytes (the "
+                         "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this GEMM library has no multi-GPU path "
@@ -137,6 +141,14 @@ def main():
     import block_scaled_precision_02_amd as q
 
     torch.cuda.set_device(0)
+    if args.copy_bytes:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "launches": args.steps}), flush=True)
+        return
     name = args.workload
     R = args.rot or ROT[name]
     log(f"[bench] generating {name} x{R}")
@@ -149,6 +161,9 @@ def main():
     stream = torch.cuda.current_stream()
     run = Launcher(d0, sets, out, stream.cuda_stream)
     tile = q.select_tile({"i8": 0, "f8": 1, "e4m3": 2, "e2m1": 3}[dtype_of(d0)], M, N, K)
+    if args.tile >= 0:
+        q.force_tile(args.tile)
+        tile = args.tile
 
     log(f"[bench] warmup {args.warmup}")
     for i in range(args.warmup):
@@ -186,7 +201,7 @@ def main():
         "dtype": {"i8": "int8", "f8": "e4m3", "e4m3": "mxfp8-e4m3", "e2m1": "mxfp4-e2m1"}[dtype_of(d0)],
         "data": "synthetic",
         "config": {"workload": f"{name} M={M} N={N} K={K}" + (" bias" if d0["bias"] is not None else ""),
-                   "tile": q.tile_rows(tile), "rotating_sets": R, "pct_of_peak": round(100 * value / peak, 2)},
+                   "tile_id": tile, "rotating_sets": R, "pct_of_peak": round(100 * value / peak, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": unit_of(d0), "frac": round(achieved / peak, 4), "traffic": None,
                      "kernel_ms": round(kernel_ms, 6)},

@@ -102,10 +102,14 @@ __device__ __forceinline__ void lds_barrier()
 }
 
 // Position of 16-byte chunk c of staged row r inside an LDS tile of rows of
-// 128 bytes.  Rows r..r+7 place the same logical chunk in 8 different slots.
+// 128 bytes.  A fragment read has 16 consecutive lanes on 16 consecutive rows
+// at the same logical chunk; the slot c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1),
+// puts rows r..r+7 in 8 different 16-byte slots of their 128-byte rows and,
+// over 16 rows, the even rows and the odd rows each in 8 different slots, so
+// neither 8 lanes over 128 bytes of banks nor 16 lanes over 256 bytes collide.
 __device__ __forceinline__ int lds_off(int r, int c)
 {
-    return r * KSTEP_BYTES + ((c ^ (r & 7)) << 4);
+    return r * KSTEP_BYTES + ((c ^ (r & 7) ^ ((r >> 3) & 1)) << 4);
 }
 
 // Workgroup -> output tile.  Workgroups are handed to the 8 XCDs round-robin;
@@ -225,13 +229,16 @@ __device__ __forceinline__ unsigned pack_bf16(float x, float y)
     return __builtin_bit_cast(unsigned, v);
 }
 
-template <int PATH, int TM, int TN, bool BIAS, int BROWS, bool SVEC, int OUT>
-__global__ void __launch_bounds__(256, 1) qgemm_kernel(const Params p)
+template <int PATH, int WM, int WN, int TM, int TN, bool BIAS, int BROWS, bool SVEC, int OUT>
+__global__ void __launch_bounds__(64 * WM * WN, 1) qgemm_kernel(const Params p)
 {
-    constexpr int BM = 2 * TM * 32, BN = 2 * TN * 32;
+    constexpr int NT = 64 * WM * WN;        // threads: WM x WN waves
+    constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+    constexpr int RSTEP = NT / CHUNKS;      // rows staged per pass of the workgroup
     constexpr int NSUB = PathTraits<PATH>::NSUB;
-    constexpr int CA = BM * CHUNKS / 256;   // A chunks staged per thread per step
-    constexpr int CB = BN * CHUNKS / 256;
+    constexpr int CA = BM * CHUNKS / NT;    // A chunks staged per thread per step
+    constexpr int CB = BN * CHUNKS / NT;
+    static_assert(CA * NT == BM * CHUNKS && CB * NT == BN * CHUNKS, "tile / thread mismatch");
     constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4);
     using Frag = typename PathTraits<PATH>::Frag;
     using Acc = typename AccT<PATH>::T;
@@ -240,7 +247,7 @@ __global__ void __launch_bounds__(256, 1) qgemm_kernel(const Params p)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     const int h = lane >> 5, r32 = lane & 31;
 
     int tm, tn;
@@ -255,14 +262,19 @@ __global__ void __launch_bounds__(256, 1) qgemm_kernel(const Params p)
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + (int64_t)n0 * p.ldb,
                                                 (uint32_t)((rows_b - 1) * p.ldb + p.kbytes));
 
-    // Staging map: thread tid copies chunk tid%8 of rows tid/8 + 32*i.
+    // Staging map: thread tid copies chunk tid%8 of rows tid/8 + RSTEP*i.
+    // RS register sets: step s is fetched into set s%RS, parked in LDS buffer
+    // s&1 during step s-1, and its set is then refilled with step s+RS.  Two
+    // sets (fetch ~1.75 steps ahead) where the fragments are 16 bytes; one
+    // set (~0.75 steps) for e4m3, whose 32-byte fragments leave no room.
+    constexpr int RS = (PATH == PATH_F8 || PATH == PATH_MX8) ? 1 : 2;
     const int st_row = tid >> 3, st_c = tid & 7;
-    u32x4 ga[CA], gb[CB];
+    u32x4 ga[RS][CA], gb[RS][CB];
 
     // MX scale ranges and per-lane row offsets.
     __amdgpu_buffer_rsrc_t rsa, rsb;
     int sa_off[TM], sb_off[TN];
-    unsigned sa_next[TM], sb_next[TN], sa_cur[TM], sb_cur[TN];
+    unsigned sa_ld[RS][TM], sb_ld[RS][TN];
     if constexpr (MX) {
         rsa = make_rsrc(p.mx_sa + (int64_t)m0 * p.kblocks, (uint32_t)(rows_a * p.kblocks));
         if constexpr (BROWS == 1) {
@@ -279,33 +291,35 @@ __global__ void __launch_bounds__(256, 1) qgemm_kernel(const Params p)
             sb_off[j] = (BROWS == 1 ? (wn * TN * 32 + j * 32 + r32) : (wn * TN + j)) * p.kblocks;
     }
 
-    auto load_step = [&](int kt) {
+    auto load_step = [&](int kt, auto setc) {
+        constexpr int SET = decltype(setc)::value;
         const int kb = kt * KSTEP_BYTES + st_c * 16;
         const bool kin = kb < p.kbytes;
 #pragma unroll
         for (int i = 0; i < CA; ++i)
-            ga[i] = ld16(ra, kin ? (unsigned)((st_row + 32 * i) * p.lda + kb) : OOB);
+            ga[SET][i] = ld16(ra, kin ? (unsigned)((st_row + RSTEP * i) * p.lda + kb) : OOB);
 #pragma unroll
         for (int i = 0; i < CB; ++i)
-            gb[i] = ld16(rb, kin ? (unsigned)((st_row + 32 * i) * p.ldb + kb) : OOB);
+            gb[SET][i] = ld16(rb, kin ? (unsigned)((st_row + RSTEP * i) * p.ldb + kb) : OOB);
         if constexpr (MX) {
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                sa_next[i] = load_scale_word<PATH, SVEC>(rsa, sa_off[i], kt, h, p.kblocks);
+                sa_ld[SET][i] = load_scale_word<PATH, SVEC>(rsa, sa_off[i], kt, h, p.kblocks);
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                sb_next[j] = load_scale_word<PATH, SVEC>(rsb, sb_off[j], kt, h, p.kblocks);
+                sb_ld[SET][j] = load_scale_word<PATH, SVEC>(rsb, sb_off[j], kt, h, p.kblocks);
         }
     };
-    auto store_step = [&](int buf) {
+    auto store_step = [&](int buf, auto setc) {
+        constexpr int SET = decltype(setc)::value;
         uint8_t *ta = &lds[buf][0];
         uint8_t *tb = &lds[buf][BM * KSTEP_BYTES];
 #pragma unroll
         for (int i = 0; i < CA; ++i)
-            *(u32x4 *)(ta + lds_off(st_row + 32 * i, st_c)) = ga[i];
+            *(u32x4 *)(ta + lds_off(st_row + RSTEP * i, st_c)) = ga[SET][i];
 #pragma unroll
         for (int i = 0; i < CB; ++i)
-            *(u32x4 *)(tb + lds_off(st_row + 32 * i, st_c)) = gb[i];
+            *(u32x4 *)(tb + lds_off(st_row + RSTEP * i, st_c)) = gb[SET][i];
     };
 
     Acc acc[TM][TN];
@@ -315,65 +329,151 @@ __global__ void __launch_bounds__(256, 1) qgemm_kernel(const Params p)
         for (int j = 0; j < TN; ++j)
             acc[i][j] = Acc{};
 
-    // Prologue: step 0 into LDS buffer 0, step 1 into registers.
-    load_step(0);
-    store_step(0);
-    if constexpr (MX) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) sa_cur[i] = sa_next[i];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) sb_cur[j] = sb_next[j];
-    }
-    if (p.ksteps > 1)
-        load_step(1);
-    lds_barrier();
-
     const int arow = wm * TM * 32 + r32;
     const int brow = wn * TN * 32 + r32;
 
-    for (int kt = 0; kt < p.ksteps; ++kt) {
+    // Fragments of two consecutive K sub-steps (S even -> set 0, odd -> 1).
+    Frag fa[2][TM], fb[2][TN];
+    // MX scale words of the step being multiplied and of the step parked next.
+    unsigned sa_use[TM], sb_use[TN], sa_nxt[TM], sb_nxt[TN];
+
+    auto read_frags = [&](auto sc, int buf, auto setc) {
+        constexpr int S = decltype(sc)::value;
+        constexpr int SET = decltype(setc)::value;
+        const uint8_t *ta = &lds[buf][0];
+        const uint8_t *tb = &lds[buf][BM * KSTEP_BYTES];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            fa[SET][i] = load_frag<PATH, S>(ta, arow + 32 * i, h);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            fb[SET][j] = load_frag<PATH, S>(tb, brow + 32 * j, h);
+    };
+    // MFMAs of sub-step S over tile pairs [Q0, Q1) of the TM*TN grid, in
+    // serpentine order (consecutive MFMAs share a fragment).
+    auto mfmas = [&](auto sc, auto q0c, auto q1c) {
+        constexpr int S = decltype(sc)::value;
+        constexpr int SET = S & 1;
+        static_for<decltype(q0c)::value, decltype(q1c)::value>([&](auto qc) {
+            constexpr int Q = decltype(qc)::value;
+            constexpr int i = Q / TN;
+            constexpr int j = (i & 1) ? (TN - 1 - Q % TN) : (Q % TN);
+            mfma<PATH, S>(acc[i][j], fb[SET][j], fa[SET][i], MX ? sb_use[j] : 0u, MX ? sa_use[i] : 0u);
+        });
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    // Prologue: steps 0..RS-1 into the register sets, step 0 into LDS buffer
+    // 0, step RS into set 0, then the sub-step 0 fragments of step 0.
+    load_step(0, I0());
+    if constexpr (RS == 2)
+        load_step(1, I1());
+    store_step(0, I0());
+    if constexpr (MX) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) sa_use[i] = sa_ld[0][i];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) sb_use[j] = sb_ld[0][j];
+    }
+    load_step(RS, I0());
+    lds_barrier();
+    read_frags(I0(), 0, I0());
+
+    // One K step.  Region A (before the barrier): park step kt+1 (register
+    // set (kt+1)&1) in the idle LDS buffer -- it was last read before the
+    // previous barrier -- refill that set with step kt+3, and read the
+    // fragments of sub-steps 1..NSUB-1 while the MFMAs of the sub-step before
+    // run.  Half-way through the last sub-step every wave has finished
+    // reading buffer cur and its LDS writes have landed: barrier.  Region B:
+    // the sub-step 0 fragments of step kt+1 come from the other buffer under
+    // the last MFMAs.
+    constexpr int NQ = TM * TN;
+    constexpr int RPF = (PATH == PATH_F8 || PATH == PATH_MX8) ? 2 : 1;   // ds_reads per fragment
+    constexpr int NDSR = (TM + TN) * RPF;                               // per sub-step
+    constexpr int NSTG = CA + CB;                                       // staged chunks per thread
+    constexpr int NSCL = MX ? (TM + TN) * (SVEC ? 1 : (PATH == PATH_MX4 ? 4 : 2)) : 0;
+    auto kstep = [&](int kt, auto setc0, auto storec, auto loadc, auto nextc) {
+        constexpr int SET = decltype(setc0)::value % RS;   // register set of step kt+1
+        using setc = std::integral_constant<int, SET>;
+        constexpr bool STORE = decltype(storec)::value;
+        constexpr bool LOAD = decltype(loadc)::value;
+        constexpr bool NEXT = decltype(nextc)::value;
         const int cur = kt & 1;
-        unsigned sa_step[TM], sb_step[TN];
-        if constexpr (MX) {
-#pragma unroll
-            for (int i = 0; i < TM; ++i) sa_step[i] = sa_cur[i];
-#pragma unroll
-            for (int j = 0; j < TN; ++j) sb_step[j] = sb_cur[j];
-        }
-        if (kt + 1 < p.ksteps) {
-            // Step kt+1 has had a whole step to arrive: park it in the idle
-            // buffer (last read before the previous barrier), then start
-            // fetching step kt+2.
-            store_step(cur ^ 1);
-            if constexpr (MX) {
-#pragma unroll
-                for (int i = 0; i < TM; ++i) sa_cur[i] = sa_next[i];
-#pragma unroll
-                for (int j = 0; j < TN; ++j) sb_cur[j] = sb_next[j];
-            }
-            if (kt + 2 < p.ksteps)
-                load_step(kt + 2);
-        }
-        const uint8_t *ta = &lds[cur][0];
-        const uint8_t *tb = &lds[cur][BM * KSTEP_BYTES];
         static_for<0, NSUB>([&](auto sc) {
             constexpr int S = decltype(sc)::value;
-            Frag fa[TM], fb[TN];
+            if constexpr (S == 0 && STORE) {
+                store_step(cur ^ 1, setc());
+                if constexpr (MX) {
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-                fa[i] = load_frag<PATH, S>(ta, arow + 32 * i, h);
+                    for (int i = 0; i < TM; ++i) sa_nxt[i] = sa_ld[SET][i];
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                fb[j] = load_frag<PATH, S>(tb, brow + 32 * j, h);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int jj = 0; jj < TN; ++jj) {
-                    const int j = (i & 1) ? (TN - 1 - jj) : jj;   // serpentine: reuse fb[j]
-                    mfma<PATH, S>(acc[i][j], fb[j], fa[i], MX ? sb_step[j] : 0u, MX ? sa_step[i] : 0u);
+                    for (int j = 0; j < TN; ++j) sb_nxt[j] = sb_ld[SET][j];
                 }
+            }
+            if constexpr (S == 1 && LOAD)
+                load_step(kt + 1 + RS, setc());
+            if constexpr (S + 1 < NSUB)
+                read_frags(std::integral_constant<int, S + 1>(), cur, std::integral_constant<int, (S + 1) & 1>());
+            if constexpr (S + 1 < NSUB) {
+                mfmas(sc, I0(), std::integral_constant<int, NQ>());
+            } else {
+                mfmas(sc, I0(), std::integral_constant<int, NQ / 2>());
+            }
         });
-        lds_barrier();
+        // Issue order for region A: each MFMA followed by its share of the
+        // sub-step's memory operations.
+        static_for<0, NSUB>([&](auto sc) {
+            constexpr int S = decltype(sc)::value;
+            constexpr int NM = (S + 1 < NSUB) ? NQ : NQ / 2;
+            constexpr int W = (S == 0 && STORE) ? NSTG : 0;
+            constexpr int V = (S == 1 && LOAD) ? NSTG + NSCL : 0;
+            constexpr int R = (S + 1 < NSUB) ? NDSR : 0;
+            static_for<0, NM>([&](auto jc) {
+                constexpr int J = decltype(jc)::value;
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                constexpr int w = W * (J + 1) / NM - W * J / NM;
+                constexpr int v = V * (J + 1) / NM - V * J / NM;
+                constexpr int r = R * (J + 1) / NM - R * J / NM;
+                if constexpr (w > 0) __builtin_amdgcn_sched_group_barrier(0x200, w, 0);
+                if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);
+                if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+            });
+        });
+        if constexpr (NEXT) {
+            __builtin_amdgcn_sched_barrier(0);
+            lds_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(I0(), cur ^ 1, I0());
+        }
+        mfmas(std::integral_constant<int, NSUB - 1>(), std::integral_constant<int, NQ / 2>(),
+              std::integral_constant<int, NQ>());
+        if constexpr (NEXT) {
+            static_for<0, NQ / 2>([&](auto jc) {
+                constexpr int J = decltype(jc)::value;
+                constexpr int NM = NQ / 2;
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                constexpr int r = NDSR * (J + 1) / NM - NDSR * J / NM;
+                if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+            });
+            if constexpr (MX) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i) sa_use[i] = sa_nxt[i];
+#pragma unroll
+                for (int j = 0; j < TN; ++j) sb_use[j] = sb_nxt[j];
+            }
+        }
+    };
+
+    // Steps alternate register sets, so the loop handles two at a time.  The
+    // step count is rounded up to even: fetches past K read zeros (the K
+    // predicate pushes them out of range, scale words included), so a step
+    // past the end adds exact zeros to the accumulators, and the loads and
+    // parks of steps beyond it touch no memory that is read back.
+    const int ks2 = (p.ksteps + 1) & ~1;
+    for (int kt = 0; kt < ks2; kt += 2) {
+        kstep(kt, I1(), std::true_type(), std::true_type(), std::true_type());
+        kstep(kt + 1, I0(), std::true_type(), std::true_type(), std::true_type());
     }
 
     // ---------------------------------------------------------- epilogue
@@ -395,6 +495,19 @@ __global__ void __launch_bounds__(256, 1) qgemm_kernel(const Params p)
         rsb_e = make_rsrc(p.scale_b + n0, (uint32_t)(rows_b * 4));
     if constexpr (BIAS)
         rbias = make_rsrc(p.bias + n0, (uint32_t)(rows_b * 2));
+    // Full bf16 tiles leave through LDS: each wave parks its (TM*32) x (TN*32)
+    // block of bf16 results in its own stash (16-byte chunks XOR-swizzled by
+    // row), then writes whole 16-byte row pieces, consecutive lanes covering
+    // consecutive bytes of a row, so every store instruction fills complete
+    // cache lines instead of touching 32 rows.
+    constexpr int SROWB = TN * 32 * 2;              // stash row bytes (bf16)
+    constexpr int SCHK = SROWB / 16;                // 16-byte chunks per row
+    uint8_t *stash = &lds[0][0] + wave * (TM * 32) * SROWB;
+    static_assert(WM * WN * TM * 32 * SROWB <= 2 * (BM + BN) * KSTEP_BYTES, "stash does not fit");
+    if constexpr (OUT == OUT_BF16) {
+        if (full)
+            lds_barrier();   // every wave is done with the operand buffers
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int mloc = arow + 32 * i;
@@ -473,7 +586,10 @@ __global__ void __launch_bounds__(256, 1) qgemm_kernel(const Params p)
                     }
                     const u32x2 v = {pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3])};
                     if (full) {
-                        __builtin_amdgcn_raw_buffer_store_b64(v, rc, off, 0, 0);
+                        // park in this wave's LDS stash (written out below)
+                        const int srow = 32 * i + r32;
+                        const int chunk = 4 * j + g;
+                        *(u32x2 *)(stash + srow * SROWB + ((chunk ^ (srow & (SCHK - 1))) << 4) + 8 * h) = v;
                     } else {
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
@@ -482,6 +598,21 @@ __global__ void __launch_bounds__(256, 1) qgemm_kernel(const Params p)
                                 (nloc + r < rows_b) ? off + 2 * r : OOB, 0, 0);
                     }
                 }
+            }
+        }
+    }
+    if constexpr (OUT == OUT_BF16) {
+        if (full) {
+            constexpr int LPR = SCHK;                   // lanes per stash row
+            constexpr int RPI = 64 / LPR;               // rows per store instruction
+            const int c = lane % LPR;
+            const unsigned gbase = (unsigned)((int64_t)(wm * TM * 32) * p.ldc * 2) + col0 +
+                                   (unsigned)((wn * TN * 32) * 2 + c * 16);
+#pragma unroll
+            for (int it = 0; it < TM * 32 / RPI; ++it) {
+                const int srow = it * RPI + lane / LPR;
+                const u32x4 v = *(const u32x4 *)(stash + srow * SROWB + ((c ^ (srow & (SCHK - 1))) << 4));
+                __builtin_amdgcn_raw_buffer_store_b128(v, rc, gbase + (unsigned)(srow * p.ldc * 2), 0, 0);
             }
         }
     }

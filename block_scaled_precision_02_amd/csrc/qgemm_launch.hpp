@@ -5,16 +5,19 @@
 
 namespace qgemm {
 
-// Tile ids of the host table: 0 -> 256x256 (2x2 waves of 128x128),
-// 1 -> 128x128 (2x2 waves of 64x64).
-constexpr int NUM_TILES = 2;
-__host__ __device__ constexpr int tile_edge(int tile) { return tile == 0 ? 256 : 128; }
+// Tile ids of the host table:
+//   0 -> 256x256, 2x2 waves of 128x128 (1 wave per SIMD, 256 accumulators)
+//   1 -> 128x128, 2x2 waves of 64x64
+//   2 -> 256x256, 2x4 waves of 128x64 (2 waves per SIMD, 128 accumulators)
+constexpr int NUM_TILES = 3;
+__host__ __device__ constexpr int tile_edge(int tile) { return tile == 1 ? 128 : 256; }
+__host__ __device__ constexpr int tile_threads(int tile) { return tile == 2 ? 512 : 256; }
 
-template <int PATH, int TM, int TN, bool BIAS, int BROWS, bool SVEC, int OUT>
+template <int PATH, int WM, int WN, int TM, int TN, bool BIAS, int BROWS, bool SVEC, int OUT>
 hipError_t launch_variant(const Params &p, hipStream_t s)
 {
-    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(256);
-    hipLaunchKernelGGL((qgemm_kernel<PATH, TM, TN, BIAS, BROWS, SVEC, OUT>), grid, block, 0, s, p);
+    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(64 * WM * WN);
+    hipLaunchKernelGGL((qgemm_kernel<PATH, WM, WN, TM, TN, BIAS, BROWS, SVEC, OUT>), grid, block, 0, s, p);
     return hipGetLastError();
 }
 
@@ -22,8 +25,9 @@ template <int PATH, bool BIAS, int BROWS, bool SVEC, int OUT>
 hipError_t launch_tile(int tile, const Params &p, hipStream_t s)
 {
     switch (tile) {
-    case 0: return launch_variant<PATH, 4, 4, BIAS, BROWS, SVEC, OUT>(p, s);
-    case 1: return launch_variant<PATH, 2, 2, BIAS, BROWS, SVEC, OUT>(p, s);
+    case 0: return launch_variant<PATH, 2, 2, 4, 4, BIAS, BROWS, SVEC, OUT>(p, s);
+    case 1: return launch_variant<PATH, 2, 2, 2, 2, BIAS, BROWS, SVEC, OUT>(p, s);
+    case 2: return launch_variant<PATH, 2, 4, 4, 2, BIAS, BROWS, SVEC, OUT>(p, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -131,7 +131,8 @@ def test_tile_table():
     assert L.qgemm_select_tile(3, 8192, 8192, 8192) == 0
     assert L.qgemm_select_tile(0, 30000, 21504, 5376) == 0
     assert L.qgemm_select_tile(7, 64, 64, 64) == -1
-    assert L.qgemm_tile_rows(0) == 256 and L.qgemm_tile_rows(1) == 128 and L.qgemm_tile_rows(5) == 0
+    assert L.qgemm_tile_rows(0) == 256 and L.qgemm_tile_rows(1) == 128 and L.qgemm_tile_rows(2) == 256
+    assert L.qgemm_tile_rows(5) == 0
     assert L.qgemm_force_tile(9) == -2
     assert L.qgemm_force_tile(1) == -1
     assert L.qgemm_force_tile(-1) == 1
