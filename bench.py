@@ -96,6 +96,22 @@ def upload(d):
     return t
 
 
+def traffic_bytes(name):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary, already scaled by the copy-kernel factors; None when the kernel
+    source has changed since those counters were taken."""
+    import hashlib
+    try:
+        t = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+        src = open(os.path.join(ROOT, t["kernel_source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != t.get("kernel_sha256"):
+        return None
+    w = t.get("workloads", {}).get(name)
+    return None if w is None else w["fetch_bytes"] + w["write_bytes"]
+
+
 def cpu_baseline(d, target_s):
     """The oracle, as it is, on whole rows of the same workload: a few rows
     first to calibrate, then enough rows for about target_s seconds."""
@@ -203,7 +219,7 @@ def main():
         "config": {"workload": f"{name} M={M} N={N} K={K}" + (" bias" if d0["bias"] is not None else ""),
                    "tile_id": tile, "rotating_sets": R, "pct_of_peak": round(100 * value / peak, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
-                     "unit": unit_of(d0), "frac": round(achieved / peak, 4), "traffic": None,
+                     "unit": unit_of(d0), "frac": round(achieved / peak, 4), "traffic": traffic_bytes(name),
                      "kernel_ms": round(kernel_ms, 6)},
         "cpu_baseline": None,
     }

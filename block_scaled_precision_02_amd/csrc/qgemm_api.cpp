@@ -84,27 +84,42 @@ qgemm_status check_device()
 }
 
 // ------------------------------------------------------------ tile table
-// Rows are checked in order; the first whose bounds hold picks the tile.
-// A miss falls through to the default rule.  256x256 is the throughput tile
-// (one workgroup per CU, 256 accumulators per lane in AGPRs); 128x128 keeps
-// more workgroups in flight when the 256x256 grid would leave CUs idle.
-struct TileRow {
-    int path;          // -1: any path
-    int64_t max_tiles; // the 256x256 grid has at most this many tiles
+// A launch runs in rounds of (CUs x workgroups per CU) tiles; a round lasts
+// about as long as one workgroup's tile at its measured MFMA efficiency when
+// its co-resident workgroups share the CU.  The table picks the candidate with
+// the smallest rounds x round-time; ties keep the earlier (larger) tile.  The
+// efficiencies are relative figures from the benchmark workloads: the 192x192
+// tile moves ~1.3x the LDS bytes per MFMA of the 256x256 tile, the 128x128
+// tile ~2x.
+struct TileCand {
     int tile;
+    int per_cu;      // workgroups resident per CU (LDS and registers)
+    double eff;      // MFMA efficiency relative to the 256x256 tile
 };
-const TileRow TILE_TABLE[] = {
-    {-1, 128, 1},   // under half the 256 CUs busy with the big tile
+const TileCand TILE_TABLE[] = {
+    {0, 1, 1.00},   // 256x256, 4 waves, 128 KB LDS
+    {3, 1, 0.85},   // 192x192, 4 waves, 96 KB LDS
+    {1, 2, 0.55},   // 128x128, 4 waves, 64 KB LDS: two per CU
 };
-constexpr int DEFAULT_TILE = 0;
+constexpr int NUM_CU = 256;
 
 int select_tile_impl(int path, int64_t M, int64_t N)
 {
-    const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
-    for (const TileRow &r : TILE_TABLE)
-        if ((r.path < 0 || r.path == path) && big <= r.max_tiles)
-            return r.tile;
-    return DEFAULT_TILE;
+    (void)path;
+    int best = TILE_TABLE[0].tile;
+    double best_cost = -1.0;
+    for (const TileCand &c : TILE_TABLE) {
+        const int64_t e = tile_edge(c.tile);
+        const int64_t tiles = ((M + e - 1) / e) * ((N + e - 1) / e);
+        const int64_t slots = (int64_t)NUM_CU * c.per_cu;
+        const int64_t rounds = (tiles + slots - 1) / slots;
+        const double cost = (double)rounds * (double)(e * e) * c.per_cu / c.eff;
+        if (best_cost < 0 || cost < best_cost * 0.999) {
+            best = c.tile;
+            best_cost = cost;
+        }
+    }
+    return best;
 }
 
 // ------------------------------------------------------------ common checks

@@ -502,9 +502,10 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) qgemm_kernel(const Params p)
     // cache lines instead of touching 32 rows.
     constexpr int SROWB = TN * 32 * 2;              // stash row bytes (bf16)
     constexpr int SCHK = SROWB / 16;                // 16-byte chunks per row
+    constexpr bool STASH = OUT == OUT_BF16 && (SCHK & (SCHK - 1)) == 0 && 64 % SCHK == 0 &&
+                           WM * WN * TM * 32 * SROWB <= 2 * (BM + BN) * KSTEP_BYTES;
     uint8_t *stash = &lds[0][0] + wave * (TM * 32) * SROWB;
-    static_assert(WM * WN * TM * 32 * SROWB <= 2 * (BM + BN) * KSTEP_BYTES, "stash does not fit");
-    if constexpr (OUT == OUT_BF16) {
+    if constexpr (STASH) {
         if (full)
             lds_barrier();   // every wave is done with the operand buffers
     }
@@ -585,7 +586,9 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) qgemm_kernel(const Params p)
                         f[r] = x;
                     }
                     const u32x2 v = {pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3])};
-                    if (full) {
+                    if (full && !STASH) {
+                        __builtin_amdgcn_raw_buffer_store_b64(v, rc, off, 0, 0);
+                    } else if (full) {
                         // park in this wave's LDS stash (written out below)
                         const int srow = 32 * i + r32;
                         const int chunk = 4 * j + g;
@@ -601,7 +604,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) qgemm_kernel(const Params p)
             }
         }
     }
-    if constexpr (OUT == OUT_BF16) {
+    if constexpr (STASH) {
         if (full) {
             constexpr int LPR = SCHK;                   // lanes per stash row
             constexpr int RPI = 64 / LPR;               // rows per store instruction

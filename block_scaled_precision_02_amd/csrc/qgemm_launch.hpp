@@ -9,8 +9,9 @@ namespace qgemm {
 //   0 -> 256x256, 2x2 waves of 128x128 (1 wave per SIMD, 256 accumulators)
 //   1 -> 128x128, 2x2 waves of 64x64
 //   2 -> 256x256, 2x4 waves of 128x64 (2 waves per SIMD, 128 accumulators)
-constexpr int NUM_TILES = 3;
-__host__ __device__ constexpr int tile_edge(int tile) { return tile == 1 ? 128 : 256; }
+//   3 -> 192x192, 2x2 waves of 96x96 (144 accumulators)
+constexpr int NUM_TILES = 4;
+__host__ __device__ constexpr int tile_edge(int tile) { return tile == 1 ? 128 : (tile == 3 ? 192 : 256); }
 __host__ __device__ constexpr int tile_threads(int tile) { return tile == 2 ? 512 : 256; }
 
 template <int PATH, int WM, int WN, int TM, int TN, bool BIAS, int BROWS, bool SVEC, int OUT>
@@ -28,6 +29,7 @@ hipError_t launch_tile(int tile, const Params &p, hipStream_t s)
     case 0: return launch_variant<PATH, 2, 2, 4, 4, BIAS, BROWS, SVEC, OUT>(p, s);
     case 1: return launch_variant<PATH, 2, 2, 2, 2, BIAS, BROWS, SVEC, OUT>(p, s);
     case 2: return launch_variant<PATH, 2, 4, 4, 2, BIAS, BROWS, SVEC, OUT>(p, s);
+    case 3: return launch_variant<PATH, 2, 2, 3, 3, BIAS, BROWS, SVEC, OUT>(p, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -141,8 +141,8 @@ const char *qgemm_status_string(qgemm_status status);
 
 /* Tile variant the host-side table picks for a problem (pure host logic, no
  * HIP call).  path: 0 int8, 1 fp8, 2 MX e4m3, 3 MX e2m1.  Returns the tile id
- * (0: 256x256 with 4 waves, 1: 128x128, 2: 256x256 with 8 waves), or -1 for
- * a bad path. */
+ * (0: 256x256 with 4 waves, 1: 128x128, 2: 256x256 with 8 waves, 3: 192x192),
+ * or -1 for a bad path. */
 int qgemm_select_tile(int path, int64_t M, int64_t N, int64_t K);
 
 /* Block edge (rows of A = rows of B) of a tile id, or 0 for an unknown id. */

@@ -125,14 +125,25 @@ def test_fake_arch_refused_before_any_hip_call(monkeypatch):
 
 def test_tile_table():
     L = q.lib()
-    # a 256x256 grid that would leave most CUs idle picks the 128x128 tile
-    assert L.qgemm_select_tile(0, 256, 256, 512) == 1
-    assert L.qgemm_select_tile(1, 4096, 2112, 7168) == 0      # 144 tiles: still the big tile
-    assert L.qgemm_select_tile(3, 8192, 8192, 8192) == 0
-    assert L.qgemm_select_tile(0, 30000, 21504, 5376) == 0
+    # full rounds of 256x256 tiles keep the big tile
+    assert L.qgemm_select_tile(3, 8192, 8192, 8192) == 0        # 1024 tiles = 4 rounds
+    assert L.qgemm_select_tile(0, 30000, 21504, 5376) == 0      # 9912 tiles
+    assert L.qgemm_select_tile(2, 16384, 7168, 2048) == 0       # 1792 tiles = 7 rounds
+    # 144 tiles of 256x256 leave 112 CUs idle; 242 tiles of 192x192 fill one round
+    assert L.qgemm_select_tile(1, 4096, 2112, 7168) == 3
     assert L.qgemm_select_tile(7, 64, 64, 64) == -1
-    assert L.qgemm_tile_rows(0) == 256 and L.qgemm_tile_rows(1) == 128 and L.qgemm_tile_rows(2) == 256
-    assert L.qgemm_tile_rows(5) == 0
+    for t, e in ((0, 256), (1, 128), (2, 256), (3, 192)):
+        assert L.qgemm_tile_rows(t) == e
+    assert L.qgemm_tile_rows(4) == 0 and L.qgemm_tile_rows(-1) == 0
     assert L.qgemm_force_tile(9) == -2
     assert L.qgemm_force_tile(1) == -1
     assert L.qgemm_force_tile(-1) == 1
+
+
+def test_tile_table_is_sane_everywhere():
+    """Every choice names a compiled tile and never leaves the grid empty."""
+    L = q.lib()
+    for M in (1, 17, 255, 256, 257, 1000, 4096, 30000):
+        for N in (1, 33, 256, 2112, 7168, 21504):
+            t = L.qgemm_select_tile(0, M, N, 512)
+            assert L.qgemm_tile_rows(t) in (128, 192, 256)

@@ -46,7 +46,7 @@ def _full_check(d, what, tile=None):
 # ------------------------------------------------------------------ INT8
 
 @pytest.mark.parametrize("bias", [True, False])
-@pytest.mark.parametrize("tile", [0, 1, 2])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3])
 def test_i8_small_workload(bias, tile):
     d = inputs.make("i8_small", bias=bias)
     _full_check(d, f"i8_small bias={bias}", tile)
@@ -55,7 +55,7 @@ def test_i8_small_workload(bias, tile):
 def test_i8_accumulator_exact():
     d = inputs.make("i8_small")
     A, B = parity.dev(d["A"]), parity.dev(d["B"])
-    for tile in (0, 1, 2):
+    for tile in (0, 1, 2, 3):
         q.force_tile(tile)
         acc = q.qgemm_i8_acc_i32(A, B)
         torch.cuda.synchronize()
@@ -196,10 +196,11 @@ def test_tile_variants_identical(name):
     tile variant, so the variants agree bit for bit."""
     d = inputs.make(name, M=300, N=280, K=512)
     outs = []
-    for tile in (0, 1, 2):
+    for tile in (0, 1, 2, 3):
         q.force_tile(tile)
         outs.append(parity.bits(parity.gpu_run(d)))
-    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    for t in (1, 2, 3):
+        assert np.array_equal(outs[0], outs[t]), f"tile {t}"
 
 
 def test_non_default_stream():
