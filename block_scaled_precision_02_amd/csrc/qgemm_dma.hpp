@@ -1,0 +1,331 @@
+// qgemm_dma.hpp -- the scaled GEMM with operands fetched straight into LDS.
+//
+// Same computation, tile geometry, fragment maps and epilogue as
+// qgemm_kernel.hpp, with a different way of filling LDS:
+//
+//  * K advances 64 bytes per stage and LDS holds DNST = 4 stages.  Each
+//    stage of A and B is fetched with buffer_load_dwordx4 ... lds (the data
+//    goes from memory to LDS without passing through VGPRs), three stages
+//    ahead of its use: the wave issues no LDS writes and holds no staging
+//    registers, and the fetch of stage t+3 overlaps the MFMAs of stages
+//    t..t+2.
+//  * The loads are issued from inline assembly so that the compiler does not
+//    add waits of its own for them; the kernel waits with s_waitcnt vmcnt(n),
+//    n counting the loads the wave issued after the stage it needs, then a
+//    barrier (every wave waited for its own share).
+//  * MX scales arrive the same way: 16 bytes of each scale row (the scales of
+//    four stages) per fetch, double-buffered, fetched four stages ahead; the
+//    scale words are read from LDS together with the fragments.
+//  * A 16-byte chunk c of staged row r sits at slot c ^ ((r >> 2) & 3) of its
+//    64-byte row, so a fragment read (16 lanes on 16 consecutive rows at one
+//    logical chunk) covers 16 different 16-byte slots of 256 bytes of banks.
+//    A fetch instruction writes 1 KB of LDS (16 rows); lane i lands at
+//    byte 16i of it, so lane i fetches the chunk that belongs in slot i%4 of
+//    row i/4.
+//
+// Requirements (checked on the host, which otherwise uses qgemm_kernel):
+// K bytes a multiple of 4 stages (256 bytes), and for MX a scale row length
+// K/32 that is a multiple of 16 bytes.  Rows past M / N are fetched from out of
+// range offsets; whatever lands in LDS for them only reaches output rows and
+// columns that are never stored.
+#pragma once
+#include "qgemm_kernel.hpp"
+
+namespace qgemm {
+
+constexpr int DSTAGE = 64;   // K bytes per stage
+constexpr int DNST = 4;      // stages resident in LDS
+
+__device__ __forceinline__ int dlds_off(int r, int c)
+{
+    return r * DSTAGE + ((c ^ ((r >> 2) & 3)) << 4);
+}
+
+// One wave-wide 16-byte-per-lane fetch into LDS at lds_addr + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voff), "s"(r)
+                 : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+template <int PATH> struct DmaTraits;
+// sub-steps per 64-byte stage and the chunk (of 4) a lane half reads
+template <> struct DmaTraits<PATH_I8> { static constexpr int NSUB = 2; };   // chunk 2S+h
+template <> struct DmaTraits<PATH_F8> { static constexpr int NSUB = 1; };   // chunks h, 2+h
+template <> struct DmaTraits<PATH_MX8> { static constexpr int NSUB = 1; };  // chunks h, 2+h
+template <> struct DmaTraits<PATH_MX4> { static constexpr int NSUB = 2; };  // chunk 2h+S
+
+// Fragment of a 32-row MFMA operand for sub-step S of a 64-byte stage.
+//   int8:  16 bytes, chunk 2S+h (32 elements per sub-step)
+//   e4m3:  32 bytes; VGPRs 0-3 form the instruction's first 32-element block
+//          with the other lane half, VGPRs 4-7 the second: chunk h -> block 0,
+//          chunk 2+h -> block 1 of the stage; lane half h's scale is block h's.
+//   e2m1:  16 bytes = one 32-element block, chunk 2h+S (block 2h+S); lane
+//          half h's scales are blocks 2h and 2h+1 of the stage.
+template <int PATH, int S>
+__device__ __forceinline__ typename PathTraits<PATH>::Frag dma_frag(const uint8_t *tile, int row, int h)
+{
+    typename PathTraits<PATH>::Frag f;
+    if constexpr (PATH == PATH_I8) {
+        f = *(const i32x4 *)(tile + dlds_off(row, 2 * S + h));
+    } else if constexpr (PATH == PATH_MX4) {
+        i32x4 lo = *(const i32x4 *)(tile + dlds_off(row, 2 * h + S));
+        f = i32x8{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+    } else {
+        i32x4 lo = *(const i32x4 *)(tile + dlds_off(row, h));
+        i32x4 hi = *(const i32x4 *)(tile + dlds_off(row, 2 + h));
+        f = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    return f;
+}
+
+template <int PATH, int TM, int TN, bool BIAS, int BROWS, int OUT>
+__global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
+{
+    constexpr int WM = 2, WN = 2;
+    constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+    constexpr int NSUB = DmaTraits<PATH>::NSUB;
+    constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4);
+    constexpr int STAGE_BYTES = (BM + BN) * DSTAGE;
+    constexpr int OPND_BYTES = DNST * STAGE_BYTES;
+    // MX scale chunks: per buffer, BM rows of A and 64 rows of B (32x32
+    // layout: BN/32 valid rows; the rest of the 64 absorb the fetch's spare
+    // lanes) or BN rows (1x32), 16 bytes each.
+    constexpr int SB_ROWS = (BROWS == 1) ? BN : 64;
+    constexpr int SCL_BUF = (BM + SB_ROWS) * 16;
+    constexpr int SCL_BYTES = MX ? 2 * SCL_BUF : 0;
+    constexpr int NQ = TM * TN;
+    constexpr int RPF = (PATH == PATH_F8 || PATH == PATH_MX8) ? 2 : 1;
+    constexpr int NDSR = (TM + TN) * RPF;                 // fragment reads per sub-step
+    constexpr int DMA_A = BM / 16 / 4, DMA_B = BN / 16 / 4; // fetches per wave per stage
+    constexpr int NDMA = DMA_A + DMA_B;
+    constexpr int NSCD = MX ? 2 : 0;                      // scale fetches per wave per chunk
+    static_assert(DMA_A * 64 == BM && DMA_B * 64 == BN, "tile rows must be a multiple of 64");
+    static_assert(BM == 256 && (BROWS == 1 ? BN == 256 : true), "one scale fetch per wave per operand");
+    using Frag = typename PathTraits<PATH>::Frag;
+    using Acc = typename AccT<PATH>::T;
+
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[OPND_BYTES + SCL_BYTES];
+    const unsigned lds0 = (unsigned)(uintptr_t)(&lds[0]);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int h = lane >> 5, r32 = lane & 31;
+
+    int tm, tn;
+    tile_of(p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int rows_a = min(BM, p.M - m0), rows_b = min(BN, p.N - n0);
+
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * p.lda,
+                                                (uint32_t)((rows_a - 1) * p.lda + p.kbytes));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + (int64_t)n0 * p.ldb,
+                                                (uint32_t)((rows_b - 1) * p.ldb + p.kbytes));
+
+    // Fetch map: wave w's j-th A fetch covers rows 16*(4w+j) .. +15; lane i
+    // takes row +i/4 and the chunk that belongs in slot i%4.
+    unsigned a_off[DMA_A], b_off[DMA_B];
+#pragma unroll
+    for (int j = 0; j < DMA_A; ++j) {
+        const int r = 16 * (DMA_A * wave + j) + (lane >> 2);
+        const int c = (lane & 3) ^ ((r >> 2) & 3);
+        a_off[j] = r < rows_a ? (unsigned)(r * p.lda + 16 * c) : OOB;
+    }
+#pragma unroll
+    for (int j = 0; j < DMA_B; ++j) {
+        const int r = 16 * (DMA_B * wave + j) + (lane >> 2);
+        const int c = (lane & 3) ^ ((r >> 2) & 3);
+        b_off[j] = r < rows_b ? (unsigned)(r * p.ldb + 16 * c) : OOB;
+    }
+    auto fetch_stage = [&](int t, int slot) {
+        const unsigned kb = (unsigned)(t * DSTAGE);
+        const unsigned la = lds0 + slot * STAGE_BYTES + 16 * DMA_A * wave * DSTAGE;
+        const unsigned lb = lds0 + slot * STAGE_BYTES + BM * DSTAGE + 16 * DMA_B * wave * DSTAGE;
+#pragma unroll
+        for (int j = 0; j < DMA_A; ++j)
+            dma16(ra, a_off[j] == OOB ? OOB : a_off[j] + kb, la + j * 16 * DSTAGE);
+#pragma unroll
+        for (int j = 0; j < DMA_B; ++j)
+            dma16(rb, b_off[j] == OOB ? OOB : b_off[j] + kb, lb + j * 16 * DSTAGE);
+    };
+
+    // MX scale chunks: chunk u holds 16 bytes of every scale row; e2m1 starts
+    // at byte 16u (stages 4u..4u+3 x 4 blocks), e4m3 at byte 8u (its first 8
+    // bytes are stages 4u..4u+3 x 2 blocks; the rest comes again in chunk u+1).
+    __amdgpu_buffer_rsrc_t rsa, rsb;
+    unsigned sa_fo = OOB, sb_fo = OOB;
+    if constexpr (MX) {
+        rsa = make_rsrc(p.mx_sa + (int64_t)m0 * p.kblocks, (uint32_t)(rows_a * p.kblocks));
+        const int srows_b = BROWS == 1 ? rows_b : (rows_b + 31) / 32;
+        rsb = make_rsrc(p.mx_sb + (int64_t)(n0 / BROWS) * p.kblocks, (uint32_t)(srows_b * p.kblocks));
+        const int ra_row = 64 * wave + lane;                       // A scale row of this lane
+        sa_fo = ra_row < rows_a ? (unsigned)(ra_row * p.kblocks) : OOB;
+        const int rb_row = BROWS == 1 ? 64 * wave + lane : lane;   // 32x32: every wave fetches rows 0..63
+        sb_fo = rb_row < srows_b ? (unsigned)(rb_row * p.kblocks) : OOB;
+    }
+    auto fetch_scales = [&](int u) {
+        if constexpr (MX) {
+            const unsigned base = lds0 + OPND_BYTES + (u & 1) * SCL_BUF;
+            // four stages of scales: 16 bytes (e2m1) or 8 bytes (e4m3) per row
+            const unsigned kb = (unsigned)((PATH == PATH_MX4 ? 16 : 8) * u);
+            dma16(rsa, sa_fo == OOB ? OOB : sa_fo + kb, base + 64 * 16 * wave);
+            dma16(rsb, sb_fo == OOB ? OOB : sb_fo + kb, base + BM * 16 + (BROWS == 1 ? 64 * 16 * wave : 0));
+        }
+    };
+
+    Acc acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = Acc{};
+
+    const int arow = wm * TM * 32 + r32;
+    const int brow = wn * TN * 32 + r32;
+    Frag fa[2][TM], fb[2][TN];
+    unsigned sa_use[TM], sb_use[TN], sa_nxt[TM], sb_nxt[TN];
+
+    // Fragments of sub-step S of stage slot `slot` into register set SET.
+    auto read_frags = [&](auto sc, int slot, auto setc) {
+        constexpr int S = decltype(sc)::value;
+        constexpr int SET = decltype(setc)::value;
+        const uint8_t *ta = &lds[slot * STAGE_BYTES];
+        const uint8_t *tb = ta + BM * DSTAGE;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            fa[SET][i] = dma_frag<PATH, S>(ta, arow + 32 * i, h);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            fb[SET][j] = dma_frag<PATH, S>(tb, brow + 32 * j, h);
+    };
+    // Scale words of stage t (J = t % 4) for this lane: byte S of the word is
+    // sub-step S's scale for the lane's block.
+    auto read_scales = [&](int t, auto jc) {
+        if constexpr (MX) {
+            constexpr int J = decltype(jc)::value;
+            const uint8_t *sbuf = &lds[OPND_BYTES + ((t >> 2) & 1) * SCL_BUF];
+            // e2m1: bytes 4J + 2h, +1;  e4m3: byte 2J + h
+            constexpr int WB = (PATH == PATH_MX4) ? 4 * J : (2 * J) & ~3;
+            const int sh = (PATH == PATH_MX4) ? 16 * h : 8 * (((2 * J) & 3) + h);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                sa_nxt[i] = *(const unsigned *)(sbuf + (arow + 32 * i) * 16 + WB) >> sh;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int row = BROWS == 1 ? brow + 32 * j : wn * TN + j;
+                sb_nxt[j] = *(const unsigned *)(sbuf + BM * 16 + row * 16 + WB) >> sh;
+            }
+        }
+    };
+    auto mfmas = [&](auto sc, auto setc, auto q0c, auto q1c) {
+        constexpr int S = decltype(sc)::value;
+        constexpr int SET = decltype(setc)::value;
+        static_for<decltype(q0c)::value, decltype(q1c)::value>([&](auto qc) {
+            constexpr int Q = decltype(qc)::value;
+            constexpr int i = Q / TN;
+            constexpr int j = (i & 1) ? (TN - 1 - Q % TN) : (Q % TN);
+            mfma<PATH, S>(acc[i][j], fb[SET][j], fa[SET][i], MX ? sb_use[j] : 0u, MX ? sa_use[i] : 0u);
+        });
+    };
+    auto use_next_scales = [&]() {
+        if constexpr (MX) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) sa_use[i] = sa_nxt[i];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) sb_use[j] = sb_nxt[j];
+        }
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    // Prologue: scale chunk 0, stages 0..2; wait for chunk 0 and stage 0.
+    fetch_scales(0);
+    fetch_stage(0, 0);
+    fetch_stage(1, 1);
+    fetch_stage(2, 2);
+    wait_vmcnt<2 * NDMA>();
+    lds_barrier();
+    read_frags(I0(), 0, I0());
+    read_scales(0, I0());
+    use_next_scales();
+
+    // Stage t = 4q + J.  Region A: fetch scale chunk q+1 (J == 0) and stage
+    // t+3 into the slot stage t-1 used (free since the last barrier), read
+    // the fragments of the later sub-steps, multiply.  Then wait for stage
+    // t+1 -- the loads issued after it are those of stages t+2 and t+3 --
+    // and meet at the barrier; region B reads stage t+1's first fragments
+    // (and scale words) under the last sub-step's MFMAs.
+    auto stage = [&](int t, auto jc) {
+        constexpr int J = decltype(jc)::value;
+        constexpr int SET0 = (NSUB == 1) ? (J & 1) : 0;    // register set of sub-step 0
+        if constexpr (J == 0)
+            fetch_scales((t >> 2) + 1);
+        fetch_stage(t + 3, (J + 3) & 3);
+        if constexpr (NSUB == 2) {
+            read_frags(I1(), J, I1());
+            mfmas(I0(), I0(), I0(), std::integral_constant<int, NQ>());
+            // issue order: each MFMA followed by a share of the fragment reads
+            // (the fetches, inline assembly, keep their place ahead of them)
+            static_for<0, NQ>([&](auto qc) {
+                constexpr int Q = decltype(qc)::value;
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                constexpr int r = NDSR * (Q + 1) / NQ - NDSR * Q / NQ;
+                if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+            });
+        } else {
+            mfmas(I0(), std::integral_constant<int, SET0>(), I0(), std::integral_constant<int, NQ / 2>());
+        }
+        // loads issued after stage t+1's: stages t+2 and t+3, plus the scale
+        // chunk when it went out at stage t or t-1
+        constexpr int AFTER = 2 * NDMA + ((J == 0 || J == 1) ? NSCD : 0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<AFTER>();
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        constexpr int SETN = (NSUB == 1) ? ((J + 1) & 1) : 0;
+        read_frags(I0(), (J + 1) & 3, std::integral_constant<int, SETN>());
+        read_scales(t + 1, std::integral_constant<int, (J + 1) & 3>());
+        if constexpr (NSUB == 2) {
+            mfmas(I1(), I1(), I0(), std::integral_constant<int, NQ>());
+        } else {
+            mfmas(I0(), std::integral_constant<int, SET0>(), std::integral_constant<int, NQ / 2>(),
+                  std::integral_constant<int, NQ>());
+        }
+        constexpr int NB = (NSUB == 2) ? NQ : NQ / 2;
+        constexpr int RB = NDSR + (MX ? TM + TN : 0);
+        static_for<0, NB>([&](auto qc) {
+            constexpr int Q = decltype(qc)::value;
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            constexpr int r = RB * (Q + 1) / NB - RB * Q / NB;
+            if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+        });
+        use_next_scales();
+    };
+
+    // The host guarantees kbytes % 256 == 0: a whole number of 4-stage
+    // rounds.  The last round fetches stages past K (from in-range or
+    // out-of-range offsets, never multiplied).
+    const int nstages = p.kbytes / DSTAGE;
+    for (int t = 0; t < nstages; t += 4) {
+        stage(t, I0());
+        stage(t + 1, I1());
+        stage(t + 2, std::integral_constant<int, 2>());
+        stage(t + 3, std::integral_constant<int, 3>());
+    }
+    wait_vmcnt<0>();   // nothing may still be landing in LDS once it holds the output
+
+    store_tile<PATH, WM, WN, TM, TN, BIAS, OUT, OPND_BYTES>(p, acc, &lds[0], m0, n0, rows_a, rows_b);
+}
+
+}  // namespace qgemm

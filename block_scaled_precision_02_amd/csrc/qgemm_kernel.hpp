@@ -229,6 +229,166 @@ __device__ __forceinline__ unsigned pack_bf16(float x, float y)
     return __builtin_bit_cast(unsigned, v);
 }
 
+// ------------------------------------------------------------ epilogue
+// Shared by the kernels: scale, bias, round and store one workgroup tile.
+// LDSBYTES is the LDS the kernel owns (reused as the output stash once every
+// wave is done with the operand buffers).
+template <int PATH, int WM, int WN, int TM, int TN, bool BIAS, int OUT, int LDSBYTES, class Acc>
+__device__ __forceinline__ void store_tile(const Params &p, Acc (&acc)[TM][TN], uint8_t *lds_base, int m0,
+                                           int n0, int rows_a, int rows_b)
+{
+    constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+    constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int h = lane >> 5, r32 = lane & 31;
+    const int arow = wm * TM * 32 + r32;
+    // ---------------------------------------------------------- epilogue
+    // Lane holds, for tile (i, j): m = m0 + arow + 32i, and for g = 0..3 the
+    // four consecutive n = n0 + wn*TN*32 + 32j + 8g + 4h + {0..3} in
+    // acc[i][j][4g..4g+3].  Every access goes through a range-checked buffer
+    // descriptor: loads past M / N read 0, stores past them are dropped, so
+    // the only difference between a full tile and an edge tile is that the
+    // edge tile stores element by element (columns past N inside a row of
+    // ldc must not be touched).
+    constexpr int ESZ = (OUT == OUT_I32) ? 4 : 2;
+    const bool full = (rows_a == BM) && (rows_b == BN);
+    const int nloc_base = wn * TN * 32 + 4 * h;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc((const uint8_t *)p.C + (int64_t)m0 * p.ldc * ESZ,
+                                                (uint32_t)((int64_t)rows_a * p.ldc * ESZ));
+    const unsigned col0 = (unsigned)(n0 * ESZ);
+    __amdgpu_buffer_rsrc_t rsb_e, rbias;
+    if constexpr (OUT == OUT_BF16 && !MX)
+        rsb_e = make_rsrc(p.scale_b + n0, (uint32_t)(rows_b * 4));
+    if constexpr (BIAS)
+        rbias = make_rsrc(p.bias + n0, (uint32_t)(rows_b * 2));
+    // Full bf16 tiles leave through LDS: each wave parks its (TM*32) x (TN*32)
+    // block of bf16 results in its own stash (16-byte chunks XOR-swizzled by
+    // row), then writes whole 16-byte row pieces, consecutive lanes covering
+    // consecutive bytes of a row, so every store instruction fills complete
+    // cache lines instead of touching 32 rows.
+    constexpr int SROWB = TN * 32 * 2;              // stash row bytes (bf16)
+    constexpr int SCHK = SROWB / 16;                // 16-byte chunks per row
+    constexpr bool STASH = OUT == OUT_BF16 && (SCHK & (SCHK - 1)) == 0 && 64 % SCHK == 0 &&
+                           WM * WN * TM * 32 * SROWB <= LDSBYTES;
+    uint8_t *stash = lds_base + wave * (TM * 32) * SROWB;
+    if constexpr (STASH) {
+        if (full)
+            lds_barrier();   // every wave is done with the operand buffers
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int mloc = arow + 32 * i;
+        const bool mok = mloc < rows_a;
+        float sa = 0.f;
+        if constexpr (OUT == OUT_BF16 && !MX) {
+            if (mok)
+                sa = p.scale_a[m0 + mloc];
+        }
+        const unsigned rowoff = (unsigned)((int64_t)mloc * p.ldc * ESZ);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int nloc = nloc_base + 32 * j + 8 * g;
+                const unsigned off = rowoff + col0 + (unsigned)(nloc * ESZ);
+                if constexpr (OUT == OUT_I32) {
+                    const i32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1],
+                                     acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                    if (full) {
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rc, off, 0, 0);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            __builtin_amdgcn_raw_buffer_store_b32(
+                                (unsigned)v[r], rc, (nloc + r < rows_b) ? off + 4 * r : OOB, 0, 0);
+                    }
+                } else {
+                    // Per-column scale and bias: one vector load in a full tile;
+                    // element loads at an edge (a vector load that runs past the
+                    // range returns zeros for all of its elements).
+                    float f[4];
+                    unsigned sbw[4], bbw[4];
+                    if (full) {
+                        if constexpr (!MX) {
+                            const u32x4 t = ld16(rsb_e, (unsigned)(nloc * 4));
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) sbw[r] = t[r];
+                        }
+                        if constexpr (BIAS) {
+                            const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(rbias, (unsigned)(nloc * 2), 0, 0);
+                            const unsigned t0 = t[0], t1 = t[1];
+                            bbw[0] = t0 << 16;
+                            bbw[1] = t0 & 0xffff0000u;
+                            bbw[2] = t1 << 16;
+                            bbw[3] = t1 & 0xffff0000u;
+                        }
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const bool in = nloc + r < rows_b;
+                            if constexpr (!MX)
+                                sbw[r] = __builtin_amdgcn_raw_buffer_load_b32(
+                                    rsb_e, in ? (unsigned)((nloc + r) * 4) : OOB, 0, 0);
+                            if constexpr (BIAS)
+                                bbw[r] = (unsigned)__builtin_amdgcn_raw_buffer_load_b16(
+                                             rbias, in ? (unsigned)((nloc + r) * 2) : OOB, 0, 0) << 16;
+                        }
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float x;
+                        if constexpr (PATH == PATH_I8)
+                            x = (float)acc[i][j][4 * g + r];
+                        else
+                            x = acc[i][j][4 * g + r];
+                        // (scalars only under bit_cast: clang's bit_cast of an
+                        // ext_vector element reads element 0)
+                        if constexpr (!MX) {
+                            x = x * sa;
+                            x = x * __builtin_bit_cast(float, sbw[r]);
+                        }
+                        if constexpr (BIAS)
+                            x = x + __builtin_bit_cast(float, bbw[r]);
+                        f[r] = x;
+                    }
+                    const u32x2 v = {pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3])};
+                    if (full && !STASH) {
+                        __builtin_amdgcn_raw_buffer_store_b64(v, rc, off, 0, 0);
+                    } else if (full) {
+                        // park in this wave's LDS stash (written out below)
+                        const int srow = 32 * i + r32;
+                        const int chunk = 4 * j + g;
+                        *(u32x2 *)(stash + srow * SROWB + ((chunk ^ (srow & (SCHK - 1))) << 4) + 8 * h) = v;
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            __builtin_amdgcn_raw_buffer_store_b16(
+                                (unsigned short)(v[r >> 1] >> (16 * (r & 1))), rc,
+                                (nloc + r < rows_b) ? off + 2 * r : OOB, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+    if constexpr (STASH) {
+        if (full) {
+            constexpr int LPR = SCHK;                   // lanes per stash row
+            constexpr int RPI = 64 / LPR;               // rows per store instruction
+            const int c = lane % LPR;
+            const unsigned gbase = (unsigned)((int64_t)(wm * TM * 32) * p.ldc * 2) + col0 +
+                                   (unsigned)((wn * TN * 32) * 2 + c * 16);
+#pragma unroll
+            for (int it = 0; it < TM * 32 / RPI; ++it) {
+                const int srow = it * RPI + lane / LPR;
+                const u32x4 v = *(const u32x4 *)(stash + srow * SROWB + ((c ^ (srow & (SCHK - 1))) << 4));
+                __builtin_amdgcn_raw_buffer_store_b128(v, rc, gbase + (unsigned)(srow * p.ldc * 2), 0, 0);
+            }
+        }
+    }
+}
+
 template <int PATH, int WM, int WN, int TM, int TN, bool BIAS, int BROWS, bool SVEC, int OUT>
 __global__ void __launch_bounds__(64 * WM * WN, 1) qgemm_kernel(const Params p)
 {
@@ -476,149 +636,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) qgemm_kernel(const Params p)
         kstep(kt + 1, I0(), std::true_type(), std::true_type(), std::true_type());
     }
 
-    // ---------------------------------------------------------- epilogue
-    // Lane holds, for tile (i, j): m = m0 + arow + 32i, and for g = 0..3 the
-    // four consecutive n = n0 + wn*TN*32 + 32j + 8g + 4h + {0..3} in
-    // acc[i][j][4g..4g+3].  Every access goes through a range-checked buffer
-    // descriptor: loads past M / N read 0, stores past them are dropped, so
-    // the only difference between a full tile and an edge tile is that the
-    // edge tile stores element by element (columns past N inside a row of
-    // ldc must not be touched).
-    constexpr int ESZ = (OUT == OUT_I32) ? 4 : 2;
-    const bool full = (rows_a == BM) && (rows_b == BN);
-    const int nloc_base = wn * TN * 32 + 4 * h;
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc((const uint8_t *)p.C + (int64_t)m0 * p.ldc * ESZ,
-                                                (uint32_t)((int64_t)rows_a * p.ldc * ESZ));
-    const unsigned col0 = (unsigned)(n0 * ESZ);
-    __amdgpu_buffer_rsrc_t rsb_e, rbias;
-    if constexpr (OUT == OUT_BF16 && !MX)
-        rsb_e = make_rsrc(p.scale_b + n0, (uint32_t)(rows_b * 4));
-    if constexpr (BIAS)
-        rbias = make_rsrc(p.bias + n0, (uint32_t)(rows_b * 2));
-    // Full bf16 tiles leave through LDS: each wave parks its (TM*32) x (TN*32)
-    // block of bf16 results in its own stash (16-byte chunks XOR-swizzled by
-    // row), then writes whole 16-byte row pieces, consecutive lanes covering
-    // consecutive bytes of a row, so every store instruction fills complete
-    // cache lines instead of touching 32 rows.
-    constexpr int SROWB = TN * 32 * 2;              // stash row bytes (bf16)
-    constexpr int SCHK = SROWB / 16;                // 16-byte chunks per row
-    constexpr bool STASH = OUT == OUT_BF16 && (SCHK & (SCHK - 1)) == 0 && 64 % SCHK == 0 &&
-                           WM * WN * TM * 32 * SROWB <= 2 * (BM + BN) * KSTEP_BYTES;
-    uint8_t *stash = &lds[0][0] + wave * (TM * 32) * SROWB;
-    if constexpr (STASH) {
-        if (full)
-            lds_barrier();   // every wave is done with the operand buffers
-    }
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int mloc = arow + 32 * i;
-        const bool mok = mloc < rows_a;
-        float sa = 0.f;
-        if constexpr (OUT == OUT_BF16 && !MX) {
-            if (mok)
-                sa = p.scale_a[m0 + mloc];
-        }
-        const unsigned rowoff = (unsigned)((int64_t)mloc * p.ldc * ESZ);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int nloc = nloc_base + 32 * j + 8 * g;
-                const unsigned off = rowoff + col0 + (unsigned)(nloc * ESZ);
-                if constexpr (OUT == OUT_I32) {
-                    const i32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1],
-                                     acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                    if (full) {
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rc, off, 0, 0);
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            __builtin_amdgcn_raw_buffer_store_b32(
-                                (unsigned)v[r], rc, (nloc + r < rows_b) ? off + 4 * r : OOB, 0, 0);
-                    }
-                } else {
-                    // Per-column scale and bias: one vector load in a full tile;
-                    // element loads at an edge (a vector load that runs past the
-                    // range returns zeros for all of its elements).
-                    float f[4];
-                    unsigned sbw[4], bbw[4];
-                    if (full) {
-                        if constexpr (!MX) {
-                            const u32x4 t = ld16(rsb_e, (unsigned)(nloc * 4));
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) sbw[r] = t[r];
-                        }
-                        if constexpr (BIAS) {
-                            const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(rbias, (unsigned)(nloc * 2), 0, 0);
-                            const unsigned t0 = t[0], t1 = t[1];
-                            bbw[0] = t0 << 16;
-                            bbw[1] = t0 & 0xffff0000u;
-                            bbw[2] = t1 << 16;
-                            bbw[3] = t1 & 0xffff0000u;
-                        }
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const bool in = nloc + r < rows_b;
-                            if constexpr (!MX)
-                                sbw[r] = __builtin_amdgcn_raw_buffer_load_b32(
-                                    rsb_e, in ? (unsigned)((nloc + r) * 4) : OOB, 0, 0);
-                            if constexpr (BIAS)
-                                bbw[r] = (unsigned)__builtin_amdgcn_raw_buffer_load_b16(
-                                             rbias, in ? (unsigned)((nloc + r) * 2) : OOB, 0, 0) << 16;
-                        }
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float x;
-                        if constexpr (PATH == PATH_I8)
-                            x = (float)acc[i][j][4 * g + r];
-                        else
-                            x = acc[i][j][4 * g + r];
-                        // (scalars only under bit_cast: clang's bit_cast of an
-                        // ext_vector element reads element 0)
-                        if constexpr (!MX) {
-                            x = x * sa;
-                            x = x * __builtin_bit_cast(float, sbw[r]);
-                        }
-                        if constexpr (BIAS)
-                            x = x + __builtin_bit_cast(float, bbw[r]);
-                        f[r] = x;
-                    }
-                    const u32x2 v = {pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3])};
-                    if (full && !STASH) {
-                        __builtin_amdgcn_raw_buffer_store_b64(v, rc, off, 0, 0);
-                    } else if (full) {
-                        // park in this wave's LDS stash (written out below)
-                        const int srow = 32 * i + r32;
-                        const int chunk = 4 * j + g;
-                        *(u32x2 *)(stash + srow * SROWB + ((chunk ^ (srow & (SCHK - 1))) << 4) + 8 * h) = v;
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            __builtin_amdgcn_raw_buffer_store_b16(
-                                (unsigned short)(v[r >> 1] >> (16 * (r & 1))), rc,
-                                (nloc + r < rows_b) ? off + 2 * r : OOB, 0, 0);
-                    }
-                }
-            }
-        }
-    }
-    if constexpr (STASH) {
-        if (full) {
-            constexpr int LPR = SCHK;                   // lanes per stash row
-            constexpr int RPI = 64 / LPR;               // rows per store instruction
-            const int c = lane % LPR;
-            const unsigned gbase = (unsigned)((int64_t)(wm * TM * 32) * p.ldc * 2) + col0 +
-                                   (unsigned)((wn * TN * 32) * 2 + c * 16);
-#pragma unroll
-            for (int it = 0; it < TM * 32 / RPI; ++it) {
-                const int srow = it * RPI + lane / LPR;
-                const u32x4 v = *(const u32x4 *)(stash + srow * SROWB + ((c ^ (srow & (SCHK - 1))) << 4));
-                __builtin_amdgcn_raw_buffer_store_b128(v, rc, gbase + (unsigned)(srow * p.ldc * 2), 0, 0);
-            }
-        }
-    }
+    store_tile<PATH, WM, WN, TM, TN, BIAS, OUT, 2 * (BM + BN) * KSTEP_BYTES>(p, acc, &lds[0][0], m0, n0, rows_a,
+                                                                      rows_b);
 }
 
 }  // namespace qgemm

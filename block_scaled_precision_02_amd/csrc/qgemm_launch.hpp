@@ -1,7 +1,7 @@
 // qgemm_launch.hpp -- host-side launch of one kernel variant.
 #pragma once
 #include <hip/hip_runtime.h>
-#include "qgemm_kernel.hpp"
+#include "qgemm_dma.hpp"
 
 namespace qgemm {
 
@@ -10,7 +10,10 @@ namespace qgemm {
 //   1 -> 128x128, 2x2 waves of 64x64
 //   2 -> 256x256, 2x4 waves of 128x64 (2 waves per SIMD, 128 accumulators)
 //   3 -> 192x192, 2x2 waves of 96x96 (144 accumulators)
-constexpr int NUM_TILES = 4;
+//   4 -> 256x256 as tile 0, operands fetched straight into LDS (qgemm_dma.hpp);
+//        needs K bytes % 256 == 0 and, for MX, K/32 % 16 == 0 with aligned scales
+constexpr int NUM_TILES = 5;
+constexpr int DMA_TILE = 4;
 __host__ __device__ constexpr int tile_edge(int tile) { return tile == 1 ? 128 : (tile == 3 ? 192 : 256); }
 __host__ __device__ constexpr int tile_threads(int tile) { return tile == 2 ? 512 : 256; }
 
@@ -30,6 +33,16 @@ hipError_t launch_tile(int tile, const Params &p, hipStream_t s)
     case 1: return launch_variant<PATH, 2, 2, 2, 2, BIAS, BROWS, SVEC, OUT>(p, s);
     case 2: return launch_variant<PATH, 2, 4, 4, 2, BIAS, BROWS, SVEC, OUT>(p, s);
     case 3: return launch_variant<PATH, 2, 2, 3, 3, BIAS, BROWS, SVEC, OUT>(p, s);
+    case DMA_TILE:
+        if constexpr (PATH == PATH_MX8 || PATH == PATH_MX4) {
+            if (!SVEC)
+                return hipErrorInvalidValue;
+        }
+        {
+            const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(256);
+            hipLaunchKernelGGL((qgemm_dma_kernel<PATH, 4, 4, BIAS, BROWS, OUT>), grid, block, 0, s, p);
+            return hipGetLastError();
+        }
     default: return hipErrorInvalidValue;
     }
 }

@@ -46,7 +46,7 @@ def _full_check(d, what, tile=None):
 # ------------------------------------------------------------------ INT8
 
 @pytest.mark.parametrize("bias", [True, False])
-@pytest.mark.parametrize("tile", [0, 1, 2, 3])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4])
 def test_i8_small_workload(bias, tile):
     d = inputs.make("i8_small", bias=bias)
     _full_check(d, f"i8_small bias={bias}", tile)
@@ -55,7 +55,7 @@ def test_i8_small_workload(bias, tile):
 def test_i8_accumulator_exact():
     d = inputs.make("i8_small")
     A, B = parity.dev(d["A"]), parity.dev(d["B"])
-    for tile in (0, 1, 2, 3):
+    for tile in (0, 1, 2, 3, 4):
         q.force_tile(tile)
         acc = q.qgemm_i8_acc_i32(A, B)
         torch.cuda.synchronize()
@@ -192,15 +192,74 @@ def test_mx_random_scales_repeated(name):
 
 @pytest.mark.parametrize("name", ["i8_small", "f8_ptpc", "mxfp8", "mxfp4"])
 def test_tile_variants_identical(name):
-    """Each output's accumulation chain is the same sequence of MFMAs in every
-    tile variant, so the variants agree bit for bit."""
+    """Tiles 0-3 run each output's accumulation as the same sequence of MFMAs,
+    so they agree bit for bit; the LDS-fetch kernel (tile 4) groups K blocks
+    into MFMAs differently, so it is bit-identical for INT8 and within the
+    tolerance for FP8 / MX."""
     d = inputs.make(name, M=300, N=280, K=512)
     outs = []
-    for tile in (0, 1, 2, 3):
+    for tile in (0, 1, 2, 3, 4):
         q.force_tile(tile)
         outs.append(parity.bits(parity.gpu_run(d)))
     for t in (1, 2, 3):
         assert np.array_equal(outs[0], outs[t]), f"tile {t}"
+    if d["kind"] == "i8":
+        assert np.array_equal(outs[0], outs[4])
+    else:
+        ref, absdot, _ = parity.oracle_run(d)
+        parity.compare(d, outs[4], ref, absdot, f"{name} tile 4")
+
+
+DMA_SHAPES = [(1, 1, 256), (17, 33, 512), (255, 257, 1024), (300, 520, 2048), (513, 64, 256)]
+
+
+@pytest.mark.parametrize("name", ["i8_small", "f8_ptpc", "mxfp8", "mxfp4"])
+@pytest.mark.parametrize("M,N,K", DMA_SHAPES)
+def test_dma_kernel_edges(name, M, N, K):
+    """The LDS-fetch kernel on ragged M / N, NaN-filled output with canaries
+    beyond N and M (K a whole number of its stages)."""
+    kk = K if name != "mxfp4" else 2 * K      # e2m1: K elements are K/2 bytes
+    d = inputs.make(name, M=M, N=N, K=kk, bias=(M % 2 == 1))
+    q.force_tile(4)
+    ldc = N + (-N) % 8 + 8
+    buf = torch.full((M + 3, ldc), float("nan"), dtype=torch.bfloat16, device="cuda")
+    before = parity.bits(buf)
+    parity.gpu_run(d, out=buf[:M, :N])
+    after = parity.bits(buf)
+    ref, absdot, _ = parity.oracle_run(d)
+    parity.compare(d, after[:M, :N], ref, absdot, f"dma {name} {M}x{N}x{kk}")
+    assert np.array_equal(after[:M, N:], before[:M, N:]), "wrote past N"
+    assert np.array_equal(after[M:], before[M:]), "wrote past M"
+
+
+@pytest.mark.parametrize("name", ["mxfp8", "mxfp4"])
+def test_dma_kernel_other_b_layout_and_random_scales(name):
+    rng = np.random.default_rng(78)
+    d = inputs.make(name, M=260, N=300, K=1024)
+    fmt = d["fmt"]
+    brows = 1 if d["b_rows_per_scale"] == 32 else 32
+    cb, sb = inputs.mx_quantise(rng.standard_normal((300, 1024)).astype(np.float32), fmt, brows)
+    if fmt == "e2m1":
+        cb = inputs.pack_e2m1(cb)
+    d = dict(d, B=cb, scale_b=sb, b_rows_per_scale=brows,
+             scale_a=rng.integers(118, 136, d["scale_a"].shape, dtype=np.uint8))
+    q.force_tile(4)
+    ref, absdot, _ = parity.oracle_run(d)
+    first = None
+    for it in range(6):
+        got = parity.bits(parity.gpu_run(d))
+        if first is None:
+            parity.compare(d, got, ref, absdot, f"dma {name} B rows {brows}")
+            first = got
+        else:
+            assert np.array_equal(got, first), f"launch {it} differs"
+
+
+def test_dma_tile_falls_back_when_k_does_not_fit():
+    d = inputs.make("i8_small", M=100, N=70, K=96)
+    q.force_tile(4)
+    ref, _, _ = parity.oracle_run(d)
+    parity.compare(d, parity.bits(parity.gpu_run(d)), ref, None, "tile 4 fallback K=96")
 
 
 def test_non_default_stream():
@@ -222,13 +281,15 @@ def _sample_rows(M, n, rng):
     return np.unique(np.concatenate([head, mid, tail]))
 
 
+@pytest.mark.parametrize("tile", [-1, 4])
 @pytest.mark.parametrize("name", ["f8_ptpc", "mxfp8", "mxfp4", "i8_qkv"])
-def test_full_workload_sampled(name):
+def test_full_workload_sampled(name, tile):
     """The workload at its full size, launched as the benchmark launches it;
     the oracle checks a sample of whole output rows (first, last -- inside
     the partial tile when M is not a tile multiple -- and random ones)."""
     d = inputs.make(name)
-    _say(f"[parity] full {name} M={d['M']} N={d['N']} K={d['K']}")
+    _say(f"[parity] full {name} M={d['M']} N={d['N']} K={d['K']} tile {tile}")
+    q.force_tile(tile)
     out = parity.gpu_run(d)
     torch.cuda.synchronize()
     rng = np.random.default_rng(1)
