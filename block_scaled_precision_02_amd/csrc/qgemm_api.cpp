@@ -283,10 +283,14 @@ const char *qgemm_last_error(void) { return g_last_error.c_str(); }
 
 int qgemm_select_tile(int path, int64_t M, int64_t N, int64_t K)
 {
-    (void)K;
     if (path < 0 || path > 3)
         return -1;
-    return select_tile_impl(path, M, N);
+    const int64_t kbytes = path == 3 ? K / 2 : K;
+    const int prev = g_forced_tile;
+    g_forced_tile = -1;
+    const int t = pick_tile(path, Shape{M, N, K}, kbytes, true);   // scales assumed aligned
+    g_forced_tile = prev;
+    return t;
 }
 
 int qgemm_tile_rows(int tile) { return (tile >= 0 && tile < NUM_TILES) ? tile_edge(tile) : 0; }

@@ -140,7 +140,8 @@ const char *qgemm_last_error(void);
 const char *qgemm_status_string(qgemm_status status);
 
 /* Tile variant the host-side table picks for a problem (pure host logic, no
- * HIP call).  path: 0 int8, 1 fp8, 2 MX e4m3, 3 MX e2m1.  Returns the tile id
+ * HIP call; for MX, assuming 16-byte-aligned scale arrays).  path: 0 int8,
+ * 1 fp8, 2 MX e4m3, 3 MX e2m1.  Returns the tile id
  * (0: 256x256 with 4 waves, 1: 128x128, 2: 256x256 with 8 waves, 3: 192x192,
  * 4: 256x256 with operands fetched straight into LDS, used when K bytes are a
  * multiple of 256 and MX scale rows a multiple of 16 bytes, else tile 0),

@@ -126,9 +126,11 @@ def test_fake_arch_refused_before_any_hip_call(monkeypatch):
 def test_tile_table():
     L = q.lib()
     # full rounds of 256x256 tiles keep the big tile
-    assert L.qgemm_select_tile(3, 8192, 8192, 8192) == 0        # 1024 tiles = 4 rounds
     assert L.qgemm_select_tile(0, 30000, 21504, 5376) == 0      # 9912 tiles
-    assert L.qgemm_select_tile(2, 16384, 7168, 2048) == 0       # 1792 tiles = 7 rounds
+    # MX on 256x256 tiles takes the LDS-fetch kernel when K fits its stages
+    assert L.qgemm_select_tile(3, 8192, 8192, 8192) == 4        # 1024 tiles = 4 rounds
+    assert L.qgemm_select_tile(2, 16384, 7168, 2048) == 4       # 1792 tiles = 7 rounds
+    assert L.qgemm_select_tile(2, 16384, 7168, 2016) == 0       # K/32 = 63: not whole chunks
     # 144 tiles of 256x256 leave 112 CUs idle; 242 tiles of 192x192 fill one round
     assert L.qgemm_select_tile(1, 4096, 2112, 7168) == 3
     assert L.qgemm_select_tile(7, 64, 64, 64) == -1
@@ -147,3 +149,4 @@ def test_tile_table_is_sane_everywhere():
         for N in (1, 33, 256, 2112, 7168, 21504):
             t = L.qgemm_select_tile(0, M, N, 512)
             assert L.qgemm_tile_rows(t) in (128, 192, 256)
+            assert L.qgemm_force_tile(-1) == -1
