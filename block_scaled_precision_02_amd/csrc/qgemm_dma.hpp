@@ -114,7 +114,9 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
     using Frag = typename PathTraits<PATH>::Frag;
     using Acc = typename AccT<PATH>::T;
 
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[OPND_BYTES + SCL_BYTES];
+    constexpr bool PRM = OUT == OUT_BF16 && (!MX || BIAS);
+    constexpr int PRM_OFF = OPND_BYTES + SCL_BYTES;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[OPND_BYTES + SCL_BYTES + (PRM ? PRM_BYTES : 0)];
     const unsigned lds0 = (unsigned)(uintptr_t)(&lds[0]);
 
     const int tid = threadIdx.x;
@@ -249,7 +251,16 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    // Prologue: scale chunk 0, stages 0..2; wait for chunk 0 and stage 0.
+    // Prologue: the tile's epilogue operands (waves 0-2, one fetch each),
+    // scale chunk 0, stages 0..2; wait for all but stages 1 and 2.
+    if constexpr (PRM) {
+        if (wave == 0 && !MX)
+            dma16(make_rsrc(p.scale_a + m0, (uint32_t)(rows_a * 4)), 16 * lane, lds0 + PRM_OFF);
+        if (wave == 1 && !MX)
+            dma16(make_rsrc(p.scale_b + n0, (uint32_t)(rows_b * 4)), 16 * lane, lds0 + PRM_OFF + PRM_SB);
+        if (wave == 2 && BIAS)
+            dma16(make_rsrc(p.bias + n0, (uint32_t)(rows_b * 2)), 16 * lane, lds0 + PRM_OFF + PRM_BIAS);
+    }
     fetch_scales(0);
     fetch_stage(0, 0);
     fetch_stage(1, 1);
@@ -325,7 +336,8 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
     }
     wait_vmcnt<0>();   // nothing may still be landing in LDS once it holds the output
 
-    store_tile<PATH, WM, WN, TM, TN, BIAS, OUT, OPND_BYTES>(p, acc, &lds[0], m0, n0, rows_a, rows_b);
+    store_tile<PATH, WM, WN, TM, TN, BIAS, OUT, OPND_BYTES, PRM>(p, acc, &lds[0], &lds[PRM_OFF], m0, n0, rows_a,
+                                                                 rows_b);
 }
 
 }  // namespace qgemm

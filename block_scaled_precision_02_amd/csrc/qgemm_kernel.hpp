@@ -230,12 +230,23 @@ __device__ __forceinline__ unsigned pack_bf16(float x, float y)
 }
 
 // ------------------------------------------------------------ epilogue
+// Per-tile epilogue operands (row scales, column scales, bias) parked in LDS
+// while the K loop runs, so the epilogue reads them at LDS latency instead of
+// waiting on memory between groups of outputs:
+//   [0, 1024)     scale_a[m0 .. m0+BM) fp32
+//   [1024, 2048)  scale_b[n0 .. n0+BN) fp32
+//   [2048, 2560)  bias[n0 .. n0+BN) bf16; [2560, 3072) absorbs a 16-byte-per-
+//                 lane fetch's unused half
+// Only full tiles read them; an edge tile loads element by element.
+constexpr int PRM_SB = 1024, PRM_BIAS = 2048, PRM_BYTES = 3072;
+
 // Shared by the kernels: scale, bias, round and store one workgroup tile.
-// LDSBYTES is the LDS the kernel owns (reused as the output stash once every
-// wave is done with the operand buffers).
-template <int PATH, int WM, int WN, int TM, int TN, bool BIAS, int OUT, int LDSBYTES, class Acc>
-__device__ __forceinline__ void store_tile(const Params &p, Acc (&acc)[TM][TN], uint8_t *lds_base, int m0,
-                                           int n0, int rows_a, int rows_b)
+// LDSBYTES is the LDS at lds_base the kernel owns (reused as the output
+// stash once every wave is done with the operand buffers); prm is the
+// parked epilogue operands (used by full tiles when PRM).
+template <int PATH, int WM, int WN, int TM, int TN, bool BIAS, int OUT, int LDSBYTES, bool PRM, class Acc>
+__device__ __forceinline__ void store_tile(const Params &p, Acc (&acc)[TM][TN], uint8_t *lds_base,
+                                           const uint8_t *prm, int m0, int n0, int rows_a, int rows_b)
 {
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4);
@@ -244,14 +255,13 @@ __device__ __forceinline__ void store_tile(const Params &p, Acc (&acc)[TM][TN], 
     const int wm = wave / WN, wn = wave % WN;
     const int h = lane >> 5, r32 = lane & 31;
     const int arow = wm * TM * 32 + r32;
-    // ---------------------------------------------------------- epilogue
     // Lane holds, for tile (i, j): m = m0 + arow + 32i, and for g = 0..3 the
     // four consecutive n = n0 + wn*TN*32 + 32j + 8g + 4h + {0..3} in
-    // acc[i][j][4g..4g+3].  Every access goes through a range-checked buffer
-    // descriptor: loads past M / N read 0, stores past them are dropped, so
-    // the only difference between a full tile and an edge tile is that the
-    // edge tile stores element by element (columns past N inside a row of
-    // ldc must not be touched).
+    // acc[i][j][4g..4g+3].  Every global access goes through a range-checked
+    // buffer descriptor: loads past M / N read 0, stores past them are
+    // dropped, so the only difference between a full tile and an edge tile
+    // is that the edge tile loads its operands and stores its results element
+    // by element (columns past N inside a row of ldc must not be touched).
     constexpr int ESZ = (OUT == OUT_I32) ? 4 : 2;
     const bool full = (rows_a == BM) && (rows_b == BN);
     const int nloc_base = wn * TN * 32 + 4 * h;
@@ -277,47 +287,43 @@ __device__ __forceinline__ void store_tile(const Params &p, Acc (&acc)[TM][TN], 
         if (full)
             lds_barrier();   // every wave is done with the operand buffers
     }
+    // Full tiles and edge tiles each get straight-line code.
+    auto body = [&](auto fullc) {
+        constexpr bool FULL = decltype(fullc)::value;
+        // Row scales of the lane's TM rows.
+        float sa[TM];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int mloc = arow + 32 * i;
-        const bool mok = mloc < rows_a;
-        float sa = 0.f;
-        if constexpr (OUT == OUT_BF16 && !MX) {
-            if (mok)
-                sa = p.scale_a[m0 + mloc];
+        for (int i = 0; i < TM; ++i) {
+            sa[i] = 0.f;
+            if constexpr (OUT == OUT_BF16 && !MX) {
+                const int mloc = arow + 32 * i;
+                if (PRM && FULL)
+                    sa[i] = *(const float *)(prm + 4 * mloc);
+                else if (mloc < rows_a)
+                    sa[i] = p.scale_a[m0 + mloc];
+            }
         }
-        const unsigned rowoff = (unsigned)((int64_t)mloc * p.ldc * ESZ);
+        // Column groups outermost: a group's scales and bias serve all TM rows.
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int nloc = nloc_base + 32 * j + 8 * g;
-                const unsigned off = rowoff + col0 + (unsigned)(nloc * ESZ);
-                if constexpr (OUT == OUT_I32) {
-                    const i32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1],
-                                     acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                    if (full) {
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rc, off, 0, 0);
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            __builtin_amdgcn_raw_buffer_store_b32(
-                                (unsigned)v[r], rc, (nloc + r < rows_b) ? off + 4 * r : OOB, 0, 0);
-                    }
-                } else {
-                    // Per-column scale and bias: one vector load in a full tile;
-                    // element loads at an edge (a vector load that runs past the
-                    // range returns zeros for all of its elements).
-                    float f[4];
-                    unsigned sbw[4], bbw[4];
-                    if (full) {
+                unsigned sbw[4] = {0, 0, 0, 0}, bbw[4] = {0, 0, 0, 0};
+                if constexpr (OUT == OUT_BF16) {
+                    // Per-column scale and bias: parked copies or one vector load
+                    // in a full tile; element loads at an edge (a vector load that
+                    // runs past the range returns zeros for all of its elements).
+                    if constexpr (FULL) {
                         if constexpr (!MX) {
-                            const u32x4 t = ld16(rsb_e, (unsigned)(nloc * 4));
+                            const u32x4 t = PRM ? *(const u32x4 *)(prm + PRM_SB + 4 * nloc)
+                                                : ld16(rsb_e, (unsigned)(nloc * 4));
 #pragma unroll
                             for (int r = 0; r < 4; ++r) sbw[r] = t[r];
                         }
                         if constexpr (BIAS) {
-                            const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(rbias, (unsigned)(nloc * 2), 0, 0);
+                            const u32x2 t = PRM ? *(const u32x2 *)(prm + PRM_BIAS + 2 * nloc)
+                                                : __builtin_amdgcn_raw_buffer_load_b64(rbias, (unsigned)(nloc * 2), 0, 0);
                             const unsigned t0 = t[0], t1 = t[1];
                             bbw[0] = t0 << 16;
                             bbw[1] = t0 & 0xffff0000u;
@@ -336,42 +342,65 @@ __device__ __forceinline__ void store_tile(const Params &p, Acc (&acc)[TM][TN], 
                                              rbias, in ? (unsigned)((nloc + r) * 2) : OOB, 0, 0) << 16;
                         }
                     }
+                }
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float x;
-                        if constexpr (PATH == PATH_I8)
-                            x = (float)acc[i][j][4 * g + r];
-                        else
-                            x = acc[i][j][4 * g + r];
-                        // (scalars only under bit_cast: clang's bit_cast of an
-                        // ext_vector element reads element 0)
-                        if constexpr (!MX) {
-                            x = x * sa;
-                            x = x * __builtin_bit_cast(float, sbw[r]);
+                for (int i = 0; i < TM; ++i) {
+                    const int mloc = arow + 32 * i;
+                    const unsigned off = (unsigned)((int64_t)mloc * p.ldc * ESZ) + col0 + (unsigned)(nloc * ESZ);
+                    if constexpr (OUT == OUT_I32) {
+                        const i32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1],
+                                         acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                        if constexpr (FULL) {
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rc, off, 0, 0);
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                __builtin_amdgcn_raw_buffer_store_b32(
+                                    (unsigned)v[r], rc, (nloc + r < rows_b) ? off + 4 * r : OOB, 0, 0);
                         }
-                        if constexpr (BIAS)
-                            x = x + __builtin_bit_cast(float, bbw[r]);
-                        f[r] = x;
-                    }
-                    const u32x2 v = {pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3])};
-                    if (full && !STASH) {
-                        __builtin_amdgcn_raw_buffer_store_b64(v, rc, off, 0, 0);
-                    } else if (full) {
-                        // park in this wave's LDS stash (written out below)
-                        const int srow = 32 * i + r32;
-                        const int chunk = 4 * j + g;
-                        *(u32x2 *)(stash + srow * SROWB + ((chunk ^ (srow & (SCHK - 1))) << 4) + 8 * h) = v;
                     } else {
+                        float f[4];
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            __builtin_amdgcn_raw_buffer_store_b16(
-                                (unsigned short)(v[r >> 1] >> (16 * (r & 1))), rc,
-                                (nloc + r < rows_b) ? off + 2 * r : OOB, 0, 0);
+                        for (int r = 0; r < 4; ++r) {
+                            float x;
+                            if constexpr (PATH == PATH_I8)
+                                x = (float)acc[i][j][4 * g + r];
+                            else
+                                x = acc[i][j][4 * g + r];
+                            // (scalars only under bit_cast: clang's bit_cast of an
+                            // ext_vector element reads element 0)
+                            if constexpr (!MX) {
+                                x = x * sa[i];
+                                x = x * __builtin_bit_cast(float, sbw[r]);
+                            }
+                            if constexpr (BIAS)
+                                x = x + __builtin_bit_cast(float, bbw[r]);
+                            f[r] = x;
+                        }
+                        const u32x2 v = {pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3])};
+                        if constexpr (FULL && !STASH) {
+                            __builtin_amdgcn_raw_buffer_store_b64(v, rc, off, 0, 0);
+                        } else if constexpr (FULL) {
+                            // park in this wave's LDS stash (written out below)
+                            const int srow = 32 * i + r32;
+                            const int chunk = 4 * j + g;
+                            *(u32x2 *)(stash + srow * SROWB + ((chunk ^ (srow & (SCHK - 1))) << 4) + 8 * h) = v;
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                __builtin_amdgcn_raw_buffer_store_b16(
+                                    (unsigned short)(v[r >> 1] >> (16 * (r & 1))), rc,
+                                    (nloc + r < rows_b) ? off + 2 * r : OOB, 0, 0);
+                        }
                     }
                 }
             }
         }
-    }
+    };
+    if (full)
+        body(std::true_type());
+    else
+        body(std::false_type());
     if constexpr (STASH) {
         if (full) {
             constexpr int LPR = SCHK;                   // lanes per stash row
@@ -404,6 +433,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) qgemm_kernel(const Params p)
     using Acc = typename AccT<PATH>::T;
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + BN) * KSTEP_BYTES];
+    constexpr bool PRM = OUT == OUT_BF16 && (!MX || BIAS);
+    __shared__ __attribute__((aligned(16))) uint8_t prm[PRM ? PRM_BYTES : 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -524,8 +555,29 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) qgemm_kernel(const Params p)
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    // Prologue: steps 0..RS-1 into the register sets, step 0 into LDS buffer
-    // 0, step RS into set 0, then the sub-step 0 fragments of step 0.
+    // Prologue: the tile's epilogue operands (one per thread, ahead of the
+    // operand loads), steps 0..RS-1 into the register sets, step 0 into LDS
+    // buffer 0, step RS into set 0, then the sub-step 0 fragments of step 0.
+    unsigned pv_sa = 0, pv_sb = 0;
+    unsigned short pv_bias = 0;
+    if constexpr (PRM) {
+        if (tid < BM) {
+            if constexpr (!MX) {
+                const __amdgpu_buffer_rsrc_t r = make_rsrc(p.scale_a + m0, (uint32_t)(rows_a * 4));
+                pv_sa = __builtin_amdgcn_raw_buffer_load_b32(r, tid < rows_a ? (unsigned)(4 * tid) : OOB, 0, 0);
+            }
+        }
+        if (tid < BN) {
+            if constexpr (!MX) {
+                const __amdgpu_buffer_rsrc_t r = make_rsrc(p.scale_b + n0, (uint32_t)(rows_b * 4));
+                pv_sb = __builtin_amdgcn_raw_buffer_load_b32(r, tid < rows_b ? (unsigned)(4 * tid) : OOB, 0, 0);
+            }
+            if constexpr (BIAS) {
+                const __amdgpu_buffer_rsrc_t r = make_rsrc(p.bias + n0, (uint32_t)(rows_b * 2));
+                pv_bias = __builtin_amdgcn_raw_buffer_load_b16(r, tid < rows_b ? (unsigned)(2 * tid) : OOB, 0, 0);
+            }
+        }
+    }
     load_step(0, I0());
     if constexpr (RS == 2)
         load_step(1, I1());
@@ -537,6 +589,16 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) qgemm_kernel(const Params p)
         for (int j = 0; j < TN; ++j) sb_use[j] = sb_ld[0][j];
     }
     load_step(RS, I0());
+    if constexpr (PRM) {
+        if (tid < BM && !MX)
+            *(unsigned *)(prm + 4 * tid) = pv_sa;
+        if (tid < BN) {
+            if constexpr (!MX)
+                *(unsigned *)(prm + PRM_SB + 4 * tid) = pv_sb;
+            if constexpr (BIAS)
+                *(unsigned short *)(prm + PRM_BIAS + 2 * tid) = pv_bias;
+        }
+    }
     lds_barrier();
     read_frags(I0(), 0, I0());
 
@@ -636,8 +698,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) qgemm_kernel(const Params p)
         kstep(kt + 1, I0(), std::true_type(), std::true_type(), std::true_type());
     }
 
-    store_tile<PATH, WM, WN, TM, TN, BIAS, OUT, 2 * (BM + BN) * KSTEP_BYTES>(p, acc, &lds[0][0], m0, n0, rows_a,
-                                                                      rows_b);
+    store_tile<PATH, WM, WN, TM, TN, BIAS, OUT, 2 * (BM + BN) * KSTEP_BYTES, PRM>(p, acc, &lds[0][0], prm, m0, n0,
+                                                                           rows_a, rows_b);
 }
 
 }  // namespace qgemm
