@@ -136,7 +136,9 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
                                                 (uint32_t)((rows_b - 1) * p.ldb + p.kbytes));
 
     // Fetch map: wave w's j-th A fetch covers rows 16*(4w+j) .. +15; lane i
-    // takes row +i/4 and the chunk that belongs in slot i%4.
+    // takes row +i/4 and the chunk that belongs in slot i%4.  A row past M / N
+    // gets offset OOB; OOB plus any K offset stays beyond the range (which is
+    // below 2^31), so its fetches read zeros without a per-fetch select.
     unsigned a_off[DMA_A], b_off[DMA_B];
 #pragma unroll
     for (int j = 0; j < DMA_A; ++j) {
@@ -156,10 +158,10 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
         const unsigned lb = lds0 + slot * STAGE_BYTES + BM * DSTAGE + 16 * DMA_B * wave * DSTAGE;
 #pragma unroll
         for (int j = 0; j < DMA_A; ++j)
-            dma16(ra, a_off[j] == OOB ? OOB : a_off[j] + kb, la + j * 16 * DSTAGE);
+            dma16(ra, a_off[j] + kb, la + j * 16 * DSTAGE);
 #pragma unroll
         for (int j = 0; j < DMA_B; ++j)
-            dma16(rb, b_off[j] == OOB ? OOB : b_off[j] + kb, lb + j * 16 * DSTAGE);
+            dma16(rb, b_off[j] + kb, lb + j * 16 * DSTAGE);
     };
 
     // MX scale chunks: chunk u holds 16 bytes of every scale row; e2m1 starts
@@ -181,8 +183,8 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
             const unsigned base = lds0 + OPND_BYTES + (u & 1) * SCL_BUF;
             // four stages of scales: 16 bytes (e2m1) or 8 bytes (e4m3) per row
             const unsigned kb = (unsigned)((PATH == PATH_MX4 ? 16 : 8) * u);
-            dma16(rsa, sa_fo == OOB ? OOB : sa_fo + kb, base + 64 * 16 * wave);
-            dma16(rsb, sb_fo == OOB ? OOB : sb_fo + kb, base + BM * 16 + (BROWS == 1 ? 64 * 16 * wave : 0));
+            dma16(rsa, sa_fo + kb, base + 64 * 16 * wave);
+            dma16(rsb, sb_fo + kb, base + BM * 16 + (BROWS == 1 ? 64 * 16 * wave : 0));
         }
     };
 
@@ -211,22 +213,26 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
         for (int j = 0; j < TN; ++j)
             fb[SET][j] = dma_frag<PATH, S>(tb, brow + 32 * j, h);
     };
-    // Scale words of stage t (J = t % 4) for this lane: byte S of the word is
-    // sub-step S's scale for the lane's block.
+    // Scale operand of stage t (J = t % 4) for this lane: byte S of it is
+    // sub-step S's scale for the lane's block -- e2m1: bytes 4J + 2h and
+    // 4J + 2h + 1 of the row's chunk (one 16-bit read); e4m3: byte 2J + h.
     auto read_scales = [&](int t, auto jc) {
         if constexpr (MX) {
             constexpr int J = decltype(jc)::value;
             const uint8_t *sbuf = &lds[OPND_BYTES + ((t >> 2) & 1) * SCL_BUF];
-            // e2m1: bytes 4J + 2h, +1;  e4m3: byte 2J + h
-            constexpr int WB = (PATH == PATH_MX4) ? 4 * J : (2 * J) & ~3;
-            const int sh = (PATH == PATH_MX4) ? 16 * h : 8 * (((2 * J) & 3) + h);
+            auto rd = [&](const uint8_t *row_base) -> unsigned {
+                if constexpr (PATH == PATH_MX4)
+                    return *(const unsigned short *)(row_base + 4 * J + 2 * h);
+                else
+                    return *(const unsigned char *)(row_base + 2 * J + h);
+            };
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                sa_nxt[i] = *(const unsigned *)(sbuf + (arow + 32 * i) * 16 + WB) >> sh;
+                sa_nxt[i] = rd(sbuf + (arow + 32 * i) * 16);
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int row = BROWS == 1 ? brow + 32 * j : wn * TN + j;
-                sb_nxt[j] = *(const unsigned *)(sbuf + BM * 16 + row * 16 + WB) >> sh;
+                sb_nxt[j] = rd(sbuf + BM * 16 + row * 16);
             }
         }
     };
