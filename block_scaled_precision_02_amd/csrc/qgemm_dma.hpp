@@ -9,10 +9,11 @@
 //    ahead of its use: the wave issues no LDS writes and holds no staging
 //    registers, and the fetch of stage t+3 overlaps the MFMAs of stages
 //    t..t+2.
-//  * The loads are issued from inline assembly so that the compiler does not
-//    add waits of its own for them; the kernel waits with s_waitcnt vmcnt(n),
-//    n counting the loads the wave issued after the stage it needs, then a
-//    barrier (every wave waited for its own share).
+//  * The kernel waits for a stage with s_waitcnt vmcnt(n), n counting the
+//    loads the wave issued after the stage it needs, then a barrier (every
+//    wave waited for its own share).  Fetches are spread between the MFMAs
+//    (a burst of them stalls the wave's instruction issue, and with it the
+//    matrix core, while the address unit works through them).
 //  * MX scales arrive the same way: 16 bytes of each scale row (the scales of
 //    four stages) per fetch, double-buffered, fetched four stages ahead; the
 //    scale words are read from LDS together with the fragments.
@@ -41,13 +42,15 @@ __device__ __forceinline__ int dlds_off(int r, int c)
     return r * DSTAGE + ((c ^ ((r >> 2) & 3)) << 4);
 }
 
-// One wave-wide 16-byte-per-lane fetch into LDS at lds_addr + 16 * lane.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned lds_addr)
+typedef __attribute__((address_space(3))) void *lds_ptr;
+
+// One wave-wide 16-byte-per-lane fetch into LDS at dst + 16 * lane (dst is
+// wave-uniform; it becomes M0).  The compiler sees a vector memory load, so
+// it can interleave fetches with the MFMAs; it inserts no wait for the LDS
+// data, which the kernel waits for itself (s_waitcnt vmcnt + barrier).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned voff, uint8_t *dst)
 {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(lds_addr), "v"(voff), "s"(r)
-                 : "memory");
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)dst, 16, voff, 0, 0, 0);
 }
 
 template <int N>
@@ -117,7 +120,6 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
     constexpr bool PRM = OUT == OUT_BF16 && (!MX || BIAS);
     constexpr int PRM_OFF = OPND_BYTES + SCL_BYTES;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[OPND_BYTES + SCL_BYTES + (PRM ? PRM_BYTES : 0)];
-    const unsigned lds0 = (unsigned)(uintptr_t)(&lds[0]);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -154,8 +156,8 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
     }
     auto fetch_stage = [&](int t, int slot) {
         const unsigned kb = (unsigned)(t * DSTAGE);
-        const unsigned la = lds0 + slot * STAGE_BYTES + 16 * DMA_A * wave * DSTAGE;
-        const unsigned lb = lds0 + slot * STAGE_BYTES + BM * DSTAGE + 16 * DMA_B * wave * DSTAGE;
+        uint8_t *la = &lds[slot * STAGE_BYTES + 16 * DMA_A * wave * DSTAGE];
+        uint8_t *lb = &lds[slot * STAGE_BYTES + BM * DSTAGE + 16 * DMA_B * wave * DSTAGE];
 #pragma unroll
         for (int j = 0; j < DMA_A; ++j)
             dma16(ra, a_off[j] + kb, la + j * 16 * DSTAGE);
@@ -180,7 +182,7 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
     }
     auto fetch_scales = [&](int u) {
         if constexpr (MX) {
-            const unsigned base = lds0 + OPND_BYTES + (u & 1) * SCL_BUF;
+            uint8_t *base = &lds[OPND_BYTES + (u & 1) * SCL_BUF];
             // four stages of scales: 16 bytes (e2m1) or 8 bytes (e4m3) per row
             const unsigned kb = (unsigned)((PATH == PATH_MX4 ? 16 : 8) * u);
             dma16(rsa, sa_fo + kb, base + 64 * 16 * wave);
@@ -206,12 +208,14 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
         constexpr int SET = decltype(setc)::value;
         const uint8_t *ta = &lds[slot * STAGE_BYTES];
         const uint8_t *tb = ta + BM * DSTAGE;
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-            fa[SET][i] = dma_frag<PATH, S>(ta, arow + 32 * i, h);
+        // in the order the serpentine MFMA sequence consumes them
+        fa[SET][0] = dma_frag<PATH, S>(ta, arow, h);
 #pragma unroll
         for (int j = 0; j < TN; ++j)
             fb[SET][j] = dma_frag<PATH, S>(tb, brow + 32 * j, h);
+#pragma unroll
+        for (int i = 1; i < TM; ++i)
+            fa[SET][i] = dma_frag<PATH, S>(ta, arow + 32 * i, h);
     };
     // Scale operand of stage t (J = t % 4) for this lane: byte S of it is
     // sub-step S's scale for the lane's block -- e2m1: bytes 4J + 2h and
@@ -261,11 +265,11 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
     // scale chunk 0, stages 0..2; wait for all but stages 1 and 2.
     if constexpr (PRM) {
         if (wave == 0 && !MX)
-            dma16(make_rsrc(p.scale_a + m0, (uint32_t)(rows_a * 4)), 16 * lane, lds0 + PRM_OFF);
+            dma16(make_rsrc(p.scale_a + m0, (uint32_t)(rows_a * 4)), 16 * lane, &lds[PRM_OFF]);
         if (wave == 1 && !MX)
-            dma16(make_rsrc(p.scale_b + n0, (uint32_t)(rows_b * 4)), 16 * lane, lds0 + PRM_OFF + PRM_SB);
+            dma16(make_rsrc(p.scale_b + n0, (uint32_t)(rows_b * 4)), 16 * lane, &lds[PRM_OFF + PRM_SB]);
         if (wave == 2 && BIAS)
-            dma16(make_rsrc(p.bias + n0, (uint32_t)(rows_b * 2)), 16 * lane, lds0 + PRM_OFF + PRM_BIAS);
+            dma16(make_rsrc(p.bias + n0, (uint32_t)(rows_b * 2)), 16 * lane, &lds[PRM_OFF + PRM_BIAS]);
     }
     fetch_scales(0);
     fetch_stage(0, 0);
@@ -292,16 +296,23 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
         if constexpr (NSUB == 2) {
             read_frags(I1(), J, I1());
             mfmas(I0(), I0(), I0(), std::integral_constant<int, NQ>());
-            // issue order: each MFMA followed by a share of the fragment reads
-            // (the fetches, inline assembly, keep their place ahead of them)
-            static_for<0, NQ>([&](auto qc) {
-                constexpr int Q = decltype(qc)::value;
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                constexpr int r = NDSR * (Q + 1) / NQ - NDSR * Q / NQ;
-                if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
-            });
         } else {
             mfmas(I0(), std::integral_constant<int, SET0>(), I0(), std::integral_constant<int, NQ / 2>());
+        }
+        // issue order: each MFMA followed by its share of the fetches and of
+        // the fragment reads
+        {
+            constexpr int NA = (NSUB == 2) ? NQ : NQ / 2;
+            constexpr int V = NDMA + (J == 0 ? NSCD : 0);
+            constexpr int R = (NSUB == 2) ? NDSR : 0;
+            static_for<0, NA>([&](auto qc) {
+                constexpr int Q = decltype(qc)::value;
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                constexpr int v = V * (Q + 1) / NA - V * Q / NA;
+                constexpr int r = R * (Q + 1) / NA - R * Q / NA;
+                if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);
+                if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+            });
         }
         // loads issued after stage t+1's: stages t+2 and t+3, plus the scale
         // chunk when it went out at stage t or t-1
