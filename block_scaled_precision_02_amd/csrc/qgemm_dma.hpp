@@ -112,6 +112,10 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
     constexpr int DMA_A = BM / 16 / 4, DMA_B = BN / 16 / 4; // fetches per wave per stage
     constexpr int NDMA = DMA_A + DMA_B;
     constexpr int NSCD = MX ? 2 : 0;                      // scale fetches per wave per chunk
+    // A rows of a stage are fetched one region earlier than its B rows
+    // (region B of the stage 4 back) except for MX, whose region B is busy
+    // with scale reads.
+    constexpr bool SPLIT = !MX;
     static_assert(DMA_A * 64 == BM && DMA_B * 64 == BN, "tile rows must be a multiple of 64");
     static_assert(BM == 256 && (BROWS == 1 ? BN == 256 : true), "one scale fetch per wave per operand");
     using Frag = typename PathTraits<PATH>::Frag;
@@ -154,16 +158,20 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
         const int c = (lane & 3) ^ ((r >> 2) & 3);
         b_off[j] = r < rows_b ? (unsigned)(r * p.ldb + 16 * c) : OOB;
     }
-    auto fetch_stage = [&](int t, int slot) {
+    // Stage t goes to slot t % 4, its A rows (part 0) and B rows (part 1)
+    // fetched separately.
+    auto fetch_part = [&](int t, auto partc) {
         const unsigned kb = (unsigned)(t * DSTAGE);
-        uint8_t *la = &lds[slot * STAGE_BYTES + 16 * DMA_A * wave * DSTAGE];
-        uint8_t *lb = &lds[slot * STAGE_BYTES + BM * DSTAGE + 16 * DMA_B * wave * DSTAGE];
+        uint8_t *slot = &lds[(t & 3) * STAGE_BYTES];
+        if constexpr (decltype(partc)::value == 0) {
 #pragma unroll
-        for (int j = 0; j < DMA_A; ++j)
-            dma16(ra, a_off[j] + kb, la + j * 16 * DSTAGE);
+            for (int j = 0; j < DMA_A; ++j)
+                dma16(ra, a_off[j] + kb, slot + (DMA_A * wave + j) * 16 * DSTAGE);
+        } else {
 #pragma unroll
-        for (int j = 0; j < DMA_B; ++j)
-            dma16(rb, b_off[j] + kb, lb + j * 16 * DSTAGE);
+            for (int j = 0; j < DMA_B; ++j)
+                dma16(rb, b_off[j] + kb, slot + BM * DSTAGE + (DMA_B * wave + j) * 16 * DSTAGE);
+        }
     };
 
     // MX scale chunks: chunk u holds 16 bytes of every scale row; e2m1 starts
@@ -259,10 +267,8 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
         }
     };
 
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
     // Prologue: the tile's epilogue operands (waves 0-2, one fetch each),
-    // scale chunk 0, stages 0..2; wait for all but stages 1 and 2.
+    // scale chunk 0, stages 0..2 and the A rows of stage 3; wait for stage 0.
     if constexpr (PRM) {
         if (wave == 0 && !MX)
             dma16(make_rsrc(p.scale_a + m0, (uint32_t)(rows_a * 4)), 16 * lane, &lds[PRM_OFF]);
@@ -271,28 +277,44 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
         if (wave == 2 && BIAS)
             dma16(make_rsrc(p.bias + n0, (uint32_t)(rows_b * 2)), 16 * lane, &lds[PRM_OFF + PRM_BIAS]);
     }
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    // (issue order is what the wait counts: no reordering across stages)
     fetch_scales(0);
-    fetch_stage(0, 0);
-    fetch_stage(1, 1);
-    fetch_stage(2, 2);
-    wait_vmcnt<2 * NDMA>();
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
+        fetch_part(t, I0());
+        fetch_part(t, I1());
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (SPLIT)
+        fetch_part(3, I0());
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<2 * NDMA + (SPLIT ? DMA_A : 0)>();
     lds_barrier();
     read_frags(I0(), 0, I0());
     read_scales(0, I0());
     use_next_scales();
 
-    // Stage t = 4q + J.  Region A: fetch scale chunk q+1 (J == 0) and stage
-    // t+3 into the slot stage t-1 used (free since the last barrier), read
-    // the fragments of the later sub-steps, multiply.  Then wait for stage
-    // t+1 -- the loads issued after it are those of stages t+2 and t+3 --
-    // and meet at the barrier; region B reads stage t+1's first fragments
-    // (and scale words) under the last sub-step's MFMAs.
+    // Stage t = 4q + J.  Region A: fetch scale chunk q+1 (J == 0) and the B
+    // rows (SPLIT) or all rows of stage t+3 into the slot stage t-1 used
+    // (free since the last barrier), read the fragments of the later
+    // sub-steps, multiply.  Then wait for stage t+1 -- the loads issued
+    // after it are those of stages t+2 and t+3 -- and meet at the barrier.
+    // Region B fetches the A rows of stage t+4 (SPLIT) into stage t's slot
+    // (its last reads were before the barrier) and reads stage t+1's first
+    // fragments (and scale words) under the last sub-step's MFMAs.  SPLIT
+    // starts a stage's fetches half a stage earlier and spreads them over
+    // both regions.
     auto stage = [&](int t, auto jc) {
         constexpr int J = decltype(jc)::value;
         constexpr int SET0 = (NSUB == 1) ? (J & 1) : 0;    // register set of sub-step 0
         if constexpr (J == 0)
             fetch_scales((t >> 2) + 1);
-        fetch_stage(t + 3, (J + 3) & 3);
+        if constexpr (!SPLIT)
+            fetch_part(t + 3, I0());
+        fetch_part(t + 3, I1());
         if constexpr (NSUB == 2) {
             read_frags(I1(), J, I1());
             mfmas(I0(), I0(), I0(), std::integral_constant<int, NQ>());
@@ -303,7 +325,7 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
         // the fragment reads
         {
             constexpr int NA = (NSUB == 2) ? NQ : NQ / 2;
-            constexpr int V = NDMA + (J == 0 ? NSCD : 0);
+            constexpr int V = (SPLIT ? DMA_B : NDMA) + (J == 0 ? NSCD : 0);
             constexpr int R = (NSUB == 2) ? NDSR : 0;
             static_for<0, NA>([&](auto qc) {
                 constexpr int Q = decltype(qc)::value;
@@ -322,6 +344,8 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
         lds_barrier();
         __builtin_amdgcn_sched_barrier(0);
         constexpr int SETN = (NSUB == 1) ? ((J + 1) & 1) : 0;
+        if constexpr (SPLIT)
+            fetch_part(t + 4, I0());
         read_frags(I0(), (J + 1) & 3, std::integral_constant<int, SETN>());
         read_scales(t + 1, std::integral_constant<int, (J + 1) & 3>());
         if constexpr (NSUB == 2) {
@@ -335,7 +359,10 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
         static_for<0, NB>([&](auto qc) {
             constexpr int Q = decltype(qc)::value;
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            constexpr int VB = SPLIT ? DMA_A : 0;
+            constexpr int v = VB * (Q + 1) / NB - VB * Q / NB;
             constexpr int r = RB * (Q + 1) / NB - RB * Q / NB;
+            if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);
             if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
         });
         use_next_scales();
