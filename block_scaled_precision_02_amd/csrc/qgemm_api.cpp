@@ -256,7 +256,7 @@ int pick_tile(int path, Shape s, int64_t kbytes, bool svec)
     int t = g_forced_tile >= 0 ? g_forced_tile : select_tile_impl(path, s.M, s.N);
     if (g_forced_tile < 0 && t == 0 && path >= 2 && dma_eligible(path, kbytes, s.K, svec))
         t = DMA_TILE;
-    if (t == DMA_TILE && !dma_eligible(path, kbytes, s.K, svec))
+    if (is_dma_tile(t) && !dma_eligible(path, kbytes, s.K, svec))
         t = 0;
     return t;
 }

@@ -91,10 +91,13 @@ __device__ __forceinline__ typename PathTraits<PATH>::Frag dma_frag(const uint8_
     return f;
 }
 
-template <int PATH, int TM, int TN, bool BIAS, int BROWS, int OUT>
-__global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
+// WN = 2: 4 waves (one per SIMD) of 128x128; WN = 4: 8 waves (two per
+// SIMD, so one can issue MFMAs while the other waits) of 128x64.
+template <int PATH, int WN, int TM, int TN, bool BIAS, int BROWS, int OUT>
+__global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
 {
-    constexpr int WM = 2, WN = 2;
+    constexpr int WM = 2;
+    constexpr int NW = WM * WN;                           // waves
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     constexpr int NSUB = DmaTraits<PATH>::NSUB;
     constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4);
@@ -109,14 +112,16 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
     constexpr int NQ = TM * TN;
     constexpr int RPF = (PATH == PATH_F8 || PATH == PATH_MX8) ? 2 : 1;
     constexpr int NDSR = (TM + TN) * RPF;                 // fragment reads per sub-step
-    constexpr int DMA_A = BM / 16 / 4, DMA_B = BN / 16 / 4; // fetches per wave per stage
+    constexpr int DMA_A = BM / 16 / NW, DMA_B = BN / 16 / NW; // fetches per wave per stage
     constexpr int NDMA = DMA_A + DMA_B;
-    constexpr int NSCD = MX ? 2 : 0;                      // scale fetches per wave per chunk
+    // scale fetches per wave per chunk: 4 waves fetch A and B scale rows,
+    // 8 waves split them (waves 0-3 A, 4-7 B)
+    constexpr int NSCD = MX ? 8 / NW : 0;
     // A rows of a stage are fetched one region earlier than its B rows
     // (region B of the stage 4 back) except for MX, whose region B is busy
     // with scale reads.
     constexpr bool SPLIT = !MX;
-    static_assert(DMA_A * 64 == BM && DMA_B * 64 == BN, "tile rows must be a multiple of 64");
+    static_assert(DMA_A * 16 * NW == BM && DMA_B * 16 * NW == BN, "tile rows must be a multiple of 16 per wave");
     static_assert(BM == 256 && (BROWS == 1 ? BN == 256 : true), "one scale fetch per wave per operand");
     using Frag = typename PathTraits<PATH>::Frag;
     using Acc = typename AccT<PATH>::T;
@@ -183,9 +188,10 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
         rsa = make_rsrc(p.mx_sa + (int64_t)m0 * p.kblocks, (uint32_t)(rows_a * p.kblocks));
         const int srows_b = BROWS == 1 ? rows_b : (rows_b + 31) / 32;
         rsb = make_rsrc(p.mx_sb + (int64_t)(n0 / BROWS) * p.kblocks, (uint32_t)(srows_b * p.kblocks));
-        const int ra_row = 64 * wave + lane;                       // A scale row of this lane
+        const int sw = NW == 8 ? (wave & 3) : wave;               // scale row group of this wave
+        const int ra_row = 64 * sw + lane;                         // A scale row of this lane
         sa_fo = ra_row < rows_a ? (unsigned)(ra_row * p.kblocks) : OOB;
-        const int rb_row = BROWS == 1 ? 64 * wave + lane : lane;   // 32x32: every wave fetches rows 0..63
+        const int rb_row = BROWS == 1 ? 64 * sw + lane : lane;     // 32x32: rows 0..63, fetched alike by every wave
         sb_fo = rb_row < srows_b ? (unsigned)(rb_row * p.kblocks) : OOB;
     }
     auto fetch_scales = [&](int u) {
@@ -193,8 +199,14 @@ __global__ void __launch_bounds__(256, 1) qgemm_dma_kernel(const Params p)
             uint8_t *base = &lds[OPND_BYTES + (u & 1) * SCL_BUF];
             // four stages of scales: 16 bytes (e2m1) or 8 bytes (e4m3) per row
             const unsigned kb = (unsigned)((PATH == PATH_MX4 ? 16 : 8) * u);
-            dma16(rsa, sa_fo + kb, base + 64 * 16 * wave);
-            dma16(rsb, sb_fo + kb, base + BM * 16 + (BROWS == 1 ? 64 * 16 * wave : 0));
+            if constexpr (NW == 4) {
+                dma16(rsa, sa_fo + kb, base + 64 * 16 * wave);
+                dma16(rsb, sb_fo + kb, base + BM * 16 + (BROWS == 1 ? 64 * 16 * wave : 0));
+            } else if (wave < 4) {
+                dma16(rsa, sa_fo + kb, base + 64 * 16 * wave);
+            } else {
+                dma16(rsb, sb_fo + kb, base + BM * 16 + (BROWS == 1 ? 64 * 16 * (wave - 4) : 0));
+            }
         }
     };
 

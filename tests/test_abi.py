@@ -134,9 +134,9 @@ def test_tile_table():
     # 144 tiles of 256x256 leave 112 CUs idle; 242 tiles of 192x192 fill one round
     assert L.qgemm_select_tile(1, 4096, 2112, 7168) == 3
     assert L.qgemm_select_tile(7, 64, 64, 64) == -1
-    for t, e in ((0, 256), (1, 128), (2, 256), (3, 192), (4, 256)):
+    for t, e in ((0, 256), (1, 128), (2, 256), (3, 192), (4, 256), (5, 256)):
         assert L.qgemm_tile_rows(t) == e
-    assert L.qgemm_tile_rows(5) == 0 and L.qgemm_tile_rows(-1) == 0
+    assert L.qgemm_tile_rows(6) == 0 and L.qgemm_tile_rows(-1) == 0
     assert L.qgemm_force_tile(9) == -2
     assert L.qgemm_force_tile(1) == -1
     assert L.qgemm_force_tile(-1) == 1

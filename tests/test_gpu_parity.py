@@ -46,7 +46,7 @@ def _full_check(d, what, tile=None):
 # ------------------------------------------------------------------ INT8
 
 @pytest.mark.parametrize("bias", [True, False])
-@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5])
 def test_i8_small_workload(bias, tile):
     d = inputs.make("i8_small", bias=bias)
     _full_check(d, f"i8_small bias={bias}", tile)
@@ -55,7 +55,7 @@ def test_i8_small_workload(bias, tile):
 def test_i8_accumulator_exact():
     d = inputs.make("i8_small")
     A, B = parity.dev(d["A"]), parity.dev(d["B"])
-    for tile in (0, 1, 2, 3, 4):
+    for tile in (0, 1, 2, 3, 4, 5):
         q.force_tile(tile)
         acc = q.qgemm_i8_acc_i32(A, B)
         torch.cuda.synchronize()
@@ -193,16 +193,18 @@ def test_mx_random_scales_repeated(name):
 @pytest.mark.parametrize("name", ["i8_small", "f8_ptpc", "mxfp8", "mxfp4"])
 def test_tile_variants_identical(name):
     """Tiles 0-3 run each output's accumulation as the same sequence of MFMAs,
-    so they agree bit for bit; the LDS-fetch kernel (tile 4) groups K blocks
-    into MFMAs differently, so it is bit-identical for INT8 and within the
-    tolerance for FP8 / MX."""
+    so they agree bit for bit; the LDS-fetch kernels (tiles 4 and 5) group K
+    blocks into MFMAs differently, so they are bit-identical for INT8 and
+    within the tolerance for FP8 / MX (and identical to each other: their
+    per-output MFMA sequences match)."""
     d = inputs.make(name, M=300, N=280, K=512)
     outs = []
-    for tile in (0, 1, 2, 3, 4):
+    for tile in (0, 1, 2, 3, 4, 5):
         q.force_tile(tile)
         outs.append(parity.bits(parity.gpu_run(d)))
     for t in (1, 2, 3):
         assert np.array_equal(outs[0], outs[t]), f"tile {t}"
+    assert np.array_equal(outs[4], outs[5]), "tiles 4 and 5"
     if d["kind"] == "i8":
         assert np.array_equal(outs[0], outs[4])
     else:
@@ -213,14 +215,15 @@ def test_tile_variants_identical(name):
 DMA_SHAPES = [(1, 1, 256), (17, 33, 512), (255, 257, 1024), (300, 520, 2048), (513, 64, 256)]
 
 
+@pytest.mark.parametrize("tile", [4, 5])
 @pytest.mark.parametrize("name", ["i8_small", "f8_ptpc", "mxfp8", "mxfp4"])
 @pytest.mark.parametrize("M,N,K", DMA_SHAPES)
-def test_dma_kernel_edges(name, M, N, K):
-    """The LDS-fetch kernel on ragged M / N, NaN-filled output with canaries
-    beyond N and M (K a whole number of its stages)."""
+def test_dma_kernel_edges(name, M, N, K, tile):
+    """The LDS-fetch kernels on ragged M / N, NaN-filled output with canaries
+    beyond N and M (K a whole number of their stages)."""
     kk = K if name != "mxfp4" else 2 * K      # e2m1: K elements are K/2 bytes
     d = inputs.make(name, M=M, N=N, K=kk, bias=(M % 2 == 1))
-    q.force_tile(4)
+    q.force_tile(tile)
     ldc = N + (-N) % 8 + 8
     buf = torch.full((M + 3, ldc), float("nan"), dtype=torch.bfloat16, device="cuda")
     before = parity.bits(buf)
@@ -232,8 +235,9 @@ def test_dma_kernel_edges(name, M, N, K):
     assert np.array_equal(after[M:], before[M:]), "wrote past M"
 
 
+@pytest.mark.parametrize("tile", [4, 5])
 @pytest.mark.parametrize("name", ["mxfp8", "mxfp4"])
-def test_dma_kernel_other_b_layout_and_random_scales(name):
+def test_dma_kernel_other_b_layout_and_random_scales(name, tile):
     rng = np.random.default_rng(78)
     d = inputs.make(name, M=260, N=300, K=1024)
     fmt = d["fmt"]
@@ -243,7 +247,7 @@ def test_dma_kernel_other_b_layout_and_random_scales(name):
         cb = inputs.pack_e2m1(cb)
     d = dict(d, B=cb, scale_b=sb, b_rows_per_scale=brows,
              scale_a=rng.integers(118, 136, d["scale_a"].shape, dtype=np.uint8))
-    q.force_tile(4)
+    q.force_tile(tile)
     ref, absdot, _ = parity.oracle_run(d)
     first = None
     for it in range(6):
@@ -255,11 +259,12 @@ def test_dma_kernel_other_b_layout_and_random_scales(name):
             assert np.array_equal(got, first), f"launch {it} differs"
 
 
-def test_dma_tile_falls_back_when_k_does_not_fit():
+@pytest.mark.parametrize("tile", [4, 5])
+def test_dma_tile_falls_back_when_k_does_not_fit(tile):
     d = inputs.make("i8_small", M=100, N=70, K=96)
-    q.force_tile(4)
+    q.force_tile(tile)
     ref, _, _ = parity.oracle_run(d)
-    parity.compare(d, parity.bits(parity.gpu_run(d)), ref, None, "tile 4 fallback K=96")
+    parity.compare(d, parity.bits(parity.gpu_run(d)), ref, None, f"tile {tile} fallback K=96")
 
 
 def test_non_default_stream():
@@ -281,7 +286,7 @@ def _sample_rows(M, n, rng):
     return np.unique(np.concatenate([head, mid, tail]))
 
 
-@pytest.mark.parametrize("tile", [-1, 4])
+@pytest.mark.parametrize("tile", [-1, 4, 5])
 @pytest.mark.parametrize("name", ["f8_ptpc", "mxfp8", "mxfp4", "i8_qkv"])
 def test_full_workload_sampled(name, tile):
     """The workload at its full size, launched as the benchmark launches it;
