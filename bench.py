@@ -96,20 +96,68 @@ def upload(d):
     return t
 
 
+KERNEL_SOURCES = "block_scaled_precision_02_amd/csrc"
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_digest():
+    """sha256 over every kernel source file (name and bytes, sorted by name)."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, KERNEL_SOURCES)
+    for n in sorted(os.listdir(d)):
+        if n.endswith((".hip", ".hpp", ".cpp", ".h")):
+            h.update(n.encode())
+            h.update(open(os.path.join(d, n), "rb").read())
+    return h.hexdigest()
+
+
 def traffic_bytes(name):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     summary, already scaled by the copy-kernel factors; None when the kernel
-    source has changed since those counters were taken."""
-    import hashlib
+    sources have changed since those counters were taken."""
     try:
-        t = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
-        src = open(os.path.join(ROOT, t["kernel_source"]), "rb").read()
-    except (OSError, ValueError, KeyError):
+        t = json.load(open(TRAFFIC_JSON))
+    except (OSError, ValueError):
         return None
-    if hashlib.sha256(src).hexdigest() != t.get("kernel_sha256"):
+    if t.get("kernel_sha256") != kernel_digest():
         return None
     w = t.get("workloads", {}).get(name)
     return None if w is None else w["fetch_bytes"] + w["write_bytes"]
+
+
+def _counter_per_dispatch(csv_path, counter, kernel_substr):
+    import csv
+    import collections
+    agg = collections.defaultdict(float)
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]:
+            agg[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    return [agg[d] for d in sorted(agg)]
+
+
+def write_traffic(prof_dir, workloads, out_path=TRAFFIC_JSON):
+    """Build profiles/traffic.json from rocprofv3 --pmc runs laid out as
+    <prof_dir>/{fetch,write}_<name>/run_counter_collection.csv, <name> being
+    each workload and "copy" (bench.py --copy-bytes 1 GiB, the calibration).
+    Counters are KiB per dispatch; the timed dispatches are all but the first
+    (warmup) one of each run; the copy factor is 1 GiB over what the counter
+    reads for the copy."""
+    out = {"kernel_sources": KERNEL_SOURCES, "kernel_sha256": kernel_digest(), "copy_factor": {},
+           "workloads": {}, "unit": "bytes per launch"}
+    for what, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        copy = _counter_per_dispatch(os.path.join(prof_dir, f"{what}_copy", "run_counter_collection.csv"),
+                                     counter, "copyBuffer")
+        factor = float(1 << 30) / (copy[-1] * 1024.0)
+        out["copy_factor"][counter] = round(factor, 4)
+        for name in workloads:
+            v = _counter_per_dispatch(os.path.join(prof_dir, f"{what}_{name}", "run_counter_collection.csv"),
+                                      counter, "qgemm")
+            v = v[1:] if len(v) > 1 else v
+            out["workloads"].setdefault(name, {})[f"{what}_bytes"] = round(sum(v) / len(v) * 1024.0 * factor)
+    with open(out_path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    return out
 
 
 def cpu_baseline(d, target_s):
@@ -146,7 +194,13 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead: time a plain device copy of this many bytes (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--traffic-from", default=None, metavar="DIR",
+                    help="instead: write profiles/traffic.json from the rocprofv3 FETCH_SIZE / "
+                         "WRITE_SIZE runs under DIR (no GPU needed)")
     args = ap.parse_args()
+    if args.traffic_from:
+        print(json.dumps(write_traffic(args.traffic_from, ["i8_qkv", "mxfp4"])))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this GEMM library has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)

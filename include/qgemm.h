@@ -141,11 +141,15 @@ const char *qgemm_status_string(qgemm_status status);
 
 /* Tile variant the host-side table picks for a problem (pure host logic, no
  * HIP call; for MX, assuming 16-byte-aligned scale arrays).  path: 0 int8,
- * 1 fp8, 2 MX e4m3, 3 MX e2m1.  Returns the tile id
- * (0: 256x256 with 4 waves, 1: 128x128, 2: 256x256 with 8 waves, 3: 192x192,
- * 4: 256x256 with operands fetched straight into LDS, used when K bytes are a
- * multiple of 256 and MX scale rows a multiple of 16 bytes, else tile 0),
- * or -1 for a bad path. */
+ * 1 fp8, 2 MX e4m3, 3 MX e2m1.  Returns the tile id, or -1 for a bad path:
+ *   0: 256x256, 4 waves, operands staged through registers
+ *   1: 128x128    2: 256x256 with 8 waves, staged through registers
+ *   3: 192x192
+ *   4: 256x256, 4 waves, operands fetched straight into LDS
+ *   5: 256x256, 8 waves, operands fetched straight into LDS
+ * Tiles 4 and 5 need K bytes a multiple of 256 and MX scale rows a multiple
+ * of 16 bytes; where the table's choice is 256x256 and these hold, it runs
+ * as tile 5. */
 int qgemm_select_tile(int path, int64_t M, int64_t N, int64_t K);
 
 /* Block edge (rows of A = rows of B) of a tile id, or 0 for an unknown id. */
@@ -153,7 +157,8 @@ int qgemm_tile_rows(int tile);
 
 /* Force a tile id for later calls on the calling thread (benchmarks and the
  * variant-equivalence tests); -1 restores the table.  Returns the previous
- * value, or -2 (and changes nothing) for an unknown id. */
+ * value, or -2 (and changes nothing) for an unknown id.  A forced LDS-fetch
+ * tile whose requirements a call does not meet runs as tile 0. */
 int qgemm_force_tile(int tile);
 
 #ifdef __cplusplus

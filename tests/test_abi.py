@@ -125,11 +125,12 @@ def test_fake_arch_refused_before_any_hip_call(monkeypatch):
 
 def test_tile_table():
     L = q.lib()
-    # full rounds of 256x256 tiles keep the big tile
-    assert L.qgemm_select_tile(0, 30000, 21504, 5376) == 0      # 9912 tiles
-    # MX on 256x256 tiles takes the LDS-fetch kernel when K fits its stages
-    assert L.qgemm_select_tile(3, 8192, 8192, 8192) == 4        # 1024 tiles = 4 rounds
-    assert L.qgemm_select_tile(2, 16384, 7168, 2048) == 4       # 1792 tiles = 7 rounds
+    # full rounds of 256x256 tiles keep the big tile, run by the eight-wave
+    # LDS-fetch kernel when K fits its stages
+    assert L.qgemm_select_tile(0, 30000, 21504, 5376) == 5      # 9912 tiles
+    assert L.qgemm_select_tile(0, 30000, 21504, 5408) == 0      # K bytes not a multiple of 256
+    assert L.qgemm_select_tile(3, 8192, 8192, 8192) == 5        # 1024 tiles = 4 rounds
+    assert L.qgemm_select_tile(2, 16384, 7168, 2048) == 5       # 1792 tiles = 7 rounds
     assert L.qgemm_select_tile(2, 16384, 7168, 2016) == 0       # K/32 = 63: not whole chunks
     # 144 tiles of 256x256 leave 112 CUs idle; 242 tiles of 192x192 fill one round
     assert L.qgemm_select_tile(1, 4096, 2112, 7168) == 3
