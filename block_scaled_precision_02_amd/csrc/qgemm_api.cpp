@@ -236,9 +236,9 @@ qgemm_status finish(hipError_t e)
     return QGEMM_OK;
 }
 
-// The LDS-fetch kernels (tiles 4 and 5) run 256x256 tiles whose K is a whole
-// number of their 4 x 64-byte stages and, for MX, whose scale rows are whole
-// 16-byte chunks (the caller's scale arrays then also load in aligned words).
+// The LDS-fetch kernels (tiles 4-7) run tiles whose K is a whole number of
+// their 4 x 64-byte stages and, for MX, whose scale rows are whole 16-byte
+// chunks (the caller's scale arrays then also load in aligned words).
 bool dma_eligible(int path, int64_t kbytes, int64_t K, bool svec)
 {
     if (kbytes % 256)
@@ -248,15 +248,16 @@ bool dma_eligible(int path, int64_t kbytes, int64_t K, bool svec)
     return true;
 }
 
-// Where the table picks a 256x256 tile, the eight-wave LDS-fetch kernel runs
-// it when K fits (one MI355X, same box: INT8 30000x21504x5376 2155 TOPS vs
+// When K fits, the table's tile edge runs in an LDS-fetch kernel: 256 as the
+// eight-wave kernel (one MI355X, same box: INT8 30000x21504x5376 2155 TOPS vs
 // 2130 for the four-wave LDS-fetch kernel and ~2100 for register staging;
-// MXFP4 8192^3 3756 vs 3668 TFLOPS; MXFP8 16384x7168x2048 1940 vs 1933).
+// MXFP4 8192^3 3756 vs 3668 TFLOPS; MXFP8 16384x7168x2048 1940 vs 1933), 192
+// and 128 as their four-wave LDS-fetch forms.
 int pick_tile(int path, Shape s, int64_t kbytes, bool svec)
 {
     int t = g_forced_tile >= 0 ? g_forced_tile : select_tile_impl(path, s.M, s.N);
-    if (g_forced_tile < 0 && t == 0 && dma_eligible(path, kbytes, s.K, svec))
-        t = DMA8_TILE;
+    if (g_forced_tile < 0 && dma_eligible(path, kbytes, s.K, svec))
+        t = (t == 0) ? DMA8_TILE : (t == 3) ? DMA192_TILE : (t == 1) ? DMA128_TILE : t;
     if (is_dma_tile(t) && !dma_eligible(path, kbytes, s.K, svec))
         t = 0;
     return t;

@@ -103,11 +103,12 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4);
     constexpr int STAGE_BYTES = (BM + BN) * DSTAGE;
     constexpr int OPND_BYTES = DNST * STAGE_BYTES;
-    // MX scale chunks: per buffer, BM rows of A and 64 rows of B (32x32
-    // layout: BN/32 valid rows; the rest of the 64 absorb the fetch's spare
-    // lanes) or BN rows (1x32), 16 bytes each.
-    constexpr int SB_ROWS = (BROWS == 1) ? BN : 64;
-    constexpr int SCL_BUF = (BM + SB_ROWS) * 16;
+    // MX scale chunks: per buffer, 256 rows of A and 256 rows of B (1x32) or
+    // 64 (32x32 layout: BN/32 valid rows), 16 bytes each -- what four fetches
+    // of 64 rows cover; rows past the tile read zeros and are never used.
+    constexpr int SA_ROWS = 256;
+    constexpr int SB_ROWS = (BROWS == 1) ? 256 : 64;
+    constexpr int SCL_BUF = (SA_ROWS + SB_ROWS) * 16;
     constexpr int SCL_BYTES = MX ? 2 * SCL_BUF : 0;
     constexpr int NQ = TM * TN;
     constexpr int RPF = (PATH == PATH_F8 || PATH == PATH_MX8) ? 2 : 1;
@@ -122,7 +123,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // with scale reads.
     constexpr bool SPLIT = !MX;
     static_assert(DMA_A * 16 * NW == BM && DMA_B * 16 * NW == BN, "tile rows must be a multiple of 16 per wave");
-    static_assert(BM == 256 && (BROWS == 1 ? BN == 256 : true), "one scale fetch per wave per operand");
+    static_assert(BM <= SA_ROWS && (BROWS == 1 ? BN <= SB_ROWS : BN / 32 <= SB_ROWS), "scale rows per buffer");
     using Frag = typename PathTraits<PATH>::Frag;
     using Acc = typename AccT<PATH>::T;
 
@@ -201,11 +202,11 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             const unsigned kb = (unsigned)((PATH == PATH_MX4 ? 16 : 8) * u);
             if constexpr (NW == 4) {
                 dma16(rsa, sa_fo + kb, base + 64 * 16 * wave);
-                dma16(rsb, sb_fo + kb, base + BM * 16 + (BROWS == 1 ? 64 * 16 * wave : 0));
+                dma16(rsb, sb_fo + kb, base + SA_ROWS * 16 + (BROWS == 1 ? 64 * 16 * wave : 0));
             } else if (wave < 4) {
                 dma16(rsa, sa_fo + kb, base + 64 * 16 * wave);
             } else {
-                dma16(rsb, sb_fo + kb, base + BM * 16 + (BROWS == 1 ? 64 * 16 * (wave - 4) : 0));
+                dma16(rsb, sb_fo + kb, base + SA_ROWS * 16 + (BROWS == 1 ? 64 * 16 * (wave - 4) : 0));
             }
         }
     };
@@ -256,7 +257,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int row = BROWS == 1 ? brow + 32 * j : wn * TN + j;
-                sb_nxt[j] = rd(sbuf + BM * 16 + row * 16);
+                sb_nxt[j] = rd(sbuf + SA_ROWS * 16 + row * 16);
             }
         }
     };

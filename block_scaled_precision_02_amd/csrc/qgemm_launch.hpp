@@ -14,10 +14,15 @@ namespace qgemm {
 //        needs K bytes % 256 == 0 and, for MX, K/32 % 16 == 0 with aligned scales
 //   5 -> 256x256 fetched straight into LDS as tile 4, 2x4 waves of 128x64 (two
 //        waves per SIMD); same requirements
-constexpr int NUM_TILES = 6;
-constexpr int DMA_TILE = 4, DMA8_TILE = 5;
-__host__ __device__ constexpr bool is_dma_tile(int tile) { return tile == DMA_TILE || tile == DMA8_TILE; }
-__host__ __device__ constexpr int tile_edge(int tile) { return tile == 1 ? 128 : (tile == 3 ? 192 : 256); }
+//   6 -> 192x192 fetched straight into LDS, 2x2 waves of 96x96; same requirements
+//   7 -> 128x128 fetched straight into LDS, 2x2 waves of 64x64; same requirements
+constexpr int NUM_TILES = 8;
+constexpr int DMA_TILE = 4, DMA8_TILE = 5, DMA192_TILE = 6, DMA128_TILE = 7;
+__host__ __device__ constexpr bool is_dma_tile(int tile) { return tile >= DMA_TILE && tile <= DMA128_TILE; }
+__host__ __device__ constexpr int tile_edge(int tile)
+{
+    return (tile == 1 || tile == DMA128_TILE) ? 128 : ((tile == 3 || tile == DMA192_TILE) ? 192 : 256);
+}
 __host__ __device__ constexpr int tile_threads(int tile) { return (tile == 2 || tile == DMA8_TILE) ? 512 : 256; }
 
 template <int PATH, int WM, int WN, int TM, int TN, bool BIAS, int BROWS, bool SVEC, int OUT>
@@ -38,6 +43,8 @@ hipError_t launch_tile(int tile, const Params &p, hipStream_t s)
     case 3: return launch_variant<PATH, 2, 2, 3, 3, BIAS, BROWS, SVEC, OUT>(p, s);
     case DMA_TILE:
     case DMA8_TILE:
+    case DMA192_TILE:
+    case DMA128_TILE:
         if constexpr (PATH == PATH_MX8 || PATH == PATH_MX4) {
             if (!SVEC)
                 return hipErrorInvalidValue;
@@ -46,8 +53,12 @@ hipError_t launch_tile(int tile, const Params &p, hipStream_t s)
             const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(tile_threads(tile));
             if (tile == DMA_TILE)
                 hipLaunchKernelGGL((qgemm_dma_kernel<PATH, 2, 4, 4, BIAS, BROWS, OUT>), grid, block, 0, s, p);
-            else
+            else if (tile == DMA8_TILE)
                 hipLaunchKernelGGL((qgemm_dma_kernel<PATH, 4, 4, 2, BIAS, BROWS, OUT>), grid, block, 0, s, p);
+            else if (tile == DMA192_TILE)
+                hipLaunchKernelGGL((qgemm_dma_kernel<PATH, 2, 3, 3, BIAS, BROWS, OUT>), grid, block, 0, s, p);
+            else
+                hipLaunchKernelGGL((qgemm_dma_kernel<PATH, 2, 2, 2, BIAS, BROWS, OUT>), grid, block, 0, s, p);
             return hipGetLastError();
         }
     default: return hipErrorInvalidValue;

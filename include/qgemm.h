@@ -147,9 +147,11 @@ const char *qgemm_status_string(qgemm_status status);
  *   3: 192x192
  *   4: 256x256, 4 waves, operands fetched straight into LDS
  *   5: 256x256, 8 waves, operands fetched straight into LDS
- * Tiles 4 and 5 need K bytes a multiple of 256 and MX scale rows a multiple
- * of 16 bytes; where the table's choice is 256x256 and these hold, it runs
- * as tile 5. */
+ *   6: 192x192, 4 waves, operands fetched straight into LDS
+ *   7: 128x128, 4 waves, operands fetched straight into LDS
+ * Tiles 4-7 need K bytes a multiple of 256 and MX scale rows a multiple of
+ * 16 bytes; where these hold, the table's 256x256 choice runs as tile 5,
+ * 192x192 as tile 6 and 128x128 as tile 7. */
 int qgemm_select_tile(int path, int64_t M, int64_t N, int64_t K);
 
 /* Block edge (rows of A = rows of B) of a tile id, or 0 for an unknown id. */

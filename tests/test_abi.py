@@ -132,12 +132,14 @@ def test_tile_table():
     assert L.qgemm_select_tile(3, 8192, 8192, 8192) == 5        # 1024 tiles = 4 rounds
     assert L.qgemm_select_tile(2, 16384, 7168, 2048) == 5       # 1792 tiles = 7 rounds
     assert L.qgemm_select_tile(2, 16384, 7168, 2016) == 0       # K/32 = 63: not whole chunks
-    # 144 tiles of 256x256 leave 112 CUs idle; 242 tiles of 192x192 fill one round
-    assert L.qgemm_select_tile(1, 4096, 2112, 7168) == 3
+    # 144 tiles of 256x256 leave 112 CUs idle; 242 tiles of 192x192 fill one
+    # round (LDS-fetch form when K fits, register-staged otherwise)
+    assert L.qgemm_select_tile(1, 4096, 2112, 7168) == 6
+    assert L.qgemm_select_tile(1, 4096, 2112, 7200) == 3
     assert L.qgemm_select_tile(7, 64, 64, 64) == -1
-    for t, e in ((0, 256), (1, 128), (2, 256), (3, 192), (4, 256), (5, 256)):
+    for t, e in ((0, 256), (1, 128), (2, 256), (3, 192), (4, 256), (5, 256), (6, 192), (7, 128)):
         assert L.qgemm_tile_rows(t) == e
-    assert L.qgemm_tile_rows(6) == 0 and L.qgemm_tile_rows(-1) == 0
+    assert L.qgemm_tile_rows(8) == 0 and L.qgemm_tile_rows(-1) == 0
     assert L.qgemm_force_tile(9) == -2
     assert L.qgemm_force_tile(1) == -1
     assert L.qgemm_force_tile(-1) == 1

@@ -46,7 +46,7 @@ def _full_check(d, what, tile=None):
 # ------------------------------------------------------------------ INT8
 
 @pytest.mark.parametrize("bias", [True, False])
-@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6, 7])
 def test_i8_small_workload(bias, tile):
     d = inputs.make("i8_small", bias=bias)
     _full_check(d, f"i8_small bias={bias}", tile)
@@ -55,7 +55,7 @@ def test_i8_small_workload(bias, tile):
 def test_i8_accumulator_exact():
     d = inputs.make("i8_small")
     A, B = parity.dev(d["A"]), parity.dev(d["B"])
-    for tile in (0, 1, 2, 3, 4, 5):
+    for tile in (0, 1, 2, 3, 4, 5, 6, 7):
         q.force_tile(tile)
         acc = q.qgemm_i8_acc_i32(A, B)
         torch.cuda.synchronize()
@@ -193,18 +193,19 @@ def test_mx_random_scales_repeated(name):
 @pytest.mark.parametrize("name", ["i8_small", "f8_ptpc", "mxfp8", "mxfp4"])
 def test_tile_variants_identical(name):
     """Tiles 0-3 run each output's accumulation as the same sequence of MFMAs,
-    so they agree bit for bit; the LDS-fetch kernels (tiles 4 and 5) group K
+    so they agree bit for bit; the LDS-fetch kernels (tiles 4-7) group K
     blocks into MFMAs differently, so they are bit-identical for INT8 and
     within the tolerance for FP8 / MX (and identical to each other: their
     per-output MFMA sequences match)."""
     d = inputs.make(name, M=300, N=280, K=512)
     outs = []
-    for tile in (0, 1, 2, 3, 4, 5):
+    for tile in (0, 1, 2, 3, 4, 5, 6, 7):
         q.force_tile(tile)
         outs.append(parity.bits(parity.gpu_run(d)))
     for t in (1, 2, 3):
         assert np.array_equal(outs[0], outs[t]), f"tile {t}"
-    assert np.array_equal(outs[4], outs[5]), "tiles 4 and 5"
+    for t in (5, 6, 7):
+        assert np.array_equal(outs[4], outs[t]), f"tiles 4 and {t}"
     if d["kind"] == "i8":
         assert np.array_equal(outs[0], outs[4])
     else:
@@ -215,7 +216,7 @@ def test_tile_variants_identical(name):
 DMA_SHAPES = [(1, 1, 256), (17, 33, 512), (255, 257, 1024), (300, 520, 2048), (513, 64, 256)]
 
 
-@pytest.mark.parametrize("tile", [4, 5])
+@pytest.mark.parametrize("tile", [4, 5, 6, 7])
 @pytest.mark.parametrize("name", ["i8_small", "f8_ptpc", "mxfp8", "mxfp4"])
 @pytest.mark.parametrize("M,N,K", DMA_SHAPES)
 def test_dma_kernel_edges(name, M, N, K, tile):
@@ -235,7 +236,7 @@ def test_dma_kernel_edges(name, M, N, K, tile):
     assert np.array_equal(after[M:], before[M:]), "wrote past M"
 
 
-@pytest.mark.parametrize("tile", [4, 5])
+@pytest.mark.parametrize("tile", [4, 5, 6, 7])
 @pytest.mark.parametrize("name", ["mxfp8", "mxfp4"])
 def test_dma_kernel_other_b_layout_and_random_scales(name, tile):
     rng = np.random.default_rng(78)
@@ -259,7 +260,7 @@ def test_dma_kernel_other_b_layout_and_random_scales(name, tile):
             assert np.array_equal(got, first), f"launch {it} differs"
 
 
-@pytest.mark.parametrize("tile", [4, 5])
+@pytest.mark.parametrize("tile", [4, 5, 6, 7])
 def test_dma_tile_falls_back_when_k_does_not_fit(tile):
     d = inputs.make("i8_small", M=100, N=70, K=96)
     q.force_tile(tile)
@@ -286,7 +287,7 @@ def _sample_rows(M, n, rng):
     return np.unique(np.concatenate([head, mid, tail]))
 
 
-@pytest.mark.parametrize("tile", [-1, 4, 5])
+@pytest.mark.parametrize("tile", [-1, 4, 5, 6])
 @pytest.mark.parametrize("name", ["f8_ptpc", "mxfp8", "mxfp4", "i8_qkv"])
 def test_full_workload_sampled(name, tile):
     """The workload at its full size, launched as the benchmark launches it;
