@@ -26,8 +26,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "effective TFLOPS/TOPS (2MNK/t) per dtype; % of MI355X dense MFMA peak"
-# MI355X dense matrix-core peaks (TOPS / TFLOPS)
+# MI355X dense matrix-core peaks (TOPS / TFLOPS) and HBM bandwidth (GB/s)
 PEAK = {"i8": 5000.0, "f8": 5000.0, "e4m3": 5000.0, "e2m1": 10100.0}
+HBM_GBPS = 8000.0
 # The pages' number for the INT8 30000x21504x5376 workload: 209.9 TOPS, on a
 # different GPU (RX 9070 XT); context only.
 PAGES_I8_QKV_TOPS = 209.9
@@ -112,6 +113,18 @@ def kernel_digest():
     return h.hexdigest()
 
 
+def min_bytes(d):
+    """Algorithmic HBM bytes of one call: A, B, C and the scale / bias arrays,
+    each read or written once."""
+    M, N, K = d["M"], d["N"], d["K"]
+    ab = (M + N) * (K // 2 if d.get("fmt") == "e2m1" else K)
+    if d["kind"] == "mx":
+        sc = M * (K // 32) + (-(-N // d["b_rows_per_scale"])) * (K // 32)
+    else:
+        sc = 4 * (M + N)
+    return ab + sc + 2 * M * N + (2 * N if d["bias"] is not None else 0)
+
+
 def traffic_bytes(name):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     summary, already scaled by the copy-kernel factors; None when the kernel
@@ -191,6 +204,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tile", type=int, default=-1, help="force a tile id (-1: the table's choice)")
+    ap.add_argument("--shape", default=None, metavar="M,N,K",
+                    help="run the workload's recipe at another shape (e.g. the skinny-M cases)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead: time a plain device copy of this many bytes (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -220,12 +235,15 @@ def main():
         print(json.dumps({"copy_bytes": args.copy_bytes, "launches": args.steps}), flush=True)
         return
     name = args.workload
+    shape = {}
+    if args.shape:
+        shape = dict(zip("MNK", (int(v) for v in args.shape.split(","))))
     R = args.rot or ROT[name]
-    log(f"[bench] generating {name} x{R}")
-    d0 = inputs.make(name)
+    log(f"[bench] generating {name} {shape or ''} x{R}")
+    d0 = inputs.make(name, **shape)
     sets = [upload(d0)]
     for r in range(1, R):
-        sets.append(upload(inputs.make(name, rot=r)))
+        sets.append(upload(inputs.make(name, rot=r, **shape)))
     M, N, K = d0["M"], d0["N"], d0["K"]
     out = torch.empty((M, N + (-N) % 8), dtype=torch.bfloat16, device="cuda")[:, :N]
     stream = torch.cuda.current_stream()
@@ -256,6 +274,18 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     peak = PEAK[dtype_of(d0)]
+    nbytes = min_bytes(d0)
+    # below the ridge (peak ops per HBM byte) the call is bound by HBM, not MFMA
+    hbm_bound = flops / nbytes < peak * 1e12 / (HBM_GBPS * 1e9)
+    if hbm_bound:
+        gbps = nbytes / (kernel_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_GBPS, "unit": "GB/s",
+                    "frac": round(gbps / HBM_GBPS, 4)}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": unit_of(d0),
+                    "frac": round(achieved / peak, 4)}
+    roofline.update({"traffic": None if shape else traffic_bytes(name), "kernel_ms": round(kernel_ms, 6),
+                     "algorithmic_bytes": nbytes})
 
     res = {
         "metric": METRIC,
@@ -267,14 +297,12 @@ def main():
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(value / PAGES_I8_QKV_TOPS, 4) if name == "i8_qkv" else None,
+        "vs_baseline": round(value / PAGES_I8_QKV_TOPS, 4) if name == "i8_qkv" and not shape else None,
         "dtype": {"i8": "int8", "f8": "e4m3", "e4m3": "mxfp8-e4m3", "e2m1": "mxfp4-e2m1"}[dtype_of(d0)],
         "data": "synthetic",
         "config": {"workload": f"{name} M={M} N={N} K={K}" + (" bias" if d0["bias"] is not None else ""),
                    "tile_id": tile, "rotating_sets": R, "pct_of_peak": round(100 * value / peak, 2)},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
-                     "unit": unit_of(d0), "frac": round(achieved / peak, 4), "traffic": traffic_bytes(name),
-                     "kernel_ms": round(kernel_ms, 6)},
+        "roofline": roofline,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

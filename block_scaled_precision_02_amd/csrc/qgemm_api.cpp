@@ -10,6 +10,7 @@
 // than padded to whole 32-row tiles.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -85,8 +86,9 @@ qgemm_status check_device()
 
 // ------------------------------------------------------------ tile table
 // A launch runs in rounds of (CUs x workgroups per CU) tiles; a round lasts
-// about as long as one workgroup's tile at its measured MFMA efficiency when
-// its co-resident workgroups share the CU.  The table picks the candidate with
+// about as long as one workgroup's tile at its measured MFMA efficiency, times
+// the workgroups that share a CU (none while the grid is smaller than the
+// chip).  The table picks the candidate with
 // the smallest rounds x round-time; ties keep the earlier (larger) tile.  The
 // efficiencies are relative figures from the benchmark workloads: the 192x192
 // tile moves ~1.3x the LDS bytes per MFMA of the 256x256 tile, the 128x128
@@ -113,7 +115,10 @@ int select_tile_impl(int path, int64_t M, int64_t N)
         const int64_t tiles = ((M + e - 1) / e) * ((N + e - 1) / e);
         const int64_t slots = (int64_t)NUM_CU * c.per_cu;
         const int64_t rounds = (tiles + slots - 1) / slots;
-        const double cost = (double)rounds * (double)(e * e) * c.per_cu / c.eff;
+        // workgroups that actually share a CU: none while the grid is smaller
+        // than the chip
+        const int64_t share = std::min<int64_t>(c.per_cu, (tiles + NUM_CU - 1) / NUM_CU);
+        const double cost = (double)rounds * (double)(e * e) * (double)share / c.eff;
         if (best_cost < 0 || cost < best_cost * 0.999) {
             best = c.tile;
             best_cost = cost;
@@ -215,10 +220,11 @@ Params base_params(const void *A, int64_t lda, const void *B, int64_t ldb, void 
     p.kbytes = (int)kbytes;
     p.ksteps = (int)((kbytes + KSTEP_BYTES - 1) / KSTEP_BYTES);
     p.kblocks = (int)(s.K / 32);
-    const int edge = tile_edge(tile);
-    p.tiles_m = (int)((s.M + edge - 1) / edge);
-    p.tiles_n = (int)((s.N + edge - 1) / edge);
-    p.group_m = 8;
+    const int em = tile_edge_m(tile), en = tile_edge_n(tile);
+    p.tiles_m = (int)((s.M + em - 1) / em);
+    p.tiles_n = (int)((s.N + en - 1) / en);
+    // small-M tiles: every row tile of one column block runs next to the others
+    p.group_m = is_skinny_tile(tile) ? p.tiles_m : 8;
     return p;
 }
 
@@ -253,12 +259,26 @@ bool dma_eligible(int path, int64_t kbytes, int64_t K, bool svec)
 // 2130 for the four-wave LDS-fetch kernel and ~2100 for register staging;
 // MXFP4 8192^3 3756 vs 3668 TFLOPS; MXFP8 16384x7168x2048 1940 vs 1933), 192
 // and 128 as their four-wave LDS-fetch forms.
-int pick_tile(int path, Shape s, int64_t kbytes, bool svec)
+// Small M (INT8 and FP8 with bf16 output): the call streams B; the small-M
+// kernel spreads B over N/16 workgroups whose eight waves split K.
+constexpr int64_t SKINNY_MAX_M = 64;
+
+int pick_tile(int path, Shape s, int64_t kbytes, bool svec, bool bf16_out)
 {
-    int t = g_forced_tile >= 0 ? g_forced_tile : select_tile_impl(path, s.M, s.N);
-    if (g_forced_tile < 0 && dma_eligible(path, kbytes, s.K, svec))
-        t = (t == 0) ? DMA8_TILE : (t == 3) ? DMA192_TILE : (t == 1) ? DMA128_TILE : t;
+    const bool skinny_ok = (path == 0 || path == 1) && bf16_out;
+    int t;
+    if (g_forced_tile >= 0) {
+        t = g_forced_tile;
+    } else if (skinny_ok && s.M <= SKINNY_MAX_M) {
+        t = s.M <= 16 ? SKINNY16_TILE : SKINNY64_TILE;
+    } else {
+        t = select_tile_impl(path, s.M, s.N);
+        if (dma_eligible(path, kbytes, s.K, svec))
+            t = (t == 0) ? DMA8_TILE : (t == 3) ? DMA192_TILE : (t == 1) ? DMA128_TILE : t;
+    }
     if (is_dma_tile(t) && !dma_eligible(path, kbytes, s.K, svec))
+        t = 0;
+    if (is_skinny_tile(t) && !skinny_ok)
         t = 0;
     return t;
 }
@@ -290,7 +310,7 @@ int qgemm_select_tile(int path, int64_t M, int64_t N, int64_t K)
     const int64_t kbytes = path == 3 ? K / 2 : K;
     const int prev = g_forced_tile;
     g_forced_tile = -1;
-    const int t = pick_tile(path, Shape{M, N, K}, kbytes, true);   // scales assumed aligned
+    const int t = pick_tile(path, Shape{M, N, K}, kbytes, true, true);   // scales assumed aligned, bf16 out
     g_forced_tile = prev;
     return t;
 }
@@ -321,7 +341,7 @@ static qgemm_status i8_common(const int8_t *A, int64_t lda, const int8_t *B, int
     }
     TRY(check_output(C, ldc, s.N, out == OUT_I32 ? 4 : 2));
     TRY(check_device());
-    const int tile = pick_tile(0, s, s.K, true);
+    const int tile = pick_tile(0, s, s.K, true, out == OUT_BF16);
     Params p = base_params(A, lda, B, ldb, C, ldc, s, s.K, tile);
     TRY(check_grid(p));
     p.scale_a = sa;
@@ -357,7 +377,7 @@ qgemm_status qgemm_f8_pertoken(const uint8_t *A, int64_t lda, const uint8_t *B, 
     TRY(check_bias(bias));
     TRY(check_output(C, ldc, N, 2));
     TRY(check_device());
-    const int tile = pick_tile(1, s, K, true);
+    const int tile = pick_tile(1, s, K, true, true);
     Params p = base_params(A, lda, B, ldb, C, ldc, s, K, tile);
     TRY(check_grid(p));
     p.scale_a = scale_a;
@@ -397,7 +417,7 @@ qgemm_status qgemm_mx(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const 
     const int wb = (fmt == QGEMM_MX_E2M1) ? 4 : 2;
     const bool svec = ((K / 32) % wb == 0) && aligned(scale_a, wb) && aligned(scale_b, wb);
     const bool svec16 = svec && aligned(scale_a, 16) && aligned(scale_b, 16);
-    const int tile = pick_tile(path, s, row_bytes, svec16);
+    const int tile = pick_tile(path, s, row_bytes, svec16, true);
     Params p = base_params(A, lda_bytes, B, ldb_bytes, C, ldc, s, row_bytes, tile);
     TRY(check_grid(p));
     p.mx_sa = scale_a;

@@ -2,6 +2,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include "qgemm_dma.hpp"
+#include "qgemm_skinny.hpp"
 
 namespace qgemm {
 
@@ -16,14 +17,26 @@ namespace qgemm {
 //        waves per SIMD); same requirements
 //   6 -> 192x192 fetched straight into LDS, 2x2 waves of 96x96; same requirements
 //   7 -> 128x128 fetched straight into LDS, 2x2 waves of 64x64; same requirements
-constexpr int NUM_TILES = 8;
+//   8 -> small M (qgemm_skinny.hpp): 16 rows x 16 columns, eight waves splitting
+//        K; INT8 and FP8 with bf16 output
+//   9 -> small M: 64 rows x 16 columns, eight waves splitting K; same paths
+constexpr int NUM_TILES = 10;
 constexpr int DMA_TILE = 4, DMA8_TILE = 5, DMA192_TILE = 6, DMA128_TILE = 7;
+constexpr int SKINNY16_TILE = 8, SKINNY64_TILE = 9;
 __host__ __device__ constexpr bool is_dma_tile(int tile) { return tile >= DMA_TILE && tile <= DMA128_TILE; }
-__host__ __device__ constexpr int tile_edge(int tile)
+__host__ __device__ constexpr bool is_skinny_tile(int tile) { return tile == SKINNY16_TILE || tile == SKINNY64_TILE; }
+// Output rows (of A) and columns (rows of B) of one workgroup's tile.
+__host__ __device__ constexpr int tile_edge_m(int tile)
 {
-    return (tile == 1 || tile == DMA128_TILE) ? 128 : ((tile == 3 || tile == DMA192_TILE) ? 192 : 256);
+    return tile == SKINNY16_TILE ? 16 : tile == SKINNY64_TILE ? 64
+         : (tile == 1 || tile == DMA128_TILE) ? 128 : ((tile == 3 || tile == DMA192_TILE) ? 192 : 256);
 }
-__host__ __device__ constexpr int tile_threads(int tile) { return (tile == 2 || tile == DMA8_TILE) ? 512 : 256; }
+__host__ __device__ constexpr int tile_edge_n(int tile) { return is_skinny_tile(tile) ? 16 : tile_edge_m(tile); }
+__host__ __device__ constexpr int tile_edge(int tile) { return tile_edge_m(tile); }
+__host__ __device__ constexpr int tile_threads(int tile)
+{
+    return (tile == 2 || tile == DMA8_TILE || is_skinny_tile(tile)) ? 512 : 256;
+}
 
 template <int PATH, int WM, int WN, int TM, int TN, bool BIAS, int BROWS, bool SVEC, int OUT>
 hipError_t launch_variant(const Params &p, hipStream_t s)
@@ -60,6 +73,18 @@ hipError_t launch_tile(int tile, const Params &p, hipStream_t s)
             else
                 hipLaunchKernelGGL((qgemm_dma_kernel<PATH, 2, 2, 2, BIAS, BROWS, OUT>), grid, block, 0, s, p);
             return hipGetLastError();
+        }
+    case SKINNY16_TILE:
+    case SKINNY64_TILE:
+        if constexpr ((PATH == PATH_I8 || PATH == PATH_F8) && OUT == OUT_BF16) {
+            const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(tile_threads(tile));
+            if (tile == SKINNY16_TILE)
+                hipLaunchKernelGGL((qgemm_skinny_kernel<PATH, 1, skinny_depth<PATH, 1>(), BIAS>), grid, block, 0, s, p);
+            else
+                hipLaunchKernelGGL((qgemm_skinny_kernel<PATH, 4, skinny_depth<PATH, 4>(), BIAS>), grid, block, 0, s, p);
+            return hipGetLastError();
+        } else {
+            return hipErrorInvalidValue;
         }
     default: return hipErrorInvalidValue;
     }

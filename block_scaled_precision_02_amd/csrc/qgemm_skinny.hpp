@@ -1,0 +1,216 @@
+// qgemm_skinny.hpp -- the scaled GEMM for small M, where the call is bound by
+// streaming B from HBM rather than by the matrix cores.
+//
+//     C[m,n] = bf16( sa[m] * sb[n] * sum_k A[m,k] B[n,k] + bias[n] )   (INT8, FP8)
+//
+// The 256x256 tiles of the main kernels leave most CUs idle when M is a few
+// rows (a 2112-column B gives 9 tiles of 256): here a workgroup owns 16
+// columns of C (one 16x16 MFMA block wide) and TM blocks of 16 rows, and
+// its eight waves split K: wave w takes the K steps w, w+8, w+16, ...
+// (2112 columns -> 132 workgroups, each streaming 16 rows of B with eight
+// waves in flight).  The partial sums meet in LDS and are added in wave
+// order, so the result does not depend on timing.
+//
+//  * No LDS staging: a 16x16 MFMA operand is 16 rows with four lanes per row,
+//    so a wave's 16-byte-per-lane load of one operand fragment reads 16 rows
+//    x 64 contiguous bytes -- the same row pieces the LDS-fetch kernels use.
+//    The sum over K does not depend on which K a lane holds as long as A and
+//    B agree, so lane group g (lane / 16) takes byte chunk g of each 64-byte
+//    piece (and, for the 128-byte e4m3 step, chunk g + 4 in its upper half).
+//  * Each wave keeps D steps of fragments in flight in a register ring (the
+//    compiler waits on each slot's loads just before its MFMA).
+//  * Rows past M / N read zeros through the buffer range check (their offset
+//    is pushed out of range, and stays out of range after any K offset);
+//    16-byte chunks at or past the row's K bytes read zeros the same way, so
+//    K needs no multiple beyond the 32 every call has.
+//  * Output: with B as the instruction's first operand each lane ends with
+//    four consecutive n for one m (lane l: m = 16i + l%16, n = 4(l/16) + r),
+//    stored as one 8-byte vector when the four columns exist.
+#pragma once
+#include "qgemm_kernel.hpp"
+
+namespace qgemm {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int PATH> struct SkinnyTraits;
+// K bytes per MFMA step; 16-byte chunks per lane per step
+template <> struct SkinnyTraits<PATH_I8> {
+    static constexpr int KSTEP = 64, NCH = 1;
+    using Frag = i32x4;
+    using Acc = i32x4;
+};
+template <> struct SkinnyTraits<PATH_F8> {
+    static constexpr int KSTEP = 128, NCH = 2;
+    using Frag = i32x8;
+    using Acc = f32x4;
+};
+
+constexpr int SK_WAVES = 8;
+
+// Steps in flight per wave: the register ring is D x (TM + 1) fragments and
+// a wave has 256 registers (two waves per SIMD).
+template <int PATH, int TM> constexpr int skinny_depth()
+{
+    return TM == 1 ? (PATH == PATH_I8 ? 16 : 8) : (PATH == PATH_I8 ? 8 : 4);
+}
+
+template <int PATH, int TM, int D, bool BIAS>
+__global__ void __launch_bounds__(64 * SK_WAVES, 1) qgemm_skinny_kernel(const Params p)
+{
+    using T = SkinnyTraits<PATH>;
+    using Frag = typename T::Frag;
+    using Acc = typename T::Acc;
+    constexpr int BM = 16 * TM, BN = 16;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15, g = lane >> 4;
+
+    int tm, tn;
+    tile_of(p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int rows_a = min(BM, p.M - m0), rows_b = min(BN, p.N - n0);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * p.lda,
+                                                (uint32_t)((rows_a - 1) * p.lda + p.kbytes));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + (int64_t)n0 * p.ldb,
+                                                (uint32_t)((rows_b - 1) * p.ldb + p.kbytes));
+    unsigned a_row[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int r = 16 * i + r16;
+        a_row[i] = r < rows_a ? (unsigned)(r * p.lda) : OOB;
+    }
+    const unsigned b_row = r16 < rows_b ? (unsigned)(r16 * p.ldb) : OOB;
+
+    const int ksteps = (p.kbytes + T::KSTEP - 1) / T::KSTEP;
+    const int nst = ksteps > wave ? (ksteps - wave + SK_WAVES - 1) / SK_WAVES : 0;
+
+    Frag fa[D][TM], fb[D];
+    Acc acc[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+        acc[i] = Acc{};
+
+    // Fragments of this wave's step j into ring slot SLOT (zeros past K).
+    auto load = [&](auto slotc, int j) {
+        constexpr int SLOT = decltype(slotc)::value;
+        const int s = wave + SK_WAVES * j;
+#pragma unroll
+        for (int c = 0; c < T::NCH; ++c) {
+            const int kc = s * T::KSTEP + 64 * c + 16 * g;
+            const bool kin = s < ksteps && kc < p.kbytes;
+            const u32x4 vb = ld16(rb, kin ? b_row + (unsigned)kc : OOB);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                fb[SLOT][4 * c + q] = (int)vb[q];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const u32x4 va = ld16(ra, kin ? a_row[i] + (unsigned)kc : OOB);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    fa[SLOT][i][4 * c + q] = (int)va[q];
+            }
+        }
+    };
+    auto mma = [&](auto slotc) {
+        constexpr int SLOT = decltype(slotc)::value;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            if constexpr (PATH == PATH_I8)
+                acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb[SLOT], fa[SLOT][i], acc[i], 0, 0, 0);
+            else
+                acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[SLOT], fa[SLOT][i], acc[i], 0, 0,
+                                                                          0, 0, 0, 0);
+        }
+    };
+
+    static_for<0, D>([&](auto sc) { load(sc, decltype(sc)::value); });
+    // Steps past the wave's last load zeros and add exact zeros.
+    for (int j0 = 0; j0 < nst; j0 += D) {
+        static_for<0, D>([&](auto sc) {
+            mma(sc);
+            load(sc, j0 + decltype(sc)::value + D);
+        });
+    }
+
+    // Partial sums of waves 1..7 through LDS; wave 0 adds them in wave order.
+    __shared__ __attribute__((aligned(16))) int red[SK_WAVES - 1][TM][4][64];
+    if (wave > 0) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                // (a scalar copy first: clang's bit_cast of an ext_vector
+                // element reads element 0)
+                const auto e = acc[i][r];
+                red[wave - 1][i][r][lane] = __builtin_bit_cast(int, e);
+            }
+    }
+    __syncthreads();
+    if (wave != 0)
+        return;
+#pragma unroll
+    for (int w = 0; w < SK_WAVES - 1; ++w)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int v = red[w][i][r][lane];
+                if constexpr (PATH == PATH_I8)
+                    acc[i][r] += v;
+                else
+                    acc[i][r] += __builtin_bit_cast(float, v);
+            }
+
+    // Epilogue (the fixed-order binary32 sequence of the main kernels).
+    const int nloc = 4 * g;
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(p.scale_b + n0, (uint32_t)(rows_b * 4));
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.scale_a + m0, (uint32_t)(rows_a * 4));
+    __amdgpu_buffer_rsrc_t rbias;
+    if constexpr (BIAS)
+        rbias = make_rsrc(p.bias + n0, (uint32_t)(rows_b * 2));
+    unsigned sbw[4], bbw[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const bool in = nloc + r < rows_b;
+        sbw[r] = __builtin_amdgcn_raw_buffer_load_b32(rsb, in ? (unsigned)((nloc + r) * 4) : OOB, 0, 0);
+        if constexpr (BIAS)
+            bbw[r] = (unsigned)__builtin_amdgcn_raw_buffer_load_b16(rbias, in ? (unsigned)((nloc + r) * 2) : OOB, 0,
+                                                                  0) << 16;
+    }
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc((const uint8_t *)p.C + (int64_t)m0 * p.ldc * 2,
+                                                (uint32_t)((int64_t)rows_a * p.ldc * 2));
+    const bool full_n = nloc + 4 <= rows_b;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int mloc = 16 * i + r16;
+        const float sa = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rsa, mloc < rows_a ? (unsigned)(mloc * 4) : OOB, 0, 0));
+        float f[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float x;
+            if constexpr (PATH == PATH_I8)
+                x = (float)acc[i][r];
+            else
+                x = acc[i][r];
+            x = x * sa;
+            x = x * __builtin_bit_cast(float, sbw[r]);
+            if constexpr (BIAS)
+                x = x + __builtin_bit_cast(float, bbw[r]);
+            f[r] = x;
+        }
+        const u32x2 v = {pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3])};
+        const unsigned off = mloc < rows_a ? (unsigned)((int64_t)mloc * p.ldc * 2 + (n0 + nloc) * 2) : OOB;
+        if (full_n) {
+            __builtin_amdgcn_raw_buffer_store_b64(v, rc, off, 0, 0);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(v[r >> 1] >> (16 * (r & 1))), rc,
+                                                      (nloc + r < rows_b) ? off + 2 * r : OOB, 0, 0);
+        }
+    }
+}
+
+}  // namespace qgemm

@@ -137,10 +137,16 @@ def test_tile_table():
     assert L.qgemm_select_tile(1, 4096, 2112, 7168) == 6
     assert L.qgemm_select_tile(1, 4096, 2112, 7200) == 3
     assert L.qgemm_select_tile(7, 64, 64, 64) == -1
-    for t, e in ((0, 256), (1, 128), (2, 256), (3, 192), (4, 256), (5, 256), (6, 192), (7, 128)):
+    # small M, INT8 / FP8: the small-M kernel (16- or 64-row tiles); MX keeps the table
+    assert L.qgemm_select_tile(1, 1, 2112, 7168) == 8
+    assert L.qgemm_select_tile(1, 16, 2112, 7168) == 8
+    assert L.qgemm_select_tile(0, 64, 3072, 3072) == 9
+    assert L.qgemm_select_tile(1, 65, 2112, 7168) != 9
+    assert L.qgemm_select_tile(2, 16, 7168, 2048) not in (8, 9)
+    for t, e in ((0, 256), (1, 128), (2, 256), (3, 192), (4, 256), (5, 256), (6, 192), (7, 128), (8, 16), (9, 64)):
         assert L.qgemm_tile_rows(t) == e
-    assert L.qgemm_tile_rows(8) == 0 and L.qgemm_tile_rows(-1) == 0
-    assert L.qgemm_force_tile(9) == -2
+    assert L.qgemm_tile_rows(10) == 0 and L.qgemm_tile_rows(-1) == 0
+    assert L.qgemm_force_tile(10) == -2
     assert L.qgemm_force_tile(1) == -1
     assert L.qgemm_force_tile(-1) == 1
 
@@ -151,5 +157,5 @@ def test_tile_table_is_sane_everywhere():
     for M in (1, 17, 255, 256, 257, 1000, 4096, 30000):
         for N in (1, 33, 256, 2112, 7168, 21504):
             t = L.qgemm_select_tile(0, M, N, 512)
-            assert L.qgemm_tile_rows(t) in (128, 192, 256)
+            assert L.qgemm_tile_rows(t) in (16, 64, 128, 192, 256)
             assert L.qgemm_force_tile(-1) == -1

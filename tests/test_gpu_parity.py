@@ -268,6 +268,44 @@ def test_dma_tile_falls_back_when_k_does_not_fit(tile):
     parity.compare(d, parity.bits(parity.gpu_run(d)), ref, None, f"tile {tile} fallback K=96")
 
 
+SKINNY_SHAPES = [(1, 1, 32), (1, 300, 512), (5, 33, 96), (16, 16, 1024), (17, 70, 224), (64, 129, 544),
+                 (33, 2112, 7168)]
+
+
+@pytest.mark.parametrize("tile", [8, 9])
+@pytest.mark.parametrize("name", ["i8_small", "f8_ptpc"])
+@pytest.mark.parametrize("M,N,K", SKINNY_SHAPES)
+def test_skinny_kernel_edges(name, M, N, K, tile):
+    """The small-M kernel (eight waves splitting K, partial sums added in
+    LDS) on ragged M / N / K, NaN-filled output with canaries beyond N and M;
+    INT8 also bit for bit against the 256x256 register-staged tile."""
+    d = inputs.make(name, M=M, N=N, K=K, bias=(M % 2 == 1))
+    q.force_tile(tile)
+    ldc = N + (-N) % 8 + 8
+    buf = torch.full((M + 3, ldc), float("nan"), dtype=torch.bfloat16, device="cuda")
+    before = parity.bits(buf)
+    parity.gpu_run(d, out=buf[:M, :N])
+    after = parity.bits(buf)
+    ref, absdot, _ = parity.oracle_run(d)
+    parity.compare(d, after[:M, :N], ref, absdot, f"skinny {name} {M}x{N}x{K} tile {tile}")
+    assert np.array_equal(after[:M, N:], before[:M, N:]), "wrote past N"
+    assert np.array_equal(after[M:], before[M:]), "wrote past M"
+    if d["kind"] == "i8":
+        q.force_tile(0)
+        assert np.array_equal(after[:M, :N], parity.bits(parity.gpu_run(d)))
+
+
+@pytest.mark.parametrize("M", [1, 16, 64])
+def test_skinny_table_choice_full_width(M):
+    """FP8 per-token at M = 1, 16, 64 over the full 2112 x 7168 weight, as the
+    table launches it (the small-M kernel), every output row checked."""
+    d = inputs.make("f8_ptpc", M=M)
+    q.force_tile(-1)
+    assert q.select_tile(1, M, d["N"], d["K"]) in (8, 9)
+    ref, absdot, _ = parity.oracle_run(d)
+    parity.compare(d, parity.bits(parity.gpu_run(d)), ref, absdot, f"skinny f8 M={M}")
+
+
 def test_non_default_stream():
     d = inputs.make("mxfp4", M=256, N=512, K=512)
     s = torch.cuda.Stream()
