@@ -222,6 +222,9 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     const int brow = wn * TN * 32 + r32;
     Frag fa[2][TM], fb[2][TN];
     unsigned sa_use[TM], sb_use[TN], sa_nxt[TM], sb_nxt[TN];
+    // the words of each scale row's chunk that cover the current round
+    constexpr int SCW = (PATH == PATH_MX4) ? 4 : 2;
+    unsigned cra[TM][SCW], crb[TN][SCW];
 
     // Fragments of sub-step S of stage slot `slot` into register set SET.
     auto read_frags = [&](auto sc, int slot, auto setc) {
@@ -238,27 +241,49 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         for (int i = 1; i < TM; ++i)
             fa[SET][i] = dma_frag<PATH, S>(ta, arow + 32 * i, h);
     };
-    // Scale operand of stage t (J = t % 4) for this lane: byte S of it is
-    // sub-step S's scale for the lane's block -- e2m1: bytes 4J + 2h and
-    // 4J + 2h + 1 of the row's chunk (one 16-bit read); e4m3: byte 2J + h.
-    auto read_scales = [&](int t, auto jc) {
+    // Scale operands.  Once per round (4 stages) each lane reads the words of
+    // its rows' 16-byte scale chunks that the round uses (one aligned 16- or
+    // 8-byte LDS read per row: narrower per-stage reads of 32 rows at a
+    // 16-byte stride land 4 rows to a bank); each stage then shifts out its
+    // operand: byte S of it is sub-step S's scale for the lane's block --
+    // e2m1: bytes 4J + 2h, 4J + 2h + 1 of the chunk; e4m3: byte 2J + h.
+    auto read_chunk = [&](int t) {
         if constexpr (MX) {
-            constexpr int J = decltype(jc)::value;
             const uint8_t *sbuf = &lds[OPND_BYTES + ((t >> 2) & 1) * SCL_BUF];
-            auto rd = [&](const uint8_t *row_base) -> unsigned {
-                if constexpr (PATH == PATH_MX4)
-                    return *(const unsigned short *)(row_base + 4 * J + 2 * h);
-                else
-                    return *(const unsigned char *)(row_base + 2 * J + h);
+            auto rd = [&](const uint8_t *row_base, unsigned (&w)[SCW]) {
+                if constexpr (SCW == 4) {
+                    const u32x4 v = *(const u32x4 *)row_base;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) w[q] = v[q];
+                } else {
+                    const u32x2 v = *(const u32x2 *)row_base;
+                    w[0] = v[0];
+                    w[1] = v[1];
+                }
             };
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                sa_nxt[i] = rd(sbuf + (arow + 32 * i) * 16);
+                rd(sbuf + (arow + 32 * i) * 16, cra[i]);
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int row = BROWS == 1 ? brow + 32 * j : wn * TN + j;
-                sb_nxt[j] = rd(sbuf + SA_ROWS * 16 + row * 16);
+                rd(sbuf + SA_ROWS * 16 + row * 16, crb[j]);
             }
+        }
+    };
+    auto read_scales = [&](int t, auto jc) {
+        if constexpr (MX) {
+            constexpr int J = decltype(jc)::value;
+            if constexpr (J == 0)
+                read_chunk(t);
+            constexpr int W = (PATH == PATH_MX4) ? J : J >> 1;
+            const unsigned sh = (PATH == PATH_MX4) ? 16u * h : 8u * (2 * (J & 1) + h);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                sa_nxt[i] = cra[i][W] >> sh;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                sb_nxt[j] = crb[j][W] >> sh;
         }
     };
     auto mfmas = [&](auto sc, auto setc, auto q0c, auto q1c) {
@@ -368,7 +393,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
                   std::integral_constant<int, NQ>());
         }
         constexpr int NB = (NSUB == 2) ? NQ : NQ / 2;
-        constexpr int RB = NDSR + (MX ? TM + TN : 0);
+        constexpr int RB = NDSR + ((MX && ((J + 1) & 3) == 0) ? TM + TN : 0);
         static_for<0, NB>([&](auto qc) {
             constexpr int Q = decltype(qc)::value;
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
