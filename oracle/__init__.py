@@ -13,6 +13,11 @@ Functions follow the definitions in ``qgemm_oracle.c``:
                   Measured: "ptpc").
   mx           -- MX e4m3 / e2m1 with ue8m0 per 32 K elements (ROCm/mori PR
                   #806, What; ROCm/FlyDSL PR #990).
+  quant_f8_pertoken, quant_mx
+               -- the activation quantisers producing those operands from
+                  bf16 (ROCm/mori PR #806, What: the quantiser's [M, K/32]
+                  uint8 scales; the scale rules are readings, stated in
+                  ``qgemm_oracle.c``).
 """
 import ctypes
 import os
@@ -62,6 +67,13 @@ def _load():
                  "orc_bf16_rne_array"):
         getattr(lib, name).restype = None
         getattr(lib, name).argtypes = [_P, _P, _I64]
+    for name in ("orc_enc_e4m3_array", "orc_enc_e2m1_array"):
+        getattr(lib, name).restype = None
+        getattr(lib, name).argtypes = [_P, _P, _I64]
+    lib.orc_quant_f8_pertoken.restype = None
+    lib.orc_quant_f8_pertoken.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64]
+    lib.orc_quant_mx.restype = ctypes.c_int
+    lib.orc_quant_mx.argtypes = [ctypes.c_int, _P, _I64, _P, _I64, _P, _I64, _I64, _I64]
     lib.orc_i8_rowwise.restype = ctypes.c_int
     lib.orc_i8_rowwise.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _P, _I64, _P,
                                    _I64, _I64, _I64]
@@ -182,3 +194,46 @@ def mx(fmt, A, B, scale_a, scale_b, b_rows_per_scale, K, bias=None):
     if rc != 0:
         raise ValueError("bad MX format or B-scale layout")
     return C, acc, absdot
+
+
+def enc_e4m3(y):
+    """float64 values -> e4m3fn codes (nearest, ties to even, saturating, sign kept)."""
+    y = _c(y, np.float64)
+    out = np.empty(y.shape, np.uint8)
+    _load().orc_enc_e4m3_array(_ptr(y), _ptr(out), y.size)
+    return out
+
+
+def enc_e2m1(y):
+    """float64 values -> e2m1 codes, one per byte (0..15)."""
+    y = _c(y, np.float64)
+    out = np.empty(y.shape, np.uint8)
+    _load().orc_enc_e2m1_array(_ptr(y), _ptr(out), y.size)
+    return out
+
+
+def quant_f8_pertoken(X):
+    """Per-token e4m3 quantiser.  X [M,K] bf16 bits (uint16).
+    Returns (Q uint8 [M,K] e4m3 codes, scale float32 [M])."""
+    X = _c(X, np.uint16)
+    M, K = X.shape
+    Q = np.empty((M, K), np.uint8)
+    s = np.empty(M, np.float32)
+    _load().orc_quant_f8_pertoken(_ptr(X), K, _ptr(Q), K, _ptr(s), M, K)
+    return Q, s
+
+
+def quant_mx(fmt, X):
+    """MX quantiser, one ue8m0 scale per 32 elements of a row.  X [M,K] bf16
+    bits (uint16), K % 32 == 0.  Returns (Q uint8 [M,K] (e4m3) or [M,K/2]
+    (e2m1, element k even in the low nibble), S uint8 [M,K/32])."""
+    X = _c(X, np.uint16)
+    M, K = X.shape
+    assert K % 32 == 0
+    row = K if fmt == MX_E4M3 else K // 2
+    Q = np.zeros((M, row), np.uint8)
+    S = np.empty((M, K // 32), np.uint8)
+    rc = _load().orc_quant_mx(fmt, _ptr(X), K, _ptr(Q), row, _ptr(S), K // 32, M, K)
+    if rc != 0:
+        raise ValueError("bad MX format")
+    return Q, S

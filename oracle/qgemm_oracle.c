@@ -260,7 +260,135 @@ int orc_mx(int fmt, const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb
     return 0;
 }
 
+/* ----------------------------------------------------------- quantisers */
+
+/* The quantisers that produce the GEMM's operands from bf16 activations.
+ * "perf(gemm-ar): mxfp8 with row-major scales staged through LDS" (ROCm/mori
+ * PR #806), What: the quantiser hands the GEMM its A scales as [M, K/32]
+ * uint8 ue8m0 codes, row-major; Measured: per-token ("ptpc") e4m3 scales.
+ * The pages give no formula for either scale.  The readings taken:
+ *  - per-token e4m3: scale[m] = fp32(amax_m / 448), 448 being the largest
+ *    finite e4m3 magnitude, and code = enc(fp32(x / scale[m])); an all-zero
+ *    row gets scale 0 and keeps each zero's sign;
+ *  - MX: the OCP Microscaling v1.0 scale rule, shared exponent
+ *    X = floor(log2(amax)) - emax (emax 8 for e4m3, 2 for e2m1), stored as
+ *    the ue8m0 code X + 127 clamped to [0, 254] (0 for an all-zero block),
+ *    and code = enc(x * 2^-(code - 127));
+ *  - enc: the nearest representable magnitude, ties to the even code,
+ *    magnitudes beyond the largest finite one saturating to it; the sign bit
+ *    is x's sign bit (so a negative value that rounds to zero is -0).
+ * Inputs are finite; for NaN or infinite inputs the result is unspecified. */
+
+/* Nearest of the first ncodes magnitudes dec(0) < dec(1) < ... to a >= 0:
+ * a plain walk up the decoded grid. */
+static int enc_nearest(double a, double (*dec)(uint8_t), int ncodes)
+{
+    if (a >= dec((uint8_t)(ncodes - 1)))
+        return ncodes - 1;
+    int hi = 0;
+    while (dec((uint8_t)hi) < a)
+        ++hi;                                   /* first grid value >= a */
+    if (hi == 0)
+        return 0;
+    const double dhi = dec((uint8_t)hi) - a, dlo = a - dec((uint8_t)(hi - 1));
+    if (dhi < dlo)
+        return hi;
+    if (dlo < dhi)
+        return hi - 1;
+    return (hi % 2 == 0) ? hi : hi - 1;         /* tie: the even code */
+}
+
+/* e4m3fn code of y: magnitude codes 0..126 (0x7F is NaN), sign in bit 7. */
+uint8_t orc_enc_e4m3(double y)
+{
+    return (uint8_t)((signbit(y) ? 0x80 : 0) | enc_nearest(fabs(y), orc_dec_e4m3, 127));
+}
+
+/* e2m1 code of y: magnitude codes 0..7, sign in bit 3. */
+uint8_t orc_enc_e2m1(double y)
+{
+    return (uint8_t)((signbit(y) ? 0x8 : 0) | enc_nearest(fabs(y), orc_dec_e2m1, 8));
+}
+
+/* Per-token e4m3 quantiser.  X [M,K] bf16 bits (row stride ldx elements) ->
+ * Q [M,K] e4m3 codes (row stride ldq bytes) and scale [M] binary32. */
+void orc_quant_f8_pertoken(const uint16_t *X, int64_t ldx, uint8_t *Q, int64_t ldq, float *scale,
+                           int64_t M, int64_t K)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t *x = X + m * ldx;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            const float v = fabsf(orc_bf16_to_f32(x[k]));
+            if (v > amax)
+                amax = v;
+        }
+        const float s = amax / 448.0f;          /* binary32 division */
+        scale[m] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            const float v = orc_bf16_to_f32(x[k]);
+            const float y = (s > 0.0f) ? v / s : v; /* s == 0: every v is +-0 */
+            Q[m * ldq + k] = orc_enc_e4m3((double)y);
+        }
+    }
+}
+
+/* MX quantiser, one ue8m0 scale per 32 elements of a row.  fmt 0: e4m3, Q
+ * [M,K] bytes; fmt 1: e2m1, Q [M,K/2] bytes (element k even in the low nibble
+ * of byte k/2, k odd in the high one).  X [M,K] bf16 bits (row stride ldx
+ * elements), K % 32 == 0; Q row stride ldq bytes; S [M,K/32] codes, row
+ * stride lds bytes.  Returns 0, or -1 for an unknown fmt. */
+int orc_quant_mx(int fmt, const uint16_t *X, int64_t ldx, uint8_t *Q, int64_t ldq, uint8_t *S,
+                 int64_t lds, int64_t M, int64_t K)
+{
+    if (fmt != 0 && fmt != 1)
+        return -1;
+    const int emax = (fmt == 0) ? 8 : 2;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t b = 0; b < K / 32; ++b) {
+            const uint16_t *x = X + m * ldx + 32 * b;
+            double amax = 0.0;
+            for (int j = 0; j < 32; ++j)
+                amax = fmax(amax, fabs((double)orc_bf16_to_f32(x[j])));
+            int code = 0;
+            if (amax > 0.0) {
+                int e;
+                frexp(amax, &e);                 /* amax = f * 2^e, f in [0.5, 1) */
+                const int X_ = (e - 1) - emax;   /* floor(log2(amax)) - emax */
+                code = X_ + 127 < 0 ? 0 : (X_ + 127 > 254 ? 254 : X_ + 127);
+            }
+            S[m * lds + b] = (uint8_t)code;
+            for (int j = 0; j < 32; ++j) {
+                const double y = ldexp((double)orc_bf16_to_f32(x[j]), 127 - code);  /* exact */
+                if (fmt == 0) {
+                    Q[m * ldq + 32 * b + j] = orc_enc_e4m3(y);
+                } else {
+                    uint8_t *byte = &Q[m * ldq + 16 * b + j / 2];
+                    const uint8_t c = orc_enc_e2m1(y);
+                    *byte = (j % 2 == 0) ? (uint8_t)((*byte & 0xF0) | c) : (uint8_t)((*byte & 0x0F) | (c << 4));
+                }
+            }
+        }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------- array forms for tests */
+
+void orc_enc_e4m3_array(const double *in, uint8_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_enc_e4m3(in[i]);
+}
+
+void orc_enc_e2m1_array(const double *in, uint8_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_enc_e2m1(in[i]);
+}
+
 
 void orc_dec_e4m3_array(const uint8_t *codes, double *out, int64_t n)
 {
