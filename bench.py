@@ -194,6 +194,81 @@ def cpu_baseline(d, target_s):
             "sample": f"{n} of {d['M']} rows of A (all {d['N']} columns, K={d['K']}), {t:.1f} s"}
 
 
+def bench_quant(args):
+    """The activation quantiser on the A operand shape of a GEMM workload:
+    HBM-bound, so the rate is algorithmic bytes (bf16 in, codes and scales
+    out) over the kernel time, against the HBM peak."""
+    import torch
+    from block_scaled_precision_02_amd import inputs
+    import block_scaled_precision_02_amd as q
+
+    wl, M, K = inputs.QUANT_SHAPES[args.quant]
+    R = args.rot or 4          # 4 x 58-268 MB of activations: past the 256 MB MALL
+    log(f"[bench] quantiser {args.quant} M={M} K={K} x{R}")
+    xs = [torch.from_numpy(inputs.make_activations(M, K, rot=r).view(np.int16)).cuda() for r in range(R)]
+    L = q.lib()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    if args.quant == "f8":
+        Q = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+        S = torch.empty(M, dtype=torch.float32, device="cuda")
+        nbytes = 2 * M * K + M * K + 4 * M
+
+        def run(i):
+            return L.qgemm_quant_f8_pertoken(xs[i % R].data_ptr(), K, Q.data_ptr(), K, S.data_ptr(), M, K, sp)
+        dtype = "bf16->e4m3"
+    else:
+        fmt = 0 if args.quant == "mxfp8" else 1
+        row = K if fmt == 0 else K // 2
+        Q = torch.empty((M, row), dtype=torch.uint8, device="cuda")
+        S = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
+        nbytes = 2 * M * K + M * row + M * (K // 32)
+
+        def run(i):
+            return L.qgemm_quant_mx(fmt, xs[i % R].data_ptr(), K, Q.data_ptr(), row, S.data_ptr(), K // 32, M, K,
+                                    sp)
+        dtype = "bf16->mx-" + ("e4m3" if fmt == 0 else "e2m1")
+    for i in range(args.warmup):
+        if run(i) != 0:
+            raise RuntimeError(L.qgemm_last_error().decode())
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        run(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    gbps = nbytes / (kernel_ms * 1e-3) / 1e9
+    res = {"metric": "activation quantiser HBM rate (algorithmic bytes / kernel time)",
+           "value": round(nbytes / (wall / args.steps) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 6),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+           "data": "synthetic",
+           "config": {"workload": f"quant {args.quant} M={M} K={K} (A of {wl})", "rotating_sets": R},
+           "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_GBPS, "unit": "GB/s",
+                        "frac": round(gbps / HBM_GBPS, 4), "traffic": None, "kernel_ms": round(kernel_ms, 6),
+                        "algorithmic_bytes": nbytes},
+           "cpu_baseline": None}
+    if not args.no_cpu_baseline:
+        import oracle
+        X = inputs.make_activations(M, K)
+        rows = max(1, min(M, int(M * 0.25)))
+        t0 = time.perf_counter()
+        if args.quant == "f8":
+            oracle.quant_f8_pertoken(X[:rows])
+        else:
+            oracle.quant_mx(0 if args.quant == "mxfp8" else 1, X[:rows])
+        t = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(nbytes * rows / M / t / 1e9, 3), "unit": "GB/s",
+                               "cores": oracle.num_threads(), "kind": "oracle",
+                               "sample": f"{rows} of {M} rows"}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,6 +284,8 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead: time a plain device copy of this many bytes (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--quant", default=None, choices=["f8", "mxfp8", "mxfp4"],
+                    help="instead: time the activation quantiser on the A shape of that workload")
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
                     help="instead: write profiles/traffic.json from the rocprofv3 FETCH_SIZE / "
                          "WRITE_SIZE runs under DIR (no GPU needed)")
@@ -233,6 +310,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": args.copy_bytes, "launches": args.steps}), flush=True)
+        return
+    if args.quant:
+        print(json.dumps(bench_quant(args)), flush=True)
         return
     name = args.workload
     shape = {}

@@ -12,6 +12,8 @@ call raises.
     qgemm_i8_acc_i32(A, B, out=None)
     qgemm_f8_pertoken(A, B, scale_a, scale_b, bias=None, out=None)
     qgemm_mx(fmt, A, B, scale_a, scale_b, b_layout, bias=None, out=None, K=None)
+    qgemm_quant_f8_pertoken(X, out=None, scale=None)      -> (Q, scale)
+    qgemm_quant_mx(fmt, X, out=None, scales=None)         -> (Q, S)
 
 Operands are [rows, K] with unit stride along K (row stride may exceed the
 row; it is passed as lda).  ``out`` may be a view of a wider buffer (row
@@ -39,6 +41,7 @@ QGEMM_MX_BSCALE_32x32 = 32
 
 # Every symbol include/qgemm.h declares.
 EXPORTS = ("qgemm_i8_rowwise", "qgemm_i8_acc_i32", "qgemm_f8_pertoken", "qgemm_mx",
+           "qgemm_quant_f8_pertoken", "qgemm_quant_mx",
            "qgemm_last_error", "qgemm_status_string", "qgemm_select_tile",
            "qgemm_tile_rows", "qgemm_force_tile")
 
@@ -66,6 +69,10 @@ def lib():
     L.qgemm_mx.restype = st
     L.qgemm_mx.argtypes = [ctypes.c_int, _P, _I64, _P, _I64, _P, _P, ctypes.c_int, _P, _P, _I64,
                            _I64, _I64, _I64, _P]
+    L.qgemm_quant_f8_pertoken.restype = st
+    L.qgemm_quant_f8_pertoken.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64, _P]
+    L.qgemm_quant_mx.restype = st
+    L.qgemm_quant_mx.argtypes = [ctypes.c_int, _P, _I64, _P, _I64, _P, _I64, _I64, _I64, _P]
     L.qgemm_last_error.restype = ctypes.c_char_p
     L.qgemm_last_error.argtypes = []
     L.qgemm_status_string.restype = ctypes.c_char_p
@@ -285,3 +292,70 @@ def qgemm_mx(fmt, A, B, scale_a, scale_b, b_layout, bias=None, out=None, stream=
                               _ptr(bias), _ptr(out), _ldc(out, N), M, N, K,
                               _stream(A.device, stream)))
     return out
+
+
+# ------------------------------------------------------------ quantisers
+
+def _activations(X):
+    torch = _torch()
+    ld = _operand(X, "X", (torch.bfloat16, torch.int16, torch.uint16))
+    return ld // 2
+
+
+def _codes_out(out, shape, device, name):
+    torch = _torch()
+    M, row = shape
+    if out is None:
+        # rows padded to a multiple of 16 bytes (the library's ldq rule)
+        return torch.empty((M, row + (-row) % 16), dtype=torch.uint8, device=device)[:, :row]
+    if tuple(out.shape) != shape or out.dtype not in (torch.uint8, torch.float8_e4m3fn) or out.device != device:
+        raise ValueError(f"{name} must be uint8 {shape} on {device}")
+    if row > 1 and out.stride(1) != 1:
+        raise ValueError(f"{name} must have unit stride along K")
+    return out
+
+
+def _ld_bytes(t, row):
+    return t.stride(0) * t.element_size() if t.shape[0] > 1 else row + (-row) % 16
+
+
+def qgemm_quant_f8_pertoken(X, out=None, scale=None, stream=None):
+    """Per-token e4m3 quantiser: bf16 X [M, K] -> (Q uint8 e4m3fn codes [M, K],
+    scale fp32 [M]), the A operand and scale_a of qgemm_f8_pertoken."""
+    torch = _torch()
+    ldx = _activations(X)
+    M, K = X.shape
+    out = _codes_out(out, (M, K), X.device, "out")
+    if scale is None:
+        scale = torch.empty(M, dtype=torch.float32, device=X.device)
+    _vector(scale, "scale", M, (torch.float32,))
+    _same_device(X.device, out, scale)
+    with torch.cuda.device(X.device):
+        _check(lib().qgemm_quant_f8_pertoken(_ptr(X), ldx, _ptr(out), _ld_bytes(out, K), _ptr(scale), M, K,
+                                             _stream(X.device, stream)))
+    return out, scale
+
+
+def qgemm_quant_mx(fmt, X, out=None, scales=None, stream=None):
+    """MX quantiser: bf16 X [M, K] -> (Q uint8 [M, K] (e4m3) or [M, K/2] (e2m1,
+    two codes per byte), S uint8 ue8m0 [M, K/32]), the A operand and scale_a
+    of qgemm_mx."""
+    torch = _torch()
+    if fmt not in (QGEMM_MX_E4M3, QGEMM_MX_E2M1):
+        raise ValueError(f"unknown MX format {fmt}")
+    ldx = _activations(X)
+    M, K = X.shape
+    row = K if fmt == QGEMM_MX_E4M3 else K // 2
+    out = _codes_out(out, (M, row), X.device, "out")
+    if scales is None:
+        scales = torch.empty((M, K // 32), dtype=torch.uint8, device=X.device)
+    if tuple(scales.shape) != (M, K // 32) or scales.dtype != torch.uint8 or scales.device != X.device:
+        raise ValueError(f"scales must be uint8 [{M}, {K // 32}] on {X.device}")
+    if K // 32 > 1 and scales.stride(1) != 1:
+        raise ValueError("scales must have unit stride along K/32")
+    lds = scales.stride(0) if M > 1 else K // 32
+    _same_device(X.device, out, scales)
+    with torch.cuda.device(X.device):
+        _check(lib().qgemm_quant_mx(fmt, _ptr(X), ldx, _ptr(out), _ld_bytes(out, row), _ptr(scales), lds, M, K,
+                                    _stream(X.device, stream)))
+    return out, scales

@@ -20,6 +20,7 @@
 
 #include "../../include/qgemm.h"
 #include "qgemm_launch.hpp"
+#include "qgemm_quant.hpp"
 
 using namespace qgemm;
 
@@ -427,6 +428,61 @@ qgemm_status qgemm_mx(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const 
     if (fmt == QGEMM_MX_E4M3)
         return finish(launch_mx8(tile, bias != nullptr, brows, svec, p, (hipStream_t)stream));
     return finish(launch_mx4(tile, bias != nullptr, brows, svec, p, (hipStream_t)stream));
+}
+
+// ------------------------------------------------------------ quantisers
+
+static qgemm_status check_quant(const uint16_t *X, int64_t ldx, const void *Q, int64_t ldq, int64_t M, int64_t K,
+                                int64_t q_row_bytes)
+{
+    TRY(check_shape(Shape{M, 1, K}, false));
+    if (M == 0)
+        return QGEMM_OK;
+    if (!X)
+        return fail(QGEMM_ERR_NULL_POINTER, "X is NULL");
+    if (!Q)
+        return fail(QGEMM_ERR_NULL_POINTER, "Q is NULL");
+    if (!aligned(X, 16) || !aligned(Q, 16))
+        return fail(QGEMM_ERR_BAD_LAYOUT, "X and Q must be 16-byte aligned");
+    if (ldx < K || ldx % 8 || ldx >= LD_LIMIT)
+        return fail(QGEMM_ERR_BAD_LAYOUT, "ldx=%lld elements: need >= K=%lld, a multiple of 8, below 2^31",
+                    (long long)ldx, (long long)K);
+    if (ldq < q_row_bytes || ldq % 16 || ldq >= LD_LIMIT)
+        return fail(QGEMM_ERR_BAD_LAYOUT, "ldq=%lld bytes: need >= %lld, a multiple of 16, below 2^31",
+                    (long long)ldq, (long long)q_row_bytes);
+    return QGEMM_OK;
+}
+
+qgemm_status qgemm_quant_f8_pertoken(const uint16_t *X, int64_t ldx, uint8_t *Q, int64_t ldq, float *scale,
+                                     int64_t M, int64_t K, void *stream)
+{
+    TRY(check_quant(X, ldx, Q, ldq, M, K, K));
+    if (M == 0)
+        return QGEMM_OK;
+    if (!scale)
+        return fail(QGEMM_ERR_NULL_POINTER, "scale is NULL");
+    if (!aligned(scale, 4))
+        return fail(QGEMM_ERR_BAD_LAYOUT, "scale is not 4-byte aligned");
+    TRY(check_device());
+    return finish(launch_quant_f8_pertoken(X, ldx, Q, ldq, scale, (int)M, (int)K, (hipStream_t)stream));
+}
+
+qgemm_status qgemm_quant_mx(qgemm_mx_fmt fmt, const uint16_t *X, int64_t ldx, void *Q, int64_t ldq, uint8_t *S,
+                            int64_t lds, int64_t M, int64_t K, void *stream)
+{
+    if (fmt != QGEMM_MX_E4M3 && fmt != QGEMM_MX_E2M1)
+        return fail(QGEMM_ERR_BAD_FORMAT, "unknown MX element format %d", (int)fmt);
+    TRY(check_quant(X, ldx, Q, ldq, M, K, fmt == QGEMM_MX_E4M3 ? K : K / 2));
+    if (M == 0)
+        return QGEMM_OK;
+    if (!S)
+        return fail(QGEMM_ERR_NULL_POINTER, "S is NULL");
+    if (lds < K / 32 || lds >= LD_LIMIT)
+        return fail(QGEMM_ERR_BAD_LAYOUT, "lds=%lld bytes: need >= K/32=%lld, below 2^31", (long long)lds,
+                    (long long)(K / 32));
+    TRY(check_device());
+    return finish(launch_quant_mx(fmt == QGEMM_MX_E4M3 ? 0 : 1, X, ldx, (uint8_t *)Q, ldq, S, lds, (int)M, (int)K,
+                                  (hipStream_t)stream));
 }
 
 }  // extern "C"

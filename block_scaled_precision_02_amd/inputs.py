@@ -128,6 +128,26 @@ def bf16_bits(x):
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
+# ------------------------------------------------------------ activations
+
+# Activation shapes of the quantisers: the A operand of each GEMM workload.
+QUANT_SHAPES = {"f8": ("f8_ptpc", 4096, 7168), "mxfp8": ("mxfp8", 16384, 2048), "mxfp4": ("mxfp4", 8192, 8192)}
+
+
+def make_activations(M, K, seed=300, rot=0, outlier_cols=8):
+    """bf16 activations [M, K] as bit patterns (uint16): standard normal
+    values, each row scaled by 2^u (u uniform in [-6, 6]) so that rows differ
+    in range, plus a few columns of 16x outliers (the heavy channels that make
+    per-token and per-block scales matter).  Seeded by (seed, rot)."""
+    r = rng(seed, 0, rot)
+    x = r.standard_normal((M, K)).astype(np.float32)
+    x *= np.exp2(r.uniform(-6, 6, (M, 1))).astype(np.float32)
+    if outlier_cols and K:
+        cols = r.choice(K, size=min(outlier_cols, K), replace=False)
+        x[:, cols] *= np.float32(16.0)
+    return bf16_bits(x)
+
+
 # ------------------------------------------------------------ workloads
 
 def make(name, rot=0, M=None, N=None, K=None, bias=None, seed=None):

@@ -133,6 +133,48 @@ qgemm_status qgemm_mx(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const 
                       qgemm_mx_bscale b_layout, const uint16_t *bias, uint16_t *C, int64_t ldc,
                       int64_t M, int64_t N, int64_t K, void *stream);
 
+/* Per-token e4m3 quantiser: the A operand and scale_a of qgemm_f8_pertoken
+ * from bf16 activations.  "perf(gemm-ar): mxfp8 with row-major scales staged
+ * through LDS" (ROCm/mori PR #806), Measured, names the per-token ("ptpc")
+ * scales; the page gives no formula, and the one taken is:
+ *   scale[m] = fp32( amax_m / 448 ),  amax_m = max_k |X[m,k]|  (binary32)
+ *   Q[m,k]   = enc_e4m3( fp32( X[m,k] / scale[m] ) )          (IEEE division)
+ * enc: the nearest e4m3fn value, ties to the even code, magnitudes beyond 448
+ * saturating to 448, the sign bit copied from the value (a negative value
+ * that rounds to zero gives -0, 0x80).  A row of zeros gets scale 0 and each
+ * zero's own sign.
+ *   X      [M, K] bf16 bit patterns, row stride ldx ELEMENTS (multiple of 8)
+ *   Q      [M, K] e4m3fn codes (output), row stride ldq bytes (multiple of 16)
+ *   scale  [M] fp32 (output), 4-byte aligned
+ * X and Q 16-byte aligned; K a positive multiple of 32; Q and scale must not
+ * overlap X.  Inputs are finite: a row holding NaN or infinity gets
+ * unspecified codes and scale.  Nothing outside Q's [M, K] and scale[0..M)
+ * is written. */
+qgemm_status qgemm_quant_f8_pertoken(const uint16_t *X, int64_t ldx, uint8_t *Q, int64_t ldq, float *scale,
+                                     int64_t M, int64_t K, void *stream);
+
+/* MX quantiser: the A operand and scale_a of qgemm_mx from bf16 activations,
+ * one ue8m0 scale per 32 elements of a row, handed over as [M, K/32] uint8
+ * row-major as ROCm/mori PR #806 ("perf(gemm-ar): mxfp8 with row-major scales
+ * staged through LDS", What) describes the quantiser's output.  The scale
+ * rule is the OCP Microscaling v1.0 one:
+ *   X_b   = floor(log2(amax_b)) - emax   (emax 8 for e4m3, 2 for e2m1)
+ *   S     = X_b + 127 clamped to [0, 254]; 0 for an all-zero block
+ *   code  = enc( X[m,k] * 2^-(S - 127) )  (exact scaling by a power of two)
+ * enc as for qgemm_quant_f8_pertoken, on the e4m3fn grid (max 448) or the
+ * e2m1 grid (max 6).
+ *   fmt    QGEMM_MX_E4M3: Q [M, K] bytes; QGEMM_MX_E2M1: Q [M, K/2] bytes,
+ *          element k (k even) in bits 3:0 of byte k/2, k+1 in bits 7:4
+ *   X      [M, K] bf16 bit patterns, row stride ldx ELEMENTS (multiple of 8)
+ *   Q      row stride ldq bytes (multiple of 16)
+ *   S      [M, K/32] ue8m0 codes (output), row stride lds bytes (>= K/32)
+ * X and Q 16-byte aligned; K a positive multiple of 32; outputs must not
+ * overlap X.  Inputs are finite: a block holding NaN or infinity gets
+ * unspecified codes and scale.  Nothing outside Q's [M, K] elements and S's
+ * [M, K/32] is written. */
+qgemm_status qgemm_quant_mx(qgemm_mx_fmt fmt, const uint16_t *X, int64_t ldx, void *Q, int64_t ldq, uint8_t *S,
+                            int64_t lds, int64_t M, int64_t K, void *stream);
+
 /* Text of the last non-OK status returned on the calling thread ("" if none). */
 const char *qgemm_last_error(void);
 
@@ -149,12 +191,16 @@ const char *qgemm_status_string(qgemm_status status);
  *   5: 256x256, 8 waves, operands fetched straight into LDS
  *   6: 192x192, 4 waves, operands fetched straight into LDS
  *   7: 128x128, 4 waves, operands fetched straight into LDS
+ *   8: 16 rows x 16 columns, 8 waves splitting K (small M; INT8 and FP8)
+ *   9: 64 rows x 16 columns, 8 waves splitting K (small M; INT8 and FP8)
  * Tiles 4-7 need K bytes a multiple of 256 and MX scale rows a multiple of
  * 16 bytes; where these hold, the table's 256x256 choice runs as tile 5,
- * 192x192 as tile 6 and 128x128 as tile 7. */
+ * 192x192 as tile 6 and 128x128 as tile 7.  INT8 and FP8 calls with M <= 64
+ * take tile 8 (M <= 16) or 9. */
 int qgemm_select_tile(int path, int64_t M, int64_t N, int64_t K);
 
-/* Block edge (rows of A = rows of B) of a tile id, or 0 for an unknown id. */
+/* Rows of A one tile covers (for tiles 0-7 also the rows of B; tiles 8 and 9
+ * cover 16 rows of B), or 0 for an unknown id. */
 int qgemm_tile_rows(int tile);
 
 /* Force a tile id for later calls on the calling thread (benchmarks and the

@@ -159,3 +159,55 @@ def test_tile_table_is_sane_everywhere():
             t = L.qgemm_select_tile(0, M, N, 512)
             assert L.qgemm_tile_rows(t) in (16, 64, 128, 192, 256)
             assert L.qgemm_force_tile(-1) == -1
+
+
+def qf8(X=FAKE, ldx=64, Q=FAKE2, ldq=64, s=FAKE3, M=4, K=64):
+    return q.lib().qgemm_quant_f8_pertoken(X, ldx, Q, ldq, s, M, K, None)
+
+
+def qmx(fmt=0, X=FAKE, ldx=64, Q=FAKE2, ldq=64, S=FAKE3, lds=2, M=4, K=64):
+    return q.lib().qgemm_quant_mx(fmt, X, ldx, Q, ldq, S, lds, M, K, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), q.QGEMM_ERR_NULL_POINTER),
+    (dict(Q=None), q.QGEMM_ERR_NULL_POINTER),
+    (dict(s=None), q.QGEMM_ERR_NULL_POINTER),
+    (dict(K=48, ldx=48, ldq=48), q.QGEMM_ERR_BAD_SHAPE),
+    (dict(M=-1), q.QGEMM_ERR_BAD_SHAPE),
+    (dict(ldx=32), q.QGEMM_ERR_BAD_LAYOUT),          # below the row
+    (dict(ldx=68), q.QGEMM_ERR_BAD_LAYOUT),          # not a multiple of 8 elements
+    (dict(ldq=72), q.QGEMM_ERR_BAD_LAYOUT),          # not a multiple of 16 bytes
+    (dict(X=FAKE + 8), q.QGEMM_ERR_BAD_LAYOUT),
+    (dict(s=FAKE3 + 2), q.QGEMM_ERR_BAD_LAYOUT),
+])
+def test_quant_f8_rejects(kw, status):
+    assert qf8(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(fmt=2), q.QGEMM_ERR_BAD_FORMAT),
+    (dict(S=None), q.QGEMM_ERR_NULL_POINTER),
+    (dict(lds=1), q.QGEMM_ERR_BAD_LAYOUT),           # below K/32
+    (dict(fmt=0, ldq=48), q.QGEMM_ERR_BAD_LAYOUT),   # e4m3 row is K bytes
+    (dict(Q=FAKE2 + 4), q.QGEMM_ERR_BAD_LAYOUT),
+    (dict(K=0), q.QGEMM_ERR_BAD_SHAPE),
+])
+def test_quant_mx_rejects(kw, status):
+    assert qmx(**kw) == status
+
+
+def test_quant_row_lengths_and_noops():
+    # e2m1 codes take K/2 bytes a row; M = 0 is a no-op with no device call
+    assert qmx(fmt=1, ldq=32, M=0) == q.QGEMM_OK
+    assert qf8(M=0) == q.QGEMM_OK
+    assert qmx(M=0) == q.QGEMM_OK
+
+
+def test_quant_checks_pass_before_the_device_check(monkeypatch):
+    """Valid arguments reach the device check (refused here by a fake
+    architecture, before any HIP call): e2m1 rows of K/2 bytes are accepted."""
+    monkeypatch.setenv("QGEMM_FAKE_ARCH", "gfx1201")
+    assert qmx(fmt=1, ldq=32) == q.QGEMM_ERR_UNSUPPORTED_DEVICE
+    assert qmx(fmt=0) == q.QGEMM_ERR_UNSUPPORTED_DEVICE
+    assert qf8() == q.QGEMM_ERR_UNSUPPORTED_DEVICE
