@@ -102,12 +102,13 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_digest():
-    """sha256 over every kernel source file (name and bytes, sorted by name)."""
+    """sha256 over the GEMM's kernel source files (name and bytes, sorted by
+    name); the activation quantisers' own files are not part of it."""
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(ROOT, KERNEL_SOURCES)
     for n in sorted(os.listdir(d)):
-        if n.endswith((".hip", ".hpp", ".cpp", ".h")):
+        if n.endswith((".hip", ".hpp", ".cpp", ".h")) and not n.startswith("qgemm_quant"):
             h.update(n.encode())
             h.update(open(os.path.join(d, n), "rb").read())
     return h.hexdigest()

@@ -11,14 +11,16 @@
 //
 // Both kernels move bytes and do a little ALU work per element: HBM-bound,
 // no matrix cores.
-//  * Per-token: one wave per row.  A lane keeps up to 16 of its row's
-//    16-byte pieces in registers (rows up to 8192 elements are read once),
-//    takes the row's max |x| by butterfly shuffles, then divides and rounds
-//    from the registers; pieces beyond the 16 are read again (from L2).
+//  * Per-token: one workgroup of 256 threads per row.  A thread keeps up to
+//    4 of the row's 16-byte pieces in registers (rows up to 8192 elements
+//    are read once); the row's max |x| comes from butterfly shuffles within
+//    each wave and the four wave maxima in LDS; then each thread divides and
+//    rounds from its registers, re-reading (from L2) pieces beyond the 4.
 //    The division is the IEEE binary32 one (the compiler's correctly rounded
 //    sequence), as the definition fixes the quotient.
 //  * MX: four lanes per 32-element block, 8 elements (one 16-byte load) per
-//    lane; the block's max |x| by two shuffles; the scale code comes from the
+//    lane and four such blocks per thread, all loaded first; the block's max
+//    |x| by two shuffles; the scale code comes from the
 //    max's binary32 exponent field E: floor(log2 amax) = E - 127 for a normal
 //    amax, and a subnormal or zero amax gives code 0 either way, so the code
 //    is max(E - emax, 0).  Scaling by 2^(127 - code) is exact (a power of two,
@@ -87,7 +89,8 @@ __device__ __forceinline__ float piece_amax(u32x4q w)
 
 // ------------------------------------------------------------ per-token e4m3
 
-constexpr int PT_KEEP = 16;   // 16-byte pieces a lane keeps in registers
+constexpr int PT_THREADS = 256;   // one workgroup per row
+constexpr int PT_KEEP = 4;        // 16-byte pieces a thread keeps in registers
 
 __device__ __forceinline__ u32x2q pertoken_codes(u32x4q w, float s)
 {
@@ -102,13 +105,11 @@ __device__ __forceinline__ u32x2q pertoken_codes(u32x4q w, float s)
     return u32x2q{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
 }
 
-__global__ void __launch_bounds__(256) quant_f8_pertoken_kernel(const uint16_t *X, int64_t ldx, uint8_t *Q,
-                                                                 int64_t ldq, float *scale, int M, int K)
+__global__ void __launch_bounds__(PT_THREADS) quant_f8_pertoken_kernel(const uint16_t *X, int64_t ldx, uint8_t *Q,
+                                                                        int64_t ldq, float *scale, int M, int K)
 {
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-    if (row >= M)
-        return;   // the whole wave
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int row = blockIdx.x;
     const u32x4q *x = (const u32x4q *)(X + (int64_t)row * ldx);
     u32x2q *q = (u32x2q *)(Q + (int64_t)row * ldq);
     const int nv = K / 8;
@@ -116,74 +117,97 @@ __global__ void __launch_bounds__(256) quant_f8_pertoken_kernel(const uint16_t *
     u32x4q keep[PT_KEEP];
 #pragma unroll
     for (int c = 0; c < PT_KEEP; ++c) {
-        const int v = lane + 64 * c;
+        const int v = t + PT_THREADS * c;
         keep[c] = v < nv ? x[v] : u32x4q{0, 0, 0, 0};
     }
     float amax = 0.0f;
 #pragma unroll
     for (int c = 0; c < PT_KEEP; ++c)
         amax = fmaxf(amax, piece_amax(keep[c]));
-    for (int v = lane + 64 * PT_KEEP; v < nv; v += 64)
+    for (int v = t + PT_THREADS * PT_KEEP; v < nv; v += PT_THREADS)
         amax = fmaxf(amax, piece_amax(x[v]));
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1)
         amax = fmaxf(amax, __shfl_xor(amax, off));
+    __shared__ float wmax[PT_THREADS / 64];
+    if (lane == 0)
+        wmax[wave] = amax;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < PT_THREADS / 64; ++w)
+        amax = fmaxf(amax, wmax[w]);
 
     const float s = amax / 448.0f;
-    if (lane == 0)
+    if (t == 0)
         scale[row] = s;
 #pragma unroll
     for (int c = 0; c < PT_KEEP; ++c) {
-        const int v = lane + 64 * c;
+        const int v = t + PT_THREADS * c;
         if (v < nv)
             q[v] = pertoken_codes(keep[c], s);
     }
-    for (int v = lane + 64 * PT_KEEP; v < nv; v += 64)
+    for (int v = t + PT_THREADS * PT_KEEP; v < nv; v += PT_THREADS)
         q[v] = pertoken_codes(x[v], s);
 }
 
 // ------------------------------------------------------------ MX
 
-// Thread g of the launch handles 8 elements: quarter g % 4 of block g / 4 of
-// the launch's rows (row r0 + (g / 4) / kb, block (g / 4) % kb).  The grid
-// covers rows * kb * 4 threads (< 2^31: the host splits larger calls).
+constexpr int MX_U = 4;   // quarter blocks per thread, loaded before any is used
+
+// Quarter g of the launch (8 elements, one 16-byte load) is quarter g % 4 of
+// block g / 4 of the launch's rows: row (g / 4) / kb, block (g / 4) % kb.
+// Thread t of workgroup w takes the quarters w * 1024 + t + 256 u, u < 4, so
+// a block's four quarters sit on four neighbouring lanes.  The launch covers
+// rows * kb * 4 quarters (below 2^31: the host splits larger calls).
 template <int FMT>
 __global__ void __launch_bounds__(256) quant_mx_kernel(const uint16_t *X, int64_t ldx, uint8_t *Q, int64_t ldq,
                                                        uint8_t *S, int64_t lds, unsigned rows, unsigned kb)
 {
     constexpr unsigned EMAX = FMT == 0 ? 8u : 2u;
-    const unsigned g = blockIdx.x * 256u + threadIdx.x;
-    const unsigned blk = g >> 2, part = g & 3u;
-    const unsigned row = blk / kb, b = blk - row * kb;
-    if (row >= rows)
-        return;   // whole groups of four: the grid is a multiple of 4 threads
-    const u32x4q w = *(const u32x4q *)(X + (int64_t)row * ldx + 32 * b + 8 * part);
-    float amax = piece_amax(w);
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    const unsigned E = (__float_as_uint(amax) >> 23) & 0xffu;
-    const unsigned code = E > EMAX ? E - EMAX : 0u;            // <= 254 - EMAX for finite input
-    const float mul = __uint_as_float((254u - code) << 23);    // 2^(127 - code)
-    unsigned c[8];
+    const unsigned total = rows * kb * 4u;
+    const unsigned base = blockIdx.x * (256u * MX_U) + threadIdx.x, part = threadIdx.x & 3u;
+    u32x4q w[MX_U];
+    unsigned row[MX_U], b[MX_U];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const float lo = bf16_lo(w[q]) * mul, hi = bf16_hi(w[q]) * mul;
-        c[2 * q] = FMT == 0 ? enc_e4m3(lo) : enc_e2m1(lo);
-        c[2 * q + 1] = FMT == 0 ? enc_e4m3(hi) : enc_e2m1(hi);
+    for (int u = 0; u < MX_U; ++u) {
+        const unsigned g = base + 256u * u, blk = g >> 2;
+        row[u] = blk / kb;
+        b[u] = blk - row[u] * kb;
+        // a block's four lanes agree on g < total (total is a multiple of 4)
+        w[u] = g < total ? *(const u32x4q *)(X + (int64_t)row[u] * ldx + 32 * b[u] + 8 * part)
+                         : u32x4q{0, 0, 0, 0};
     }
-    uint8_t *qrow = Q + (int64_t)row * ldq;
-    if constexpr (FMT == 0) {
-        *(u32x2q *)(qrow + 32 * b + 8 * part) =
-            u32x2q{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
-    } else {
-        unsigned v = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            v |= c[i] << (4 * i);                                // element 2j low nibble, 2j+1 high
-        *(unsigned *)(qrow + 16 * b + 4 * part) = v;
+    for (int u = 0; u < MX_U; ++u) {
+        float amax = piece_amax(w[u]);
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        if (base + 256u * u >= total)
+            continue;
+        const unsigned E = (__float_as_uint(amax) >> 23) & 0xffu;
+        const unsigned code = E > EMAX ? E - EMAX : 0u;            // <= 254 - EMAX for finite input
+        const float mul = __uint_as_float((254u - code) << 23);    // 2^(127 - code)
+        unsigned c[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float lo = bf16_lo(w[u][q]) * mul, hi = bf16_hi(w[u][q]) * mul;
+            c[2 * q] = FMT == 0 ? enc_e4m3(lo) : enc_e2m1(lo);
+            c[2 * q + 1] = FMT == 0 ? enc_e4m3(hi) : enc_e2m1(hi);
+        }
+        uint8_t *qrow = Q + (int64_t)row[u] * ldq;
+        if constexpr (FMT == 0) {
+            *(u32x2q *)(qrow + 32 * b[u] + 8 * part) = u32x2q{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                                                              c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
+        } else {
+            unsigned v = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v |= c[i] << (4 * i);                            // element 2j low nibble, 2j+1 high
+            *(unsigned *)(qrow + 16 * b[u] + 4 * part) = v;
+        }
+        if (part == 0)
+            S[(int64_t)row[u] * lds + b[u]] = (uint8_t)code;
     }
-    if (part == 0)
-        S[(int64_t)row * lds + b] = (uint8_t)code;
 }
 
 // ------------------------------------------------------------ launchers
@@ -191,8 +215,8 @@ __global__ void __launch_bounds__(256) quant_mx_kernel(const uint16_t *X, int64_
 hipError_t launch_quant_f8_pertoken(const uint16_t *X, int64_t ldx, uint8_t *Q, int64_t ldq, float *scale,
                                     int M, int K, hipStream_t s)
 {
-    const unsigned grid = (unsigned)((M + 3) / 4);
-    hipLaunchKernelGGL(quant_f8_pertoken_kernel, dim3(grid), dim3(256), 0, s, X, ldx, Q, ldq, scale, M, K);
+    hipLaunchKernelGGL(quant_f8_pertoken_kernel, dim3((unsigned)M), dim3(PT_THREADS), 0, s, X, ldx, Q, ldq, scale,
+                       M, K);
     return hipGetLastError();
 }
 
@@ -200,12 +224,13 @@ hipError_t launch_quant_mx(int fmt, const uint16_t *X, int64_t ldx, uint8_t *Q, 
                            int64_t lds, int M, int K, hipStream_t s)
 {
     const int64_t kb = K / 32;
-    // rows per launch: keep rows * kb * 4 threads (rounded up to whole
+    // rows per launch: keep rows * kb * 4 quarters (rounded up to whole
     // workgroups) below 2^31
-    const int64_t max_rows = (((int64_t)1 << 31) - 256) / (4 * kb);
+    const int64_t per_wg = 256 * MX_U;
+    const int64_t max_rows = (((int64_t)1 << 31) - per_wg) / (4 * kb);
     for (int64_t r0 = 0; r0 < M; r0 += max_rows) {
         const int64_t rows = M - r0 < max_rows ? M - r0 : max_rows;
-        const unsigned grid = (unsigned)((rows * kb * 4 + 255) / 256);
+        const unsigned grid = (unsigned)((rows * kb * 4 + per_wg - 1) / per_wg);
         const uint16_t *x = X + r0 * ldx;
         uint8_t *q = Q + r0 * ldq;
         uint8_t *sc = S + r0 * lds;
