@@ -13,6 +13,8 @@ Functions follow the definitions in ``qgemm_oracle.c``:
                   Measured: "ptpc").
   mx           -- MX e4m3 / e2m1 with ue8m0 per 32 K elements (ROCm/mori PR
                   #806, What; ROCm/FlyDSL PR #990).
+  pack_b       -- the prepacked weight layout of the ``_prepacked`` GEMM entry
+                  points (defined in ``qgemm_oracle.c``).
   quant_f8_pertoken, quant_mx
                -- the activation quantisers producing those operands from
                   bf16 (ROCm/mori PR #806, What: the quantiser's [M, K/32]
@@ -74,6 +76,8 @@ def _load():
     lib.orc_quant_f8_pertoken.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64]
     lib.orc_quant_mx.restype = ctypes.c_int
     lib.orc_quant_mx.argtypes = [ctypes.c_int, _P, _I64, _P, _I64, _P, _I64, _I64, _I64]
+    lib.orc_pack_b.restype = None
+    lib.orc_pack_b.argtypes = [_P, _I64, _I64, _I64, _P]
     lib.orc_i8_rowwise.restype = ctypes.c_int
     lib.orc_i8_rowwise.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _P, _I64, _P,
                                    _I64, _I64, _I64]
@@ -237,3 +241,14 @@ def quant_mx(fmt, X):
     if rc != 0:
         raise ValueError("bad MX format")
     return Q, S
+
+
+def pack_b(B):
+    """B [N, row_bytes] bytes (row_bytes % 64 == 0) -> the prepacked layout,
+    uint8 [ceil(N/16) * 16 * row_bytes]."""
+    B = _c(B, np.uint8)
+    N, row = B.shape
+    assert row % 64 == 0
+    out = np.empty(((N + 15) // 16) * 16 * row, np.uint8)
+    _load().orc_pack_b(_ptr(B), row, N, row, _ptr(out))
+    return out

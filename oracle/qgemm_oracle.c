@@ -375,6 +375,33 @@ int orc_quant_mx(int fmt, const uint16_t *X, int64_t ldx, uint8_t *Q, int64_t ld
     return 0;
 }
 
+/* ---------------------------------------------------------- prepacked B */
+
+/* The weight layout the prepacked GEMM entry points read.  Both MI355X GEMMs
+ * on the pages take B in a layout prepared once ("gemm_a8w8_bpreshuffle" in
+ * ROCm/aiter PR #6262, description; the "BpreShuffle" FP4 kernel compared
+ * against in ROCm/FlyDSL PR #990, description); their orders are their own
+ * kernels'.  This library's order: B (N rows of row_bytes bytes, row_bytes a
+ * multiple of 64) becomes ceil(N/16) groups of 16 rows; group R is
+ * nst = row_bytes/64 blocks of 1024 bytes, block t holding bytes
+ * 64t .. 64t+63 of rows 16R .. 16R+15: its 16-byte slot p (0..63) is row
+ * 16R + p/4, bytes 64t + 16c .. 64t + 16c + 15 with c = (p mod 4) XOR
+ * ((p / 16) mod 4).  Rows at or past N are zeros.
+ * Bp[((R*nst + t)*64 + p)*16 + b] = B[16R + p/4][64t + 16c + b]. */
+void orc_pack_b(const uint8_t *B, int64_t ldb, int64_t N, int64_t row_bytes, uint8_t *Bp)
+{
+    const int64_t nst = row_bytes / 64, groups = (N + 15) / 16;
+    for (int64_t R = 0; R < groups; ++R)
+        for (int64_t t = 0; t < nst; ++t)
+            for (int p = 0; p < 64; ++p) {
+                const int64_t row = 16 * R + p / 4;
+                const int c = (p % 4) ^ ((p / 16) % 4);
+                uint8_t *dst = Bp + ((R * nst + t) * 64 + p) * 16;
+                for (int b = 0; b < 16; ++b)
+                    dst[b] = row < N ? B[row * ldb + 64 * t + 16 * c + b] : 0;
+            }
+}
+
 /* ------------------------------------------------- array forms for tests */
 
 void orc_enc_e4m3_array(const double *in, uint8_t *out, int64_t n)
