@@ -52,7 +52,7 @@ class Launcher:
     """Binds one workload's device buffers to a direct C-ABI call (the
     binding's argument checks are done once, outside the timed loop)."""
 
-    def __init__(self, d, sets, out, stream):
+    def __init__(self, d, sets, out, stream, prepacked=False):
         import block_scaled_precision_02_amd as q
         self.L = q.lib()
         self.d = d
@@ -64,6 +64,25 @@ class Launcher:
         self.args = []
         for s in sets:
             bias = None if s["bias"] is None else s["bias"].data_ptr()
+            if prepacked:
+                # B prepacked once, outside the timed region (the weights are static)
+                pb = q.qgemm_prepack_b(s["B"]).data
+                s["Bp"] = pb
+                if d["kind"] == "i8":
+                    a = (s["A"].data_ptr(), s["A"].stride(0), pb.data_ptr(), s["scale_a"].data_ptr(),
+                         s["scale_b"].data_ptr(), bias, out.data_ptr(), self.ldc, d["M"], N, d["K"], self.stream)
+                    self.args.append((self.L.qgemm_i8_rowwise_prepacked, a))
+                elif d["kind"] == "f8":
+                    a = (s["A"].data_ptr(), s["A"].stride(0), pb.data_ptr(), s["scale_a"].data_ptr(),
+                         s["scale_b"].data_ptr(), bias, out.data_ptr(), self.ldc, d["M"], N, d["K"], self.stream)
+                    self.args.append((self.L.qgemm_f8_pertoken_prepacked, a))
+                else:
+                    fmt = 0 if d["fmt"] == "e4m3" else 1
+                    a = (fmt, s["A"].data_ptr(), s["A"].stride(0), pb.data_ptr(), s["scale_a"].data_ptr(),
+                         s["scale_b"].data_ptr(), d["b_rows_per_scale"], bias, out.data_ptr(), self.ldc, d["M"], N,
+                         d["K"], self.stream)
+                    self.args.append((self.L.qgemm_mx_prepacked, a))
+                continue
             if d["kind"] == "i8":
                 a = (s["A"].data_ptr(), s["A"].stride(0), s["B"].data_ptr(), s["B"].stride(0),
                      s["scale_a"].data_ptr(), s["scale_b"].data_ptr(), bias, out.data_ptr(),
@@ -103,12 +122,13 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 def kernel_digest():
     """sha256 over the GEMM's kernel source files (name and bytes, sorted by
-    name); the activation quantisers' own files are not part of it."""
+    name); the activation quantisers' and the B prepacking's own files are
+    not part of it."""
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(ROOT, KERNEL_SOURCES)
     for n in sorted(os.listdir(d)):
-        if n.endswith((".hip", ".hpp", ".cpp", ".h")) and not n.startswith("qgemm_quant"):
+        if n.endswith((".hip", ".hpp", ".cpp", ".h")) and not n.startswith(("qgemm_quant", "qgemm_pack")):
             h.update(n.encode())
             h.update(open(os.path.join(d, n), "rb").read())
     return h.hexdigest()
@@ -285,6 +305,8 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead: time a plain device copy of this many bytes (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--prepacked", action="store_true",
+                    help="B prepacked once (qgemm_prepack_b) and the _prepacked entry points timed")
     ap.add_argument("--quant", default=None, choices=["f8", "mxfp8", "mxfp4"],
                     help="instead: time the activation quantiser on the A shape of that workload")
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
@@ -328,7 +350,7 @@ def main():
     M, N, K = d0["M"], d0["N"], d0["K"]
     out = torch.empty((M, N + (-N) % 8), dtype=torch.bfloat16, device="cuda")[:, :N]
     stream = torch.cuda.current_stream()
-    run = Launcher(d0, sets, out, stream.cuda_stream)
+    run = Launcher(d0, sets, out, stream.cuda_stream, prepacked=args.prepacked)
     tile = q.select_tile({"i8": 0, "f8": 1, "e4m3": 2, "e2m1": 3}[dtype_of(d0)], M, N, K)
     if args.tile >= 0:
         q.force_tile(args.tile)
@@ -365,7 +387,8 @@ def main():
     else:
         roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": unit_of(d0),
                     "frac": round(achieved / peak, 4)}
-    roofline.update({"traffic": None if shape else traffic_bytes(name), "kernel_ms": round(kernel_ms, 6),
+    roofline.update({"traffic": None if (shape or args.prepacked) else traffic_bytes(name),
+                     "kernel_ms": round(kernel_ms, 6),
                      "algorithmic_bytes": nbytes})
 
     res = {
@@ -381,7 +404,8 @@ def main():
         "vs_baseline": round(value / PAGES_I8_QKV_TOPS, 4) if name == "i8_qkv" and not shape else None,
         "dtype": {"i8": "int8", "f8": "e4m3", "e4m3": "mxfp8-e4m3", "e2m1": "mxfp4-e2m1"}[dtype_of(d0)],
         "data": "synthetic",
-        "config": {"workload": f"{name} M={M} N={N} K={K}" + (" bias" if d0["bias"] is not None else ""),
+        "config": {"workload": f"{name} M={M} N={N} K={K}" + (" bias" if d0["bias"] is not None else "")
+                   + (" prepacked B" if args.prepacked else ""),
                    "tile_id": tile, "rotating_sets": R, "pct_of_peak": round(100 * value / peak, 2)},
         "roofline": roofline,
         "cpu_baseline": None,

@@ -12,6 +12,10 @@ call raises.
     qgemm_i8_acc_i32(A, B, out=None)
     qgemm_f8_pertoken(A, B, scale_a, scale_b, bias=None, out=None)
     qgemm_mx(fmt, A, B, scale_a, scale_b, b_layout, bias=None, out=None, K=None)
+    qgemm_prepack_b(B, row_bytes=None, out=None)          -> PackedB
+    qgemm_i8_rowwise_prepacked(A, Bp, scale_a, scale_b, bias=None, out=None)
+    qgemm_f8_pertoken_prepacked(A, Bp, scale_a, scale_b, bias=None, out=None)
+    qgemm_mx_prepacked(fmt, A, Bp, scale_a, scale_b, b_layout, bias=None, out=None)
     qgemm_quant_f8_pertoken(X, out=None, scale=None)      -> (Q, scale)
     qgemm_quant_mx(fmt, X, out=None, scales=None)         -> (Q, S)
 
@@ -41,6 +45,8 @@ QGEMM_MX_BSCALE_32x32 = 32
 
 # Every symbol include/qgemm.h declares.
 EXPORTS = ("qgemm_i8_rowwise", "qgemm_i8_acc_i32", "qgemm_f8_pertoken", "qgemm_mx",
+           "qgemm_prepacked_b_bytes", "qgemm_prepack_b", "qgemm_i8_rowwise_prepacked",
+           "qgemm_f8_pertoken_prepacked", "qgemm_mx_prepacked",
            "qgemm_quant_f8_pertoken", "qgemm_quant_mx",
            "qgemm_last_error", "qgemm_status_string", "qgemm_select_tile",
            "qgemm_tile_rows", "qgemm_force_tile")
@@ -69,6 +75,17 @@ def lib():
     L.qgemm_mx.restype = st
     L.qgemm_mx.argtypes = [ctypes.c_int, _P, _I64, _P, _I64, _P, _P, ctypes.c_int, _P, _P, _I64,
                            _I64, _I64, _I64, _P]
+    L.qgemm_prepacked_b_bytes.restype = _I64
+    L.qgemm_prepacked_b_bytes.argtypes = [_I64, _I64]
+    L.qgemm_prepack_b.restype = st
+    L.qgemm_prepack_b.argtypes = [_P, _I64, _I64, _I64, _P, _P]
+    L.qgemm_i8_rowwise_prepacked.restype = st
+    L.qgemm_i8_rowwise_prepacked.argtypes = [_P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
+    L.qgemm_f8_pertoken_prepacked.restype = st
+    L.qgemm_f8_pertoken_prepacked.argtypes = [_P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
+    L.qgemm_mx_prepacked.restype = st
+    L.qgemm_mx_prepacked.argtypes = [ctypes.c_int, _P, _I64, _P, _P, _P, ctypes.c_int, _P, _P, _I64, _I64, _I64,
+                                     _I64, _P]
     L.qgemm_quant_f8_pertoken.restype = st
     L.qgemm_quant_f8_pertoken.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64, _P]
     L.qgemm_quant_mx.restype = st
@@ -359,3 +376,103 @@ def qgemm_quant_mx(fmt, X, out=None, scales=None, stream=None):
         _check(lib().qgemm_quant_mx(fmt, _ptr(X), ldx, _ptr(out), _ld_bytes(out, row), _ptr(scales), lds, M, K,
                                     _stream(X.device, stream)))
     return out, scales
+
+
+# ------------------------------------------------------------ prepacked B
+
+class PackedB:
+    """A B operand in the prepacked layout: ``data`` (uint8 device tensor of
+    qgemm_prepacked_b_bytes(N, row_bytes) bytes), the row count N and the
+    row length in bytes of the B it was made from."""
+
+    def __init__(self, data, N, row_bytes):
+        self.data, self.N, self.row_bytes = data, N, row_bytes
+
+
+def qgemm_prepack_b(B, out=None, stream=None):
+    """B [N, row_bytes] (int8, e4m3 or e2m1 bytes; row_bytes a multiple of
+    256) -> PackedB, for the ``_prepacked`` GEMMs."""
+    torch = _torch()
+    ldb = _operand(B, "B", (torch.int8, torch.uint8, torch.float8_e4m3fn))
+    N, row = B.shape[0], B.shape[1] * B.element_size()
+    nbytes = lib().qgemm_prepacked_b_bytes(N, row)
+    if nbytes < 0:
+        raise ValueError(f"B rows of {row} bytes cannot be prepacked (need a multiple of 256)")
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=B.device)
+    if out.numel() * out.element_size() != nbytes or not out.is_contiguous() or out.device != B.device:
+        raise ValueError(f"out must be a contiguous buffer of {nbytes} bytes on {B.device}")
+    with torch.cuda.device(B.device):
+        _check(lib().qgemm_prepack_b(_ptr(B), ldb, N, row, _ptr(out), _stream(B.device, stream)))
+    return PackedB(out, N, row)
+
+
+def _packed(Bp, row):
+    if not isinstance(Bp, PackedB):
+        raise ValueError("Bp must be a PackedB from qgemm_prepack_b")
+    if Bp.row_bytes != row:
+        raise ValueError(f"Bp was packed from rows of {Bp.row_bytes} bytes; A's rows are {row} bytes")
+    return Bp
+
+
+def qgemm_i8_rowwise_prepacked(A, Bp, scale_a, scale_b, bias=None, out=None, stream=None):
+    """INT8 rowwise GEMM with a prepacked B -> bf16 [M, N]."""
+    torch = _torch()
+    lda = _operand(A, "A", (torch.int8,))
+    M, K = A.shape
+    Bp = _packed(Bp, K)
+    N = Bp.N
+    sa = _vector(scale_a, "scale_a", M, (torch.float32,))
+    sb = _vector(scale_b, "scale_b", N, (torch.float32,))
+    bias = _bias(bias, N)
+    _same_device(A.device, Bp.data, sa, sb, bias)
+    out = _out(out, M, N, A.device, torch.bfloat16)
+    with torch.cuda.device(A.device):
+        _check(lib().qgemm_i8_rowwise_prepacked(_ptr(A), lda, _ptr(Bp.data), _ptr(sa), _ptr(sb), _ptr(bias),
+                                                _ptr(out), _ldc(out, N), M, N, K, _stream(A.device, stream)))
+    return out
+
+
+def qgemm_f8_pertoken_prepacked(A, Bp, scale_a, scale_b, bias=None, out=None, stream=None):
+    """FP8 per-token / per-channel GEMM with a prepacked B -> bf16 [M, N]."""
+    torch = _torch()
+    lda = _operand(A, "A", _fp8_dtypes())
+    M, K = A.shape
+    Bp = _packed(Bp, K)
+    N = Bp.N
+    sa = _vector(scale_a, "scale_a", M, (torch.float32,))
+    sb = _vector(scale_b, "scale_b", N, (torch.float32,))
+    bias = _bias(bias, N)
+    _same_device(A.device, Bp.data, sa, sb, bias)
+    out = _out(out, M, N, A.device, torch.bfloat16)
+    with torch.cuda.device(A.device):
+        _check(lib().qgemm_f8_pertoken_prepacked(_ptr(A), lda, _ptr(Bp.data), _ptr(sa), _ptr(sb), _ptr(bias),
+                                                 _ptr(out), _ldc(out, N), M, N, K, _stream(A.device, stream)))
+    return out
+
+
+def qgemm_mx_prepacked(fmt, A, Bp, scale_a, scale_b, b_layout, bias=None, out=None, stream=None):
+    """MX GEMM with a prepacked B -> bf16 [M, N] (scales as for qgemm_mx)."""
+    torch = _torch()
+    dts = (torch.uint8, torch.float8_e4m3fn) if fmt == QGEMM_MX_E4M3 else (torch.uint8,)
+    lda = _operand(A, "A", dts)
+    M, row = A.shape
+    Bp = _packed(Bp, row)
+    N = Bp.N
+    K = row if fmt == QGEMM_MX_E4M3 else 2 * row
+    brows = -(-N // b_layout) if b_layout in (1, 32) else N
+    if scale_a is None or tuple(scale_a.shape) != (M, K // 32):
+        raise ValueError(f"scale_a must be [{M}, {K // 32}]")
+    if scale_b is None or tuple(scale_b.shape) != (brows, K // 32):
+        raise ValueError(f"scale_b must be [{brows}, {K // 32}]")
+    sa = _vector(scale_a.reshape(-1) if scale_a.is_contiguous() else scale_a, "scale_a", M * (K // 32),
+                 (torch.uint8,))
+    sb = _vector(scale_b.reshape(-1) if scale_b.is_contiguous() else scale_b, "scale_b", brows * (K // 32),
+                 (torch.uint8,))
+    bias = _bias(bias, N)
+    _same_device(A.device, Bp.data, sa, sb, bias)
+    out = _out(out, M, N, A.device, torch.bfloat16)
+    with torch.cuda.device(A.device):
+        _check(lib().qgemm_mx_prepacked(fmt, _ptr(A), lda, _ptr(Bp.data), _ptr(sa), _ptr(sb), b_layout,
+                                        _ptr(bias), _ptr(out), _ldc(out, N), M, N, K, _stream(A.device, stream)))
+    return out

@@ -20,6 +20,7 @@
 
 #include "../../include/qgemm.h"
 #include "qgemm_launch.hpp"
+#include "qgemm_pack.hpp"
 #include "qgemm_quant.hpp"
 
 using namespace qgemm;
@@ -284,6 +285,21 @@ int pick_tile(int path, Shape s, int64_t kbytes, bool svec, bool bf16_out)
     return t;
 }
 
+// A prepacked B is read only by the LDS-fetch and small-M kernels (the caller
+// checked that K fits them): a forced register-staged tile runs as the
+// LDS-fetch kernel of its edge, and the table's choice as for row-major B.
+int pick_tile_packed(int path, Shape s, int64_t kbytes, bool bf16_out)
+{
+    const int t = pick_tile(path, s, kbytes, true, bf16_out);
+    switch (t) {
+    case 0: return g_forced_tile == 0 ? DMA_TILE : DMA8_TILE;
+    case 1: return DMA128_TILE;
+    case 2: return DMA8_TILE;
+    case 3: return DMA192_TILE;
+    default: return t;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -327,23 +343,43 @@ int qgemm_force_tile(int tile)
     return prev;
 }
 
-static qgemm_status i8_common(const int8_t *A, int64_t lda, const int8_t *B, int64_t ldb, const float *sa,
+// A prepacked B (qgemm_prepack_b's layout): 16-byte aligned, row bytes a
+// whole number of the LDS-fetch kernel's 4 x 64-byte stage rounds.
+static qgemm_status check_packed_b(const void *Bp, int64_t row_bytes)
+{
+    if (!Bp)
+        return fail(QGEMM_ERR_NULL_POINTER, "Bp is NULL");
+    if (!aligned(Bp, 16))
+        return fail(QGEMM_ERR_BAD_LAYOUT, "Bp is not 16-byte aligned");
+    if (row_bytes % 256)
+        return fail(QGEMM_ERR_BAD_SHAPE, "a prepacked B needs rows of a multiple of 256 bytes, got %lld",
+                    (long long)row_bytes);
+    if (row_bytes * 256 >= LD_LIMIT)
+        return fail(QGEMM_ERR_BAD_SHAPE, "rows of %lld bytes: 256 rows exceed 2^31 bytes", (long long)row_bytes);
+    return QGEMM_OK;
+}
+
+static qgemm_status i8_common(const int8_t *A, int64_t lda, const void *B, int64_t ldb, const float *sa,
                               const float *sb, const uint16_t *bias, void *C, int64_t ldc, Shape s, void *stream,
-                              int out)
+                              int out, bool packed = false)
 {
     TRY(check_shape(s, true));
     if (s.M == 0 || s.N == 0)
         return QGEMM_OK;
     TRY(check_operand("A", A, lda, s.K));
-    TRY(check_operand("B", B, ldb, s.K));
+    if (packed)
+        TRY(check_packed_b(B, s.K));
+    else
+        TRY(check_operand("B", B, ldb, s.K));
     if (out == OUT_BF16) {
         TRY(check_fp32_scales(sa, sb));
         TRY(check_bias(bias));
     }
     TRY(check_output(C, ldc, s.N, out == OUT_I32 ? 4 : 2));
     TRY(check_device());
-    const int tile = pick_tile(0, s, s.K, true, out == OUT_BF16);
-    Params p = base_params(A, lda, B, ldb, C, ldc, s, s.K, tile);
+    const int tile = packed ? pick_tile_packed(0, s, s.K, out == OUT_BF16) : pick_tile(0, s, s.K, true, out == OUT_BF16);
+    Params p = base_params(A, lda, B, packed ? s.K : ldb, C, ldc, s, s.K, tile);
+    p.b_packed = packed;
     TRY(check_grid(p));
     p.scale_a = sa;
     p.scale_b = sb;
@@ -364,22 +400,26 @@ qgemm_status qgemm_i8_acc_i32(const int8_t *A, int64_t lda, const int8_t *B, int
     return i8_common(A, lda, B, ldb, nullptr, nullptr, nullptr, C, ldc, Shape{M, N, K}, stream, OUT_I32);
 }
 
-qgemm_status qgemm_f8_pertoken(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb, const float *scale_a,
-                               const float *scale_b, const uint16_t *bias, uint16_t *C, int64_t ldc, int64_t M,
-                               int64_t N, int64_t K, void *stream)
+static qgemm_status f8_common(const uint8_t *A, int64_t lda, const void *B, int64_t ldb, const float *scale_a,
+                              const float *scale_b, const uint16_t *bias, uint16_t *C, int64_t ldc, int64_t M,
+                              int64_t N, int64_t K, void *stream, bool packed)
 {
     const Shape s{M, N, K};
     TRY(check_shape(s, false));
     if (M == 0 || N == 0)
         return QGEMM_OK;
     TRY(check_operand("A", A, lda, K));
-    TRY(check_operand("B", B, ldb, K));
+    if (packed)
+        TRY(check_packed_b(B, K));
+    else
+        TRY(check_operand("B", B, ldb, K));
     TRY(check_fp32_scales(scale_a, scale_b));
     TRY(check_bias(bias));
     TRY(check_output(C, ldc, N, 2));
     TRY(check_device());
-    const int tile = pick_tile(1, s, K, true, true);
-    Params p = base_params(A, lda, B, ldb, C, ldc, s, K, tile);
+    const int tile = packed ? pick_tile_packed(1, s, K, true) : pick_tile(1, s, K, true, true);
+    Params p = base_params(A, lda, B, packed ? K : ldb, C, ldc, s, K, tile);
+    p.b_packed = packed;
     TRY(check_grid(p));
     p.scale_a = scale_a;
     p.scale_b = scale_b;
@@ -387,10 +427,17 @@ qgemm_status qgemm_f8_pertoken(const uint8_t *A, int64_t lda, const uint8_t *B, 
     return finish(launch_f8(tile, bias != nullptr, p, (hipStream_t)stream));
 }
 
-qgemm_status qgemm_mx(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const void *B, int64_t ldb_bytes,
-                      const uint8_t *scale_a, const uint8_t *scale_b, qgemm_mx_bscale b_layout,
-                      const uint16_t *bias, uint16_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                      void *stream)
+qgemm_status qgemm_f8_pertoken(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb, const float *scale_a,
+                               const float *scale_b, const uint16_t *bias, uint16_t *C, int64_t ldc, int64_t M,
+                               int64_t N, int64_t K, void *stream)
+{
+    return f8_common(A, lda, B, ldb, scale_a, scale_b, bias, C, ldc, M, N, K, stream, false);
+}
+
+static qgemm_status mx_common(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const void *B, int64_t ldb_bytes,
+                              const uint8_t *scale_a, const uint8_t *scale_b, qgemm_mx_bscale b_layout,
+                              const uint16_t *bias, uint16_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                              void *stream, bool packed)
 {
     const Shape s{M, N, K};
     if (fmt != QGEMM_MX_E4M3 && fmt != QGEMM_MX_E2M1)
@@ -402,14 +449,16 @@ qgemm_status qgemm_mx(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const 
         return QGEMM_OK;
     const int64_t row_bytes = (fmt == QGEMM_MX_E4M3) ? K : K / 2;
     TRY(check_operand("A", A, lda_bytes, row_bytes));
-    TRY(check_operand("B", B, ldb_bytes, row_bytes));
+    if (packed)
+        TRY(check_packed_b(B, row_bytes));
+    else
+        TRY(check_operand("B", B, ldb_bytes, row_bytes));
     if (!scale_a)
         return fail(QGEMM_ERR_NULL_POINTER, "scale_a is NULL");
     if (!scale_b)
         return fail(QGEMM_ERR_NULL_POINTER, "scale_b is NULL");
     TRY(check_bias(bias));
     TRY(check_output(C, ldc, N, 2));
-    TRY(check_device());
     const int path = (fmt == QGEMM_MX_E4M3) ? 2 : 3;
     // Scale words load whole when every lane's bytes of a K step are aligned:
     // e2m1 takes 4 bytes per lane half (K/32 % 4 == 0), e4m3 takes 2 (K/32 even),
@@ -418,8 +467,13 @@ qgemm_status qgemm_mx(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const 
     const int wb = (fmt == QGEMM_MX_E2M1) ? 4 : 2;
     const bool svec = ((K / 32) % wb == 0) && aligned(scale_a, wb) && aligned(scale_b, wb);
     const bool svec16 = svec && aligned(scale_a, 16) && aligned(scale_b, 16);
-    const int tile = pick_tile(path, s, row_bytes, svec16, true);
-    Params p = base_params(A, lda_bytes, B, ldb_bytes, C, ldc, s, row_bytes, tile);
+    if (packed && !dma_eligible(path, row_bytes, K, svec16))
+        return fail(QGEMM_ERR_BAD_LAYOUT, "a prepacked MX B needs K/32 a multiple of 16 and 16-byte aligned scale "
+                                          "arrays");
+    TRY(check_device());
+    const int tile = packed ? pick_tile_packed(path, s, row_bytes, true) : pick_tile(path, s, row_bytes, svec16, true);
+    Params p = base_params(A, lda_bytes, B, packed ? row_bytes : ldb_bytes, C, ldc, s, row_bytes, tile);
+    p.b_packed = packed;
     TRY(check_grid(p));
     p.mx_sa = scale_a;
     p.mx_sb = scale_b;
@@ -428,6 +482,64 @@ qgemm_status qgemm_mx(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const 
     if (fmt == QGEMM_MX_E4M3)
         return finish(launch_mx8(tile, bias != nullptr, brows, svec, p, (hipStream_t)stream));
     return finish(launch_mx4(tile, bias != nullptr, brows, svec, p, (hipStream_t)stream));
+}
+
+qgemm_status qgemm_mx(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const void *B, int64_t ldb_bytes,
+                      const uint8_t *scale_a, const uint8_t *scale_b, qgemm_mx_bscale b_layout,
+                      const uint16_t *bias, uint16_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                      void *stream)
+{
+    return mx_common(fmt, A, lda_bytes, B, ldb_bytes, scale_a, scale_b, b_layout, bias, C, ldc, M, N, K, stream,
+                     false);
+}
+
+// ------------------------------------------------------------ prepacked B
+
+int64_t qgemm_prepacked_b_bytes(int64_t N, int64_t row_bytes)
+{
+    if (N < 0 || row_bytes <= 0 || row_bytes % 256 || N >= LD_LIMIT || row_bytes * 256 >= LD_LIMIT)
+        return -1;
+    return (N + 15) / 16 * 16 * row_bytes;
+}
+
+qgemm_status qgemm_prepack_b(const void *B, int64_t ldb, int64_t N, int64_t row_bytes, void *Bp, void *stream)
+{
+    if (N < 0 || N >= LD_LIMIT)
+        return fail(QGEMM_ERR_BAD_SHAPE, "N=%lld: need 0 <= N < 2^31", (long long)N);
+    if (row_bytes <= 0 || row_bytes % 256 || row_bytes * 256 >= LD_LIMIT)
+        return fail(QGEMM_ERR_BAD_SHAPE, "row_bytes=%lld: need a positive multiple of 256, 256 rows below 2^31",
+                    (long long)row_bytes);
+    if (N == 0)
+        return QGEMM_OK;
+    TRY(check_operand("B", B, ldb, row_bytes));
+    if (!Bp)
+        return fail(QGEMM_ERR_NULL_POINTER, "Bp is NULL");
+    if (!aligned(Bp, 16))
+        return fail(QGEMM_ERR_BAD_LAYOUT, "Bp is not 16-byte aligned");
+    TRY(check_device());
+    return finish(launch_prepack_b((const uint8_t *)B, ldb, N, row_bytes, (uint8_t *)Bp, (hipStream_t)stream));
+}
+
+qgemm_status qgemm_i8_rowwise_prepacked(const int8_t *A, int64_t lda, const void *Bp, const float *scale_a,
+                                        const float *scale_b, const uint16_t *bias, uint16_t *C, int64_t ldc,
+                                        int64_t M, int64_t N, int64_t K, void *stream)
+{
+    return i8_common(A, lda, Bp, 0, scale_a, scale_b, bias, C, ldc, Shape{M, N, K}, stream, OUT_BF16, true);
+}
+
+qgemm_status qgemm_f8_pertoken_prepacked(const uint8_t *A, int64_t lda, const void *Bp, const float *scale_a,
+                                         const float *scale_b, const uint16_t *bias, uint16_t *C, int64_t ldc,
+                                         int64_t M, int64_t N, int64_t K, void *stream)
+{
+    return f8_common(A, lda, Bp, 0, scale_a, scale_b, bias, C, ldc, M, N, K, stream, true);
+}
+
+qgemm_status qgemm_mx_prepacked(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const void *Bp,
+                                const uint8_t *scale_a, const uint8_t *scale_b, qgemm_mx_bscale b_layout,
+                                const uint16_t *bias, uint16_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                void *stream)
+{
+    return mx_common(fmt, A, lda_bytes, Bp, 0, scale_a, scale_b, b_layout, bias, C, ldc, M, N, K, stream, true);
 }
 
 // ------------------------------------------------------------ quantisers

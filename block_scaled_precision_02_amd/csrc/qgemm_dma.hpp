@@ -144,8 +144,14 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
 
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * p.lda,
                                                 (uint32_t)((rows_a - 1) * p.lda + p.kbytes));
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + (int64_t)n0 * p.ldb,
-                                                (uint32_t)((rows_b - 1) * p.ldb + p.kbytes));
+    // B row-major, or prepacked: 16-row groups of 1 KB blocks, block t of a
+    // group holding its rows' 64-byte K piece t already in this kernel's LDS
+    // order, so that a fetch reads one contiguous kilobyte.
+    const int64_t gbytes = (int64_t)16 * p.kbytes;        // one packed group
+    const __amdgpu_buffer_rsrc_t rb =
+        p.b_packed ? make_rsrc(p.B + (int64_t)(n0 / 16) * gbytes, (uint32_t)(((rows_b + 15) / 16) * gbytes))
+                   : make_rsrc(p.B + (int64_t)n0 * p.ldb, (uint32_t)((rows_b - 1) * p.ldb + p.kbytes));
+    const unsigned bstep = p.b_packed ? 1024u : (unsigned)DSTAGE;   // B bytes per stage along K
 
     // Fetch map: wave w's j-th A fetch covers rows 16*(4w+j) .. +15; lane i
     // takes row +i/4 and the chunk that belongs in slot i%4.  A row past M / N
@@ -160,14 +166,18 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     }
 #pragma unroll
     for (int j = 0; j < DMA_B; ++j) {
-        const int r = 16 * (DMA_B * wave + j) + (lane >> 2);
+        const int g = DMA_B * wave + j;                   // 16-row group in the tile
+        const int r = 16 * g + (lane >> 2);
         const int c = (lane & 3) ^ ((r >> 2) & 3);
-        b_off[j] = r < rows_b ? (unsigned)(r * p.ldb + 16 * c) : OOB;
+        if (p.b_packed)
+            b_off[j] = 16 * g < rows_b ? (unsigned)(g * gbytes + 16 * lane) : OOB;
+        else
+            b_off[j] = r < rows_b ? (unsigned)(r * p.ldb + 16 * c) : OOB;
     }
     // Stage t goes to slot t % 4, its A rows (part 0) and B rows (part 1)
     // fetched separately.
     auto fetch_part = [&](int t, auto partc) {
-        const unsigned kb = (unsigned)(t * DSTAGE);
+        const unsigned kb = (unsigned)(t * DSTAGE), kbb = (unsigned)t * bstep;
         uint8_t *slot = &lds[(t & 3) * STAGE_BYTES];
         if constexpr (decltype(partc)::value == 0) {
 #pragma unroll
@@ -176,7 +186,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         } else {
 #pragma unroll
             for (int j = 0; j < DMA_B; ++j)
-                dma16(rb, b_off[j] + kb, slot + BM * DSTAGE + (DMA_B * wave + j) * 16 * DSTAGE);
+                dma16(rb, b_off[j] + kbb, slot + BM * DSTAGE + (DMA_B * wave + j) * 16 * DSTAGE);
         }
     };
 

@@ -68,6 +68,8 @@ struct Params {
     int kblocks;                   // K / 32 (MX scale row length in bytes)
     int tiles_m, tiles_n;
     int group_m;                   // tile rows per group in the launch order
+    int b_packed;                  // B in the prepacked layout (LDS-fetch and small-M kernels only):
+                                   // 16-row groups of kbytes/64 blocks of 1 KB, B = the group of row 0
 };
 
 constexpr int KSTEP_BYTES = 128;

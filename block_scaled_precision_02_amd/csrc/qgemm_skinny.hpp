@@ -72,8 +72,12 @@ __global__ void __launch_bounds__(64 * SK_WAVES, 1) qgemm_skinny_kernel(const Pa
     const int rows_a = min(BM, p.M - m0), rows_b = min(BN, p.N - n0);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * p.lda,
                                                 (uint32_t)((rows_a - 1) * p.lda + p.kbytes));
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + (int64_t)n0 * p.ldb,
-                                                (uint32_t)((rows_b - 1) * p.ldb + p.kbytes));
+    // B row-major, or prepacked (the workgroup's 16 columns are one packed
+    // group: 64-byte K piece t of its rows is the 1 KB block t, row r's chunk
+    // c at slot 4r + (c ^ ((r >> 2) & 3)); rows past N are zeros there)
+    const __amdgpu_buffer_rsrc_t rb =
+        p.b_packed ? make_rsrc(p.B + (int64_t)(n0 / 16) * 16 * p.kbytes, (uint32_t)(16 * p.kbytes))
+                   : make_rsrc(p.B + (int64_t)n0 * p.ldb, (uint32_t)((rows_b - 1) * p.ldb + p.kbytes));
     unsigned a_row[TM];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -81,6 +85,7 @@ __global__ void __launch_bounds__(64 * SK_WAVES, 1) qgemm_skinny_kernel(const Pa
         a_row[i] = r < rows_a ? (unsigned)(r * p.lda) : OOB;
     }
     const unsigned b_row = r16 < rows_b ? (unsigned)(r16 * p.ldb) : OOB;
+    const unsigned b_slot = 16u * (4 * r16 + (g ^ ((r16 >> 2) & 3)));   // packed: this lane's slot
 
     const int ksteps = (p.kbytes + T::KSTEP - 1) / T::KSTEP;
     const int nst = ksteps > wave ? (ksteps - wave + SK_WAVES - 1) / SK_WAVES : 0;
@@ -99,7 +104,9 @@ __global__ void __launch_bounds__(64 * SK_WAVES, 1) qgemm_skinny_kernel(const Pa
         for (int c = 0; c < T::NCH; ++c) {
             const int kc = s * T::KSTEP + 64 * c + 16 * g;
             const bool kin = s < ksteps && kc < p.kbytes;
-            const u32x4 vb = ld16(rb, kin ? b_row + (unsigned)kc : OOB);
+            const unsigned bo = p.b_packed ? b_slot + (unsigned)((s * T::KSTEP + 64 * c) / 64) * 1024u
+                                           : b_row + (unsigned)kc;
+            const u32x4 vb = ld16(rb, kin ? bo : OOB);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 fb[SLOT][4 * c + q] = (int)vb[q];

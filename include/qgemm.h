@@ -133,6 +133,51 @@ qgemm_status qgemm_mx(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const 
                       qgemm_mx_bscale b_layout, const uint16_t *bias, uint16_t *C, int64_t ldc,
                       int64_t M, int64_t N, int64_t K, void *stream);
 
+/* Prepacked B.  B (the weights, static across calls) can be rewritten once
+ * into the order the LDS-fetch kernel's B stages take in LDS, so that each
+ * of its fetches reads one contiguous kilobyte instead of 16 rows x 64 bytes
+ * (on one MI355X: INT8 30000x21504x5376 +4.5%, MXFP4 8192^3 +6%, MXFP8
+ * 16384x7168x2048 +3%, FP8 4096x2112x7168 +11%).  The MI355X
+ * GEMMs on the pages read such a prepared B too ("gemm_a8w8_bpreshuffle",
+ * ROCm/aiter PR #6262, description; the "BpreShuffle" FP4 kernel of
+ * ROCm/FlyDSL PR #990, description); the order here is this library's own:
+ *   ceil(N/16) groups of 16 rows; group R is row_bytes/64 blocks of 1024
+ *   bytes; block t holds bytes 64t .. 64t+63 of rows 16R .. 16R+15, its
+ *   16-byte slot p (0..63) being row 16R + p/4, bytes 64t + 16c .. +15,
+ *   c = (p mod 4) XOR ((p/16) mod 4); rows at or past N are zeros.
+ * row_bytes = K (int8, e4m3) or K/2 (e2m1), a positive multiple of 256 with
+ * 256 * row_bytes below 2^31.  The layout does not depend on the element type
+ * or the scales. */
+
+/* Bytes of a prepacked B: ceil(N/16) * 16 * row_bytes, or -1 if N or
+ * row_bytes is out of range.  Pure host logic. */
+int64_t qgemm_prepacked_b_bytes(int64_t N, int64_t row_bytes);
+
+/* Write B [N, row_bytes] (row stride ldb bytes, 16-byte aligned, ldb a
+ * multiple of 16) into Bp (qgemm_prepacked_b_bytes(N, row_bytes) bytes,
+ * 16-byte aligned, caller-owned, not overlapping B).  Asynchronous on stream;
+ * N == 0 is a no-op. */
+qgemm_status qgemm_prepack_b(const void *B, int64_t ldb, int64_t N, int64_t row_bytes, void *Bp, void *stream);
+
+/* The three GEMMs with B prepacked by qgemm_prepack_b (row_bytes = the row of
+ * B the call would otherwise take).  Same arguments, numerics and results as
+ * qgemm_i8_rowwise / qgemm_f8_pertoken / qgemm_mx with Bp in place of (B,
+ * ldb); in addition K must give rows of a multiple of 256 bytes
+ * (QGEMM_ERR_BAD_SHAPE otherwise) and, for MX, K/32 must be a multiple of 16
+ * with 16-byte aligned scale arrays (QGEMM_ERR_BAD_LAYOUT otherwise).  INT8
+ * results are bit-identical to qgemm_i8_rowwise's; FP8 / MX results equal
+ * those of qgemm_*'s LDS-fetch tiles. */
+qgemm_status qgemm_i8_rowwise_prepacked(const int8_t *A, int64_t lda, const void *Bp, const float *scale_a,
+                                        const float *scale_b, const uint16_t *bias, uint16_t *C, int64_t ldc,
+                                        int64_t M, int64_t N, int64_t K, void *stream);
+qgemm_status qgemm_f8_pertoken_prepacked(const uint8_t *A, int64_t lda, const void *Bp, const float *scale_a,
+                                         const float *scale_b, const uint16_t *bias, uint16_t *C, int64_t ldc,
+                                         int64_t M, int64_t N, int64_t K, void *stream);
+qgemm_status qgemm_mx_prepacked(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const void *Bp,
+                                const uint8_t *scale_a, const uint8_t *scale_b, qgemm_mx_bscale b_layout,
+                                const uint16_t *bias, uint16_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                void *stream);
+
 /* Per-token e4m3 quantiser: the A operand and scale_a of qgemm_f8_pertoken
  * from bf16 activations.  "perf(gemm-ar): mxfp8 with row-major scales staged
  * through LDS" (ROCm/mori PR #806), Measured, names the per-token ("ptpc")

@@ -211,3 +211,51 @@ def test_quant_checks_pass_before_the_device_check(monkeypatch):
     assert qmx(fmt=1, ldq=32) == q.QGEMM_ERR_UNSUPPORTED_DEVICE
     assert qmx(fmt=0) == q.QGEMM_ERR_UNSUPPORTED_DEVICE
     assert qf8() == q.QGEMM_ERR_UNSUPPORTED_DEVICE
+
+
+def test_prepacked_b_bytes():
+    L = q.lib()
+    assert L.qgemm_prepacked_b_bytes(1, 256) == 16 * 256
+    assert L.qgemm_prepacked_b_bytes(16, 256) == 16 * 256
+    assert L.qgemm_prepacked_b_bytes(17, 512) == 32 * 512
+    assert L.qgemm_prepacked_b_bytes(0, 256) == 0
+    assert L.qgemm_prepacked_b_bytes(4, 320) == -1       # not a multiple of 256
+    assert L.qgemm_prepacked_b_bytes(-1, 256) == -1
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, 256, 4, 320, FAKE2), q.QGEMM_ERR_BAD_SHAPE),
+    ((FAKE, 256, -1, 256, FAKE2), q.QGEMM_ERR_BAD_SHAPE),
+    ((None, 256, 4, 256, FAKE2), q.QGEMM_ERR_NULL_POINTER),
+    ((FAKE, 256, 4, 256, None), q.QGEMM_ERR_NULL_POINTER),
+    ((FAKE, 128, 4, 256, FAKE2), q.QGEMM_ERR_BAD_LAYOUT),
+    ((FAKE, 256, 4, 256, FAKE2 + 8), q.QGEMM_ERR_BAD_LAYOUT),
+    ((FAKE, 256, 0, 256, None), q.QGEMM_OK),
+])
+def test_prepack_rejects(args, status):
+    assert q.lib().qgemm_prepack_b(*args, None) == status
+
+
+def test_prepacked_gemms_reject():
+    L = q.lib()
+    # K bytes not a multiple of 256
+    assert L.qgemm_i8_rowwise_prepacked(FAKE, 128, FAKE2, FAKE3, FAKE3, None, FAKE, 64, 64, 64, 128,
+                                        None) == q.QGEMM_ERR_BAD_SHAPE
+    assert L.qgemm_f8_pertoken_prepacked(FAKE, 256, None, FAKE3, FAKE3, None, FAKE, 64, 64, 64, 256,
+                                         None) == q.QGEMM_ERR_NULL_POINTER
+    # MX e4m3 K = 256: K/32 = 8 is not a multiple of 16
+    assert L.qgemm_mx_prepacked(0, FAKE, 256, FAKE2, FAKE3, FAKE3, 1, None, FAKE, 64, 64, 64, 256,
+                                None) == q.QGEMM_ERR_BAD_LAYOUT
+    # ... and misaligned scale arrays
+    assert L.qgemm_mx_prepacked(0, FAKE, 512, FAKE2, FAKE3 + 4, FAKE3, 1, None, FAKE, 64, 64, 64, 512,
+                                None) == q.QGEMM_ERR_BAD_LAYOUT
+
+
+def test_prepacked_gemms_pass_their_checks(monkeypatch):
+    monkeypatch.setenv("QGEMM_FAKE_ARCH", "gfx1201")
+    L = q.lib()
+    assert L.qgemm_i8_rowwise_prepacked(FAKE, 256, FAKE2, FAKE3, FAKE3, None, FAKE, 64, 64, 64, 256,
+                                        None) == q.QGEMM_ERR_UNSUPPORTED_DEVICE
+    assert L.qgemm_mx_prepacked(1, FAKE, 256, FAKE2, FAKE3, FAKE3, 32, None, FAKE, 64, 64, 64, 512,
+                                None) == q.QGEMM_ERR_UNSUPPORTED_DEVICE
+    assert L.qgemm_prepack_b(FAKE, 256, 4, 256, FAKE2, None) == q.QGEMM_ERR_UNSUPPORTED_DEVICE

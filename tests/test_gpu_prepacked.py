@@ -1,0 +1,117 @@
+"""GPU parity of the prepacked-B path: the prepacking kernel bit for bit
+against the oracle's layout, and the ``_prepacked`` GEMMs against the oracle
+GEMM on the unpacked B (INT8 bit-exact; FP8 / MX within the tolerance) and
+bit for bit against the same tile reading the row-major B (the same bytes
+reach LDS in the same order)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+from block_scaled_precision_02_amd import inputs  # noqa: E402
+import block_scaled_precision_02_amd as q  # noqa: E402
+
+from tests import parity  # noqa: E402
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _gpu_only():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    q.force_tile(-1)
+    yield
+    q.force_tile(-1)
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    return oracle
+
+
+@pytest.mark.parametrize("N,row", [(1, 256), (17, 256), (300, 512), (2112, 7168)])
+def test_prepack_bit_exact(orc, N, row):
+    _say(f"[prepack] N={N} row={row}")
+    rng = np.random.default_rng(N * 7 + row)
+    B = rng.integers(0, 256, (N, row), dtype=np.uint8)
+    Bd = torch.zeros((N, row + 64), dtype=torch.uint8, device="cuda")
+    Bd[:, :row] = torch.from_numpy(B).cuda()
+    nbytes = q.lib().qgemm_prepacked_b_bytes(N, row)
+    buf = torch.full((nbytes + 256,), 0xA5, dtype=torch.uint8, device="cuda")
+    pb = q.qgemm_prepack_b(Bd[:, :row], out=buf[:nbytes])
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    assert np.array_equal(got[:nbytes], orc.pack_b(B))
+    assert (got[nbytes:] == 0xA5).all(), "wrote past Bp"
+    assert pb.N == N and pb.row_bytes == row
+
+
+def _run_packed(d, out=None):
+    bias = None if d["bias"] is None else parity.dev(d["bias"].view(np.int16))
+    B = parity.dev(d["B"])
+    pb = q.qgemm_prepack_b(B)
+    A, sa, sb = parity.dev(d["A"]), parity.dev(d["scale_a"]), parity.dev(d["scale_b"])
+    if d["kind"] == "i8":
+        return q.qgemm_i8_rowwise_prepacked(A, pb, sa, sb, bias, out=out)
+    if d["kind"] == "f8":
+        return q.qgemm_f8_pertoken_prepacked(A, pb, sa, sb, bias, out=out)
+    fmt = q.QGEMM_MX_E4M3 if d["fmt"] == "e4m3" else q.QGEMM_MX_E2M1
+    return q.qgemm_mx_prepacked(fmt, A, pb, sa, sb, d["b_rows_per_scale"], bias, out=out)
+
+
+SHAPES = [(1, 1, 512), (17, 33, 512), (255, 257, 1024), (300, 520, 2048), (513, 64, 512), (64, 300, 1024)]
+
+
+@pytest.mark.parametrize("tile", [-1, 4, 5, 6, 7, 8, 9])
+@pytest.mark.parametrize("name", ["i8_small", "f8_ptpc", "mxfp8", "mxfp4"])
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_prepacked_gemm_edges(name, M, N, K, tile):
+    """Ragged M / N, NaN-filled output with canaries past N and M; every
+    LDS-fetch tile and (INT8 / FP8) the small-M tiles; bit for bit equal to
+    the same tile on the row-major B."""
+    if tile in (8, 9) and name.startswith("mx"):
+        pytest.skip("the small-M kernel has no MX form")
+    kk = K if name != "mxfp4" else 2 * K      # e2m1: K elements are K/2 bytes
+    d = inputs.make(name, M=M, N=N, K=kk, bias=(M % 2 == 1))
+    _say(f"[prepacked] {name} {M}x{N}x{kk} tile {tile}")
+    q.force_tile(tile)
+    ldc = N + (-N) % 8 + 8
+    buf = torch.full((M + 3, ldc), float("nan"), dtype=torch.bfloat16, device="cuda")
+    before = parity.bits(buf)
+    _run_packed(d, out=buf[:M, :N])
+    after = parity.bits(buf)
+    ref, absdot, _ = parity.oracle_run(d)
+    parity.compare(d, after[:M, :N], ref, absdot, f"prepacked {name} {M}x{N}x{kk} tile {tile}")
+    assert np.array_equal(after[:M, N:], before[:M, N:]), "wrote past N"
+    assert np.array_equal(after[M:], before[M:]), "wrote past M"
+    # the same tile on the row-major B: the same bytes in LDS, the same result
+    same = {-1: -1, 4: 4, 5: 5, 6: 6, 7: 7, 8: 8, 9: 9}[tile]
+    q.force_tile(same)
+    if tile == -1 and name.startswith("mx") and d["M"] <= 64:
+        return
+    plain = parity.bits(parity.gpu_run(d))
+    assert np.array_equal(after[:M, :N], plain), "prepacked and row-major B differ"
+
+
+@pytest.mark.parametrize("name", ["f8_ptpc", "mxfp8", "mxfp4", "i8_qkv"])
+def test_prepacked_full_workload_sampled(name):
+    """Each workload at its full size with a prepacked B, as the table
+    launches it; sampled whole rows against the oracle."""
+    d = inputs.make(name)
+    _say(f"[prepacked] full {name} M={d['M']} N={d['N']} K={d['K']}")
+    out = _run_packed(d)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    M = d["M"]
+    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(M - 8, M), rng.choice(M, 8, replace=False)]))
+    got = parity.bits(out[torch.from_numpy(rows).cuda()])
+    ref, absdot, _ = parity.oracle_run(d, rows=rows)
+    parity.compare(d, got, ref, absdot, f"prepacked full {name}")
