@@ -261,17 +261,21 @@ bool dma_eligible(int path, int64_t kbytes, int64_t K, bool svec)
 // 2130 for the four-wave LDS-fetch kernel and ~2100 for register staging;
 // MXFP4 8192^3 3756 vs 3668 TFLOPS; MXFP8 16384x7168x2048 1940 vs 1933), 192
 // and 128 as their four-wave LDS-fetch forms.
-// Small M (INT8 and FP8 with bf16 output): the call streams B; the small-M
-// kernel spreads B over N/16 workgroups whose eight waves split K.
-constexpr int64_t SKINNY_MAX_M = 64;
+// Small M (bf16 output): the call streams B; the small-M kernel spreads B
+// over N/16 workgroups whose eight waves split K.  MX only up to 16 rows: its
+// 64-row form loses to the 128x128 LDS-fetch tile (one MI355X, MXFP8
+// 64x7168x2048: 19.9 vs 13.1 us; MXFP4 64x8192x8192: 43 vs 23.5 us), while
+// the 16-row form wins (MXFP8 1x7168x2048 8.0 vs 9.5 us, MXFP4 1x8192x8192
+// 13.5 vs 18.3 us).
+constexpr int64_t SKINNY_MAX_M = 64, SKINNY_MAX_M_MX = 16;
 
 int pick_tile(int path, Shape s, int64_t kbytes, bool svec, bool bf16_out)
 {
-    const bool skinny_ok = (path == 0 || path == 1) && bf16_out;
+    const bool skinny_ok = bf16_out;
     int t;
     if (g_forced_tile >= 0) {
         t = g_forced_tile;
-    } else if (skinny_ok && s.M <= SKINNY_MAX_M) {
+    } else if (skinny_ok && s.M <= (path >= 2 ? SKINNY_MAX_M_MX : SKINNY_MAX_M)) {
         t = s.M <= 16 ? SKINNY16_TILE : SKINNY64_TILE;
     } else {
         t = select_tile_impl(path, s.M, s.N);

@@ -18,7 +18,7 @@ namespace qgemm {
 //   6 -> 192x192 fetched straight into LDS, 2x2 waves of 96x96; same requirements
 //   7 -> 128x128 fetched straight into LDS, 2x2 waves of 64x64; same requirements
 //   8 -> small M (qgemm_skinny.hpp): 16 rows x 16 columns, eight waves splitting
-//        K; INT8 and FP8 with bf16 output
+//        K; bf16 output
 //   9 -> small M: 64 rows x 16 columns, eight waves splitting K; same paths
 constexpr int NUM_TILES = 10;
 constexpr int DMA_TILE = 4, DMA8_TILE = 5, DMA192_TILE = 6, DMA128_TILE = 7;
@@ -76,12 +76,14 @@ hipError_t launch_tile(int tile, const Params &p, hipStream_t s)
         }
     case SKINNY16_TILE:
     case SKINNY64_TILE:
-        if constexpr ((PATH == PATH_I8 || PATH == PATH_F8) && OUT == OUT_BF16) {
+        if constexpr (OUT == OUT_BF16) {
             const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(tile_threads(tile));
             if (tile == SKINNY16_TILE)
-                hipLaunchKernelGGL((qgemm_skinny_kernel<PATH, 1, skinny_depth<PATH, 1>(), BIAS>), grid, block, 0, s, p);
+                hipLaunchKernelGGL((qgemm_skinny_kernel<PATH, 1, skinny_depth<PATH, 1>(), BIAS, BROWS>), grid, block, 0,
+                                   s, p);
             else
-                hipLaunchKernelGGL((qgemm_skinny_kernel<PATH, 4, skinny_depth<PATH, 4>(), BIAS>), grid, block, 0, s, p);
+                hipLaunchKernelGGL((qgemm_skinny_kernel<PATH, 4, skinny_depth<PATH, 4>(), BIAS, BROWS>), grid, block, 0,
+                                   s, p);
             return hipGetLastError();
         } else {
             return hipErrorInvalidValue;

@@ -2,6 +2,7 @@
 // streaming B from HBM rather than by the matrix cores.
 //
 //     C[m,n] = bf16( sa[m] * sb[n] * sum_k A[m,k] B[n,k] + bias[n] )   (INT8, FP8)
+//     C[m,n] = bf16( sum_k A~[m,k] B~[n,k] + bias[n] )                  (MX)
 //
 // The 256x256 tiles of the main kernels leave most CUs idle when M is a few
 // rows (a 2112-column B gives 9 tiles of 256): here a workgroup owns 16
@@ -26,6 +27,15 @@
 //  * Output: with B as the instruction's first operand each lane ends with
 //    four consecutive n for one m (lane l: m = 16i + l%16, n = 4(l/16) + r),
 //    stored as one 8-byte vector when the four columns exist.
+//  * MX (v_mfma_scale_f32_16x16x128_f8f6f4 with ue8m0 scale operands): a
+//    step is 128 elements, four 32-element blocks, and lane group g gives the
+//    scale of block g of the step (the instruction applies a lane group's
+//    scale to the block that the same group position holds in its own K
+//    order: for e4m3, VGPRs 0-3 of groups 2j, 2j+1 form block j < 2 and VGPRs
+//    4-7 form blocks 2 and 3, which the map above -- chunks g and g + 4 --
+//    makes the step's blocks in K order; for e2m1 a group's 16 bytes are its
+//    block).  Scale bytes are loaded per lane and step; blocks past K/32 and
+//    rows past M / N read 0, whose data is zero too.
 #pragma once
 #include "qgemm_kernel.hpp"
 
@@ -45,22 +55,43 @@ template <> struct SkinnyTraits<PATH_F8> {
     using Frag = i32x8;
     using Acc = f32x4;
 };
+template <> struct SkinnyTraits<PATH_MX8> {
+    static constexpr int KSTEP = 128, NCH = 2;
+    using Frag = i32x8;
+    using Acc = f32x4;
+};
+template <> struct SkinnyTraits<PATH_MX4> {   // 64 bytes = 128 e2m1 elements
+    static constexpr int KSTEP = 64, NCH = 1;
+    using Frag = i32x4;                       // the low half of the instruction's operand
+    using Acc = f32x4;
+};
 
 constexpr int SK_WAVES = 8;
 
-// Steps in flight per wave: the register ring is D x (TM + 1) fragments and
-// a wave has 256 registers (two waves per SIMD).
+// Steps in flight per wave: the register ring is D x (TM + 1) fragments (and,
+// for MX, as many scale bytes) and a wave has 256 registers at two waves per
+// SIMD.  The 16-row MX forms keep to 128 registers so that two workgroups
+// share a CU: an MX weight's K is often short (2048 e4m3 = 16 steps, 2 per
+// wave), so a workgroup's time is mostly one memory round trip, and 7168
+// columns make 448 workgroups -- one round with two per CU instead of two
+// (MXFP8 1 x 7168 x 2048: 13.2 -> 8.0 us).
 template <int PATH, int TM> constexpr int skinny_depth()
 {
+    if constexpr (PATH == PATH_MX4)
+        return TM == 1 ? 8 : 4;
+    if constexpr (PATH == PATH_MX8)
+        return TM == 1 ? 4 : 2;
     return TM == 1 ? (PATH == PATH_I8 ? 16 : 8) : (PATH == PATH_I8 ? 8 : 4);
 }
 
-template <int PATH, int TM, int D, bool BIAS>
-__global__ void __launch_bounds__(64 * SK_WAVES, 1) qgemm_skinny_kernel(const Params p)
+template <int PATH, int TM, int D, bool BIAS, int BROWS>
+__global__ void __launch_bounds__(64 * SK_WAVES, ((PATH == PATH_MX8 || PATH == PATH_MX4) && TM == 1) ? 2 : 1)
+    qgemm_skinny_kernel(const Params p)
 {
     using T = SkinnyTraits<PATH>;
     using Frag = typename T::Frag;
     using Acc = typename T::Acc;
+    constexpr bool MX = PATH == PATH_MX8 || PATH == PATH_MX4;
     constexpr int BM = 16 * TM, BN = 16;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -90,7 +121,24 @@ __global__ void __launch_bounds__(64 * SK_WAVES, 1) qgemm_skinny_kernel(const Pa
     const int ksteps = (p.kbytes + T::KSTEP - 1) / T::KSTEP;
     const int nst = ksteps > wave ? (ksteps - wave + SK_WAVES - 1) / SK_WAVES : 0;
 
+    // MX scale rows: A row 16i + l%16; B row l%16 (1x32) or its 32-row group
+    __amdgpu_buffer_rsrc_t rsa, rsb;
+    unsigned sa_row[TM], sb_row = OOB;
+    if constexpr (MX) {
+        rsa = make_rsrc(p.mx_sa + (int64_t)m0 * p.kblocks, (uint32_t)(rows_a * p.kblocks));
+        const int sb0 = n0 / BROWS, sb_rows = (n0 + rows_b - 1) / BROWS - sb0 + 1;
+        rsb = make_rsrc(p.mx_sb + (int64_t)sb0 * p.kblocks, (uint32_t)(sb_rows * p.kblocks));
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int r = 16 * i + r16;
+            sa_row[i] = r < rows_a ? (unsigned)(r * p.kblocks) : OOB;
+        }
+        if (r16 < rows_b)
+            sb_row = (unsigned)(((n0 + r16) / BROWS - sb0) * p.kblocks);
+    }
+
     Frag fa[D][TM], fb[D];
+    unsigned ssa[MX ? D : 1][TM], ssb[MX ? D : 1];
     Acc acc[TM];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -118,16 +166,35 @@ __global__ void __launch_bounds__(64 * SK_WAVES, 1) qgemm_skinny_kernel(const Pa
                     fa[SLOT][i][4 * c + q] = (int)va[q];
             }
         }
+        if constexpr (MX) {
+            // block g of step s; past K/32 (or past the wave's steps) reads 0
+            const int kblk = 4 * s + g;
+            const bool bin = s < ksteps && kblk < p.kblocks;
+            ssb[SLOT] = __builtin_amdgcn_raw_buffer_load_b8(rsb, bin ? sb_row + (unsigned)kblk : OOB, 0, 0);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                ssa[SLOT][i] = __builtin_amdgcn_raw_buffer_load_b8(rsa, bin ? sa_row[i] + (unsigned)kblk : OOB, 0, 0);
+        }
     };
     auto mma = [&](auto slotc) {
         constexpr int SLOT = decltype(slotc)::value;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            if constexpr (PATH == PATH_I8)
+            if constexpr (PATH == PATH_I8) {
                 acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb[SLOT], fa[SLOT][i], acc[i], 0, 0, 0);
-            else
+            } else if constexpr (PATH == PATH_F8) {
                 acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[SLOT], fa[SLOT][i], acc[i], 0, 0,
                                                                           0, 0, 0, 0);
+            } else if constexpr (PATH == PATH_MX8) {
+                acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    fb[SLOT], fa[SLOT][i], acc[i], 0, 0, 0, (int)ssb[SLOT], 0, (int)ssa[SLOT][i]);
+            } else {
+                const i32x4 b4 = fb[SLOT], a4 = fa[SLOT][i];
+                const i32x8 b8 = {b4[0], b4[1], b4[2], b4[3], 0, 0, 0, 0};
+                const i32x8 a8 = {a4[0], a4[1], a4[2], a4[3], 0, 0, 0, 0};
+                acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, acc[i], 4, 4, 0, (int)ssb[SLOT],
+                                                                          0, (int)ssa[SLOT][i]);
+            }
         }
     };
 
@@ -171,16 +238,19 @@ __global__ void __launch_bounds__(64 * SK_WAVES, 1) qgemm_skinny_kernel(const Pa
 
     // Epilogue (the fixed-order binary32 sequence of the main kernels).
     const int nloc = 4 * g;
-    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(p.scale_b + n0, (uint32_t)(rows_b * 4));
-    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.scale_a + m0, (uint32_t)(rows_a * 4));
-    __amdgpu_buffer_rsrc_t rbias;
+    __amdgpu_buffer_rsrc_t rsbe, rsae, rbias;
+    if constexpr (!MX) {
+        rsbe = make_rsrc(p.scale_b + n0, (uint32_t)(rows_b * 4));
+        rsae = make_rsrc(p.scale_a + m0, (uint32_t)(rows_a * 4));
+    }
     if constexpr (BIAS)
         rbias = make_rsrc(p.bias + n0, (uint32_t)(rows_b * 2));
-    unsigned sbw[4], bbw[4] = {0, 0, 0, 0};
+    unsigned sbw[4] = {0, 0, 0, 0}, bbw[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const bool in = nloc + r < rows_b;
-        sbw[r] = __builtin_amdgcn_raw_buffer_load_b32(rsb, in ? (unsigned)((nloc + r) * 4) : OOB, 0, 0);
+        if constexpr (!MX)
+            sbw[r] = __builtin_amdgcn_raw_buffer_load_b32(rsbe, in ? (unsigned)((nloc + r) * 4) : OOB, 0, 0);
         if constexpr (BIAS)
             bbw[r] = (unsigned)__builtin_amdgcn_raw_buffer_load_b16(rbias, in ? (unsigned)((nloc + r) * 2) : OOB, 0,
                                                                   0) << 16;
@@ -191,8 +261,10 @@ __global__ void __launch_bounds__(64 * SK_WAVES, 1) qgemm_skinny_kernel(const Pa
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int mloc = 16 * i + r16;
-        const float sa = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(rsa, mloc < rows_a ? (unsigned)(mloc * 4) : OOB, 0, 0));
+        float sa = 1.0f;
+        if constexpr (!MX)
+            sa = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                               rsae, mloc < rows_a ? (unsigned)(mloc * 4) : OOB, 0, 0));
         float f[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -201,8 +273,10 @@ __global__ void __launch_bounds__(64 * SK_WAVES, 1) qgemm_skinny_kernel(const Pa
                 x = (float)acc[i][r];
             else
                 x = acc[i][r];
-            x = x * sa;
-            x = x * __builtin_bit_cast(float, sbw[r]);
+            if constexpr (!MX) {
+                x = x * sa;
+                x = x * __builtin_bit_cast(float, sbw[r]);
+            }
             if constexpr (BIAS)
                 x = x + __builtin_bit_cast(float, bbw[r]);
             f[r] = x;

@@ -236,12 +236,13 @@ const char *qgemm_status_string(qgemm_status status);
  *   5: 256x256, 8 waves, operands fetched straight into LDS
  *   6: 192x192, 4 waves, operands fetched straight into LDS
  *   7: 128x128, 4 waves, operands fetched straight into LDS
- *   8: 16 rows x 16 columns, 8 waves splitting K (small M; INT8 and FP8)
- *   9: 64 rows x 16 columns, 8 waves splitting K (small M; INT8 and FP8)
+ *   8: 16 rows x 16 columns, 8 waves splitting K (small M)
+ *   9: 64 rows x 16 columns, 8 waves splitting K (small M)
  * Tiles 4-7 need K bytes a multiple of 256 and MX scale rows a multiple of
  * 16 bytes; where these hold, the table's 256x256 choice runs as tile 5,
- * 192x192 as tile 6 and 128x128 as tile 7.  INT8 and FP8 calls with M <= 64
- * take tile 8 (M <= 16) or 9. */
+ * 192x192 as tile 6 and 128x128 as tile 7.  Calls with M <= 64 take tile 8
+ * (M <= 16) or 9 (INT8 and FP8 only: MX takes the small-M kernel up to
+ * M = 16). */
 int qgemm_select_tile(int path, int64_t M, int64_t N, int64_t K);
 
 /* Rows of A one tile covers (for tiles 0-7 also the rows of B; tiles 8 and 9

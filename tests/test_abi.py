@@ -137,12 +137,14 @@ def test_tile_table():
     assert L.qgemm_select_tile(1, 4096, 2112, 7168) == 6
     assert L.qgemm_select_tile(1, 4096, 2112, 7200) == 3
     assert L.qgemm_select_tile(7, 64, 64, 64) == -1
-    # small M, INT8 / FP8: the small-M kernel (16- or 64-row tiles); MX keeps the table
+    # small M: the small-M kernel (16- or 64-row tiles), every path
     assert L.qgemm_select_tile(1, 1, 2112, 7168) == 8
     assert L.qgemm_select_tile(1, 16, 2112, 7168) == 8
     assert L.qgemm_select_tile(0, 64, 3072, 3072) == 9
     assert L.qgemm_select_tile(1, 65, 2112, 7168) != 9
-    assert L.qgemm_select_tile(2, 16, 7168, 2048) not in (8, 9)
+    assert L.qgemm_select_tile(2, 16, 7168, 2048) == 8
+    assert L.qgemm_select_tile(3, 16, 8192, 8192) == 8
+    assert L.qgemm_select_tile(3, 17, 8192, 8192) not in (8, 9)    # MX: the 16-row form only
     for t, e in ((0, 256), (1, 128), (2, 256), (3, 192), (4, 256), (5, 256), (6, 192), (7, 128), (8, 16), (9, 64)):
         assert L.qgemm_tile_rows(t) == e
     assert L.qgemm_tile_rows(10) == 0 and L.qgemm_tile_rows(-1) == 0

@@ -273,12 +273,14 @@ SKINNY_SHAPES = [(1, 1, 32), (1, 300, 512), (5, 33, 96), (16, 16, 1024), (17, 70
 
 
 @pytest.mark.parametrize("tile", [8, 9])
-@pytest.mark.parametrize("name", ["i8_small", "f8_ptpc"])
+@pytest.mark.parametrize("name", ["i8_small", "f8_ptpc", "mxfp8", "mxfp4"])
 @pytest.mark.parametrize("M,N,K", SKINNY_SHAPES)
 def test_skinny_kernel_edges(name, M, N, K, tile):
     """The small-M kernel (eight waves splitting K, partial sums added in
     LDS) on ragged M / N / K, NaN-filled output with canaries beyond N and M;
-    INT8 also bit for bit against the 256x256 register-staged tile."""
+    INT8 also bit for bit against the 256x256 register-staged tile.  MX: the
+    32x32 B-scale recipe for e4m3 (a 16-column workgroup meets one or two
+    scale rows), 1x32 for e2m1."""
     d = inputs.make(name, M=M, N=N, K=K, bias=(M % 2 == 1))
     q.force_tile(tile)
     ldc = N + (-N) % 8 + 8
@@ -295,15 +297,20 @@ def test_skinny_kernel_edges(name, M, N, K, tile):
         assert np.array_equal(after[:M, :N], parity.bits(parity.gpu_run(d)))
 
 
+@pytest.mark.parametrize("name,path", [("f8_ptpc", 1), ("mxfp8", 2), ("mxfp4", 3)])
 @pytest.mark.parametrize("M", [1, 16, 64])
-def test_skinny_table_choice_full_width(M):
-    """FP8 per-token at M = 1, 16, 64 over the full 2112 x 7168 weight, as the
-    table launches it (the small-M kernel), every output row checked."""
-    d = inputs.make("f8_ptpc", M=M)
+def test_skinny_table_choice_full_width(name, path, M):
+    """M = 1, 16, 64 over each workload's full weight (FP8 2112 x 7168, MXFP8
+    7168 x 2048, MXFP4 8192 x 8192), as the table launches it (the small-M
+    kernel, for MX up to 16 rows), every output row checked."""
+    d = inputs.make(name, M=M)
     q.force_tile(-1)
-    assert q.select_tile(1, M, d["N"], d["K"]) in (8, 9)
+    if path >= 2 and M > 16:
+        assert q.select_tile(path, M, d["N"], d["K"]) not in (8, 9)   # MX: 16-row form only
+    else:
+        assert q.select_tile(path, M, d["N"], d["K"]) in (8, 9)
     ref, absdot, _ = parity.oracle_run(d)
-    parity.compare(d, parity.bits(parity.gpu_run(d)), ref, absdot, f"skinny f8 M={M}")
+    parity.compare(d, parity.bits(parity.gpu_run(d)), ref, absdot, f"skinny {name} M={M}")
 
 
 def test_non_default_stream():
