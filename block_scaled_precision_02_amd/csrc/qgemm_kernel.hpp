@@ -242,6 +242,16 @@ __device__ __forceinline__ unsigned pack_bf16(float x, float y)
 // Only full tiles read them; an edge tile loads element by element.
 constexpr int PRM_SB = 1024, PRM_BIAS = 2048, PRM_BYTES = 3072;
 
+// Cache policy of the whole-row output stores: non-temporal.  C is written
+// once and never read back by the kernel; streaming it past the caches leaves
+// L2 to the A and B panels that neighbouring tiles share (one MI355X: INT8
+// 30000x21504x5376 +3%, MXFP4 8192^3 +3%, MXFP8 16384x7168x2048 +9%).  Stores
+// of partial rows (edge tiles) keep the default policy: written past the
+// caches, partial lines cost far more.
+constexpr int CPOL_NT = 2;
+
+constexpr int pow2_at_least(int x) { return x <= 1 ? 1 : 2 * pow2_at_least((x + 1) / 2); }
+
 // Shared by the kernels: scale, bias, round and store one workgroup tile.
 // LDSBYTES is the LDS at lds_base the kernel owns (reused as the output
 // stash once every wave is done with the operand buffers); prm is the
@@ -279,12 +289,14 @@ __device__ __forceinline__ void store_tile(const Params &p, Acc (&acc)[TM][TN], 
     // block of bf16 results in its own stash (16-byte chunks XOR-swizzled by
     // row), then writes whole 16-byte row pieces, consecutive lanes covering
     // consecutive bytes of a row, so every store instruction fills complete
-    // cache lines instead of touching 32 rows.
-    constexpr int SROWB = TN * 32 * 2;              // stash row bytes (bf16)
-    constexpr int SCHK = SROWB / 16;                // 16-byte chunks per row
-    constexpr bool STASH = OUT == OUT_BF16 && (SCHK & (SCHK - 1)) == 0 && 64 % SCHK == 0 &&
-                           WM * WN * TM * 32 * SROWB <= LDSBYTES;
-    uint8_t *stash = lds_base + wave * (TM * 32) * SROWB;
+    // cache lines instead of touching 32 rows.  A stash row holds the wave's
+    // SCHK chunks in PCHK slots (the next power of two: 192-byte rows of the
+    // 192x192 tile take 256).
+    constexpr int SCHK = TN * 32 * 2 / 16;          // 16-byte chunks of a wave's row (bf16)
+    constexpr int PCHK = pow2_at_least(SCHK);       // stash slots per row
+    constexpr int SPITCH = PCHK * 16;               // stash row pitch
+    constexpr bool STASH = OUT == OUT_BF16 && PCHK <= 64 && WM * WN * TM * 32 * SPITCH <= LDSBYTES;
+    uint8_t *stash = lds_base + wave * (TM * 32) * SPITCH;
     if constexpr (STASH) {
         if (full)
             lds_barrier();   // every wave is done with the operand buffers
@@ -353,7 +365,7 @@ __device__ __forceinline__ void store_tile(const Params &p, Acc (&acc)[TM][TN], 
                         const i32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1],
                                          acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
                         if constexpr (FULL) {
-                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rc, off, 0, 0);
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rc, off, 0, CPOL_NT);
                         } else {
 #pragma unroll
                             for (int r = 0; r < 4; ++r)
@@ -386,7 +398,7 @@ __device__ __forceinline__ void store_tile(const Params &p, Acc (&acc)[TM][TN], 
                             // park in this wave's LDS stash (written out below)
                             const int srow = 32 * i + r32;
                             const int chunk = 4 * j + g;
-                            *(u32x2 *)(stash + srow * SROWB + ((chunk ^ (srow & (SCHK - 1))) << 4) + 8 * h) = v;
+                            *(u32x2 *)(stash + srow * SPITCH + ((chunk ^ (srow & (PCHK - 1))) << 4) + 8 * h) = v;
                         } else {
 #pragma unroll
                             for (int r = 0; r < 4; ++r)
@@ -405,7 +417,7 @@ __device__ __forceinline__ void store_tile(const Params &p, Acc (&acc)[TM][TN], 
         body(std::false_type());
     if constexpr (STASH) {
         if (full) {
-            constexpr int LPR = SCHK;                   // lanes per stash row
+            constexpr int LPR = PCHK;                   // lanes per stash row (those past SCHK idle)
             constexpr int RPI = 64 / LPR;               // rows per store instruction
             const int c = lane % LPR;
             const unsigned gbase = (unsigned)((int64_t)(wm * TM * 32) * p.ldc * 2) + col0 +
@@ -413,8 +425,9 @@ __device__ __forceinline__ void store_tile(const Params &p, Acc (&acc)[TM][TN], 
 #pragma unroll
             for (int it = 0; it < TM * 32 / RPI; ++it) {
                 const int srow = it * RPI + lane / LPR;
-                const u32x4 v = *(const u32x4 *)(stash + srow * SROWB + ((c ^ (srow & (SCHK - 1))) << 4));
-                __builtin_amdgcn_raw_buffer_store_b128(v, rc, gbase + (unsigned)(srow * p.ldc * 2), 0, 0);
+                const u32x4 v = *(const u32x4 *)(stash + srow * SPITCH + ((c ^ (srow & (PCHK - 1))) << 4));
+                const unsigned off = c < SCHK ? gbase + (unsigned)(srow * p.ldc * 2) : OOB;
+                __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, CPOL_NT);
             }
         }
     }
