@@ -25,6 +25,9 @@
 //    amax, and a subnormal or zero amax gives code 0 either way, so the code
 //    is max(E - emax, 0).  Scaling by 2^(127 - code) is exact (a power of two,
 //    no overflow since |x| <= amax < 2^(E - 126)).
+//  * The codes are written with non-temporal stores (whole rows per wave;
+//    one MI355X: per-token 4096x7168 +5%, MX e4m3 16384x2048 +10%, e2m1
+//    unchanged); non-temporal loads of X were slower.
 //  * Rounding to the element grid works on the binary32 bits: for a
 //    magnitude in the normal range, adding half an element step minus one
 //    plus the kept lowest bit and truncating rounds to nearest even, a carry
@@ -144,10 +147,10 @@ __global__ void __launch_bounds__(PT_THREADS) quant_f8_pertoken_kernel(const uin
     for (int c = 0; c < PT_KEEP; ++c) {
         const int v = t + PT_THREADS * c;
         if (v < nv)
-            q[v] = pertoken_codes(keep[c], s);
+            __builtin_nontemporal_store(pertoken_codes(keep[c], s), &q[v]);
     }
     for (int v = t + PT_THREADS * PT_KEEP; v < nv; v += PT_THREADS)
-        q[v] = pertoken_codes(x[v], s);
+        __builtin_nontemporal_store(pertoken_codes(x[v], s), &q[v]);
 }
 
 // ------------------------------------------------------------ MX
@@ -196,14 +199,15 @@ __global__ void __launch_bounds__(256) quant_mx_kernel(const uint16_t *X, int64_
         }
         uint8_t *qrow = Q + (int64_t)row[u] * ldq;
         if constexpr (FMT == 0) {
-            *(u32x2q *)(qrow + 32 * b[u] + 8 * part) = u32x2q{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
-                                                              c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
+            const u32x2q v = {c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                              c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
+            __builtin_nontemporal_store(v, (u32x2q *)(qrow + 32 * b[u] + 8 * part));
         } else {
             unsigned v = 0;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 v |= c[i] << (4 * i);                            // element 2j low nibble, 2j+1 high
-            *(unsigned *)(qrow + 16 * b[u] + 4 * part) = v;
+            __builtin_nontemporal_store(v, (unsigned *)(qrow + 16 * b[u] + 4 * part));
         }
         if (part == 0)
             S[(int64_t)row[u] * lds + b[u]] = (uint8_t)code;
