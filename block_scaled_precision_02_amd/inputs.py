@@ -23,6 +23,12 @@ rotating input set):
              1x32 blocks for A and B (scales [M,K/32] and [N,K/32]); two codes
              per byte, even k in the low nibble; no bias.
   i8_qkv     INT8 M=30000 N=21504 K=5376 with bias, values as i8_small.
+  f8_block   FP8 e4m3 with block scales, M=16384 N=7168 K=2048 (seed 106):
+             A, B ~ N(0,1) (fp32); s = amax/448 (fp32) per 1x128 block of A
+             (scale_A [M, K/128]) and per 128x128 block of B (scale_B
+             [ceil(N/128), K/128]), codes = e4m3(x/s) rounded to nearest
+             even; no bias.  (ROCm/mori PR #806 measures its "blockscale"
+             GEMM at this shape; the block sizes are a reading.)
 
 The recipes follow the workloads named for this GEMM (INT8 rowwise as in
 comfy-kitchen PR #174's 30000x21504x5376 projection; per-token FP8 and MXFP8
@@ -40,6 +46,7 @@ WORKLOADS = {
     "mxfp8": ("mx", 16384, 7168, 2048, 103, False, "e4m3", 32),
     "mxfp4": ("mx", 8192, 8192, 8192, 104, False, "e2m1", 1),
     "i8_qkv": ("i8", 30000, 21504, 5376, 105, True, None, None),
+    "f8_block": ("f8b", 16384, 7168, 2048, 106, False, None, 128),
 }
 ORDER = ["i8_small", "f8_ptpc", "mxfp8", "mxfp4", "i8_qkv"]
 
@@ -121,6 +128,21 @@ def mx_quantise(x, fmt, block_rows):
     return quantise(y, fmt), code
 
 
+def block_quantise_e4m3(x, block_rows):
+    """e4m3 with one fp32 scale s = amax/448 per block_rows x 128 block of
+    x [R, K] (K % 128 == 0; an all-zero block gets s = 1).  Returns
+    (codes [R, K] uint8, scales [ceil(R/block_rows), K/128] float32)."""
+    R, K = x.shape
+    Rb = -(-R // block_rows)
+    pad = Rb * block_rows - R
+    xp = np.pad(np.abs(x), ((0, pad), (0, 0))) if pad else np.abs(x)
+    amax = xp.reshape(Rb, block_rows, K // 128, 128).max(axis=(1, 3)).astype(np.float32)
+    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    s = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    sfull = np.repeat(np.repeat(s, block_rows, axis=0)[:R], 128, axis=1)
+    return quantise(np.asarray(x, np.float32) / sfull, "e4m3"), s
+
+
 def bf16_bits(x):
     """float values -> bfloat16 bit patterns via torch's own cast."""
     import torch
@@ -174,6 +196,12 @@ def make(name, rot=0, M=None, N=None, K=None, bias=None, seed=None):
             s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
             s = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
             d[key] = quantise(x / s[:, None], "e4m3")
+            d["scale_a" if key == "A" else "scale_b"] = s
+    elif kind == "f8b":
+        for tid, rows, br, key in ((0, M, 1, "A"), (1, N, 128, "B")):
+            x = rng(seed, tid, rot).standard_normal(size=(rows, K), dtype=np.float32)
+            codes, s = block_quantise_e4m3(x, br)
+            d[key] = codes
             d["scale_a" if key == "A" else "scale_b"] = s
     elif kind == "mx":
         xa = rng(seed, 0, rot).standard_normal(size=(M, K), dtype=np.float32)

@@ -13,6 +13,11 @@ Functions follow the definitions in ``qgemm_oracle.c``:
                   Measured: "ptpc").
   mx           -- MX e4m3 / e2m1 with ue8m0 per 32 K elements (ROCm/mori PR
                   #806, What; ROCm/FlyDSL PR #990).
+  f8_blockscale
+               -- FP8 e4m3 with fp32 scales per 128-element K block: A per
+                  row, B per 128 rows (ROCm/mori PR #806, commit message
+                  table: "blockscale"; the block sizes are a reading, stated
+                  in ``qgemm_oracle.c``).
   pack_b       -- the prepacked weight layout of the ``_prepacked`` GEMM entry
                   points (defined in ``qgemm_oracle.c``).
   quant_f8_pertoken, quant_mx
@@ -84,6 +89,9 @@ def _load():
     lib.orc_f8_pertoken.restype = None
     lib.orc_f8_pertoken.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _P, _I64, _P, _P,
                                     _I64, _I64, _I64]
+    lib.orc_f8_blockscale.restype = ctypes.c_int
+    lib.orc_f8_blockscale.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _P, _I64, _P, _P,
+                                      _I64, _I64, _I64]
     lib.orc_mx.restype = ctypes.c_int
     lib.orc_mx.argtypes = [ctypes.c_int, _P, _I64, _P, _I64, _P, _P, ctypes.c_int, _P,
                            _P, _I64, _P, _P, _I64, _I64, _I64]
@@ -197,6 +205,30 @@ def mx(fmt, A, B, scale_a, scale_b, b_rows_per_scale, K, bias=None):
                         M, N, K)
     if rc != 0:
         raise ValueError("bad MX format or B-scale layout")
+    return C, acc, absdot
+
+
+def f8_blockscale(A, B, scale_a, scale_b, bias=None):
+    """FP8 e4m3 GEMM with block scales.  A [M,K], B [N,K] uint8 e4m3 codes,
+    K % 128 == 0; scale_a float32 [M, K/128]; scale_b float32
+    [ceil(N/128), K/128].
+    Returns (C uint16 [M,N], acc float64 [M,N], absdot float64 [M,N])."""
+    A = _c(A, np.uint8)
+    B = _c(B, np.uint8)
+    M, K = A.shape
+    N = B.shape[0]
+    assert B.shape[1] == K and K % 128 == 0
+    sa = _c(scale_a, np.float32)
+    sb = _c(scale_b, np.float32)
+    assert sa.shape == (M, K // 128) and sb.shape == ((N + 127) // 128, K // 128)
+    bias = _c(bias, np.uint16)
+    C = np.empty((M, N), np.uint16)
+    acc = np.empty((M, N), np.float64)
+    absdot = np.empty((M, N), np.float64)
+    rc = _load().orc_f8_blockscale(_ptr(A), K, _ptr(B), K, _ptr(sa), _ptr(sb), _ptr(bias),
+                                   _ptr(C), N, _ptr(acc), _ptr(absdot), M, N, K)
+    if rc != 0:
+        raise ValueError("K must be a multiple of 128")
     return C, acc, absdot
 
 

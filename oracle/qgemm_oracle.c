@@ -260,6 +260,72 @@ int orc_mx(int fmt, const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb
     return 0;
 }
 
+/* ------------------------------------------------------- FP8 blockscale */
+
+/* FP8 e4m3 GEMM with block-wise fp32 scales: the "blockscale" variant that
+ * "perf(gemm-ar): mxfp8 with row-major scales staged through LDS" (ROCm/mori
+ * PR #806) measures next to per-token FP8 and MXFP8 (commit message table,
+ * M=16384 N=7168 K=2048).  The page names the variant but not its blocks;
+ * the reading taken: K is cut into blocks of 128 elements, A has one scale
+ * per row and K block (scale_a [M, K/128], row stride K/128) and B one per
+ * 128 rows and K block (scale_b [ceil(N/128), K/128]), both binary32 and
+ * row-major, so that
+ *
+ *     C[m,n] = bf16( sum_kb sa[m,kb] * sb[n/128,kb] * P[m,n,kb] (+ bias[n]) ),
+ *     P[m,n,kb] = sum over the block's k of dec(A[m,k]) * dec(B[n,k]).
+ *
+ * P is exact in double (at most 128 products, each a multiple of 2^-18 below
+ * 2^35.7); sa*sb is exact in double (two 24-bit significands); each term
+ * sa*sb*P and the sum over blocks round once in double, so acc lies within
+ * (K/128 + 1) * 2^-53 * absdot of the exact sum, far inside the GEMM's
+ * tolerance.  acc / absdot as for FP8 (absdot = sum_k |sa sb a_k b_k|).
+ * K must be a multiple of 128.
+ *
+ * Per output: f = (float)acc; [f = f + bias[n]]; C = bf16_rne(f).
+ * Returns 0, or -1 if K is not a multiple of 128. */
+int orc_f8_blockscale(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                      const float *scale_a, const float *scale_b, const uint16_t *bias,
+                      uint16_t *C, int64_t ldc, double *acc, double *absdot,
+                      int64_t M, int64_t N, int64_t K)
+{
+    if (K % 128 != 0)
+        return -1;
+    const int64_t KB = K / 128;
+    double lut[256];
+    for (int c = 0; c < 256; ++c)
+        lut[c] = orc_dec_e4m3((uint8_t)c);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            const uint8_t *a = A + m * lda;
+            const uint8_t *b = B + n * ldb;
+            const float *sarow = scale_a + m * KB;
+            const float *sbrow = scale_b + (n / 128) * KB;
+            double s = 0.0, t = 0.0;
+            for (int64_t kb = 0; kb < KB; ++kb) {
+                double p = 0.0, q = 0.0;
+                for (int64_t k = 128 * kb; k < 128 * kb + 128; ++k) {
+                    double x = lut[a[k]] * lut[b[k]];
+                    p += x;
+                    q += fabs(x);
+                }
+                double w = (double)sarow[kb] * (double)sbrow[kb];
+                s += w * p;
+                t += fabs(w) * q;
+            }
+            if (acc)
+                acc[m * N + n] = s;
+            if (absdot)
+                absdot[m * N + n] = t;
+            float f = (float)s;
+            if (bias)
+                f = f + orc_bf16_to_f32(bias[n]);
+            C[m * ldc + n] = orc_bf16_rne(f);
+        }
+    }
+    return 0;
+}
+
 /* ----------------------------------------------------------- quantisers */
 
 /* The quantisers that produce the GEMM's operands from bf16 activations.
