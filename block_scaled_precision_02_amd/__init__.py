@@ -11,6 +11,7 @@ call raises.
     qgemm_i8_rowwise(A, B, scale_a, scale_b, bias=None, out=None)
     qgemm_i8_acc_i32(A, B, out=None)
     qgemm_f8_pertoken(A, B, scale_a, scale_b, bias=None, out=None)
+    qgemm_f8_blockscale(A, B, scale_a, scale_b, bias=None, out=None)
     qgemm_mx(fmt, A, B, scale_a, scale_b, b_layout, bias=None, out=None, K=None)
     qgemm_prepack_b(B, row_bytes=None, out=None)          -> PackedB
     qgemm_i8_rowwise_prepacked(A, Bp, scale_a, scale_b, bias=None, out=None)
@@ -44,7 +45,7 @@ QGEMM_MX_BSCALE_1x32 = 1
 QGEMM_MX_BSCALE_32x32 = 32
 
 # Every symbol include/qgemm.h declares.
-EXPORTS = ("qgemm_i8_rowwise", "qgemm_i8_acc_i32", "qgemm_f8_pertoken", "qgemm_mx",
+EXPORTS = ("qgemm_i8_rowwise", "qgemm_i8_acc_i32", "qgemm_f8_pertoken", "qgemm_f8_blockscale", "qgemm_mx",
            "qgemm_prepacked_b_bytes", "qgemm_prepack_b", "qgemm_i8_rowwise_prepacked",
            "qgemm_f8_pertoken_prepacked", "qgemm_mx_prepacked",
            "qgemm_quant_f8_pertoken", "qgemm_quant_mx",
@@ -72,6 +73,8 @@ def lib():
     L.qgemm_i8_acc_i32.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _P]
     L.qgemm_f8_pertoken.restype = st
     L.qgemm_f8_pertoken.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
+    L.qgemm_f8_blockscale.restype = st
+    L.qgemm_f8_blockscale.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
     L.qgemm_mx.restype = st
     L.qgemm_mx.argtypes = [ctypes.c_int, _P, _I64, _P, _I64, _P, _P, ctypes.c_int, _P, _P, _I64,
                            _I64, _I64, _I64, _P]
@@ -274,6 +277,40 @@ def qgemm_f8_pertoken(A, B, scale_a, scale_b, bias=None, out=None, stream=None):
     with torch.cuda.device(A.device):
         _check(lib().qgemm_f8_pertoken(_ptr(A), lda, _ptr(B), ldb, _ptr(sa), _ptr(sb), _ptr(bias),
                                        _ptr(out), _ldc(out, N), M, N, K, _stream(A.device, stream)))
+    return out
+
+
+def _matrix(t, name, shape, dtypes):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.dtype not in dtypes:
+        raise ValueError(f"{name} must be a tensor of {dtypes}")
+    if tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous with shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    return t
+
+
+def qgemm_f8_blockscale(A, B, scale_a, scale_b, bias=None, out=None, stream=None):
+    """FP8 e4m3 GEMM with fp32 scales per 128-element K block -> bf16 [M, N].
+    scale_a [M, K/128], scale_b [ceil(N/128), K/128], both contiguous."""
+    torch = _torch()
+    lda = _operand(A, "A", _fp8_dtypes())
+    ldb = _operand(B, "B", _fp8_dtypes())
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError(f"A is [M, K={K}] but B is {tuple(B.shape)}")
+    if K % 128:
+        raise ValueError(f"K={K} is not a multiple of 128")
+    sa = _matrix(scale_a, "scale_a", (M, K // 128), (torch.float32,))
+    sb = _matrix(scale_b, "scale_b", ((N + 127) // 128, K // 128), (torch.float32,))
+    bias = _bias(bias, N)
+    _same_device(A.device, B, sa, sb, bias)
+    out = _out(out, M, N, A.device, torch.bfloat16)
+    with torch.cuda.device(A.device):
+        _check(lib().qgemm_f8_blockscale(_ptr(A), lda, _ptr(B), ldb, _ptr(sa), _ptr(sb), _ptr(bias),
+                                         _ptr(out), _ldc(out, N), M, N, K, _stream(A.device, stream)))
     return out
 
 

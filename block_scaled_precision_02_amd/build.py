@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqgemm.so")
-SOURCES = ["qgemm_api.cpp", "qgemm_i8.hip", "qgemm_f8.hip", "qgemm_mx8.hip", "qgemm_mx4.hip",
+SOURCES = ["qgemm_api.cpp", "qgemm_i8.hip", "qgemm_f8.hip", "qgemm_mx8.hip", "qgemm_mx4.hip", "qgemm_f8b.hip",
            "qgemm_quant.hip", "qgemm_pack.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -326,8 +326,10 @@ const char *qgemm_last_error(void) { return g_last_error.c_str(); }
 
 int qgemm_select_tile(int path, int64_t M, int64_t N, int64_t K)
 {
-    if (path < 0 || path > 3)
+    if (path < 0 || path > 4)
         return -1;
+    if (path == 4)
+        return DMA128_TILE;   // blockscale: one variant
     const int64_t kbytes = path == 3 ? K / 2 : K;
     const int prev = g_forced_tile;
     g_forced_tile = -1;
@@ -436,6 +438,40 @@ qgemm_status qgemm_f8_pertoken(const uint8_t *A, int64_t lda, const uint8_t *B, 
                                int64_t N, int64_t K, void *stream)
 {
     return f8_common(A, lda, B, ldb, scale_a, scale_b, bias, C, ldc, M, N, K, stream, false);
+}
+
+// Blockscale FP8 runs in the LDS-fetch kernel's 128x128 form only: K must be
+// a whole number of its 4-stage rounds with scale rows (K/32 bytes) of whole
+// 16-byte chunks, i.e. K % 512 == 0.
+constexpr int64_t F8B_K_MULTIPLE = 512;
+
+qgemm_status qgemm_f8_blockscale(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb, const float *scale_a,
+                                 const float *scale_b, const uint16_t *bias, uint16_t *C, int64_t ldc, int64_t M,
+                                 int64_t N, int64_t K, void *stream)
+{
+    const Shape s{M, N, K};
+    TRY(check_shape(s, false));
+    if (K % F8B_K_MULTIPLE)
+        return fail(QGEMM_ERR_BAD_SHAPE, "K=%lld: blockscale needs K a multiple of %lld", (long long)K,
+                    (long long)F8B_K_MULTIPLE);
+    if (M == 0 || N == 0)
+        return QGEMM_OK;
+    TRY(check_operand("A", A, lda, K));
+    TRY(check_operand("B", B, ldb, K));
+    TRY(check_fp32_scales(scale_a, scale_b));
+    if (!aligned(scale_a, 16) || !aligned(scale_b, 16))
+        return fail(QGEMM_ERR_BAD_LAYOUT, "blockscale scale arrays must be 16-byte aligned");
+    TRY(check_bias(bias));
+    TRY(check_output(C, ldc, N, 2));
+    TRY(check_device());
+    const int tile = DMA128_TILE;
+    Params p = base_params(A, lda, B, ldb, C, ldc, s, K, tile);
+    TRY(check_grid(p));
+    // the scale matrices travel as byte rows of K/32 bytes (K/128 floats)
+    p.mx_sa = (const uint8_t *)scale_a;
+    p.mx_sb = (const uint8_t *)scale_b;
+    p.bias = bias;
+    return finish(launch_f8b(tile, bias != nullptr, p, (hipStream_t)stream));
 }
 
 static qgemm_status mx_common(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const void *B, int64_t ldb_bytes,

@@ -17,6 +17,15 @@
 //  * MX scales arrive the same way: 16 bytes of each scale row (the scales of
 //    four stages) per fetch, double-buffered, fetched four stages ahead; the
 //    scale words are read from LDS together with the fragments.
+//  * Blockscale FP8 (fp32 scales per 128-element K block: A [M, K/128], B
+//    [ceil(N/128), K/128]) has scale rows of K/32 bytes, as long as an e4m3
+//    MX scale row, and a round of four stages covers two of its blocks in 8
+//    bytes of each row, as it covers eight MX blocks: its scales are staged
+//    exactly like the e4m3 MX scales.  A block is two stages; its MFMAs
+//    accumulate into a partial sum that starts at zero, and after the
+//    block's second stage each lane folds it into the total with
+//    fma(partial, sa[m, kb] * sb[n/128, kb], total) (a lane's 32x32 result
+//    tile has one row m and lies inside one 128-column block).
 //  * A 16-byte chunk c of staged row r sits at slot c ^ ((r >> 2) & 3) of its
 //    64-byte row, so a fragment read (16 lanes on 16 consecutive rows at one
 //    logical chunk) covers 16 different 16-byte slots of 256 bytes of banks.
@@ -66,6 +75,7 @@ template <> struct DmaTraits<PATH_I8> { static constexpr int NSUB = 2; };   // c
 template <> struct DmaTraits<PATH_F8> { static constexpr int NSUB = 1; };   // chunks h, 2+h
 template <> struct DmaTraits<PATH_MX8> { static constexpr int NSUB = 1; };  // chunks h, 2+h
 template <> struct DmaTraits<PATH_MX4> { static constexpr int NSUB = 2; };  // chunk 2h+S
+template <> struct DmaTraits<PATH_F8B> { static constexpr int NSUB = 1; };  // chunks h, 2+h
 
 // Fragment of a 32-row MFMA operand for sub-step S of a 64-byte stage.
 //   int8:  16 bytes, chunk 2S+h (32 elements per sub-step)
@@ -101,6 +111,10 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     constexpr int NSUB = DmaTraits<PATH>::NSUB;
     constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4);
+    constexpr bool BS = (PATH == PATH_F8B);               // blockscale FP8
+    constexpr bool SCL = MX || BS;                        // scale chunks staged through LDS
+    static_assert(!BS || BROWS == 128, "blockscale B scales cover 128 rows");
+    static_assert(BROWS == 1 || (BN % BROWS == 0 || BROWS == 32), "B scale rows must align with the tile");
     constexpr int STAGE_BYTES = (BM + BN) * DSTAGE;
     constexpr int OPND_BYTES = DNST * STAGE_BYTES;
     // MX scale chunks: per buffer, 256 rows of A and 256 rows of B (1x32) or
@@ -109,25 +123,25 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr int SA_ROWS = 256;
     constexpr int SB_ROWS = (BROWS == 1) ? 256 : 64;
     constexpr int SCL_BUF = (SA_ROWS + SB_ROWS) * 16;
-    constexpr int SCL_BYTES = MX ? 2 * SCL_BUF : 0;
+    constexpr int SCL_BYTES = SCL ? 2 * SCL_BUF : 0;
     constexpr int NQ = TM * TN;
-    constexpr int RPF = (PATH == PATH_F8 || PATH == PATH_MX8) ? 2 : 1;
+    constexpr int RPF = (PATH == PATH_F8 || PATH == PATH_MX8 || PATH == PATH_F8B) ? 2 : 1;
     constexpr int NDSR = (TM + TN) * RPF;                 // fragment reads per sub-step
     constexpr int DMA_A = BM / 16 / NW, DMA_B = BN / 16 / NW; // fetches per wave per stage
     constexpr int NDMA = DMA_A + DMA_B;
     // scale fetches per wave per chunk: 4 waves fetch A and B scale rows,
     // 8 waves split them (waves 0-3 A, 4-7 B)
-    constexpr int NSCD = MX ? 8 / NW : 0;
+    constexpr int NSCD = SCL ? 8 / NW : 0;
     // A rows of a stage are fetched one region earlier than its B rows
     // (region B of the stage 4 back) except for MX, whose region B is busy
     // with scale reads.
-    constexpr bool SPLIT = !MX;
+    constexpr bool SPLIT = !SCL;
     static_assert(DMA_A * 16 * NW == BM && DMA_B * 16 * NW == BN, "tile rows must be a multiple of 16 per wave");
     static_assert(BM <= SA_ROWS && (BROWS == 1 ? BN <= SB_ROWS : BN / 32 <= SB_ROWS), "scale rows per buffer");
     using Frag = typename PathTraits<PATH>::Frag;
     using Acc = typename AccT<PATH>::T;
 
-    constexpr bool PRM = OUT == OUT_BF16 && (!MX || BIAS);
+    constexpr bool PRM = OUT == OUT_BF16 && (!SCL || BIAS);
     constexpr int PRM_OFF = OPND_BYTES + SCL_BYTES;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[OPND_BYTES + SCL_BYTES + (PRM ? PRM_BYTES : 0)];
 
@@ -195,20 +209,20 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // bytes are stages 4u..4u+3 x 2 blocks; the rest comes again in chunk u+1).
     __amdgpu_buffer_rsrc_t rsa, rsb;
     unsigned sa_fo = OOB, sb_fo = OOB;
-    if constexpr (MX) {
+    if constexpr (SCL) {
         rsa = make_rsrc(p.mx_sa + (int64_t)m0 * p.kblocks, (uint32_t)(rows_a * p.kblocks));
-        const int srows_b = BROWS == 1 ? rows_b : (rows_b + 31) / 32;
+        const int srows_b = (rows_b + BROWS - 1) / BROWS;
         rsb = make_rsrc(p.mx_sb + (int64_t)(n0 / BROWS) * p.kblocks, (uint32_t)(srows_b * p.kblocks));
         const int sw = NW == 8 ? (wave & 3) : wave;               // scale row group of this wave
         const int ra_row = 64 * sw + lane;                         // A scale row of this lane
         sa_fo = ra_row < rows_a ? (unsigned)(ra_row * p.kblocks) : OOB;
-        const int rb_row = BROWS == 1 ? 64 * sw + lane : lane;     // 32x32: rows 0..63, fetched alike by every wave
+        const int rb_row = BROWS == 1 ? 64 * sw + lane : lane;     // 32 / 128 rows: rows 0..63, fetched alike by every wave
         sb_fo = rb_row < srows_b ? (unsigned)(rb_row * p.kblocks) : OOB;
     }
     auto fetch_scales = [&](int u) {
-        if constexpr (MX) {
+        if constexpr (SCL) {
             uint8_t *base = &lds[OPND_BYTES + (u & 1) * SCL_BUF];
-            // four stages of scales: 16 bytes (e2m1) or 8 bytes (e4m3) per row
+            // four stages of scales: 16 bytes (e2m1) or 8 bytes (e4m3, blockscale) per row
             const unsigned kb = (unsigned)((PATH == PATH_MX4 ? 16 : 8) * u);
             if constexpr (NW == 4) {
                 dma16(rsa, sa_fo + kb, base + 64 * 16 * wave);
@@ -227,6 +241,11 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
             acc[i][j] = Acc{};
+    // blockscale: the current K block's partial sums and the fold factors
+    // sa * sb of the stage being multiplied (use) and of the next (nxt)
+    constexpr int BTM = BS ? TM : 1, BTN = BS ? TN : 1;
+    Acc pacc[BTM][BTN];
+    float fs_use[BTM][BTN], fs_nxt[BTM][BTN];
 
     const int arow = wm * TM * 32 + r32;
     const int brow = wn * TN * 32 + r32;
@@ -258,7 +277,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // operand: byte S of it is sub-step S's scale for the lane's block --
     // e2m1: bytes 4J + 2h, 4J + 2h + 1 of the chunk; e4m3: byte 2J + h.
     auto read_chunk = [&](int t) {
-        if constexpr (MX) {
+        if constexpr (SCL) {
             const uint8_t *sbuf = &lds[OPND_BYTES + ((t >> 2) & 1) * SCL_BUF];
             auto rd = [&](const uint8_t *row_base, unsigned (&w)[SCW]) {
                 if constexpr (SCW == 4) {
@@ -276,13 +295,27 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
                 rd(sbuf + (arow + 32 * i) * 16, cra[i]);
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                const int row = BROWS == 1 ? brow + 32 * j : wn * TN + j;
+                const int row = BROWS == 1 ? brow + 32 * j : (wn * TN * 32 + 32 * j) / BROWS;
                 rd(sbuf + SA_ROWS * 16 + row * 16, crb[j]);
             }
         }
     };
     auto read_scales = [&](int t, auto jc) {
-        if constexpr (MX) {
+        if constexpr (BS) {
+            // fold factors of the block stage J belongs to (word J/2 of the
+            // round's 8 bytes); only the block's second stage folds
+            constexpr int J = decltype(jc)::value;
+            if constexpr (J == 0)
+                read_chunk(t);
+            if constexpr (J & 1) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        fs_nxt[i][j] = __builtin_bit_cast(float, cra[i][J >> 1]) *
+                                       __builtin_bit_cast(float, crb[j][J >> 1]);
+            }
+        } else if constexpr (MX) {
             constexpr int J = decltype(jc)::value;
             if constexpr (J == 0)
                 read_chunk(t);
@@ -296,18 +329,38 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
                 sb_nxt[j] = crb[j][W] >> sh;
         }
     };
-    auto mfmas = [&](auto sc, auto setc, auto q0c, auto q1c) {
+    auto mfmas = [&](auto sc, auto setc, auto q0c, auto q1c, auto jc) {
         constexpr int S = decltype(sc)::value;
         constexpr int SET = decltype(setc)::value;
+        constexpr int J = decltype(jc)::value;
         static_for<decltype(q0c)::value, decltype(q1c)::value>([&](auto qc) {
             constexpr int Q = decltype(qc)::value;
             constexpr int i = Q / TN;
             constexpr int j = (i & 1) ? (TN - 1 - Q % TN) : (Q % TN);
-            mfma<PATH, S>(acc[i][j], fb[SET][j], fa[SET][i], MX ? sb_use[j] : 0u, MX ? sa_use[i] : 0u);
+            if constexpr (BS) {
+                if constexpr ((J & 1) == 0) {
+                    // first stage of a K block: the partial sum starts at zero
+                    pacc[i][j] = Acc{};
+                    mfma<PATH, S>(pacc[i][j], fb[SET][j], fa[SET][i], 0u, 0u);
+                } else {
+                    mfma<PATH, S>(pacc[i][j], fb[SET][j], fa[SET][i], 0u, 0u);
+                    const float f = fs_use[i][j];
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        acc[i][j][e] = __builtin_fmaf(pacc[i][j][e], f, acc[i][j][e]);
+                }
+            } else {
+                mfma<PATH, S>(acc[i][j], fb[SET][j], fa[SET][i], MX ? sb_use[j] : 0u, MX ? sa_use[i] : 0u);
+            }
         });
     };
     auto use_next_scales = [&]() {
-        if constexpr (MX) {
+        if constexpr (BS) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) fs_use[i][j] = fs_nxt[i][j];
+        } else if constexpr (MX) {
 #pragma unroll
             for (int i = 0; i < TM; ++i) sa_use[i] = sa_nxt[i];
 #pragma unroll
@@ -318,9 +371,9 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // Prologue: the tile's epilogue operands (waves 0-2, one fetch each),
     // scale chunk 0, stages 0..2 and the A rows of stage 3; wait for stage 0.
     if constexpr (PRM) {
-        if (wave == 0 && !MX)
+        if (wave == 0 && !SCL)
             dma16(make_rsrc(p.scale_a + m0, (uint32_t)(rows_a * 4)), 16 * lane, &lds[PRM_OFF]);
-        if (wave == 1 && !MX)
+        if (wave == 1 && !SCL)
             dma16(make_rsrc(p.scale_b + n0, (uint32_t)(rows_b * 4)), 16 * lane, &lds[PRM_OFF + PRM_SB]);
         if (wave == 2 && BIAS)
             dma16(make_rsrc(p.bias + n0, (uint32_t)(rows_b * 2)), 16 * lane, &lds[PRM_OFF + PRM_BIAS]);
@@ -365,9 +418,9 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         fetch_part(t + 3, I1());
         if constexpr (NSUB == 2) {
             read_frags(I1(), J, I1());
-            mfmas(I0(), I0(), I0(), std::integral_constant<int, NQ>());
+            mfmas(I0(), I0(), I0(), std::integral_constant<int, NQ>(), jc);
         } else {
-            mfmas(I0(), std::integral_constant<int, SET0>(), I0(), std::integral_constant<int, NQ / 2>());
+            mfmas(I0(), std::integral_constant<int, SET0>(), I0(), std::integral_constant<int, NQ / 2>(), jc);
         }
         // issue order: each MFMA followed by its share of the fetches and of
         // the fragment reads
@@ -397,13 +450,13 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         read_frags(I0(), (J + 1) & 3, std::integral_constant<int, SETN>());
         read_scales(t + 1, std::integral_constant<int, (J + 1) & 3>());
         if constexpr (NSUB == 2) {
-            mfmas(I1(), I1(), I0(), std::integral_constant<int, NQ>());
+            mfmas(I1(), I1(), I0(), std::integral_constant<int, NQ>(), jc);
         } else {
             mfmas(I0(), std::integral_constant<int, SET0>(), std::integral_constant<int, NQ / 2>(),
-                  std::integral_constant<int, NQ>());
+                  std::integral_constant<int, NQ>(), jc);
         }
         constexpr int NB = (NSUB == 2) ? NQ : NQ / 2;
-        constexpr int RB = NDSR + ((MX && ((J + 1) & 3) == 0) ? TM + TN : 0);
+        constexpr int RB = NDSR + ((SCL && ((J + 1) & 3) == 0) ? TM + TN : 0);
         static_for<0, NB>([&](auto qc) {
             constexpr int Q = decltype(qc)::value;
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);

@@ -48,7 +48,9 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-enum Path { PATH_I8 = 0, PATH_F8 = 1, PATH_MX8 = 2, PATH_MX4 = 3 };
+// PATH_F8B: e4m3 with fp32 scales per 128-element K block (A per row, B per
+// 128 rows), applied inside the K loop; LDS-fetch kernel only.
+enum Path { PATH_I8 = 0, PATH_F8 = 1, PATH_MX8 = 2, PATH_MX4 = 3, PATH_F8B = 4 };
 enum OutKind { OUT_BF16 = 0, OUT_I32 = 1 };
 
 // Kernel arguments (one struct, passed by value).
@@ -139,6 +141,7 @@ template <> struct PathTraits<PATH_I8> { static constexpr int NSUB = 4; using Fr
 template <> struct PathTraits<PATH_F8> { static constexpr int NSUB = 2; using Frag = i32x8; };
 template <> struct PathTraits<PATH_MX8> { static constexpr int NSUB = 2; using Frag = i32x8; };
 template <> struct PathTraits<PATH_MX4> { static constexpr int NSUB = 4; using Frag = i32x8; };
+template <> struct PathTraits<PATH_F8B> { static constexpr int NSUB = 2; using Frag = i32x8; };
 
 // Fragment of one 32-row MFMA operand for K sub-step S, read from a staged
 // tile.  Lane (h = lane/32, row = lane%32):
@@ -181,7 +184,7 @@ __device__ __forceinline__ void mfma(typename AccT<PATH>::T &acc,
 {
     if constexpr (PATH == PATH_I8) {
         acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb, fa, acc, 0, 0, 0);
-    } else if constexpr (PATH == PATH_F8) {
+    } else if constexpr (PATH == PATH_F8 || PATH == PATH_F8B) {
         // scale operands 0 with op_sel 0: the unscaled f8f6f4 encoding.
         acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, acc, 0, 0, 0, 0, 0, 0);
     } else if constexpr (PATH == PATH_MX8) {
@@ -261,7 +264,9 @@ __device__ __forceinline__ void store_tile(const Params &p, Acc (&acc)[TM][TN], 
                                            const uint8_t *prm, int m0, int n0, int rows_a, int rows_b)
 {
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
-    constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4);
+    // MX and blockscale apply their scales inside the K loop: the epilogue
+    // only adds the bias and rounds
+    constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4 || PATH == PATH_F8B);
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;

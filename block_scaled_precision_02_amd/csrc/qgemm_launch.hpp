@@ -97,5 +97,7 @@ hipError_t launch_i8(int tile, bool bias, int out, const Params &p, hipStream_t 
 hipError_t launch_f8(int tile, bool bias, const Params &p, hipStream_t s);
 hipError_t launch_mx8(int tile, bool bias, int brows, bool svec, const Params &p, hipStream_t s);
 hipError_t launch_mx4(int tile, bool bias, int brows, bool svec, const Params &p, hipStream_t s);
+// FP8 blockscale: tile 7 only (needs K % 512 == 0 and 16-byte aligned scale arrays).
+hipError_t launch_f8b(int tile, bool bias, const Params &p, hipStream_t s);
 
 }  // namespace qgemm

@@ -16,6 +16,9 @@
  *                      per-channel (row of B) scales, the "ptpc" GEMM of
  *                      ROCm/mori PR #806 "perf(gemm-ar): mxfp8 with row-major
  *                      scales staged through LDS", commit message table.
+ *   qgemm_f8_blockscale  e4m3 A and B with fp32 scales per 128-element K
+ *                      block (A per row, B per 128 rows): the "blockscale"
+ *                      GEMM of the same page.
  *   qgemm_mx           MX: e4m3 or e2m1 elements with one ue8m0 scale per 32
  *                      elements along K; A scales [M, K/32] and B scales
  *                      [N/32, K/32] as uint8 row-major ("mxfp8_raw", ROCm/mori
@@ -118,6 +121,27 @@ qgemm_status qgemm_f8_pertoken(const uint8_t *A, int64_t lda, const uint8_t *B, 
                                const float *scale_a, const float *scale_b, const uint16_t *bias,
                                uint16_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
                                void *stream);
+
+/* FP8 e4m3 GEMM with block-wise fp32 scales, the "blockscale" GEMM that
+ * ROCm/mori PR #806 "perf(gemm-ar): mxfp8 with row-major scales staged
+ * through LDS" measures next to "ptpc" and "mxfp8" (commit message table).
+ * The page names no block sizes; this entry point takes K blocks of 128:
+ *   A        [M, K] e4m3fn codes, row stride lda bytes
+ *   B        [N, K] e4m3fn codes, row stride ldb bytes
+ *   scale_a  fp32 [M, K/128], row-major, row stride K/128: one scale per row
+ *            of A and K block (per token)
+ *   scale_b  fp32 [ceil(N/128), K/128], row-major: one scale per 128 rows of
+ *            B and K block
+ *   bias, C  as for qgemm_i8_rowwise
+ * acc = sum_kb scale_a[m,kb] * scale_b[n/128,kb] * P[kb], P[kb] the fp32
+ * matrix-core sum of the block's 128 products, each block folded into the
+ * fp32 total with one fused multiply-add; then f = acc, [+ bias], bf16
+ * round-nearest-even.  K must be a multiple of 512 (QGEMM_ERR_BAD_SHAPE) and
+ * both scale arrays 16-byte aligned (QGEMM_ERR_BAD_LAYOUT). */
+qgemm_status qgemm_f8_blockscale(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                                 const float *scale_a, const float *scale_b, const uint16_t *bias,
+                                 uint16_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                 void *stream);
 
 /* MX GEMM (block-scaled e4m3 or e2m1).
  *   A        [M, K] elements of fmt, row stride lda_bytes (K or K/2 bytes of data)
@@ -228,7 +252,8 @@ const char *qgemm_status_string(qgemm_status status);
 
 /* Tile variant the host-side table picks for a problem (pure host logic, no
  * HIP call; for MX, assuming 16-byte-aligned scale arrays).  path: 0 int8,
- * 1 fp8, 2 MX e4m3, 3 MX e2m1.  Returns the tile id, or -1 for a bad path:
+ * 1 fp8, 2 MX e4m3, 3 MX e2m1, 4 fp8 blockscale (always tile 7).  Returns
+ * the tile id, or -1 for a bad path:
  *   0: 256x256, 4 waves, operands staged through registers
  *   1: 128x128    2: 256x256 with 8 waves, staged through registers
  *   3: 192x192

@@ -73,6 +73,9 @@ def gpu_run(d, out=None, stream=None):
     if d["kind"] == "f8":
         return q.qgemm_f8_pertoken(dev(d["A"]), dev(d["B"]), dev(d["scale_a"]),
                                    dev(d["scale_b"]), bias, out=out, stream=stream)
+    if d["kind"] == "f8b":
+        return q.qgemm_f8_blockscale(dev(d["A"]), dev(d["B"]), dev(d["scale_a"]),
+                                     dev(d["scale_b"]), bias, out=out, stream=stream)
     fmt = q.QGEMM_MX_E4M3 if d["fmt"] == "e4m3" else q.QGEMM_MX_E2M1
     return q.qgemm_mx(fmt, dev(d["A"]), dev(d["B"]), dev(d["scale_a"]), dev(d["scale_b"]),
                       d["b_rows_per_scale"], bias, out=out, stream=stream)
@@ -86,6 +89,7 @@ def oracle_run(d, rows=None, cols=None):
     if rows is not None:
         A, sa = A[rows], sa[rows]
     if cols is not None:
+        assert d["kind"] != "f8b", "blockscale B scales cover 128 rows: compare whole rows of C"
         if d["kind"] == "mx" and d["b_rows_per_scale"] == 32:
             sb = np.repeat(sb, 32, axis=0)[:d["N"]][cols]
             brows = 1
@@ -98,6 +102,9 @@ def oracle_run(d, rows=None, cols=None):
         return C, None, acc
     if d["kind"] == "f8":
         C, _, absdot = oracle.f8_pertoken(A, B, sa, sb, bias)
+        return C, absdot, None
+    if d["kind"] == "f8b":
+        C, _, absdot = oracle.f8_blockscale(A, B, sa, sb, bias)
         return C, absdot, None
     fmt = oracle.MX_E4M3 if d["fmt"] == "e4m3" else oracle.MX_E2M1
     brows = d["b_rows_per_scale"] if cols is None else 1

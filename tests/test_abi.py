@@ -261,3 +261,36 @@ def test_prepacked_gemms_pass_their_checks(monkeypatch):
     assert L.qgemm_mx_prepacked(1, FAKE, 256, FAKE2, FAKE3, FAKE3, 32, None, FAKE, 64, 64, 64, 512,
                                 None) == q.QGEMM_ERR_UNSUPPORTED_DEVICE
     assert L.qgemm_prepack_b(FAKE, 256, 4, 256, FAKE2, None) == q.QGEMM_ERR_UNSUPPORTED_DEVICE
+
+
+def f8b(A=FAKE, lda=512, B=FAKE2, ldb=512, sa=FAKE3, sb=FAKE3, bias=None, C=FAKE, ldc=64, M=64, N=64,
+        K=512):
+    return q.lib().qgemm_f8_blockscale(A, lda, B, ldb, sa, sb, bias, C, ldc, M, N, K, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(A=None), q.QGEMM_ERR_NULL_POINTER),
+    (dict(sa=None), q.QGEMM_ERR_NULL_POINTER),
+    (dict(sb=None), q.QGEMM_ERR_NULL_POINTER),
+    (dict(C=None), q.QGEMM_ERR_NULL_POINTER),
+    (dict(K=0), q.QGEMM_ERR_BAD_SHAPE),
+    (dict(K=640, lda=640, ldb=640), q.QGEMM_ERR_BAD_SHAPE),     # blockscale needs K % 512 == 0
+    (dict(K=128, lda=128, ldb=128), q.QGEMM_ERR_BAD_SHAPE),
+    (dict(M=-1), q.QGEMM_ERR_BAD_SHAPE),
+    (dict(lda=256), q.QGEMM_ERR_BAD_LAYOUT),
+    (dict(sa=FAKE3 + 4), q.QGEMM_ERR_BAD_LAYOUT),                # scales must be 16-byte aligned
+    (dict(sb=FAKE3 + 8), q.QGEMM_ERR_BAD_LAYOUT),
+    (dict(ldc=60, N=60), q.QGEMM_ERR_BAD_LAYOUT),
+    (dict(bias=FAKE3 + 1), q.QGEMM_ERR_BAD_LAYOUT),
+])
+def test_f8_blockscale_rejects(kw, status):
+    assert f8b(**kw) == status
+    msg = q.lib().qgemm_last_error().decode()
+    assert msg.startswith(q.lib().qgemm_status_string(status).decode())
+
+
+def test_f8_blockscale_checks_pass_before_the_device_check(monkeypatch):
+    monkeypatch.setenv("QGEMM_FAKE_ARCH", "gfx1201")
+    assert f8b() == q.QGEMM_ERR_UNSUPPORTED_DEVICE
+    assert f8b(M=0) == q.QGEMM_OK
+    assert q.select_tile(4, 16384, 7168, 2048) == 7

@@ -1,0 +1,129 @@
+"""GPU parity of the FP8 blockscale GEMM (qgemm_f8_blockscale) against the CPU
+oracle on the same seeded inputs, through the C ABI (the ctypes binding).
+
+Bar: per element |gpu - oracle| <= 1e-2 * sum_k |sa sb a_k b_k| + 1 bf16 ulp,
+cosine >= 0.99999.  Shapes span several 128x128 tiles with ragged M and N
+tails (B scale rows cover 128 rows, so a ragged N leaves a partial scale
+row); scales over a wide range, negative and zero, so that a block scale
+applied to the wrong block or row leaves the bound.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+from block_scaled_precision_02_amd import inputs  # noqa: E402
+import block_scaled_precision_02_amd as q  # noqa: E402
+
+from tests import parity  # noqa: E402
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _gpu_only():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    q.force_tile(-1)
+    yield
+    q.force_tile(-1)
+
+
+def _check(d, what, out=None):
+    _say(f"[parity] {what} M={d['M']} N={d['N']} K={d['K']}")
+    out = parity.gpu_run(d, out=out)
+    torch.cuda.synchronize()
+    ref, absdot, _ = parity.oracle_run(d)
+    worst, cos = parity.compare(d, parity.bits(out), ref, absdot, what)
+    _say(f"[parity] {what}: worst err/bound {worst:.3g} cos {cos:.8f}")
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 512), (17, 33, 512), (300, 520, 1024), (129, 200, 2048),
+                                   (1, 1, 512), (130, 384, 1536)])
+@pytest.mark.parametrize("bias", [False, True])
+def test_f8b_small(M, N, K, bias):
+    d = inputs.make("f8_block", M=M, N=N, K=K, bias=bias)
+    _check(d, f"f8b bias={bias}")
+
+
+def _wide_scales(shape, rng):
+    s = np.exp2(rng.uniform(-16, 8, size=shape)) * np.where(rng.random(shape) < 0.2, -1.0, 1.0)
+    s[rng.random(shape) < 0.05] = 0.0
+    return s.astype(np.float32)
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 1024), (200, 300, 2048)])
+def test_f8b_scale_indexing(M, N, K):
+    """Every (row, K block) and (128-row group, K block) scale differs by up to
+    2^24, some negative, some zero."""
+    d = inputs.make("f8_block", M=M, N=N, K=K)
+    rng = np.random.default_rng(77)
+    d["scale_a"] = _wide_scales(d["scale_a"].shape, rng)
+    d["scale_b"] = _wide_scales(d["scale_b"].shape, rng)
+    _check(d, "f8b wide scales")
+
+
+EDGE_SHAPES = [(1, 1, 512), (17, 31, 512), (100, 200, 1024), (257, 300, 512), (1000, 129, 2048)]
+
+
+@pytest.mark.parametrize("M,N,K", EDGE_SHAPES)
+def test_f8b_edges_canaries(M, N, K):
+    """NaN-filled output with canary columns (ldc > N) and a canary row block:
+    nothing outside [0,M) x [0,N) may change."""
+    d = inputs.make("f8_block", M=M, N=N, K=K, bias=True)
+    ldc = N + (-N) % 8 + 8
+    buf = torch.full((M + 3, ldc), float("nan"), dtype=torch.bfloat16, device="cuda")
+    before = parity.bits(buf)
+    _check(d, "f8b canaries", out=buf[:M, :N])
+    after = parity.bits(buf)
+    assert np.array_equal(after[:M, N:], before[:M, N:]), "wrote past N"
+    assert np.array_equal(after[M:], before[M:]), "wrote past M"
+
+
+def test_f8b_side_stream_and_repeat():
+    d = inputs.make("f8_block", M=384, N=256, K=1024)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out1 = parity.gpu_run(d, stream=s)
+        out2 = parity.gpu_run(d, stream=s)
+    s.synchronize()
+    b1, b2 = parity.bits(out1), parity.bits(out2)
+    assert np.array_equal(b1, b2), "two launches on the same inputs differ"
+    ref, absdot, _ = parity.oracle_run(d)
+    parity.compare(d, b1, ref, absdot, "f8b side stream")
+
+
+def _sample_rows(M, n, rng):
+    tail = np.arange(max(0, M - 8), M)
+    head = np.arange(0, min(8, M))
+    mid = rng.choice(M, size=max(0, n - len(head) - len(tail)), replace=False)
+    return np.unique(np.concatenate([head, mid, tail]))
+
+
+def test_f8b_full_workload_sampled():
+    """16384 x 7168 x 2048, launched as the benchmark launches it; the oracle
+    checks a sample of whole output rows."""
+    d = inputs.make("f8_block")
+    _say(f"[parity] full f8_block M={d['M']} N={d['N']} K={d['K']}")
+    out = parity.gpu_run(d)
+    torch.cuda.synchronize()
+    rows = _sample_rows(d["M"], 24, np.random.default_rng(1))
+    got = parity.bits(out[torch.from_numpy(rows).cuda()])
+    ref, absdot, _ = parity.oracle_run(d, rows=rows)
+    worst, cos = parity.compare(d, got, ref, absdot, "full f8_block")
+    _say(f"[parity] full f8_block: worst err/bound {worst:.3g} cos {cos:.8f}")
+
+
+def test_f8b_rejects_k_not_multiple_of_512():
+    A = torch.zeros((4, 640), dtype=torch.uint8, device="cuda")
+    sa = torch.ones((4, 5), dtype=torch.float32, device="cuda")
+    sb = torch.ones((1, 5), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        q.qgemm_f8_blockscale(A, A, sa, sb)
