@@ -20,9 +20,11 @@ namespace qgemm {
 //   8 -> small M (qgemm_skinny.hpp): 16 rows x 16 columns, eight waves splitting
 //        K; bf16 output
 //   9 -> small M: 64 rows x 16 columns, eight waves splitting K; same paths
-constexpr int NUM_TILES = 10;
+//  10 -> FP8 blockscale only: 256 rows x 128 columns fetched straight into LDS,
+//        2x2 waves of 128x64 (one wave per SIMD: 128 totals + 128 partial sums)
+constexpr int NUM_TILES = 11;
 constexpr int DMA_TILE = 4, DMA8_TILE = 5, DMA192_TILE = 6, DMA128_TILE = 7;
-constexpr int SKINNY16_TILE = 8, SKINNY64_TILE = 9;
+constexpr int SKINNY16_TILE = 8, SKINNY64_TILE = 9, F8B256_TILE = 10;
 __host__ __device__ constexpr bool is_dma_tile(int tile) { return tile >= DMA_TILE && tile <= DMA128_TILE; }
 __host__ __device__ constexpr bool is_skinny_tile(int tile) { return tile == SKINNY16_TILE || tile == SKINNY64_TILE; }
 // Output rows (of A) and columns (rows of B) of one workgroup's tile.
@@ -31,7 +33,10 @@ __host__ __device__ constexpr int tile_edge_m(int tile)
     return tile == SKINNY16_TILE ? 16 : tile == SKINNY64_TILE ? 64
          : (tile == 1 || tile == DMA128_TILE) ? 128 : ((tile == 3 || tile == DMA192_TILE) ? 192 : 256);
 }
-__host__ __device__ constexpr int tile_edge_n(int tile) { return is_skinny_tile(tile) ? 16 : tile_edge_m(tile); }
+__host__ __device__ constexpr int tile_edge_n(int tile)
+{
+    return is_skinny_tile(tile) ? 16 : tile == F8B256_TILE ? 128 : tile_edge_m(tile);
+}
 __host__ __device__ constexpr int tile_edge(int tile) { return tile_edge_m(tile); }
 __host__ __device__ constexpr int tile_threads(int tile)
 {
@@ -97,7 +102,7 @@ hipError_t launch_i8(int tile, bool bias, int out, const Params &p, hipStream_t 
 hipError_t launch_f8(int tile, bool bias, const Params &p, hipStream_t s);
 hipError_t launch_mx8(int tile, bool bias, int brows, bool svec, const Params &p, hipStream_t s);
 hipError_t launch_mx4(int tile, bool bias, int brows, bool svec, const Params &p, hipStream_t s);
-// FP8 blockscale: tile 7 only (needs K % 512 == 0 and 16-byte aligned scale arrays).
+// FP8 blockscale: tiles 7 and 10 (need K % 512 == 0 and 16-byte aligned scale arrays).
 hipError_t launch_f8b(int tile, bool bias, const Params &p, hipStream_t s);
 
 }  // namespace qgemm

@@ -252,8 +252,9 @@ const char *qgemm_status_string(qgemm_status status);
 
 /* Tile variant the host-side table picks for a problem (pure host logic, no
  * HIP call; for MX, assuming 16-byte-aligned scale arrays).  path: 0 int8,
- * 1 fp8, 2 MX e4m3, 3 MX e2m1, 4 fp8 blockscale (always tile 7).  Returns
- * the tile id, or -1 for a bad path:
+ * 1 fp8, 2 MX e4m3, 3 MX e2m1, 4 fp8 blockscale (tile 10 when its grid of
+ * 256x128 tiles fills the 256 CUs at least once, else tile 7).  Returns the
+ * tile id, or -1 for a bad path:
  *   0: 256x256, 4 waves, operands staged through registers
  *   1: 128x128    2: 256x256 with 8 waves, staged through registers
  *   3: 192x192
@@ -263,6 +264,7 @@ const char *qgemm_status_string(qgemm_status status);
  *   7: 128x128, 4 waves, operands fetched straight into LDS
  *   8: 16 rows x 16 columns, 8 waves splitting K (small M)
  *   9: 64 rows x 16 columns, 8 waves splitting K (small M)
+ *  10: 256 rows x 128 columns, fp8 blockscale only
  * Tiles 4-7 need K bytes a multiple of 256 and MX scale rows a multiple of
  * 16 bytes; where these hold, the table's 256x256 choice runs as tile 5,
  * 192x192 as tile 6 and 128x128 as tile 7.  Calls with M <= 64 take tile 8
@@ -271,7 +273,7 @@ const char *qgemm_status_string(qgemm_status status);
 int qgemm_select_tile(int path, int64_t M, int64_t N, int64_t K);
 
 /* Rows of A one tile covers (for tiles 0-7 also the rows of B; tiles 8 and 9
- * cover 16 rows of B), or 0 for an unknown id. */
+ * cover 16 rows of B, tile 10 128), or 0 for an unknown id. */
 int qgemm_tile_rows(int tile);
 
 /* Force a tile id for later calls on the calling thread (benchmarks and the

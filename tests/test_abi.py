@@ -145,10 +145,11 @@ def test_tile_table():
     assert L.qgemm_select_tile(2, 16, 7168, 2048) == 8
     assert L.qgemm_select_tile(3, 16, 8192, 8192) == 8
     assert L.qgemm_select_tile(3, 17, 8192, 8192) not in (8, 9)    # MX: the 16-row form only
-    for t, e in ((0, 256), (1, 128), (2, 256), (3, 192), (4, 256), (5, 256), (6, 192), (7, 128), (8, 16), (9, 64)):
+    for t, e in ((0, 256), (1, 128), (2, 256), (3, 192), (4, 256), (5, 256), (6, 192), (7, 128), (8, 16), (9, 64),
+                 (10, 256)):
         assert L.qgemm_tile_rows(t) == e
-    assert L.qgemm_tile_rows(10) == 0 and L.qgemm_tile_rows(-1) == 0
-    assert L.qgemm_force_tile(10) == -2
+    assert L.qgemm_tile_rows(11) == 0 and L.qgemm_tile_rows(-1) == 0
+    assert L.qgemm_force_tile(11) == -2
     assert L.qgemm_force_tile(1) == -1
     assert L.qgemm_force_tile(-1) == 1
 
@@ -293,4 +294,6 @@ def test_f8_blockscale_checks_pass_before_the_device_check(monkeypatch):
     monkeypatch.setenv("QGEMM_FAKE_ARCH", "gfx1201")
     assert f8b() == q.QGEMM_ERR_UNSUPPORTED_DEVICE
     assert f8b(M=0) == q.QGEMM_OK
-    assert q.select_tile(4, 16384, 7168, 2048) == 7
+    assert q.select_tile(4, 16384, 7168, 2048) == 10
+    assert q.select_tile(4, 256, 7168, 2048) == 7          # 56 tiles of 256x128: too few for the chip
+    assert q.select_tile(4, 1024, 8192, 2048) == 10         # 4 x 64 = 256 tiles

@@ -45,12 +45,18 @@ def _check(d, what, out=None):
     return out
 
 
+# tile 7: 128x128 (the default); tile 10: 256x128
+TILES = [7, 10]
+
+
+@pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("M,N,K", [(256, 256, 512), (17, 33, 512), (300, 520, 1024), (129, 200, 2048),
                                    (1, 1, 512), (130, 384, 1536)])
 @pytest.mark.parametrize("bias", [False, True])
-def test_f8b_small(M, N, K, bias):
+def test_f8b_small(M, N, K, bias, tile):
+    q.force_tile(tile)
     d = inputs.make("f8_block", M=M, N=N, K=K, bias=bias)
-    _check(d, f"f8b bias={bias}")
+    _check(d, f"f8b bias={bias} tile={tile}")
 
 
 def _wide_scales(shape, rng):
@@ -59,10 +65,12 @@ def _wide_scales(shape, rng):
     return s.astype(np.float32)
 
 
-@pytest.mark.parametrize("M,N,K", [(256, 256, 1024), (200, 300, 2048)])
-def test_f8b_scale_indexing(M, N, K):
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("M,N,K", [(256, 256, 1024), (200, 300, 2048), (520, 260, 512)])
+def test_f8b_scale_indexing(M, N, K, tile):
     """Every (row, K block) and (128-row group, K block) scale differs by up to
     2^24, some negative, some zero."""
+    q.force_tile(tile)
     d = inputs.make("f8_block", M=M, N=N, K=K)
     rng = np.random.default_rng(77)
     d["scale_a"] = _wide_scales(d["scale_a"].shape, rng)
@@ -73,10 +81,12 @@ def test_f8b_scale_indexing(M, N, K):
 EDGE_SHAPES = [(1, 1, 512), (17, 31, 512), (100, 200, 1024), (257, 300, 512), (1000, 129, 2048)]
 
 
+@pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("M,N,K", EDGE_SHAPES)
-def test_f8b_edges_canaries(M, N, K):
+def test_f8b_edges_canaries(M, N, K, tile):
     """NaN-filled output with canary columns (ldc > N) and a canary row block:
     nothing outside [0,M) x [0,N) may change."""
+    q.force_tile(tile)
     d = inputs.make("f8_block", M=M, N=N, K=K, bias=True)
     ldc = N + (-N) % 8 + 8
     buf = torch.full((M + 3, ldc), float("nan"), dtype=torch.bfloat16, device="cuda")
@@ -107,9 +117,11 @@ def _sample_rows(M, n, rng):
     return np.unique(np.concatenate([head, mid, tail]))
 
 
-def test_f8b_full_workload_sampled():
+@pytest.mark.parametrize("tile", [-1, 10])
+def test_f8b_full_workload_sampled(tile):
     """16384 x 7168 x 2048, launched as the benchmark launches it; the oracle
     checks a sample of whole output rows."""
+    q.force_tile(tile)
     d = inputs.make("f8_block")
     _say(f"[parity] full f8_block M={d['M']} N={d['N']} K={d['K']}")
     out = parity.gpu_run(d)
