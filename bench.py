@@ -324,7 +324,7 @@ def main():
                          "WRITE_SIZE runs under DIR (no GPU needed)")
     args = ap.parse_args()
     if args.traffic_from:
-        print(json.dumps(write_traffic(args.traffic_from, ["i8_qkv", "mxfp4"])))
+        print(json.dumps(write_traffic(args.traffic_from, ["i8_qkv", "mxfp4", "f8_block"])))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this GEMM library has no multi-GPU path "
