@@ -23,6 +23,9 @@ rotating input set):
              1x32 blocks for A and B (scales [M,K/32] and [N,K/32]); two codes
              per byte, even k in the low nibble; no bias.
   i8_qkv     INT8 M=30000 N=21504 K=5376 with bias, values as i8_small.
+  mx_a8w4    MX with e4m3 A (activations) and e2m1 B (weights), M=N=K=8192
+             (seed 107): A as mxfp8's A, B as mxfp4's B, 1x32 scales on both
+             ([M,K/32], [N,K/32]); no bias.
   f8_block   FP8 e4m3 with block scales, M=16384 N=7168 K=2048 (seed 106):
              A, B ~ N(0,1) (fp32); s = amax/448 (fp32) per 1x128 block of A
              (scale_A [M, K/128]) and per 128x128 block of B (scale_B
@@ -47,6 +50,7 @@ WORKLOADS = {
     "mxfp4": ("mx", 8192, 8192, 8192, 104, False, "e2m1", 1),
     "i8_qkv": ("i8", 30000, 21504, 5376, 105, True, None, None),
     "f8_block": ("f8b", 16384, 7168, 2048, 106, False, None, 128),
+    "mx_a8w4": ("mx", 8192, 8192, 8192, 107, False, "e4m3/e2m1", 1),
 }
 ORDER = ["i8_small", "f8_ptpc", "mxfp8", "mxfp4", "i8_qkv"]
 
@@ -204,14 +208,17 @@ def make(name, rot=0, M=None, N=None, K=None, bias=None, seed=None):
             d[key] = codes
             d["scale_a" if key == "A" else "scale_b"] = s
     elif kind == "mx":
+        fa, fb = fmt.split("/") if "/" in fmt else (fmt, fmt)
         xa = rng(seed, 0, rot).standard_normal(size=(M, K), dtype=np.float32)
-        ca, sa = mx_quantise(xa, fmt, 1)
+        ca, sa = mx_quantise(xa, fa, 1)
         del xa
         xb = rng(seed, 1, rot).standard_normal(size=(N, K), dtype=np.float32)
-        cb, sb = mx_quantise(xb, fmt, brows)
+        cb, sb = mx_quantise(xb, fb, brows)
         del xb
-        if fmt == "e2m1":
-            ca, cb = pack_e2m1(ca), pack_e2m1(cb)
+        if fa == "e2m1":
+            ca = pack_e2m1(ca)
+        if fb == "e2m1":
+            cb = pack_e2m1(cb)
         d.update(A=ca, B=cb, scale_a=sa, scale_b=sb)
     else:
         raise ValueError(name)

@@ -13,6 +13,8 @@ Functions follow the definitions in ``qgemm_oracle.c``:
                   Measured: "ptpc").
   mx           -- MX e4m3 / e2m1 with ue8m0 per 32 K elements (ROCm/mori PR
                   #806, What; ROCm/FlyDSL PR #990).
+  mx2          -- MX with its own element format per operand (e.g. e4m3
+                  activations x e2m1 weights); the same scale rule.
   f8_blockscale
                -- FP8 e4m3 with fp32 scales per 128-element K block: A per
                   row, B per 128 rows (ROCm/mori PR #806, commit message
@@ -89,6 +91,9 @@ def _load():
     lib.orc_f8_pertoken.restype = None
     lib.orc_f8_pertoken.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _P, _I64, _P, _P,
                                     _I64, _I64, _I64]
+    lib.orc_mx2.restype = ctypes.c_int
+    lib.orc_mx2.argtypes = [ctypes.c_int, ctypes.c_int, _P, _I64, _P, _I64, _P, _P, ctypes.c_int, _P,
+                            _P, _I64, _P, _P, _I64, _I64, _I64]
     lib.orc_f8_blockscale.restype = ctypes.c_int
     lib.orc_f8_blockscale.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _P, _I64, _P, _P,
                                       _I64, _I64, _I64]
@@ -203,6 +208,31 @@ def mx(fmt, A, B, scale_a, scale_b, b_rows_per_scale, K, bias=None):
     rc = _load().orc_mx(fmt, _ptr(A), row_bytes, _ptr(B), row_bytes, _ptr(sa), _ptr(sb),
                         b_rows_per_scale, _ptr(bias), _ptr(C), N, _ptr(acc), _ptr(absdot),
                         M, N, K)
+    if rc != 0:
+        raise ValueError("bad MX format or B-scale layout")
+    return C, acc, absdot
+
+
+def mx2(fmt_a, fmt_b, A, B, scale_a, scale_b, b_rows_per_scale, K, bias=None):
+    """MX GEMM with a format per operand (MX_E4M3: [rows, K] bytes; MX_E2M1:
+    [rows, K/2] bytes, element k even in the low nibble).  Scales as for mx.
+    Returns (C uint16 [M,N], acc float64 [M,N], absdot float64 [M,N])."""
+    A = _c(A, np.uint8)
+    B = _c(B, np.uint8)
+    M, N = A.shape[0], B.shape[0]
+    row_a = K if fmt_a == MX_E4M3 else K // 2
+    row_b = K if fmt_b == MX_E4M3 else K // 2
+    assert A.shape[1] == row_a and B.shape[1] == row_b and K % 32 == 0
+    sa = _c(scale_a, np.uint8)
+    sb = _c(scale_b, np.uint8)
+    assert sa.shape == (M, K // 32)
+    assert sb.shape == ((N + b_rows_per_scale - 1) // b_rows_per_scale, K // 32)
+    bias = _c(bias, np.uint16)
+    C = np.empty((M, N), np.uint16)
+    acc = np.empty((M, N), np.float64)
+    absdot = np.empty((M, N), np.float64)
+    rc = _load().orc_mx2(fmt_a, fmt_b, _ptr(A), row_a, _ptr(B), row_b, _ptr(sa), _ptr(sb),
+                         b_rows_per_scale, _ptr(bias), _ptr(C), N, _ptr(acc), _ptr(absdot), M, N, K)
     if rc != 0:
         raise ValueError("bad MX format or B-scale layout")
     return C, acc, absdot

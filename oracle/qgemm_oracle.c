@@ -260,6 +260,71 @@ int orc_mx(int fmt, const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb
     return 0;
 }
 
+/* MX GEMM with its own element format per operand: fmt_a for A, fmt_b for B
+ * (0 = e4m3, one byte per element; 1 = e2m1, two per byte as in orc_mx).  The
+ * MX scale rule of "perf(gemm-ar): mxfp8 with row-major scales staged through
+ * LDS" (ROCm/mori PR #806, What) and "[fp4_gemm_4wave] MXFP4 GEMM perf
+ * optimize" (ROCm/FlyDSL PR #990) applies to each operand unchanged: one ue8m0
+ * scale per 32 elements along K, A scales [M, K/32], B scales [N, K/32] or
+ * [ceil(N/32), K/32].  With fmt_a == fmt_b this is orc_mx.  Each product
+ * A~ B~ is exact in double; the sum is exact under the same bound as orc_mx
+ * (an e4m3 x e2m1 product is a multiple of 2^-10 below 2^11.4).
+ * Returns 0, or -1 for an unknown format / b_rows_per_scale. */
+int orc_mx2(int fmt_a, int fmt_b, const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+            const uint8_t *scale_a, const uint8_t *scale_b, int b_rows_per_scale,
+            const uint16_t *bias, uint16_t *C, int64_t ldc, double *acc, double *absdot,
+            int64_t M, int64_t N, int64_t K)
+{
+    if ((fmt_a != 0 && fmt_a != 1) || (fmt_b != 0 && fmt_b != 1) ||
+        (b_rows_per_scale != 1 && b_rows_per_scale != 32))
+        return -1;
+    const int64_t KB = K / 32;
+    double lut8[256], lut4[16], lut_s[256];
+    for (int c = 0; c < 256; ++c) {
+        lut8[c] = orc_dec_e4m3((uint8_t)c);
+        lut_s[c] = orc_dec_ue8m0((uint8_t)c);
+    }
+    for (int c = 0; c < 16; ++c)
+        lut4[c] = orc_dec_e2m1((uint8_t)c);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            const uint8_t *sarow = scale_a + m * KB;
+            const uint8_t *sbrow = scale_b + (n / b_rows_per_scale) * KB;
+            double s = 0.0, t = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double a, b;
+                if (fmt_a == 0) {
+                    a = lut8[A[m * lda + k]];
+                } else {
+                    const uint8_t ab = A[m * lda + k / 2];
+                    a = lut4[(k & 1) ? (ab >> 4) : (ab & 15)];
+                }
+                if (fmt_b == 0) {
+                    b = lut8[B[n * ldb + k]];
+                } else {
+                    const uint8_t bb = B[n * ldb + k / 2];
+                    b = lut4[(k & 1) ? (bb >> 4) : (bb & 15)];
+                }
+                a *= lut_s[sarow[k / 32]];
+                b *= lut_s[sbrow[k / 32]];
+                const double p = a * b;
+                s += p;
+                t += fabs(p);
+            }
+            if (acc)
+                acc[m * N + n] = s;
+            if (absdot)
+                absdot[m * N + n] = t;
+            float f = (float)s;
+            if (bias)
+                f = f + orc_bf16_to_f32(bias[n]);
+            C[m * ldc + n] = orc_bf16_rne(f);
+        }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------- FP8 blockscale */
 
 /* FP8 e4m3 GEMM with block-wise fp32 scales: the "blockscale" variant that
