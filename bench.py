@@ -7,7 +7,8 @@ tile schedule, HBM->LDS staging, MFMA K loop, fused scale/bias epilogue) on
 one batch of seeded synthetic inputs already resident in HBM.  The default
 workload is the INT8 rowwise projection M=30000 N=21504 K=5376 with bias;
 --workload picks another (i8_small, f8_ptpc, mxfp8, mxfp4, i8_qkv, and
-f8_block: FP8 with fp32 scales per 128-element K block, 16384x7168x2048).
+f8_block: FP8 with fp32 scales per 128-element K block, 16384x7168x2048;
+mx_a8w4: MX e4m3 A x e2m1 B, 8192^3).
 
 Prints one JSON line: effective TOPS/TFLOPS = 2MNK / t, the roofline of the
 kernel (achieved over the dense MFMA peak of its dtype, from HIP events on
@@ -28,13 +29,15 @@ sys.path.insert(0, ROOT)
 
 METRIC = "effective TFLOPS/TOPS (2MNK/t) per dtype; % of MI355X dense MFMA peak"
 # MI355X dense matrix-core peaks (TOPS / TFLOPS) and HBM bandwidth (GB/s)
-PEAK = {"i8": 5000.0, "f8": 5000.0, "f8b": 5000.0, "e4m3": 5000.0, "e2m1": 10100.0}
+# (e4m3 x e2m1 MX runs at the e4m3 rate: the scaled MFMA takes 64 cycles when
+# either operand is 8-bit)
+PEAK = {"i8": 5000.0, "f8": 5000.0, "f8b": 5000.0, "e4m3": 5000.0, "e2m1": 10100.0, "e4m3/e2m1": 5000.0}
 HBM_GBPS = 8000.0
 # The pages' number for the INT8 30000x21504x5376 workload: 209.9 TOPS, on a
 # different GPU (RX 9070 XT); context only.
 PAGES_I8_QKV_TOPS = 209.9
 # Rotating input sets so operands are not served from the 256 MB MALL.
-ROT = {"i8_small": 1, "f8_ptpc": 8, "mxfp8": 2, "mxfp4": 3, "i8_qkv": 2, "f8_block": 2}
+ROT = {"i8_small": 1, "f8_ptpc": 8, "mxfp8": 2, "mxfp4": 3, "i8_qkv": 2, "f8_block": 2, "mx_a8w4": 3}
 
 
 def log(*a):
@@ -65,8 +68,8 @@ class Launcher:
         self.args = []
         for s in sets:
             bias = None if s["bias"] is None else s["bias"].data_ptr()
-            if prepacked and d["kind"] == "f8b":
-                raise SystemExit("bench.py: the blockscale GEMM has no prepacked entry point")
+            if prepacked and (d["kind"] == "f8b" or "/" in (d["fmt"] or "")):
+                raise SystemExit("bench.py: the blockscale and mixed-format GEMMs have no prepacked entry point")
             if prepacked:
                 # B prepacked once, outside the timed region (the weights are static)
                 pb = q.qgemm_prepack_b(s["B"]).data
@@ -101,6 +104,12 @@ class Launcher:
                      s["scale_a"].data_ptr(), s["scale_b"].data_ptr(), bias, out.data_ptr(),
                      self.ldc, d["M"], N, d["K"], self.stream)
                 self.args.append((self.L.qgemm_f8_blockscale, a))
+            elif "/" in d["fmt"]:
+                fa, fb = (0 if f == "e4m3" else 1 for f in d["fmt"].split("/"))
+                a = (fa, fb, s["A"].data_ptr(), s["A"].stride(0), s["B"].data_ptr(), s["B"].stride(0),
+                     s["scale_a"].data_ptr(), s["scale_b"].data_ptr(), d["b_rows_per_scale"], bias,
+                     out.data_ptr(), self.ldc, d["M"], N, d["K"], self.stream)
+                self.args.append((self.L.qgemm_mx_mixed, a))
             else:
                 fmt = 0 if d["fmt"] == "e4m3" else 1
                 a = (fmt, s["A"].data_ptr(), s["A"].stride(0), s["B"].data_ptr(), s["B"].stride(0),
@@ -146,7 +155,9 @@ def min_bytes(d):
     """Algorithmic HBM bytes of one call: A, B, C and the scale / bias arrays,
     each read or written once."""
     M, N, K = d["M"], d["N"], d["K"]
-    ab = (M + N) * (K // 2 if d.get("fmt") == "e2m1" else K)
+    fmts = (d.get("fmt") or "").split("/")
+    fa, fb = (fmts[0], fmts[-1]) if fmts[0] else (None, None)
+    ab = M * (K // 2 if fa == "e2m1" else K) + N * (K // 2 if fb == "e2m1" else K)
     if d["kind"] == "mx":
         sc = M * (K // 32) + (-(-N // d["b_rows_per_scale"])) * (K // 32)
     elif d["kind"] == "f8b":
@@ -361,7 +372,7 @@ def main():
     out = torch.empty((M, N + (-N) % 8), dtype=torch.bfloat16, device="cuda")[:, :N]
     stream = torch.cuda.current_stream()
     run = Launcher(d0, sets, out, stream.cuda_stream, prepacked=args.prepacked)
-    tile = q.select_tile({"i8": 0, "f8": 1, "e4m3": 2, "e2m1": 3, "f8b": 4}[dtype_of(d0)], M, N, K)
+    tile = q.select_tile({"i8": 0, "f8": 1, "e4m3": 2, "e2m1": 3, "f8b": 4, "e4m3/e2m1": 5}[dtype_of(d0)], M, N, K)
     if args.tile >= 0:
         q.force_tile(args.tile)
         tile = args.tile
@@ -413,7 +424,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": round(value / PAGES_I8_QKV_TOPS, 4) if name == "i8_qkv" and not shape else None,
         "dtype": {"i8": "int8", "f8": "e4m3", "f8b": "e4m3", "e4m3": "mxfp8-e4m3",
-                  "e2m1": "mxfp4-e2m1"}[dtype_of(d0)],
+                  "e2m1": "mxfp4-e2m1", "e4m3/e2m1": "mx-e4m3xe2m1"}[dtype_of(d0)],
         "data": "synthetic",
         "config": {"workload": f"{name} M={M} N={N} K={K}" + (" bias" if d0["bias"] is not None else "")
                    + (" prepacked B" if args.prepacked else ""),

@@ -13,6 +13,7 @@ call raises.
     qgemm_f8_pertoken(A, B, scale_a, scale_b, bias=None, out=None)
     qgemm_f8_blockscale(A, B, scale_a, scale_b, bias=None, out=None)
     qgemm_mx(fmt, A, B, scale_a, scale_b, b_layout, bias=None, out=None, K=None)
+    qgemm_mx_mixed(fmt_a, fmt_b, A, B, scale_a, scale_b, b_layout, bias=None, out=None)
     qgemm_prepack_b(B, row_bytes=None, out=None)          -> PackedB
     qgemm_i8_rowwise_prepacked(A, Bp, scale_a, scale_b, bias=None, out=None)
     qgemm_f8_pertoken_prepacked(A, Bp, scale_a, scale_b, bias=None, out=None)
@@ -45,7 +46,7 @@ QGEMM_MX_BSCALE_1x32 = 1
 QGEMM_MX_BSCALE_32x32 = 32
 
 # Every symbol include/qgemm.h declares.
-EXPORTS = ("qgemm_i8_rowwise", "qgemm_i8_acc_i32", "qgemm_f8_pertoken", "qgemm_f8_blockscale", "qgemm_mx",
+EXPORTS = ("qgemm_i8_rowwise", "qgemm_i8_acc_i32", "qgemm_f8_pertoken", "qgemm_f8_blockscale", "qgemm_mx", "qgemm_mx_mixed",
            "qgemm_prepacked_b_bytes", "qgemm_prepack_b", "qgemm_i8_rowwise_prepacked",
            "qgemm_f8_pertoken_prepacked", "qgemm_mx_prepacked",
            "qgemm_quant_f8_pertoken", "qgemm_quant_mx",
@@ -78,6 +79,9 @@ def lib():
     L.qgemm_mx.restype = st
     L.qgemm_mx.argtypes = [ctypes.c_int, _P, _I64, _P, _I64, _P, _P, ctypes.c_int, _P, _P, _I64,
                            _I64, _I64, _I64, _P]
+    L.qgemm_mx_mixed.restype = st
+    L.qgemm_mx_mixed.argtypes = [ctypes.c_int, ctypes.c_int, _P, _I64, _P, _I64, _P, _P, ctypes.c_int, _P, _P,
+                                 _I64, _I64, _I64, _I64, _P]
     L.qgemm_prepacked_b_bytes.restype = _I64
     L.qgemm_prepacked_b_bytes.argtypes = [_I64, _I64]
     L.qgemm_prepack_b.restype = st
@@ -345,6 +349,41 @@ def qgemm_mx(fmt, A, B, scale_a, scale_b, b_layout, bias=None, out=None, stream=
         _check(lib().qgemm_mx(fmt, _ptr(A), lda, _ptr(B), ldb, _ptr(sa), _ptr(sb), b_layout,
                               _ptr(bias), _ptr(out), _ldc(out, N), M, N, K,
                               _stream(A.device, stream)))
+    return out
+
+
+def qgemm_mx_mixed(fmt_a, fmt_b, A, B, scale_a, scale_b, b_layout, bias=None, out=None, stream=None):
+    """MX GEMM with a format per operand -> bf16 [M, N] (e4m3 A with e2m1 B,
+    or equal formats).  A [M, K] (e4m3) or [M, K/2] (e2m1) bytes, B likewise;
+    scales as for qgemm_mx."""
+    torch = _torch()
+
+    def dts(fmt):
+        return (torch.uint8, torch.float8_e4m3fn) if fmt == QGEMM_MX_E4M3 else (torch.uint8,)
+    lda = _operand(A, "A", dts(fmt_a))
+    ldb = _operand(B, "B", dts(fmt_b))
+    M, N = A.shape[0], B.shape[0]
+    K = A.shape[1] if fmt_a == QGEMM_MX_E4M3 else 2 * A.shape[1]
+    kb = B.shape[1] if fmt_b == QGEMM_MX_E4M3 else 2 * B.shape[1]
+    if kb != K:
+        raise ValueError(f"A holds K={K} elements per row but B holds {kb}")
+    sdt = (torch.uint8,) + ((torch.float8_e8m0fnu,) if hasattr(torch, "float8_e8m0fnu") else ())
+    brows = -(-N // b_layout) if b_layout in (1, 32) else N
+    if scale_a is None or tuple(scale_a.shape) != (M, K // 32):
+        raise ValueError(f"scale_a must be [{M}, {K // 32}]")
+    if scale_b is None or tuple(scale_b.shape) != (brows, K // 32):
+        raise ValueError(f"scale_b must be [{brows}, {K // 32}]")
+    sa = _vector(scale_a.reshape(-1) if scale_a.is_contiguous() else scale_a, "scale_a",
+                 M * (K // 32), sdt)
+    sb = _vector(scale_b.reshape(-1) if scale_b.is_contiguous() else scale_b, "scale_b",
+                 brows * (K // 32), sdt)
+    bias = _bias(bias, N)
+    _same_device(A.device, B, sa, sb, bias)
+    out = _out(out, M, N, A.device, torch.bfloat16)
+    with torch.cuda.device(A.device):
+        _check(lib().qgemm_mx_mixed(fmt_a, fmt_b, _ptr(A), lda, _ptr(B), ldb, _ptr(sa), _ptr(sb), b_layout,
+                                    _ptr(bias), _ptr(out), _ldc(out, N), M, N, K,
+                                    _stream(A.device, stream)))
     return out
 
 

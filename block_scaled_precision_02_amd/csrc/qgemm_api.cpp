@@ -313,6 +313,18 @@ int pick_tile_packed(int path, Shape s, int64_t kbytes, bool bf16_out)
 // rows): one MI355X, 16384x7168x2048 0.302 ms vs 0.310 ms.
 constexpr int64_t F8B_K_MULTIPLE = 512;
 
+// Mixed MX (e4m3 A, e2m1 B) runs in the LDS-fetch kernel: 256x256 (tile 5,
+// or 4 when forced) or 128x128 (tile 7) -- the table's 192x192 choice and
+// small M take tile 7.
+int pick_tile_mx84(Shape s)
+{
+    if (g_forced_tile == DMA_TILE || g_forced_tile == DMA8_TILE || g_forced_tile == DMA128_TILE)
+        return g_forced_tile;
+    if (s.M <= SKINNY_MAX_M_MX)
+        return DMA128_TILE;
+    return select_tile_impl(2, s.M, s.N) == 0 ? DMA8_TILE : DMA128_TILE;
+}
+
 int pick_tile_f8b(int64_t M, int64_t N)
 {
     if (g_forced_tile == F8B256_TILE || g_forced_tile == DMA128_TILE)
@@ -342,8 +354,15 @@ const char *qgemm_last_error(void) { return g_last_error.c_str(); }
 
 int qgemm_select_tile(int path, int64_t M, int64_t N, int64_t K)
 {
-    if (path < 0 || path > 4)
+    if (path < 0 || path > 5)
         return -1;
+    if (path == 5) {   // MX e4m3 A x e2m1 B
+        const int prev = g_forced_tile;
+        g_forced_tile = -1;
+        const int t = pick_tile_mx84(Shape{M, N, K});
+        g_forced_tile = prev;
+        return t;
+    }
     if (path == 4) {
         const int prev = g_forced_tile;
         g_forced_tile = -1;
@@ -538,6 +557,48 @@ static qgemm_status mx_common(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes
     if (fmt == QGEMM_MX_E4M3)
         return finish(launch_mx8(tile, bias != nullptr, brows, svec, p, (hipStream_t)stream));
     return finish(launch_mx4(tile, bias != nullptr, brows, svec, p, (hipStream_t)stream));
+}
+
+qgemm_status qgemm_mx_mixed(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *A, int64_t lda_bytes, const void *B,
+                            int64_t ldb_bytes, const uint8_t *scale_a, const uint8_t *scale_b,
+                            qgemm_mx_bscale b_layout, const uint16_t *bias, uint16_t *C, int64_t ldc, int64_t M,
+                            int64_t N, int64_t K, void *stream)
+{
+    const bool known_a = fmt_a == QGEMM_MX_E4M3 || fmt_a == QGEMM_MX_E2M1;
+    const bool known_b = fmt_b == QGEMM_MX_E4M3 || fmt_b == QGEMM_MX_E2M1;
+    if (!known_a || !known_b)
+        return fail(QGEMM_ERR_BAD_FORMAT, "unknown MX element format %d / %d", (int)fmt_a, (int)fmt_b);
+    if (fmt_a == fmt_b)
+        return mx_common(fmt_a, A, lda_bytes, B, ldb_bytes, scale_a, scale_b, b_layout, bias, C, ldc, M, N, K, stream,
+                         false);
+    if (fmt_a != QGEMM_MX_E4M3)
+        return fail(QGEMM_ERR_BAD_FORMAT, "e2m1 A with e4m3 B is not supported (e4m3 A with e2m1 B is)");
+    if (b_layout != QGEMM_MX_BSCALE_1x32 && b_layout != QGEMM_MX_BSCALE_32x32)
+        return fail(QGEMM_ERR_BAD_FORMAT, "unknown B-scale layout %d", (int)b_layout);
+    const Shape s{M, N, K};
+    TRY(check_shape(s, false));
+    if (K % 512)
+        return fail(QGEMM_ERR_BAD_SHAPE, "K=%lld: e4m3 x e2m1 needs K a multiple of 512", (long long)K);
+    if (M == 0 || N == 0)
+        return QGEMM_OK;
+    TRY(check_operand("A", A, lda_bytes, K));
+    TRY(check_operand("B", B, ldb_bytes, K / 2));
+    if (!scale_a)
+        return fail(QGEMM_ERR_NULL_POINTER, "scale_a is NULL");
+    if (!scale_b)
+        return fail(QGEMM_ERR_NULL_POINTER, "scale_b is NULL");
+    if (!aligned(scale_a, 16) || !aligned(scale_b, 16))
+        return fail(QGEMM_ERR_BAD_LAYOUT, "e4m3 x e2m1 scale arrays must be 16-byte aligned");
+    TRY(check_bias(bias));
+    TRY(check_output(C, ldc, N, 2));
+    TRY(check_device());
+    const int tile = pick_tile_mx84(s);
+    Params p = base_params(A, lda_bytes, B, ldb_bytes, C, ldc, s, K, tile);   // kbytes: A's row
+    TRY(check_grid(p));
+    p.mx_sa = scale_a;
+    p.mx_sb = scale_b;
+    p.bias = bias;
+    return finish(launch_mx84(tile, bias != nullptr, (int)b_layout, p, (hipStream_t)stream));
 }
 
 qgemm_status qgemm_mx(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const void *B, int64_t ldb_bytes,

@@ -26,6 +26,13 @@
 //    block's second stage each lane folds it into the total with
 //    fma(partial, sa[m, kb] * sb[n/128, kb], total) (a lane's 32x32 result
 //    tile has one row m and lies inside one 128-column block).
+//  * Mixed MX, e4m3 A with e2m1 B: a stage is still 64 K elements, which are
+//    64 bytes of an A row and 32 bytes of a B row.  B stages hold rows of 32
+//    bytes (chunk c of row r at slot c ^ ((r >> 3) & 1): 16 lanes on 16 rows
+//    at one chunk cover 16 slots of 256 bytes of banks); a B fetch covers 32
+//    rows.  Lane half h's 16 bytes of a B row are the instruction's K block h
+//    (32 e2m1 elements, scale of lane half h), as its e4m3 A fragment's chunks
+//    h and 2+h are; both operands' scales are staged as for e4m3 MX.
 //  * A 16-byte chunk c of staged row r sits at slot c ^ ((r >> 2) & 3) of its
 //    64-byte row, so a fragment read (16 lanes on 16 consecutive rows at one
 //    logical chunk) covers 16 different 16-byte slots of 256 bytes of banks.
@@ -76,6 +83,15 @@ template <> struct DmaTraits<PATH_F8> { static constexpr int NSUB = 1; };   // c
 template <> struct DmaTraits<PATH_MX8> { static constexpr int NSUB = 1; };  // chunks h, 2+h
 template <> struct DmaTraits<PATH_MX4> { static constexpr int NSUB = 2; };  // chunk 2h+S
 template <> struct DmaTraits<PATH_F8B> { static constexpr int NSUB = 1; };  // chunks h, 2+h
+template <> struct DmaTraits<PATH_MX84> { static constexpr int NSUB = 1; }; // A chunks h, 2+h; B chunk h of 32 B
+
+// B fragment of the mixed path: lane half h's 16 bytes (32 e2m1 elements) of
+// a 32-byte staged B row; VGPRs 4-7 unused.
+__device__ __forceinline__ i32x8 dma_frag_b32(const uint8_t *tile, int row, int h)
+{
+    const i32x4 lo = *(const i32x4 *)(tile + row * 32 + ((h ^ ((row >> 3) & 1)) << 4));
+    return i32x8{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+}
 
 // Fragment of a 32-row MFMA operand for sub-step S of a 64-byte stage.
 //   int8:  16 bytes, chunk 2S+h (32 elements per sub-step)
@@ -110,12 +126,15 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr int NW = WM * WN;                           // waves
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     constexpr int NSUB = DmaTraits<PATH>::NSUB;
-    constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4);
+    constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4 || PATH == PATH_MX84);
+    constexpr bool B4 = (PATH == PATH_MX84);              // e2m1 B under e4m3 A: 32-byte B stage rows
     constexpr bool BS = (PATH == PATH_F8B);               // blockscale FP8
     constexpr bool SCL = MX || BS;                        // scale chunks staged through LDS
     static_assert(!BS || BROWS == 128, "blockscale B scales cover 128 rows");
     static_assert(BROWS == 1 || (BN % BROWS == 0 || BROWS == 32), "B scale rows must align with the tile");
-    constexpr int STAGE_BYTES = (BM + BN) * DSTAGE;
+    constexpr int BSTAGE = B4 ? DSTAGE / 2 : DSTAGE;     // B bytes per row and stage
+    constexpr int BROWS_PER_FETCH = 1024 / BSTAGE;        // rows one 1 KB B fetch covers
+    constexpr int STAGE_BYTES = BM * DSTAGE + BN * BSTAGE;
     constexpr int OPND_BYTES = DNST * STAGE_BYTES;
     // MX scale chunks: per buffer, 256 rows of A and 256 rows of B (1x32) or
     // 64 (32x32 layout: BN/32 valid rows), 16 bytes each -- what four fetches
@@ -125,9 +144,10 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr int SCL_BUF = (SA_ROWS + SB_ROWS) * 16;
     constexpr int SCL_BYTES = SCL ? 2 * SCL_BUF : 0;
     constexpr int NQ = TM * TN;
-    constexpr int RPF = (PATH == PATH_F8 || PATH == PATH_MX8 || PATH == PATH_F8B) ? 2 : 1;
-    constexpr int NDSR = (TM + TN) * RPF;                 // fragment reads per sub-step
-    constexpr int DMA_A = BM / 16 / NW, DMA_B = BN / 16 / NW; // fetches per wave per stage
+    constexpr int RPF = (PATH == PATH_F8 || PATH == PATH_MX8 || PATH == PATH_F8B || PATH == PATH_MX84) ? 2 : 1;
+    constexpr int RPF_B = B4 ? 1 : RPF;
+    constexpr int NDSR = TM * RPF + TN * RPF_B;           // fragment reads per sub-step
+    constexpr int DMA_A = BM / 16 / NW, DMA_B = BN / BROWS_PER_FETCH / NW; // fetches per wave per stage
     constexpr int NDMA = DMA_A + DMA_B;
     // scale fetches per wave per chunk: 4 waves fetch A and B scale rows,
     // 8 waves split them (waves 0-3 A, 4-7 B)
@@ -136,14 +156,21 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // (region B of the stage 4 back) except for MX, whose region B is busy
     // with scale reads.
     constexpr bool SPLIT = !SCL;
-    static_assert(DMA_A * 16 * NW == BM && DMA_B * 16 * NW == BN, "tile rows must be a multiple of 16 per wave");
+    static_assert(DMA_A * 16 * NW == BM && DMA_B * BROWS_PER_FETCH * NW == BN,
+                  "tile rows must be a whole number of fetches per wave");
     static_assert(BM <= SA_ROWS && (BROWS == 1 ? BN <= SB_ROWS : BN / 32 <= SB_ROWS), "scale rows per buffer");
     using Frag = typename PathTraits<PATH>::Frag;
     using Acc = typename AccT<PATH>::T;
 
     constexpr bool PRM = OUT == OUT_BF16 && (!SCL || BIAS);
-    constexpr int PRM_OFF = OPND_BYTES + SCL_BYTES;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[OPND_BYTES + SCL_BYTES + (PRM ? PRM_BYTES : 0)];
+    // the epilogue's output stash (whole-row stores) reuses the operand and
+    // scale buffers; the mixed path's smaller B stages leave less than the
+    // 256x256 stash needs, so its block is sized up to that
+    constexpr int STASH_NEED = NW * TM * 32 * pow2_at_least(TN * 32 * 2 / 16) * 16;
+    constexpr int BODY = B4 ? (OPND_BYTES + SCL_BYTES > STASH_NEED ? OPND_BYTES + SCL_BYTES : STASH_NEED)
+                            : OPND_BYTES + SCL_BYTES;
+    constexpr int PRM_OFF = BODY;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[BODY + (PRM ? PRM_BYTES : 0)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -164,8 +191,8 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     const int64_t gbytes = (int64_t)16 * p.kbytes;        // one packed group
     const __amdgpu_buffer_rsrc_t rb =
         p.b_packed ? make_rsrc(p.B + (int64_t)(n0 / 16) * gbytes, (uint32_t)(((rows_b + 15) / 16) * gbytes))
-                   : make_rsrc(p.B + (int64_t)n0 * p.ldb, (uint32_t)((rows_b - 1) * p.ldb + p.kbytes));
-    const unsigned bstep = p.b_packed ? 1024u : (unsigned)DSTAGE;   // B bytes per stage along K
+                   : make_rsrc(p.B + (int64_t)n0 * p.ldb, (uint32_t)((rows_b - 1) * p.ldb + (B4 ? p.kbytes / 2 : p.kbytes)));
+    const unsigned bstep = p.b_packed ? 1024u : (unsigned)BSTAGE;   // B bytes per stage along K
 
     // Fetch map: wave w's j-th A fetch covers rows 16*(4w+j) .. +15; lane i
     // takes row +i/4 and the chunk that belongs in slot i%4.  A row past M / N
@@ -183,10 +210,16 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         const int g = DMA_B * wave + j;                   // 16-row group in the tile
         const int r = 16 * g + (lane >> 2);
         const int c = (lane & 3) ^ ((r >> 2) & 3);
-        if (p.b_packed)
+        if constexpr (B4) {
+            // 32 rows of 32 bytes: lane i takes row i/2, the chunk of slot i%2
+            const int r4 = BROWS_PER_FETCH * g + (lane >> 1);
+            const int c4 = (lane & 1) ^ ((r4 >> 3) & 1);
+            b_off[j] = r4 < rows_b ? (unsigned)(r4 * p.ldb + 16 * c4) : OOB;
+        } else if (p.b_packed) {
             b_off[j] = 16 * g < rows_b ? (unsigned)(g * gbytes + 16 * lane) : OOB;
-        else
+        } else {
             b_off[j] = r < rows_b ? (unsigned)(r * p.ldb + 16 * c) : OOB;
+        }
     }
     // Stage t goes to slot t % 4, its A rows (part 0) and B rows (part 1)
     // fetched separately.
@@ -200,7 +233,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         } else {
 #pragma unroll
             for (int j = 0; j < DMA_B; ++j)
-                dma16(rb, b_off[j] + kbb, slot + BM * DSTAGE + (DMA_B * wave + j) * 16 * DSTAGE);
+                dma16(rb, b_off[j] + kbb, slot + BM * DSTAGE + (DMA_B * wave + j) * 1024);
         }
     };
 
@@ -264,8 +297,12 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         // in the order the serpentine MFMA sequence consumes them
         fa[SET][0] = dma_frag<PATH, S>(ta, arow, h);
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-            fb[SET][j] = dma_frag<PATH, S>(tb, brow + 32 * j, h);
+        for (int j = 0; j < TN; ++j) {
+            if constexpr (B4)
+                fb[SET][j] = dma_frag_b32(tb, brow + 32 * j, h);
+            else
+                fb[SET][j] = dma_frag<PATH, S>(tb, brow + 32 * j, h);
+        }
 #pragma unroll
         for (int i = 1; i < TM; ++i)
             fa[SET][i] = dma_frag<PATH, S>(ta, arow + 32 * i, h);
@@ -481,8 +518,8 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     }
     wait_vmcnt<0>();   // nothing may still be landing in LDS once it holds the output
 
-    store_tile<PATH, WM, WN, TM, TN, BIAS, OUT, OPND_BYTES, PRM>(p, acc, &lds[0], &lds[PRM_OFF], m0, n0, rows_a,
-                                                                 rows_b);
+    store_tile<PATH, WM, WN, TM, TN, BIAS, OUT, (B4 ? BODY : OPND_BYTES), PRM>(p, acc, &lds[0], &lds[PRM_OFF], m0, n0,
+                                                                            rows_a, rows_b);
 }
 
 }  // namespace qgemm

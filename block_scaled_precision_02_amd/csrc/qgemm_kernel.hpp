@@ -50,7 +50,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // PATH_F8B: e4m3 with fp32 scales per 128-element K block (A per row, B per
 // 128 rows), applied inside the K loop; LDS-fetch kernel only.
-enum Path { PATH_I8 = 0, PATH_F8 = 1, PATH_MX8 = 2, PATH_MX4 = 3, PATH_F8B = 4 };
+// PATH_MX84: MX with e4m3 A and e2m1 B (ue8m0 scales per 32 K elements on
+// both); LDS-fetch kernel only.
+enum Path { PATH_I8 = 0, PATH_F8 = 1, PATH_MX8 = 2, PATH_MX4 = 3, PATH_F8B = 4, PATH_MX84 = 5 };
 enum OutKind { OUT_BF16 = 0, OUT_I32 = 1 };
 
 // Kernel arguments (one struct, passed by value).
@@ -142,6 +144,7 @@ template <> struct PathTraits<PATH_F8> { static constexpr int NSUB = 2; using Fr
 template <> struct PathTraits<PATH_MX8> { static constexpr int NSUB = 2; using Frag = i32x8; };
 template <> struct PathTraits<PATH_MX4> { static constexpr int NSUB = 4; using Frag = i32x8; };
 template <> struct PathTraits<PATH_F8B> { static constexpr int NSUB = 2; using Frag = i32x8; };
+template <> struct PathTraits<PATH_MX84> { static constexpr int NSUB = 2; using Frag = i32x8; };
 
 // Fragment of one 32-row MFMA operand for K sub-step S, read from a staged
 // tile.  Lane (h = lane/32, row = lane%32):
@@ -189,6 +192,9 @@ __device__ __forceinline__ void mfma(typename AccT<PATH>::T &acc,
         acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, acc, 0, 0, 0, 0, 0, 0);
     } else if constexpr (PATH == PATH_MX8) {
         acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, acc, 0, 0, S, (int)sc_b, S, (int)sc_a);
+    } else if constexpr (PATH == PATH_MX84) {
+        // first operand (B) e2m1: cbsz = 4; second (A) e4m3: blgp = 0
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, acc, 4, 0, S, (int)sc_b, S, (int)sc_a);
     } else {
         acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, acc, 4, 4, S, (int)sc_b, S, (int)sc_a);
     }
@@ -266,7 +272,7 @@ __device__ __forceinline__ void store_tile(const Params &p, Acc (&acc)[TM][TN], 
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     // MX and blockscale apply their scales inside the K loop: the epilogue
     // only adds the bias and rounds
-    constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4 || PATH == PATH_F8B);
+    constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4 || PATH == PATH_F8B || PATH == PATH_MX84);
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;

@@ -157,6 +157,21 @@ qgemm_status qgemm_mx(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const 
                       qgemm_mx_bscale b_layout, const uint16_t *bias, uint16_t *C, int64_t ldc,
                       int64_t M, int64_t N, int64_t K, void *stream);
 
+/* MX GEMM with a format per operand: fmt_a for A, fmt_b for B, otherwise as
+ * qgemm_mx (one ue8m0 scale per 32 elements along K for each operand, the
+ * scale layouts of qgemm_mx).  Equal formats are qgemm_mx.  Of the mixed
+ * pairs, e4m3 A (activations) with e2m1 B (weights) is supported:
+ *   A        [M, K] e4m3fn codes, row stride lda_bytes (>= K)
+ *   B        [N, K] e2m1, two per byte (even k in the low nibble), row stride
+ *            ldb_bytes (>= K/2)
+ * It needs K a multiple of 512 (QGEMM_ERR_BAD_SHAPE) and 16-byte aligned
+ * scale arrays (QGEMM_ERR_BAD_LAYOUT); e2m1 A with e4m3 B returns
+ * QGEMM_ERR_BAD_FORMAT.  Numerics as qgemm_mx. */
+qgemm_status qgemm_mx_mixed(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *A, int64_t lda_bytes,
+                            const void *B, int64_t ldb_bytes, const uint8_t *scale_a, const uint8_t *scale_b,
+                            qgemm_mx_bscale b_layout, const uint16_t *bias, uint16_t *C, int64_t ldc,
+                            int64_t M, int64_t N, int64_t K, void *stream);
+
 /* Prepacked B.  B (the weights, static across calls) can be rewritten once
  * into the order the LDS-fetch kernel's B stages take in LDS, so that each
  * of its fetches reads one contiguous kilobyte instead of 16 rows x 64 bytes
@@ -253,7 +268,8 @@ const char *qgemm_status_string(qgemm_status status);
 /* Tile variant the host-side table picks for a problem (pure host logic, no
  * HIP call; for MX, assuming 16-byte-aligned scale arrays).  path: 0 int8,
  * 1 fp8, 2 MX e4m3, 3 MX e2m1, 4 fp8 blockscale (tile 10 when its grid of
- * 256x128 tiles fills the 256 CUs at least once, else tile 7).  Returns the
+ * 256x128 tiles fills the 256 CUs at least once, else tile 7), 5 MX e4m3 A
+ * with e2m1 B (tile 5 where the table picks 256x256, else 7).  Returns the
  * tile id, or -1 for a bad path:
  *   0: 256x256, 4 waves, operands staged through registers
  *   1: 128x128    2: 256x256 with 8 waves, staged through registers

@@ -76,6 +76,10 @@ def gpu_run(d, out=None, stream=None):
     if d["kind"] == "f8b":
         return q.qgemm_f8_blockscale(dev(d["A"]), dev(d["B"]), dev(d["scale_a"]),
                                      dev(d["scale_b"]), bias, out=out, stream=stream)
+    if "/" in d["fmt"]:
+        fa, fb = (q.QGEMM_MX_E4M3 if f == "e4m3" else q.QGEMM_MX_E2M1 for f in d["fmt"].split("/"))
+        return q.qgemm_mx_mixed(fa, fb, dev(d["A"]), dev(d["B"]), dev(d["scale_a"]), dev(d["scale_b"]),
+                                d["b_rows_per_scale"], bias, out=out, stream=stream)
     fmt = q.QGEMM_MX_E4M3 if d["fmt"] == "e4m3" else q.QGEMM_MX_E2M1
     return q.qgemm_mx(fmt, dev(d["A"]), dev(d["B"]), dev(d["scale_a"]), dev(d["scale_b"]),
                       d["b_rows_per_scale"], bias, out=out, stream=stream)
@@ -106,8 +110,12 @@ def oracle_run(d, rows=None, cols=None):
     if d["kind"] == "f8b":
         C, _, absdot = oracle.f8_blockscale(A, B, sa, sb, bias)
         return C, absdot, None
-    fmt = oracle.MX_E4M3 if d["fmt"] == "e4m3" else oracle.MX_E2M1
     brows = d["b_rows_per_scale"] if cols is None else 1
+    if "/" in d["fmt"]:
+        fa, fb = (oracle.MX_E4M3 if f == "e4m3" else oracle.MX_E2M1 for f in d["fmt"].split("/"))
+        C, _, absdot = oracle.mx2(fa, fb, A, B, sa, sb, brows, d["K"], bias)
+        return C, absdot, None
+    fmt = oracle.MX_E4M3 if d["fmt"] == "e4m3" else oracle.MX_E2M1
     C, _, absdot = oracle.mx(fmt, A, B, sa, sb, brows, d["K"], bias)
     return C, absdot, None
 

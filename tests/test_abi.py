@@ -297,3 +297,32 @@ def test_f8_blockscale_checks_pass_before_the_device_check(monkeypatch):
     assert q.select_tile(4, 16384, 7168, 2048) == 10
     assert q.select_tile(4, 256, 7168, 2048) == 7          # 56 tiles of 256x128: too few for the chip
     assert q.select_tile(4, 1024, 8192, 2048) == 10         # 4 x 64 = 256 tiles
+
+
+def mx2(fa=0, fb=1, A=FAKE, lda=512, B=FAKE2, ldb=256, sa=FAKE3, sb=FAKE3, layout=1, bias=None, C=FAKE,
+        ldc=64, M=64, N=64, K=512):
+    return q.lib().qgemm_mx_mixed(fa, fb, A, lda, B, ldb, sa, sb, layout, bias, C, ldc, M, N, K, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(fa=2), q.QGEMM_ERR_BAD_FORMAT),
+    (dict(fb=7), q.QGEMM_ERR_BAD_FORMAT),
+    (dict(fa=1, fb=0), q.QGEMM_ERR_BAD_FORMAT),                 # e2m1 A with e4m3 B
+    (dict(layout=16), q.QGEMM_ERR_BAD_FORMAT),
+    (dict(K=640, lda=640, ldb=320), q.QGEMM_ERR_BAD_SHAPE),      # K % 512
+    (dict(A=None), q.QGEMM_ERR_NULL_POINTER),
+    (dict(sb=None), q.QGEMM_ERR_NULL_POINTER),
+    (dict(ldb=128), q.QGEMM_ERR_BAD_LAYOUT),                     # e2m1 B row is K/2 = 256 bytes
+    (dict(lda=256), q.QGEMM_ERR_BAD_LAYOUT),                     # e4m3 A row is K = 512 bytes
+    (dict(sa=FAKE3 + 4), q.QGEMM_ERR_BAD_LAYOUT),
+])
+def test_mx_mixed_rejects(kw, status):
+    assert mx2(**kw) == status
+
+
+def test_mx_mixed_checks_pass_before_the_device_check(monkeypatch):
+    monkeypatch.setenv("QGEMM_FAKE_ARCH", "gfx1201")
+    assert mx2() == q.QGEMM_ERR_UNSUPPORTED_DEVICE
+    assert mx2(M=0) == q.QGEMM_OK
+    assert q.select_tile(5, 8192, 8192, 8192) == 5
+    assert q.select_tile(5, 16, 8192, 8192) == 7
