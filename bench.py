@@ -335,7 +335,7 @@ def main():
                          "WRITE_SIZE runs under DIR (no GPU needed)")
     args = ap.parse_args()
     if args.traffic_from:
-        print(json.dumps(write_traffic(args.traffic_from, ["i8_qkv", "mxfp4", "f8_block"])))
+        print(json.dumps(write_traffic(args.traffic_from, ["i8_qkv", "mxfp4", "f8_block", "mx_a8w4"])))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this GEMM library has no multi-GPU path "
