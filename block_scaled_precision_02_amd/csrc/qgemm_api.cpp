@@ -245,14 +245,18 @@ qgemm_status finish(hipError_t e)
 }
 
 // The LDS-fetch kernels (tiles 4-7) run tiles whose K is a whole number of
-// their 4 x 64-byte stages and, for MX, whose scale rows are whole 16-byte
-// chunks (the caller's scale arrays then also load in aligned words).
+// their 4 x 64-byte stages.  For MX, a 4-stage round reads 16 bytes of each
+// scale row (e2m1) or the first 8 bytes of a 16-byte chunk (e4m3): e2m1 scale
+// rows must be whole 16-byte chunks, e4m3 ones whole 8-byte words (K % 256),
+// and the caller's scale arrays aligned to that (svec: the caller's check).
 bool dma_eligible(int path, int64_t kbytes, int64_t K, bool svec)
 {
     if (kbytes % 256)
         return false;
-    if (path >= 2)
+    if (path == 3)
         return svec && (K / 32) % 16 == 0;
+    if (path == 2)
+        return svec && (K / 32) % 8 == 0;
     return true;
 }
 
@@ -307,11 +311,11 @@ int pick_tile_packed(int path, Shape s, int64_t kbytes, bool bf16_out)
 }
 
 // Blockscale FP8 runs in the LDS-fetch kernel: K must be a whole number of
-// its 4-stage rounds with scale rows (K/32 bytes) of whole 16-byte chunks,
-// i.e. K % 512 == 0.  The 256x128 tile (one workgroup per CU) when its grid
+// its 4-stage rounds (K % 256 == 0), each of which reads 8 bytes (two K
+// blocks) of every scale row.  The 256x128 tile (one workgroup per CU) when its grid
 // fills the chip at least once, else the 128x128 tile (two per CU, half the
 // rows): one MI355X, 16384x7168x2048 0.302 ms vs 0.310 ms.
-constexpr int64_t F8B_K_MULTIPLE = 512;
+constexpr int64_t F8B_K_MULTIPLE = 256;
 
 // Mixed MX (e4m3 A, e2m1 B) runs in the LDS-fetch kernel: 256x256 (tile 5,
 // or 4 when forced) or 128x128 (tile 7) -- the table's 192x192 choice and
@@ -494,8 +498,8 @@ qgemm_status qgemm_f8_blockscale(const uint8_t *A, int64_t lda, const uint8_t *B
     TRY(check_operand("A", A, lda, K));
     TRY(check_operand("B", B, ldb, K));
     TRY(check_fp32_scales(scale_a, scale_b));
-    if (!aligned(scale_a, 16) || !aligned(scale_b, 16))
-        return fail(QGEMM_ERR_BAD_LAYOUT, "blockscale scale arrays must be 16-byte aligned");
+    if (!aligned(scale_a, 8) || !aligned(scale_b, 8))
+        return fail(QGEMM_ERR_BAD_LAYOUT, "blockscale scale arrays must be 8-byte aligned");
     TRY(check_bias(bias));
     TRY(check_output(C, ldc, N, 2));
     TRY(check_device());
@@ -537,14 +541,16 @@ static qgemm_status mx_common(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes
     const int path = (fmt == QGEMM_MX_E4M3) ? 2 : 3;
     // Scale words load whole when every lane's bytes of a K step are aligned:
     // e2m1 takes 4 bytes per lane half (K/32 % 4 == 0), e4m3 takes 2 (K/32 even),
-    // and the scale arrays themselves start aligned (16 bytes covers the
-    // LDS-fetch kernel's 16-byte scale chunks).
+    // and the scale arrays themselves start aligned.  The LDS-fetch kernel
+    // reads 16 (e2m1) or 8 (e4m3) bytes of each scale row per round: the
+    // arrays must be aligned to that.
     const int wb = (fmt == QGEMM_MX_E2M1) ? 4 : 2;
     const bool svec = ((K / 32) % wb == 0) && aligned(scale_a, wb) && aligned(scale_b, wb);
-    const bool svec16 = svec && aligned(scale_a, 16) && aligned(scale_b, 16);
+    const unsigned chunk_align = (fmt == QGEMM_MX_E2M1) ? 16 : 8;
+    const bool svec16 = svec && aligned(scale_a, chunk_align) && aligned(scale_b, chunk_align);
     if (packed && !dma_eligible(path, row_bytes, K, svec16))
-        return fail(QGEMM_ERR_BAD_LAYOUT, "a prepacked MX B needs K/32 a multiple of 16 and 16-byte aligned scale "
-                                          "arrays");
+        return fail(QGEMM_ERR_BAD_LAYOUT, "a prepacked MX B needs K/32 a multiple of 16 (e2m1) or 8 (e4m3) and scale "
+                                          "arrays aligned to 16 (e2m1) or 8 (e4m3) bytes");
     TRY(check_device());
     const int tile = packed ? pick_tile_packed(path, s, row_bytes, true) : pick_tile(path, s, row_bytes, svec16, true);
     Params p = base_params(A, lda_bytes, B, packed ? row_bytes : ldb_bytes, C, ldc, s, row_bytes, tile);
@@ -577,8 +583,8 @@ qgemm_status qgemm_mx_mixed(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *
         return fail(QGEMM_ERR_BAD_FORMAT, "unknown B-scale layout %d", (int)b_layout);
     const Shape s{M, N, K};
     TRY(check_shape(s, false));
-    if (K % 512)
-        return fail(QGEMM_ERR_BAD_SHAPE, "K=%lld: e4m3 x e2m1 needs K a multiple of 512", (long long)K);
+    if (K % 256)
+        return fail(QGEMM_ERR_BAD_SHAPE, "K=%lld: e4m3 x e2m1 needs K a multiple of 256", (long long)K);
     if (M == 0 || N == 0)
         return QGEMM_OK;
     TRY(check_operand("A", A, lda_bytes, K));
@@ -587,8 +593,8 @@ qgemm_status qgemm_mx_mixed(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *
         return fail(QGEMM_ERR_NULL_POINTER, "scale_a is NULL");
     if (!scale_b)
         return fail(QGEMM_ERR_NULL_POINTER, "scale_b is NULL");
-    if (!aligned(scale_a, 16) || !aligned(scale_b, 16))
-        return fail(QGEMM_ERR_BAD_LAYOUT, "e4m3 x e2m1 scale arrays must be 16-byte aligned");
+    if (!aligned(scale_a, 8) || !aligned(scale_b, 8))
+        return fail(QGEMM_ERR_BAD_LAYOUT, "e4m3 x e2m1 scale arrays must be 8-byte aligned");
     TRY(check_bias(bias));
     TRY(check_output(C, ldc, N, 2));
     TRY(check_device());

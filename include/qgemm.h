@@ -136,8 +136,8 @@ qgemm_status qgemm_f8_pertoken(const uint8_t *A, int64_t lda, const uint8_t *B, 
  * acc = sum_kb scale_a[m,kb] * scale_b[n/128,kb] * P[kb], P[kb] the fp32
  * matrix-core sum of the block's 128 products, each block folded into the
  * fp32 total with one fused multiply-add; then f = acc, [+ bias], bf16
- * round-nearest-even.  K must be a multiple of 512 (QGEMM_ERR_BAD_SHAPE) and
- * both scale arrays 16-byte aligned (QGEMM_ERR_BAD_LAYOUT). */
+ * round-nearest-even.  K must be a multiple of 256 (QGEMM_ERR_BAD_SHAPE) and
+ * both scale arrays 8-byte aligned (QGEMM_ERR_BAD_LAYOUT). */
 qgemm_status qgemm_f8_blockscale(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
                                  const float *scale_a, const float *scale_b, const uint16_t *bias,
                                  uint16_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
@@ -164,7 +164,7 @@ qgemm_status qgemm_mx(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const 
  *   A        [M, K] e4m3fn codes, row stride lda_bytes (>= K)
  *   B        [N, K] e2m1, two per byte (even k in the low nibble), row stride
  *            ldb_bytes (>= K/2)
- * It needs K a multiple of 512 (QGEMM_ERR_BAD_SHAPE) and 16-byte aligned
+ * It needs K a multiple of 256 (QGEMM_ERR_BAD_SHAPE) and 8-byte aligned
  * scale arrays (QGEMM_ERR_BAD_LAYOUT); e2m1 A with e4m3 B returns
  * QGEMM_ERR_BAD_FORMAT.  Numerics as qgemm_mx. */
 qgemm_status qgemm_mx_mixed(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *A, int64_t lda_bytes,
@@ -203,7 +203,8 @@ qgemm_status qgemm_prepack_b(const void *B, int64_t ldb, int64_t N, int64_t row_
  * qgemm_i8_rowwise / qgemm_f8_pertoken / qgemm_mx with Bp in place of (B,
  * ldb); in addition K must give rows of a multiple of 256 bytes
  * (QGEMM_ERR_BAD_SHAPE otherwise) and, for MX, K/32 must be a multiple of 16
- * with 16-byte aligned scale arrays (QGEMM_ERR_BAD_LAYOUT otherwise).  INT8
+ * (e2m1) or 8 (e4m3) with scale arrays aligned to 16 (e2m1) or 8 (e4m3) bytes
+ * (QGEMM_ERR_BAD_LAYOUT otherwise).  INT8
  * results are bit-identical to qgemm_i8_rowwise's; FP8 / MX results equal
  * those of qgemm_*'s LDS-fetch tiles. */
 qgemm_status qgemm_i8_rowwise_prepacked(const int8_t *A, int64_t lda, const void *Bp, const float *scale_a,
@@ -282,7 +283,7 @@ const char *qgemm_status_string(qgemm_status status);
  *   9: 64 rows x 16 columns, 8 waves splitting K (small M)
  *  10: 256 rows x 128 columns, fp8 blockscale only
  * Tiles 4-7 need K bytes a multiple of 256 and MX scale rows a multiple of
- * 16 bytes; where these hold, the table's 256x256 choice runs as tile 5,
+ * 16 (e2m1) or 8 (e4m3) bytes; where these hold, the table's 256x256 choice runs as tile 5,
  * 192x192 as tile 6 and 128x128 as tile 7.  Calls with M <= 64 take tile 8
  * (M <= 16) or 9 (INT8 and FP8 only: MX takes the small-M kernel up to
  * M = 16). */

@@ -246,17 +246,19 @@ def test_prepacked_gemms_reject():
                                         None) == q.QGEMM_ERR_BAD_SHAPE
     assert L.qgemm_f8_pertoken_prepacked(FAKE, 256, None, FAKE3, FAKE3, None, FAKE, 64, 64, 64, 256,
                                          None) == q.QGEMM_ERR_NULL_POINTER
-    # MX e4m3 K = 256: K/32 = 8 is not a multiple of 16
-    assert L.qgemm_mx_prepacked(0, FAKE, 256, FAKE2, FAKE3, FAKE3, 1, None, FAKE, 64, 64, 64, 256,
-                                None) == q.QGEMM_ERR_BAD_LAYOUT
-    # ... and misaligned scale arrays
+    # MX scale arrays must be aligned to the bytes one round reads: 8 (e4m3), 16 (e2m1)
     assert L.qgemm_mx_prepacked(0, FAKE, 512, FAKE2, FAKE3 + 4, FAKE3, 1, None, FAKE, 64, 64, 64, 512,
+                                None) == q.QGEMM_ERR_BAD_LAYOUT
+    assert L.qgemm_mx_prepacked(1, FAKE, 256, FAKE2, FAKE3 + 8, FAKE3, 1, None, FAKE, 64, 64, 64, 512,
                                 None) == q.QGEMM_ERR_BAD_LAYOUT
 
 
 def test_prepacked_gemms_pass_their_checks(monkeypatch):
     monkeypatch.setenv("QGEMM_FAKE_ARCH", "gfx1201")
     L = q.lib()
+    # MX e4m3 at K = 256 (K/32 = 8) with 8-byte aligned scales
+    assert L.qgemm_mx_prepacked(0, FAKE, 256, FAKE2, FAKE3 + 8, FAKE3, 1, None, FAKE, 64, 64, 64, 256,
+                                None) == q.QGEMM_ERR_UNSUPPORTED_DEVICE
     assert L.qgemm_i8_rowwise_prepacked(FAKE, 256, FAKE2, FAKE3, FAKE3, None, FAKE, 64, 64, 64, 256,
                                         None) == q.QGEMM_ERR_UNSUPPORTED_DEVICE
     assert L.qgemm_mx_prepacked(1, FAKE, 256, FAKE2, FAKE3, FAKE3, 32, None, FAKE, 64, 64, 64, 512,
@@ -275,12 +277,12 @@ def f8b(A=FAKE, lda=512, B=FAKE2, ldb=512, sa=FAKE3, sb=FAKE3, bias=None, C=FAKE
     (dict(sb=None), q.QGEMM_ERR_NULL_POINTER),
     (dict(C=None), q.QGEMM_ERR_NULL_POINTER),
     (dict(K=0), q.QGEMM_ERR_BAD_SHAPE),
-    (dict(K=640, lda=640, ldb=640), q.QGEMM_ERR_BAD_SHAPE),     # blockscale needs K % 512 == 0
+    (dict(K=640, lda=640, ldb=640), q.QGEMM_ERR_BAD_SHAPE),     # blockscale needs K % 256 == 0
     (dict(K=128, lda=128, ldb=128), q.QGEMM_ERR_BAD_SHAPE),
     (dict(M=-1), q.QGEMM_ERR_BAD_SHAPE),
     (dict(lda=256), q.QGEMM_ERR_BAD_LAYOUT),
-    (dict(sa=FAKE3 + 4), q.QGEMM_ERR_BAD_LAYOUT),                # scales must be 16-byte aligned
-    (dict(sb=FAKE3 + 8), q.QGEMM_ERR_BAD_LAYOUT),
+    (dict(sa=FAKE3 + 4), q.QGEMM_ERR_BAD_LAYOUT),                # scales must be 8-byte aligned
+    (dict(sb=FAKE3 + 12), q.QGEMM_ERR_BAD_LAYOUT),
     (dict(ldc=60, N=60), q.QGEMM_ERR_BAD_LAYOUT),
     (dict(bias=FAKE3 + 1), q.QGEMM_ERR_BAD_LAYOUT),
 ])
@@ -309,7 +311,7 @@ def mx2(fa=0, fb=1, A=FAKE, lda=512, B=FAKE2, ldb=256, sa=FAKE3, sb=FAKE3, layou
     (dict(fb=7), q.QGEMM_ERR_BAD_FORMAT),
     (dict(fa=1, fb=0), q.QGEMM_ERR_BAD_FORMAT),                 # e2m1 A with e4m3 B
     (dict(layout=16), q.QGEMM_ERR_BAD_FORMAT),
-    (dict(K=640, lda=640, ldb=320), q.QGEMM_ERR_BAD_SHAPE),      # K % 512
+    (dict(K=640, lda=640, ldb=320), q.QGEMM_ERR_BAD_SHAPE),      # K % 256
     (dict(A=None), q.QGEMM_ERR_NULL_POINTER),
     (dict(sb=None), q.QGEMM_ERR_NULL_POINTER),
     (dict(ldb=128), q.QGEMM_ERR_BAD_LAYOUT),                     # e2m1 B row is K/2 = 256 bytes

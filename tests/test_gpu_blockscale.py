@@ -51,7 +51,8 @@ TILES = [7, 10]
 
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("M,N,K", [(256, 256, 512), (17, 33, 512), (300, 520, 1024), (129, 200, 2048),
-                                   (1, 1, 512), (130, 384, 1536)])
+                                   (1, 1, 512), (130, 384, 1536), (260, 300, 256), (200, 136, 768),
+                                   (384, 256, 1792)])
 @pytest.mark.parametrize("bias", [False, True])
 def test_f8b_small(M, N, K, bias, tile):
     q.force_tile(tile)
@@ -133,7 +134,7 @@ def test_f8b_full_workload_sampled(tile):
     _say(f"[parity] full f8_block: worst err/bound {worst:.3g} cos {cos:.8f}")
 
 
-def test_f8b_rejects_k_not_multiple_of_512():
+def test_f8b_rejects_k_not_multiple_of_256():
     A = torch.zeros((4, 640), dtype=torch.uint8, device="cuda")
     sa = torch.ones((4, 5), dtype=torch.float32, device="cuda")
     sb = torch.ones((1, 5), dtype=torch.float32, device="cuda")

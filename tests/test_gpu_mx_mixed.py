@@ -57,7 +57,8 @@ def _check(d, what, out=None):
 
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("brows", [1, 32])
-@pytest.mark.parametrize("M,N,K", [(256, 256, 512), (33, 70, 512), (300, 520, 1024), (1, 1, 512), (257, 300, 1536)])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 512), (33, 70, 512), (300, 520, 1024), (1, 1, 512), (257, 300, 1536),
+                                   (300, 264, 256), (256, 512, 768), (130, 200, 1792)])
 def test_mx84_small(M, N, K, brows, tile):
     q.force_tile(tile)
     _check(_make(M, N, K, brows), f"mx84 brows={brows} tile={tile}")
@@ -101,7 +102,7 @@ def test_mx84_rejects():
     A8 = torch.zeros((4, 640), dtype=torch.uint8, device="cuda")
     B4 = torch.zeros((4, 320), dtype=torch.uint8, device="cuda")
     s = torch.full((4, 20), 127, dtype=torch.uint8, device="cuda")
-    with pytest.raises(ValueError):      # K = 640 is not a multiple of 512
+    with pytest.raises(ValueError):      # K = 640 is not a multiple of 256
         q.qgemm_mx_mixed(q.QGEMM_MX_E4M3, q.QGEMM_MX_E2M1, A8, B4, s, s, 1)
     with pytest.raises(ValueError):      # e2m1 A with e4m3 B
         q.qgemm_mx_mixed(q.QGEMM_MX_E2M1, q.QGEMM_MX_E4M3, B4, A8, s, s, 1)

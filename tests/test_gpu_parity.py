@@ -349,3 +349,37 @@ def test_full_workload_sampled(name, tile):
     ref, absdot, _ = parity.oracle_run(d, rows=rows)
     worst, cos = parity.compare(d, got, ref, absdot, f"full {name}")
     _say(f"[parity] full {name}: worst err/bound {worst:.3g} cos {cos:.8f}")
+
+
+@pytest.mark.parametrize("tile", [4, 5, 6, 7])
+@pytest.mark.parametrize("M,N,K", [(300, 520, 768), (257, 256, 1792), (64, 96, 256)])
+def test_mx8_dma_kernel_scale_rows_of_8_byte_words(M, N, K, tile):
+    """e4m3 MX on the LDS-fetch kernels with K a multiple of 256 but not of 512:
+    each 4-stage round reads the first 8 bytes of a 16-byte scale chunk that
+    may run past the row (into the next row, or past the range at the last
+    one); random scale codes so that a misplaced scale leaves the bound."""
+    d = inputs.make("mxfp8", M=M, N=N, K=K, bias=True)
+    rng = np.random.default_rng(M + N + K)
+    d["scale_a"] = rng.integers(112, 142, d["scale_a"].shape, dtype=np.uint8)
+    d["scale_b"] = rng.integers(112, 142, d["scale_b"].shape, dtype=np.uint8)
+    q.force_tile(tile)
+    _say(f"[parity] mx8 K%512!=0 {M}x{N}x{K} tile {tile}")
+    out = parity.gpu_run(d)
+    torch.cuda.synchronize()
+    ref, absdot, _ = parity.oracle_run(d)
+    parity.compare(d, parity.bits(out), ref, absdot, f"mx8 {M}x{N}x{K} tile {tile}")
+
+
+def test_mx8_pages_shape_sampled():
+    """MXFP8 at 32768 x 7168 x 1792 (the MI355X MXFP8 shape of ROCm/mori PR
+    #806's measurements), launched with the table's tile; sampled rows."""
+    d = inputs.make("mxfp8", M=32768, N=7168, K=1792)
+    assert q.select_tile(2, 32768, 7168, 1792) == 5
+    _say("[parity] full mxfp8 32768x7168x1792")
+    out = parity.gpu_run(d)
+    torch.cuda.synchronize()
+    rows = _sample_rows(d["M"], 16, np.random.default_rng(4))
+    got = parity.bits(out[torch.from_numpy(rows).cuda()])
+    ref, absdot, _ = parity.oracle_run(d, rows=rows)
+    worst, cos = parity.compare(d, got, ref, absdot, "full mxfp8 32768x7168x1792")
+    _say(f"[parity] full mxfp8 32768x7168x1792: worst err/bound {worst:.3g} cos {cos:.8f}")
