@@ -33,9 +33,21 @@ METRIC = "effective TFLOPS/TOPS (2MNK/t) per dtype; % of MI355X dense MFMA peak"
 # either operand is 8-bit)
 PEAK = {"i8": 5000.0, "f8": 5000.0, "f8b": 5000.0, "e4m3": 5000.0, "e2m1": 10100.0, "e4m3/e2m1": 5000.0}
 HBM_GBPS = 8000.0
-# The pages' number for the INT8 30000x21504x5376 workload: 209.9 TOPS, on a
-# different GPU (RX 9070 XT); context only.
-PAGES_I8_QKV_TOPS = 209.9
+# The pages' numbers for exactly these workloads (2MNK / their time where they
+# give a time), quoted by vs_baseline; context, not targets:
+#  - INT8 30000x21504x5376: 209.9 TOPS on an RX 9070 XT (comfy-kitchen PR #174,
+#    Performance) -- another GPU;
+#  - MXFP8 16384x7168x2048: 246.2 us and 32768x7168x1792: 462.2 us, FP8
+#    blockscale 16384x7168x2048: 362.3 us, all on MI355X (ROCm/mori PR #806,
+#    commit message table; its MXFP8 reads a packed scale layout);
+#  - MXFP4 8192^3: 5034 TFLOPS on MI355X (ROCm/FlyDSL PR #990, Performance).
+PAGES_REF = {
+    ("i8_qkv", 30000, 21504, 5376): 209.9,
+    ("mxfp8", 16384, 7168, 2048): 2.0 * 16384 * 7168 * 2048 / 246.2e-6 / 1e12,
+    ("mxfp8", 32768, 7168, 1792): 2.0 * 32768 * 7168 * 1792 / 462.2e-6 / 1e12,
+    ("f8_block", 16384, 7168, 2048): 2.0 * 16384 * 7168 * 2048 / 362.3e-6 / 1e12,
+    ("mxfp4", 8192, 8192, 8192): 5034.0,
+}
 # Rotating input sets so operands are not served from the 256 MB MALL.
 ROT = {"i8_small": 1, "f8_ptpc": 8, "mxfp8": 2, "mxfp4": 3, "i8_qkv": 2, "f8_block": 2, "mx_a8w4": 3}
 
@@ -422,7 +434,7 @@ def main():
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(value / PAGES_I8_QKV_TOPS, 4) if name == "i8_qkv" and not shape else None,
+        "vs_baseline": round(value / PAGES_REF[(name, M, N, K)], 4) if (name, M, N, K) in PAGES_REF else None,
         "dtype": {"i8": "int8", "f8": "e4m3", "f8b": "e4m3", "e4m3": "mxfp8-e4m3",
                   "e2m1": "mxfp4-e2m1", "e4m3/e2m1": "mx-e4m3xe2m1"}[dtype_of(d0)],
         "data": "synthetic",
