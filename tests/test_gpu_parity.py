@@ -383,3 +383,25 @@ def test_mx8_pages_shape_sampled():
     ref, absdot, _ = parity.oracle_run(d, rows=rows)
     worst, cos = parity.compare(d, got, ref, absdot, "full mxfp8 32768x7168x1792")
     _say(f"[parity] full mxfp8 32768x7168x1792: worst err/bound {worst:.3g} cos {cos:.8f}")
+
+
+@pytest.mark.parametrize("tile,K", [(-1, 131040), (0, 131040), (5, 130816)])
+def test_i8_largest_k(tile, K):
+    """The largest K the int32 accumulator admits (K * 128^2 < 2^31, K a
+    multiple of 32; 130816 for the LDS-fetch tile, a multiple of 256), with
+    every product at the extreme: A = -128, B = -128 gives acc = K * 16384
+    exactly, 2.1e9, and the bf16 output bit-exact against the oracle."""
+    M, N = 3, 40
+    d = inputs.make("i8_small", M=M, N=N, K=K)
+    d["A"] = np.full((M, K), -128, np.int8)
+    d["B"] = np.full((N, K), -128, np.int8)
+    d["B"][1::2, ::2] = 127          # odd rows of B: alternating -128 / 127
+    q.force_tile(tile)
+    _say(f"[parity] i8 largest K={K} tile {tile}")
+    acc = q.qgemm_i8_acc_i32(parity.dev(d["A"]), parity.dev(d["B"]))
+    out = parity.gpu_run(d)
+    torch.cuda.synchronize()
+    ref, _, ref_acc = parity.oracle_run(d)
+    assert acc[0, 0].item() == K * 16384
+    assert np.array_equal(acc.cpu().numpy(), ref_acc)
+    parity.compare(d, parity.bits(out), ref, None, f"i8 K={K} tile {tile}")
