@@ -318,21 +318,25 @@ int pick_tile_packed(int path, Shape s, int64_t kbytes, bool bf16_out)
 constexpr int64_t F8B_K_MULTIPLE = 256;
 
 // Mixed MX (e4m3 A, e2m1 B) runs in the LDS-fetch kernel: 256x256 (tile 5,
-// or 4 when forced) or 128x128 (tile 7) -- the table's 192x192 choice and
-// small M take tile 7.
+// or 4 when forced) or 128x128 (tile 7) -- the table's 192x192 choice takes
+// tile 7 -- and for M <= 16 in the small-M kernel (tile 8; 9 when forced).
 int pick_tile_mx84(Shape s)
 {
-    if (g_forced_tile == DMA_TILE || g_forced_tile == DMA8_TILE || g_forced_tile == DMA128_TILE)
+    if (g_forced_tile == DMA_TILE || g_forced_tile == DMA8_TILE || g_forced_tile == DMA128_TILE ||
+        g_forced_tile == SKINNY16_TILE || g_forced_tile == SKINNY64_TILE)
         return g_forced_tile;
     if (s.M <= SKINNY_MAX_M_MX)
-        return DMA128_TILE;
+        return SKINNY16_TILE;
     return select_tile_impl(2, s.M, s.N) == 0 ? DMA8_TILE : DMA128_TILE;
 }
 
 int pick_tile_f8b(int64_t M, int64_t N)
 {
-    if (g_forced_tile == F8B256_TILE || g_forced_tile == DMA128_TILE)
+    if (g_forced_tile == F8B256_TILE || g_forced_tile == DMA128_TILE || g_forced_tile == SKINNY16_TILE ||
+        g_forced_tile == SKINNY64_TILE)
         return g_forced_tile;
+    if (M <= SKINNY_MAX_M_MX)   // small M: the small-M kernel, one 16-row block
+        return SKINNY16_TILE;
     return ((M + 255) / 256) * ((N + 127) / 128) >= NUM_CU ? F8B256_TILE : DMA128_TILE;
 }
 

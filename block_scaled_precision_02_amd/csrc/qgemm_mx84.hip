@@ -2,7 +2,7 @@
 // per 32 K elements on both (v_mfma_scale_f32_32x32x64_f8f6f4 with an FP4
 // first operand and an FP8 second), run by the LDS-fetch kernel: tiles 4, 5
 // and 7 (the 192x192 tile's B rows are not a whole number of 32-row fetches
-// per wave).
+// per wave); small M by the small-M kernel (tiles 8, 9).
 #include "qgemm_launch.hpp"
 
 namespace qgemm {
@@ -19,6 +19,14 @@ static hipError_t mx84_tile(int tile, const Params &p, hipStream_t s)
         break;
     case DMA128_TILE:
         hipLaunchKernelGGL((qgemm_dma_kernel<PATH_MX84, 2, 2, 2, BIAS, BROWS, OUT_BF16>), grid, block, 0, s, p);
+        break;
+    case SKINNY16_TILE:
+        hipLaunchKernelGGL((qgemm_skinny_kernel<PATH_MX84, 1, skinny_depth<PATH_MX84, 1>(), BIAS, BROWS>), grid,
+                           block, 0, s, p);
+        break;
+    case SKINNY64_TILE:
+        hipLaunchKernelGGL((qgemm_skinny_kernel<PATH_MX84, 4, skinny_depth<PATH_MX84, 4>(), BIAS, BROWS>), grid,
+                           block, 0, s, p);
         break;
     default: return hipErrorInvalidValue;
     }

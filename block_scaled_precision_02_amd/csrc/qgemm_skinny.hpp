@@ -36,6 +36,14 @@
 //    makes the step's blocks in K order; for e2m1 a group's 16 bytes are its
 //    block).  Scale bytes are loaded per lane and step; blocks past K/32 and
 //    rows past M / N read 0, whose data is zero too.
+//  * Mixed MX (e4m3 A, e2m1 B): A keeps the e4m3 map (chunks g and g + 4 of a
+//    128-byte step); a step of B is 64 bytes, lane group g's 16 bytes being
+//    block g -- the block the same lane group's e4m3 chunks form -- and the
+//    instruction takes B as FP4 (cbsz 4) and A as FP8.
+//  * FP8 blockscale (fp32 scales per 128-element K block): a step is exactly
+//    one block, so each step's MFMA starts a fresh partial sum and the lane
+//    folds it into its total with fma(partial, sa[m, s] * sb[n/128, s]); the
+//    16 columns of a workgroup lie in one 128-row group of B.
 #pragma once
 #include "qgemm_kernel.hpp"
 
@@ -65,6 +73,16 @@ template <> struct SkinnyTraits<PATH_MX4> {   // 64 bytes = 128 e2m1 elements
     using Frag = i32x4;                       // the low half of the instruction's operand
     using Acc = f32x4;
 };
+template <> struct SkinnyTraits<PATH_MX84> {  // A: 128 e4m3 bytes; B: 64 e2m1 bytes (its low half)
+    static constexpr int KSTEP = 128, NCH = 2;
+    using Frag = i32x8;
+    using Acc = f32x4;
+};
+template <> struct SkinnyTraits<PATH_F8B> {
+    static constexpr int KSTEP = 128, NCH = 2;
+    using Frag = i32x8;
+    using Acc = f32x4;
+};
 
 constexpr int SK_WAVES = 8;
 
@@ -79,19 +97,24 @@ template <int PATH, int TM> constexpr int skinny_depth()
 {
     if constexpr (PATH == PATH_MX4)
         return TM == 1 ? 8 : 4;
-    if constexpr (PATH == PATH_MX8)
+    if constexpr (PATH == PATH_MX8 || PATH == PATH_MX84 || PATH == PATH_F8B)
         return TM == 1 ? 4 : 2;
     return TM == 1 ? (PATH == PATH_I8 ? 16 : 8) : (PATH == PATH_I8 ? 8 : 4);
 }
 
 template <int PATH, int TM, int D, bool BIAS, int BROWS>
-__global__ void __launch_bounds__(64 * SK_WAVES, ((PATH == PATH_MX8 || PATH == PATH_MX4) && TM == 1) ? 2 : 1)
+__global__ void __launch_bounds__(64 * SK_WAVES,
+                                  ((PATH == PATH_MX8 || PATH == PATH_MX4 || PATH == PATH_MX84 || PATH == PATH_F8B) &&
+                                   TM == 1) ? 2 : 1)
     qgemm_skinny_kernel(const Params p)
 {
     using T = SkinnyTraits<PATH>;
     using Frag = typename T::Frag;
     using Acc = typename T::Acc;
-    constexpr bool MX = PATH == PATH_MX8 || PATH == PATH_MX4;
+    constexpr bool MX = PATH == PATH_MX8 || PATH == PATH_MX4 || PATH == PATH_MX84;
+    constexpr bool B4 = PATH == PATH_MX84;          // e2m1 B under e4m3 A: 64 B of B per step
+    constexpr bool BS = PATH == PATH_F8B;           // fp32 scales per 128-element K block
+    constexpr bool INK = MX || BS;                  // scales applied inside the K loop
     constexpr int BM = 16 * TM, BN = 16;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -106,9 +129,10 @@ __global__ void __launch_bounds__(64 * SK_WAVES, ((PATH == PATH_MX8 || PATH == P
     // B row-major, or prepacked (the workgroup's 16 columns are one packed
     // group: 64-byte K piece t of its rows is the 1 KB block t, row r's chunk
     // c at slot 4r + (c ^ ((r >> 2) & 3)); rows past N are zeros there)
+    const int kbytes_b = B4 ? p.kbytes / 2 : p.kbytes;
     const __amdgpu_buffer_rsrc_t rb =
         p.b_packed ? make_rsrc(p.B + (int64_t)(n0 / 16) * 16 * p.kbytes, (uint32_t)(16 * p.kbytes))
-                   : make_rsrc(p.B + (int64_t)n0 * p.ldb, (uint32_t)((rows_b - 1) * p.ldb + p.kbytes));
+                   : make_rsrc(p.B + (int64_t)n0 * p.ldb, (uint32_t)((rows_b - 1) * p.ldb + kbytes_b));
     unsigned a_row[TM];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -121,10 +145,12 @@ __global__ void __launch_bounds__(64 * SK_WAVES, ((PATH == PATH_MX8 || PATH == P
     const int ksteps = (p.kbytes + T::KSTEP - 1) / T::KSTEP;
     const int nst = ksteps > wave ? (ksteps - wave + SK_WAVES - 1) / SK_WAVES : 0;
 
-    // MX scale rows: A row 16i + l%16; B row l%16 (1x32) or its 32-row group
+    // MX scale rows: A row 16i + l%16; B row l%16 (1x32) or its 32-row group.
+    // Blockscale: fp32 rows of K/128 values (K/32 bytes): A row 16i + l%16,
+    // B row n0/128 (the same for the whole workgroup).
     __amdgpu_buffer_rsrc_t rsa, rsb;
     unsigned sa_row[TM], sb_row = OOB;
-    if constexpr (MX) {
+    if constexpr (INK) {
         rsa = make_rsrc(p.mx_sa + (int64_t)m0 * p.kblocks, (uint32_t)(rows_a * p.kblocks));
         const int sb0 = n0 / BROWS, sb_rows = (n0 + rows_b - 1) / BROWS - sb0 + 1;
         rsb = make_rsrc(p.mx_sb + (int64_t)sb0 * p.kblocks, (uint32_t)(sb_rows * p.kblocks));
@@ -138,7 +164,7 @@ __global__ void __launch_bounds__(64 * SK_WAVES, ((PATH == PATH_MX8 || PATH == P
     }
 
     Frag fa[D][TM], fb[D];
-    unsigned ssa[MX ? D : 1][TM], ssb[MX ? D : 1];
+    unsigned ssa[INK ? D : 1][TM], ssb[INK ? D : 1];
     Acc acc[TM];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -152,12 +178,25 @@ __global__ void __launch_bounds__(64 * SK_WAVES, ((PATH == PATH_MX8 || PATH == P
         for (int c = 0; c < T::NCH; ++c) {
             const int kc = s * T::KSTEP + 64 * c + 16 * g;
             const bool kin = s < ksteps && kc < p.kbytes;
-            const unsigned bo = p.b_packed ? b_slot + (unsigned)((s * T::KSTEP + 64 * c) / 64) * 1024u
-                                           : b_row + (unsigned)kc;
-            const u32x4 vb = ld16(rb, kin ? bo : OOB);
+            if constexpr (B4) {
+                // one 16-byte e2m1 chunk per lane and step; VGPRs 4-7 unused
+                if (c == 0) {
+                    const int kcb = s * 64 + 16 * g;
+                    const u32x4 vb = ld16(rb, (s < ksteps && kcb < kbytes_b) ? b_row + (unsigned)kcb : OOB);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                fb[SLOT][4 * c + q] = (int)vb[q];
+                    for (int q = 0; q < 4; ++q) {
+                        fb[SLOT][q] = (int)vb[q];
+                        fb[SLOT][4 + q] = 0;
+                    }
+                }
+            } else {
+                const unsigned bo = p.b_packed ? b_slot + (unsigned)((s * T::KSTEP + 64 * c) / 64) * 1024u
+                                               : b_row + (unsigned)kc;
+                const u32x4 vb = ld16(rb, kin ? bo : OOB);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    fb[SLOT][4 * c + q] = (int)vb[q];
+            }
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 const u32x4 va = ld16(ra, kin ? a_row[i] + (unsigned)kc : OOB);
@@ -174,6 +213,14 @@ __global__ void __launch_bounds__(64 * SK_WAVES, ((PATH == PATH_MX8 || PATH == P
 #pragma unroll
             for (int i = 0; i < TM; ++i)
                 ssa[SLOT][i] = __builtin_amdgcn_raw_buffer_load_b8(rsa, bin ? sa_row[i] + (unsigned)kblk : OOB, 0, 0);
+        } else if constexpr (BS) {
+            // block s: fp32 word s of each scale row (0 past K/128)
+            const bool bin = s < ksteps;
+            ssb[SLOT] = __builtin_amdgcn_raw_buffer_load_b32(rsb, bin ? (unsigned)(4 * s) : OOB, 0, 0);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                ssa[SLOT][i] = __builtin_amdgcn_raw_buffer_load_b32(rsa, bin ? sa_row[i] + (unsigned)(4 * s) : OOB,
+                                                                    0, 0);
         }
     };
     auto mma = [&](auto slotc) {
@@ -188,6 +235,16 @@ __global__ void __launch_bounds__(64 * SK_WAVES, ((PATH == PATH_MX8 || PATH == P
             } else if constexpr (PATH == PATH_MX8) {
                 acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                     fb[SLOT], fa[SLOT][i], acc[i], 0, 0, 0, (int)ssb[SLOT], 0, (int)ssa[SLOT][i]);
+            } else if constexpr (PATH == PATH_MX84) {
+                acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    fb[SLOT], fa[SLOT][i], acc[i], 4, 0, 0, (int)ssb[SLOT], 0, (int)ssa[SLOT][i]);
+            } else if constexpr (PATH == PATH_F8B) {
+                const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[SLOT], fa[SLOT][i], f32x4{},
+                                                                                   0, 0, 0, 0, 0, 0);
+                const float w = __builtin_bit_cast(float, ssa[SLOT][i]) * __builtin_bit_cast(float, ssb[SLOT]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[i][r] = __builtin_fmaf(part[r], w, acc[i][r]);
             } else {
                 const i32x4 b4 = fb[SLOT], a4 = fa[SLOT][i];
                 const i32x8 b8 = {b4[0], b4[1], b4[2], b4[3], 0, 0, 0, 0};
@@ -239,7 +296,7 @@ __global__ void __launch_bounds__(64 * SK_WAVES, ((PATH == PATH_MX8 || PATH == P
     // Epilogue (the fixed-order binary32 sequence of the main kernels).
     const int nloc = 4 * g;
     __amdgpu_buffer_rsrc_t rsbe, rsae, rbias;
-    if constexpr (!MX) {
+    if constexpr (!INK) {
         rsbe = make_rsrc(p.scale_b + n0, (uint32_t)(rows_b * 4));
         rsae = make_rsrc(p.scale_a + m0, (uint32_t)(rows_a * 4));
     }
@@ -249,7 +306,7 @@ __global__ void __launch_bounds__(64 * SK_WAVES, ((PATH == PATH_MX8 || PATH == P
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const bool in = nloc + r < rows_b;
-        if constexpr (!MX)
+        if constexpr (!INK)
             sbw[r] = __builtin_amdgcn_raw_buffer_load_b32(rsbe, in ? (unsigned)((nloc + r) * 4) : OOB, 0, 0);
         if constexpr (BIAS)
             bbw[r] = (unsigned)__builtin_amdgcn_raw_buffer_load_b16(rbias, in ? (unsigned)((nloc + r) * 2) : OOB, 0,
@@ -262,7 +319,7 @@ __global__ void __launch_bounds__(64 * SK_WAVES, ((PATH == PATH_MX8 || PATH == P
     for (int i = 0; i < TM; ++i) {
         const int mloc = 16 * i + r16;
         float sa = 1.0f;
-        if constexpr (!MX)
+        if constexpr (!INK)
             sa = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                                rsae, mloc < rows_a ? (unsigned)(mloc * 4) : OOB, 0, 0));
         float f[4];
@@ -273,7 +330,7 @@ __global__ void __launch_bounds__(64 * SK_WAVES, ((PATH == PATH_MX8 || PATH == P
                 x = (float)acc[i][r];
             else
                 x = acc[i][r];
-            if constexpr (!MX) {
+            if constexpr (!INK) {
                 x = x * sa;
                 x = x * __builtin_bit_cast(float, sbw[r]);
             }

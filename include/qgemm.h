@@ -268,9 +268,10 @@ const char *qgemm_status_string(qgemm_status status);
 
 /* Tile variant the host-side table picks for a problem (pure host logic, no
  * HIP call; for MX, assuming 16-byte-aligned scale arrays).  path: 0 int8,
- * 1 fp8, 2 MX e4m3, 3 MX e2m1, 4 fp8 blockscale (tile 10 when its grid of
- * 256x128 tiles fills the 256 CUs at least once, else tile 7), 5 MX e4m3 A
- * with e2m1 B (tile 5 where the table picks 256x256, else 7).  Returns the
+ * 1 fp8, 2 MX e4m3, 3 MX e2m1, 4 fp8 blockscale (tile 8 for M <= 16, else
+ * tile 10 when its grid of 256x128 tiles fills the 256 CUs at least once,
+ * else tile 7), 5 MX e4m3 A with e2m1 B (tile 8 for M <= 16, else tile 5
+ * where the table picks 256x256, else 7).  Returns the
  * tile id, or -1 for a bad path:
  *   0: 256x256, 4 waves, operands staged through registers
  *   1: 128x128    2: 256x256 with 8 waves, staged through registers

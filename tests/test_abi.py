@@ -298,6 +298,7 @@ def test_f8_blockscale_checks_pass_before_the_device_check(monkeypatch):
     assert f8b(M=0) == q.QGEMM_OK
     assert q.select_tile(4, 16384, 7168, 2048) == 10
     assert q.select_tile(4, 256, 7168, 2048) == 7          # 56 tiles of 256x128: too few for the chip
+    assert q.select_tile(4, 16, 7168, 2048) == 8           # small M: the small-M kernel
     assert q.select_tile(4, 1024, 8192, 2048) == 10         # 4 x 64 = 256 tiles
 
 
@@ -327,4 +328,5 @@ def test_mx_mixed_checks_pass_before_the_device_check(monkeypatch):
     assert mx2() == q.QGEMM_ERR_UNSUPPORTED_DEVICE
     assert mx2(M=0) == q.QGEMM_OK
     assert q.select_tile(5, 8192, 8192, 8192) == 5
-    assert q.select_tile(5, 16, 8192, 8192) == 7
+    assert q.select_tile(5, 16, 8192, 8192) == 8           # small M: the small-M kernel
+    assert q.select_tile(5, 17, 8192, 8192) == 7           # the table: 64 tiles of 128 beat 32 of 256

@@ -140,3 +140,31 @@ def test_f8b_rejects_k_not_multiple_of_256():
     sb = torch.ones((1, 5), dtype=torch.float32, device="cuda")
     with pytest.raises(ValueError):
         q.qgemm_f8_blockscale(A, A, sa, sb)
+
+
+SMALL_M = [(1, 7168, 2048, 8), (5, 200, 256, 8), (16, 300, 1792, 8), (1, 1, 512, 8), (33, 130, 512, 9),
+           (64, 264, 768, 9)]
+
+
+@pytest.mark.parametrize("M,N,K,tile", SMALL_M)
+def test_f8b_small_m_kernel(M, N, K, tile):
+    """The small-M kernel (eight waves splitting K, one 128-element step = one
+    scale block): ragged N, canaries, bias, wide-range scales."""
+    q.force_tile(tile)
+    d = inputs.make("f8_block", M=M, N=N, K=K, bias=(M % 2 == 1))
+    rng = np.random.default_rng(M * 7 + N)
+    d["scale_a"] = _wide_scales(d["scale_a"].shape, rng)
+    d["scale_b"] = _wide_scales(d["scale_b"].shape, rng)
+    ldc = N + (-N) % 8 + 8
+    buf = torch.full((M + 3, ldc), float("nan"), dtype=torch.bfloat16, device="cuda")
+    before = parity.bits(buf)
+    _check(d, f"f8b small M tile {tile}", out=buf[:M, :N])
+    after = parity.bits(buf)
+    assert np.array_equal(after[:M, N:], before[:M, N:]), "wrote past N"
+    assert np.array_equal(after[M:], before[M:]), "wrote past M"
+
+
+def test_f8b_small_m_table_choice():
+    assert q.select_tile(4, 16, 7168, 2048) == 8
+    d = inputs.make("f8_block", M=16, N=7168, K=2048)
+    _check(d, "f8b decode 16x7168x2048")

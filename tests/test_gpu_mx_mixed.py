@@ -129,3 +129,26 @@ def test_mx84_full_workload_sampled(tile):
     ref, absdot, _ = parity.oracle_run(d, rows=rows)
     worst, cos = parity.compare(d, got, ref, absdot, "full mx_a8w4")
     _say(f"[parity] full mx_a8w4: worst err/bound {worst:.3g} cos {cos:.8f}")
+
+
+SMALL_M = [(1, 7168, 2048, 8), (5, 200, 256, 8), (16, 300, 1792, 8), (1, 1, 512, 8), (33, 130, 512, 9),
+           (64, 264, 768, 9)]
+
+
+@pytest.mark.parametrize("brows", [1, 32])
+@pytest.mark.parametrize("M,N,K,tile", SMALL_M)
+def test_mx84_small_m_kernel(M, N, K, tile, brows):
+    """The small-M kernel: A e4m3 in its two-chunk map, B one 16-byte e2m1
+    chunk per lane and step; ragged N, canaries, bias, random scale codes."""
+    q.force_tile(tile)
+    d = _make(M, N, K, brows, bias=(M % 2 == 1))
+    rng = np.random.default_rng(M * 5 + N + brows)
+    d["scale_a"] = rng.integers(112, 142, d["scale_a"].shape, dtype=np.uint8)
+    d["scale_b"] = rng.integers(112, 142, d["scale_b"].shape, dtype=np.uint8)
+    ldc = N + (-N) % 8 + 8
+    buf = torch.full((M + 3, ldc), float("nan"), dtype=torch.bfloat16, device="cuda")
+    before = parity.bits(buf)
+    _check(d, f"mx84 small M tile {tile}", out=buf[:M, :N])
+    after = parity.bits(buf)
+    assert np.array_equal(after[:M, N:], before[:M, N:]), "wrote past N"
+    assert np.array_equal(after[M:], before[M:]), "wrote past M"
