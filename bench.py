@@ -80,8 +80,8 @@ class Launcher:
         self.args = []
         for s in sets:
             bias = None if s["bias"] is None else s["bias"].data_ptr()
-            if prepacked and (d["kind"] == "f8b" or "/" in (d["fmt"] or "")):
-                raise SystemExit("bench.py: the blockscale and mixed-format GEMMs have no prepacked entry point")
+            if prepacked and "/" in (d["fmt"] or ""):
+                raise SystemExit("bench.py: the mixed-format GEMM has no prepacked entry point")
             if prepacked:
                 # B prepacked once, outside the timed region (the weights are static)
                 pb = q.qgemm_prepack_b(s["B"]).data
@@ -90,10 +90,11 @@ class Launcher:
                     a = (s["A"].data_ptr(), s["A"].stride(0), pb.data_ptr(), s["scale_a"].data_ptr(),
                          s["scale_b"].data_ptr(), bias, out.data_ptr(), self.ldc, d["M"], N, d["K"], self.stream)
                     self.args.append((self.L.qgemm_i8_rowwise_prepacked, a))
-                elif d["kind"] == "f8":
+                elif d["kind"] in ("f8", "f8b"):
                     a = (s["A"].data_ptr(), s["A"].stride(0), pb.data_ptr(), s["scale_a"].data_ptr(),
                          s["scale_b"].data_ptr(), bias, out.data_ptr(), self.ldc, d["M"], N, d["K"], self.stream)
-                    self.args.append((self.L.qgemm_f8_pertoken_prepacked, a))
+                    fn = self.L.qgemm_f8_pertoken_prepacked if d["kind"] == "f8" else self.L.qgemm_f8_blockscale_prepacked
+                    self.args.append((fn, a))
                 else:
                     fmt = 0 if d["fmt"] == "e4m3" else 1
                     a = (fmt, s["A"].data_ptr(), s["A"].stride(0), pb.data_ptr(), s["scale_a"].data_ptr(),

@@ -17,6 +17,7 @@ call raises.
     qgemm_prepack_b(B, row_bytes=None, out=None)          -> PackedB
     qgemm_i8_rowwise_prepacked(A, Bp, scale_a, scale_b, bias=None, out=None)
     qgemm_f8_pertoken_prepacked(A, Bp, scale_a, scale_b, bias=None, out=None)
+    qgemm_f8_blockscale_prepacked(A, Bp, scale_a, scale_b, bias=None, out=None)
     qgemm_mx_prepacked(fmt, A, Bp, scale_a, scale_b, b_layout, bias=None, out=None)
     qgemm_quant_f8_pertoken(X, out=None, scale=None)      -> (Q, scale)
     qgemm_quant_mx(fmt, X, out=None, scales=None)         -> (Q, S)
@@ -48,7 +49,7 @@ QGEMM_MX_BSCALE_32x32 = 32
 # Every symbol include/qgemm.h declares.
 EXPORTS = ("qgemm_i8_rowwise", "qgemm_i8_acc_i32", "qgemm_f8_pertoken", "qgemm_f8_blockscale", "qgemm_mx", "qgemm_mx_mixed",
            "qgemm_prepacked_b_bytes", "qgemm_prepack_b", "qgemm_i8_rowwise_prepacked",
-           "qgemm_f8_pertoken_prepacked", "qgemm_mx_prepacked",
+           "qgemm_f8_pertoken_prepacked", "qgemm_f8_blockscale_prepacked", "qgemm_mx_prepacked",
            "qgemm_quant_f8_pertoken", "qgemm_quant_mx",
            "qgemm_last_error", "qgemm_status_string", "qgemm_select_tile",
            "qgemm_tile_rows", "qgemm_force_tile")
@@ -90,6 +91,8 @@ def lib():
     L.qgemm_i8_rowwise_prepacked.argtypes = [_P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
     L.qgemm_f8_pertoken_prepacked.restype = st
     L.qgemm_f8_pertoken_prepacked.argtypes = [_P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
+    L.qgemm_f8_blockscale_prepacked.restype = st
+    L.qgemm_f8_blockscale_prepacked.argtypes = [_P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
     L.qgemm_mx_prepacked.restype = st
     L.qgemm_mx_prepacked.argtypes = [ctypes.c_int, _P, _I64, _P, _P, _P, ctypes.c_int, _P, _P, _I64, _I64, _I64,
                                      _I64, _P]
@@ -524,6 +527,27 @@ def qgemm_f8_pertoken_prepacked(A, Bp, scale_a, scale_b, bias=None, out=None, st
     with torch.cuda.device(A.device):
         _check(lib().qgemm_f8_pertoken_prepacked(_ptr(A), lda, _ptr(Bp.data), _ptr(sa), _ptr(sb), _ptr(bias),
                                                  _ptr(out), _ldc(out, N), M, N, K, _stream(A.device, stream)))
+    return out
+
+
+def qgemm_f8_blockscale_prepacked(A, Bp, scale_a, scale_b, bias=None, out=None, stream=None):
+    """FP8 blockscale GEMM with a prepacked B -> bf16 [M, N]; scale_a
+    [M, K/128], scale_b [ceil(N/128), K/128] fp32, contiguous."""
+    torch = _torch()
+    lda = _operand(A, "A", _fp8_dtypes())
+    M, K = A.shape
+    Bp = _packed(Bp, K)
+    N = Bp.N
+    if K % 128:
+        raise ValueError(f"K={K} is not a multiple of 128")
+    sa = _matrix(scale_a, "scale_a", (M, K // 128), (torch.float32,))
+    sb = _matrix(scale_b, "scale_b", ((N + 127) // 128, K // 128), (torch.float32,))
+    bias = _bias(bias, N)
+    _same_device(A.device, Bp.data, sa, sb, bias)
+    out = _out(out, M, N, A.device, torch.bfloat16)
+    with torch.cuda.device(A.device):
+        _check(lib().qgemm_f8_blockscale_prepacked(_ptr(A), lda, _ptr(Bp.data), _ptr(sa), _ptr(sb), _ptr(bias),
+                                                   _ptr(out), _ldc(out, N), M, N, K, _stream(A.device, stream)))
     return out
 
 

@@ -488,9 +488,9 @@ qgemm_status qgemm_f8_pertoken(const uint8_t *A, int64_t lda, const uint8_t *B, 
     return f8_common(A, lda, B, ldb, scale_a, scale_b, bias, C, ldc, M, N, K, stream, false);
 }
 
-qgemm_status qgemm_f8_blockscale(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb, const float *scale_a,
-                                 const float *scale_b, const uint16_t *bias, uint16_t *C, int64_t ldc, int64_t M,
-                                 int64_t N, int64_t K, void *stream)
+static qgemm_status f8b_common(const uint8_t *A, int64_t lda, const void *B, int64_t ldb, const float *scale_a,
+                               const float *scale_b, const uint16_t *bias, uint16_t *C, int64_t ldc, int64_t M,
+                               int64_t N, int64_t K, void *stream, bool packed)
 {
     const Shape s{M, N, K};
     TRY(check_shape(s, false));
@@ -500,7 +500,10 @@ qgemm_status qgemm_f8_blockscale(const uint8_t *A, int64_t lda, const uint8_t *B
     if (M == 0 || N == 0)
         return QGEMM_OK;
     TRY(check_operand("A", A, lda, K));
-    TRY(check_operand("B", B, ldb, K));
+    if (packed)
+        TRY(check_packed_b(B, K));
+    else
+        TRY(check_operand("B", B, ldb, K));
     TRY(check_fp32_scales(scale_a, scale_b));
     if (!aligned(scale_a, 8) || !aligned(scale_b, 8))
         return fail(QGEMM_ERR_BAD_LAYOUT, "blockscale scale arrays must be 8-byte aligned");
@@ -508,13 +511,21 @@ qgemm_status qgemm_f8_blockscale(const uint8_t *A, int64_t lda, const uint8_t *B
     TRY(check_output(C, ldc, N, 2));
     TRY(check_device());
     const int tile = pick_tile_f8b(M, N);
-    Params p = base_params(A, lda, B, ldb, C, ldc, s, K, tile);
+    Params p = base_params(A, lda, B, packed ? K : ldb, C, ldc, s, K, tile);
+    p.b_packed = packed;
     TRY(check_grid(p));
     // the scale matrices travel as byte rows of K/32 bytes (K/128 floats)
     p.mx_sa = (const uint8_t *)scale_a;
     p.mx_sb = (const uint8_t *)scale_b;
     p.bias = bias;
     return finish(launch_f8b(tile, bias != nullptr, p, (hipStream_t)stream));
+}
+
+qgemm_status qgemm_f8_blockscale(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb, const float *scale_a,
+                                 const float *scale_b, const uint16_t *bias, uint16_t *C, int64_t ldc, int64_t M,
+                                 int64_t N, int64_t K, void *stream)
+{
+    return f8b_common(A, lda, B, ldb, scale_a, scale_b, bias, C, ldc, M, N, K, stream, false);
 }
 
 static qgemm_status mx_common(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const void *B, int64_t ldb_bytes,
@@ -659,6 +670,13 @@ qgemm_status qgemm_f8_pertoken_prepacked(const uint8_t *A, int64_t lda, const vo
                                          int64_t M, int64_t N, int64_t K, void *stream)
 {
     return f8_common(A, lda, Bp, 0, scale_a, scale_b, bias, C, ldc, M, N, K, stream, true);
+}
+
+qgemm_status qgemm_f8_blockscale_prepacked(const uint8_t *A, int64_t lda, const void *Bp, const float *scale_a,
+                                           const float *scale_b, const uint16_t *bias, uint16_t *C, int64_t ldc,
+                                           int64_t M, int64_t N, int64_t K, void *stream)
+{
+    return f8b_common(A, lda, Bp, 0, scale_a, scale_b, bias, C, ldc, M, N, K, stream, true);
 }
 
 qgemm_status qgemm_mx_prepacked(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const void *Bp,

@@ -213,6 +213,11 @@ qgemm_status qgemm_i8_rowwise_prepacked(const int8_t *A, int64_t lda, const void
 qgemm_status qgemm_f8_pertoken_prepacked(const uint8_t *A, int64_t lda, const void *Bp, const float *scale_a,
                                          const float *scale_b, const uint16_t *bias, uint16_t *C, int64_t ldc,
                                          int64_t M, int64_t N, int64_t K, void *stream);
+/* qgemm_f8_blockscale with Bp in place of (B, ldb): results equal
+ * qgemm_f8_blockscale's on the same tile. */
+qgemm_status qgemm_f8_blockscale_prepacked(const uint8_t *A, int64_t lda, const void *Bp, const float *scale_a,
+                                           const float *scale_b, const uint16_t *bias, uint16_t *C, int64_t ldc,
+                                           int64_t M, int64_t N, int64_t K, void *stream);
 qgemm_status qgemm_mx_prepacked(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const void *Bp,
                                 const uint8_t *scale_a, const uint8_t *scale_b, qgemm_mx_bscale b_layout,
                                 const uint16_t *bias, uint16_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,

@@ -330,3 +330,14 @@ def test_mx_mixed_checks_pass_before_the_device_check(monkeypatch):
     assert q.select_tile(5, 8192, 8192, 8192) == 5
     assert q.select_tile(5, 16, 8192, 8192) == 8           # small M: the small-M kernel
     assert q.select_tile(5, 17, 8192, 8192) == 7           # the table: 64 tiles of 128 beat 32 of 256
+
+
+def test_blockscale_prepacked_rejects_and_passes(monkeypatch):
+    L = q.lib()
+    assert L.qgemm_f8_blockscale_prepacked(FAKE, 512, None, FAKE3, FAKE3, None, FAKE, 64, 64, 64, 512,
+                                           None) == q.QGEMM_ERR_NULL_POINTER
+    assert L.qgemm_f8_blockscale_prepacked(FAKE, 640, FAKE2, FAKE3, FAKE3, None, FAKE, 64, 64, 64, 640,
+                                           None) == q.QGEMM_ERR_BAD_SHAPE
+    monkeypatch.setenv("QGEMM_FAKE_ARCH", "gfx1201")
+    assert L.qgemm_f8_blockscale_prepacked(FAKE, 512, FAKE2, FAKE3, FAKE3, None, FAKE, 64, 64, 64, 512,
+                                           None) == q.QGEMM_ERR_UNSUPPORTED_DEVICE

@@ -63,6 +63,8 @@ def _run_packed(d, out=None):
         return q.qgemm_i8_rowwise_prepacked(A, pb, sa, sb, bias, out=out)
     if d["kind"] == "f8":
         return q.qgemm_f8_pertoken_prepacked(A, pb, sa, sb, bias, out=out)
+    if d["kind"] == "f8b":
+        return q.qgemm_f8_blockscale_prepacked(A, pb, sa, sb, bias, out=out)
     fmt = q.QGEMM_MX_E4M3 if d["fmt"] == "e4m3" else q.QGEMM_MX_E2M1
     return q.qgemm_mx_prepacked(fmt, A, pb, sa, sb, d["b_rows_per_scale"], bias, out=out)
 
@@ -96,7 +98,29 @@ def test_prepacked_gemm_edges(name, M, N, K, tile):
     assert np.array_equal(after[:M, :N], plain), "prepacked and row-major B differ"
 
 
-@pytest.mark.parametrize("name", ["f8_ptpc", "mxfp8", "mxfp4", "i8_qkv"])
+@pytest.mark.parametrize("tile", [-1, 7, 10, 8, 9])
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_prepacked_blockscale_edges(M, N, K, tile):
+    """The blockscale GEMM on a prepacked B: every tile it runs on, ragged M /
+    N, canaries; bit for bit equal to the same tile on the row-major B."""
+    d = inputs.make("f8_block", M=M, N=N, K=K, bias=(M % 2 == 1))
+    _say(f"[prepacked] f8_block {M}x{N}x{K} tile {tile}")
+    q.force_tile(tile)
+    ldc = N + (-N) % 8 + 8
+    buf = torch.full((M + 3, ldc), float("nan"), dtype=torch.bfloat16, device="cuda")
+    before = parity.bits(buf)
+    _run_packed(d, out=buf[:M, :N])
+    after = parity.bits(buf)
+    ref, absdot, _ = parity.oracle_run(d)
+    parity.compare(d, after[:M, :N], ref, absdot, f"prepacked f8_block {M}x{N}x{K} tile {tile}")
+    assert np.array_equal(after[:M, N:], before[:M, N:]), "wrote past N"
+    assert np.array_equal(after[M:], before[M:]), "wrote past M"
+    q.force_tile(tile)
+    plain = parity.bits(parity.gpu_run(d))
+    assert np.array_equal(after[:M, :N], plain), "prepacked and row-major B differ"
+
+
+@pytest.mark.parametrize("name", ["f8_ptpc", "mxfp8", "mxfp4", "i8_qkv", "f8_block"])
 def test_prepacked_full_workload_sampled(name):
     """Each workload at its full size with a prepacked B, as the table
     launches it; sampled whole rows against the oracle."""
