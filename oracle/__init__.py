@@ -22,7 +22,7 @@ Functions follow the definitions in ``qgemm_oracle.c``:
                   in ``qgemm_oracle.c``).
   pack_b       -- the prepacked weight layout of the ``_prepacked`` GEMM entry
                   points (defined in ``qgemm_oracle.c``).
-  quant_f8_pertoken, quant_mx
+  quant_f8_pertoken, quant_f8_block, quant_mx
                -- the activation quantisers producing those operands from
                   bf16 (ROCm/mori PR #806, What: the quantiser's [M, K/32]
                   uint8 scales; the scale rules are readings, stated in
@@ -81,6 +81,8 @@ def _load():
         getattr(lib, name).argtypes = [_P, _P, _I64]
     lib.orc_quant_f8_pertoken.restype = None
     lib.orc_quant_f8_pertoken.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64]
+    lib.orc_quant_f8_block.restype = ctypes.c_int
+    lib.orc_quant_f8_block.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64, _I64]
     lib.orc_quant_mx.restype = ctypes.c_int
     lib.orc_quant_mx.argtypes = [ctypes.c_int, _P, _I64, _P, _I64, _P, _I64, _I64, _I64]
     lib.orc_pack_b.restype = None
@@ -287,6 +289,20 @@ def quant_f8_pertoken(X):
     s = np.empty(M, np.float32)
     _load().orc_quant_f8_pertoken(_ptr(X), K, _ptr(Q), K, _ptr(s), M, K)
     return Q, s
+
+
+def quant_f8_block(X):
+    """Blockscale e4m3 quantiser, one fp32 scale per 128 elements of a row.
+    X [M,K] bf16 bits (uint16), K % 128 == 0.
+    Returns (Q uint8 [M,K] e4m3 codes, S float32 [M, K/128])."""
+    X = _c(X, np.uint16)
+    M, K = X.shape
+    assert K % 128 == 0
+    Q = np.empty((M, K), np.uint8)
+    S = np.empty((M, K // 128), np.float32)
+    if _load().orc_quant_f8_block(_ptr(X), K, _ptr(Q), K, _ptr(S), K // 128, M, K) != 0:
+        raise ValueError("K must be a multiple of 128")
+    return Q, S
 
 
 def quant_mx(fmt, X):

@@ -465,6 +465,40 @@ void orc_quant_f8_pertoken(const uint16_t *X, int64_t ldx, uint8_t *Q, int64_t l
     }
 }
 
+/* Blockscale e4m3 quantiser, the operand of orc_f8_blockscale's A: the
+ * per-token rule applied to each 128-element block of a row (the blockscale
+ * GEMM's block reading): scale S[m, b] = fp32(amax_block / 448) and
+ * code = enc(fp32(x / S[m, b])), an all-zero block keeping its signed zeros
+ * with scale 0.  X [M,K] bf16 bits (row stride ldx), K % 128 == 0; Q [M,K]
+ * codes (row stride ldq bytes); S [M, K/128] binary32 (row stride lds
+ * elements).  Returns 0, or -1 if K is not a multiple of 128. */
+int orc_quant_f8_block(const uint16_t *X, int64_t ldx, uint8_t *Q, int64_t ldq, float *S, int64_t lds,
+                       int64_t M, int64_t K)
+{
+    if (K % 128 != 0)
+        return -1;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t b = 0; b < K / 128; ++b) {
+            const uint16_t *x = X + m * ldx + 128 * b;
+            float amax = 0.0f;
+            for (int j = 0; j < 128; ++j) {
+                const float v = fabsf(orc_bf16_to_f32(x[j]));
+                if (v > amax)
+                    amax = v;
+            }
+            const float s = amax / 448.0f;          /* binary32 division */
+            S[m * lds + b] = s;
+            for (int j = 0; j < 128; ++j) {
+                const float v = orc_bf16_to_f32(x[j]);
+                const float y = (s > 0.0f) ? v / s : v;
+                Q[m * ldq + 128 * b + j] = orc_enc_e4m3((double)y);
+            }
+        }
+    }
+    return 0;
+}
+
 /* MX quantiser, one ue8m0 scale per 32 elements of a row.  fmt 0: e4m3, Q
  * [M,K] bytes; fmt 1: e2m1, Q [M,K/2] bytes (element k even in the low nibble
  * of byte k/2, k odd in the high one).  X [M,K] bf16 bits (row stride ldx

@@ -247,3 +247,44 @@ def test_mx_agrees_with_the_input_generator_away_from_signed_zero(orc):
         mine = Q if fmt == 0 else np.stack([Q & 15, Q >> 4], axis=2).reshape(16, 512)
         zero_mag = (mine & (0x7F if fmt == 0 else 7)) == 0
         assert np.array_equal(np.where(zero_mag, 0, mine), np.where(zero_mag, 0, codes))
+
+
+# ------------------------------------------------------------ blockscale e4m3
+
+def test_f8_block_on_one_block_is_the_pertoken_quantiser(orc):
+    """K = 128: one block per row, so the blockscale quantiser is the
+    per-token one (pinned above), bit for bit."""
+    X = _rows(M=24, K=128, seed=9)
+    Q, S = orc.quant_f8_block(X)
+    Qp, Sp = orc.quant_f8_pertoken(X)
+    np.testing.assert_array_equal(Q, Qp)
+    np.testing.assert_array_equal(S[:, 0].view(np.uint32), Sp.view(np.uint32))
+
+
+def test_f8_block_is_the_pertoken_quantiser_per_block(orc):
+    """Each 128-column slice of a row is quantised as the per-token quantiser
+    quantises that slice alone; all-zero blocks keep their signed zeros."""
+    X = _rows(M=12, K=640, seed=10)
+    X[3, 128:256] = 0
+    X[3, 129:256:2] = 0x8000
+    Q, S = orc.quant_f8_block(X)
+    for b in range(5):
+        Qp, Sp = orc.quant_f8_pertoken(np.ascontiguousarray(X[:, 128 * b:128 * b + 128]))
+        np.testing.assert_array_equal(Q[:, 128 * b:128 * b + 128], Qp)
+        np.testing.assert_array_equal(S[:, b].view(np.uint32), Sp.view(np.uint32))
+    assert S[3, 1] == 0 and (Q[3, 129:256:2] == 0x80).all() and (Q[3, 128:256:2] == 0).all()
+
+
+def test_f8_block_agrees_with_the_input_generator_away_from_signed_zero(orc):
+    """The blockscale workload's input recipe (its own quantiser, numpy and
+    torch's e4m3 grid) gives the same codes and scales, except that it writes
+    +0 where a negative value rounds to zero."""
+    from block_scaled_precision_02_amd import inputs
+    x = np.random.default_rng(11).standard_normal((9, 384)).astype(np.float32)
+    X = inputs.bf16_bits(x)
+    xb = (X.astype(np.uint32) << 16).view(np.float32)
+    codes, s = inputs.block_quantise_e4m3(xb, 1)
+    Q, S = orc.quant_f8_block(X)
+    np.testing.assert_array_equal(S.view(np.uint32), s.view(np.uint32))
+    diff = Q != codes
+    assert np.all((Q[diff] == 0x80) & (codes[diff] == 0))
