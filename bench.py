@@ -272,6 +272,14 @@ def bench_quant(args):
         def run(i):
             return L.qgemm_quant_f8_pertoken(xs[i % R].data_ptr(), K, Q.data_ptr(), K, S.data_ptr(), M, K, sp)
         dtype = "bf16->e4m3"
+    elif args.quant == "f8_block":
+        Q = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+        S = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+        nbytes = 2 * M * K + M * K + 4 * M * (K // 128)
+
+        def run(i):
+            return L.qgemm_quant_f8_block(xs[i % R].data_ptr(), K, Q.data_ptr(), K, S.data_ptr(), K // 128, M, K, sp)
+        dtype = "bf16->e4m3 (1x128 blocks)"
     else:
         fmt = 0 if args.quant == "mxfp8" else 1
         row = K if fmt == 0 else K // 2
@@ -315,6 +323,8 @@ def bench_quant(args):
         t0 = time.perf_counter()
         if args.quant == "f8":
             oracle.quant_f8_pertoken(X[:rows])
+        elif args.quant == "f8_block":
+            oracle.quant_f8_block(X[:rows])
         else:
             oracle.quant_mx(0 if args.quant == "mxfp8" else 1, X[:rows])
         t = time.perf_counter() - t0
@@ -341,7 +351,7 @@ def main():
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--prepacked", action="store_true",
                     help="B prepacked once (qgemm_prepack_b) and the _prepacked entry points timed")
-    ap.add_argument("--quant", default=None, choices=["f8", "mxfp8", "mxfp4"],
+    ap.add_argument("--quant", default=None, choices=["f8", "mxfp8", "mxfp4", "f8_block"],
                     help="instead: time the activation quantiser on the A shape of that workload")
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
                     help="instead: write profiles/traffic.json from the rocprofv3 FETCH_SIZE / "

@@ -20,6 +20,7 @@ call raises.
     qgemm_f8_blockscale_prepacked(A, Bp, scale_a, scale_b, bias=None, out=None)
     qgemm_mx_prepacked(fmt, A, Bp, scale_a, scale_b, b_layout, bias=None, out=None)
     qgemm_quant_f8_pertoken(X, out=None, scale=None)      -> (Q, scale)
+    qgemm_quant_f8_block(X, out=None, scales=None)        -> (Q, S)
     qgemm_quant_mx(fmt, X, out=None, scales=None)         -> (Q, S)
 
 Operands are [rows, K] with unit stride along K (row stride may exceed the
@@ -50,7 +51,7 @@ QGEMM_MX_BSCALE_32x32 = 32
 EXPORTS = ("qgemm_i8_rowwise", "qgemm_i8_acc_i32", "qgemm_f8_pertoken", "qgemm_f8_blockscale", "qgemm_mx", "qgemm_mx_mixed",
            "qgemm_prepacked_b_bytes", "qgemm_prepack_b", "qgemm_i8_rowwise_prepacked",
            "qgemm_f8_pertoken_prepacked", "qgemm_f8_blockscale_prepacked", "qgemm_mx_prepacked",
-           "qgemm_quant_f8_pertoken", "qgemm_quant_mx",
+           "qgemm_quant_f8_pertoken", "qgemm_quant_f8_block", "qgemm_quant_mx",
            "qgemm_last_error", "qgemm_status_string", "qgemm_select_tile",
            "qgemm_tile_rows", "qgemm_force_tile")
 
@@ -98,6 +99,8 @@ def lib():
                                      _I64, _P]
     L.qgemm_quant_f8_pertoken.restype = st
     L.qgemm_quant_f8_pertoken.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64, _P]
+    L.qgemm_quant_f8_block.restype = st
+    L.qgemm_quant_f8_block.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _P]
     L.qgemm_quant_mx.restype = st
     L.qgemm_quant_mx.argtypes = [ctypes.c_int, _P, _I64, _P, _I64, _P, _I64, _I64, _I64, _P]
     L.qgemm_last_error.restype = ctypes.c_char_p
@@ -430,6 +433,28 @@ def qgemm_quant_f8_pertoken(X, out=None, scale=None, stream=None):
         _check(lib().qgemm_quant_f8_pertoken(_ptr(X), ldx, _ptr(out), _ld_bytes(out, K), _ptr(scale), M, K,
                                              _stream(X.device, stream)))
     return out, scale
+
+
+def qgemm_quant_f8_block(X, out=None, scales=None, stream=None):
+    """Blockscale e4m3 quantiser: X [M, K] bf16 (K % 128 == 0) -> (Q uint8
+    [M, K] e4m3 codes, S fp32 [M, K/128]), the A operand and scale_a of
+    qgemm_f8_blockscale."""
+    torch = _torch()
+    ldx = _activations(X)
+    M, K = X.shape
+    if K % 128:
+        raise ValueError(f"K={K} is not a multiple of 128")
+    out = _codes_out(out, (M, K), X.device, "out")
+    if scales is None:
+        scales = torch.empty((M, K // 128), dtype=torch.float32, device=X.device)
+    if (scales.dtype != torch.float32 or tuple(scales.shape) != (M, K // 128) or scales.device != X.device
+            or (M > 1 and scales.stride(1) != 1)):
+        raise ValueError(f"scales must be float32 [{M}, {K // 128}] with unit stride along K/128 on {X.device}")
+    lds = scales.stride(0) if M > 1 else K // 128
+    with torch.cuda.device(X.device):
+        _check(lib().qgemm_quant_f8_block(_ptr(X), ldx, _ptr(out), _ld_bytes(out, K), _ptr(scales), lds, M, K,
+                                          _stream(X.device, stream)))
+    return out, scales
 
 
 def qgemm_quant_mx(fmt, X, out=None, scales=None, stream=None):

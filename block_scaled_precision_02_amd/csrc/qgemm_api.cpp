@@ -724,6 +724,25 @@ qgemm_status qgemm_quant_f8_pertoken(const uint16_t *X, int64_t ldx, uint8_t *Q,
     return finish(launch_quant_f8_pertoken(X, ldx, Q, ldq, scale, (int)M, (int)K, (hipStream_t)stream));
 }
 
+qgemm_status qgemm_quant_f8_block(const uint16_t *X, int64_t ldx, uint8_t *Q, int64_t ldq, float *S, int64_t lds,
+                                  int64_t M, int64_t K, void *stream)
+{
+    TRY(check_quant(X, ldx, Q, ldq, M, K, K));
+    if (K % 128)
+        return fail(QGEMM_ERR_BAD_SHAPE, "K=%lld is not a multiple of 128", (long long)K);
+    if (M == 0)
+        return QGEMM_OK;
+    if (!S)
+        return fail(QGEMM_ERR_NULL_POINTER, "S is NULL");
+    if (!aligned(S, 4))
+        return fail(QGEMM_ERR_BAD_LAYOUT, "S is not 4-byte aligned");
+    if (lds < K / 128 || lds >= LD_LIMIT)
+        return fail(QGEMM_ERR_BAD_LAYOUT, "lds=%lld elements: need >= K/128=%lld, below 2^31", (long long)lds,
+                    (long long)(K / 128));
+    TRY(check_device());
+    return finish(launch_quant_f8_block(X, ldx, Q, ldq, S, lds, (int)M, (int)K, (hipStream_t)stream));
+}
+
 qgemm_status qgemm_quant_mx(qgemm_mx_fmt fmt, const uint16_t *X, int64_t ldx, void *Q, int64_t ldq, uint8_t *S,
                             int64_t lds, int64_t M, int64_t K, void *stream)
 {

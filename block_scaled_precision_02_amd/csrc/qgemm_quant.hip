@@ -25,6 +25,10 @@
 //    amax, and a subnormal or zero amax gives code 0 either way, so the code
 //    is max(E - emax, 0).  Scaling by 2^(127 - code) is exact (a power of two,
 //    no overflow since |x| <= amax < 2^(E - 126)).
+//  * Blockscale e4m3 (one fp32 scale per 128 elements of a row, the operand of
+//    the blockscale GEMM): sixteen lanes per block, one 16-byte load each and
+//    four blocks per thread loaded first; the block max by four shuffles, then
+//    the per-token rule within the block (scale amax/448, IEEE division).
 //  * The codes are written with non-temporal stores (whole rows per wave;
 //    one MI355X: per-token 4096x7168 +5%, MX e4m3 16384x2048 +10%, e2m1
 //    unchanged); non-temporal loads of X were slower.
@@ -214,6 +218,45 @@ __global__ void __launch_bounds__(256) quant_mx_kernel(const uint16_t *X, int64_
     }
 }
 
+// ------------------------------------------------------------ blockscale e4m3
+
+// Piece g of the launch (8 elements, one 16-byte load) is piece g % 16 of
+// block g / 16 of the launch's rows: row (g / 16) / kb, block (g / 16) % kb.
+// Thread t of workgroup w takes the pieces w * 1024 + t + 256 u, u < 4, so a
+// block's sixteen pieces sit on sixteen neighbouring lanes (an aligned group).
+__global__ void __launch_bounds__(256) quant_f8_block_kernel(const uint16_t *X, int64_t ldx, uint8_t *Q,
+                                                             int64_t ldq, float *S, int64_t lds, unsigned rows,
+                                                             unsigned kb)
+{
+    const unsigned total = rows * kb * 16u;
+    const unsigned base = blockIdx.x * (256u * MX_U) + threadIdx.x, part = threadIdx.x & 15u;
+    u32x4q w[MX_U];
+    unsigned row[MX_U], b[MX_U];
+#pragma unroll
+    for (int u = 0; u < MX_U; ++u) {
+        const unsigned g = base + 256u * u, blk = g >> 4;
+        row[u] = blk / kb;
+        b[u] = blk - row[u] * kb;
+        // a block's sixteen lanes agree on g < total (total is a multiple of 16)
+        w[u] = g < total ? *(const u32x4q *)(X + (int64_t)row[u] * ldx + 128 * b[u] + 8 * part)
+                         : u32x4q{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < MX_U; ++u) {
+        float amax = piece_amax(w[u]);
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1)
+            amax = fmaxf(amax, __shfl_xor(amax, off));
+        if (base + 256u * u >= total)
+            continue;
+        const float s = amax / 448.0f;
+        uint8_t *qrow = Q + (int64_t)row[u] * ldq;
+        __builtin_nontemporal_store(pertoken_codes(w[u], s), (u32x2q *)(qrow + 128 * b[u] + 8 * part));
+        if (part == 0)
+            S[(int64_t)row[u] * lds + b[u]] = s;
+    }
+}
+
 // ------------------------------------------------------------ launchers
 
 hipError_t launch_quant_f8_pertoken(const uint16_t *X, int64_t ldx, uint8_t *Q, int64_t ldq, float *scale,
@@ -222,6 +265,26 @@ hipError_t launch_quant_f8_pertoken(const uint16_t *X, int64_t ldx, uint8_t *Q, 
     hipLaunchKernelGGL(quant_f8_pertoken_kernel, dim3((unsigned)M), dim3(PT_THREADS), 0, s, X, ldx, Q, ldq, scale,
                        M, K);
     return hipGetLastError();
+}
+
+hipError_t launch_quant_f8_block(const uint16_t *X, int64_t ldx, uint8_t *Q, int64_t ldq, float *S, int64_t lds,
+                                 int M, int K, hipStream_t s)
+{
+    const int64_t kb = K / 128;
+    // rows per launch: keep rows * kb * 16 pieces (rounded up to whole
+    // workgroups) below 2^31
+    const int64_t per_wg = 256 * MX_U;
+    const int64_t max_rows = (((int64_t)1 << 31) - per_wg) / (16 * kb);
+    for (int64_t r0 = 0; r0 < M; r0 += max_rows) {
+        const int64_t rows = M - r0 < max_rows ? M - r0 : max_rows;
+        const unsigned grid = (unsigned)((rows * kb * 16 + per_wg - 1) / per_wg);
+        hipLaunchKernelGGL(quant_f8_block_kernel, dim3(grid), dim3(256), 0, s, X + r0 * ldx, ldx, Q + r0 * ldq, ldq,
+                           S + r0 * lds, lds, (unsigned)rows, (unsigned)kb);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_quant_mx(int fmt, const uint16_t *X, int64_t ldx, uint8_t *Q, int64_t ldq, uint8_t *S,

@@ -157,7 +157,8 @@ def bf16_bits(x):
 # ------------------------------------------------------------ activations
 
 # Activation shapes of the quantisers: the A operand of each GEMM workload.
-QUANT_SHAPES = {"f8": ("f8_ptpc", 4096, 7168), "mxfp8": ("mxfp8", 16384, 2048), "mxfp4": ("mxfp4", 8192, 8192)}
+QUANT_SHAPES = {"f8": ("f8_ptpc", 4096, 7168), "mxfp8": ("mxfp8", 16384, 2048), "mxfp4": ("mxfp4", 8192, 8192),
+                "f8_block": ("f8_block", 16384, 2048)}
 
 
 def make_activations(M, K, seed=300, rot=0, outlier_cols=8):

@@ -265,6 +265,21 @@ qgemm_status qgemm_quant_f8_pertoken(const uint16_t *X, int64_t ldx, uint8_t *Q,
 qgemm_status qgemm_quant_mx(qgemm_mx_fmt fmt, const uint16_t *X, int64_t ldx, void *Q, int64_t ldq, uint8_t *S,
                             int64_t lds, int64_t M, int64_t K, void *stream);
 
+/* Blockscale e4m3 quantiser: bf16 activations -> the A operand and A scales
+ * of qgemm_f8_blockscale (the per-token rule applied to each 128-element
+ * block of a row; the page names the blockscale GEMM, the block reading is
+ * the library's).
+ *   X      [M, K] bf16 bits, row stride ldx elements (multiple of 8)
+ *   Q      [M, K] e4m3fn codes (output), row stride ldq bytes (multiple of 16)
+ *   S      [M, K/128] fp32 scales (output), row stride lds elements (>= K/128)
+ * Per row m and block b: S[m,b] = fp32(amax / 448) over the block's |x|,
+ * Q = e4m3(fp32(x / S[m,b])) (nearest, ties to even, saturating, sign kept;
+ * an all-zero block gets scale 0 and keeps its signed zeros).  K must be a
+ * multiple of 128 (QGEMM_ERR_BAD_SHAPE); X and Q 16-byte aligned, S 4-byte
+ * aligned; outputs must not overlap X. */
+qgemm_status qgemm_quant_f8_block(const uint16_t *X, int64_t ldx, uint8_t *Q, int64_t ldq, float *S, int64_t lds,
+                                  int64_t M, int64_t K, void *stream);
+
 /* Text of the last non-OK status returned on the calling thread ("" if none). */
 const char *qgemm_last_error(void);
 

@@ -341,3 +341,15 @@ def test_blockscale_prepacked_rejects_and_passes(monkeypatch):
     monkeypatch.setenv("QGEMM_FAKE_ARCH", "gfx1201")
     assert L.qgemm_f8_blockscale_prepacked(FAKE, 512, FAKE2, FAKE3, FAKE3, None, FAKE, 64, 64, 64, 512,
                                            None) == q.QGEMM_ERR_UNSUPPORTED_DEVICE
+
+
+def test_quant_f8_block_rejects(monkeypatch):
+    L = q.lib()
+    f = L.qgemm_quant_f8_block
+    assert f(FAKE, 96, FAKE2, 96, FAKE3, 1, 4, 96, None) == q.QGEMM_ERR_BAD_SHAPE      # K % 128
+    assert f(FAKE, 256, FAKE2, 256, None, 2, 4, 256, None) == q.QGEMM_ERR_NULL_POINTER
+    assert f(FAKE, 256, FAKE2, 256, FAKE3, 1, 4, 256, None) == q.QGEMM_ERR_BAD_LAYOUT  # lds < K/128
+    assert f(FAKE, 256, FAKE2, 256, FAKE3 + 2, 2, 4, 256, None) == q.QGEMM_ERR_BAD_LAYOUT
+    assert f(FAKE, 256, FAKE2, 256, FAKE3, 2, 0, 256, None) == q.QGEMM_OK
+    monkeypatch.setenv("QGEMM_FAKE_ARCH", "gfx1201")
+    assert f(FAKE, 256, FAKE2, 256, FAKE3, 2, 4, 256, None) == q.QGEMM_ERR_UNSUPPORTED_DEVICE

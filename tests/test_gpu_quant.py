@@ -118,7 +118,27 @@ def test_quant_mx_bit_exact(orc, fmt, M, K):
     assert (got_s[:M, K // 32:] == 0x5A).all() and (got_s[M:] == 0x5A).all(), "wrote outside S"
 
 
-@pytest.mark.parametrize("which", ["f8", "mxfp8", "mxfp4"])
+BLOCK_SHAPES = [(3, 128), (17, 7168), (5, 8192), (64, 256), (300, 640), (1, 65536)]
+
+
+@pytest.mark.parametrize("M,K", BLOCK_SHAPES)
+def test_quant_f8_block_bit_exact(orc, M, K):
+    _say(f"[quant] f8 block M={M} K={K}")
+    X = _inputs(M, K, seed=M * 139 + K)
+    qbuf = torch.full((M + 2, K + 32), 0xA5, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((M + 2, K // 128 + 3), float("nan"), dtype=torch.float32, device="cuda")
+    q.qgemm_quant_f8_block(_dev(X, ld=K + 64), out=qbuf[:M, :K], scales=sbuf[:M, :K // 128])
+    torch.cuda.synchronize()
+    Qr, Sr = orc.quant_f8_block(X)
+    got_q = qbuf.cpu().numpy()
+    got_s = sbuf.cpu().numpy()
+    assert np.array_equal(got_q[:M, :K], Qr), f"{np.count_nonzero(got_q[:M, :K] != Qr)} codes differ"
+    assert np.array_equal(got_s[:M, :K // 128].view(np.uint32), Sr.view(np.uint32))
+    assert (got_q[:M, K:] == 0xA5).all() and (got_q[M:] == 0xA5).all(), "wrote outside Q"
+    assert np.isnan(got_s[:M, K // 128:]).all() and np.isnan(got_s[M:]).all(), "wrote outside S"
+
+
+@pytest.mark.parametrize("which", ["f8", "mxfp8", "mxfp4", "f8_block"])
 def test_quant_full_workload_shape(orc, which):
     """The activation shape of each GEMM workload, as the benchmark times it;
     every code and scale compared."""
@@ -129,6 +149,10 @@ def test_quant_full_workload_shape(orc, which):
     if which == "f8":
         Qd, sd = q.qgemm_quant_f8_pertoken(Xd)
         Qr, sr = orc.quant_f8_pertoken(X)
+        assert np.array_equal(sd.cpu().numpy().view(np.uint32), sr.view(np.uint32))
+    elif which == "f8_block":
+        Qd, sd = q.qgemm_quant_f8_block(Xd)
+        Qr, sr = orc.quant_f8_block(X)
         assert np.array_equal(sd.cpu().numpy().view(np.uint32), sr.view(np.uint32))
     else:
         fmt = q.QGEMM_MX_E4M3 if which == "mxfp8" else q.QGEMM_MX_E2M1
@@ -161,3 +185,19 @@ def test_quantised_operands_feed_the_gemms(orc):
         (QA, SA), (QB, SB) = orc.quant_mx(fmt, Xa), orc.quant_mx(fmt, Xb)
         ref, _, absdot = orc.mx(fmt, QA, QB, SA, SB, 1, K)
         parity.compare(dict(kind="mx", M=M, N=N, K=K), C, ref, absdot, f"quantised mx {fmt}")
+
+
+def test_quantised_blockscale_operand_feeds_the_gemm(orc):
+    """Activations quantised per 1x128 block on the GPU feed the blockscale
+    GEMM (weights in 128x128 blocks from the input recipe); compared with the
+    oracle GEMM on the oracle's quantisation of the same bf16 values."""
+    M, N, K = 200, 300, 1024
+    Xa = inputs.make_activations(M, K, seed=43)
+    qa, sa = q.qgemm_quant_f8_block(torch.from_numpy(Xa.view(np.int16)).cuda())
+    xb = np.random.default_rng(44).standard_normal((N, K)).astype(np.float32)
+    B, sb = inputs.block_quantise_e4m3(xb, 128)
+    C = parity.bits(q.qgemm_f8_blockscale(qa, parity.dev(B), sa, parity.dev(sb)))
+    QA, SA = orc.quant_f8_block(Xa)
+    assert np.array_equal(qa.cpu().numpy(), QA)
+    ref, _, absdot = orc.f8_blockscale(QA, B, SA, sb)
+    parity.compare(dict(kind="f8b", M=M, N=N, K=K), C, ref, absdot, "quantised blockscale")
