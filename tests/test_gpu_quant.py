@@ -201,3 +201,50 @@ def test_quantised_blockscale_operand_feeds_the_gemm(orc):
     assert np.array_equal(qa.cpu().numpy(), QA)
     ref, _, absdot = orc.f8_blockscale(QA, B, SA, sb)
     parity.compare(dict(kind="f8b", M=M, N=N, K=K), C, ref, absdot, "quantised blockscale")
+
+
+def _near_midpoint_rows(n_scales=6000, seed=12):
+    """Rows of 128 bf16 values: element 0 is the row's amax (so the scale is
+    s = fp32(amax / 448), an inexact quotient), the rest are bf16 values x
+    whose binary32 quotient x / s lies within 16 units in the last place of
+    an e4m3 rounding midpoint (found by search), or of the e4m3 subnormal
+    boundary; filler below amax elsewhere.  Returns (rows, hits)."""
+    rng = np.random.default_rng(seed)
+    # every positive bf16 value from 2^-14 up to 2^7
+    allv = (np.arange(0x3880, 0x4300, dtype=np.uint32) << 16).view(np.float32)
+    rows, hits = [], 0
+    for amax in (rng.uniform(0.5, 100.0, n_scales)).astype(np.float32):
+        amax = (np.array([amax]).astype(np.float32).view(np.uint32) & 0xFFFF0000).view(np.float32)[0]
+        s = np.float32(amax) / np.float32(448.0)
+        cand = allv[(allv <= amax) & (allv >= s * np.float32(2.0 ** -6))]
+        qv = (cand / s).astype(np.float32)
+        low = qv.view(np.uint32) & 0xFFFFF
+        sel = cand[np.abs(low.astype(np.int64) - 0x80000) <= 16]
+        if len(sel) == 0:
+            continue
+        hits += len(sel)
+        row = (rng.uniform(-1, 1, 128) * amax).astype(np.float32)
+        row[0] = amax
+        k = min(len(sel), 127)
+        row[1:1 + k] = sel[:k] * np.where(rng.random(k) < 0.5, -1.0, 1.0).astype(np.float32)
+        rows.append(row)
+    return _bf16(np.stack(rows)), hits
+
+
+def test_quant_quotients_near_e4m3_midpoints(orc):
+    """The per-token and blockscale quantisers reach the code of the IEEE
+    quotient without dividing every element; quotients near a rounding
+    midpoint take the division.  Rows built so that every element's quotient
+    sits within 16 units of a midpoint: codes bit-exact against the oracle."""
+    X, hits = _near_midpoint_rows()
+    assert hits >= 50, hits
+    _say(f"[quant] near-midpoint quotients: {hits} in {X.shape[0]} rows")
+    Xd = torch.from_numpy(X.view(np.int16)).cuda()
+    Qd, sd = q.qgemm_quant_f8_pertoken(Xd)
+    Qr, sr = orc.quant_f8_pertoken(X)
+    assert np.array_equal(sd.cpu().numpy().view(np.uint32), sr.view(np.uint32))
+    assert np.array_equal(Qd.cpu().numpy(), Qr), f"{np.count_nonzero(Qd.cpu().numpy() != Qr)} codes differ"
+    Qd, sd = q.qgemm_quant_f8_block(Xd)
+    Qr, sr = orc.quant_f8_block(X)
+    assert np.array_equal(sd.cpu().numpy().view(np.uint32), sr.view(np.uint32))
+    assert np.array_equal(Qd.cpu().numpy(), Qr), f"{np.count_nonzero(Qd.cpu().numpy() != Qr)} codes differ"
