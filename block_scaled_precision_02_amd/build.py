@@ -1,6 +1,7 @@
 """Build libqgemm.so in-tree: hipcc, gfx950 only.
 
-    python -m block_scaled_precision_02_amd.build
+    python -m block_scaled_precision_02_amd.build              # build libqgemm.so
+    python -m block_scaled_precision_02_amd.build --resources  # per-kernel register / LDS audit
 
 Every HIP source under csrc/ compiles to an object in parallel, then one
 shared library is linked next to this file.  Flags: -O3, no fast-math, no
@@ -53,6 +54,62 @@ def build(jobs=None):
     return LIB
 
 
+# ------------------------------------------------------------ resource audit
+
+_REMARKS = (("VGPRs", "VGPRs"), ("AGPRs", "AGPRs"), ("TotalSGPRs", "SGPRs"), ("ScratchSize [bytes/lane]", "scratch B/lane"),
+            ("VGPRs Spill", "VGPR spill"), ("SGPRs Spill", "SGPR spill"), ("LDS Size [bytes/block]", "LDS B"),
+            ("Occupancy [waves/SIMD]", "waves/SIMD"))
+
+
+def _audit(src):
+    import re
+    cmd = ([HIPCC] + FLAGS + EXTRA_FLAGS.get(src, []) + ["-Rpass-analysis=kernel-resource-usage", "-c",
+           os.path.join(CSRC, src), "-o", os.path.join(BUILD, src + ".audit.o")])
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}")
+    rows, kern, vals = [], None, {}
+    for line in r.stderr.splitlines():
+        m = re.search(r"remark:\s+(.*?):\s+(\S+)\s+\[-Rpass-analysis", line)
+        if not m:
+            continue
+        key, val = m.group(1).strip(), m.group(2)
+        if key == "Function Name":
+            if kern:
+                rows.append((kern, vals))
+            kern, vals = val, {}
+        else:
+            vals[key] = val
+    if kern:
+        rows.append((kern, vals))
+    return src, rows
+
+
+def resources(out=sys.stdout):
+    """Compile every HIP source with the compiler's per-kernel resource
+    remarks and print one markdown row per kernel instantiation."""
+    import shutil
+    os.makedirs(BUILD, exist_ok=True)
+    filt = shutil.which("llvm-cxxfilt") or shutil.which("c++filt")
+    srcs = [s for s in SOURCES if s.endswith(".hip")]
+    with concurrent.futures.ThreadPoolExecutor(min(len(srcs), os.cpu_count() or 4, 16)) as ex:
+        results = list(ex.map(_audit, srcs))
+    print("| Source | Kernel | " + " | ".join(h for _, h in _REMARKS) + " |", file=out)
+    print("|---|---|" + "---|" * len(_REMARKS), file=out)
+    for src, rows in results:
+        names = [k for k, _ in rows]
+        if filt and names:
+            dem = subprocess.run([filt], input="\n".join(names), capture_output=True, text=True).stdout.splitlines()
+            if len(dem) == len(names):
+                names = dem
+        for name, (_, vals) in zip(names, rows):
+            name = name.replace("(qgemm::Params)", "").replace("void qgemm::", "").strip()
+            print(f"| {src} | `{name}` | " + " | ".join(vals.get(k, "-") for k, _ in _REMARKS) + " |", file=out)
+
+
 if __name__ == "__main__":
+    if len(sys.argv) > 1 and sys.argv[1] == "--resources":
+        resources()
+        sys.exit(0)
     print(build())
     sys.exit(0)
