@@ -334,6 +334,43 @@ def bench_quant(args):
     return res
 
 
+def time_graph(d, sets, out, args):
+    """args.graph calls (cycling over the input sets) captured in one HIP graph
+    on a side stream, replayed; per-call time = replay time / calls.  Every
+    replay's output must equal the eager call's on the same last input set."""
+    import torch
+    n = args.graph
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    run = Launcher(d, sets, out, side.cuda_stream, prepacked=args.prepacked)
+    with torch.cuda.stream(side):
+        run(n - 1)                                   # eager: the graph's last call, same inputs
+    side.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for i in range(n):
+            run(i)
+    replays = max(3, args.steps // n)
+    for _ in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, eager):
+            raise RuntimeError("graph replay output differs from the eager call")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    ev0.record(stream)
+    for _ in range(replays):
+        g.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / (replays * n)
+    return {"calls_per_graph": n, "replays": replays, "ms_per_call": round(ms, 6),
+            "rate": round(2.0 * d["M"] * d["N"] * d["K"] / (ms * 1e-3) / 1e12, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -353,6 +390,9 @@ def main():
                     help="B prepacked once (qgemm_prepack_b) and the _prepacked entry points timed")
     ap.add_argument("--quant", default=None, choices=["f8", "mxfp8", "mxfp4", "f8_block"],
                     help="instead: time the activation quantiser on the A shape of that workload")
+    ap.add_argument("--graph", type=int, default=0, metavar="N",
+                    help="also time N calls captured in one HIP graph and replayed (the host-side checks and the "
+                         "per-call launch overhead apart); the replays' output is checked against the eager call's")
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
                     help="instead: write profiles/traffic.json from the rocprofv3 FETCH_SIZE / "
                          "WRITE_SIZE runs under DIR (no GPU needed)")
@@ -455,6 +495,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if args.graph:
+        res["config"]["graph"] = time_graph(d0, sets, out, args)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(d0, args.cpu_seconds)
