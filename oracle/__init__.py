@@ -22,6 +22,8 @@ Functions follow the definitions in ``qgemm_oracle.c``:
                   in ``qgemm_oracle.c``).
   pack_b       -- the prepacked weight layout of the ``_prepacked`` GEMM entry
                   points (defined in ``qgemm_oracle.c``).
+  pack_b32     -- the prepacked layout of an e2m1 B under e4m3 A (32-row
+                  groups of 32-byte pieces; ``qgemm_mx_mixed_prepacked``).
   quant_f8_pertoken, quant_f8_block, quant_mx
                -- the activation quantisers producing those operands from
                   bf16 (ROCm/mori PR #806, What: the quantiser's [M, K/32]
@@ -85,6 +87,8 @@ def _load():
     lib.orc_quant_f8_block.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64, _I64]
     lib.orc_quant_mx.restype = ctypes.c_int
     lib.orc_quant_mx.argtypes = [ctypes.c_int, _P, _I64, _P, _I64, _P, _I64, _I64, _I64]
+    lib.orc_pack_b32.restype = None
+    lib.orc_pack_b32.argtypes = [_P, _I64, _I64, _I64, _P]
     lib.orc_pack_b.restype = None
     lib.orc_pack_b.argtypes = [_P, _I64, _I64, _I64, _P]
     lib.orc_i8_rowwise.restype = ctypes.c_int
@@ -329,4 +333,15 @@ def pack_b(B):
     assert row % 64 == 0
     out = np.empty(((N + 15) // 16) * 16 * row, np.uint8)
     _load().orc_pack_b(_ptr(B), row, N, row, _ptr(out))
+    return out
+
+
+def pack_b32(B):
+    """B [N, row_bytes] bytes (row_bytes % 32 == 0) -> the prepacked layout of
+    an e2m1 B under e4m3 A, uint8 [ceil(N/32) * 32 * row_bytes]."""
+    B = _c(B, np.uint8)
+    N, row = B.shape
+    assert row % 32 == 0
+    out = np.empty(((N + 31) // 32) * 32 * row, np.uint8)
+    _load().orc_pack_b32(_ptr(B), row, N, row, _ptr(out))
     return out

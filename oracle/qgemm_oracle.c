@@ -567,6 +567,27 @@ void orc_pack_b(const uint8_t *B, int64_t ldb, int64_t N, int64_t row_bytes, uin
             }
 }
 
+/* The prepacked layout of an e2m1 B under e4m3 A (the mixed MX GEMM, whose
+ * LDS-fetch stages hold 32-byte B rows): ceil(N/32) groups of 32 rows; group
+ * R is row_bytes/32 blocks of 1 KB; block t holds bytes 32t .. 32t + 31 of rows
+ * 32R .. 32R + 31, its 16-byte slot p being row 32R + p/2, bytes 32t + 16c ..
+ * 32t + 16c + 15 with c = (p mod 2) XOR ((p / 16) mod 2).  Rows at or past N
+ * are zeros.  row_bytes % 32 == 0.
+ * Bp[((R*nst + t)*64 + p)*16 + b] = B[32R + p/2][32t + 16c + b]. */
+void orc_pack_b32(const uint8_t *B, int64_t ldb, int64_t N, int64_t row_bytes, uint8_t *Bp)
+{
+    const int64_t nst = row_bytes / 32, groups = (N + 31) / 32;
+    for (int64_t R = 0; R < groups; ++R)
+        for (int64_t t = 0; t < nst; ++t)
+            for (int p = 0; p < 64; ++p) {
+                const int64_t row = 32 * R + p / 2;
+                const int c = (p % 2) ^ ((p / 16) % 2);
+                uint8_t *dst = Bp + ((R * nst + t) * 64 + p) * 16;
+                for (int b = 0; b < 16; ++b)
+                    dst[b] = row < N ? B[row * ldb + 32 * t + 16 * c + b] : 0;
+            }
+}
+
 /* ------------------------------------------------- array forms for tests */
 
 void orc_enc_e4m3_array(const double *in, uint8_t *out, int64_t n)

@@ -71,3 +71,50 @@ def test_every_byte_once(orc, N, row):
         U.reshape(G, 16, row)[:, rows[:, None], 64 * t + 16 * chunks[:, None] + np.arange(16)] = blocks[:, t]
     assert np.array_equal(U[:N], B)
     assert (U[N:] == 0).all()
+
+
+# ------------------------------------------ e2m1 B under e4m3 A (32-byte rows)
+
+def test_b32_hand_worked_positions(orc):
+    """Slot p of block (R, t) holds row 32R + p/2, bytes 32t + 16((p mod 2)
+    XOR ((p/16) mod 2)) .. +15."""
+    N, row = 40, 128             # 2 groups (the second 24 rows short), 4 blocks per group
+    B = _distinct(N, row)
+    Bp = orc.pack_b32(B)
+    assert Bp.size == 64 * 128
+    piece = lambda i: Bp[16 * i:16 * i + 16]
+    # block (0, 0): slot 0 -> row 0 chunk 0, slot 1 -> row 0 chunk 1, slot 2 -> row 1 chunk 0
+    assert np.array_equal(piece(0), B[0, 0:16])
+    assert np.array_equal(piece(1), B[0, 16:32])
+    assert np.array_equal(piece(2), B[1, 0:16])
+    # slot 16 -> row 8, chunk 0 ^ 1 = 1; slot 17 -> row 8 chunk 0; slot 33 -> row 16, chunk 1 ^ 0 = 1
+    assert np.array_equal(piece(16), B[8, 16:32])
+    assert np.array_equal(piece(17), B[8, 0:16])
+    assert np.array_equal(piece(33), B[16, 16:32])
+    # slot 63 -> row 31, chunk 1 ^ 1 = 0
+    assert np.array_equal(piece(63), B[31, 0:16])
+    # block (0, 2): bytes 64..95; slot 128 + 18 -> row 9, chunk 0 ^ 1 = 1 -> bytes 80..95
+    assert np.array_equal(piece(128 + 18), B[9, 80:96])
+    # group 1 after 4 blocks: slot 256 -> row 32 chunk 0; rows 40..63 are zeros (slots 16..63 of its blocks)
+    assert np.array_equal(piece(256), B[32, 0:16])
+    g1 = Bp[4 * 1024:].reshape(4, 64, 16)
+    assert (g1[:, 16:, :] == 0).all()
+
+
+@pytest.mark.parametrize("N,row", [(1, 32), (32, 32), (33, 64), (300, 256), (257, 1024)])
+def test_b32_every_byte_once(orc, N, row):
+    rng = np.random.default_rng(N * 3 + row)
+    B = rng.integers(0, 256, (N, row), dtype=np.uint8)
+    Bp = orc.pack_b32(B)
+    G = (N + 31) // 32
+    assert Bp.size == G * 32 * row
+    nst = row // 32
+    p = np.arange(64)
+    rows = p // 2
+    chunks = (p % 2) ^ ((p // 16) % 2)
+    blocks = Bp.reshape(G, nst, 64, 16)
+    U = np.zeros((G * 32, row), np.uint8)
+    for t in range(nst):
+        U.reshape(G, 32, row)[:, rows[:, None], 32 * t + 16 * chunks[:, None] + np.arange(16)] = blocks[:, t]
+    assert np.array_equal(U[:N], B)
+    assert (U[N:] == 0).all()
