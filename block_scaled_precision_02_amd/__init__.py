@@ -19,6 +19,8 @@ call raises.
     qgemm_f8_pertoken_prepacked(A, Bp, scale_a, scale_b, bias=None, out=None)
     qgemm_f8_blockscale_prepacked(A, Bp, scale_a, scale_b, bias=None, out=None)
     qgemm_mx_prepacked(fmt, A, Bp, scale_a, scale_b, b_layout, bias=None, out=None)
+    qgemm_prepack_b32(B, out=None)                        -> PackedB (the mixed GEMM's e2m1 B)
+    qgemm_mx_mixed_prepacked(fmt_a, fmt_b, A, Bp, scale_a, scale_b, b_layout, bias=None, out=None)
     qgemm_quant_f8_pertoken(X, out=None, scale=None)      -> (Q, scale)
     qgemm_quant_f8_block(X, out=None, scales=None)        -> (Q, S)
     qgemm_quant_mx(fmt, X, out=None, scales=None)         -> (Q, S)
@@ -49,6 +51,7 @@ QGEMM_MX_BSCALE_32x32 = 32
 
 # Every symbol include/qgemm.h declares.
 EXPORTS = ("qgemm_i8_rowwise", "qgemm_i8_acc_i32", "qgemm_f8_pertoken", "qgemm_f8_blockscale", "qgemm_mx", "qgemm_mx_mixed",
+           "qgemm_prepacked_b32_bytes", "qgemm_prepack_b32", "qgemm_mx_mixed_prepacked",
            "qgemm_prepacked_b_bytes", "qgemm_prepack_b", "qgemm_i8_rowwise_prepacked",
            "qgemm_f8_pertoken_prepacked", "qgemm_f8_blockscale_prepacked", "qgemm_mx_prepacked",
            "qgemm_quant_f8_pertoken", "qgemm_quant_f8_block", "qgemm_quant_mx",
@@ -84,6 +87,13 @@ def lib():
     L.qgemm_mx_mixed.restype = st
     L.qgemm_mx_mixed.argtypes = [ctypes.c_int, ctypes.c_int, _P, _I64, _P, _I64, _P, _P, ctypes.c_int, _P, _P,
                                  _I64, _I64, _I64, _I64, _P]
+    L.qgemm_prepacked_b32_bytes.restype = _I64
+    L.qgemm_prepacked_b32_bytes.argtypes = [_I64, _I64]
+    L.qgemm_prepack_b32.restype = st
+    L.qgemm_prepack_b32.argtypes = [_P, _I64, _I64, _I64, _P, _P]
+    L.qgemm_mx_mixed_prepacked.restype = st
+    L.qgemm_mx_mixed_prepacked.argtypes = [ctypes.c_int, ctypes.c_int, _P, _I64, _P, _P, _P, ctypes.c_int, _P, _P,
+                                           _I64, _I64, _I64, _I64, _P]
     L.qgemm_prepacked_b_bytes.restype = _I64
     L.qgemm_prepacked_b_bytes.argtypes = [_I64, _I64]
     L.qgemm_prepack_b.restype = st
@@ -489,8 +499,8 @@ class PackedB:
     qgemm_prepacked_b_bytes(N, row_bytes) bytes), the row count N and the
     row length in bytes of the B it was made from."""
 
-    def __init__(self, data, N, row_bytes):
-        self.data, self.N, self.row_bytes = data, N, row_bytes
+    def __init__(self, data, N, row_bytes, group_rows=16):
+        self.data, self.N, self.row_bytes, self.group_rows = data, N, row_bytes, group_rows
 
 
 def qgemm_prepack_b(B, out=None, stream=None):
@@ -511,8 +521,56 @@ def qgemm_prepack_b(B, out=None, stream=None):
     return PackedB(out, N, row)
 
 
+def qgemm_prepack_b32(B, out=None, stream=None):
+    """The mixed GEMM's e2m1 B [N, K/2] bytes (K/2 a multiple of 128) ->
+    PackedB in 32-row groups of 32-byte pieces, for qgemm_mx_mixed_prepacked."""
+    torch = _torch()
+    ldb = _operand(B, "B", (torch.uint8,))
+    N, row = B.shape
+    nbytes = lib().qgemm_prepacked_b32_bytes(N, row)
+    if nbytes < 0:
+        raise ValueError(f"B rows of {row} bytes cannot be prepacked (need a multiple of 128)")
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=B.device)
+    if out.numel() * out.element_size() != nbytes or not out.is_contiguous() or out.device != B.device:
+        raise ValueError(f"out must be a contiguous buffer of {nbytes} bytes on {B.device}")
+    with torch.cuda.device(B.device):
+        _check(lib().qgemm_prepack_b32(_ptr(B), ldb, N, row, _ptr(out), _stream(B.device, stream)))
+    return PackedB(out, N, row, group_rows=32)
+
+
+def qgemm_mx_mixed_prepacked(fmt_a, fmt_b, A, Bp, scale_a, scale_b, b_layout, bias=None, out=None, stream=None):
+    """The mixed MX GEMM (e4m3 A, e2m1 B) with B from qgemm_prepack_b32 -> bf16 [M, N]."""
+    torch = _torch()
+    lda = _operand(A, "A", (torch.uint8, torch.float8_e4m3fn))
+    M, K = A.shape
+    if fmt_a != QGEMM_MX_E4M3 or fmt_b != QGEMM_MX_E2M1:
+        raise ValueError("the prepacked mixed GEMM takes e4m3 A and e2m1 B")
+    if not isinstance(Bp, PackedB) or Bp.group_rows != 32:
+        raise ValueError("Bp must be a PackedB from qgemm_prepack_b32")
+    if Bp.row_bytes != K // 2:
+        raise ValueError(f"Bp was packed from rows of {Bp.row_bytes} bytes; K/2 = {K // 2}")
+    N = Bp.N
+    sdt = (torch.uint8,) + ((torch.float8_e8m0fnu,) if hasattr(torch, "float8_e8m0fnu") else ())
+    brows = -(-N // b_layout) if b_layout in (1, 32) else N
+    if scale_a is None or tuple(scale_a.shape) != (M, K // 32):
+        raise ValueError(f"scale_a must be [{M}, {K // 32}]")
+    if scale_b is None or tuple(scale_b.shape) != (brows, K // 32):
+        raise ValueError(f"scale_b must be [{brows}, {K // 32}]")
+    sa = _vector(scale_a.reshape(-1) if scale_a.is_contiguous() else scale_a, "scale_a", M * (K // 32), sdt)
+    sb = _vector(scale_b.reshape(-1) if scale_b.is_contiguous() else scale_b, "scale_b", brows * (K // 32), sdt)
+    bias = _bias(bias, N)
+    _same_device(A.device, Bp.data, sa, sb, bias)
+    out = _out(out, M, N, A.device, torch.bfloat16)
+    with torch.cuda.device(A.device):
+        _check(lib().qgemm_mx_mixed_prepacked(fmt_a, fmt_b, _ptr(A), lda, _ptr(Bp.data), _ptr(sa), _ptr(sb),
+                                              b_layout, _ptr(bias), _ptr(out), _ldc(out, N), M, N, K,
+                                              _stream(A.device, stream)))
+    return out
+
+
 def _packed(Bp, row):
-    if not isinstance(Bp, PackedB):
+    if not isinstance(Bp, PackedB) or Bp.group_rows != 16:
         raise ValueError("Bp must be a PackedB from qgemm_prepack_b")
     if Bp.row_bytes != row:
         raise ValueError(f"Bp was packed from rows of {Bp.row_bytes} bytes; A's rows are {row} bytes")

@@ -580,18 +580,21 @@ static qgemm_status mx_common(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes
     return finish(launch_mx4(tile, bias != nullptr, brows, svec, p, (hipStream_t)stream));
 }
 
-qgemm_status qgemm_mx_mixed(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *A, int64_t lda_bytes, const void *B,
-                            int64_t ldb_bytes, const uint8_t *scale_a, const uint8_t *scale_b,
-                            qgemm_mx_bscale b_layout, const uint16_t *bias, uint16_t *C, int64_t ldc, int64_t M,
-                            int64_t N, int64_t K, void *stream)
+static qgemm_status mx_mixed_common(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *A, int64_t lda_bytes,
+                                    const void *B, int64_t ldb_bytes, const uint8_t *scale_a, const uint8_t *scale_b,
+                                    qgemm_mx_bscale b_layout, const uint16_t *bias, uint16_t *C, int64_t ldc,
+                                    int64_t M, int64_t N, int64_t K, void *stream, bool packed)
 {
     const bool known_a = fmt_a == QGEMM_MX_E4M3 || fmt_a == QGEMM_MX_E2M1;
     const bool known_b = fmt_b == QGEMM_MX_E4M3 || fmt_b == QGEMM_MX_E2M1;
     if (!known_a || !known_b)
         return fail(QGEMM_ERR_BAD_FORMAT, "unknown MX element format %d / %d", (int)fmt_a, (int)fmt_b);
-    if (fmt_a == fmt_b)
+    if (fmt_a == fmt_b) {
+        if (packed)
+            return fail(QGEMM_ERR_BAD_FORMAT, "equal formats: use qgemm_mx_prepacked with qgemm_prepack_b's layout");
         return mx_common(fmt_a, A, lda_bytes, B, ldb_bytes, scale_a, scale_b, b_layout, bias, C, ldc, M, N, K, stream,
                          false);
+    }
     if (fmt_a != QGEMM_MX_E4M3)
         return fail(QGEMM_ERR_BAD_FORMAT, "e2m1 A with e4m3 B is not supported (e4m3 A with e2m1 B is)");
     if (b_layout != QGEMM_MX_BSCALE_1x32 && b_layout != QGEMM_MX_BSCALE_32x32)
@@ -603,7 +606,14 @@ qgemm_status qgemm_mx_mixed(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *
     if (M == 0 || N == 0)
         return QGEMM_OK;
     TRY(check_operand("A", A, lda_bytes, K));
-    TRY(check_operand("B", B, ldb_bytes, K / 2));
+    if (packed) {
+        if (!B)
+            return fail(QGEMM_ERR_NULL_POINTER, "Bp is NULL");
+        if (!aligned(B, 16))
+            return fail(QGEMM_ERR_BAD_LAYOUT, "Bp is not 16-byte aligned");
+    } else {
+        TRY(check_operand("B", B, ldb_bytes, K / 2));
+    }
     if (!scale_a)
         return fail(QGEMM_ERR_NULL_POINTER, "scale_a is NULL");
     if (!scale_b)
@@ -613,13 +623,59 @@ qgemm_status qgemm_mx_mixed(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *
     TRY(check_bias(bias));
     TRY(check_output(C, ldc, N, 2));
     TRY(check_device());
-    const int tile = pick_tile_mx84(s);
-    Params p = base_params(A, lda_bytes, B, ldb_bytes, C, ldc, s, K, tile);   // kbytes: A's row
+    int tile = pick_tile_mx84(s);
+    if (packed && is_skinny_tile(tile))   // the small-M kernel reads the row-major B only
+        tile = DMA128_TILE;
+    Params p = base_params(A, lda_bytes, B, packed ? K / 2 : ldb_bytes, C, ldc, s, K, tile);   // kbytes: A's row
+    p.b_packed = packed;
     TRY(check_grid(p));
     p.mx_sa = scale_a;
     p.mx_sb = scale_b;
     p.bias = bias;
     return finish(launch_mx84(tile, bias != nullptr, (int)b_layout, p, (hipStream_t)stream));
+}
+
+qgemm_status qgemm_mx_mixed(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *A, int64_t lda_bytes, const void *B,
+                            int64_t ldb_bytes, const uint8_t *scale_a, const uint8_t *scale_b,
+                            qgemm_mx_bscale b_layout, const uint16_t *bias, uint16_t *C, int64_t ldc, int64_t M,
+                            int64_t N, int64_t K, void *stream)
+{
+    return mx_mixed_common(fmt_a, fmt_b, A, lda_bytes, B, ldb_bytes, scale_a, scale_b, b_layout, bias, C, ldc, M, N, K,
+                           stream, false);
+}
+
+qgemm_status qgemm_mx_mixed_prepacked(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *A, int64_t lda_bytes,
+                                      const void *Bp, const uint8_t *scale_a, const uint8_t *scale_b,
+                                      qgemm_mx_bscale b_layout, const uint16_t *bias, uint16_t *C, int64_t ldc,
+                                      int64_t M, int64_t N, int64_t K, void *stream)
+{
+    return mx_mixed_common(fmt_a, fmt_b, A, lda_bytes, Bp, 0, scale_a, scale_b, b_layout, bias, C, ldc, M, N, K,
+                           stream, true);
+}
+
+int64_t qgemm_prepacked_b32_bytes(int64_t N, int64_t row_bytes)
+{
+    if (N < 0 || row_bytes <= 0 || row_bytes % 128 || N >= LD_LIMIT || row_bytes * 256 >= LD_LIMIT)
+        return -1;
+    return (N + 31) / 32 * 32 * row_bytes;
+}
+
+qgemm_status qgemm_prepack_b32(const void *B, int64_t ldb, int64_t N, int64_t row_bytes, void *Bp, void *stream)
+{
+    if (N < 0 || N >= LD_LIMIT)
+        return fail(QGEMM_ERR_BAD_SHAPE, "N=%lld: need 0 <= N < 2^31", (long long)N);
+    if (row_bytes <= 0 || row_bytes % 128 || row_bytes * 256 >= LD_LIMIT)
+        return fail(QGEMM_ERR_BAD_SHAPE, "row_bytes=%lld: need a positive multiple of 128, 256 rows below 2^31",
+                    (long long)row_bytes);
+    if (N == 0)
+        return QGEMM_OK;
+    TRY(check_operand("B", B, ldb, row_bytes));
+    if (!Bp)
+        return fail(QGEMM_ERR_NULL_POINTER, "Bp is NULL");
+    if (!aligned(Bp, 16))
+        return fail(QGEMM_ERR_BAD_LAYOUT, "Bp is not 16-byte aligned");
+    TRY(check_device());
+    return finish(launch_prepack_b32((const uint8_t *)B, ldb, N, row_bytes, (uint8_t *)Bp, (hipStream_t)stream));
 }
 
 qgemm_status qgemm_mx(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const void *B, int64_t ldb_bytes,

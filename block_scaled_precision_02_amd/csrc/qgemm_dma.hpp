@@ -185,13 +185,16 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
 
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * p.lda,
                                                 (uint32_t)((rows_a - 1) * p.lda + p.kbytes));
-    // B row-major, or prepacked: 16-row groups of 1 KB blocks, block t of a
-    // group holding its rows' 64-byte K piece t already in this kernel's LDS
-    // order, so that a fetch reads one contiguous kilobyte.
-    const int64_t gbytes = (int64_t)16 * p.kbytes;        // one packed group
+    // B row-major, or prepacked: 16-row groups of 1 KB blocks (32-row groups
+    // for the mixed path's 32-byte B rows), block t of a group holding its
+    // rows' K piece t already in this kernel's LDS order, so that a fetch
+    // reads one contiguous kilobyte.
+    constexpr int PGR = BROWS_PER_FETCH;                  // rows per packed group
+    const int kbytes_b = B4 ? p.kbytes / 2 : p.kbytes;
+    const int64_t gbytes = (int64_t)PGR * kbytes_b;       // one packed group
     const __amdgpu_buffer_rsrc_t rb =
-        p.b_packed ? make_rsrc(p.B + (int64_t)(n0 / 16) * gbytes, (uint32_t)(((rows_b + 15) / 16) * gbytes))
-                   : make_rsrc(p.B + (int64_t)n0 * p.ldb, (uint32_t)((rows_b - 1) * p.ldb + (B4 ? p.kbytes / 2 : p.kbytes)));
+        p.b_packed ? make_rsrc(p.B + (int64_t)(n0 / PGR) * gbytes, (uint32_t)(((rows_b + PGR - 1) / PGR) * gbytes))
+                   : make_rsrc(p.B + (int64_t)n0 * p.ldb, (uint32_t)((rows_b - 1) * p.ldb + kbytes_b));
     const unsigned bstep = p.b_packed ? 1024u : (unsigned)BSTAGE;   // B bytes per stage along K
 
     // Fetch map: wave w's j-th A fetch covers rows 16*(4w+j) .. +15; lane i
@@ -212,9 +215,13 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         const int c = (lane & 3) ^ ((r >> 2) & 3);
         if constexpr (B4) {
             // 32 rows of 32 bytes: lane i takes row i/2, the chunk of slot i%2
+            // (prepacked: slot i of the group's block)
             const int r4 = BROWS_PER_FETCH * g + (lane >> 1);
             const int c4 = (lane & 1) ^ ((r4 >> 3) & 1);
-            b_off[j] = r4 < rows_b ? (unsigned)(r4 * p.ldb + 16 * c4) : OOB;
+            if (p.b_packed)
+                b_off[j] = PGR * g < rows_b ? (unsigned)(g * gbytes + 16 * lane) : OOB;
+            else
+                b_off[j] = r4 < rows_b ? (unsigned)(r4 * p.ldb + 16 * c4) : OOB;
         } else if (p.b_packed) {
             b_off[j] = 16 * g < rows_b ? (unsigned)(g * gbytes + 16 * lane) : OOB;
         } else {

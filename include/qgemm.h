@@ -172,6 +172,25 @@ qgemm_status qgemm_mx_mixed(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *
                             qgemm_mx_bscale b_layout, const uint16_t *bias, uint16_t *C, int64_t ldc,
                             int64_t M, int64_t N, int64_t K, void *stream);
 
+/* The mixed GEMM (e4m3 A, e2m1 B) on a prepacked B.  qgemm_prepack_b32
+ * rewrites B [N, row_bytes] (row_bytes = K/2, a positive multiple of 128;
+ * row stride ldb bytes, 16-byte aligned, ldb a multiple of 16) into Bp
+ * (qgemm_prepacked_b32_bytes(N, row_bytes) bytes, 16-byte aligned,
+ * caller-owned): ceil(N/32) groups of 32 rows, group R holding row_bytes/32
+ * blocks of 1 KB, block t bytes 32t .. 32t+31 of the group's rows, 16-byte
+ * slot p being row 32R + p/2, chunk (p mod 2) XOR ((p/16) mod 2); rows past N
+ * are zeros -- the order the mixed GEMM's B stages take in LDS.
+ * qgemm_prepacked_b32_bytes returns -1 for a bad size.  qgemm_mx_mixed_prepacked
+ * is qgemm_mx_mixed (e4m3 A with e2m1 B only; equal formats return
+ * QGEMM_ERR_BAD_FORMAT) with Bp in place of (B, ldb); results equal
+ * qgemm_mx_mixed's on the same tile; M <= 16 runs the 128x128 tile. */
+int64_t qgemm_prepacked_b32_bytes(int64_t N, int64_t row_bytes);
+qgemm_status qgemm_prepack_b32(const void *B, int64_t ldb, int64_t N, int64_t row_bytes, void *Bp, void *stream);
+qgemm_status qgemm_mx_mixed_prepacked(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *A, int64_t lda_bytes,
+                                      const void *Bp, const uint8_t *scale_a, const uint8_t *scale_b,
+                                      qgemm_mx_bscale b_layout, const uint16_t *bias, uint16_t *C, int64_t ldc,
+                                      int64_t M, int64_t N, int64_t K, void *stream);
+
 /* Prepacked B.  B (the weights, static across calls) can be rewritten once
  * into the order the LDS-fetch kernel's B stages take in LDS, so that each
  * of its fetches reads one contiguous kilobyte instead of 16 rows x 64 bytes

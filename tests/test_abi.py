@@ -353,3 +353,17 @@ def test_quant_f8_block_rejects(monkeypatch):
     assert f(FAKE, 256, FAKE2, 256, FAKE3, 2, 0, 256, None) == q.QGEMM_OK
     monkeypatch.setenv("QGEMM_FAKE_ARCH", "gfx1201")
     assert f(FAKE, 256, FAKE2, 256, FAKE3, 2, 4, 256, None) == q.QGEMM_ERR_UNSUPPORTED_DEVICE
+
+
+def test_prepacked_b32_sizes_and_rejects(monkeypatch):
+    L = q.lib()
+    assert L.qgemm_prepacked_b32_bytes(33, 128) == 64 * 128
+    assert L.qgemm_prepacked_b32_bytes(32, 96) == -1
+    assert L.qgemm_prepack_b32(FAKE, 128, 33, 64, FAKE2, None) == q.QGEMM_ERR_BAD_SHAPE
+    assert L.qgemm_prepack_b32(FAKE, 128, 33, 128, None, None) == q.QGEMM_ERR_NULL_POINTER
+    m = L.qgemm_mx_mixed_prepacked
+    assert m(0, 0, FAKE, 512, FAKE2, FAKE3, FAKE3, 1, None, FAKE, 64, 64, 64, 512, None) == q.QGEMM_ERR_BAD_FORMAT
+    assert m(0, 1, FAKE, 512, None, FAKE3, FAKE3, 1, None, FAKE, 64, 64, 64, 512, None) == q.QGEMM_ERR_NULL_POINTER
+    assert m(0, 1, FAKE, 512, FAKE2 + 8, FAKE3, FAKE3, 1, None, FAKE, 64, 64, 64, 512, None) == q.QGEMM_ERR_BAD_LAYOUT
+    monkeypatch.setenv("QGEMM_FAKE_ARCH", "gfx1201")
+    assert m(0, 1, FAKE, 512, FAKE2, FAKE3, FAKE3, 1, None, FAKE, 64, 64, 64, 512, None) == q.QGEMM_ERR_UNSUPPORTED_DEVICE

@@ -134,3 +134,54 @@ def test_prepacked_full_workload_sampled(name):
     got = parity.bits(out[torch.from_numpy(rows).cuda()])
     ref, absdot, _ = parity.oracle_run(d, rows=rows)
     parity.compare(d, got, ref, absdot, f"prepacked full {name}")
+
+
+# ------------------------------------------ mixed MX: e2m1 B in 32-row groups
+
+@pytest.mark.parametrize("N,row", [(1, 128), (33, 128), (300, 256), (7168, 1024)])
+def test_prepack_b32_bit_exact(orc, N, row):
+    B = np.random.default_rng(N + row).integers(0, 256, (N, row), dtype=np.uint8)
+    pb = q.qgemm_prepack_b32(parity.dev(B))
+    torch.cuda.synchronize()
+    assert np.array_equal(pb.data.cpu().numpy(), orc.pack_b32(B))
+
+
+def _run_mixed_packed(d, out=None):
+    bias = None if d["bias"] is None else parity.dev(d["bias"].view(np.int16))
+    pb = q.qgemm_prepack_b32(parity.dev(d["B"]))
+    return q.qgemm_mx_mixed_prepacked(q.QGEMM_MX_E4M3, q.QGEMM_MX_E2M1, parity.dev(d["A"]), pb,
+                                      parity.dev(d["scale_a"]), parity.dev(d["scale_b"]), d["b_rows_per_scale"],
+                                      bias, out=out)
+
+
+@pytest.mark.parametrize("tile", [-1, 4, 5, 7])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (17, 33, 512), (255, 257, 1024), (300, 520, 2048), (64, 300, 768)])
+def test_prepacked_mixed_edges(M, N, K, tile):
+    """The mixed GEMM on a prepacked e2m1 B: ragged M / N, canaries; bit for bit
+    equal to the same tile on the row-major B (M <= 16 runs the 128x128 tile)."""
+    d = inputs.make("mx_a8w4", M=M, N=N, K=K, bias=(M % 2 == 1))
+    _say(f"[prepacked] mx_a8w4 {M}x{N}x{K} tile {tile}")
+    q.force_tile(tile)
+    ldc = N + (-N) % 8 + 8
+    buf = torch.full((M + 3, ldc), float("nan"), dtype=torch.bfloat16, device="cuda")
+    before = parity.bits(buf)
+    _run_mixed_packed(d, out=buf[:M, :N])
+    after = parity.bits(buf)
+    ref, absdot, _ = parity.oracle_run(d)
+    parity.compare(d, after[:M, :N], ref, absdot, f"prepacked mx_a8w4 {M}x{N}x{K} tile {tile}")
+    assert np.array_equal(after[:M, N:], before[:M, N:]), "wrote past N"
+    assert np.array_equal(after[M:], before[M:]), "wrote past M"
+    q.force_tile(7 if (tile == -1 and M <= 16) else tile)
+    plain = parity.bits(parity.gpu_run(d))
+    assert np.array_equal(after[:M, :N], plain), "prepacked and row-major B differ"
+
+
+def test_prepacked_mixed_full_workload_sampled():
+    d = inputs.make("mx_a8w4")
+    out = _run_mixed_packed(d)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(d["M"] - 8, d["M"]),
+                                     np.random.default_rng(3).choice(d["M"], 8, replace=False)]))
+    got = parity.bits(out[torch.from_numpy(rows).cuda()])
+    ref, absdot, _ = parity.oracle_run(d, rows=rows)
+    parity.compare(d, got, ref, absdot, "prepacked full mx_a8w4")
