@@ -245,18 +245,17 @@ qgemm_status finish(hipError_t e)
 }
 
 // The LDS-fetch kernels (tiles 4-7) run tiles whose K is a whole number of
-// their 4 x 64-byte stages.  For MX, a 4-stage round reads 16 bytes of each
-// scale row (e2m1) or the first 8 bytes of a 16-byte chunk (e4m3): e2m1 scale
-// rows must be whole 16-byte chunks, e4m3 ones whole 8-byte words (K % 256),
-// and the caller's scale arrays aligned to that (svec: the caller's check).
+// their 64-byte stages (a last round of fewer than four is masked).  For MX,
+// a round reads 16 bytes of each scale row from byte 16u (e2m1) or 8u (e4m3):
+// scale rows of whole dwords (K % 128), so that each such fetch is dword
+// aligned, and the caller's scale arrays aligned to 16 / 8 bytes (svec: the
+// caller's check).
 bool dma_eligible(int path, int64_t kbytes, int64_t K, bool svec)
 {
-    if (kbytes % 256)
+    if (kbytes % 64)
         return false;
-    if (path == 3)
-        return svec && (K / 32) % 16 == 0;
-    if (path == 2)
-        return svec && (K / 32) % 8 == 0;
+    if (path == 2 || path == 3)
+        return svec && (K / 32) % 4 == 0;
     return true;
 }
 
@@ -311,11 +310,12 @@ int pick_tile_packed(int path, Shape s, int64_t kbytes, bool bf16_out)
 }
 
 // Blockscale FP8 runs in the LDS-fetch kernel: K must be a whole number of
-// its 4-stage rounds (K % 256 == 0), each of which reads 8 bytes (two K
-// blocks) of every scale row.  The 256x128 tile (one workgroup per CU) when its grid
+// 128-element blocks (two stages); a round reads 8 bytes (two K blocks) of
+// every scale row, a last round of one block masks the other.  A prepacked B
+// keeps the packer's K % 256.  The 256x128 tile (one workgroup per CU) when its grid
 // fills the chip at least once, else the 128x128 tile (two per CU, half the
 // rows): one MI355X, 16384x7168x2048 0.302 ms vs 0.310 ms.
-constexpr int64_t F8B_K_MULTIPLE = 256;
+constexpr int64_t F8B_K_MULTIPLE = 128;
 
 // Mixed MX (e4m3 A, e2m1 B) runs in the LDS-fetch kernel: 256x256 (tile 5,
 // or 4 when forced) or 128x128 (tile 7) -- the table's 192x192 choice takes
@@ -563,7 +563,7 @@ static qgemm_status mx_common(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes
     const bool svec = ((K / 32) % wb == 0) && aligned(scale_a, wb) && aligned(scale_b, wb);
     const unsigned chunk_align = (fmt == QGEMM_MX_E2M1) ? 16 : 8;
     const bool svec16 = svec && aligned(scale_a, chunk_align) && aligned(scale_b, chunk_align);
-    if (packed && !dma_eligible(path, row_bytes, K, svec16))
+    if (packed && (row_bytes % 256 || !dma_eligible(path, row_bytes, K, svec16)))
         return fail(QGEMM_ERR_BAD_LAYOUT, "a prepacked MX B needs K/32 a multiple of 16 (e2m1) or 8 (e4m3) and scale "
                                           "arrays aligned to 16 (e2m1) or 8 (e4m3) bytes");
     TRY(check_device());
@@ -601,8 +601,9 @@ static qgemm_status mx_mixed_common(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, cons
         return fail(QGEMM_ERR_BAD_FORMAT, "unknown B-scale layout %d", (int)b_layout);
     const Shape s{M, N, K};
     TRY(check_shape(s, false));
-    if (K % 256)
-        return fail(QGEMM_ERR_BAD_SHAPE, "K=%lld: e4m3 x e2m1 needs K a multiple of 256", (long long)K);
+    if (K % (packed ? 256 : 128))
+        return fail(QGEMM_ERR_BAD_SHAPE, "K=%lld: e4m3 x e2m1 needs K a multiple of %d", (long long)K,
+                    packed ? 256 : 128);
     if (M == 0 || N == 0)
         return QGEMM_OK;
     TRY(check_operand("A", A, lda_bytes, K));

@@ -41,8 +41,10 @@
 //    row i/4.
 //
 // Requirements (checked on the host, which otherwise uses qgemm_kernel):
-// K bytes a multiple of 4 stages (256 bytes), and for MX a scale row length
-// K/32 that is a multiple of 16 bytes.  Rows past M / N are fetched from out of
+// K bytes a whole number of stages (64 bytes), and for the scaled paths scale
+// rows of whole dwords (K % 128).  A last round of fewer than four stages
+// fetches the rest through descriptors of empty range (zeros) and replaces
+// their scale words by neutral ones.  Rows past M / N are fetched from out of
 // range offsets; whatever lands in LDS for them only reaches output rows and
 // columns that are never stored.
 #pragma once
@@ -183,8 +185,12 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     const int m0 = tm * BM, n0 = tn * BN;
     const int rows_a = min(BM, p.M - m0), rows_b = min(BN, p.N - n0);
 
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * p.lda,
-                                                (uint32_t)((rows_a - 1) * p.lda + p.kbytes));
+    // K is a whole number of stages; the last round may hold fewer than four.
+    // Its stages at or past K are fetched through descriptors of empty range
+    // (zeros land in LDS, whatever the offset), so their MFMAs add nothing.
+    const int nst = p.kbytes / DSTAGE;
+    const uint8_t *const a_base = p.A + (int64_t)m0 * p.lda;
+    const uint32_t a_range = (uint32_t)((rows_a - 1) * p.lda + p.kbytes);
     // B row-major, or prepacked: 16-row groups of 1 KB blocks (32-row groups
     // for the mixed path's 32-byte B rows), block t of a group holding its
     // rows' K piece t already in this kernel's LDS order, so that a fetch
@@ -192,9 +198,9 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr int PGR = BROWS_PER_FETCH;                  // rows per packed group
     const int kbytes_b = B4 ? p.kbytes / 2 : p.kbytes;
     const int64_t gbytes = (int64_t)PGR * kbytes_b;       // one packed group
-    const __amdgpu_buffer_rsrc_t rb =
-        p.b_packed ? make_rsrc(p.B + (int64_t)(n0 / PGR) * gbytes, (uint32_t)(((rows_b + PGR - 1) / PGR) * gbytes))
-                   : make_rsrc(p.B + (int64_t)n0 * p.ldb, (uint32_t)((rows_b - 1) * p.ldb + kbytes_b));
+    const uint8_t *const b_base = p.b_packed ? p.B + (int64_t)(n0 / PGR) * gbytes : p.B + (int64_t)n0 * p.ldb;
+    const uint32_t b_range = p.b_packed ? (uint32_t)(((rows_b + PGR - 1) / PGR) * gbytes)
+                                        : (uint32_t)((rows_b - 1) * p.ldb + kbytes_b);
     const unsigned bstep = p.b_packed ? 1024u : (unsigned)BSTAGE;   // B bytes per stage along K
 
     // Fetch map: wave w's j-th A fetch covers rows 16*(4w+j) .. +15; lane i
@@ -232,12 +238,15 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // fetched separately.
     auto fetch_part = [&](int t, auto partc) {
         const unsigned kb = (unsigned)(t * DSTAGE), kbb = (unsigned)t * bstep;
+        const bool live = t < nst;
         uint8_t *slot = &lds[(t & 3) * STAGE_BYTES];
         if constexpr (decltype(partc)::value == 0) {
+            const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base, live ? a_range : 0u);
 #pragma unroll
             for (int j = 0; j < DMA_A; ++j)
                 dma16(ra, a_off[j] + kb, slot + (DMA_A * wave + j) * 16 * DSTAGE);
         } else {
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base, live ? b_range : 0u);
 #pragma unroll
             for (int j = 0; j < DMA_B; ++j)
                 dma16(rb, b_off[j] + kbb, slot + BM * DSTAGE + (DMA_B * wave + j) * 1024);
@@ -341,6 +350,18 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             for (int j = 0; j < TN; ++j) {
                 const int row = BROWS == 1 ? brow + 32 * j : (wn * TN * 32 + 32 * j) / BROWS;
                 rd(sbuf + SA_ROWS * 16 + row * 16, crb[j]);
+            }
+            // Words of stages past K (the last round's tail) hold the next
+            // row's scales or zeros: make them finite and neutral -- scale
+            // 2^0 under zero data for MX, a fold factor of 0 for blockscale.
+            constexpr unsigned NEUTRAL = BS ? 0u : 0x7F7F7F7Fu;
+#pragma unroll
+            for (int w = 1; w < SCW; ++w) {
+                const bool past = t + w * (4 / SCW) >= nst;
+#pragma unroll
+                for (int i = 0; i < TM; ++i) cra[i][w] = past ? NEUTRAL : cra[i][w];
+#pragma unroll
+                for (int j = 0; j < TN; ++j) crb[j][w] = past ? NEUTRAL : crb[j][w];
             }
         }
     };
@@ -513,11 +534,11 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         use_next_scales();
     };
 
-    // The host guarantees kbytes % 256 == 0: a whole number of 4-stage
-    // rounds.  The last round fetches stages past K (from in-range or
-    // out-of-range offsets, never multiplied).
-    const int nstages = p.kbytes / DSTAGE;
-    for (int t = 0; t < nstages; t += 4) {
+    // The host guarantees kbytes % 64 == 0 (a whole number of stages; for
+    // the scaled paths, of the stages that one scale word covers).  Fetches
+    // run three stages ahead, into stages past K that are never multiplied
+    // or, in a partial last round, multiplied as zeros.
+    for (int t = 0; t < nst; t += 4) {
         stage(t, I0());
         stage(t + 1, I1());
         stage(t + 2, std::integral_constant<int, 2>());

@@ -102,9 +102,11 @@ hipError_t launch_i8(int tile, bool bias, int out, const Params &p, hipStream_t 
 hipError_t launch_f8(int tile, bool bias, const Params &p, hipStream_t s);
 hipError_t launch_mx8(int tile, bool bias, int brows, bool svec, const Params &p, hipStream_t s);
 hipError_t launch_mx4(int tile, bool bias, int brows, bool svec, const Params &p, hipStream_t s);
-// FP8 blockscale: tiles 7 and 10 (need K % 512 == 0 and 16-byte aligned scale arrays).
+// FP8 blockscale: tiles 7 and 10, small-M tiles 8 and 9 (need K % 256 == 0 and
+// 8-byte aligned scale arrays).
 hipError_t launch_f8b(int tile, bool bias, const Params &p, hipStream_t s);
-// MX with e4m3 A and e2m1 B: tiles 4, 5 and 7 (same requirements as MX on them).
+// MX with e4m3 A and e2m1 B: tiles 4, 5, 7 and small-M tiles 8, 9 (same
+// requirements as MX on them).
 hipError_t launch_mx84(int tile, bool bias, int brows, const Params &p, hipStream_t s);
 
 }  // namespace qgemm

@@ -3,7 +3,7 @@
  *
  *     C = bf16( scale_A (.) scale_B (.) (A . B^T) + bias )
  *
- * in three element paths:
+ * in these element paths:
  *   qgemm_i8_rowwise   int8 A and B, int32 accumulation, fp32 per-row scale of
  *                      A and per-row scale of B ("rowwise"), optional bf16
  *                      bias, bf16 out.  Defined by comfy-kitchen PR #174
@@ -25,6 +25,12 @@
  *                      PR #806, What) or [N, K/32] (the 1x32 FP4 scales of
  *                      ROCm/FlyDSL PR #990 "[fp4_gemm_4wave] MXFP4 GEMM perf
  *                      optimize").
+ *   qgemm_mx_mixed     MX with e4m3 A (activations) and e2m1 B (weights),
+ *                      each operand under its own format and the same
+ *                      ue8m0 per-32 scale rule.
+ *
+ * Prepacked variants of each GEMM take a B already laid out in the order the
+ * kernels' LDS stages use (qgemm_prepack_b, qgemm_prepack_b32).
  *
  * Numerics (all paths): the product is accumulated exactly (int32) for int8
  * and in fp32 by the matrix cores for e4m3 / e2m1; the epilogue is, per
@@ -136,7 +142,7 @@ qgemm_status qgemm_f8_pertoken(const uint8_t *A, int64_t lda, const uint8_t *B, 
  * acc = sum_kb scale_a[m,kb] * scale_b[n/128,kb] * P[kb], P[kb] the fp32
  * matrix-core sum of the block's 128 products, each block folded into the
  * fp32 total with one fused multiply-add; then f = acc, [+ bias], bf16
- * round-nearest-even.  K must be a multiple of 256 (QGEMM_ERR_BAD_SHAPE) and
+ * round-nearest-even.  K must be a multiple of 128 (QGEMM_ERR_BAD_SHAPE) and
  * both scale arrays 8-byte aligned (QGEMM_ERR_BAD_LAYOUT). */
 qgemm_status qgemm_f8_blockscale(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
                                  const float *scale_a, const float *scale_b, const uint16_t *bias,
@@ -164,7 +170,7 @@ qgemm_status qgemm_mx(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const 
  *   A        [M, K] e4m3fn codes, row stride lda_bytes (>= K)
  *   B        [N, K] e2m1, two per byte (even k in the low nibble), row stride
  *            ldb_bytes (>= K/2)
- * It needs K a multiple of 256 (QGEMM_ERR_BAD_SHAPE) and 8-byte aligned
+ * It needs K a multiple of 128 (QGEMM_ERR_BAD_SHAPE) and 8-byte aligned
  * scale arrays (QGEMM_ERR_BAD_LAYOUT); e2m1 A with e4m3 B returns
  * QGEMM_ERR_BAD_FORMAT.  Numerics as qgemm_mx. */
 qgemm_status qgemm_mx_mixed(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *A, int64_t lda_bytes,
@@ -182,8 +188,9 @@ qgemm_status qgemm_mx_mixed(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *
  * are zeros -- the order the mixed GEMM's B stages take in LDS.
  * qgemm_prepacked_b32_bytes returns -1 for a bad size.  qgemm_mx_mixed_prepacked
  * is qgemm_mx_mixed (e4m3 A with e2m1 B only; equal formats return
- * QGEMM_ERR_BAD_FORMAT) with Bp in place of (B, ldb); results equal
- * qgemm_mx_mixed's on the same tile; M <= 16 runs the 128x128 tile. */
+ * QGEMM_ERR_BAD_FORMAT) with Bp in place of (B, ldb) and K a multiple of 256
+ * (the packer's rows); results equal qgemm_mx_mixed's on the same tile;
+ * M <= 16 runs the 128x128 tile. */
 int64_t qgemm_prepacked_b32_bytes(int64_t N, int64_t row_bytes);
 qgemm_status qgemm_prepack_b32(const void *B, int64_t ldb, int64_t N, int64_t row_bytes, void *Bp, void *stream);
 qgemm_status qgemm_mx_mixed_prepacked(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *A, int64_t lda_bytes,
@@ -232,8 +239,8 @@ qgemm_status qgemm_i8_rowwise_prepacked(const int8_t *A, int64_t lda, const void
 qgemm_status qgemm_f8_pertoken_prepacked(const uint8_t *A, int64_t lda, const void *Bp, const float *scale_a,
                                          const float *scale_b, const uint16_t *bias, uint16_t *C, int64_t ldc,
                                          int64_t M, int64_t N, int64_t K, void *stream);
-/* qgemm_f8_blockscale with Bp in place of (B, ldb): results equal
- * qgemm_f8_blockscale's on the same tile. */
+/* qgemm_f8_blockscale with Bp in place of (B, ldb) and K a multiple of 256
+ * (the packer's rows): results equal qgemm_f8_blockscale's on the same tile. */
 qgemm_status qgemm_f8_blockscale_prepacked(const uint8_t *A, int64_t lda, const void *Bp, const float *scale_a,
                                            const float *scale_b, const uint16_t *bias, uint16_t *C, int64_t ldc,
                                            int64_t M, int64_t N, int64_t K, void *stream);
@@ -322,8 +329,10 @@ const char *qgemm_status_string(qgemm_status status);
  *   8: 16 rows x 16 columns, 8 waves splitting K (small M)
  *   9: 64 rows x 16 columns, 8 waves splitting K (small M)
  *  10: 256 rows x 128 columns, fp8 blockscale only
- * Tiles 4-7 need K bytes a multiple of 256 and MX scale rows a multiple of
- * 16 (e2m1) or 8 (e4m3) bytes; where these hold, the table's 256x256 choice runs as tile 5,
+ * Tiles 4-7 need K bytes a multiple of 64 (whole stages; a last round of
+ * fewer than four is masked) and MX scale rows of whole dwords (K % 128),
+ * with scale arrays aligned to 16 (e2m1) or 8 (e4m3) bytes; where these
+ * hold, the table's 256x256 choice runs as tile 5,
  * 192x192 as tile 6 and 128x128 as tile 7.  Calls with M <= 64 take tile 8
  * (M <= 16) or 9 (INT8 and FP8 only: MX takes the small-M kernel up to
  * M = 16). */

@@ -128,10 +128,14 @@ def test_tile_table():
     # full rounds of 256x256 tiles keep the big tile, run by the eight-wave
     # LDS-fetch kernel when K fits its stages
     assert L.qgemm_select_tile(0, 30000, 21504, 5376) == 5      # 9912 tiles
-    assert L.qgemm_select_tile(0, 30000, 21504, 5408) == 0      # K bytes not a multiple of 256
+    assert L.qgemm_select_tile(0, 30000, 21504, 5408) == 0      # K bytes not whole 64-byte stages
+    assert L.qgemm_select_tile(0, 30000, 21504, 5440) == 5      # 85 stages: a partial last round
     assert L.qgemm_select_tile(3, 8192, 8192, 8192) == 5        # 1024 tiles = 4 rounds
     assert L.qgemm_select_tile(2, 16384, 7168, 2048) == 5       # 1792 tiles = 7 rounds
-    assert L.qgemm_select_tile(2, 16384, 7168, 2016) == 0       # K/32 = 63: not whole chunks
+    assert L.qgemm_select_tile(2, 16384, 7168, 2016) == 0       # K/32 = 63: scale rows not whole dwords
+    assert L.qgemm_select_tile(2, 16384, 7168, 2176) == 5       # K/32 = 68: a partial last round
+    assert L.qgemm_select_tile(3, 8192, 8192, 8320) == 5        # e2m1, 65 stages
+    assert L.qgemm_select_tile(2, 16384, 7168, 2080) == 0       # K/32 = 65
     # 144 tiles of 256x256 leave 112 CUs idle; 242 tiles of 192x192 fill one
     # round (LDS-fetch form when K fits, register-staged otherwise)
     assert L.qgemm_select_tile(1, 4096, 2112, 7168) == 6
@@ -277,8 +281,8 @@ def f8b(A=FAKE, lda=512, B=FAKE2, ldb=512, sa=FAKE3, sb=FAKE3, bias=None, C=FAKE
     (dict(sb=None), q.QGEMM_ERR_NULL_POINTER),
     (dict(C=None), q.QGEMM_ERR_NULL_POINTER),
     (dict(K=0), q.QGEMM_ERR_BAD_SHAPE),
-    (dict(K=640, lda=640, ldb=640), q.QGEMM_ERR_BAD_SHAPE),     # blockscale needs K % 256 == 0
-    (dict(K=128, lda=128, ldb=128), q.QGEMM_ERR_BAD_SHAPE),
+    (dict(K=576, lda=576, ldb=576), q.QGEMM_ERR_BAD_SHAPE),     # blockscale needs K % 128 == 0
+    (dict(K=192, lda=192, ldb=192), q.QGEMM_ERR_BAD_SHAPE),
     (dict(M=-1), q.QGEMM_ERR_BAD_SHAPE),
     (dict(lda=256), q.QGEMM_ERR_BAD_LAYOUT),
     (dict(sa=FAKE3 + 4), q.QGEMM_ERR_BAD_LAYOUT),                # scales must be 8-byte aligned
@@ -312,7 +316,7 @@ def mx2(fa=0, fb=1, A=FAKE, lda=512, B=FAKE2, ldb=256, sa=FAKE3, sb=FAKE3, layou
     (dict(fb=7), q.QGEMM_ERR_BAD_FORMAT),
     (dict(fa=1, fb=0), q.QGEMM_ERR_BAD_FORMAT),                 # e2m1 A with e4m3 B
     (dict(layout=16), q.QGEMM_ERR_BAD_FORMAT),
-    (dict(K=640, lda=640, ldb=320), q.QGEMM_ERR_BAD_SHAPE),      # K % 256
+    (dict(K=576, lda=576, ldb=288), q.QGEMM_ERR_BAD_SHAPE),      # K % 128
     (dict(A=None), q.QGEMM_ERR_NULL_POINTER),
     (dict(sb=None), q.QGEMM_ERR_NULL_POINTER),
     (dict(ldb=128), q.QGEMM_ERR_BAD_LAYOUT),                     # e2m1 B row is K/2 = 256 bytes

@@ -134,8 +134,8 @@ def test_f8b_full_workload_sampled(tile):
     _say(f"[parity] full f8_block: worst err/bound {worst:.3g} cos {cos:.8f}")
 
 
-def test_f8b_rejects_k_not_multiple_of_256():
-    A = torch.zeros((4, 640), dtype=torch.uint8, device="cuda")
+def test_f8b_rejects_k_not_multiple_of_128():
+    A = torch.zeros((4, 576), dtype=torch.uint8, device="cuda")
     sa = torch.ones((4, 5), dtype=torch.float32, device="cuda")
     sb = torch.ones((1, 5), dtype=torch.float32, device="cuda")
     with pytest.raises(ValueError):

@@ -99,10 +99,10 @@ def test_mx84_equal_formats_are_qgemm_mx():
 
 
 def test_mx84_rejects():
-    A8 = torch.zeros((4, 640), dtype=torch.uint8, device="cuda")
-    B4 = torch.zeros((4, 320), dtype=torch.uint8, device="cuda")
-    s = torch.full((4, 20), 127, dtype=torch.uint8, device="cuda")
-    with pytest.raises(ValueError):      # K = 640 is not a multiple of 256
+    A8 = torch.zeros((4, 576), dtype=torch.uint8, device="cuda")
+    B4 = torch.zeros((4, 288), dtype=torch.uint8, device="cuda")
+    s = torch.full((4, 18), 127, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):      # K = 576 is not a multiple of 128
         q.qgemm_mx_mixed(q.QGEMM_MX_E4M3, q.QGEMM_MX_E2M1, A8, B4, s, s, 1)
     with pytest.raises(ValueError):      # e2m1 A with e4m3 B
         q.qgemm_mx_mixed(q.QGEMM_MX_E2M1, q.QGEMM_MX_E4M3, B4, A8, s, s, 1)

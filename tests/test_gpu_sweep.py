@@ -38,7 +38,7 @@ def _shape(rng, name):
     M = int(rng.choice([int(rng.integers(1, 17)), int(rng.integers(17, 65)), int(rng.integers(65, 520))]))
     N = int(rng.integers(1, 520))
     if name in ("f8_block", "mx_a8w4"):
-        K = 256 * int(rng.integers(1, 7))                  # these paths: K a multiple of 256
+        K = 128 * int(rng.integers(1, 13))                 # these paths: K a multiple of 128
     elif name == "mxfp4":
         K = 64 * int(rng.integers(1, 25))                  # whole bytes; on / off the 16-byte scale chunks
     else:
