@@ -159,3 +159,13 @@ def test_partial_round_full_size_mxfp8():
     got = parity.bits(out[torch.from_numpy(rows).cuda()])
     ref, absdot, _ = parity.oracle_run(d, rows=rows)
     parity.compare(d, got, ref, absdot, "ktail full mxfp8")
+
+
+@pytest.mark.parametrize("name,tile", [("f8_block", 8), ("f8_block", 9), ("mx_a8w4", 8), ("mxfp8", 8),
+                                       ("mxfp4", 8), ("i8_small", 9), ("f8_ptpc", 8)])
+@pytest.mark.parametrize("K", [128, 384])
+def test_small_m_kernel_k_not_multiple_of_256(name, tile, K):
+    """The small-M kernel (eight waves splitting K) at K that the LDS-fetch
+    kernels take as a partial round: same poisoned padding and scales."""
+    M = 12 if tile == 8 else 40
+    _check(name, M, 300, K, tile)
