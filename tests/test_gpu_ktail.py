@@ -169,3 +169,22 @@ def test_small_m_kernel_k_not_multiple_of_256(name, tile, K):
     kernels take as a partial round: same poisoned padding and scales."""
     M = 12 if tile == 8 else 40
     _check(name, M, 300, K, tile)
+
+
+@pytest.mark.parametrize("name,shape,path,tile", [("f8_block", (16384, 7168, 2176), 4, 10),
+                                                  ("i8_qkv", (30000, 21504, 5440), 0, 5)])
+def test_partial_round_full_size(name, shape, path, tile):
+    """Blockscale 16384 x 7168 x 2176 (17 blocks: a last round of one block)
+    and INT8 30000 x 21504 x 5440 (85 stages: a last round of one stage), in
+    the launch the benchmark uses, on sampled whole rows."""
+    M, N, K = shape
+    assert q.select_tile(path, M, N, K) == tile
+    d = inputs.make(name, M=M, N=N, K=K)
+    _say(f"[ktail] full {name} {M}x{N}x{K}")
+    out = parity.gpu_run(d)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([np.arange(8), rng.choice(M, 12, replace=False), np.arange(M - 8, M)]))
+    got = parity.bits(out[torch.from_numpy(rows).cuda()])
+    ref, absdot, _ = parity.oracle_run(d, rows=rows)
+    parity.compare(d, got, ref, absdot, f"ktail full {name}")
