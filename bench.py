@@ -1,19 +1,28 @@
 """Benchmark of the scaled low-precision GEMM on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]          # the five workloads
+    python bench.py --workload NAME [--shape M,N,K] [--tile T]   # one workload
 
 A step is one call of the GEMM (argument checks, tile choice, one kernel:
 tile schedule, HBM->LDS staging, MFMA K loop, fused scale/bias epilogue) on
-one batch of seeded synthetic inputs already resident in HBM.  The default
-workload is the INT8 rowwise projection M=30000 N=21504 K=5376 with bias;
---workload picks another (i8_small, f8_ptpc, mxfp8, mxfp4, i8_qkv, and
-f8_block: FP8 with fp32 scales per 128-element K block, 16384x7168x2048;
-mx_a8w4: MX e4m3 A x e2m1 B, 8192^3).
+one batch of seeded synthetic inputs already resident in HBM.
 
-Prints one JSON line: effective TOPS/TFLOPS = 2MNK / t, the roofline of the
-kernel (achieved over the dense MFMA peak of its dtype, from HIP events on
-the launch stream), and the CPU oracle timed on a bounded sample of the same
-workload on this host.
+Default run.  The headline (`value`, `ms_per_step`, `roofline`) is the INT8
+rowwise projection M=30000 N=21504 K=5376 with bias: W warmup steps, then
+exactly K timed steps between two device synchronisations.  The same line
+carries `per_config`: each of the five workloads (INT8 256x256x512, FP8
+per-token 4096x2112x7168, MXFP8 16384x7168x2048, MXFP4 8192^3, INT8
+30000x21504x5376) timed cold -- R input sets at distinct device addresses,
+R = ceil(512 MB / operand bytes) so that the operands cannot be served from
+the 256 MB MALL or L2 -- in 3 passes of >= 100 ms (median, min, spread),
+with the shader clock sampled during the passes, a hot (one input set)
+secondary, the prepacked-B entry point, and a parity verdict on sampled
+output rows against the CPU oracle.  The oracle also gives the CPU baseline
+(a bounded sample of the headline workload on this host's cores).
+
+--workload picks one workload instead (i8_small, f8_ptpc, mxfp8, mxfp4,
+i8_qkv, f8_block: FP8 with fp32 scales per 128-element K block,
+16384x7168x2048; mx_a8w4: MX e4m3 A x e2m1 B, 8192^3).
 """
 import argparse
 import ctypes
@@ -34,22 +43,33 @@ METRIC = "effective TFLOPS/TOPS (2MNK/t) per dtype; % of MI355X dense MFMA peak"
 PEAK = {"i8": 5000.0, "f8": 5000.0, "f8b": 5000.0, "e4m3": 5000.0, "e2m1": 10100.0, "e4m3/e2m1": 5000.0}
 HBM_GBPS = 8000.0
 # The pages' numbers for exactly these workloads (2MNK / their time where they
-# give a time), quoted by vs_baseline; context, not targets:
-#  - INT8 30000x21504x5376: 209.9 TOPS on an RX 9070 XT (comfy-kitchen PR #174,
-#    Performance) -- another GPU;
+# give a time); context, not targets:
 #  - MXFP8 16384x7168x2048: 246.2 us and 32768x7168x1792: 462.2 us, FP8
 #    blockscale 16384x7168x2048: 362.3 us, all on MI355X (ROCm/mori PR #806,
 #    commit message table; its MXFP8 reads a packed scale layout);
-#  - MXFP4 8192^3: 5034 TFLOPS on MI355X (ROCm/FlyDSL PR #990, Performance).
+#  - MXFP4 8192^3: 5034 TFLOPS on MI355X with a preshuffled B (ROCm/FlyDSL PR
+#    #990, Performance), so it is set against the prepacked-B call.
+# vs_baseline divides by one of these only when the pages measured MI355X.
 PAGES_REF = {
-    ("i8_qkv", 30000, 21504, 5376): 209.9,
     ("mxfp8", 16384, 7168, 2048): 2.0 * 16384 * 7168 * 2048 / 246.2e-6 / 1e12,
     ("mxfp8", 32768, 7168, 1792): 2.0 * 32768 * 7168 * 1792 / 462.2e-6 / 1e12,
     ("f8_block", 16384, 7168, 2048): 2.0 * 16384 * 7168 * 2048 / 362.3e-6 / 1e12,
-    ("mxfp4", 8192, 8192, 8192): 5034.0,
 }
-# Rotating input sets so operands are not served from the 256 MB MALL.
-ROT = {"i8_small": 1, "f8_ptpc": 8, "mxfp8": 2, "mxfp4": 3, "i8_qkv": 2, "f8_block": 2, "mx_a8w4": 3}
+PAGES_REF_PREPACKED = {("mxfp4", 8192, 8192, 8192): 5034.0}
+# The one number the pages give for the INT8 workload was measured on another
+# GPU (RX 9070 XT, gfx1201; comfy-kitchen PR #174, Performance): reported as
+# context, never divided into an MI355X rate.
+PAGES_CONTEXT = {("i8_qkv", 30000, 21504, 5376): {"value": 209.9, "unit": "TOPS", "hardware": "RX 9070 XT (gfx1201)",
+                                                  "source": "comfy-kitchen PR #174, Performance"}}
+# Cold timing: R input sets at distinct device addresses, R = ceil(512 MB /
+# operand bytes), twice the 256 MB MALL, so no launch finds its operands in
+# the MALL or L2 from an earlier one (FP8 4096x2112x7168: 12, MXFP8
+# 16384x7168x2048: 11, MXFP4 8192^3: 8, INT8 30000x21504x5376: 2).  The INT8
+# 256x256x512 workload is launch-latency bound and runs on one set.
+COLD_BYTES = 512e6
+LATENCY_BOUND = {"i8_small"}
+SUITE = [(1, "i8_small"), (2, "f8_ptpc"), (3, "mxfp8"), (4, "mxfp4"), (5, "i8_qkv")]
+HEADLINE = "i8_qkv"
 
 
 def log(*a):
@@ -251,7 +271,7 @@ def cpu_baseline(d, target_s):
     t = time.perf_counter() - t0
     ops = 2.0 * n * d["N"] * d["K"]
     return {"value": round(ops / t / 1e12, 6), "unit": unit_of(d), "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "host": host_info(),
             "sample": f"{n} of {d['M']} rows of A (all {d['N']} columns, K={d['K']}), {t:.1f} s"}
 
 
@@ -377,12 +397,350 @@ def time_graph(d, sets, out, args):
             "rate": round(2.0 * d["M"] * d["N"] * d["K"] / (ms * 1e-3) / 1e12, 3)}
 
 
+def operand_bytes(d):
+    """Bytes of one input set: A, B, the scale arrays and the bias."""
+    n = 0
+    for k in ("A", "B", "scale_a", "scale_b", "bias"):
+        if d.get(k) is not None:
+            n += np.asarray(d[k]).nbytes
+    return n
+
+
+def cold_sets(d):
+    return 1 if d["name"] in LATENCY_BOUND else max(2, -(-int(COLD_BYTES) // operand_bytes(d)))
+
+
+def make_sets(d0, R):
+    """Set 0 uploaded from the generator, sets 1..R-1 device copies of it at
+    distinct addresses (the caches key on addresses, not on values)."""
+    s0 = upload(d0)
+    sets = [s0]
+    for _ in range(1, R):
+        sets.append({k: (None if v is None else v.clone()) for k, v in s0.items()})
+    return sets
+
+
+class ClockSampler:
+    """Samples the shader clock the driver reports (the starred level of
+    pp_dpm_sclk, which on this part reads the current frequency) every
+    `period` seconds from a thread while a timed region runs.  None where
+    the file does not exist."""
+
+    def __init__(self, period=0.02):
+        import glob
+        import threading
+        f = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = f[0] if f else None
+        self.period = period
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+
+    def read(self):
+        if self.path is None:
+            return None
+        try:
+            for line in open(self.path):
+                if "*" in line:
+                    return float(line.split(":")[1].strip().rstrip("*").strip().lower().replace("mhz", ""))
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def __enter__(self):
+        import threading
+        if self.path is not None:
+            def loop():
+                while not self._stop.is_set():
+                    v = self.read()
+                    if v is not None:
+                        self.samples.append(v)
+                    self._stop.wait(self.period)
+            self._thread = threading.Thread(target=loop, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = np.array(self.samples)
+        return {"median": float(np.median(v)), "min": float(v.min()), "max": float(v.max()), "samples": len(v)}
+
+
+def gpu_busy_percent(samples=5, period=0.02):
+    """The driver's busy figure before a timed region (idle check), or None."""
+    import glob
+    f = sorted(glob.glob("/sys/class/drm/card*/device/gpu_busy_percent"))
+    if not f:
+        return None
+    vals = []
+    for _ in range(samples):
+        try:
+            vals.append(int(open(f[0]).read().strip()))
+        except (OSError, ValueError):
+            return None
+        time.sleep(period)
+    return max(vals)
+
+
+def time_passes(run, stream, nsets, passes=3, min_pass_s=0.1, max_launches=2000, warmup=None):
+    """Warm up (50 launches, 500 for kernels under 0.5 ms), then `passes`
+    passes of n back-to-back launches cycling over the input sets, each pass
+    timed with a pair of HIP events on the launch stream; n is chosen so a
+    pass lasts >= min_pass_s.  Returns (ms per launch of each pass, n)."""
+    import torch
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # estimate
+    for i in range(3):
+        run(i)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(10):
+        run(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    est = ev0.elapsed_time(ev1) / 10.0
+    w = warmup if warmup is not None else (500 if est < 0.5 else 50)
+    for i in range(w):
+        run(i)
+    n = int(min(max_launches, max(20, -(-min_pass_s * 1e3 // est))))
+    n = max(n, nsets)
+    out = []
+    for _ in range(passes):
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(n):
+            run(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        out.append(ev0.elapsed_time(ev1) / n)
+    return out, n
+
+
+def pass_stats(ms, flops, peak):
+    med = float(np.median(ms))
+    return {"ms_median": round(med, 6), "ms_min": round(float(min(ms)), 6), "ms_max": round(float(max(ms)), 6),
+            "spread": round((max(ms) - min(ms)) / med, 4), "rate": round(flops / (med * 1e-3) / 1e12, 3),
+            "rate_best": round(flops / (min(ms) * 1e-3) / 1e12, 3),
+            "frac": round(flops / (med * 1e-3) / 1e12 / peak, 4)}
+
+
+def sample_rows(M, n=16):
+    """First two, last two (inside the partial tile when M is not a tile
+    multiple) and evenly spaced rows between."""
+    if M <= n:
+        return np.arange(M)
+    mid = np.linspace(2, M - 3, n - 4).round().astype(np.int64)
+    return np.unique(np.concatenate([[0, 1], mid, [M - 2, M - 1]]))
+
+
+def workload_label(d, prepacked=False):
+    return (f"{d['name']} M={d['M']} N={d['N']} K={d['K']}" + (" bias" if d["bias"] is not None else "")
+            + (" prepacked B" if prepacked else ""))
+
+
+def bench_config(cfg, name, args, headline=None):
+    """One workload of the suite: cold passes (with the clock sampled), hot
+    passes, the prepacked-B call, and the output rows kept for the parity
+    check (made later, in the CPU leg).  `headline` (a dict) receives the
+    contract's K-step timing when this is the headline workload."""
+    import torch
+    from block_scaled_precision_02_amd import inputs
+    import block_scaled_precision_02_amd as q
+
+    log(f"[bench] config {cfg}: {name}")
+    d0 = inputs.make(name)
+    M, N, K = d0["M"], d0["N"], d0["K"]
+    R = cold_sets(d0)
+    flops = 2.0 * M * N * K
+    peak = PEAK[dtype_of(d0)]
+    sets = make_sets(d0, R)
+    out = torch.empty((M, N + (-N) % 8), dtype=torch.bfloat16, device="cuda")[:, :N]
+    stream = torch.cuda.current_stream()
+    q.force_tile(-1)
+    tile = q.select_tile({"i8": 0, "f8": 1, "e4m3": 2, "e2m1": 3}[dtype_of(d0)], M, N, K)
+    rec = {"config": cfg, "workload": workload_label(d0), "dtype": dtype_of(d0), "unit": unit_of(d0),
+           "peak": peak, "tile_id": tile, "input_sha256": inputs.digest(d0)[:16],
+           "rotating_sets": R, "rotating_bytes": R * operand_bytes(d0)}
+    run = Launcher(d0, sets, out, stream.cuda_stream)
+    rec["gpu_busy_before"] = gpu_busy_percent()
+    if headline is not None:
+        # the contract's timing: W warmup steps, exactly K steps between two
+        # synchronisations, HIP events on the launch stream for the kernel
+        log(f"[bench] headline: warmup {args.warmup}, timing {args.steps} steps")
+        for i in range(args.warmup):
+            run(i)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(args.steps):
+            run(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        headline.update(d=d0, wall=wall, kernel_ms=ev0.elapsed_time(ev1) / args.steps, tile=tile, R=R)
+    with ClockSampler() as clk:
+        ms, n = time_passes(run, stream, R)
+    rec.update({"launches_per_pass": n, "passes": len(ms)})
+    rec.update(pass_stats(ms, flops, peak))
+    sclk = clk.summary()
+    rec["sclk_mhz"] = sclk
+    if sclk is not None:
+        rec["frac_at_sclk"] = round(rec["frac"] * 2400.0 / sclk["median"], 4)
+    # parity rows of the last cold launch (every set holds the same values)
+    rows = np.arange(M) if name in LATENCY_BOUND else sample_rows(M)
+    torch.cuda.synchronize()
+    got = out[torch.from_numpy(rows).cuda()].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    rec["_parity"] = [(d0, rows, got)]
+    # hot: one input set, everything it can keep in the caches
+    hot = Launcher(d0, sets[:1], out, stream.cuda_stream)
+    hms, hn = time_passes(hot, stream, 1)
+    rec["hot"] = dict(rotating_sets=1, launches_per_pass=hn, **pass_stats(hms, flops, peak))
+    if name in LATENCY_BOUND:
+        # the no-bias variant (its signed zeros checked by the parity leg),
+        # and the host-side cost apart: calls replayed from one HIP graph
+        d1 = dict(d0, bias=None)
+        nb = make_sets(d1, 1)
+        out1 = torch.empty_like(out)
+        Launcher(d1, nb, out1, stream.cuda_stream)(0)
+        torch.cuda.synchronize()
+        got1 = out1.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        rec["_parity"].append((d1, np.arange(M), got1))
+        ga = argparse.Namespace(graph=100, steps=1000, prepacked=False)
+        rec["graph"] = time_graph(d0, sets, out, ga)
+    else:
+        pk = Launcher(d0, sets, out, stream.cuda_stream, prepacked=True)
+        pms, pn = time_passes(pk, stream, R)
+        rec["prepacked"] = dict(launches_per_pass=pn, **pass_stats(pms, flops, peak))
+        ref = PAGES_REF_PREPACKED.get((name, M, N, K))
+        if ref is not None:
+            rec["prepacked"]["vs_pages"] = round(rec["prepacked"]["rate"] / ref, 4)
+    ref = PAGES_REF.get((name, M, N, K))
+    if ref is not None:
+        rec["vs_pages"] = round(rec["rate"] / ref, 4)
+    if (name, M, N, K) in PAGES_CONTEXT:
+        rec["pages_context"] = PAGES_CONTEXT[(name, M, N, K)]
+    del run, hot, sets, out
+    torch.cuda.empty_cache()
+    return rec
+
+
+def parity_verdict(items):
+    """The oracle on the kept output rows (CPU leg): INT8 bit for bit, FP8 /
+    MX within the per-element bound and the cosine floor."""
+    from tests import parity
+    res = {"rows": 0, "pass": True}
+    worst, cos = 0.0, 1.0
+    for d, rows, got in items:
+        ref, absdot, _ = parity.oracle_run(d, rows=rows)
+        res["rows"] += len(rows)
+        try:
+            w, c = parity.compare(d, got, ref, absdot, d["name"])
+            worst, cos = max(worst, w), min(cos, c)
+        except AssertionError as e:
+            res["pass"] = False
+            res["error"] = str(e)[:300]
+    if items[0][0]["kind"] == "i8":
+        res["check"] = "bit-exact"
+    else:
+        res.update(check="|err| <= 1e-2*sum|ab| + 1 ulp, cos >= 0.99999", worst_err_over_bound=round(worst, 4),
+                   cos=round(cos, 9))
+    return res
+
+
+def host_info():
+    info = {"nproc": os.cpu_count()}
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            k, _, v = line.partition(":")
+            if k.strip() == "Model name":
+                info["model"] = v.strip()
+            elif k.strip() == "Socket(s)":
+                info["sockets"] = v.strip()
+    except Exception:
+        pass
+    return info
+
+
+def roofline_of(d, kernel_ms, name, shape=False, prepacked=False):
+    M, N, K = d["M"], d["N"], d["K"]
+    flops = 2.0 * M * N * K
+    peak = PEAK[dtype_of(d)]
+    nbytes = min_bytes(d)
+    # below the ridge (peak ops per HBM byte) the call is bound by HBM, not MFMA
+    if flops / nbytes < peak * 1e12 / (HBM_GBPS * 1e9):
+        gbps = nbytes / (kernel_ms * 1e-3) / 1e9
+        r = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_GBPS, "unit": "GB/s",
+             "frac": round(gbps / HBM_GBPS, 4)}
+    else:
+        achieved = flops / (kernel_ms * 1e-3) / 1e12
+        r = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": unit_of(d),
+             "frac": round(achieved / peak, 4)}
+    r.update({"traffic": None if (shape or prepacked) else traffic_bytes(name), "kernel_ms": round(kernel_ms, 6),
+              "algorithmic_bytes": nbytes})
+    return r
+
+
+DTYPE_NAME = {"i8": "int8", "f8": "e4m3", "f8b": "e4m3", "e4m3": "mxfp8-e4m3", "e2m1": "mxfp4-e2m1",
+              "e4m3/e2m1": "mx-e4m3xe2m1"}
+
+
+def suite(args):
+    """The default run: the headline plus every workload's per-config record."""
+    import torch
+    headline = {}
+    recs = []
+    for cfg, name in SUITE:
+        if args.no_suite and name != HEADLINE:
+            continue
+        recs.append(bench_config(cfg, name, args, headline if name == HEADLINE else None))
+    d = headline["d"]
+    M, N, K = d["M"], d["N"], d["K"]
+    ms_per_step = headline["wall"] * 1e3 / args.steps
+    flops = 2.0 * M * N * K
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK[dtype_of(d)]
+    res = {
+        "metric": METRIC, "value": round(value, 3), "unit": unit_of(d), "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": DTYPE_NAME[dtype_of(d)], "data": "synthetic",
+        "config": {"workload": workload_label(d), "tile_id": headline["tile"], "rotating_sets": headline["R"],
+                   "pct_of_peak": round(100 * value / peak, 2)},
+        "roofline": roofline_of(d, headline["kernel_ms"], HEADLINE),
+        "cpu_baseline": None,
+    }
+    if (HEADLINE, M, N, K) in PAGES_CONTEXT:
+        res["config"]["pages_context"] = PAGES_CONTEXT[(HEADLINE, M, N, K)]
+    torch.cuda.synchronize()
+    if not args.no_cpu_baseline:
+        log("[bench] cpu leg: oracle baseline and parity of the kept rows")
+        res["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
+        for r in recs:
+            log(f"[bench] parity config {r['config']}")
+            r["parity"] = parity_verdict(r["_parity"])
+    for r in recs:
+        del r["_parity"]
+    res["per_config"] = recs
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="i8_qkv")
+    ap.add_argument("--workload", default=None,
+                    help="time one workload (default: the headline and every workload's per-config record)")
+    ap.add_argument("--no-suite", action="store_true", help="default run: the headline only")
     ap.add_argument("--rot", type=int, default=None, help="rotating input sets")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -427,16 +785,17 @@ def main():
     if args.quant:
         print(json.dumps(bench_quant(args)), flush=True)
         return
-    name = args.workload
+    if args.workload is None and not (args.shape or args.prepacked or args.graph or args.tile >= 0 or args.rot):
+        print(json.dumps(suite(args)), flush=True)
+        return
+    name = args.workload or HEADLINE
     shape = {}
     if args.shape:
         shape = dict(zip("MNK", (int(v) for v in args.shape.split(","))))
-    R = args.rot or ROT[name]
-    log(f"[bench] generating {name} {shape or ''} x{R}")
     d0 = inputs.make(name, **shape)
-    sets = [upload(d0)]
-    for r in range(1, R):
-        sets.append(upload(inputs.make(name, rot=r, **shape)))
+    R = args.rot or cold_sets(d0)
+    log(f"[bench] {name} {shape or ''} x{R}")
+    sets = make_sets(d0, R)
     M, N, K = d0["M"], d0["N"], d0["K"]
     out = torch.empty((M, N + (-N) % 8), dtype=torch.bfloat16, device="cuda")[:, :N]
     stream = torch.cuda.current_stream()
@@ -454,33 +813,20 @@ def main():
     ev1 = torch.cuda.Event(enable_timing=True)
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        run(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(args.steps):
+            run(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     flops = 2.0 * M * N * K
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (kernel_ms * 1e-3) / 1e12
     peak = PEAK[dtype_of(d0)]
-    nbytes = min_bytes(d0)
-    # below the ridge (peak ops per HBM byte) the call is bound by HBM, not MFMA
-    hbm_bound = flops / nbytes < peak * 1e12 / (HBM_GBPS * 1e9)
-    if hbm_bound:
-        gbps = nbytes / (kernel_ms * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_GBPS, "unit": "GB/s",
-                    "frac": round(gbps / HBM_GBPS, 4)}
-    else:
-        roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": unit_of(d0),
-                    "frac": round(achieved / peak, 4)}
-    roofline.update({"traffic": None if (shape or args.prepacked) else traffic_bytes(name),
-                     "kernel_ms": round(kernel_ms, 6),
-                     "algorithmic_bytes": nbytes})
-
+    ref = (PAGES_REF_PREPACKED if args.prepacked else PAGES_REF).get((name, M, N, K))
     res = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -491,16 +837,16 @@ def main():
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(value / PAGES_REF[(name, M, N, K)], 4) if (name, M, N, K) in PAGES_REF else None,
-        "dtype": {"i8": "int8", "f8": "e4m3", "f8b": "e4m3", "e4m3": "mxfp8-e4m3",
-                  "e2m1": "mxfp4-e2m1", "e4m3/e2m1": "mx-e4m3xe2m1"}[dtype_of(d0)],
+        "vs_baseline": round(value / ref, 4) if ref else None,
+        "dtype": DTYPE_NAME[dtype_of(d0)],
         "data": "synthetic",
-        "config": {"workload": f"{name} M={M} N={N} K={K}" + (" bias" if d0["bias"] is not None else "")
-                   + (" prepacked B" if args.prepacked else ""),
-                   "tile_id": tile, "rotating_sets": R, "pct_of_peak": round(100 * value / peak, 2)},
-        "roofline": roofline,
+        "config": {"workload": workload_label(d0, args.prepacked), "tile_id": tile, "rotating_sets": R,
+                   "pct_of_peak": round(100 * value / peak, 2), "sclk_mhz": clk.summary()},
+        "roofline": roofline_of(d0, kernel_ms, name, bool(shape), args.prepacked),
         "cpu_baseline": None,
     }
+    if (name, M, N, K) in PAGES_CONTEXT:
+        res["config"]["pages_context"] = PAGES_CONTEXT[(name, M, N, K)]
     if args.graph:
         res["config"]["graph"] = time_graph(d0, sets, out, args)
     if not args.no_cpu_baseline:

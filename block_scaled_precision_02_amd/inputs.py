@@ -114,6 +114,22 @@ def floor_log2(x):
     return e.astype(np.int64) - 1
 
 
+def _by_rows(fn, R, step, *outs):
+    """Run fn(r0, r1) over row ranges [r0, r1) of `step` rows (a multiple of
+    every block height involved, so each range holds whole blocks) on a small
+    thread pool; numpy releases the GIL inside its loops, and ranges keep
+    the float64 temporaries small.  The result does not depend on the split."""
+    import concurrent.futures
+    import os
+    spans = [(r0, min(R, r0 + step)) for r0 in range(0, R, step)]
+    if len(spans) <= 1:
+        for a, b in spans:
+            fn(a, b)
+        return
+    with concurrent.futures.ThreadPoolExecutor(min(16, os.cpu_count() or 4, len(spans))) as ex:
+        list(ex.map(lambda ab: fn(*ab), spans))
+
+
 def mx_quantise(x, fmt, block_rows):
     """MX-quantise x [R, K] (K % 32 == 0) with one ue8m0 scale per
     block_rows x 32 block.  Returns (codes [R, K] uint8, scales
@@ -121,15 +137,25 @@ def mx_quantise(x, fmt, block_rows):
     emax = 8 if fmt == "e4m3" else 2
     R, K = x.shape
     Rb = -(-R // block_rows)
-    pad = Rb * block_rows - R
-    xp = np.pad(np.abs(x), ((0, pad), (0, 0))) if pad else np.abs(x)
-    amax = xp.reshape(Rb, block_rows, K // 32, 32).max(axis=(1, 3))
-    X = np.where(amax > 0, floor_log2(np.where(amax > 0, amax, 1.0)) - emax, -127)
-    code = np.clip(X + 127, 0, 254).astype(np.uint8)
-    Xe = code.astype(np.int64) - 127
-    Xfull = np.repeat(np.repeat(Xe, block_rows, axis=0)[:R], 32, axis=1)
-    y = np.ldexp(np.asarray(x, dtype=np.float64), -Xfull)
-    return quantise(y, fmt), code
+    codes = np.empty((R, K), np.uint8)
+    scales = np.empty((Rb, K // 32), np.uint8)
+
+    def part(r0, r1):
+        xs = x[r0:r1]
+        n = r1 - r0
+        nb = -(-n // block_rows)
+        pad = nb * block_rows - n
+        xp = np.pad(np.abs(xs), ((0, pad), (0, 0))) if pad else np.abs(xs)
+        amax = xp.reshape(nb, block_rows, K // 32, 32).max(axis=(1, 3))
+        X = np.where(amax > 0, floor_log2(np.where(amax > 0, amax, 1.0)) - emax, -127)
+        code = np.clip(X + 127, 0, 254).astype(np.uint8)
+        scales[r0 // block_rows:r0 // block_rows + nb] = code
+        Xe = code.astype(np.int64) - 127
+        Xfull = np.repeat(np.repeat(Xe, block_rows, axis=0)[:n], 32, axis=1)
+        codes[r0:r1] = quantise(np.ldexp(np.asarray(xs, dtype=np.float64), -Xfull), fmt)
+
+    _by_rows(part, R, 256 if block_rows <= 256 else block_rows)
+    return codes, scales
 
 
 def block_quantise_e4m3(x, block_rows):
@@ -138,13 +164,43 @@ def block_quantise_e4m3(x, block_rows):
     (codes [R, K] uint8, scales [ceil(R/block_rows), K/128] float32)."""
     R, K = x.shape
     Rb = -(-R // block_rows)
-    pad = Rb * block_rows - R
-    xp = np.pad(np.abs(x), ((0, pad), (0, 0))) if pad else np.abs(x)
-    amax = xp.reshape(Rb, block_rows, K // 128, 128).max(axis=(1, 3)).astype(np.float32)
-    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
-    s = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
-    sfull = np.repeat(np.repeat(s, block_rows, axis=0)[:R], 128, axis=1)
-    return quantise(np.asarray(x, np.float32) / sfull, "e4m3"), s
+    codes = np.empty((R, K), np.uint8)
+    scales = np.empty((Rb, K // 128), np.float32)
+
+    def part(r0, r1):
+        xs = x[r0:r1]
+        n = r1 - r0
+        nb = -(-n // block_rows)
+        pad = nb * block_rows - n
+        xp = np.pad(np.abs(xs), ((0, pad), (0, 0))) if pad else np.abs(xs)
+        amax = xp.reshape(nb, block_rows, K // 128, 128).max(axis=(1, 3)).astype(np.float32)
+        s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+        s = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+        scales[r0 // block_rows:r0 // block_rows + nb] = s
+        sfull = np.repeat(np.repeat(s, block_rows, axis=0)[:n], 128, axis=1)
+        codes[r0:r1] = quantise(np.asarray(xs, np.float32) / sfull, "e4m3")
+
+    _by_rows(part, R, 256 if block_rows <= 256 else block_rows)
+    return codes, scales
+
+
+def rowwise_quantise_e4m3(x):
+    """Per-row e4m3: s = amax/448 (fp32; an all-zero row gets s = 1), codes =
+    e4m3(x/s).  Returns (codes [R, K] uint8, s [R] float32)."""
+    R, K = x.shape
+    codes = np.empty((R, K), np.uint8)
+    scales = np.empty(R, np.float32)
+
+    def part(r0, r1):
+        xs = x[r0:r1]
+        amax = np.abs(xs).max(axis=1)
+        s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+        s = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+        scales[r0:r1] = s
+        codes[r0:r1] = quantise(xs / s[:, None], "e4m3")
+
+    _by_rows(part, R, 256)
+    return codes, scales
 
 
 def bf16_bits(x):
@@ -197,11 +253,7 @@ def make(name, rot=0, M=None, N=None, K=None, bias=None, seed=None):
     elif kind == "f8":
         for tid, rows, key in ((0, M, "A"), (1, N, "B")):
             x = rng(seed, tid, rot).standard_normal(size=(rows, K), dtype=np.float32)
-            amax = np.abs(x).max(axis=1)
-            s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
-            s = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
-            d[key] = quantise(x / s[:, None], "e4m3")
-            d["scale_a" if key == "A" else "scale_b"] = s
+            d[key], d["scale_a" if key == "A" else "scale_b"] = rowwise_quantise_e4m3(x)
     elif kind == "f8b":
         for tid, rows, br, key in ((0, M, 1, "A"), (1, N, 128, "B")):
             x = rng(seed, tid, rot).standard_normal(size=(rows, K), dtype=np.float32)

@@ -129,3 +129,50 @@ def compare(d, got_bits, ref_bits, absdot, what):
                                  f"{i}: gpu={got_bits[i]:#06x} oracle={ref_bits[i]:#06x}")
         return 0.0, 1.0
     return check_tolerance(got_bits, ref_bits, absdot, what)
+
+
+# ------------------------------------------------------------ full grids
+
+PATH_OF = {"i8": 0, "f8": 1, "f8b": 4}
+
+
+def path_of(d):
+    if d["kind"] in PATH_OF:
+        return PATH_OF[d["kind"]]
+    if "/" in (d["fmt"] or ""):
+        return 5
+    return 2 if d["fmt"] == "e4m3" else 3
+
+
+def nan_out(M, N):
+    """An exact [M, N] bf16 output filled with NaN: a tile the kernel never
+    writes keeps its NaNs (no workload here produces a NaN itself)."""
+    return torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+
+
+def band_rows(M, bm, extra=()):
+    """The first and the last row of every bm-row band of C, plus `extra`:
+    every tile of the grid contributes its first and its last row."""
+    starts = np.arange(0, M, bm)
+    ends = np.minimum(starts + bm, M) - 1
+    return np.unique(np.concatenate([starts, ends, np.asarray(extra, dtype=np.int64)]))
+
+
+def check_full_grid(d, out, tile, what, extra=()):
+    """After a launch into nan_out(): no NaN anywhere in [0,M) x [0,N) (every
+    tile was written), and the first and last row of each tile band (all
+    columns) equal to the oracle to the path's bar.  `tile` is the tile id the
+    launch ran (-1: the table's choice for this shape)."""
+    M, N = d["M"], d["N"]
+    torch.cuda.synchronize()
+    nan = torch.isnan(out)
+    if bool(nan.any()):
+        where = torch.nonzero(nan)[:5].cpu().numpy().tolist()
+        raise AssertionError(f"{what}: {int(nan.sum())} outputs never written; first at {where}")
+    if tile < 0:
+        tile = q.select_tile(path_of(d), M, N, d["K"])
+    rows = band_rows(M, q.tile_rows(tile), extra)
+    got = bits(out[torch.from_numpy(rows).cuda()])
+    ref, absdot, _ = oracle_run(d, rows=rows)
+    worst, cos = compare(d, got, ref, absdot, what)
+    return worst, cos, len(rows)

@@ -152,13 +152,9 @@ def test_partial_round_full_size_mxfp8():
     d = inputs.make("mxfp8", K=2176)
     assert q.select_tile(2, d["M"], d["N"], d["K"]) == 5
     _say(f"[ktail] full mxfp8 {d['M']}x{d['N']}x{d['K']}")
-    out = parity.gpu_run(d)
-    torch.cuda.synchronize()
+    out = parity.gpu_run(d, out=parity.nan_out(d["M"], d["N"]))
     rng = np.random.default_rng(3)
-    rows = np.unique(np.concatenate([np.arange(8), rng.choice(d["M"], 16, replace=False), np.arange(d["M"] - 8, d["M"])]))
-    got = parity.bits(out[torch.from_numpy(rows).cuda()])
-    ref, absdot, _ = parity.oracle_run(d, rows=rows)
-    parity.compare(d, got, ref, absdot, "ktail full mxfp8")
+    parity.check_full_grid(d, out, -1, "ktail full mxfp8", rng.choice(d["M"], 16, replace=False))
 
 
 @pytest.mark.parametrize("name,tile", [("f8_block", 8), ("f8_block", 9), ("mx_a8w4", 8), ("mxfp8", 8),
@@ -176,15 +172,12 @@ def test_small_m_kernel_k_not_multiple_of_256(name, tile, K):
 def test_partial_round_full_size(name, shape, path, tile):
     """Blockscale 16384 x 7168 x 2176 (17 blocks: a last round of one block)
     and INT8 30000 x 21504 x 5440 (85 stages: a last round of one stage), in
-    the launch the benchmark uses, on sampled whole rows."""
+    the launch the benchmark uses, into a NaN-filled C; the first and last
+    row of every tile band and random rows."""
     M, N, K = shape
     assert q.select_tile(path, M, N, K) == tile
     d = inputs.make(name, M=M, N=N, K=K)
     _say(f"[ktail] full {name} {M}x{N}x{K}")
-    out = parity.gpu_run(d)
-    torch.cuda.synchronize()
+    out = parity.gpu_run(d, out=parity.nan_out(M, N))
     rng = np.random.default_rng(4)
-    rows = np.unique(np.concatenate([np.arange(8), rng.choice(M, 12, replace=False), np.arange(M - 8, M)]))
-    got = parity.bits(out[torch.from_numpy(rows).cuda()])
-    ref, absdot, _ = parity.oracle_run(d, rows=rows)
-    parity.compare(d, got, ref, absdot, f"ktail full {name}")
+    parity.check_full_grid(d, out, tile, f"ktail full {name}", rng.choice(M, 12, replace=False))

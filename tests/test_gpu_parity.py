@@ -335,20 +335,17 @@ def _sample_rows(M, n, rng):
 @pytest.mark.parametrize("tile", [-1, 4, 5, 6])
 @pytest.mark.parametrize("name", ["f8_ptpc", "mxfp8", "mxfp4", "i8_qkv"])
 def test_full_workload_sampled(name, tile):
-    """The workload at its full size, launched as the benchmark launches it;
-    the oracle checks a sample of whole output rows (first, last -- inside
-    the partial tile when M is not a tile multiple -- and random ones)."""
+    """The workload at its full size, launched as the benchmark launches it
+    (and on each LDS-fetch tile), into a NaN-filled C: every output written,
+    and the first and last row of every tile band plus random rows (all
+    columns) against the oracle."""
     d = inputs.make(name)
     _say(f"[parity] full {name} M={d['M']} N={d['N']} K={d['K']} tile {tile}")
     q.force_tile(tile)
-    out = parity.gpu_run(d)
-    torch.cuda.synchronize()
-    rng = np.random.default_rng(1)
-    rows = _sample_rows(d["M"], 24, rng)
-    got = parity.bits(out[torch.from_numpy(rows).cuda()])
-    ref, absdot, _ = parity.oracle_run(d, rows=rows)
-    worst, cos = parity.compare(d, got, ref, absdot, f"full {name}")
-    _say(f"[parity] full {name}: worst err/bound {worst:.3g} cos {cos:.8f}")
+    out = parity.gpu_run(d, out=parity.nan_out(d["M"], d["N"]))
+    extra = _sample_rows(d["M"], 24, np.random.default_rng(1))
+    worst, cos, n = parity.check_full_grid(d, out, tile, f"full {name} tile {tile}", extra)
+    _say(f"[parity] full {name}: {n} rows, worst err/bound {worst:.3g} cos {cos:.8f}")
 
 
 @pytest.mark.parametrize("tile", [4, 5, 6, 7])
@@ -376,12 +373,9 @@ def test_mx8_pages_shape_sampled():
     d = inputs.make("mxfp8", M=32768, N=7168, K=1792)
     assert q.select_tile(2, 32768, 7168, 1792) == 5
     _say("[parity] full mxfp8 32768x7168x1792")
-    out = parity.gpu_run(d)
-    torch.cuda.synchronize()
-    rows = _sample_rows(d["M"], 16, np.random.default_rng(4))
-    got = parity.bits(out[torch.from_numpy(rows).cuda()])
-    ref, absdot, _ = parity.oracle_run(d, rows=rows)
-    worst, cos = parity.compare(d, got, ref, absdot, "full mxfp8 32768x7168x1792")
+    out = parity.gpu_run(d, out=parity.nan_out(d["M"], d["N"]))
+    worst, cos, _ = parity.check_full_grid(d, out, -1, "full mxfp8 32768x7168x1792",
+                                           _sample_rows(d["M"], 16, np.random.default_rng(4)))
     _say(f"[parity] full mxfp8 32768x7168x1792: worst err/bound {worst:.3g} cos {cos:.8f}")
 
 
