@@ -26,6 +26,11 @@ rotating input set):
   mx_a8w4    MX with e4m3 A (activations) and e2m1 B (weights), M=N=K=8192
              (seed 107): A as mxfp8's A, B as mxfp4's B, 1x32 scales on both
              ([M,K/32], [N,K/32]); no bias.
+  mxfp6      MX e2m3 (OCP FP6) M=N=K=8192 (seed 108): as mxfp4 with the
+             6-bit E2M3 element (emax 2: X = floor(log2(amax)) - 2), four
+             codes per three bytes (element k in bits 6k..6k+5 of the row,
+             lowest bits first), 1x32 scales on both operands; no bias.
+  mxfp6_e3m2 the same with the E3M2 element (emax 4), seed 109.
   f8_block   FP8 e4m3 with block scales, M=16384 N=7168 K=2048 (seed 106):
              A, B ~ N(0,1) (fp32); s = amax/448 (fp32) per 1x128 block of A
              (scale_A [M, K/128]) and per 128x128 block of B (scale_B
@@ -51,6 +56,8 @@ WORKLOADS = {
     "i8_qkv": ("i8", 30000, 21504, 5376, 105, True, None, None),
     "f8_block": ("f8b", 16384, 7168, 2048, 106, False, None, 128),
     "mx_a8w4": ("mx", 8192, 8192, 8192, 107, False, "e4m3/e2m1", 1),
+    "mxfp6": ("mx", 8192, 8192, 8192, 108, False, "e2m3", 1),
+    "mxfp6_e3m2": ("mx", 8192, 8192, 8192, 109, False, "e3m2", 1),
 }
 ORDER = ["i8_small", "f8_ptpc", "mxfp8", "mxfp4", "i8_qkv"]
 
@@ -74,12 +81,20 @@ def _e4m3_grid():
 
 # OCP MX v1.0 FP4 E2M1 magnitudes in code order 0..7.
 _E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+# OCP MX v1.0 FP6 magnitudes in code order 0..31: E2M3 (exponent bias 1, three
+# mantissa bits) and E3M2 (bias 3, two mantissa bits); exponent 0 subnormal.
+_E2M3_GRID = np.array([m / 8 for m in range(8)] + [(1 + m / 8) * 2.0 ** (e - 1) for e in (1, 2, 3) for m in range(8)])
+_E3M2_GRID = np.array([m / 16 for m in range(4)] + [(1 + m / 4) * 2.0 ** (e - 3) for e in range(1, 8) for m in range(4)])
+_GRIDS = {"e2m1": _E2M1_GRID, "e2m3": _E2M3_GRID, "e3m2": _E3M2_GRID}
+# largest exponent of each element type (the MX shared-exponent rule)
+EMAX = {"e4m3": 8, "e2m1": 2, "e2m3": 2, "e3m2": 4}
+SIGN_BIT = {"e4m3": 0x80, "e2m1": 0x8, "e2m3": 0x20, "e3m2": 0x20}
 _grid_cache = {}
 
 
 def _grid(fmt):
     if fmt not in _grid_cache:
-        _grid_cache[fmt] = _e4m3_grid() if fmt == "e4m3" else _E2M1_GRID
+        _grid_cache[fmt] = _e4m3_grid() if fmt == "e4m3" else _GRIDS[fmt]
     return _grid_cache[fmt]
 
 
@@ -97,7 +112,7 @@ def quantise(x, fmt):
     dhi = grid[hi] - ax
     pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
     code = np.where(pick_hi, hi, lo).astype(np.uint8)
-    sign_bit = 0x80 if fmt == "e4m3" else 0x8
+    sign_bit = SIGN_BIT[fmt]
     neg = np.signbit(x) & (code != 0)
     return np.where(neg, code | sign_bit, code).astype(np.uint8)
 
@@ -106,6 +121,23 @@ def pack_e2m1(codes):
     """[R, K] 4-bit codes -> [R, K/2] bytes, element k even in the low nibble."""
     codes = np.asarray(codes, dtype=np.uint8)
     return (codes[:, 0::2] & 15) | ((codes[:, 1::2] & 15) << 4)
+
+
+def pack_fp6(codes):
+    """[R, K] 6-bit codes (K % 4 == 0) -> [R, 3K/4] bytes: element k in bits
+    6k..6k+5 of the row, the row's bit b being bit b % 8 of byte b / 8."""
+    c = np.asarray(codes, dtype=np.uint8).reshape(codes.shape[0], -1, 4) & 63
+    c0, c1, c2, c3 = (c[..., i] for i in range(4))
+    out = np.stack([c0 | (c1 << 6), (c1 >> 2) | (c2 << 4), (c2 >> 4) | (c3 << 2)], axis=-1)
+    return out.reshape(codes.shape[0], -1).astype(np.uint8)
+
+
+def row_bytes(fmt, K):
+    return K if fmt == "e4m3" else K // 2 if fmt == "e2m1" else 3 * K // 4
+
+
+def pack(codes, fmt):
+    return pack_e2m1(codes) if fmt == "e2m1" else pack_fp6(codes) if fmt in ("e2m3", "e3m2") else codes
 
 
 def floor_log2(x):
@@ -134,7 +166,7 @@ def mx_quantise(x, fmt, block_rows):
     """MX-quantise x [R, K] (K % 32 == 0) with one ue8m0 scale per
     block_rows x 32 block.  Returns (codes [R, K] uint8, scales
     [ceil(R/block_rows), K/32] uint8)."""
-    emax = 8 if fmt == "e4m3" else 2
+    emax = EMAX[fmt]
     R, K = x.shape
     Rb = -(-R // block_rows)
     codes = np.empty((R, K), np.uint8)
@@ -268,11 +300,7 @@ def make(name, rot=0, M=None, N=None, K=None, bias=None, seed=None):
         xb = rng(seed, 1, rot).standard_normal(size=(N, K), dtype=np.float32)
         cb, sb = mx_quantise(xb, fb, brows)
         del xb
-        if fa == "e2m1":
-            ca = pack_e2m1(ca)
-        if fb == "e2m1":
-            cb = pack_e2m1(cb)
-        d.update(A=ca, B=cb, scale_a=sa, scale_b=sb)
+        d.update(A=pack(ca, fa), B=pack(cb, fb), scale_a=sa, scale_b=sb)
     else:
         raise ValueError(name)
     d["bias"] = (bf16_bits(rng(seed, 4, rot).standard_normal(size=N).astype(np.float32))

@@ -15,6 +15,8 @@ Functions follow the definitions in ``qgemm_oracle.c``:
                   #806, What; ROCm/FlyDSL PR #990).
   mx2          -- MX with its own element format per operand (e.g. e4m3
                   activations x e2m1 weights); the same scale rule.
+  mxf          -- MX with any of e4m3, e2m1 and the 6-bit e2m3 / e3m2
+                  (OCP Microscaling v1.0's FP6) per operand; the same rule.
   f8_blockscale
                -- FP8 e4m3 with fp32 scales per 128-element K block: A per
                   row, B per 128 rows (ROCm/mori PR #806, commit message
@@ -45,6 +47,8 @@ _I64 = ctypes.c_int64
 
 MX_E4M3 = 0
 MX_E2M1 = 1
+MX_E2M3 = 2
+MX_E3M2 = 3
 
 
 def build(force=True):
@@ -74,8 +78,19 @@ def _load():
     lib.orc_bf16_rne.restype = ctypes.c_uint16
     lib.orc_bf16_rne.argtypes = [ctypes.c_float]
     lib.orc_num_threads.restype = ctypes.c_int
+    lib.orc_dec_e2m3.restype = ctypes.c_double
+    lib.orc_dec_e2m3.argtypes = [ctypes.c_uint8]
+    lib.orc_dec_e3m2.restype = ctypes.c_double
+    lib.orc_dec_e3m2.argtypes = [ctypes.c_uint8]
+    lib.orc_mx_codes.restype = None
+    lib.orc_mx_codes.argtypes = [ctypes.c_int, _P, _I64, _P]
+    lib.orc_mx_row_bytes.restype = _I64
+    lib.orc_mx_row_bytes.argtypes = [ctypes.c_int, _I64]
+    lib.orc_mxf.restype = ctypes.c_int
+    lib.orc_mxf.argtypes = [ctypes.c_int, ctypes.c_int, _P, _I64, _P, _I64, _P, _P, ctypes.c_int, _P,
+                            _P, _I64, _P, _P, _I64, _I64, _I64]
     for name in ("orc_dec_e4m3_array", "orc_dec_e2m1_array", "orc_dec_ue8m0_array",
-                 "orc_bf16_rne_array"):
+                 "orc_bf16_rne_array", "orc_dec_e2m3_array", "orc_dec_e3m2_array"):
         getattr(lib, name).restype = None
         getattr(lib, name).argtypes = [_P, _P, _I64]
     for name in ("orc_enc_e4m3_array", "orc_enc_e2m1_array"):
@@ -241,6 +256,59 @@ def mx2(fmt_a, fmt_b, A, B, scale_a, scale_b, b_rows_per_scale, K, bias=None):
                          b_rows_per_scale, _ptr(bias), _ptr(C), N, _ptr(acc), _ptr(absdot), M, N, K)
     if rc != 0:
         raise ValueError("bad MX format or B-scale layout")
+    return C, acc, absdot
+
+
+def dec_e2m3(codes):
+    c = _c(codes, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _load().orc_dec_e2m3_array(_ptr(c), _ptr(out), c.size)
+    return out
+
+
+def dec_e3m2(codes):
+    c = _c(codes, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _load().orc_dec_e3m2_array(_ptr(c), _ptr(out), c.size)
+    return out
+
+
+def mx_row_bytes(fmt, K):
+    return int(_load().orc_mx_row_bytes(fmt, K))
+
+
+def mx_codes(fmt, row, K):
+    """Element codes 0..K-1 of one packed MX operand row (the element layout
+    the oracle reads)."""
+    r = _c(row, np.uint8)
+    assert r.size >= mx_row_bytes(fmt, K)
+    out = np.empty(K, np.uint8)
+    _load().orc_mx_codes(fmt, _ptr(r), K, _ptr(out))
+    return out
+
+
+def mxf(fmt_a, fmt_b, A, B, scale_a, scale_b, b_rows_per_scale, K, bias=None):
+    """MX GEMM with any of MX_E4M3, MX_E2M1, MX_E2M3, MX_E3M2 per operand
+    (rows of K, K/2, 3K/4 and 3K/4 bytes; 6-bit elements packed lowest bits
+    first, four in three bytes).  Scales as for mx.
+    Returns (C uint16 [M,N], acc float64 [M,N], absdot float64 [M,N])."""
+    A = _c(A, np.uint8)
+    B = _c(B, np.uint8)
+    M, N = A.shape[0], B.shape[0]
+    row_a, row_b = mx_row_bytes(fmt_a, K), mx_row_bytes(fmt_b, K)
+    assert A.shape[1] == row_a and B.shape[1] == row_b and K % 32 == 0
+    sa = _c(scale_a, np.uint8)
+    sb = _c(scale_b, np.uint8)
+    assert sa.shape == (M, K // 32)
+    assert sb.shape == ((N + b_rows_per_scale - 1) // b_rows_per_scale, K // 32)
+    bias = _c(bias, np.uint16)
+    C = np.empty((M, N), np.uint16)
+    acc = np.empty((M, N), np.float64)
+    absdot = np.empty((M, N), np.float64)
+    rc = _load().orc_mxf(fmt_a, fmt_b, _ptr(A), row_a, _ptr(B), row_b, _ptr(sa), _ptr(sb),
+                         b_rows_per_scale, _ptr(bias), _ptr(C), N, _ptr(acc), _ptr(absdot), M, N, K)
+    if rc != 0:
+        raise ValueError("bad MX format, B-scale layout or K")
     return C, acc, absdot
 
 

@@ -64,6 +64,26 @@ double orc_dec_e2m1(uint8_t nibble)
     return s ? -v : v;
 }
 
+/* FP6 E2M3 (OCP Microscaling v1.0): sign (bit 5), 2-bit exponent (bias 1),
+ * 3-bit mantissa; exponent field 0 is subnormal (m * 2^-3); every code is
+ * finite; the largest magnitude is 1.875 * 2^2 = 7.5. */
+double orc_dec_e2m3(uint8_t code)
+{
+    int s = (code >> 5) & 1, e = (code >> 3) & 3, m = code & 7;
+    double v = (e == 0) ? ldexp((double)m, -3) : ldexp((double)(8 + m), e - 4);
+    return s ? -v : v;
+}
+
+/* FP6 E3M2 (OCP Microscaling v1.0): sign (bit 5), 3-bit exponent (bias 3),
+ * 2-bit mantissa; exponent field 0 is subnormal (m * 2^-4); every code is
+ * finite; the largest magnitude is 1.75 * 2^4 = 28. */
+double orc_dec_e3m2(uint8_t code)
+{
+    int s = (code >> 5) & 1, e = (code >> 2) & 7, m = code & 3;
+    double v = (e == 0) ? ldexp((double)m, -4) : ldexp((double)(4 + m), e - 5);
+    return s ? -v : v;
+}
+
 /* E8M0 (unsigned, exponent only, bias 127): code c is 2^(c-127), 255 is NaN. */
 double orc_dec_ue8m0(uint8_t code)
 {
@@ -308,6 +328,94 @@ int orc_mx2(int fmt_a, int fmt_b, const uint8_t *A, int64_t lda, const uint8_t *
                 }
                 a *= lut_s[sarow[k / 32]];
                 b *= lut_s[sbrow[k / 32]];
+                const double p = a * b;
+                s += p;
+                t += fabs(p);
+            }
+            if (acc)
+                acc[m * N + n] = s;
+            if (absdot)
+                absdot[m * N + n] = t;
+            float f = (float)s;
+            if (bias)
+                f = f + orc_bf16_to_f32(bias[n]);
+            C[m * ldc + n] = orc_bf16_rne(f);
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------ MX, any element format */
+
+/* Element k of an MX operand row in format fmt, as its code:
+ *   0 e4m3: byte k;
+ *   1 e2m1: the low nibble of byte k/2 when k is even, the high one when odd;
+ *   2 e2m3, 3 e3m2 (6-bit): bits 6k .. 6k+5 of the row read as one bit string
+ *     whose bit b is bit (b mod 8) of byte b/8 -- four elements in three
+ *     bytes, the lowest bits first, as e2m1 keeps its even element in the
+ *     low nibble. */
+static unsigned mx_code(const uint8_t *row, int64_t k, int fmt)
+{
+    if (fmt == 0)
+        return row[k];
+    if (fmt == 1)
+        return (k & 1) ? (row[k / 2] >> 4) : (row[k / 2] & 15);
+    const int64_t bit = 6 * k;
+    const int sh = (int)(bit & 7);
+    unsigned v = (unsigned)row[bit >> 3] >> sh;
+    if (sh > 2)
+        v |= (unsigned)row[(bit >> 3) + 1] << (8 - sh);
+    return v & 63;
+}
+
+/* Bytes of an MX operand row of K elements in format fmt. */
+int64_t orc_mx_row_bytes(int fmt, int64_t K)
+{
+    return fmt == 0 ? K : fmt == 1 ? K / 2 : 3 * K / 4;
+}
+
+/* MX GEMM with an element format per operand, any of e4m3 (0), e2m1 (1) and
+ * the two 6-bit formats e2m3 (2) and e3m2 (3) that OCP Microscaling v1.0
+ * defines next to them (the pages name MX e4m3 and e2m1; MXFP6 is the same
+ * block rule with 6-bit elements).  Element layout as mx_code; lda / ldb are
+ * row strides in bytes; scales, bias, acc, absdot and the epilogue as orc_mx:
+ *
+ *   A~[m,k] = dec(A[m,k]) * 2^(SA[m,k/32]-127), B~ likewise,
+ *   acc = sum_k A~ B~ (double), f = (float)acc; [f = f + bias[n]];
+ *   C = bf16_rne(f).
+ *
+ * Every 6-bit value is a multiple of 2^-3 (e2m3) or 2^-4 (e3m2) of magnitude
+ * at most 7.5 or 28, so each product is exact in double and the sum is exact
+ * under the scale-spread bound of orc_mx.  K must be a multiple of 32 (of 4
+ * for whole bytes of 6-bit rows, which 32 implies).
+ * Returns 0, or -1 for an unknown format / b_rows_per_scale. */
+int orc_mxf(int fmt_a, int fmt_b, const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+            const uint8_t *scale_a, const uint8_t *scale_b, int b_rows_per_scale,
+            const uint16_t *bias, uint16_t *C, int64_t ldc, double *acc, double *absdot,
+            int64_t M, int64_t N, int64_t K)
+{
+    if (fmt_a < 0 || fmt_a > 3 || fmt_b < 0 || fmt_b > 3 || (b_rows_per_scale != 1 && b_rows_per_scale != 32) ||
+        K % 32 != 0)
+        return -1;
+    const int64_t KB = K / 32;
+    double lut[4][256], lut_s[256];
+    for (int c = 0; c < 256; ++c) {
+        lut[0][c] = orc_dec_e4m3((uint8_t)c);
+        lut[1][c] = c < 16 ? orc_dec_e2m1((uint8_t)c) : 0.0;
+        lut[2][c] = c < 64 ? orc_dec_e2m3((uint8_t)c) : 0.0;
+        lut[3][c] = c < 64 ? orc_dec_e3m2((uint8_t)c) : 0.0;
+        lut_s[c] = orc_dec_ue8m0((uint8_t)c);
+    }
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            const uint8_t *arow = A + m * lda, *brow = B + n * ldb;
+            const uint8_t *sarow = scale_a + m * KB;
+            const uint8_t *sbrow = scale_b + (n / b_rows_per_scale) * KB;
+            double s = 0.0, t = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double a = lut[fmt_a][mx_code(arow, k, fmt_a)] * lut_s[sarow[k / 32]];
+                const double b = lut[fmt_b][mx_code(brow, k, fmt_b)] * lut_s[sbrow[k / 32]];
                 const double p = a * b;
                 s += p;
                 t += fabs(p);
@@ -613,6 +721,25 @@ void orc_dec_e2m1_array(const uint8_t *nibbles, double *out, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i)
         out[i] = orc_dec_e2m1(nibbles[i]);
+}
+
+void orc_dec_e2m3_array(const uint8_t *codes, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_dec_e2m3(codes[i]);
+}
+
+void orc_dec_e3m2_array(const uint8_t *codes, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_dec_e3m2(codes[i]);
+}
+
+/* Element codes of an MX operand row (mx_code), for the tests' packing pins. */
+void orc_mx_codes(int fmt, const uint8_t *row, int64_t K, uint8_t *out)
+{
+    for (int64_t k = 0; k < K; ++k)
+        out[k] = (uint8_t)mx_code(row, k, fmt);
 }
 
 void orc_dec_ue8m0_array(const uint8_t *codes, double *out, int64_t n)
