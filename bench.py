@@ -22,7 +22,8 @@ output rows against the CPU oracle.  The oracle also gives the CPU baseline
 
 --workload picks one workload instead (i8_small, f8_ptpc, mxfp8, mxfp4,
 i8_qkv, f8_block: FP8 with fp32 scales per 128-element K block,
-16384x7168x2048; mx_a8w4: MX e4m3 A x e2m1 B, 8192^3).
+16384x7168x2048; mx_a8w4: MX e4m3 A x e2m1 B, 8192^3; mxfp6 / mxfp6_e3m2: MX
+with the 6-bit E2M3 / E3M2 elements, 8192^3).
 """
 import argparse
 import ctypes
@@ -40,7 +41,8 @@ METRIC = "effective TFLOPS/TOPS (2MNK/t) per dtype; % of MI355X dense MFMA peak"
 # MI355X dense matrix-core peaks (TOPS / TFLOPS) and HBM bandwidth (GB/s)
 # (e4m3 x e2m1 MX runs at the e4m3 rate: the scaled MFMA takes 64 cycles when
 # either operand is 8-bit)
-PEAK = {"i8": 5000.0, "f8": 5000.0, "f8b": 5000.0, "e4m3": 5000.0, "e2m1": 10100.0, "e4m3/e2m1": 5000.0}
+PEAK = {"i8": 5000.0, "f8": 5000.0, "f8b": 5000.0, "e4m3": 5000.0, "e2m1": 10100.0, "e4m3/e2m1": 5000.0,
+        "e2m3": 10100.0, "e3m2": 10100.0}
 HBM_GBPS = 8000.0
 # The pages' numbers for exactly these workloads (2MNK / their time where they
 # give a time); context, not targets:
@@ -84,6 +86,10 @@ def unit_of(d):
     return "TOPS" if d["kind"] == "i8" else "TFLOPS"
 
 
+MX_FMT = {"e4m3": 0, "e2m1": 1, "e2m3": 2, "e3m2": 3}
+ROW_BYTES = {"e4m3": lambda K: K, "e2m1": lambda K: K // 2, "e2m3": lambda K: 3 * K // 4, "e3m2": lambda K: 3 * K // 4}
+
+
 class Launcher:
     """Binds one workload's device buffers to a direct C-ABI call (the
     binding's argument checks are done once, outside the timed loop)."""
@@ -122,7 +128,7 @@ class Launcher:
                     fn = self.L.qgemm_f8_pertoken_prepacked if d["kind"] == "f8" else self.L.qgemm_f8_blockscale_prepacked
                     self.args.append((fn, a))
                 else:
-                    fmt = 0 if d["fmt"] == "e4m3" else 1
+                    fmt = MX_FMT[d["fmt"]]
                     a = (fmt, s["A"].data_ptr(), s["A"].stride(0), pb.data_ptr(), s["scale_a"].data_ptr(),
                          s["scale_b"].data_ptr(), d["b_rows_per_scale"], bias, out.data_ptr(), self.ldc, d["M"], N,
                          d["K"], self.stream)
@@ -150,7 +156,7 @@ class Launcher:
                      out.data_ptr(), self.ldc, d["M"], N, d["K"], self.stream)
                 self.args.append((self.L.qgemm_mx_mixed, a))
             else:
-                fmt = 0 if d["fmt"] == "e4m3" else 1
+                fmt = MX_FMT[d["fmt"]]
                 a = (fmt, s["A"].data_ptr(), s["A"].stride(0), s["B"].data_ptr(), s["B"].stride(0),
                      s["scale_a"].data_ptr(), s["scale_b"].data_ptr(), d["b_rows_per_scale"], bias,
                      out.data_ptr(), self.ldc, d["M"], N, d["K"], self.stream)
@@ -196,7 +202,7 @@ def min_bytes(d):
     M, N, K = d["M"], d["N"], d["K"]
     fmts = (d.get("fmt") or "").split("/")
     fa, fb = (fmts[0], fmts[-1]) if fmts[0] else (None, None)
-    ab = M * (K // 2 if fa == "e2m1" else K) + N * (K // 2 if fb == "e2m1" else K)
+    ab = M * (ROW_BYTES[fa](K) if fa else K) + N * (ROW_BYTES[fb](K) if fb else K)
     if d["kind"] == "mx":
         sc = M * (K // 32) + (-(-N // d["b_rows_per_scale"])) * (K // 32)
     elif d["kind"] == "f8b":
@@ -691,7 +697,7 @@ def roofline_of(d, kernel_ms, name, shape=False, prepacked=False):
 
 
 DTYPE_NAME = {"i8": "int8", "f8": "e4m3", "f8b": "e4m3", "e4m3": "mxfp8-e4m3", "e2m1": "mxfp4-e2m1",
-              "e4m3/e2m1": "mx-e4m3xe2m1"}
+              "e4m3/e2m1": "mx-e4m3xe2m1", "e2m3": "mxfp6-e2m3", "e3m2": "mxfp6-e3m2"}
 
 
 def suite(args):
@@ -800,7 +806,8 @@ def main():
     out = torch.empty((M, N + (-N) % 8), dtype=torch.bfloat16, device="cuda")[:, :N]
     stream = torch.cuda.current_stream()
     run = Launcher(d0, sets, out, stream.cuda_stream, prepacked=args.prepacked)
-    tile = q.select_tile({"i8": 0, "f8": 1, "e4m3": 2, "e2m1": 3, "f8b": 4, "e4m3/e2m1": 5}[dtype_of(d0)], M, N, K)
+    tile = q.select_tile({"i8": 0, "f8": 1, "e4m3": 2, "e2m1": 3, "f8b": 4, "e4m3/e2m1": 5, "e2m3": 6,
+                          "e3m2": 7}[dtype_of(d0)], M, N, K)
     if args.tile >= 0:
         q.force_tile(args.tile)
         tile = args.tile

@@ -46,6 +46,8 @@ QGEMM_ERR_HIP = 6
 
 QGEMM_MX_E4M3 = 0
 QGEMM_MX_E2M1 = 1
+QGEMM_MX_E2M3 = 2
+QGEMM_MX_E3M2 = 3
 QGEMM_MX_BSCALE_1x32 = 1
 QGEMM_MX_BSCALE_32x32 = 32
 
@@ -71,7 +73,14 @@ def lib():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(
             f"{LIB_PATH} is not built; run `python -m block_scaled_precision_02_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+    _lib = declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def declare(L):
+    """Declare the argument and return types of every exported function on a
+    loaded copy of the library (this build's, or another build of the same
+    sources) and return it."""
     st = ctypes.c_int
     L.qgemm_i8_rowwise.restype = st
     L.qgemm_i8_rowwise.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
@@ -123,7 +132,6 @@ def lib():
     L.qgemm_tile_rows.argtypes = [ctypes.c_int]
     L.qgemm_force_tile.restype = ctypes.c_int
     L.qgemm_force_tile.argtypes = [ctypes.c_int]
-    _lib = L
     return L
 
 
@@ -335,10 +343,11 @@ def qgemm_f8_blockscale(A, B, scale_a, scale_b, bias=None, out=None, stream=None
 
 
 def qgemm_mx(fmt, A, B, scale_a, scale_b, b_layout, bias=None, out=None, stream=None):
-    """MX GEMM -> bf16 [M, N].  fmt QGEMM_MX_E4M3 (A [M,K] bytes) or
-    QGEMM_MX_E2M1 (A [M,K/2] bytes, two codes per byte); scale_a [M, K/32]
-    and scale_b [N, K/32] (b_layout 1) or [ceil(N/32), K/32] (b_layout 32),
-    ue8m0 codes as uint8."""
+    """MX GEMM -> bf16 [M, N].  fmt QGEMM_MX_E4M3 (A [M,K] bytes),
+    QGEMM_MX_E2M1 (A [M,K/2] bytes, two codes per byte) or the 6-bit
+    QGEMM_MX_E2M3 / QGEMM_MX_E3M2 (A [M,3K/4] bytes, four codes per three
+    bytes); scale_a [M, K/32] and scale_b [N, K/32] (b_layout 1) or
+    [ceil(N/32), K/32] (b_layout 32), ue8m0 codes as uint8."""
     torch = _torch()
     dts = (torch.uint8, torch.float8_e4m3fn) if fmt == QGEMM_MX_E4M3 else (torch.uint8,)
     lda = _operand(A, "A", dts)
@@ -347,7 +356,12 @@ def qgemm_mx(fmt, A, B, scale_a, scale_b, b_layout, bias=None, out=None, stream=
     N = B.shape[0]
     if B.shape[1] != row:
         raise ValueError(f"A is [M, {row}] but B is {tuple(B.shape)}")
-    K = row if fmt == QGEMM_MX_E4M3 else 2 * row
+    if fmt in (QGEMM_MX_E2M3, QGEMM_MX_E3M2):
+        if row % 3:
+            raise ValueError(f"6-bit MX rows are 3K/4 bytes: {row} is not a multiple of 3")
+        K = row // 3 * 4
+    else:
+        K = row if fmt == QGEMM_MX_E4M3 else 2 * row
     sdt = (torch.uint8,) + ((torch.float8_e8m0fnu,) if hasattr(torch, "float8_e8m0fnu") else ())
     brows = -(-N // b_layout) if b_layout in (1, 32) else N
     if scale_a is None or tuple(scale_a.shape) != (M, K // 32):

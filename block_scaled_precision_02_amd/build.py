@@ -1,6 +1,6 @@
 """Build libqgemm.so in-tree: hipcc, gfx950 only.
 
-    python -m block_scaled_precision_02_amd.build              # build libqgemm.so
+    python -m block_scaled_precision_02_amd.build              # build libqgemm.so (+ the sync twin)
     python -m block_scaled_precision_02_amd.build --resources  # per-kernel register / LDS audit
 
 Every HIP source under csrc/ compiles to an object in parallel, then one
@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqgemm.so")
-SOURCES = ["qgemm_api.cpp", "qgemm_i8.hip", "qgemm_f8.hip", "qgemm_mx8.hip", "qgemm_mx4.hip", "qgemm_f8b.hip", "qgemm_mx84.hip",
+SOURCES = ["qgemm_api.cpp", "qgemm_i8.hip", "qgemm_f8.hip", "qgemm_mx8.hip", "qgemm_mx4.hip", "qgemm_f8b.hip", "qgemm_mx84.hip", "qgemm_mx6.hip",
            "qgemm_quant.hip", "qgemm_pack.hip"]
 # Per-source extra flags.  The blockscale kernel folds its MFMA partial sums
 # into the totals with VALU FMAs every 128 K elements; keeping the MFMA
@@ -29,9 +29,18 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=o
          "-fno-fast-math", "-Wall", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC] + FLAGS + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
+# The conservative-sync twin (test infrastructure): the same sources with
+# QGEMM_SYNC_TWIN=1, which drains every wait and adds a barrier at every stage
+# boundary of the LDS-staged kernels; its outputs must equal the library's bit
+# for bit.
+BUILD_SYNC = os.path.join(HERE, "_build_sync")
+LIB_SYNC = os.path.join(HERE, "libqgemm_sync.so")
+
+
+def _compile(src, twin=False):
+    obj = os.path.join(BUILD_SYNC if twin else BUILD, src + ".o")
+    cmd = ([HIPCC] + FLAGS + EXTRA_FLAGS.get(src, []) + (["-DQGEMM_SYNC_TWIN=1"] if twin else []) +
+           ["-c", os.path.join(CSRC, src), "-o", obj])
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
@@ -40,17 +49,27 @@ def _compile(src):
     return obj
 
 
-def build(jobs=None):
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 16)
-    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs=None, twin=True):
+    """Build libqgemm.so and (twin=True) the conservative-sync twin
+    libqgemm_sync.so, every object compiled in one parallel pass."""
+    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(BUILD_SYNC, exist_ok=True)
+    work = [(src, False) for src in SOURCES] + ([(src, True) for src in SOURCES] if twin else [])
+    jobs = jobs or min(len(work), 2 * (os.cpu_count() or 4), 16)
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda w: _compile(*w), work))
+    _link(objs[:len(SOURCES)], LIB)
+    if twin:
+        _link(objs[len(SOURCES):], LIB_SYNC)
     return LIB
 
 
@@ -111,5 +130,5 @@ if __name__ == "__main__":
     if len(sys.argv) > 1 and sys.argv[1] == "--resources":
         resources()
         sys.exit(0)
-    print(build())
+    print(build(twin="--no-twin" not in sys.argv))
     sys.exit(0)

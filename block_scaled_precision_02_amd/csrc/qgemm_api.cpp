@@ -58,13 +58,25 @@ bool is_gfx950(const char *name)
     return strncmp(name, "gfx950", 6) == 0 && (name[6] == 0 || name[6] == ':');
 }
 
+// Test hook: QGEMM_INJECT_LAUNCH_ERROR=<hipError_t code> makes every call
+// that passed its checks report that launch error (QGEMM_ERR_HIP) instead of
+// launching, so the error path can be exercised without a failing GPU.
+int injected_launch_error()
+{
+    const char *v = getenv("QGEMM_INJECT_LAUNCH_ERROR");
+    return (v && *v) ? atoi(v) : 0;
+}
+
 qgemm_status check_device()
 {
-    // Test hook: a fake architecture name that is not gfx950 is refused
-    // before any HIP call is made.
+    // Test hooks: a fake architecture name that is not gfx950 is refused
+    // before any HIP call is made; a fake gfx950 is accepted without one, but
+    // only while a launch error is injected (nothing can reach a kernel).
     const char *fake = getenv("QGEMM_FAKE_ARCH");
     if (fake && *fake && !is_gfx950(fake))
         return fail(QGEMM_ERR_UNSUPPORTED_DEVICE, "device reports %s, not gfx950", fake);
+    if (fake && *fake && injected_launch_error())
+        return QGEMM_OK;
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
@@ -244,19 +256,43 @@ qgemm_status finish(hipError_t e)
     return QGEMM_OK;
 }
 
+// Every launch goes through here: the kernel launch (f), or the injected
+// launch error, which leaves the output and everything else untouched.
+template <class F>
+qgemm_status launch(F &&f)
+{
+    if (const int e = injected_launch_error())
+        return fail(QGEMM_ERR_HIP, "kernel launch: injected error %d", e);
+    return finish(f());
+}
+
 // The LDS-fetch kernels (tiles 4-7) run tiles whose K is a whole number of
 // their 64-byte stages (a last round of fewer than four is masked).  For MX,
 // a round reads 16 bytes of each scale row from byte 16u (e2m1) or 8u (e4m3):
 // scale rows of whole dwords (K % 128), so that each such fetch is dword
 // aligned, and the caller's scale arrays aligned to 16 / 8 bytes (svec: the
 // caller's check).
+//
+// The masked last round keeps word 0 of a round's scale chunk live and
+// replaces later words past K; a word covers 4 / (words per round) stages, so
+// the stage count must be a whole number of words -- K % 128 for every
+// e4m3-scaled path (two stages per word) and e2m1 (K % 128 keeps K bytes a
+// whole number of 64-byte stages, one stage per word).  dma_k_ok is the one
+// place that rule lives; the MX, blockscale, mixed and 6-bit paths all take it.
+bool dma_k_ok(int path, int64_t K)
+{
+    switch (path) {
+    case 0:
+    case 1: return K % 64 == 0;    // int8 / e4m3 bytes: whole 64-byte stages
+    default: return K % 128 == 0;  // scaled paths: whole scale words per round
+    }
+}
+
 bool dma_eligible(int path, int64_t kbytes, int64_t K, bool svec)
 {
-    if (kbytes % 64)
-        return false;
     if (path == 2 || path == 3)
-        return svec && (K / 32) % 4 == 0;
-    return true;
+        return svec && kbytes % 64 == 0 && dma_k_ok(path, K);
+    return kbytes % 64 == 0 && dma_k_ok(path, K);
 }
 
 // When K fits, the table's tile edge runs in an LDS-fetch kernel: 256 as the
@@ -330,6 +366,16 @@ int pick_tile_mx84(Shape s)
     return select_tile_impl(2, s.M, s.N) == 0 ? DMA8_TILE : DMA128_TILE;
 }
 
+// MX with 6-bit elements runs in the LDS-fetch kernel only: 256x256 (tile 5,
+// or 4 when forced) or 128x128 (tile 7) -- the table's 192x192 choice and
+// small M take tile 7.
+int pick_tile_mx6(Shape s)
+{
+    if (g_forced_tile == DMA_TILE || g_forced_tile == DMA8_TILE || g_forced_tile == DMA128_TILE)
+        return g_forced_tile;
+    return select_tile_impl(3, s.M, s.N) == 0 ? DMA8_TILE : DMA128_TILE;
+}
+
 int pick_tile_f8b(int64_t M, int64_t N)
 {
     if (g_forced_tile == F8B256_TILE || g_forced_tile == DMA128_TILE || g_forced_tile == SKINNY16_TILE ||
@@ -362,8 +408,15 @@ const char *qgemm_last_error(void) { return g_last_error.c_str(); }
 
 int qgemm_select_tile(int path, int64_t M, int64_t N, int64_t K)
 {
-    if (path < 0 || path > 5)
+    if (path < 0 || path > 7)
         return -1;
+    if (path == 6 || path == 7) {   // MX e2m3 / e3m2
+        const int prev = g_forced_tile;
+        g_forced_tile = -1;
+        const int t = pick_tile_mx6(Shape{M, N, K});
+        g_forced_tile = prev;
+        return t;
+    }
     if (path == 5) {   // MX e4m3 A x e2m1 B
         const int prev = g_forced_tile;
         g_forced_tile = -1;
@@ -438,7 +491,7 @@ static qgemm_status i8_common(const int8_t *A, int64_t lda, const void *B, int64
     p.scale_a = sa;
     p.scale_b = sb;
     p.bias = bias;
-    return finish(launch_i8(tile, bias != nullptr, out, p, (hipStream_t)stream));
+    return launch([&] { return launch_i8(tile, bias != nullptr, out, p, (hipStream_t)stream); });
 }
 
 qgemm_status qgemm_i8_rowwise(const int8_t *A, int64_t lda, const int8_t *B, int64_t ldb, const float *scale_a,
@@ -478,7 +531,7 @@ static qgemm_status f8_common(const uint8_t *A, int64_t lda, const void *B, int6
     p.scale_a = scale_a;
     p.scale_b = scale_b;
     p.bias = bias;
-    return finish(launch_f8(tile, bias != nullptr, p, (hipStream_t)stream));
+    return launch([&] { return launch_f8(tile, bias != nullptr, p, (hipStream_t)stream); });
 }
 
 qgemm_status qgemm_f8_pertoken(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb, const float *scale_a,
@@ -494,7 +547,7 @@ static qgemm_status f8b_common(const uint8_t *A, int64_t lda, const void *B, int
 {
     const Shape s{M, N, K};
     TRY(check_shape(s, false));
-    if (K % F8B_K_MULTIPLE)
+    if (!dma_k_ok(4, K))
         return fail(QGEMM_ERR_BAD_SHAPE, "K=%lld: blockscale needs K a multiple of %lld", (long long)K,
                     (long long)F8B_K_MULTIPLE);
     if (M == 0 || N == 0)
@@ -518,7 +571,7 @@ static qgemm_status f8b_common(const uint8_t *A, int64_t lda, const void *B, int
     p.mx_sa = (const uint8_t *)scale_a;
     p.mx_sb = (const uint8_t *)scale_b;
     p.bias = bias;
-    return finish(launch_f8b(tile, bias != nullptr, p, (hipStream_t)stream));
+    return launch([&] { return launch_f8b(tile, bias != nullptr, p, (hipStream_t)stream); });
 }
 
 qgemm_status qgemm_f8_blockscale(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb, const float *scale_a,
@@ -528,16 +581,55 @@ qgemm_status qgemm_f8_blockscale(const uint8_t *A, int64_t lda, const uint8_t *B
     return f8b_common(A, lda, B, ldb, scale_a, scale_b, bias, C, ldc, M, N, K, stream, false);
 }
 
+// MX with 6-bit elements: rows of 3K/4 bytes, the LDS-fetch kernel's 48-byte
+// stages of 64 elements and the e4m3 scale staging (8 bytes of each scale
+// row per round, so 8-byte aligned scale arrays).
+static qgemm_status mx6_common(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const void *B, int64_t ldb_bytes,
+                               const uint8_t *scale_a, const uint8_t *scale_b, qgemm_mx_bscale b_layout,
+                               const uint16_t *bias, uint16_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                               void *stream)
+{
+    const Shape s{M, N, K};
+    TRY(check_shape(s, false));
+    if (!dma_k_ok(6, K))
+        return fail(QGEMM_ERR_BAD_SHAPE, "K=%lld: 6-bit MX needs K a multiple of 128", (long long)K);
+    if (M == 0 || N == 0)
+        return QGEMM_OK;
+    const int64_t row_bytes = 3 * K / 4;
+    TRY(check_operand("A", A, lda_bytes, row_bytes));
+    TRY(check_operand("B", B, ldb_bytes, row_bytes));
+    if (!scale_a)
+        return fail(QGEMM_ERR_NULL_POINTER, "scale_a is NULL");
+    if (!scale_b)
+        return fail(QGEMM_ERR_NULL_POINTER, "scale_b is NULL");
+    if (!aligned(scale_a, 8) || !aligned(scale_b, 8))
+        return fail(QGEMM_ERR_BAD_LAYOUT, "6-bit MX scale arrays must be 8-byte aligned");
+    TRY(check_bias(bias));
+    TRY(check_output(C, ldc, N, 2));
+    TRY(check_device());
+    const int tile = pick_tile_mx6(s);
+    Params p = base_params(A, lda_bytes, B, ldb_bytes, C, ldc, s, row_bytes, tile);
+    TRY(check_grid(p));
+    p.mx_sa = scale_a;
+    p.mx_sb = scale_b;
+    p.bias = bias;
+    return launch([&] { return launch_mx6(tile, fmt == QGEMM_MX_E3M2, bias != nullptr, (int)b_layout, p, (hipStream_t)stream); });
+}
+
 static qgemm_status mx_common(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const void *B, int64_t ldb_bytes,
                               const uint8_t *scale_a, const uint8_t *scale_b, qgemm_mx_bscale b_layout,
                               const uint16_t *bias, uint16_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
                               void *stream, bool packed)
 {
     const Shape s{M, N, K};
-    if (fmt != QGEMM_MX_E4M3 && fmt != QGEMM_MX_E2M1)
+    if (fmt != QGEMM_MX_E4M3 && fmt != QGEMM_MX_E2M1 && fmt != QGEMM_MX_E2M3 && fmt != QGEMM_MX_E3M2)
         return fail(QGEMM_ERR_BAD_FORMAT, "unknown MX element format %d", (int)fmt);
     if (b_layout != QGEMM_MX_BSCALE_1x32 && b_layout != QGEMM_MX_BSCALE_32x32)
         return fail(QGEMM_ERR_BAD_FORMAT, "unknown B-scale layout %d", (int)b_layout);
+    if (fmt == QGEMM_MX_E2M3 || fmt == QGEMM_MX_E3M2)
+        return packed ? fail(QGEMM_ERR_BAD_FORMAT, "no prepacked layout for 6-bit MX elements")
+                      : mx6_common(fmt, A, lda_bytes, B, ldb_bytes, scale_a, scale_b, b_layout, bias, C, ldc, M, N,
+                                   K, stream);
     TRY(check_shape(s, false));
     if (M == 0 || N == 0)
         return QGEMM_OK;
@@ -576,8 +668,8 @@ static qgemm_status mx_common(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes
     p.bias = bias;
     const int brows = (int)b_layout;
     if (fmt == QGEMM_MX_E4M3)
-        return finish(launch_mx8(tile, bias != nullptr, brows, svec, p, (hipStream_t)stream));
-    return finish(launch_mx4(tile, bias != nullptr, brows, svec, p, (hipStream_t)stream));
+        return launch([&] { return launch_mx8(tile, bias != nullptr, brows, svec, p, (hipStream_t)stream); });
+    return launch([&] { return launch_mx4(tile, bias != nullptr, brows, svec, p, (hipStream_t)stream); });
 }
 
 static qgemm_status mx_mixed_common(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *A, int64_t lda_bytes,
@@ -601,7 +693,7 @@ static qgemm_status mx_mixed_common(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, cons
         return fail(QGEMM_ERR_BAD_FORMAT, "unknown B-scale layout %d", (int)b_layout);
     const Shape s{M, N, K};
     TRY(check_shape(s, false));
-    if (K % (packed ? 256 : 128))
+    if (!dma_k_ok(5, K) || (packed && K % 256))
         return fail(QGEMM_ERR_BAD_SHAPE, "K=%lld: e4m3 x e2m1 needs K a multiple of %d", (long long)K,
                     packed ? 256 : 128);
     if (M == 0 || N == 0)
@@ -633,7 +725,7 @@ static qgemm_status mx_mixed_common(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, cons
     p.mx_sa = scale_a;
     p.mx_sb = scale_b;
     p.bias = bias;
-    return finish(launch_mx84(tile, bias != nullptr, (int)b_layout, p, (hipStream_t)stream));
+    return launch([&] { return launch_mx84(tile, bias != nullptr, (int)b_layout, p, (hipStream_t)stream); });
 }
 
 qgemm_status qgemm_mx_mixed(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *A, int64_t lda_bytes, const void *B,
@@ -676,7 +768,7 @@ qgemm_status qgemm_prepack_b32(const void *B, int64_t ldb, int64_t N, int64_t ro
     if (!aligned(Bp, 16))
         return fail(QGEMM_ERR_BAD_LAYOUT, "Bp is not 16-byte aligned");
     TRY(check_device());
-    return finish(launch_prepack_b32((const uint8_t *)B, ldb, N, row_bytes, (uint8_t *)Bp, (hipStream_t)stream));
+    return launch([&] { return launch_prepack_b32((const uint8_t *)B, ldb, N, row_bytes, (uint8_t *)Bp, (hipStream_t)stream); });
 }
 
 qgemm_status qgemm_mx(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const void *B, int64_t ldb_bytes,
@@ -712,7 +804,7 @@ qgemm_status qgemm_prepack_b(const void *B, int64_t ldb, int64_t N, int64_t row_
     if (!aligned(Bp, 16))
         return fail(QGEMM_ERR_BAD_LAYOUT, "Bp is not 16-byte aligned");
     TRY(check_device());
-    return finish(launch_prepack_b((const uint8_t *)B, ldb, N, row_bytes, (uint8_t *)Bp, (hipStream_t)stream));
+    return launch([&] { return launch_prepack_b((const uint8_t *)B, ldb, N, row_bytes, (uint8_t *)Bp, (hipStream_t)stream); });
 }
 
 qgemm_status qgemm_i8_rowwise_prepacked(const int8_t *A, int64_t lda, const void *Bp, const float *scale_a,
@@ -778,7 +870,7 @@ qgemm_status qgemm_quant_f8_pertoken(const uint16_t *X, int64_t ldx, uint8_t *Q,
     if (!aligned(scale, 4))
         return fail(QGEMM_ERR_BAD_LAYOUT, "scale is not 4-byte aligned");
     TRY(check_device());
-    return finish(launch_quant_f8_pertoken(X, ldx, Q, ldq, scale, (int)M, (int)K, (hipStream_t)stream));
+    return launch([&] { return launch_quant_f8_pertoken(X, ldx, Q, ldq, scale, (int)M, (int)K, (hipStream_t)stream); });
 }
 
 qgemm_status qgemm_quant_f8_block(const uint16_t *X, int64_t ldx, uint8_t *Q, int64_t ldq, float *S, int64_t lds,
@@ -797,7 +889,7 @@ qgemm_status qgemm_quant_f8_block(const uint16_t *X, int64_t ldx, uint8_t *Q, in
         return fail(QGEMM_ERR_BAD_LAYOUT, "lds=%lld elements: need >= K/128=%lld, below 2^31", (long long)lds,
                     (long long)(K / 128));
     TRY(check_device());
-    return finish(launch_quant_f8_block(X, ldx, Q, ldq, S, lds, (int)M, (int)K, (hipStream_t)stream));
+    return launch([&] { return launch_quant_f8_block(X, ldx, Q, ldq, S, lds, (int)M, (int)K, (hipStream_t)stream); });
 }
 
 qgemm_status qgemm_quant_mx(qgemm_mx_fmt fmt, const uint16_t *X, int64_t ldx, void *Q, int64_t ldq, uint8_t *S,
@@ -814,8 +906,8 @@ qgemm_status qgemm_quant_mx(qgemm_mx_fmt fmt, const uint16_t *X, int64_t ldx, vo
         return fail(QGEMM_ERR_BAD_LAYOUT, "lds=%lld bytes: need >= K/32=%lld, below 2^31", (long long)lds,
                     (long long)(K / 32));
     TRY(check_device());
-    return finish(launch_quant_mx(fmt == QGEMM_MX_E4M3 ? 0 : 1, X, ldx, (uint8_t *)Q, ldq, S, lds, (int)M, (int)K,
-                                  (hipStream_t)stream));
+    return launch([&] { return launch_quant_mx(fmt == QGEMM_MX_E4M3 ? 0 : 1, X, ldx, (uint8_t *)Q, ldq, S, lds, (int)M, (int)K,
+                                  (hipStream_t)stream); });
 }
 
 }  // extern "C"

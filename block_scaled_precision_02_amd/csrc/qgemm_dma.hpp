@@ -86,6 +86,22 @@ template <> struct DmaTraits<PATH_MX8> { static constexpr int NSUB = 1; };  // c
 template <> struct DmaTraits<PATH_MX4> { static constexpr int NSUB = 2; };  // chunk 2h+S
 template <> struct DmaTraits<PATH_F8B> { static constexpr int NSUB = 1; };  // chunks h, 2+h
 template <> struct DmaTraits<PATH_MX84> { static constexpr int NSUB = 1; }; // A chunks h, 2+h; B chunk h of 32 B
+template <> struct DmaTraits<PATH_MX6> { static constexpr int NSUB = 1; };  // 24 bytes at 24h of a 48-byte row
+template <> struct DmaTraits<PATH_MX6E3> { static constexpr int NSUB = 1; };
+
+// 6-bit (FP6) stage rows: 64 elements = 48 bytes, stored as fetched (row r at
+// 48r).  Lane half h's fragment is K block h of the stage, 32 elements = the
+// 24 bytes at 24h, in VGPRs 0-5 as the instruction reads a 6-bit operand
+// (element k of the block in bits 6k..6k+5, lowest bits first, exactly the
+// memory order).  Three 8-byte reads; 16 lanes on 16 rows 48 bytes apart at one
+// offset fall in 16 different bank pairs.
+constexpr int F6ROW = 48;
+__device__ __forceinline__ i32x8 dma_frag_f6(const uint8_t *tile, int row, int h)
+{
+    const uint8_t *q = tile + row * F6ROW + 24 * h;
+    const u32x2 a = *(const u32x2 *)q, b = *(const u32x2 *)(q + 8), c = *(const u32x2 *)(q + 16);
+    return i32x8{(int)a[0], (int)a[1], (int)b[0], (int)b[1], (int)c[0], (int)c[1], 0, 0};
+}
 
 // B fragment of the mixed path: lane half h's 16 bytes (32 e2m1 elements) of
 // a 32-byte staged B row; VGPRs 4-7 unused.
@@ -128,15 +144,17 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr int NW = WM * WN;                           // waves
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     constexpr int NSUB = DmaTraits<PATH>::NSUB;
-    constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4 || PATH == PATH_MX84);
+    constexpr bool F6 = (PATH == PATH_MX6 || PATH == PATH_MX6E3);   // 6-bit operands: 48-byte stage rows
+    constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4 || PATH == PATH_MX84 || F6);
     constexpr bool B4 = (PATH == PATH_MX84);              // e2m1 B under e4m3 A: 32-byte B stage rows
     constexpr bool BS = (PATH == PATH_F8B);               // blockscale FP8
     constexpr bool SCL = MX || BS;                        // scale chunks staged through LDS
     static_assert(!BS || BROWS == 128, "blockscale B scales cover 128 rows");
     static_assert(BROWS == 1 || (BN % BROWS == 0 || BROWS == 32), "B scale rows must align with the tile");
-    constexpr int BSTAGE = B4 ? DSTAGE / 2 : DSTAGE;     // B bytes per row and stage
-    constexpr int BROWS_PER_FETCH = 1024 / BSTAGE;        // rows one 1 KB B fetch covers
-    constexpr int STAGE_BYTES = BM * DSTAGE + BN * BSTAGE;
+    constexpr int ASTAGE = F6 ? F6ROW : DSTAGE;          // A bytes per row and stage
+    constexpr int BSTAGE = B4 ? DSTAGE / 2 : F6 ? F6ROW : DSTAGE;   // B bytes per row and stage
+    constexpr int BROWS_PER_FETCH = F6 ? 16 : 1024 / BSTAGE;       // rows one 1 KB B fetch covers (not F6)
+    constexpr int STAGE_BYTES = BM * ASTAGE + BN * BSTAGE;
     constexpr int OPND_BYTES = DNST * STAGE_BYTES;
     // MX scale chunks: per buffer, 256 rows of A and 256 rows of B (1x32) or
     // 64 (32x32 layout: BN/32 valid rows), 16 bytes each -- what four fetches
@@ -150,7 +168,12 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr int RPF_B = B4 ? 1 : RPF;
     constexpr int NDSR = TM * RPF + TN * RPF_B;           // fragment reads per sub-step
     constexpr int DMA_A = BM / 16 / NW, DMA_B = BN / BROWS_PER_FETCH / NW; // fetches per wave per stage
-    constexpr int NDMA = DMA_A + DMA_B;
+    // FP6: a stage of A (B) is BM (BN) rows of 48 bytes = BM * 48 / 1024 fetches
+    // of 1 KB; each wave takes F6W consecutive ones, all of A or all of B
+    constexpr int F6A = BM * F6ROW / 1024, F6B = BN * F6ROW / 1024, F6W = (F6A + F6B) / NW;
+    static_assert(!F6 || (F6W * NW == F6A + F6B && F6A % F6W == 0 && BM % 64 == 0 && BN % 64 == 0),
+                  "FP6 tiles: whole 64-row groups, whole fetches per wave, each wave on one operand");
+    constexpr int NDMA = F6 ? F6W : DMA_A + DMA_B;
     // scale fetches per wave per chunk: 4 waves fetch A and B scale rows,
     // 8 waves split them (waves 0-3 A, 4-7 B)
     constexpr int NSCD = SCL ? 8 / NW : 0;
@@ -158,7 +181,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // (region B of the stage 4 back) except for MX, whose region B is busy
     // with scale reads.
     constexpr bool SPLIT = !SCL;
-    static_assert(DMA_A * 16 * NW == BM && DMA_B * BROWS_PER_FETCH * NW == BN,
+    static_assert(F6 || (DMA_A * 16 * NW == BM && DMA_B * BROWS_PER_FETCH * NW == BN),
                   "tile rows must be a whole number of fetches per wave");
     static_assert(BM <= SA_ROWS && (BROWS == 1 ? BN <= SB_ROWS : BN / 32 <= SB_ROWS), "scale rows per buffer");
     using Frag = typename PathTraits<PATH>::Frag;
@@ -169,8 +192,8 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // scale buffers; the mixed path's smaller B stages leave less than the
     // 256x256 stash needs, so its block is sized up to that
     constexpr int STASH_NEED = NW * TM * 32 * pow2_at_least(TN * 32 * 2 / 16) * 16;
-    constexpr int BODY = B4 ? (OPND_BYTES + SCL_BYTES > STASH_NEED ? OPND_BYTES + SCL_BYTES : STASH_NEED)
-                            : OPND_BYTES + SCL_BYTES;
+    constexpr int BODY = (B4 || F6) ? (OPND_BYTES + SCL_BYTES > STASH_NEED ? OPND_BYTES + SCL_BYTES : STASH_NEED)
+                                    : OPND_BYTES + SCL_BYTES;
     constexpr int PRM_OFF = BODY;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[BODY + (PRM ? PRM_BYTES : 0)];
 
@@ -188,7 +211,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // K is a whole number of stages; the last round may hold fewer than four.
     // Its stages at or past K are fetched through descriptors of empty range
     // (zeros land in LDS, whatever the offset), so their MFMAs add nothing.
-    const int nst = p.kbytes / DSTAGE;
+    const int nst = F6 ? p.K / 64 : p.kbytes / DSTAGE;
     const uint8_t *const a_base = p.A + (int64_t)m0 * p.lda;
     const uint32_t a_range = (uint32_t)((rows_a - 1) * p.lda + p.kbytes);
     // B row-major, or prepacked: 16-row groups of 1 KB blocks (32-row groups
@@ -234,13 +257,41 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             b_off[j] = r < rows_b ? (unsigned)(r * p.ldb + 16 * c) : OOB;
         }
     }
+    // FP6 fetch map: fetch g of an operand's stage covers its LDS bytes
+    // [1024g, 1024g + 1024) -- lane i lands at byte 1024g + 16i, which is
+    // 16-byte chunk (1024g + 16i) % 48 / 16 of row (1024g + 16i) / 48.  Wave w
+    // takes fetches F6W*w .. F6W*w + F6W - 1 of A then B.
+    const int f6g0 = F6W * wave;
+    const bool f6_a = f6g0 < F6A;                         // wave-uniform
+    unsigned f6_off[F6 ? F6W : 1];
+    if constexpr (F6) {
+#pragma unroll
+        for (int j = 0; j < F6W; ++j) {
+            const int g = (f6_a ? f6g0 : f6g0 - F6A) + j;
+            const int byte = 1024 * g + 16 * lane;
+            const int r = byte / F6ROW, c = (byte % F6ROW) / 16;
+            f6_off[j] = r < (f6_a ? rows_a : rows_b) ? (unsigned)(r * (f6_a ? p.lda : p.ldb) + 16 * c) : OOB;
+        }
+    }
+    auto fetch_f6 = [&](int t, auto jc) {
+        constexpr int j = decltype(jc)::value;
+        const bool live = t < nst;
+        uint8_t *slot = &lds[(t & 3) * STAGE_BYTES];
+        const __amdgpu_buffer_rsrc_t r = f6_a ? make_rsrc(a_base, live ? a_range : 0u)
+                                              : make_rsrc(b_base, live ? b_range : 0u);
+        uint8_t *dst = slot + (f6_a ? 0 : BM * F6ROW) + 1024 * ((f6_a ? f6g0 : f6g0 - F6A) + j);
+        dma16(r, f6_off[j] + (unsigned)(t * F6ROW), dst);
+    };
     // Stage t goes to slot t % 4, its A rows (part 0) and B rows (part 1)
-    // fetched separately.
+    // fetched separately (FP6: part 0 is the wave's whole share).
     auto fetch_part = [&](int t, auto partc) {
         const unsigned kb = (unsigned)(t * DSTAGE), kbb = (unsigned)t * bstep;
         const bool live = t < nst;
         uint8_t *slot = &lds[(t & 3) * STAGE_BYTES];
-        if constexpr (decltype(partc)::value == 0) {
+        if constexpr (F6) {
+            if constexpr (decltype(partc)::value == 0)
+                static_for<0, F6W>([&](auto jc) { fetch_f6(t, jc); });
+        } else if constexpr (decltype(partc)::value == 0) {
             const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base, live ? a_range : 0u);
 #pragma unroll
             for (int j = 0; j < DMA_A; ++j)
@@ -250,6 +301,21 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
 #pragma unroll
             for (int j = 0; j < DMA_B; ++j)
                 dma16(rb, b_off[j] + kbb, slot + BM * DSTAGE + (DMA_B * wave + j) * 1024);
+        }
+    };
+
+    // One fetch instruction of stage t: the j-th of this wave's A (part 0) or
+    // B (part 1) rows, the same load fetch_part issues as its j-th.
+    auto fetch_one = [&](int t, auto partc, auto jc) {
+        constexpr int j = decltype(jc)::value;
+        const bool live = t < nst;
+        uint8_t *slot = &lds[(t & 3) * STAGE_BYTES];
+        if constexpr (decltype(partc)::value == 0) {
+            const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base, live ? a_range : 0u);
+            dma16(ra, a_off[j] + (unsigned)(t * DSTAGE), slot + (DMA_A * wave + j) * 16 * DSTAGE);
+        } else {
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base, live ? b_range : 0u);
+            dma16(rb, b_off[j] + (unsigned)t * bstep, slot + BM * DSTAGE + (DMA_B * wave + j) * 1024);
         }
     };
 
@@ -304,32 +370,40 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr int SCW = (PATH == PATH_MX4) ? 4 : 2;
     unsigned cra[TM][SCW], crb[TN][SCW];
 
-    // Fragments of sub-step S of stage slot `slot` into register set SET.
-    auto read_frags = [&](auto sc, int slot, auto setc) {
+    // Fragment k of sub-step S in the order the serpentine MFMA sequence
+    // consumes them: A row block 0, the TN B column blocks, A row blocks 1..
+    auto read_item = [&](auto kc, auto sc, int slot, auto setc) {
+        constexpr int k = decltype(kc)::value;
         constexpr int S = decltype(sc)::value;
         constexpr int SET = decltype(setc)::value;
         const uint8_t *ta = &lds[slot * STAGE_BYTES];
-        const uint8_t *tb = ta + BM * DSTAGE;
-        // in the order the serpentine MFMA sequence consumes them
-        fa[SET][0] = dma_frag<PATH, S>(ta, arow, h);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            if constexpr (B4)
-                fb[SET][j] = dma_frag_b32(tb, brow + 32 * j, h);
+        const uint8_t *tb = ta + BM * ASTAGE;
+        if constexpr (F6) {
+            if constexpr (k == 0)
+                fa[SET][0] = dma_frag_f6(ta, arow, h);
+            else if constexpr (k <= TN)
+                fb[SET][k - 1] = dma_frag_f6(tb, brow + 32 * (k - 1), h);
             else
-                fb[SET][j] = dma_frag<PATH, S>(tb, brow + 32 * j, h);
+                fa[SET][k - TN] = dma_frag_f6(ta, arow + 32 * (k - TN), h);
+        } else if constexpr (k == 0) {
+            fa[SET][0] = dma_frag<PATH, S>(ta, arow, h);
+        } else if constexpr (k <= TN) {
+            if constexpr (B4)
+                fb[SET][k - 1] = dma_frag_b32(tb, brow + 32 * (k - 1), h);
+            else
+                fb[SET][k - 1] = dma_frag<PATH, S>(tb, brow + 32 * (k - 1), h);
+        } else {
+            fa[SET][k - TN] = dma_frag<PATH, S>(ta, arow + 32 * (k - TN), h);
         }
-#pragma unroll
-        for (int i = 1; i < TM; ++i)
-            fa[SET][i] = dma_frag<PATH, S>(ta, arow + 32 * i, h);
     };
+
     // Scale operands.  Once per round (4 stages) each lane reads the words of
     // its rows' 16-byte scale chunks that the round uses (one aligned 16- or
     // 8-byte LDS read per row: narrower per-stage reads of 32 rows at a
     // 16-byte stride land 4 rows to a bank); each stage then shifts out its
     // operand: byte S of it is sub-step S's scale for the lane's block --
     // e2m1: bytes 4J + 2h, 4J + 2h + 1 of the chunk; e4m3: byte 2J + h.
-    auto read_chunk = [&](int t) {
+    auto load_chunk = [&](int t) {
         if constexpr (SCL) {
             const uint8_t *sbuf = &lds[OPND_BYTES + ((t >> 2) & 1) * SCL_BUF];
             auto rd = [&](const uint8_t *row_base, unsigned (&w)[SCW]) {
@@ -351,10 +425,19 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
                 const int row = BROWS == 1 ? brow + 32 * j : (wn * TN * 32 + 32 * j) / BROWS;
                 rd(sbuf + SA_ROWS * 16 + row * 16, crb[j]);
             }
+        }
+    };
+    auto neutral_chunk = [&](int t) {
+        if constexpr (SCL) {
             // Words of stages past K (the last round's tail) hold the next
             // row's scales or zeros: make them finite and neutral -- scale
             // 2^0 under zero data for MX, a fold factor of 0 for blockscale.
+            // Word 0 is always live (a round starts below K), and each word
+            // covers 4 / SCW whole stages: the host admits only K with a whole
+            // number of words (dma_k_ok: K % 128 on every scaled path), so a
+            // word is either wholly past K or wholly before it.
             constexpr unsigned NEUTRAL = BS ? 0u : 0x7F7F7F7Fu;
+            static_assert(4 % SCW == 0, "a scale word covers whole stages");
 #pragma unroll
             for (int w = 1; w < SCW; ++w) {
                 const bool past = t + w * (4 / SCW) >= nst;
@@ -365,13 +448,24 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             }
         }
     };
-    auto read_scales = [&](int t, auto jc) {
+    auto read_chunk = [&](int t) {
+        load_chunk(t);
+        neutral_chunk(t);
+    };
+    // (LOADED: the round's chunk words were loaded at the start of the
+    // region; only their masking and the shifts remain)
+    auto read_scales = [&](int t, auto jc, auto loadedc) {
+        constexpr bool LOADED = decltype(loadedc)::value;
         if constexpr (BS) {
             // fold factors of the block stage J belongs to (word J/2 of the
             // round's 8 bytes); only the block's second stage folds
             constexpr int J = decltype(jc)::value;
-            if constexpr (J == 0)
-                read_chunk(t);
+            if constexpr (J == 0) {
+                if constexpr (LOADED)
+                    neutral_chunk(t);
+                else
+                    read_chunk(t);
+            }
             if constexpr (J & 1) {
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
@@ -382,8 +476,12 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             }
         } else if constexpr (MX) {
             constexpr int J = decltype(jc)::value;
-            if constexpr (J == 0)
-                read_chunk(t);
+            if constexpr (J == 0) {
+                if constexpr (LOADED)
+                    neutral_chunk(t);
+                else
+                    read_chunk(t);
+            }
             constexpr int W = (PATH == PATH_MX4) ? J : J >> 1;
             const unsigned sh = (PATH == PATH_MX4) ? 16u * h : 8u * (2 * (J & 1) + h);
 #pragma unroll
@@ -408,17 +506,29 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
                     pacc[i][j] = Acc{};
                     mfma<PATH, S>(pacc[i][j], fb[SET][j], fa[SET][i], 0u, 0u);
                 } else {
+                    // second stage: the partial sum is folded one MFMA later
+                    // (fold), once the matrix core has produced it
                     mfma<PATH, S>(pacc[i][j], fb[SET][j], fa[SET][i], 0u, 0u);
-                    const float f = fs_use[i][j];
-#pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        acc[i][j][e] = __builtin_fmaf(pacc[i][j][e], f, acc[i][j][e]);
                 }
             } else {
                 mfma<PATH, S>(acc[i][j], fb[SET][j], fa[SET][i], MX ? sb_use[j] : 0u, MX ? sa_use[i] : 0u);
             }
         });
     };
+    // Blockscale, a K block's second stage: total += partial * (sa * sb) for
+    // the MFMA tile Q of the serpentine order.
+    auto fold = [&](auto qc) {
+        if constexpr (BS) {
+            constexpr int Q = decltype(qc)::value;
+            constexpr int i = Q / TN;
+            constexpr int j = (i & 1) ? (TN - 1 - Q % TN) : (Q % TN);
+            const float f = fs_use[i][j];
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[i][j][e] = __builtin_fmaf(pacc[i][j][e], f, acc[i][j][e]);
+        }
+    };
+    constexpr bool FOLD_ODD = BS;   // stages J odd fold their partial sums
     auto use_next_scales = [&]() {
         if constexpr (BS) {
 #pragma unroll
@@ -457,81 +567,121 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     if constexpr (SPLIT)
         fetch_part(3, I0());
     __builtin_amdgcn_sched_barrier(0);
+    twin_sync();
     wait_vmcnt<2 * NDMA + (SPLIT ? DMA_A : 0)>();
     lds_barrier();
-    read_frags(I0(), 0, I0());
-    read_scales(0, I0());
+    // stage 0's first fragments (one sub-step per stage: those its first
+    // half of MFMAs uses; its region A reads the rest)
+    static_for<0, (NSUB == 1) ? 1 + TN + (NQ / 2 - 1) / TN : TM + TN>(
+        [&](auto kc) { read_item(kc, I0(), 0, I0()); });
+    read_scales(0, I0(), std::false_type());
     use_next_scales();
 
-    // Stage t = 4q + J.  Region A: fetch scale chunk q+1 (J == 0) and the B
-    // rows (SPLIT) or all rows of stage t+3 into the slot stage t-1 used
-    // (free since the last barrier), read the fragments of the later
-    // sub-steps, multiply.  Then wait for stage t+1 -- the loads issued
-    // after it are those of stages t+2 and t+3 -- and meet at the barrier.
-    // Region B fetches the A rows of stage t+4 (SPLIT) into stage t's slot
-    // (its last reads were before the barrier) and reads stage t+1's first
-    // fragments (and scale words) under the last sub-step's MFMAs.  SPLIT
-    // starts a stage's fetches half a stage earlier and spreads them over
-    // both regions.
+    // Stage t = 4q + J, in two regions of MFMAs.  Each MFMA is followed by its
+    // share of the region's fragment reads and fetches, and a scheduling
+    // fence keeps that order: the reads for the next MFMAs go out while the
+    // current ones run (into the other register set), so the LDS latency
+    // hides behind the matrix core instead of stalling the wave right before
+    // the barrier or right before the MFMA that consumes them.
+    //  Region A: fetch scale chunk q+1 (J == 0) and the B rows (SPLIT) or all
+    //  rows of stage t+3 into the slot stage t-1 used (free since the last
+    //  barrier); read sub-step 1's fragments (NSUB == 2); multiply sub-step 0
+    //  (NSUB == 1: the first half of the stage's MFMAs).  Then wait for stage
+    //  t+1 -- the loads issued after it are those of stages t+2 and t+3 --
+    //  and meet at the barrier.
+    //  Region B: fetch the A rows of stage t+4 (SPLIT) into stage t's slot
+    //  (its last reads were before the barrier); read stage t+1's first
+    //  fragments and its scale chunk; multiply the rest of stage t.
     auto stage = [&](int t, auto jc) {
         constexpr int J = decltype(jc)::value;
+        constexpr int JN = (J + 1) & 3;
         constexpr int SET0 = (NSUB == 1) ? (J & 1) : 0;    // register set of sub-step 0
-        if constexpr (J == 0)
-            fetch_scales((t >> 2) + 1);
-        if constexpr (!SPLIT)
-            fetch_part(t + 3, I0());
-        fetch_part(t + 3, I1());
-        if constexpr (NSUB == 2) {
-            read_frags(I1(), J, I1());
-            mfmas(I0(), I0(), I0(), std::integral_constant<int, NQ>(), jc);
-        } else {
-            mfmas(I0(), std::integral_constant<int, SET0>(), I0(), std::integral_constant<int, NQ / 2>(), jc);
-        }
-        // issue order: each MFMA followed by its share of the fetches and of
-        // the fragment reads
+        constexpr int SETN = (NSUB == 1) ? ((J + 1) & 1) : 0;
+        constexpr int NIT = TM + TN;                       // fragments per sub-step
+        // One sub-step per stage (e4m3 operands): the first half of a stage's
+        // MFMAs (serpentine order) uses A row blocks 0..IMAX and every B
+        // column block, i.e. fragments [0, EARLY); those are read in the
+        // previous stage's region B, the rest in the stage's own region A, so
+        // that neither region carries a whole stage of fragment traffic.
+        constexpr int IMAX = (NQ / 2 - 1) / TN;
+        constexpr int EARLY = (NSUB == 1) ? 1 + TN + IMAX : NIT;
+        // ---- region A
         {
             constexpr int NA = (NSUB == 2) ? NQ : NQ / 2;
-            constexpr int V = (SPLIT ? DMA_B : NDMA) + (J == 0 ? NSCD : 0);
-            constexpr int R = (NSUB == 2) ? NDSR : 0;
+            constexpr int NSC = (J == 0) ? NSCD : 0;
+            constexpr int VA = SPLIT ? 0 : DMA_A;
+            constexpr int V = NSC + (F6 ? F6W : VA + DMA_B);   // fetches: scale chunk, A rows, B rows
+            constexpr int R = (NSUB == 2) ? NIT : NIT - EARLY;
+            constexpr int NR = NA > 2 ? NA - 2 : 1;        // reads go out before the last two MFMAs
             static_for<0, NA>([&](auto qc) {
                 constexpr int Q = decltype(qc)::value;
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                constexpr int v = V * (Q + 1) / NA - V * Q / NA;
-                constexpr int r = R * (Q + 1) / NA - R * Q / NA;
-                if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);
-                if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+                static_for<(Q < NR ? R * Q / NR : R), (Q < NR ? R * (Q + 1) / NR : R)>([&](auto kc) {
+                    constexpr int k = decltype(kc)::value;
+                    if constexpr (NSUB == 2)
+                        read_item(kc, I1(), J, I1());
+                    else
+                        read_item(std::integral_constant<int, EARLY + k>(), I0(), J,
+                                  std::integral_constant<int, SET0>());
+                });
+                mfmas(I0(), std::integral_constant<int, SET0>(), qc, std::integral_constant<int, Q + 1>(), jc);
+                if constexpr (FOLD_ODD && (J & 1) && Q >= 1)
+                    fold(std::integral_constant<int, Q - 1>());
+                static_for<V * Q / NA, V * (Q + 1) / NA>([&](auto vc) {
+                    constexpr int v = decltype(vc)::value;
+                    if constexpr (v < NSC)
+                        fetch_scales((t >> 2) + 1);
+                    else if constexpr (F6)
+                        fetch_f6(t + 3, std::integral_constant<int, v - NSC>());
+                    else if constexpr (v < NSC + VA)
+                        fetch_one(t + 3, I0(), std::integral_constant<int, v - NSC>());
+                    else
+                        fetch_one(t + 3, I1(), std::integral_constant<int, v - NSC - VA>());
+                });
+                __builtin_amdgcn_sched_barrier(0);
             });
+            if constexpr (FOLD_ODD && (J & 1))
+                fold(std::integral_constant<int, NA - 1>());
         }
         // loads issued after stage t+1's: stages t+2 and t+3, plus the scale
         // chunk when it went out at stage t or t-1
         constexpr int AFTER = 2 * NDMA + ((J == 0 || J == 1) ? NSCD : 0);
-        __builtin_amdgcn_sched_barrier(0);
+        twin_sync();
         wait_vmcnt<AFTER>();
         lds_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        constexpr int SETN = (NSUB == 1) ? ((J + 1) & 1) : 0;
-        if constexpr (SPLIT)
-            fetch_part(t + 4, I0());
-        read_frags(I0(), (J + 1) & 3, std::integral_constant<int, SETN>());
-        read_scales(t + 1, std::integral_constant<int, (J + 1) & 3>());
-        if constexpr (NSUB == 2) {
-            mfmas(I1(), I1(), I0(), std::integral_constant<int, NQ>(), jc);
-        } else {
-            mfmas(I0(), std::integral_constant<int, SET0>(), std::integral_constant<int, NQ / 2>(),
-                  std::integral_constant<int, NQ>(), jc);
+        // ---- region B
+        {
+            constexpr int NB = (NSUB == 2) ? NQ : NQ - NQ / 2;
+            constexpr int QB = (NSUB == 2) ? 0 : NQ / 2;   // first MFMA of the region
+            constexpr int V = SPLIT ? DMA_A : 0;
+            constexpr bool CHUNK = SCL && JN == 0;         // stage t+1 starts a round
+            constexpr int R = EARLY;
+            constexpr int NR = NB > 2 ? NB - 2 : 1;
+            if constexpr (CHUNK)
+                load_chunk(t + 1);
+            static_for<0, NB>([&](auto qc) {
+                constexpr int Q = decltype(qc)::value;
+                static_for<(Q < NR ? R * Q / NR : R), (Q < NR ? R * (Q + 1) / NR : R)>([&](auto kc) {
+                    read_item(kc, I0(), JN, std::integral_constant<int, SETN>());
+                });
+                if constexpr (NSUB == 2)
+                    mfmas(I1(), I1(), qc, std::integral_constant<int, Q + 1>(), jc);
+                else
+                    mfmas(I0(), std::integral_constant<int, SET0>(), std::integral_constant<int, QB + Q>(),
+                          std::integral_constant<int, QB + Q + 1>(), jc);
+                if constexpr (FOLD_ODD && (J & 1) && Q >= 1)
+                    fold(std::integral_constant<int, QB + Q - 1>());
+                static_for<V * Q / NB, V * (Q + 1) / NB>([&](auto vc) { fetch_one(t + 4, I0(), vc); });
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            if constexpr (FOLD_ODD && (J & 1))
+                fold(std::integral_constant<int, QB + NB - 1>());
+            read_scales(t + 1, std::integral_constant<int, JN>(), std::true_type());
         }
-        constexpr int NB = (NSUB == 2) ? NQ : NQ / 2;
-        constexpr int RB = NDSR + ((SCL && ((J + 1) & 3) == 0) ? TM + TN : 0);
-        static_for<0, NB>([&](auto qc) {
-            constexpr int Q = decltype(qc)::value;
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            constexpr int VB = SPLIT ? DMA_A : 0;
-            constexpr int v = VB * (Q + 1) / NB - VB * Q / NB;
-            constexpr int r = RB * (Q + 1) / NB - RB * Q / NB;
-            if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);
-            if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
-        });
         use_next_scales();
+        __builtin_amdgcn_sched_barrier(0);
+        twin_sync();
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     // The host guarantees kbytes % 64 == 0 (a whole number of stages; for
@@ -546,7 +696,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     }
     wait_vmcnt<0>();   // nothing may still be landing in LDS once it holds the output
 
-    store_tile<PATH, WM, WN, TM, TN, BIAS, OUT, (B4 ? BODY : OPND_BYTES), PRM>(p, acc, &lds[0], &lds[PRM_OFF], m0, n0,
+    store_tile<PATH, WM, WN, TM, TN, BIAS, OUT, ((B4 || F6) ? BODY : OPND_BYTES), PRM>(p, acc, &lds[0], &lds[PRM_OFF], m0, n0,
                                                                             rows_a, rows_b);
 }
 

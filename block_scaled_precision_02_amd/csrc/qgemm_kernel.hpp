@@ -52,7 +52,10 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // 128 rows), applied inside the K loop; LDS-fetch kernel only.
 // PATH_MX84: MX with e4m3 A and e2m1 B (ue8m0 scales per 32 K elements on
 // both); LDS-fetch kernel only.
-enum Path { PATH_I8 = 0, PATH_F8 = 1, PATH_MX8 = 2, PATH_MX4 = 3, PATH_F8B = 4, PATH_MX84 = 5 };
+// PATH_MX6 / PATH_MX6E3: MX with the 6-bit OCP FP6 elements E2M3 / E3M2 (four
+// codes per three bytes, lowest bits first); LDS-fetch kernel only.
+enum Path { PATH_I8 = 0, PATH_F8 = 1, PATH_MX8 = 2, PATH_MX4 = 3, PATH_F8B = 4, PATH_MX84 = 5, PATH_MX6 = 6,
+            PATH_MX6E3 = 7 };
 enum OutKind { OUT_BF16 = 0, OUT_I32 = 1 };
 
 // Kernel arguments (one struct, passed by value).
@@ -107,6 +110,23 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// The conservative-sync build (QGEMM_SYNC_TWIN=1: libqgemm_sync.so, built
+// beside the library for the tests): at every stage boundary of the
+// LDS-staged kernels each wave drains all of its outstanding memory and LDS
+// operations and the workgroup meets at a barrier.  Its MFMA sequence is the
+// fast build's, so the two builds' outputs must be bit-identical; a wait that
+// the fast build miscounts (data used before it landed, or overwritten while
+// still being read) shows up as a difference.  The small-M kernel takes no
+// part: its waves run different numbers of K steps.
+#ifndef QGEMM_SYNC_TWIN
+#define QGEMM_SYNC_TWIN 0
+#endif
+__device__ __forceinline__ void twin_sync()
+{
+    if constexpr (QGEMM_SYNC_TWIN)
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Position of 16-byte chunk c of staged row r inside an LDS tile of rows of
 // 128 bytes.  A fragment read has 16 consecutive lanes on 16 consecutive rows
 // at the same logical chunk; the slot c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1),
@@ -145,6 +165,8 @@ template <> struct PathTraits<PATH_MX8> { static constexpr int NSUB = 2; using F
 template <> struct PathTraits<PATH_MX4> { static constexpr int NSUB = 4; using Frag = i32x8; };
 template <> struct PathTraits<PATH_F8B> { static constexpr int NSUB = 2; using Frag = i32x8; };
 template <> struct PathTraits<PATH_MX84> { static constexpr int NSUB = 2; using Frag = i32x8; };
+template <> struct PathTraits<PATH_MX6> { static constexpr int NSUB = 1; using Frag = i32x8; };
+template <> struct PathTraits<PATH_MX6E3> { static constexpr int NSUB = 1; using Frag = i32x8; };
 
 // Fragment of one 32-row MFMA operand for K sub-step S, read from a staged
 // tile.  Lane (h = lane/32, row = lane%32):
@@ -195,6 +217,12 @@ __device__ __forceinline__ void mfma(typename AccT<PATH>::T &acc,
     } else if constexpr (PATH == PATH_MX84) {
         // first operand (B) e2m1: cbsz = 4; second (A) e4m3: blgp = 0
         acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, acc, 4, 0, S, (int)sc_b, S, (int)sc_a);
+    } else if constexpr (PATH == PATH_MX6) {
+        // FP6 E2M3 operands: format code 2 (VGPRs 0-5 of each operand)
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, acc, 2, 2, S, (int)sc_b, S, (int)sc_a);
+    } else if constexpr (PATH == PATH_MX6E3) {
+        // FP6 E3M2 operands: format code 3
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, acc, 3, 3, S, (int)sc_b, S, (int)sc_a);
     } else {
         acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, acc, 4, 4, S, (int)sc_b, S, (int)sc_a);
     }
@@ -272,7 +300,8 @@ __device__ __forceinline__ void store_tile(const Params &p, Acc (&acc)[TM][TN], 
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     // MX and blockscale apply their scales inside the K loop: the epilogue
     // only adds the bias and rounds
-    constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4 || PATH == PATH_F8B || PATH == PATH_MX84);
+    constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4 || PATH == PATH_F8B || PATH == PATH_MX84 ||
+                         PATH == PATH_MX6 || PATH == PATH_MX6E3);
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
@@ -690,6 +719,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) qgemm_kernel(const Params p)
         });
         if constexpr (NEXT) {
             __builtin_amdgcn_sched_barrier(0);
+            twin_sync();
             lds_barrier();
             __builtin_amdgcn_sched_barrier(0);
             read_frags(I0(), cur ^ 1, I0());
@@ -711,6 +741,9 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) qgemm_kernel(const Params p)
                 for (int j = 0; j < TN; ++j) sb_use[j] = sb_nxt[j];
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        twin_sync();
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     // Steps alternate register sets, so the loop handles two at a time.  The

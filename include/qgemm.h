@@ -84,11 +84,17 @@ typedef enum {
     QGEMM_ERR_HIP = 6                 /* HIP reported an error; see qgemm_last_error  */
 } qgemm_status;
 
-/* MX element format, the same for A and B. */
+/* MX element format, the same for A and B.  The pages name the MX GEMM with
+ * e4m3 and e2m1 elements; E2M3 and E3M2 are the 6-bit (FP6) element types OCP
+ * Microscaling v1.0 defines beside them, under the same block rule. */
 typedef enum {
     QGEMM_MX_E4M3 = 0, /* OCP E4M3FN, one byte per element                          */
-    QGEMM_MX_E2M1 = 1  /* OCP E2M1, two per byte: element k (k even) in bits 3:0 of
+    QGEMM_MX_E2M1 = 1, /* OCP E2M1, two per byte: element k (k even) in bits 3:0 of
                           byte k/2, element k+1 in bits 7:4                         */
+    QGEMM_MX_E2M3 = 2, /* OCP FP6 E2M3 (max 7.5), four per three bytes: element k in
+                          bits 6k..6k+5 of the row, bit b of a row being bit b%8 of
+                          byte b/8 (lowest bits first); rows of 3K/4 bytes         */
+    QGEMM_MX_E3M2 = 3  /* OCP FP6 E3M2 (max 28), packed as E2M3                     */
 } qgemm_mx_fmt;
 
 /* Rows of B that share one ue8m0 scale per 32-element K block. */
@@ -149,15 +155,19 @@ qgemm_status qgemm_f8_blockscale(const uint8_t *A, int64_t lda, const uint8_t *B
                                  uint16_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
                                  void *stream);
 
-/* MX GEMM (block-scaled e4m3 or e2m1).
- *   A        [M, K] elements of fmt, row stride lda_bytes (K or K/2 bytes of data)
+/* MX GEMM (block-scaled e4m3, e2m1, or the 6-bit e2m3 / e3m2).
+ *   A        [M, K] elements of fmt, row stride lda_bytes (K, K/2 or 3K/4 bytes
+ *            of data)
  *   B        [N, K] elements of fmt, row stride ldb_bytes
  *   scale_a  ue8m0 [M, K/32], row-major, row stride K/32 bytes
  *   scale_b  ue8m0 [N, K/32] (b_layout 1x32) or [ceil(N/32), K/32] (32x32)
  *   bias, C  as for qgemm_i8_rowwise
  * A~[m,k] = fmt(A[m,k]) * 2^(scale_a[m,k/32]-127), B~ likewise with the scale
  * of row n (1x32) or n/32 (32x32); acc = sum_k A~ B~ in fp32 (matrix cores);
- * then f = acc, [+ bias], bf16 round-nearest-even.  Scale code 255 is NaN. */
+ * then f = acc, [+ bias], bf16 round-nearest-even.  Scale code 255 is NaN.
+ * The 6-bit formats need K a multiple of 128 (QGEMM_ERR_BAD_SHAPE) and 8-byte
+ * aligned scale arrays (QGEMM_ERR_BAD_LAYOUT); qgemm_mx_prepacked does not take
+ * them (QGEMM_ERR_BAD_FORMAT). */
 qgemm_status qgemm_mx(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const void *B,
                       int64_t ldb_bytes, const uint8_t *scale_a, const uint8_t *scale_b,
                       qgemm_mx_bscale b_layout, const uint16_t *bias, uint16_t *C, int64_t ldc,

@@ -80,7 +80,8 @@ def gpu_run(d, out=None, stream=None):
         fa, fb = (q.QGEMM_MX_E4M3 if f == "e4m3" else q.QGEMM_MX_E2M1 for f in d["fmt"].split("/"))
         return q.qgemm_mx_mixed(fa, fb, dev(d["A"]), dev(d["B"]), dev(d["scale_a"]), dev(d["scale_b"]),
                                 d["b_rows_per_scale"], bias, out=out, stream=stream)
-    fmt = q.QGEMM_MX_E4M3 if d["fmt"] == "e4m3" else q.QGEMM_MX_E2M1
+    fmt = {"e4m3": q.QGEMM_MX_E4M3, "e2m1": q.QGEMM_MX_E2M1, "e2m3": q.QGEMM_MX_E2M3,
+           "e3m2": q.QGEMM_MX_E3M2}[d["fmt"]]
     return q.qgemm_mx(fmt, dev(d["A"]), dev(d["B"]), dev(d["scale_a"]), dev(d["scale_b"]),
                       d["b_rows_per_scale"], bias, out=out, stream=stream)
 
@@ -115,6 +116,10 @@ def oracle_run(d, rows=None, cols=None):
         fa, fb = (oracle.MX_E4M3 if f == "e4m3" else oracle.MX_E2M1 for f in d["fmt"].split("/"))
         C, _, absdot = oracle.mx2(fa, fb, A, B, sa, sb, brows, d["K"], bias)
         return C, absdot, None
+    if d["fmt"] in ("e2m3", "e3m2"):
+        f = oracle.MX_E2M3 if d["fmt"] == "e2m3" else oracle.MX_E3M2
+        C, _, absdot = oracle.mxf(f, f, A, B, sa, sb, brows, d["K"], bias)
+        return C, absdot, None
     fmt = oracle.MX_E4M3 if d["fmt"] == "e4m3" else oracle.MX_E2M1
     C, _, absdot = oracle.mx(fmt, A, B, sa, sb, brows, d["K"], bias)
     return C, absdot, None
@@ -141,7 +146,7 @@ def path_of(d):
         return PATH_OF[d["kind"]]
     if "/" in (d["fmt"] or ""):
         return 5
-    return 2 if d["fmt"] == "e4m3" else 3
+    return {"e4m3": 2, "e2m1": 3, "e2m3": 6, "e3m2": 7}[d["fmt"]]
 
 
 def nan_out(M, N):

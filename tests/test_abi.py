@@ -93,8 +93,15 @@ def test_i8_acc_rejects_and_f8_rejects():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(fmt=2), q.QGEMM_ERR_BAD_FORMAT),
+    (dict(fmt=4), q.QGEMM_ERR_BAD_FORMAT),
+    (dict(fmt=-1), q.QGEMM_ERR_BAD_FORMAT),
     (dict(layout=16), q.QGEMM_ERR_BAD_FORMAT),
+    (dict(fmt=2, layout=16), q.QGEMM_ERR_BAD_FORMAT),
+    (dict(fmt=2), q.QGEMM_ERR_BAD_SHAPE),                       # 6-bit: K = 64 is not a multiple of 128
+    (dict(fmt=3, K=160, lda=128, ldb=128), q.QGEMM_ERR_BAD_SHAPE),
+    (dict(fmt=2, K=128, lda=64, ldb=96), q.QGEMM_ERR_BAD_LAYOUT),  # 6-bit row is 3K/4 = 96 bytes
+    (dict(fmt=3, K=128, lda=96, ldb=96, sa=FAKE3 + 4), q.QGEMM_ERR_BAD_LAYOUT),   # scales not 8-byte aligned
+    (dict(fmt=2, K=128, lda=96, ldb=96, sa=None), q.QGEMM_ERR_NULL_POINTER),
     (dict(sa=None), q.QGEMM_ERR_NULL_POINTER),
     (dict(sb=None), q.QGEMM_ERR_NULL_POINTER),
     (dict(K=80, lda=80, ldb=80), q.QGEMM_ERR_BAD_SHAPE),
@@ -108,6 +115,18 @@ def test_mx_rejects(kw, status):
 def test_e2m1_row_is_half_k():
     # lda = K/2 bytes is a valid e2m1 row; with M = 0 the call is a no-op.
     assert mx(fmt=1, lda=32, ldb=32, M=0) == q.QGEMM_OK
+
+
+def test_fp6_row_is_three_quarters_k():
+    # lda = 3K/4 bytes is a valid 6-bit row; with N = 0 the call is a no-op.
+    assert mx(fmt=2, K=128, lda=96, ldb=96, N=0) == q.QGEMM_OK
+    assert mx(fmt=3, K=256, lda=192, ldb=192, M=0) == q.QGEMM_OK
+
+
+def test_fp6_has_no_prepacked_form():
+    L = q.lib()
+    assert L.qgemm_mx_prepacked(2, FAKE, 96, FAKE2, FAKE3, FAKE3, 1, None, FAKE, 64, 64, 64, 128,
+                                None) == q.QGEMM_ERR_BAD_FORMAT
 
 
 def test_empty_shapes_are_noops_without_device():
@@ -140,7 +159,18 @@ def test_tile_table():
     # round (LDS-fetch form when K fits, register-staged otherwise)
     assert L.qgemm_select_tile(1, 4096, 2112, 7168) == 6
     assert L.qgemm_select_tile(1, 4096, 2112, 7200) == 3
-    assert L.qgemm_select_tile(7, 64, 64, 64) == -1
+    assert L.qgemm_select_tile(8, 64, 64, 64) == -1
+    # e4m3 MX with K % 128 == 64: the scale rows are whole dwords but a round's
+    # last scale word would cover one stage of data and one past K, which the
+    # masked round cannot split -- the register-staged tile (one rule for every
+    # scaled path: K % 128)
+    assert L.qgemm_select_tile(2, 16384, 7168, 2112) == 0
+    assert L.qgemm_select_tile(3, 8192, 8192, 8256) == 0        # e2m1, K % 128 == 64 as well
+    # 6-bit MX: the LDS-fetch kernel only -- 256x256 (tile 5) or 128x128 (7)
+    assert L.qgemm_select_tile(6, 8192, 8192, 8192) == 5
+    assert L.qgemm_select_tile(7, 8192, 8192, 8192) == 5
+    assert L.qgemm_select_tile(6, 16, 8192, 8192) == 7
+    assert L.qgemm_select_tile(7, 4096, 2112, 7168) == 7         # the table's 192x192 choice
     # small M: the small-M kernel (16- or 64-row tiles), every path
     assert L.qgemm_select_tile(1, 1, 2112, 7168) == 8
     assert L.qgemm_select_tile(1, 16, 2112, 7168) == 8
@@ -371,3 +401,49 @@ def test_prepacked_b32_sizes_and_rejects(monkeypatch):
     assert m(0, 1, FAKE, 512, FAKE2 + 8, FAKE3, FAKE3, 1, None, FAKE, 64, 64, 64, 512, None) == q.QGEMM_ERR_BAD_LAYOUT
     monkeypatch.setenv("QGEMM_FAKE_ARCH", "gfx1201")
     assert m(0, 1, FAKE, 512, FAKE2, FAKE3, FAKE3, 1, None, FAKE, 64, 64, 64, 512, None) == q.QGEMM_ERR_UNSUPPORTED_DEVICE
+
+
+def _aligned(n, fill):
+    """A host buffer of n bytes at a 256-byte aligned address (stands in for
+    a device pointer: with an injected launch error nothing dereferences it)."""
+    import numpy as np
+    raw = np.full(n + 256, fill, dtype=np.uint8)
+    off = (-raw.ctypes.data) % 256
+    return raw[off:off + n]
+
+
+def test_injected_launch_error_leaves_everything_untouched(monkeypatch):
+    """QGEMM_INJECT_LAUNCH_ERROR (with a fake gfx950, so no HIP call is made):
+    every entry point that passed its checks returns QGEMM_ERR_HIP naming the
+    injected error, and the output buffer keeps every byte."""
+    import numpy as np
+    monkeypatch.setenv("QGEMM_FAKE_ARCH", "gfx950")
+    monkeypatch.setenv("QGEMM_INJECT_LAUNCH_ERROR", "98")      # hipErrorInvalidDeviceFunction
+    L = q.lib()
+    M = N = 64
+    K = 256
+    a, b = _aligned(M * K, 1), _aligned(N * K, 2)
+    s32 = _aligned(4 * max(M, N) * (K // 32), 0x3C)              # fp32 / ue8m0 scales alike
+    s32b = _aligned(4 * max(M, N) * (K // 32), 0x3C)
+    c = _aligned(2 * M * N, 0xA5)
+    before = c.copy()
+    P = lambda x: x.ctypes.data  # noqa: E731
+    calls = {
+        "i8": lambda: L.qgemm_i8_rowwise(P(a), K, P(b), K, P(s32), P(s32b), None, P(c), N, M, N, K, None),
+        "i8_acc": lambda: L.qgemm_i8_acc_i32(P(a), K, P(b), K, P(c), N // 2, M // 4, N // 2, K, None),
+        "f8": lambda: L.qgemm_f8_pertoken(P(a), K, P(b), K, P(s32), P(s32b), None, P(c), N, M, N, K, None),
+        "f8b": lambda: L.qgemm_f8_blockscale(P(a), K, P(b), K, P(s32), P(s32b), None, P(c), N, M, N, K, None),
+        "mx8": lambda: L.qgemm_mx(0, P(a), K, P(b), K, P(s32), P(s32b), 1, None, P(c), N, M, N, K, None),
+        "mx4": lambda: L.qgemm_mx(1, P(a), K // 2, P(b), K // 2, P(s32), P(s32b), 32, None, P(c), N, M, N, K, None),
+        "mx6": lambda: L.qgemm_mx(2, P(a), 3 * K // 4, P(b), 3 * K // 4, P(s32), P(s32b), 1, None, P(c), N, M, N, K,
+                                  None),
+        "mixed": lambda: L.qgemm_mx_mixed(0, 1, P(a), K, P(b), K // 2, P(s32), P(s32b), 1, None, P(c), N, M, N, K,
+                                          None),
+    }
+    for name, call in calls.items():
+        assert call() == q.QGEMM_ERR_HIP, name
+        msg = L.qgemm_last_error().decode()
+        assert "injected error 98" in msg, (name, msg)
+    assert np.array_equal(c, before)
+    # (never called without the injection here: these host buffers must not
+    # reach a kernel on a machine that has a GPU)

@@ -4,9 +4,9 @@ three stages, and the stages past K must add nothing.
 
 Each operand row is padded past K with poison (int8 127, e4m3 NaN, e2m1 6.0),
 so a stage past K that read the row's own padding would change the result.
-The scale rows next to the ones checked start with a NaN (ue8m0 255) or
-infinite (blockscale fp32) scale: a kernel whose masked tail took the next
-row's first scale word would turn a checked output into NaN.  Checked rows and
+Every scale of the rows next to the ones checked is NaN (ue8m0 255) or
+infinite (blockscale fp32): a kernel whose masked tail took any word of the
+next scale row would turn a checked output into NaN.  Checked rows and
 columns are compared with the CPU oracle: INT8 bit-exact, FP8 / MX within
 1e-2 * sum|a b| + 1 bf16 ulp and cosine >= 0.99999.
 """
@@ -76,15 +76,15 @@ def _run(d, At, Bt):
 
 
 def _poison_scales(d):
-    """Odd A scale rows and odd B scale rows start with a non-finite scale;
+    """Every scale of the odd A scale rows and odd B scale rows is non-finite;
     returns the output rows and columns whose scales are all finite."""
     M, N = d["M"], d["N"]
     if d["kind"] in ("i8", "f8"):
         return np.arange(M), np.arange(N)        # scales applied per row in the epilogue
     sa, sb = d["scale_a"].copy(), d["scale_b"].copy()
     bad = np.float32(np.inf) if d["kind"] == "f8b" else np.uint8(255)
-    sa[1::2, 0] = bad
-    sb[1::2, 0] = bad
+    sa[1::2, :] = bad        # every word of a neighbouring row, so each masked word position is checked
+    sb[1::2, :] = bad
     d["scale_a"], d["scale_b"] = sa, sb
     group = 128 if d["kind"] == "f8b" else d["b_rows_per_scale"]
     cols = np.arange(N)

@@ -1,0 +1,190 @@
+"""GPU parity of the MX GEMM with 6-bit elements (qgemm_mx with QGEMM_MX_E2M3
+or QGEMM_MX_E3M2: OCP FP6, four codes per three bytes, one ue8m0 scale per 32
+K elements) against the CPU oracle (orc_mxf) on the same seeded inputs,
+through the C ABI.
+
+Bar: per element |gpu - oracle| <= 1e-2 * sum_k |A~ B~| + 1 bf16 ulp, cosine
+>= 0.99999.  Every tile it runs on (4, 5, 7), both FP6 types, both B-scale
+layouts, ragged M / N, random scale codes (a scale paired with the wrong K
+block or row leaves the bound), bias, canaries around the output, K with a
+partial last round of stages under poisoned row padding and non-finite scales
+in the neighbouring rows, the argument checks, and the 8192^3 workload into a
+NaN-filled C.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+from block_scaled_precision_02_amd import inputs  # noqa: E402
+import block_scaled_precision_02_amd as q  # noqa: E402
+
+from tests import parity  # noqa: E402
+
+TILES = [4, 5, 7]
+FMTS = [("mxfp6", q.QGEMM_MX_E2M3), ("mxfp6_e3m2", q.QGEMM_MX_E3M2)]
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _gpu_only():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    q.force_tile(-1)
+    yield
+    q.force_tile(-1)
+
+
+def _make(name, M, N, K, brows=1, bias=False, seed=None):
+    d = inputs.make(name, M=M, N=N, K=K, bias=bias, seed=seed)
+    if brows == 32:
+        rng = np.random.default_rng(M + N + K)
+        xb = rng.standard_normal((N, K)).astype(np.float32)
+        codes, d["scale_b"] = inputs.mx_quantise(xb, d["fmt"], 32)
+        d["B"] = inputs.pack(codes, d["fmt"])
+        d["b_rows_per_scale"] = 32
+    return d
+
+
+def _check(d, what, out=None):
+    _say(f"[mx6] {what} M={d['M']} N={d['N']} K={d['K']}")
+    out = parity.gpu_run(d, out=out)
+    torch.cuda.synchronize()
+    ref, absdot, _ = parity.oracle_run(d)
+    worst, cos = parity.compare(d, parity.bits(out), ref, absdot, what)
+    _say(f"[mx6] {what}: worst err/bound {worst:.3g} cos {cos:.8f}")
+    return out
+
+
+@pytest.mark.parametrize("name,fmt", FMTS)
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("brows", [1, 32])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 512), (33, 70, 512), (300, 520, 1024), (1, 1, 128), (257, 300, 1536),
+                                   (64, 96, 256)])
+def test_mx6_shapes(name, fmt, tile, brows, M, N, K):
+    q.force_tile(tile)
+    _check(_make(name, M, N, K, brows), f"{name} tile {tile} brows {brows}")
+
+
+@pytest.mark.parametrize("name,fmt", FMTS)
+@pytest.mark.parametrize("tile", TILES)
+def test_mx6_bias_and_random_scales(name, fmt, tile):
+    """Scale codes drawn at random per block (both operands), bias on."""
+    q.force_tile(tile)
+    d = _make(name, 200, 300, 640, bias=True)
+    rng = np.random.default_rng(tile + fmt)
+    d["scale_a"] = rng.integers(110, 145, d["scale_a"].shape, dtype=np.uint8)
+    d["scale_b"] = rng.integers(110, 145, d["scale_b"].shape, dtype=np.uint8)
+    _check(d, f"{name} random scales tile {tile}")
+
+
+@pytest.mark.parametrize("name,fmt", FMTS)
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("M,N,K", [(257, 259, 384), (130, 8, 128), (5, 300, 896)])
+def test_mx6_edges_canaries(name, fmt, tile, M, N, K):
+    """C inside a larger buffer (ldc > N, rows past M): every byte outside
+    [0,M) x [0,N) keeps its canary."""
+    q.force_tile(tile)
+    d = _make(name, M, N, K, bias=True)
+    ldc = N + (-N) % 8 + 16
+    buf = torch.full((M + 3, ldc), -7.0, dtype=torch.bfloat16, device="cuda")
+    before = parity.bits(buf)
+    _check(d, f"{name} canary tile {tile}", out=buf[:M, :N])
+    after = parity.bits(buf)
+    assert np.array_equal(after[:M, N:], before[:M, N:]), "wrote past N"
+    assert np.array_equal(after[M:], before[M:]), "wrote past M"
+
+
+PAD = 48
+
+
+def _padded(x):
+    """Rows padded past their data with 0xFF bytes (codes 63: -7.5 e2m3,
+    -28 e3m2), so a stage past K that read them would change the result."""
+    buf = np.full((x.shape[0], x.shape[1] + PAD), 0xFF, dtype=np.uint8)
+    buf[:, :x.shape[1]] = x
+    return torch.from_numpy(buf).cuda()[:, :x.shape[1]]
+
+
+@pytest.mark.parametrize("name,fmt", FMTS)
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("K", [128, 384, 640])
+def test_mx6_partial_round(name, fmt, tile, K):
+    """K = 2, 6, 10 stages of 64: the last 4-stage round holds two.  Operand
+    rows padded with poison; every scale of the odd A rows and odd B rows is
+    NaN (255), so a masked tail that took a word of the next scale row turns
+    a checked output into NaN; even rows / columns are checked."""
+    q.force_tile(tile)
+    M, N = 200, 300
+    d = _make(name, M, N, K, bias=True)
+    d["scale_a"] = d["scale_a"].copy()
+    d["scale_b"] = d["scale_b"].copy()
+    d["scale_a"][1::2, :] = 255
+    d["scale_b"][1::2, :] = 255
+    _say(f"[mx6] ktail {name} {M}x{N}x{K} tile {tile}")
+    dev = parity.dev
+    out = q.qgemm_mx(fmt, _padded(d["A"]), _padded(d["B"]), dev(d["scale_a"]), dev(d["scale_b"]), 1,
+                     dev(d["bias"].view(np.int16)))
+    torch.cuda.synchronize()
+    rows, cols = np.arange(0, M, 2), np.arange(0, N, 2)
+    ref, absdot, _ = parity.oracle_run(d, rows=rows)
+    parity.compare(d, parity.bits(out)[rows][:, cols], ref[:, cols], absdot[:, cols], f"ktail {name} K={K}")
+
+
+def test_mx6_table_choice_and_forced_tiles():
+    assert q.select_tile(6, 8192, 8192, 8192) == 5
+    assert q.select_tile(7, 8192, 8192, 8192) == 5
+    assert q.select_tile(6, 16, 8192, 8192) == 7       # no small-M kernel: the 128x128 tile
+    assert q.select_tile(6, 4096, 2112, 7168 // 64 * 64) in (5, 7)
+    d = _make("mxfp6", 100, 130, 256)
+    for t in (6, 8, 9, 0):                              # tiles the 6-bit path does not build run its own
+        q.force_tile(t)
+        _check(d, f"forced tile {t}")
+
+
+def test_mx6_rejects():
+    dev = torch.device("cuda")
+    A = torch.zeros((8, 96), dtype=torch.uint8, device=dev)
+    s = torch.full((8, 4), 127, dtype=torch.uint8, device=dev)
+    A64 = torch.zeros((8, 48), dtype=torch.uint8, device=dev)
+    s64 = torch.full((8, 2), 127, dtype=torch.uint8, device=dev)
+    with pytest.raises(q.QGemmArgError) as e:           # K = 64: not a multiple of 128
+        q.qgemm_mx(q.QGEMM_MX_E2M3, A64, A64, s64, s64, 1)
+    assert e.value.status == q.QGEMM_ERR_BAD_SHAPE
+    big = torch.full((8 * 4 + 4,), 127, dtype=torch.uint8, device=dev)
+    with pytest.raises(q.QGemmArgError) as e:           # scale array 4 bytes off an 8-byte boundary
+        q.qgemm_mx(q.QGEMM_MX_E2M3, A, A, big[4:].view(8, 4), s, 1)
+    assert e.value.status == q.QGEMM_ERR_BAD_LAYOUT
+
+
+def test_mx6_e2m3_matches_e4m3_reencoding_on_gpu():
+    """The same values through the e4m3 MX kernel (every FP6 value is an e4m3
+    value): the two GPU results agree within the MX bound of each other."""
+    d = _make("mxfp6", 256, 512, 1024)
+    out6 = parity.bits(parity.gpu_run(d))
+    from tests.test_oracle_mx6 import _to_e4m3
+    d8 = dict(d, fmt="e4m3", A=_to_e4m3("e2m3", d["A"], 1024), B=_to_e4m3("e2m3", d["B"], 1024))
+    out8 = parity.bits(parity.gpu_run(d8))
+    ref, absdot, _ = parity.oracle_run(d)
+    parity.compare(d, out6, ref, absdot, "e2m3")
+    parity.compare(d8, out8, ref, absdot, "re-encoded e4m3")
+
+
+@pytest.mark.parametrize("name,fmt", FMTS)
+def test_mx6_full_workload(name, fmt):
+    """8192^3 as the table launches it, into a NaN-filled C: every output
+    written; the first and last row of every tile band and random rows
+    against the oracle."""
+    d = inputs.make(name)
+    _say(f"[mx6] full {name} {d['M']}x{d['N']}x{d['K']}")
+    out = parity.gpu_run(d, out=parity.nan_out(d["M"], d["N"]))
+    worst, cos, n = parity.check_full_grid(d, out, -1, f"full {name}",
+                                           np.random.default_rng(6).choice(d["M"], 8, replace=False))
+    _say(f"[mx6] full {name}: {n} rows, worst err/bound {worst:.3g} cos {cos:.8f}")

@@ -37,11 +37,11 @@ def _gpu_only():
 def _shape(rng, name):
     M = int(rng.choice([int(rng.integers(1, 17)), int(rng.integers(17, 65)), int(rng.integers(65, 520))]))
     N = int(rng.integers(1, 520))
-    if name in ("f8_block", "mx_a8w4"):
+    if name in ("f8_block", "mx_a8w4", "mxfp6", "mxfp6_e3m2"):
         K = 128 * int(rng.integers(1, 13))                 # these paths: K a multiple of 128
-    elif name == "mxfp4":
-        K = 64 * int(rng.integers(1, 25))                  # whole bytes; on / off the 16-byte scale chunks
     else:
+        # any multiple of 32 (e2m1 K = 32 * odd: 16-byte row ends, the
+        # register-staged and small-M tails)
         K = 32 * int(rng.integers(1, 49))
     return M, N, K
 
@@ -56,7 +56,7 @@ def _make(name, M, N, K, bias, rng):
     return d
 
 
-NAMES = ["i8_small", "f8_ptpc", "mxfp8", "mxfp4", "f8_block", "mx_a8w4"]
+NAMES = ["i8_small", "f8_ptpc", "mxfp8", "mxfp4", "f8_block", "mx_a8w4", "mxfp6", "mxfp6_e3m2"]
 
 
 @pytest.mark.parametrize("name", NAMES)
