@@ -162,7 +162,24 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr int SA_ROWS = 256;
     constexpr int SB_ROWS = (BROWS == 1) ? 256 : 64;
     constexpr int SCL_BUF = (SA_ROWS + SB_ROWS) * 16;
-    constexpr int SCL_BYTES = SCL ? 2 * SCL_BUF : 0;
+    // Wide scale staging (e2m1 with 1x32 B scales, where LDS allows): a refill
+    // brings 32 bytes of every scale row -- two rounds of 16 -- with two
+    // lanes per row, 32 rows per fetch, so each 64-byte memory request
+    // carries 32 scale bytes instead of 16.  Refill v (rounds 2v, 2v+1) goes
+    // out in two halves, at the first stage of rounds 2v-2 and 2v-1, into the
+    // buffer refill v-2 used: every round still issues the same number of
+    // scale fetches per wave, so the wait counts are those of the narrow
+    // scheme.  Buffer rows: the tile's A rows, then its B rows.
+    constexpr int RB = (PATH == PATH_MX4) ? 16 : 8;       // scale bytes per row and round
+    constexpr int G = 2;                                  // rounds per wide refill
+    constexpr int SAW = BM, SBW = BN;
+    constexpr int WIDE_BUF = (SAW + SBW) * 32;
+    constexpr bool PRM = OUT == OUT_BF16 && (!SCL || BIAS);
+    constexpr int NWA = SAW / 32, NWT = NWA + SBW / 32;   // fetches per refill: A rows, all
+    constexpr bool WIDE = PATH == PATH_MX4 && BROWS == 1 && NWT % (G * NW) == 0 &&
+                          DNST * STAGE_BYTES + 2 * WIDE_BUF + (PRM ? PRM_BYTES : 0) <= 160 * 1024;
+    constexpr int NSCW = NWT / (G * NW);                  // per wave and round
+    constexpr int SCL_BYTES = SCL ? 2 * (WIDE ? WIDE_BUF : SCL_BUF) : 0;
     constexpr int NQ = TM * TN;
     constexpr int RPF = (PATH == PATH_F8 || PATH == PATH_MX8 || PATH == PATH_F8B || PATH == PATH_MX84) ? 2 : 1;
     constexpr int RPF_B = B4 ? 1 : RPF;
@@ -176,7 +193,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr int NDMA = F6 ? F6W : DMA_A + DMA_B;
     // scale fetches per wave per chunk: 4 waves fetch A and B scale rows,
     // 8 waves split them (waves 0-3 A, 4-7 B)
-    constexpr int NSCD = SCL ? 8 / NW : 0;
+    constexpr int NSCD = SCL ? (WIDE ? NSCW : 8 / NW) : 0;
     // A rows of a stage are fetched one region earlier than its B rows
     // (region B of the stage 4 back) except for MX, whose region B is busy
     // with scale reads.
@@ -187,7 +204,6 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     using Frag = typename PathTraits<PATH>::Frag;
     using Acc = typename AccT<PATH>::T;
 
-    constexpr bool PRM = OUT == OUT_BF16 && (!SCL || BIAS);
     // the epilogue's output stash (whole-row stores) reuses the operand and
     // scale buffers; the mixed path's smaller B stages leave less than the
     // 256x256 stash needs, so its block is sized up to that
@@ -334,8 +350,45 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         const int rb_row = BROWS == 1 ? 64 * sw + lane : lane;     // 32 / 128 rows: rows 0..63, fetched alike by every wave
         sb_fo = rb_row < srows_b ? (unsigned)(rb_row * p.kblocks) : OOB;
     }
+    // Wide: half e (0, 1) of a refill is global fetches g = e * NWT/2 + NSCW *
+    // wave + k, k < NSCW; fetch g < NWA covers A scale rows 32g..32g+31, the
+    // others B rows; lane i takes row i/2, bytes 16 * (i % 2) of the refill's 32.
+    unsigned sw_off[WIDE ? 2 * NSCW : 1];
+    bool sw_a[WIDE ? 2 * NSCW : 1];
+    int sw_dst[WIDE ? 2 * NSCW : 1];
+    if constexpr (WIDE) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+            for (int k = 0; k < NSCW; ++k) {
+                const int g = e * (NWT / 2) + NSCW * wave + k;
+                const bool a = g < NWA;
+                const int row = 32 * (a ? g : g - NWA) + (lane >> 1);
+                sw_a[e * NSCW + k] = a;
+                sw_off[e * NSCW + k] = row < (a ? rows_a : rows_b) ? (unsigned)(row * p.kblocks + 16 * (lane & 1)) : OOB;
+                sw_dst[e * NSCW + k] = a ? 1024 * g : SAW * 32 + 1024 * (g - NWA);
+            }
+    }
+    // Round u's scale fetch: narrow, round u+1's 16-byte chunk of every row;
+    // wide, half u % 2 of refill u/2 + 1.
     auto fetch_scales = [&](int u) {
-        if constexpr (SCL) {
+        if constexpr (WIDE) {
+            // round 2v-2 (u = 2v-1) fetches half 0 of refill v, round 2v-1
+            // (u = 2v) half 1; the prologue (u = 0) fetches refill 0 whole
+            const int v = (u + 1) >> 1;
+            uint8_t *base = &lds[OPND_BYTES + (v & 1) * WIDE_BUF];
+            if (u == 0) {
+#pragma unroll
+                for (int k = 0; k < 2 * NSCW; ++k)
+                    dma16(sw_a[k] ? rsa : rsb, sw_off[k], base + sw_dst[k]);
+            } else {
+                const int e = (u - 1) & 1;
+#pragma unroll
+                for (int k = 0; k < NSCW; ++k)
+                    dma16(sw_a[e * NSCW + k] ? rsa : rsb, sw_off[e * NSCW + k] + 32u * (unsigned)v,
+                          base + sw_dst[e * NSCW + k]);
+            }
+        } else if constexpr (SCL) {
             uint8_t *base = &lds[OPND_BYTES + (u & 1) * SCL_BUF];
             // four stages of scales: 16 bytes (e2m1) or 8 bytes (e4m3, blockscale) per row
             const unsigned kb = (unsigned)((PATH == PATH_MX4 ? 16 : 8) * u);
@@ -405,7 +458,13 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // e2m1: bytes 4J + 2h, 4J + 2h + 1 of the chunk; e4m3: byte 2J + h.
     auto load_chunk = [&](int t) {
         if constexpr (SCL) {
-            const uint8_t *sbuf = &lds[OPND_BYTES + ((t >> 2) & 1) * SCL_BUF];
+            // narrow: round r's 16 bytes at row * 16 of buffer r % 2; wide:
+            // round r's RB bytes at row * 32 + RB * (r % G) of buffer (r / G) % 2
+            const int r = t >> 2;
+            const uint8_t *sbuf = WIDE ? &lds[OPND_BYTES + ((r / G) & 1) * WIDE_BUF] + RB * (r % G)
+                                       : &lds[OPND_BYTES + (r & 1) * SCL_BUF];
+            constexpr int SP = WIDE ? 32 : 16;                // row pitch
+            constexpr int SBOFF = WIDE ? SAW * 32 : SA_ROWS * 16;
             auto rd = [&](const uint8_t *row_base, unsigned (&w)[SCW]) {
                 if constexpr (SCW == 4) {
                     const u32x4 v = *(const u32x4 *)row_base;
@@ -419,11 +478,11 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             };
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                rd(sbuf + (arow + 32 * i) * 16, cra[i]);
+                rd(sbuf + (arow + 32 * i) * SP, cra[i]);
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int row = BROWS == 1 ? brow + 32 * j : (wn * TN * 32 + 32 * j) / BROWS;
-                rd(sbuf + SA_ROWS * 16 + row * 16, crb[j]);
+                rd(sbuf + SBOFF + row * SP, crb[j]);
             }
         }
     };
