@@ -179,6 +179,8 @@ def upload(d):
 
 
 KERNEL_SOURCES = "block_scaled_precision_02_amd/csrc"
+# workloads whose FETCH_SIZE / WRITE_SIZE runs profiles/traffic.json holds
+TRAFFIC_WORKLOADS = ["i8_qkv", "mxfp4", "f8_ptpc", "mxfp8", "mxfp6", "f8_block", "mx_a8w4"]
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -596,6 +598,8 @@ def bench_config(cfg, name, args, headline=None):
         ms, n = time_passes(run, stream, R)
     rec.update({"launches_per_pass": n, "passes": len(ms)})
     rec.update(pass_stats(ms, flops, peak))
+    rec["algorithmic_bytes"] = min_bytes(d0)
+    rec["traffic"] = traffic_bytes(name)
     sclk = clk.summary()
     rec["sclk_mhz"] = sclk
     if sclk is not None:
@@ -768,7 +772,7 @@ def main():
                          "WRITE_SIZE runs under DIR (no GPU needed)")
     args = ap.parse_args()
     if args.traffic_from:
-        print(json.dumps(write_traffic(args.traffic_from, ["i8_qkv", "mxfp4", "f8_block", "mx_a8w4"])))
+        print(json.dumps(write_traffic(args.traffic_from, TRAFFIC_WORKLOADS)))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this GEMM library has no multi-GPU path "
