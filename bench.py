@@ -473,8 +473,11 @@ class ClockSampler:
         if self._thread is not None:
             self._thread.join()
 
-    def summary(self):
-        if not self.samples:
+    def summary(self, min_samples=10):
+        """Median, min and max of the samples; None when fewer than
+        `min_samples` were taken (a region too short for the driver's
+        reading to have settled)."""
+        if len(self.samples) < min_samples:
             return None
         v = np.array(self.samples)
         return {"median": float(np.median(v)), "min": float(v.min()), "max": float(v.max()), "samples": len(v)}
