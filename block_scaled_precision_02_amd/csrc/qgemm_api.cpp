@@ -377,11 +377,13 @@ int pick_tile_mx84(Shape s)
 // MX with 6-bit elements runs in the LDS-fetch kernel only: 256x256 (tile 5,
 // or 4 when forced) or 128x128 (tile 7) -- the table's 192x192 choice and
 // small M take tile 7.
+// 6-bit MX: the four-wave 256x256 tile where the 256x256 grid fills the
+// chip, else 128x128 (the only two FP6 tiles built).
 int pick_tile_mx6(Shape s)
 {
-    if (g_forced_tile == DMA_TILE || g_forced_tile == DMA8_TILE || g_forced_tile == DMA128_TILE)
+    if (g_forced_tile == DMA_TILE || g_forced_tile == DMA128_TILE)
         return g_forced_tile;
-    return select_tile_impl(3, s.M, s.N) == 0 ? DMA8_TILE : DMA128_TILE;
+    return select_tile_impl(3, s.M, s.N) == 0 ? DMA_TILE : DMA128_TILE;
 }
 
 int pick_tile_f8b(int64_t M, int64_t N)

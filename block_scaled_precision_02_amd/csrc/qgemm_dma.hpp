@@ -33,6 +33,12 @@
 //    rows.  Lane half h's 16 bytes of a B row are the instruction's K block h
 //    (32 e2m1 elements, scale of lane half h), as its e4m3 A fragment's chunks
 //    h and 2+h are; both operands' scales are staged as for e4m3 MX.
+//  * 6-bit MX (FP6): a stage is 64 K elements, 48 bytes of a row, which is not
+//    a whole 64-byte memory segment.  The ring holds segments instead
+//    ("lines": 64 bytes of every row, laid out and fetched exactly as an
+//    8-bit stage), four in LDS; a round of four stages spans three lines,
+//    and each stage reads its fragments out of the one or two lines that
+//    hold its 48 bytes.  Every segment is fetched once, whole.
 //  * A 16-byte chunk c of staged row r sits at slot c ^ ((r >> 2) & 3) of its
 //    64-byte row, so a fragment read (16 lanes on 16 consecutive rows at one
 //    logical chunk) covers 16 different 16-byte slots of 256 bytes of banks.
@@ -89,20 +95,6 @@ template <> struct DmaTraits<PATH_MX84> { static constexpr int NSUB = 1; }; // A
 template <> struct DmaTraits<PATH_MX6> { static constexpr int NSUB = 1; };  // 24 bytes at 24h of a 48-byte row
 template <> struct DmaTraits<PATH_MX6E3> { static constexpr int NSUB = 1; };
 
-// 6-bit (FP6) stage rows: 64 elements = 48 bytes, stored as fetched (row r at
-// 48r).  Lane half h's fragment is K block h of the stage, 32 elements = the
-// 24 bytes at 24h, in VGPRs 0-5 as the instruction reads a 6-bit operand
-// (element k of the block in bits 6k..6k+5, lowest bits first, exactly the
-// memory order).  Three 8-byte reads; 16 lanes on 16 rows 48 bytes apart at one
-// offset fall in 16 different bank pairs.
-constexpr int F6ROW = 48;
-__device__ __forceinline__ i32x8 dma_frag_f6(const uint8_t *tile, int row, int h)
-{
-    const uint8_t *q = tile + row * F6ROW + 24 * h;
-    const u32x2 a = *(const u32x2 *)q, b = *(const u32x2 *)(q + 8), c = *(const u32x2 *)(q + 16);
-    return i32x8{(int)a[0], (int)a[1], (int)b[0], (int)b[1], (int)c[0], (int)c[1], 0, 0};
-}
-
 // B fragment of the mixed path: lane half h's 16 bytes (32 e2m1 elements) of
 // a 32-byte staged B row; VGPRs 4-7 unused.
 __device__ __forceinline__ i32x8 dma_frag_b32(const uint8_t *tile, int row, int h)
@@ -144,16 +136,17 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr int NW = WM * WN;                           // waves
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     constexpr int NSUB = DmaTraits<PATH>::NSUB;
-    constexpr bool F6 = (PATH == PATH_MX6 || PATH == PATH_MX6E3);   // 6-bit operands: 48-byte stage rows
+    constexpr bool F6 = (PATH == PATH_MX6 || PATH == PATH_MX6E3);   // 6-bit operands: 48-byte stages in 64-byte lines
     constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4 || PATH == PATH_MX84 || F6);
     constexpr bool B4 = (PATH == PATH_MX84);              // e2m1 B under e4m3 A: 32-byte B stage rows
     constexpr bool BS = (PATH == PATH_F8B);               // blockscale FP8
     constexpr bool SCL = MX || BS;                        // scale chunks staged through LDS
     static_assert(!BS || BROWS == 128, "blockscale B scales cover 128 rows");
     static_assert(BROWS == 1 || (BN % BROWS == 0 || BROWS == 32), "B scale rows must align with the tile");
-    constexpr int ASTAGE = F6 ? F6ROW : DSTAGE;          // A bytes per row and stage
-    constexpr int BSTAGE = B4 ? DSTAGE / 2 : F6 ? F6ROW : DSTAGE;   // B bytes per row and stage
-    constexpr int BROWS_PER_FETCH = F6 ? 16 : 1024 / BSTAGE;       // rows one 1 KB B fetch covers (not F6)
+    // bytes per row of one ring slot (FP6: a line, 64 bytes as for 8 bits)
+    constexpr int ASTAGE = DSTAGE;
+    constexpr int BSTAGE = B4 ? DSTAGE / 2 : DSTAGE;
+    constexpr int BROWS_PER_FETCH = 1024 / BSTAGE;       // rows one 1 KB B fetch covers
     constexpr int STAGE_BYTES = BM * ASTAGE + BN * BSTAGE;
     constexpr int OPND_BYTES = DNST * STAGE_BYTES;
     // MX scale chunks: per buffer, 256 rows of A and 256 rows of B (1x32) or
@@ -162,21 +155,26 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr int SA_ROWS = 256;
     constexpr int SB_ROWS = (BROWS == 1) ? 256 : 64;
     constexpr int SCL_BUF = (SA_ROWS + SB_ROWS) * 16;
-    // Wide scale staging (e2m1 with 1x32 B scales, where LDS allows): a refill
-    // brings 32 bytes of every scale row -- two rounds of 16 -- with two
-    // lanes per row, 32 rows per fetch, so each 64-byte memory request
-    // carries 32 scale bytes instead of 16.  Refill v (rounds 2v, 2v+1) goes
-    // out in two halves, at the first stage of rounds 2v-2 and 2v-1, into the
-    // buffer refill v-2 used: every round still issues the same number of
-    // scale fetches per wave, so the wait counts are those of the narrow
-    // scheme.  Buffer rows: the tile's A rows, then its B rows.
+    // Wide scale staging (MX with 1x32 B scales, where the wave count and LDS
+    // allow): a refill brings two rounds of every scale row -- 32 bytes for
+    // e2m1 (16 a round), 16 for the formats with 8 a round -- so that no
+    // fetched scale byte goes unused (the narrow chunk below is 16 bytes a
+    // round whatever the format).  e2m1 takes two lanes per row, 32 rows per
+    // fetch; the others one lane per row, 64 rows per fetch.  Refill v
+    // (rounds 2v, 2v+1) goes out in two halves, at the first stage of rounds
+    // 2v-2 and 2v-1, into the buffer refill v-2 used: every round still
+    // issues the same number of scale fetches per wave, so the wait counts
+    // are those of the narrow scheme.  Buffer rows: the tile's A rows, then
+    // its B rows.
     constexpr int RB = (PATH == PATH_MX4) ? 16 : 8;       // scale bytes per row and round
     constexpr int G = 2;                                  // rounds per wide refill
+    constexpr int RW = RB * G;                            // bytes per row and refill
+    constexpr int LPR = RW / 16, WRPF = 64 / LPR;         // lanes per row, rows per fetch
     constexpr int SAW = BM, SBW = BN;
-    constexpr int WIDE_BUF = (SAW + SBW) * 32;
+    constexpr int WIDE_BUF = (SAW + SBW) * RW;
     constexpr bool PRM = OUT == OUT_BF16 && (!SCL || BIAS);
-    constexpr int NWA = SAW / 32, NWT = NWA + SBW / 32;   // fetches per refill: A rows, all
-    constexpr bool WIDE = PATH == PATH_MX4 && BROWS == 1 && NWT % (G * NW) == 0 &&
+    constexpr int NWA = SAW / WRPF, NWT = NWA + SBW / WRPF;   // fetches per refill: A rows, all
+    constexpr bool WIDE = MX && BROWS == 1 && SAW % WRPF == 0 && SBW % WRPF == 0 && NWT % (G * NW) == 0 &&
                           DNST * STAGE_BYTES + 2 * WIDE_BUF + (PRM ? PRM_BYTES : 0) <= 160 * 1024;
     constexpr int NSCW = NWT / (G * NW);                  // per wave and round
     constexpr int SCL_BYTES = SCL ? 2 * (WIDE ? WIDE_BUF : SCL_BUF) : 0;
@@ -185,12 +183,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr int RPF_B = B4 ? 1 : RPF;
     constexpr int NDSR = TM * RPF + TN * RPF_B;           // fragment reads per sub-step
     constexpr int DMA_A = BM / 16 / NW, DMA_B = BN / BROWS_PER_FETCH / NW; // fetches per wave per stage
-    // FP6: a stage of A (B) is BM (BN) rows of 48 bytes = BM * 48 / 1024 fetches
-    // of 1 KB; each wave takes F6W consecutive ones, all of A or all of B
-    constexpr int F6A = BM * F6ROW / 1024, F6B = BN * F6ROW / 1024, F6W = (F6A + F6B) / NW;
-    static_assert(!F6 || (F6W * NW == F6A + F6B && F6A % F6W == 0 && BM % 64 == 0 && BN % 64 == 0),
-                  "FP6 tiles: whole 64-row groups, whole fetches per wave, each wave on one operand");
-    constexpr int NDMA = F6 ? F6W : DMA_A + DMA_B;
+    constexpr int NDMA = DMA_A + DMA_B;                   // fetches per wave per stage (FP6: per line)
     // scale fetches per wave per chunk: 4 waves fetch A and B scale rows,
     // 8 waves split them (waves 0-3 A, 4-7 B)
     constexpr int NSCD = SCL ? (WIDE ? NSCW : 8 / NW) : 0;
@@ -198,7 +191,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // (region B of the stage 4 back) except for MX, whose region B is busy
     // with scale reads.
     constexpr bool SPLIT = !SCL;
-    static_assert(F6 || (DMA_A * 16 * NW == BM && DMA_B * BROWS_PER_FETCH * NW == BN),
+    static_assert((DMA_A * 16 * NW == BM && DMA_B * BROWS_PER_FETCH * NW == BN),
                   "tile rows must be a whole number of fetches per wave");
     static_assert(BM <= SA_ROWS && (BROWS == 1 ? BN <= SB_ROWS : BN / 32 <= SB_ROWS), "scale rows per buffer");
     using Frag = typename PathTraits<PATH>::Frag;
@@ -227,7 +220,10 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // K is a whole number of stages; the last round may hold fewer than four.
     // Its stages at or past K are fetched through descriptors of empty range
     // (zeros land in LDS, whatever the offset), so their MFMAs add nothing.
+    // FP6: nst counts the 48-byte stages that the MFMAs take, nfetch the
+    // 64-byte lines that hold them (the last one possibly half past K).
     const int nst = F6 ? p.K / 64 : p.kbytes / DSTAGE;
+    const int nfetch = F6 ? (p.kbytes + DSTAGE - 1) / DSTAGE : nst;
     const uint8_t *const a_base = p.A + (int64_t)m0 * p.lda;
     const uint32_t a_range = (uint32_t)((rows_a - 1) * p.lda + p.kbytes);
     // B row-major, or prepacked: 16-row groups of 1 KB blocks (32-row groups
@@ -273,41 +269,13 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             b_off[j] = r < rows_b ? (unsigned)(r * p.ldb + 16 * c) : OOB;
         }
     }
-    // FP6 fetch map: fetch g of an operand's stage covers its LDS bytes
-    // [1024g, 1024g + 1024) -- lane i lands at byte 1024g + 16i, which is
-    // 16-byte chunk (1024g + 16i) % 48 / 16 of row (1024g + 16i) / 48.  Wave w
-    // takes fetches F6W*w .. F6W*w + F6W - 1 of A then B.
-    const int f6g0 = F6W * wave;
-    const bool f6_a = f6g0 < F6A;                         // wave-uniform
-    unsigned f6_off[F6 ? F6W : 1];
-    if constexpr (F6) {
-#pragma unroll
-        for (int j = 0; j < F6W; ++j) {
-            const int g = (f6_a ? f6g0 : f6g0 - F6A) + j;
-            const int byte = 1024 * g + 16 * lane;
-            const int r = byte / F6ROW, c = (byte % F6ROW) / 16;
-            f6_off[j] = r < (f6_a ? rows_a : rows_b) ? (unsigned)(r * (f6_a ? p.lda : p.ldb) + 16 * c) : OOB;
-        }
-    }
-    auto fetch_f6 = [&](int t, auto jc) {
-        constexpr int j = decltype(jc)::value;
-        const bool live = t < nst;
-        uint8_t *slot = &lds[(t & 3) * STAGE_BYTES];
-        const __amdgpu_buffer_rsrc_t r = f6_a ? make_rsrc(a_base, live ? a_range : 0u)
-                                              : make_rsrc(b_base, live ? b_range : 0u);
-        uint8_t *dst = slot + (f6_a ? 0 : BM * F6ROW) + 1024 * ((f6_a ? f6g0 : f6g0 - F6A) + j);
-        dma16(r, f6_off[j] + (unsigned)(t * F6ROW), dst);
-    };
-    // Stage t goes to slot t % 4, its A rows (part 0) and B rows (part 1)
-    // fetched separately (FP6: part 0 is the wave's whole share).
+    // Stage (FP6: line) t goes to slot t % 4, its A rows (part 0) and B rows
+    // (part 1) fetched separately.
     auto fetch_part = [&](int t, auto partc) {
         const unsigned kb = (unsigned)(t * DSTAGE), kbb = (unsigned)t * bstep;
-        const bool live = t < nst;
+        const bool live = t < nfetch;
         uint8_t *slot = &lds[(t & 3) * STAGE_BYTES];
-        if constexpr (F6) {
-            if constexpr (decltype(partc)::value == 0)
-                static_for<0, F6W>([&](auto jc) { fetch_f6(t, jc); });
-        } else if constexpr (decltype(partc)::value == 0) {
+        if constexpr (decltype(partc)::value == 0) {
             const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base, live ? a_range : 0u);
 #pragma unroll
             for (int j = 0; j < DMA_A; ++j)
@@ -324,7 +292,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // B (part 1) rows, the same load fetch_part issues as its j-th.
     auto fetch_one = [&](int t, auto partc, auto jc) {
         constexpr int j = decltype(jc)::value;
-        const bool live = t < nst;
+        const bool live = t < nfetch;
         uint8_t *slot = &lds[(t & 3) * STAGE_BYTES];
         if constexpr (decltype(partc)::value == 0) {
             const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base, live ? a_range : 0u);
@@ -351,8 +319,9 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         sb_fo = rb_row < srows_b ? (unsigned)(rb_row * p.kblocks) : OOB;
     }
     // Wide: half e (0, 1) of a refill is global fetches g = e * NWT/2 + NSCW *
-    // wave + k, k < NSCW; fetch g < NWA covers A scale rows 32g..32g+31, the
-    // others B rows; lane i takes row i/2, bytes 16 * (i % 2) of the refill's 32.
+    // wave + k, k < NSCW; fetch g < NWA covers A scale rows WRPF*g .. +WRPF-1,
+    // the others B rows; lane i takes row i/LPR, bytes 16 * (i % LPR) of the
+    // refill's RW.
     unsigned sw_off[WIDE ? 2 * NSCW : 1];
     bool sw_a[WIDE ? 2 * NSCW : 1];
     int sw_dst[WIDE ? 2 * NSCW : 1];
@@ -363,10 +332,11 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             for (int k = 0; k < NSCW; ++k) {
                 const int g = e * (NWT / 2) + NSCW * wave + k;
                 const bool a = g < NWA;
-                const int row = 32 * (a ? g : g - NWA) + (lane >> 1);
+                const int row = WRPF * (a ? g : g - NWA) + lane / LPR;
                 sw_a[e * NSCW + k] = a;
-                sw_off[e * NSCW + k] = row < (a ? rows_a : rows_b) ? (unsigned)(row * p.kblocks + 16 * (lane & 1)) : OOB;
-                sw_dst[e * NSCW + k] = a ? 1024 * g : SAW * 32 + 1024 * (g - NWA);
+                sw_off[e * NSCW + k] =
+                    row < (a ? rows_a : rows_b) ? (unsigned)(row * p.kblocks + 16 * (lane % LPR)) : OOB;
+                sw_dst[e * NSCW + k] = a ? 1024 * g : SAW * RW + 1024 * (g - NWA);
             }
     }
     // Round u's scale fetch: narrow, round u+1's 16-byte chunk of every row;
@@ -385,7 +355,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
                 const int e = (u - 1) & 1;
 #pragma unroll
                 for (int k = 0; k < NSCW; ++k)
-                    dma16(sw_a[e * NSCW + k] ? rsa : rsb, sw_off[e * NSCW + k] + 32u * (unsigned)v,
+                    dma16(sw_a[e * NSCW + k] ? rsa : rsb, sw_off[e * NSCW + k] + (unsigned)(RW * v),
                           base + sw_dst[e * NSCW + k]);
             }
         } else if constexpr (SCL) {
@@ -423,21 +393,79 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr int SCW = (PATH == PATH_MX4) ? 4 : 2;
     unsigned cra[TM][SCW], crb[TN][SCW];
 
-    // Fragment k of sub-step S in the order the serpentine MFMA sequence
-    // consumes them: A row block 0, the TN B column blocks, A row blocks 1..
-    auto read_item = [&](auto kc, auto sc, int slot, auto setc) {
+    // FP6 fragment of stage s = 4v + J for the 32-row block at `row` of the
+    // part at `part` (A at 0, B at BM * 64).  The stage's bytes [48J, 48J+48)
+    // of round v sit in lines 3v .. 3v+2 (line 3v + l in slot (3v + l) % 4);
+    // lane half h's block is the 24 bytes at 48J + 24h, read as 16 bytes at
+    // 48J + 32h and 8 bytes at 48J + 16 + 8h (both inside one line), and
+    // joined in memory order: [16 | 8] for h = 0, [8 | 16] for h = 1, into
+    // VGPRs 0-5 as the instruction reads a 6-bit operand (element k of the
+    // block in bits 6k..6k+5, lowest bits first).  The 16-byte reads of 16
+    // consecutive rows fall in 16 different bank groups; the 8-byte reads of
+    // rows r and r+16 share banks (a 48-byte stage cannot give the two halves
+    // of a 16-byte slot to one lane half, so one read in two is conflicted).
+    // FP6 fragment reads.  Stage s = 4v + J covers bytes [48J, 48J + 48) of
+    // round v, which sit in lines 3v .. 3v+2 (line 3v + l in slot
+    // (3v + l) % 4).  Lane half h's block is the 24 bytes at 48J + 24h, read
+    // as three 8-byte reads in memory order straight into VGPRs 0-5, as the
+    // instruction takes a 6-bit operand (element k of the block in bits
+    // 6k..6k+5, lowest bits first); each 8-byte read lies inside one line.
+    // (One 16-byte and one 8-byte read would cost fewer LDS cycles, but
+    // lane half 1's block starts 8 bytes into a 16-byte slot, and joining the
+    // two reads in a half-dependent order takes six selects a fragment: the
+    // wave ran out of VALU issue before LDS.)  The 8-byte reads of rows r
+    // and r+16 share banks: a 16-byte-slot swizzle cannot give the two 8-byte
+    // halves of a slot to one lane half, so each read takes two passes.
+    //
+    // Per lane and stage position J the three reads' offsets in a ring whose
+    // line 3v sat in slot 0 -- line * STAGE_BYTES, the swizzled chunk, the
+    // 8-byte half and the lane's row r32 -- are kept in 12 registers.  A read
+    // adds the round's slot of line 3v and the wave's row block (uniform),
+    // wraps at the ring's end (the within-slot part stays below STAGE_BYTES,
+    // so the wrap only touches the slot bits), and takes the operand part and
+    // the 32-row block as the instruction's immediate offset.
+    static_assert(!F6 || (STAGE_BYTES & (STAGE_BYTES - 1)) == 0, "FP6 ring addressing");
+    constexpr unsigned RING = 4u * STAGE_BYTES - 1;
+    unsigned f6o[F6 ? 4 : 1][3];
+    if constexpr (F6) {
+        const int swx = ((r32 >> 2) & 3) << 4;
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                const int b = 48 * J + 24 * h + 8 * q;   // byte of the round
+                f6o[J][q] = (unsigned)((b >> 6) * STAGE_BYTES + ((b & 48) ^ swx) + (b & 8) + r32 * DSTAGE);
+            }
+    }
+    auto f6_frag = [&](auto jc, int s, auto partc, unsigned wrow, auto blkc) -> i32x8 {
+        constexpr int J = decltype(jc)::value;
+        constexpr int IMM = decltype(partc)::value + 32 * decltype(blkc)::value * DSTAGE;
+        const unsigned u = (unsigned)(((3 * (s >> 2)) & 3) * STAGE_BYTES) + wrow * DSTAGE;   // uniform
+        const u32x2 a = *(const u32x2 *)&lds[((u + f6o[J][0]) & RING) + IMM];
+        const u32x2 b = *(const u32x2 *)&lds[((u + f6o[J][1]) & RING) + IMM];
+        const u32x2 c = *(const u32x2 *)&lds[((u + f6o[J][2]) & RING) + IMM];
+        return i32x8{(int)a[0], (int)a[1], (int)b[0], (int)b[1], (int)c[0], (int)c[1], 0, 0};
+    };
+
+    // Fragment k of sub-step S of stage s (ring slot SLOT = s % 4; FP6: J =
+    // s % 4) in the order the serpentine MFMA sequence consumes them: A row
+    // block 0, the TN B column blocks, A row blocks 1..
+    auto read_item = [&](auto kc, auto sc, auto slotc, auto setc, int s) {
         constexpr int k = decltype(kc)::value;
         constexpr int S = decltype(sc)::value;
+        constexpr int SLOT = decltype(slotc)::value;
         constexpr int SET = decltype(setc)::value;
-        const uint8_t *ta = &lds[slot * STAGE_BYTES];
+        const uint8_t *ta = &lds[SLOT * STAGE_BYTES];
         const uint8_t *tb = ta + BM * ASTAGE;
         if constexpr (F6) {
+            using P0 = std::integral_constant<int, 0>;
+            using PB = std::integral_constant<int, BM * DSTAGE>;
             if constexpr (k == 0)
-                fa[SET][0] = dma_frag_f6(ta, arow, h);
+                fa[SET][0] = f6_frag(slotc, s, P0(), (unsigned)(wm * TM * 32), P0());
             else if constexpr (k <= TN)
-                fb[SET][k - 1] = dma_frag_f6(tb, brow + 32 * (k - 1), h);
+                fb[SET][k - 1] = f6_frag(slotc, s, PB(), (unsigned)(wn * TN * 32), std::integral_constant<int, k - 1>());
             else
-                fa[SET][k - TN] = dma_frag_f6(ta, arow + 32 * (k - TN), h);
+                fa[SET][k - TN] = f6_frag(slotc, s, P0(), (unsigned)(wm * TM * 32), std::integral_constant<int, k - TN>());
         } else if constexpr (k == 0) {
             fa[SET][0] = dma_frag<PATH, S>(ta, arow, h);
         } else if constexpr (k <= TN) {
@@ -459,12 +487,12 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     auto load_chunk = [&](int t) {
         if constexpr (SCL) {
             // narrow: round r's 16 bytes at row * 16 of buffer r % 2; wide:
-            // round r's RB bytes at row * 32 + RB * (r % G) of buffer (r / G) % 2
+            // round r's RB bytes at row * RW + RB * (r % G) of buffer (r / G) % 2
             const int r = t >> 2;
             const uint8_t *sbuf = WIDE ? &lds[OPND_BYTES + ((r / G) & 1) * WIDE_BUF] + RB * (r % G)
                                        : &lds[OPND_BYTES + (r & 1) * SCL_BUF];
-            constexpr int SP = WIDE ? 32 : 16;                // row pitch
-            constexpr int SBOFF = WIDE ? SAW * 32 : SA_ROWS * 16;
+            constexpr int SP = WIDE ? RW : 16;                // row pitch
+            constexpr int SBOFF = WIDE ? SAW * RW : SA_ROWS * 16;
             auto rd = [&](const uint8_t *row_base, unsigned (&w)[SCW]) {
                 if constexpr (SCW == 4) {
                     const u32x4 v = *(const u32x4 *)row_base;
@@ -611,7 +639,8 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     };
 
     // Prologue: the tile's epilogue operands (waves 0-2, one fetch each),
-    // scale chunk 0, stages 0..2 and the A rows of stage 3; wait for stage 0.
+    // scale chunk 0, stages 0..2 and the A rows of stage 3 (FP6: lines 0..3);
+    // wait for stage 0 (line 0).
     if constexpr (PRM) {
         if (wave == 0 && !SCL)
             dma16(make_rsrc(p.scale_a + m0, (uint32_t)(rows_a * 4)), 16 * lane, &lds[PRM_OFF]);
@@ -625,7 +654,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // (issue order is what the wait counts: no reordering across stages)
     fetch_scales(0);
 #pragma unroll
-    for (int t = 0; t < 3; ++t) {
+    for (int t = 0; t < (F6 ? 4 : 3); ++t) {
         __builtin_amdgcn_sched_barrier(0);
         fetch_part(t, I0());
         fetch_part(t, I1());
@@ -635,12 +664,12 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         fetch_part(3, I0());
     __builtin_amdgcn_sched_barrier(0);
     twin_sync();
-    wait_vmcnt<2 * NDMA + (SPLIT ? DMA_A : 0)>();
+    wait_vmcnt<(F6 ? 3 : 2) * NDMA + (SPLIT ? DMA_A : 0)>();
     lds_barrier();
     // stage 0's first fragments (one sub-step per stage: those its first
     // half of MFMAs uses; its region A reads the rest)
     static_for<0, (NSUB == 1) ? 1 + TN + (NQ / 2 - 1) / TN : TM + TN>(
-        [&](auto kc) { read_item(kc, I0(), 0, I0()); });
+        [&](auto kc) { read_item(kc, I0(), I0(), I0(), 0); });
     read_scales(0, I0(), std::false_type());
     use_next_scales();
 
@@ -672,12 +701,17 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         // that neither region carries a whole stage of fragment traffic.
         constexpr int IMAX = (NQ / 2 - 1) / TN;
         constexpr int EARLY = (NSUB == 1) ? 1 + TN + IMAX : NIT;
+        // FP6 stages past K (the last round's tail) read what follows the
+        // row's last byte in a half-live line: they are not multiplied.  The
+        // other paths multiply zeros there.  (K % 128 == 0: the stage count
+        // is even, so the first two stages of a round are always live.)
+        const bool mul = !F6 || J < 2 || t < nst;
         // ---- region A
         {
             constexpr int NA = (NSUB == 2) ? NQ : NQ / 2;
             constexpr int NSC = (J == 0) ? NSCD : 0;
             constexpr int VA = SPLIT ? 0 : DMA_A;
-            constexpr int V = NSC + (F6 ? F6W : VA + DMA_B);   // fetches: scale chunk, A rows, B rows
+            constexpr int V = NSC + (F6 ? 0 : VA + DMA_B);   // fetches: scale chunk, A rows, B rows
             constexpr int R = (NSUB == 2) ? NIT : NIT - EARLY;
             constexpr int NR = NA > 2 ? NA - 2 : 1;        // reads go out before the last two MFMAs
             static_for<0, NA>([&](auto qc) {
@@ -685,20 +719,19 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
                 static_for<(Q < NR ? R * Q / NR : R), (Q < NR ? R * (Q + 1) / NR : R)>([&](auto kc) {
                     constexpr int k = decltype(kc)::value;
                     if constexpr (NSUB == 2)
-                        read_item(kc, I1(), J, I1());
+                        read_item(kc, I1(), jc, I1(), t);
                     else
-                        read_item(std::integral_constant<int, EARLY + k>(), I0(), J,
-                                  std::integral_constant<int, SET0>());
+                        read_item(std::integral_constant<int, EARLY + k>(), I0(), jc,
+                                  std::integral_constant<int, SET0>(), t);
                 });
-                mfmas(I0(), std::integral_constant<int, SET0>(), qc, std::integral_constant<int, Q + 1>(), jc);
+                if (mul)
+                    mfmas(I0(), std::integral_constant<int, SET0>(), qc, std::integral_constant<int, Q + 1>(), jc);
                 if constexpr (FOLD_ODD && (J & 1) && Q >= 1)
                     fold(std::integral_constant<int, Q - 1>());
                 static_for<V * Q / NA, V * (Q + 1) / NA>([&](auto vc) {
                     constexpr int v = decltype(vc)::value;
                     if constexpr (v < NSC)
                         fetch_scales((t >> 2) + 1);
-                    else if constexpr (F6)
-                        fetch_f6(t + 3, std::integral_constant<int, v - NSC>());
                     else if constexpr (v < NSC + VA)
                         fetch_one(t + 3, I0(), std::integral_constant<int, v - NSC>());
                     else
@@ -711,8 +744,14 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
                 fold(std::integral_constant<int, NA - 1>());
         }
         // loads issued after stage t+1's: stages t+2 and t+3, plus the scale
-        // chunk when it went out at stage t or t-1
-        constexpr int AFTER = 2 * NDMA + ((J == 0 || J == 1) ? NSCD : 0);
+        // chunk when it went out at stage t or t-1.  FP6 (round v, t = 4v + J;
+        // issue order: line 3v+3 at stage 4v-1, scale chunk v+1 at 4v, lines
+        // 3v+4..3v+6 at 4v+1..4v+3): stage t+1 needs line 3v+1 (J = 0: then
+        // lines 3v+2, 3v+3 and the chunk went out), 3v+2 (J = 1: line 3v+3 and
+        // the chunk), 3v+2 again (J = 2), or line 3v+3 and the chunk (J = 3:
+        // then lines 3v+4, 3v+5).
+        constexpr int AFTER = F6 ? (J == 1 ? 1 : 2) * NDMA + (J == 3 ? 0 : NSCD)
+                                 : 2 * NDMA + ((J == 0 || J == 1) ? NSCD : 0);
         twin_sync();
         wait_vmcnt<AFTER>();
         lds_barrier();
@@ -721,7 +760,9 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         {
             constexpr int NB = (NSUB == 2) ? NQ : NQ - NQ / 2;
             constexpr int QB = (NSUB == 2) ? 0 : NQ / 2;   // first MFMA of the region
-            constexpr int V = SPLIT ? DMA_A : 0;
+            // FP6: the line whose slot the barrier just freed (line 3v + J - 1,
+            // last read by stage t) is refilled with line 3v + J + 3
+            constexpr int V = F6 ? (J == 0 ? 0 : NDMA) : SPLIT ? DMA_A : 0;
             constexpr bool CHUNK = SCL && JN == 0;         // stage t+1 starts a round
             constexpr int R = EARLY;
             constexpr int NR = NB > 2 ? NB - 2 : 1;
@@ -730,16 +771,25 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             static_for<0, NB>([&](auto qc) {
                 constexpr int Q = decltype(qc)::value;
                 static_for<(Q < NR ? R * Q / NR : R), (Q < NR ? R * (Q + 1) / NR : R)>([&](auto kc) {
-                    read_item(kc, I0(), JN, std::integral_constant<int, SETN>());
+                    read_item(kc, I0(), std::integral_constant<int, JN>(), std::integral_constant<int, SETN>(),
+                              t + 1);
                 });
                 if constexpr (NSUB == 2)
                     mfmas(I1(), I1(), qc, std::integral_constant<int, Q + 1>(), jc);
-                else
+                else if (mul)
                     mfmas(I0(), std::integral_constant<int, SET0>(), std::integral_constant<int, QB + Q>(),
                           std::integral_constant<int, QB + Q + 1>(), jc);
                 if constexpr (FOLD_ODD && (J & 1) && Q >= 1)
                     fold(std::integral_constant<int, QB + Q - 1>());
-                static_for<V * Q / NB, V * (Q + 1) / NB>([&](auto vc) { fetch_one(t + 4, I0(), vc); });
+                static_for<V * Q / NB, V * (Q + 1) / NB>([&](auto vc) {
+                    constexpr int v = decltype(vc)::value;
+                    if constexpr (!F6)
+                        fetch_one(t + 4, I0(), vc);
+                    else if constexpr (v < DMA_A)
+                        fetch_one(3 * (t >> 2) + J + 3, I0(), vc);
+                    else
+                        fetch_one(3 * (t >> 2) + J + 3, I1(), std::integral_constant<int, v - DMA_A>());
+                });
                 if constexpr (FENCE)
                     __builtin_amdgcn_sched_barrier(0);
             });
@@ -755,10 +805,11 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             __builtin_amdgcn_sched_barrier(0);
     };
 
-    // The host guarantees kbytes % 64 == 0 (a whole number of stages; for
-    // the scaled paths, of the stages that one scale word covers).  Fetches
-    // run three stages ahead, into stages past K that are never multiplied
-    // or, in a partial last round, multiplied as zeros.
+    // The host guarantees a whole number of stages (kbytes % 64 == 0; for the
+    // scaled paths, of the stages that one scale word covers; FP6: K % 128 ==
+    // 0).  Fetches run three stages (FP6: two to three lines) ahead, into
+    // stages past K that are never multiplied or, in a partial last round,
+    // multiplied as zeros (FP6: skipped).
     for (int t = 0; t < nst; t += 4) {
         stage(t, I0());
         stage(t + 1, I1());

@@ -1,7 +1,8 @@
 // MX variants with 6-bit elements (OCP FP6 E2M3 / E3M2), LDS-fetch kernel only:
-// tiles 4 (256x256, four waves), 5 (256x256, eight waves) and 7 (128x128).
-// The 192x192 tile is not built: its 192 rows are not whole 1 KB fetches per
-// wave at 48 bytes a row.
+// tiles 4 (256x256, four waves) and 7 (128x128).  Not built: the eight-wave
+// 256x256 tile (its 256 registers a lane cannot hold the fragments' read
+// offsets beside the accumulators: it spills) and 192x192 (a ring slot of 384
+// rows x 64 bytes is not a power of two, which the FP6 ring addressing needs).
 #include "qgemm_launch.hpp"
 
 namespace qgemm {
@@ -12,9 +13,6 @@ static hipError_t tiles(int tile, const Params &p, hipStream_t s)
     switch (tile) {
     case DMA_TILE:
         hipLaunchKernelGGL((qgemm_dma_kernel<PATH, 2, 4, 4, BIAS, BROWS, OUT_BF16>), grid, block, 0, s, p);
-        break;
-    case DMA8_TILE:
-        hipLaunchKernelGGL((qgemm_dma_kernel<PATH, 4, 4, 2, BIAS, BROWS, OUT_BF16>), grid, block, 0, s, p);
         break;
     case DMA128_TILE:
         hipLaunchKernelGGL((qgemm_dma_kernel<PATH, 2, 2, 2, BIAS, BROWS, OUT_BF16>), grid, block, 0, s, p);

@@ -166,9 +166,9 @@ def test_tile_table():
     # scaled path: K % 128)
     assert L.qgemm_select_tile(2, 16384, 7168, 2112) == 0
     assert L.qgemm_select_tile(3, 8192, 8192, 8256) == 0        # e2m1, K % 128 == 64 as well
-    # 6-bit MX: the LDS-fetch kernel only -- 256x256 (tile 5) or 128x128 (7)
-    assert L.qgemm_select_tile(6, 8192, 8192, 8192) == 5
-    assert L.qgemm_select_tile(7, 8192, 8192, 8192) == 5
+    # 6-bit MX: the LDS-fetch kernel only -- 256x256 (the four-wave tile 4) or 128x128 (7)
+    assert L.qgemm_select_tile(6, 8192, 8192, 8192) == 4
+    assert L.qgemm_select_tile(7, 8192, 8192, 8192) == 4
     assert L.qgemm_select_tile(6, 16, 8192, 8192) == 7
     assert L.qgemm_select_tile(7, 4096, 2112, 7168) == 7         # the table's 192x192 choice
     # small M: the small-M kernel (16- or 64-row tiles), every path

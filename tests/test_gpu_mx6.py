@@ -4,7 +4,7 @@ K elements) against the CPU oracle (orc_mxf) on the same seeded inputs,
 through the C ABI.
 
 Bar: per element |gpu - oracle| <= 1e-2 * sum_k |A~ B~| + 1 bf16 ulp, cosine
->= 0.99999.  Every tile it runs on (4, 5, 7), both FP6 types, both B-scale
+>= 0.99999.  Every tile it runs on (4, 7), both FP6 types, both B-scale
 layouts, ragged M / N, random scale codes (a scale paired with the wrong K
 block or row leaves the bound), bias, canaries around the output, K with a
 partial last round of stages under poisoned row padding and non-finite scales
@@ -24,7 +24,7 @@ import block_scaled_precision_02_amd as q  # noqa: E402
 
 from tests import parity  # noqa: E402
 
-TILES = [4, 5, 7]
+TILES = [4, 7]
 FMTS = [("mxfp6", q.QGEMM_MX_E2M3), ("mxfp6_e3m2", q.QGEMM_MX_E3M2)]
 
 
@@ -139,12 +139,12 @@ def test_mx6_partial_round(name, fmt, tile, K):
 
 
 def test_mx6_table_choice_and_forced_tiles():
-    assert q.select_tile(6, 8192, 8192, 8192) == 5
-    assert q.select_tile(7, 8192, 8192, 8192) == 5
+    assert q.select_tile(6, 8192, 8192, 8192) == 4
+    assert q.select_tile(7, 8192, 8192, 8192) == 4
     assert q.select_tile(6, 16, 8192, 8192) == 7       # no small-M kernel: the 128x128 tile
-    assert q.select_tile(6, 4096, 2112, 7168 // 64 * 64) in (5, 7)
+    assert q.select_tile(6, 4096, 2112, 7168 // 64 * 64) in (4, 7)
     d = _make("mxfp6", 100, 130, 256)
-    for t in (6, 8, 9, 0):                              # tiles the 6-bit path does not build run its own
+    for t in (5, 6, 8, 9, 0):                           # tiles the 6-bit path does not build run its own
         q.force_tile(t)
         _check(d, f"forced tile {t}")
 
