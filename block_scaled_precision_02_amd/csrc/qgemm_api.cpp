@@ -361,8 +361,8 @@ int pick_tile_packed(int path, Shape s, int64_t kbytes, bool bf16_out)
 // rows): one MI355X, 16384x7168x2048 0.302 ms vs 0.310 ms.
 constexpr int64_t F8B_K_MULTIPLE = 128;
 
-// Mixed MX (e4m3 A, e2m1 B) runs in the LDS-fetch kernel: 256x256 (tile 5,
-// or 4 when forced) or 128x128 (tile 7) -- the table's 192x192 choice takes
+// Mixed MX (e4m3 A, e2m1 B) runs in the LDS-fetch kernel: 256x256 (tile 4,
+// or 5 when forced) or 128x128 (tile 7) -- the table's 192x192 choice takes
 // tile 7 -- and for M <= 16 in the small-M kernel (tile 8; 9 when forced).
 int pick_tile_mx84(Shape s)
 {
@@ -371,12 +371,12 @@ int pick_tile_mx84(Shape s)
         return g_forced_tile;
     if (s.M <= SKINNY_MAX_M_MX)
         return SKINNY16_TILE;
-    return select_tile_impl(2, s.M, s.N) == 0 ? DMA8_TILE : DMA128_TILE;
+    // the four-wave 256x256 tile, where the 16-byte wide scale refills apply
+    // (8192^3 on one box, alternating: 0.445 vs 0.477 ms for the eight-wave
+    // tile 5)
+    return select_tile_impl(2, s.M, s.N) == 0 ? DMA_TILE : DMA128_TILE;
 }
 
-// MX with 6-bit elements runs in the LDS-fetch kernel only: 256x256 (tile 5,
-// or 4 when forced) or 128x128 (tile 7) -- the table's 192x192 choice and
-// small M take tile 7.
 // 6-bit MX: the four-wave 256x256 tile where the 256x256 grid fills the
 // chip, else 128x128 (the only two FP6 tiles built).
 int pick_tile_mx6(Shape s)

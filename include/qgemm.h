@@ -326,7 +326,7 @@ const char *qgemm_status_string(qgemm_status status);
  * HIP call; for MX, assuming 16-byte-aligned scale arrays).  path: 0 int8,
  * 1 fp8, 2 MX e4m3, 3 MX e2m1, 4 fp8 blockscale (tile 8 for M <= 16, else
  * tile 10 when its grid of 256x128 tiles fills the 256 CUs at least once,
- * else tile 7), 5 MX e4m3 A with e2m1 B (tile 8 for M <= 16, else tile 5
+ * else tile 7), 5 MX e4m3 A with e2m1 B (tile 8 for M <= 16, else tile 4
  * where the table picks 256x256, else 7), 6 / 7 MX with 6-bit E2M3 / E3M2
  * elements (tile 4 where the table picks 256x256, else 7; no small-M tile).
  * Returns the tile id, or -1 for a bad path:
@@ -343,8 +343,8 @@ const char *qgemm_status_string(qgemm_status status);
  * Tiles 4-7 need K bytes a multiple of 64 (whole stages; a last round of
  * fewer than four is masked) and MX scale rows of whole dwords (K % 128),
  * with scale arrays aligned to 16 (e2m1) or 8 (e4m3) bytes; where these
- * hold, the table's 256x256 choice runs as tile 4 (INT8, 6-bit MX) or 5
- * (the others), 192x192 as tile 6 and 128x128 as tile 7.  Calls with M <= 64 take tile 8
+ * hold, the table's 256x256 choice runs as tile 4 (INT8, mixed and 6-bit MX)
+ * or 5 (the others), 192x192 as tile 6 and 128x128 as tile 7.  Calls with M <= 64 take tile 8
  * (M <= 16) or 9 (INT8 and FP8 only: MX takes the small-M kernel up to
  * M = 16). */
 int qgemm_select_tile(int path, int64_t M, int64_t N, int64_t K);

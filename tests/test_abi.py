@@ -361,7 +361,7 @@ def test_mx_mixed_checks_pass_before_the_device_check(monkeypatch):
     monkeypatch.setenv("QGEMM_FAKE_ARCH", "gfx1201")
     assert mx2() == q.QGEMM_ERR_UNSUPPORTED_DEVICE
     assert mx2(M=0) == q.QGEMM_OK
-    assert q.select_tile(5, 8192, 8192, 8192) == 5
+    assert q.select_tile(5, 8192, 8192, 8192) == 4
     assert q.select_tile(5, 16, 8192, 8192) == 8           # small M: the small-M kernel
     assert q.select_tile(5, 17, 8192, 8192) == 7           # the table: 64 tiles of 128 beat 32 of 256
 
