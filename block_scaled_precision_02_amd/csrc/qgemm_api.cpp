@@ -308,13 +308,14 @@ bool dma_eligible(int path, int64_t kbytes, int64_t K, bool svec)
 // 13.5 vs 18.3 us).
 constexpr int64_t SKINNY_MAX_M = 64, SKINNY_MAX_M_MX = 16;
 
-// The LDS-fetch form of the 256x256 edge.  INT8 takes the four-wave kernel
-// (one wave per SIMD, 256 accumulators in AGPRs: a third fewer LDS fragment
-// bytes per MFMA); the other paths the eight-wave one.  One MI355X, the
-// interleaved schedule, same box alternating: INT8 30000x21504x5376 3.036 ms
-// (tile 4) vs 3.088 ms (tile 5); MXFP4 8192^3 0.332 vs 0.304 ms; MXFP8
-// 16384x7168x2048 0.255 vs 0.248 ms.
-int big_dma_tile(int path) { return path == 0 ? DMA_TILE : DMA8_TILE; }
+// The LDS-fetch form of the 256x256 edge: the eight-wave kernel, whose INT8
+// and e2m1 forms fetch two stages of a row per request (one MI355X, same box
+// alternating: INT8 30000x21504x5376 2.909 ms on tile 5 vs 3.031 ms on the
+// four-wave tile 4; MXFP4 8192^3 0.304 vs 0.332 ms; MXFP8 16384x7168x2048
+// 0.248 vs 0.255 ms) -- except INT8 with a prepacked B, whose whole-line
+// fetches gain nothing from pairs and keep the four-wave kernel's deeper
+// prefetch (2.862 vs 2.900 ms).
+int big_dma_tile(int path, bool packed = false) { return (path == 0 && packed) ? DMA_TILE : DMA8_TILE; }
 
 int pick_tile(int path, Shape s, int64_t kbytes, bool svec, bool bf16_out)
 {
@@ -344,8 +345,10 @@ int pick_tile(int path, Shape s, int64_t kbytes, bool svec, bool bf16_out)
 int pick_tile_packed(int path, Shape s, int64_t kbytes, bool bf16_out)
 {
     const int t = pick_tile(path, s, kbytes, true, bf16_out);
+    if (g_forced_tile < 0 && t == big_dma_tile(path))
+        return big_dma_tile(path, true);
     switch (t) {
-    case 0: return g_forced_tile == 0 ? DMA_TILE : big_dma_tile(path);
+    case 0: return g_forced_tile == 0 ? DMA_TILE : big_dma_tile(path, true);
     case 1: return DMA128_TILE;
     case 2: return DMA8_TILE;
     case 3: return DMA192_TILE;

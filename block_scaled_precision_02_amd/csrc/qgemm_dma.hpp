@@ -110,18 +110,30 @@ __device__ __forceinline__ i32x8 dma_frag_b32(const uint8_t *tile, int row, int 
 //          chunk 2+h -> block 1 of the stage; lane half h's scale is block h's.
 //   e2m1:  16 bytes = one 32-element block, chunk 2h+S (block 2h+S); lane
 //          half h's scales are blocks 2h and 2h+1 of the stage.
-template <int PATH, int S>
+// Pair layout: two consecutive stages share a 128-byte row segment, logical
+// chunk q = 4 * (stage % 2) + c of row r at slot q ^ ((r >> 1) & 7), so that
+// 16 lanes on 16 consecutive rows at one logical chunk cover 16 different
+// 16-byte slots of 256 bytes of banks.
+__device__ __forceinline__ int plds_off(int r, int q)
+{
+    return r * 128 + ((q ^ ((r >> 1) & 7)) << 4);
+}
+
+// HALF < 0: the one-stage layout (dlds_off); else the stage's half of the
+// pair layout.
+template <int PATH, int S, int HALF>
 __device__ __forceinline__ typename PathTraits<PATH>::Frag dma_frag(const uint8_t *tile, int row, int h)
 {
+    auto off = [&](int c) { return HALF < 0 ? dlds_off(row, c) : plds_off(row, 4 * HALF + c); };
     typename PathTraits<PATH>::Frag f;
     if constexpr (PATH == PATH_I8) {
-        f = *(const i32x4 *)(tile + dlds_off(row, 2 * S + h));
+        f = *(const i32x4 *)(tile + off(2 * S + h));
     } else if constexpr (PATH == PATH_MX4) {
-        i32x4 lo = *(const i32x4 *)(tile + dlds_off(row, 2 * h + S));
+        i32x4 lo = *(const i32x4 *)(tile + off(2 * h + S));
         f = i32x8{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
     } else {
-        i32x4 lo = *(const i32x4 *)(tile + dlds_off(row, h));
-        i32x4 hi = *(const i32x4 *)(tile + dlds_off(row, 2 + h));
+        i32x4 lo = *(const i32x4 *)(tile + off(h));
+        i32x4 hi = *(const i32x4 *)(tile + off(2 + h));
         f = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
     return f;
@@ -184,6 +196,25 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr int NDSR = TM * RPF + TN * RPF_B;           // fragment reads per sub-step
     constexpr int DMA_A = BM / 16 / NW, DMA_B = BN / BROWS_PER_FETCH / NW; // fetches per wave per stage
     constexpr int NDMA = DMA_A + DMA_B;                   // fetches per wave per stage (FP6: per line)
+    // Pair fetches (the eight-wave 256x256 tile of INT8, and of e2m1 with
+    // 1x32 B scales -- with 32x32 ones it would spill): one
+    // instruction brings 8 rows x 128 bytes -- two stages of each row, whole
+    // 128-byte lines -- into the pair layout (plds_off), so a row-major
+    // operand goes out as 128-byte requests instead of 64-byte halves (the
+    // L2 request count halves; prepacked B, already fetched as whole lines,
+    // is gathered from its blocks into the same layout).  Pair k = stages 2k,
+    // 2k+1 in double slot k % 2; a pair can only be issued once both of its
+    // slots are free, i.e. after the barrier of the odd stage before, so the
+    // fetch runs two stages ahead instead of three: the eight-wave tile's
+    // longer stages hide that, the four-wave tiles' do not (one MI355X,
+    // alternating: INT8 30000x21504x5376 3.162 -> 2.999 ms moving from tile
+    // 4 to tile 5 with pairs, MXFP4 8192^3 0.291 -> 0.276 ms; FP8
+    // 4096x2112x7168 on the four-wave 192x192 tile 0.075 -> 0.082, INT8
+    // 256x256x512 on 128x128 5.4 -> 6.1 us).
+    constexpr bool PAIR = (PATH == PATH_I8 || (PATH == PATH_MX4 && BROWS == 1)) && WN == 4 && TM == 4 && TN == 2;
+    constexpr int DPA = BM / 8 / NW, DPB = BN / 8 / NW;   // pair fetches per wave: A, B
+    constexpr int NPF = PAIR ? DPA + DPB : 0;
+    static_assert(!PAIR || (DPA * 8 * NW == BM && DPB * 8 * NW == BN), "pair fetches: whole 8-row groups");
     // scale fetches per wave per chunk: 4 waves fetch A and B scale rows,
     // 8 waves split them (waves 0-3 A, 4-7 B)
     constexpr int NSCD = SCL ? (WIDE ? NSCW : 8 / NW) : 0;
@@ -269,6 +300,53 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             b_off[j] = r < rows_b ? (unsigned)(r * p.ldb + 16 * c) : OOB;
         }
     }
+    // Pair fetch map: wave w's j-th A pair fetch covers rows 8*(DPA*w + j) ..
+    // +7; lane i takes row +i/8 and the logical chunk q whose slot is i%8
+    // (chunks 4..7: the pair's second stage).
+    // pa_m / pb_m: the same offsets with the second stage's chunks sent out of
+    // range, for a pair whose second stage is past K.
+    unsigned pa_off[PAIR ? DPA : 1], pb_off[PAIR ? DPB : 1], pa_m[PAIR ? DPA : 1], pb_m[PAIR ? DPB : 1];
+    if constexpr (PAIR) {
+#pragma unroll
+        for (int j = 0; j < DPA; ++j) {
+            const int r = 8 * (DPA * wave + j) + (lane >> 3);
+            const int q = (lane & 7) ^ ((r >> 1) & 7);
+            pa_off[j] = r < rows_a ? (unsigned)(r * p.lda + 16 * q) : OOB;
+            pa_m[j] = q < 4 ? pa_off[j] : OOB;
+        }
+#pragma unroll
+        for (int j = 0; j < DPB; ++j) {
+            const int r = 8 * (DPB * wave + j) + (lane >> 3);
+            const int q = (lane & 7) ^ ((r >> 1) & 7);
+            // prepacked B (16-row groups of 1 KB blocks, block t = stage t of
+            // the group's rows in the one-stage LDS order): chunk q of pair 0
+            // is chunk q % 4 of row r in block q / 4.  The 8 rows of one fetch
+            // are 512 contiguous bytes of each of the two blocks.
+            const int c = q & 3;
+            const unsigned packed = (unsigned)((r / 16) * gbytes + (q >> 2) * 1024 + (r % 16) * DSTAGE +
+                                               ((c ^ ((r >> 2) & 3)) << 4));
+            // (packed: every row of a group that holds a row below N, as the
+            // one-stage map fetches whole groups)
+            const bool ok = p.b_packed ? 16 * (r / 16) < rows_b : r < rows_b;
+            pb_off[j] = ok ? (p.b_packed ? packed : (unsigned)(r * p.ldb + 16 * q)) : OOB;
+            pb_m[j] = q < 4 ? pb_off[j] : OOB;
+        }
+    }
+    const unsigned pbstep = p.b_packed ? 2048u : 128u;    // B bytes per pair along K
+    // The v-th pair fetch of pair k (A fetches, then B).
+    auto fetch_pair = [&](int k, auto vc) {
+        constexpr int v = decltype(vc)::value;
+        const bool live = 2 * k < nst, live_hi = 2 * k + 1 < nst;   // uniform
+        uint8_t *ds = &lds[(k & 1) * 2 * STAGE_BYTES];
+        if constexpr (v < DPA) {
+            const unsigned o = (live_hi ? pa_off[v] : pa_m[v]) + (unsigned)(128 * k);
+            dma16(make_rsrc(a_base, live ? a_range : 0u), o, ds + (DPA * wave + v) * 1024);
+        } else {
+            constexpr int j = v - DPA;
+            const unsigned o = (live_hi ? pb_off[j] : pb_m[j]) + pbstep * (unsigned)k;
+            dma16(make_rsrc(b_base, live ? b_range : 0u), o, ds + BM * 128 + (DPB * wave + j) * 1024);
+        }
+    };
     // Stage (FP6: line) t goes to slot t % 4, its A rows (part 0) and B rows
     // (part 1) fetched separately.
     auto fetch_part = [&](int t, auto partc) {
@@ -455,8 +533,10 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         constexpr int S = decltype(sc)::value;
         constexpr int SLOT = decltype(slotc)::value;
         constexpr int SET = decltype(setc)::value;
-        const uint8_t *ta = &lds[SLOT * STAGE_BYTES];
-        const uint8_t *tb = ta + BM * ASTAGE;
+        // pair layout: slot SLOT is half SLOT % 2 of double slot SLOT / 2
+        constexpr int HALF = PAIR ? (SLOT & 1) : -1;
+        const uint8_t *ta = PAIR ? &lds[(SLOT >> 1) * 2 * STAGE_BYTES] : &lds[SLOT * STAGE_BYTES];
+        const uint8_t *tb = ta + BM * (PAIR ? 128 : ASTAGE);
         if constexpr (F6) {
             using P0 = std::integral_constant<int, 0>;
             using PB = std::integral_constant<int, BM * DSTAGE>;
@@ -467,14 +547,14 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             else
                 fa[SET][k - TN] = f6_frag(slotc, s, P0(), (unsigned)(wm * TM * 32), std::integral_constant<int, k - TN>());
         } else if constexpr (k == 0) {
-            fa[SET][0] = dma_frag<PATH, S>(ta, arow, h);
+            fa[SET][0] = dma_frag<PATH, S, HALF>(ta, arow, h);
         } else if constexpr (k <= TN) {
             if constexpr (B4)
                 fb[SET][k - 1] = dma_frag_b32(tb, brow + 32 * (k - 1), h);
             else
-                fb[SET][k - 1] = dma_frag<PATH, S>(tb, brow + 32 * (k - 1), h);
+                fb[SET][k - 1] = dma_frag<PATH, S, HALF>(tb, brow + 32 * (k - 1), h);
         } else {
-            fa[SET][k - TN] = dma_frag<PATH, S>(ta, arow + 32 * (k - TN), h);
+            fa[SET][k - TN] = dma_frag<PATH, S, HALF>(ta, arow + 32 * (k - TN), h);
         }
     };
 
@@ -653,18 +733,27 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     using I1 = std::integral_constant<int, 1>;
     // (issue order is what the wait counts: no reordering across stages)
     fetch_scales(0);
+    if constexpr (PAIR) {
+        // pairs 0 and 1 (stages 0..3); wait for pair 0
 #pragma unroll
-    for (int t = 0; t < (F6 ? 4 : 3); ++t) {
+        for (int k = 0; k < 2; ++k) {
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<0, NPF>([&](auto vc) { fetch_pair(k, vc); });
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < (F6 ? 4 : 3); ++t) {
+            __builtin_amdgcn_sched_barrier(0);
+            fetch_part(t, I0());
+            fetch_part(t, I1());
+        }
         __builtin_amdgcn_sched_barrier(0);
-        fetch_part(t, I0());
-        fetch_part(t, I1());
+        if constexpr (SPLIT)
+            fetch_part(3, I0());
     }
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (SPLIT)
-        fetch_part(3, I0());
-    __builtin_amdgcn_sched_barrier(0);
     twin_sync();
-    wait_vmcnt<(F6 ? 3 : 2) * NDMA + (SPLIT ? DMA_A : 0)>();
+    wait_vmcnt<PAIR ? NPF : (F6 ? 3 : 2) * NDMA + (SPLIT ? DMA_A : 0)>();
     lds_barrier();
     // stage 0's first fragments (one sub-step per stage: those its first
     // half of MFMAs uses; its region A reads the rest)
@@ -711,7 +800,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             constexpr int NA = (NSUB == 2) ? NQ : NQ / 2;
             constexpr int NSC = (J == 0) ? NSCD : 0;
             constexpr int VA = SPLIT ? 0 : DMA_A;
-            constexpr int V = NSC + (F6 ? 0 : VA + DMA_B);   // fetches: scale chunk, A rows, B rows
+            constexpr int V = NSC + ((F6 || PAIR) ? 0 : VA + DMA_B);   // fetches: scale chunk, A rows, B rows
             constexpr int R = (NSUB == 2) ? NIT : NIT - EARLY;
             constexpr int NR = NA > 2 ? NA - 2 : 1;        // reads go out before the last two MFMAs
             static_for<0, NA>([&](auto qc) {
@@ -750,8 +839,12 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         // lines 3v+2, 3v+3 and the chunk went out), 3v+2 (J = 1: line 3v+3 and
         // the chunk), 3v+2 again (J = 2), or line 3v+3 and the chunk (J = 3:
         // then lines 3v+4, 3v+5).
-        constexpr int AFTER = F6 ? (J == 1 ? 1 : 2) * NDMA + (J == 3 ? 0 : NSCD)
-                                 : 2 * NDMA + ((J == 0 || J == 1) ? NSCD : 0);
+        // Pairs (issued in region B of odd stages: pair (t+3)/2 at stage t):
+        // stage t+1 of an even t is the second half of a pair followed by one
+        // more pair; of an odd t, the first half of the last pair issued.
+        constexpr int AFTER = PAIR ? ((J & 1) ? 0 : NPF) + ((J == 0 || J == 1) ? NSCD : 0)
+                            : F6   ? (J == 1 ? 1 : 2) * NDMA + (J == 3 ? 0 : NSCD)
+                                   : 2 * NDMA + ((J == 0 || J == 1) ? NSCD : 0);
         twin_sync();
         wait_vmcnt<AFTER>();
         lds_barrier();
@@ -762,7 +855,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             constexpr int QB = (NSUB == 2) ? 0 : NQ / 2;   // first MFMA of the region
             // FP6: the line whose slot the barrier just freed (line 3v + J - 1,
             // last read by stage t) is refilled with line 3v + J + 3
-            constexpr int V = F6 ? (J == 0 ? 0 : NDMA) : SPLIT ? DMA_A : 0;
+            constexpr int V = PAIR ? ((J & 1) ? NPF : 0) : F6 ? (J == 0 ? 0 : NDMA) : SPLIT ? DMA_A : 0;
             constexpr bool CHUNK = SCL && JN == 0;         // stage t+1 starts a round
             constexpr int R = EARLY;
             constexpr int NR = NB > 2 ? NB - 2 : 1;
@@ -783,7 +876,9 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
                     fold(std::integral_constant<int, QB + Q - 1>());
                 static_for<V * Q / NB, V * (Q + 1) / NB>([&](auto vc) {
                     constexpr int v = decltype(vc)::value;
-                    if constexpr (!F6)
+                    if constexpr (PAIR)
+                        fetch_pair((t + 3) >> 1, vc);
+                    else if constexpr (!F6)
                         fetch_one(t + 4, I0(), vc);
                     else if constexpr (v < DMA_A)
                         fetch_one(3 * (t >> 2) + J + 3, I0(), vc);

@@ -146,9 +146,9 @@ def test_tile_table():
     L = q.lib()
     # full rounds of 256x256 tiles keep the big tile, run by the eight-wave
     # LDS-fetch kernel when K fits its stages
-    assert L.qgemm_select_tile(0, 30000, 21504, 5376) == 4      # 9912 tiles; INT8: the 4-wave kernel
+    assert L.qgemm_select_tile(0, 30000, 21504, 5376) == 5      # 9912 tiles: the 8-wave kernel with pair fetches
     assert L.qgemm_select_tile(0, 30000, 21504, 5408) == 0      # K bytes not whole 64-byte stages
-    assert L.qgemm_select_tile(0, 30000, 21504, 5440) == 4      # 85 stages: a partial last round
+    assert L.qgemm_select_tile(0, 30000, 21504, 5440) == 5      # 85 stages: a partial last round
     assert L.qgemm_select_tile(3, 8192, 8192, 8192) == 5        # 1024 tiles = 4 rounds
     assert L.qgemm_select_tile(2, 16384, 7168, 2048) == 5       # 1792 tiles = 7 rounds
     assert L.qgemm_select_tile(2, 16384, 7168, 2016) == 0       # K/32 = 63: scale rows not whole dwords

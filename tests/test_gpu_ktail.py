@@ -168,7 +168,7 @@ def test_small_m_kernel_k_not_multiple_of_256(name, tile, K):
 
 
 @pytest.mark.parametrize("name,shape,path,tile", [("f8_block", (16384, 7168, 2176), 4, 10),
-                                                  ("i8_qkv", (30000, 21504, 5440), 0, 4)])
+                                                  ("i8_qkv", (30000, 21504, 5440), 0, 5)])
 def test_partial_round_full_size(name, shape, path, tile):
     """Blockscale 16384 x 7168 x 2176 (17 blocks: a last round of one block)
     and INT8 30000 x 21504 x 5440 (85 stages: a last round of one stage), in
