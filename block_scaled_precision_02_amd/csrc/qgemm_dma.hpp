@@ -301,18 +301,18 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         }
     }
     // Pair fetch map: wave w's j-th A pair fetch covers rows 8*(DPA*w + j) ..
-    // +7; lane i takes row +i/8 and the logical chunk q whose slot is i%8
-    // (chunks 4..7: the pair's second stage).
-    // pa_m / pb_m: the same offsets with the second stage's chunks sent out of
-    // range, for a pair whose second stage is past K.
-    unsigned pa_off[PAIR ? DPA : 1], pb_off[PAIR ? DPB : 1], pa_m[PAIR ? DPA : 1], pb_m[PAIR ? DPB : 1];
+    // +7 (group g); lane i takes row r = 8g + i/8 and the logical chunk
+    // q = (i & 7) ^ ((r >> 1) & 7) whose slot is i%8.  Bit 2 of q (chunks 4..7:
+    // the pair's second stage) is bit 2 of i xor bit 0 of g: a pair whose
+    // second stage is past K sends those lanes out of range.
+    unsigned pa_off[PAIR ? DPA : 1], pb_off[PAIR ? DPB : 1];
+    const bool p_lb2 = (lane >> 2) & 1;
     if constexpr (PAIR) {
 #pragma unroll
         for (int j = 0; j < DPA; ++j) {
             const int r = 8 * (DPA * wave + j) + (lane >> 3);
             const int q = (lane & 7) ^ ((r >> 1) & 7);
             pa_off[j] = r < rows_a ? (unsigned)(r * p.lda + 16 * q) : OOB;
-            pa_m[j] = q < 4 ? pa_off[j] : OOB;
         }
 #pragma unroll
         for (int j = 0; j < DPB; ++j) {
@@ -329,7 +329,6 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             // one-stage map fetches whole groups)
             const bool ok = p.b_packed ? 16 * (r / 16) < rows_b : r < rows_b;
             pb_off[j] = ok ? (p.b_packed ? packed : (unsigned)(r * p.ldb + 16 * q)) : OOB;
-            pb_m[j] = q < 4 ? pb_off[j] : OOB;
         }
     }
     const unsigned pbstep = p.b_packed ? 2048u : 128u;    // B bytes per pair along K
@@ -338,12 +337,14 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         constexpr int v = decltype(vc)::value;
         const bool live = 2 * k < nst, live_hi = 2 * k + 1 < nst;   // uniform
         uint8_t *ds = &lds[(k & 1) * 2 * STAGE_BYTES];
+        const int g = v < DPA ? DPA * wave + v : DPB * wave + (v - DPA);   // fetch group (uniform)
+        const bool hi = p_lb2 != (bool)(g & 1);
         if constexpr (v < DPA) {
-            const unsigned o = (live_hi ? pa_off[v] : pa_m[v]) + (unsigned)(128 * k);
+            const unsigned o = (!live_hi && hi) ? OOB : pa_off[v] + (unsigned)(128 * k);
             dma16(make_rsrc(a_base, live ? a_range : 0u), o, ds + (DPA * wave + v) * 1024);
         } else {
             constexpr int j = v - DPA;
-            const unsigned o = (live_hi ? pb_off[j] : pb_m[j]) + pbstep * (unsigned)k;
+            const unsigned o = (!live_hi && hi) ? OOB : pb_off[j] + pbstep * (unsigned)k;
             dma16(make_rsrc(b_base, live ? b_range : 0u), o, ds + BM * 128 + (DPB * wave + j) * 1024);
         }
     };
