@@ -160,7 +160,11 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr int BSTAGE = B4 ? DSTAGE / 2 : DSTAGE;
     constexpr int BROWS_PER_FETCH = 1024 / BSTAGE;       // rows one 1 KB B fetch covers
     constexpr int STAGE_BYTES = BM * ASTAGE + BN * BSTAGE;
-    constexpr int OPND_BYTES = DNST * STAGE_BYTES;
+    // The 192x192 tile of the unscaled paths keeps six stages (three pairs,
+    // 144 KB): pair fetches with the prefetch four stages deep (see PAIR).
+    constexpr bool P6 = (PATH == PATH_I8 || PATH == PATH_F8) && WN == 2 && TM == 3 && TN == 3;
+    constexpr int NSLOT = P6 ? 6 : DNST;                   // stages resident in LDS
+    constexpr int OPND_BYTES = NSLOT * STAGE_BYTES;
     // MX scale chunks: per buffer, 256 rows of A and 256 rows of B (1x32) or
     // 64 (32x32 layout: BN/32 valid rows), 16 bytes each -- what four fetches
     // of 64 rows cover; rows past the tile read zeros and are never used.
@@ -187,7 +191,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr bool PRM = OUT == OUT_BF16 && (!SCL || BIAS);
     constexpr int NWA = SAW / WRPF, NWT = NWA + SBW / WRPF;   // fetches per refill: A rows, all
     constexpr bool WIDE = MX && BROWS == 1 && SAW % WRPF == 0 && SBW % WRPF == 0 && NWT % (G * NW) == 0 &&
-                          DNST * STAGE_BYTES + 2 * WIDE_BUF + (PRM ? PRM_BYTES : 0) <= 160 * 1024;
+                          NSLOT * STAGE_BYTES + 2 * WIDE_BUF + (PRM ? PRM_BYTES : 0) <= 160 * 1024;
     constexpr int NSCW = NWT / (G * NW);                  // per wave and round
     constexpr int SCL_BYTES = SCL ? 2 * (WIDE ? WIDE_BUF : SCL_BUF) : 0;
     constexpr int NQ = TM * TN;
@@ -211,10 +215,13 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // 4 to tile 5 with pairs, MXFP4 8192^3 0.291 -> 0.276 ms; FP8
     // 4096x2112x7168 on the four-wave 192x192 tile 0.075 -> 0.082, INT8
     // 256x256x512 on 128x128 5.4 -> 6.1 us).
-    constexpr bool PAIR = (PATH == PATH_I8 || (PATH == PATH_MX4 && BROWS == 1)) && WN == 4 && TM == 4 && TN == 2;
+    // With six slots (P6) the pairs sit in three double slots, pair k in
+    // k % 3, and pair m+3 goes out at stage 2m+1, four stages before use.
+    constexpr bool PAIR = ((PATH == PATH_I8 || (PATH == PATH_MX4 && BROWS == 1)) && WN == 4 && TM == 4 && TN == 2) || P6;
     constexpr int DPA = BM / 8 / NW, DPB = BN / 8 / NW;   // pair fetches per wave: A, B
     constexpr int NPF = PAIR ? DPA + DPB : 0;
     static_assert(!PAIR || (DPA * 8 * NW == BM && DPB * 8 * NW == BN), "pair fetches: whole 8-row groups");
+    static_assert(!P6 || !SCL, "six-slot ring: unscaled paths only (the scale rounds are four stages)");
     // scale fetches per wave per chunk: 4 waves fetch A and B scale rows,
     // 8 waves split them (waves 0-3 A, 4-7 B)
     constexpr int NSCD = SCL ? (WIDE ? NSCW : 8 / NW) : 0;
@@ -336,7 +343,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     auto fetch_pair = [&](int k, auto vc) {
         constexpr int v = decltype(vc)::value;
         const bool live = 2 * k < nst, live_hi = 2 * k + 1 < nst;   // uniform
-        uint8_t *ds = &lds[(k & 1) * 2 * STAGE_BYTES];
+        uint8_t *ds = &lds[(P6 ? k % 3 : k & 1) * 2 * STAGE_BYTES];
         const int g = v < DPA ? DPA * wave + v : DPB * wave + (v - DPA);   // fetch group (uniform)
         const bool hi = p_lb2 != (bool)(g & 1);
         if constexpr (v < DPA) {
@@ -735,9 +742,9 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // (issue order is what the wait counts: no reordering across stages)
     fetch_scales(0);
     if constexpr (PAIR) {
-        // pairs 0 and 1 (stages 0..3); wait for pair 0
+        // pairs 0 and 1 (stages 0..3; P6: pairs 0..2); wait for pair 0
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < (P6 ? 3 : 2); ++k) {
             __builtin_amdgcn_sched_barrier(0);
             static_for<0, NPF>([&](auto vc) { fetch_pair(k, vc); });
         }
@@ -754,7 +761,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     }
     __builtin_amdgcn_sched_barrier(0);
     twin_sync();
-    wait_vmcnt<PAIR ? NPF : (F6 ? 3 : 2) * NDMA + (SPLIT ? DMA_A : 0)>();
+    wait_vmcnt<PAIR ? (P6 ? 2 : 1) * NPF : (F6 ? 3 : 2) * NDMA + (SPLIT ? DMA_A : 0)>();
     lds_barrier();
     // stage 0's first fragments (one sub-step per stage: those its first
     // half of MFMAs uses; its region A reads the rest)
@@ -779,8 +786,8 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     //  (its last reads were before the barrier); read stage t+1's first
     //  fragments and its scale chunk; multiply the rest of stage t.
     auto stage = [&](int t, auto jc) {
-        constexpr int J = decltype(jc)::value;
-        constexpr int JN = (J + 1) & 3;
+        constexpr int J = decltype(jc)::value;             // t % 4 (P6: t % 6, the slot)
+        constexpr int JN = P6 ? (J + 1) % 6 : (J + 1) & 3;
         constexpr int SET0 = (NSUB == 1) ? (J & 1) : 0;    // register set of sub-step 0
         constexpr int SETN = (NSUB == 1) ? ((J + 1) & 1) : 0;
         constexpr int NIT = TM + TN;                       // fragments per sub-step
@@ -795,7 +802,8 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         // row's last byte in a half-live line: they are not multiplied.  The
         // other paths multiply zeros there.  (K % 128 == 0: the stage count
         // is even, so the first two stages of a round are always live.)
-        const bool mul = !F6 || J < 2 || t < nst;
+        // (P6: the loop runs in steps of six stages; those past K are skipped.)
+        const bool mul = F6 ? (J < 2 || t < nst) : P6 ? t < nst : true;
         // ---- region A
         {
             constexpr int NA = (NSUB == 2) ? NQ : NQ / 2;
@@ -843,7 +851,10 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         // Pairs (issued in region B of odd stages: pair (t+3)/2 at stage t):
         // stage t+1 of an even t is the second half of a pair followed by one
         // more pair; of an odd t, the first half of the last pair issued.
-        constexpr int AFTER = PAIR ? ((J & 1) ? 0 : NPF) + ((J == 0 || J == 1) ? NSCD : 0)
+        // P6: stage t+1 is followed by two more pairs at an even t, one at an
+        // odd t.
+        constexpr int AFTER = P6 ? ((J & 1) ? 1 : 2) * NPF
+                            : PAIR ? ((J & 1) ? 0 : NPF) + ((J == 0 || J == 1) ? NSCD : 0)
                             : F6   ? (J == 1 ? 1 : 2) * NDMA + (J == 3 ? 0 : NSCD)
                                    : 2 * NDMA + ((J == 0 || J == 1) ? NSCD : 0);
         twin_sync();
@@ -877,7 +888,9 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
                     fold(std::integral_constant<int, QB + Q - 1>());
                 static_for<V * Q / NB, V * (Q + 1) / NB>([&](auto vc) {
                     constexpr int v = decltype(vc)::value;
-                    if constexpr (PAIR)
+                    if constexpr (P6)
+                        fetch_pair((t + 5) >> 1, vc);
+                    else if constexpr (PAIR)
                         fetch_pair((t + 3) >> 1, vc);
                     else if constexpr (!F6)
                         fetch_one(t + 4, I0(), vc);
@@ -906,11 +919,16 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // 0).  Fetches run three stages (FP6: two to three lines) ahead, into
     // stages past K that are never multiplied or, in a partial last round,
     // multiplied as zeros (FP6: skipped).
-    for (int t = 0; t < nst; t += 4) {
-        stage(t, I0());
-        stage(t + 1, I1());
-        stage(t + 2, std::integral_constant<int, 2>());
-        stage(t + 3, std::integral_constant<int, 3>());
+    if constexpr (P6) {
+        for (int t = 0; t < nst; t += 6)
+            static_for<0, 6>([&](auto jc) { stage(t + decltype(jc)::value, jc); });
+    } else {
+        for (int t = 0; t < nst; t += 4) {
+            stage(t, I0());
+            stage(t + 1, I1());
+            stage(t + 2, std::integral_constant<int, 2>());
+            stage(t + 3, std::integral_constant<int, 3>());
+        }
     }
     wait_vmcnt<0>();   // nothing may still be landing in LDS once it holds the output
 
