@@ -77,6 +77,7 @@ struct Params {
     int group_m;                   // tile rows per group in the launch order
     int b_packed;                  // B in the prepacked layout (LDS-fetch and small-M kernels only):
                                    // 16-row groups of kbytes/64 blocks of 1 KB, B = the group of row 0
+    int c_cached;                  // full tiles store C through the caches (else non-temporal)
 };
 
 constexpr int KSTEP_BYTES = 128;
@@ -405,7 +406,11 @@ __device__ __forceinline__ void store_tile(const Params &p, Acc (&acc)[TM][TN], 
                         const i32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1],
                                          acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
                         if constexpr (FULL) {
-                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rc, off, 0, CPOL_NT);
+                            if (p.c_cached)
+                                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rc, off, 0, 0);
+                            else
+                                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rc, off, 0,
+                                                                       CPOL_NT);
                         } else {
 #pragma unroll
                             for (int r = 0; r < 4; ++r)
@@ -467,7 +472,10 @@ __device__ __forceinline__ void store_tile(const Params &p, Acc (&acc)[TM][TN], 
                 const int srow = it * RPI + lane / LPR;
                 const u32x4 v = *(const u32x4 *)(stash + srow * SPITCH + ((c ^ (srow & (PCHK - 1))) << 4));
                 const unsigned off = c < SCHK ? gbase + (unsigned)(srow * p.ldc * 2) : OOB;
-                __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, CPOL_NT);
+                if (p.c_cached)
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, CPOL_NT);
             }
         }
     }
