@@ -384,8 +384,8 @@ def qgemm_mx(fmt, A, B, scale_a, scale_b, b_layout, bias=None, out=None, stream=
 
 def qgemm_mx_mixed(fmt_a, fmt_b, A, B, scale_a, scale_b, b_layout, bias=None, out=None, stream=None):
     """MX GEMM with a format per operand -> bf16 [M, N] (e4m3 A with e2m1 B,
-    or equal formats).  A [M, K] (e4m3) or [M, K/2] (e2m1) bytes, B likewise;
-    scales as for qgemm_mx."""
+    e2m1 A with e4m3 B, or equal formats).  A [M, K] (e4m3) or [M, K/2]
+    (e2m1) bytes, B likewise; scales as for qgemm_mx."""
     torch = _torch()
 
     def dts(fmt):

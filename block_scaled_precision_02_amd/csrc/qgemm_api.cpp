@@ -390,6 +390,16 @@ int pick_tile_mx84(Shape s)
     return select_tile_impl(2, s.M, s.N) == 0 ? DMA_TILE : DMA128_TILE;
 }
 
+// Mixed MX the other way round (e2m1 A, e4m3 B): the LDS-fetch kernel only,
+// 256x256 (tile 4, or 5 when forced) where the 256x256 grid fills the chip,
+// else 128x128 (tile 7), small M included (no small-M form).
+int pick_tile_mx48(Shape s)
+{
+    if (g_forced_tile == DMA_TILE || g_forced_tile == DMA8_TILE || g_forced_tile == DMA128_TILE)
+        return g_forced_tile;
+    return select_tile_impl(2, s.M, s.N) == 0 ? DMA_TILE : DMA128_TILE;
+}
+
 // 6-bit MX: the four-wave 256x256 tile where the 256x256 grid fills the
 // chip, else 128x128 (the only two FP6 tiles built).
 int pick_tile_mx6(Shape s)
@@ -431,8 +441,15 @@ const char *qgemm_last_error(void) { return g_last_error.c_str(); }
 
 int qgemm_select_tile(int path, int64_t M, int64_t N, int64_t K)
 {
-    if (path < 0 || path > 7)
+    if (path < 0 || path > 8)
         return -1;
+    if (path == 8) {   // MX e2m1 A x e4m3 B
+        const int prev = g_forced_tile;
+        g_forced_tile = -1;
+        const int t = pick_tile_mx48(Shape{M, N, K});
+        g_forced_tile = prev;
+        return t;
+    }
     if (path == 6 || path == 7) {   // MX e2m3 / e3m2
         const int prev = g_forced_tile;
         g_forced_tile = -1;
@@ -710,35 +727,46 @@ static qgemm_status mx_mixed_common(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, cons
         return mx_common(fmt_a, A, lda_bytes, B, ldb_bytes, scale_a, scale_b, b_layout, bias, C, ldc, M, N, K, stream,
                          false);
     }
-    if (fmt_a != QGEMM_MX_E4M3)
-        return fail(QGEMM_ERR_BAD_FORMAT, "e2m1 A with e4m3 B is not supported (e4m3 A with e2m1 B is)");
+    const bool a4 = fmt_a == QGEMM_MX_E2M1;   // e2m1 A with e4m3 B
+    if (a4 && packed)
+        return fail(QGEMM_ERR_BAD_FORMAT, "e2m1 A with e4m3 B: prepacked B is not supported (use qgemm_mx_mixed)");
     if (b_layout != QGEMM_MX_BSCALE_1x32 && b_layout != QGEMM_MX_BSCALE_32x32)
         return fail(QGEMM_ERR_BAD_FORMAT, "unknown B-scale layout %d", (int)b_layout);
+    const char *pair = a4 ? "e2m1 x e4m3" : "e4m3 x e2m1";
     const Shape s{M, N, K};
     TRY(check_shape(s, false));
     if (!dma_k_ok(5, K) || (packed && K % 256))
-        return fail(QGEMM_ERR_BAD_SHAPE, "K=%lld: e4m3 x e2m1 needs K a multiple of %d", (long long)K,
+        return fail(QGEMM_ERR_BAD_SHAPE, "K=%lld: %s needs K a multiple of %d", (long long)K, pair,
                     packed ? 256 : 128);
     if (M == 0 || N == 0)
         return QGEMM_OK;
-    TRY(check_operand("A", A, lda_bytes, K));
+    TRY(check_operand("A", A, lda_bytes, a4 ? K / 2 : K));
     if (packed) {
         if (!B)
             return fail(QGEMM_ERR_NULL_POINTER, "Bp is NULL");
         if (!aligned(B, 16))
             return fail(QGEMM_ERR_BAD_LAYOUT, "Bp is not 16-byte aligned");
     } else {
-        TRY(check_operand("B", B, ldb_bytes, K / 2));
+        TRY(check_operand("B", B, ldb_bytes, a4 ? K : K / 2));
     }
     if (!scale_a)
         return fail(QGEMM_ERR_NULL_POINTER, "scale_a is NULL");
     if (!scale_b)
         return fail(QGEMM_ERR_NULL_POINTER, "scale_b is NULL");
     if (!aligned(scale_a, 8) || !aligned(scale_b, 8))
-        return fail(QGEMM_ERR_BAD_LAYOUT, "e4m3 x e2m1 scale arrays must be 8-byte aligned");
+        return fail(QGEMM_ERR_BAD_LAYOUT, "%s scale arrays must be 8-byte aligned", pair);
     TRY(check_bias(bias));
     TRY(check_output(C, ldc, N, 2));
     TRY(check_device());
+    if (a4) {
+        const int tile = pick_tile_mx48(s);
+        Params p = base_params(A, lda_bytes, B, ldb_bytes, C, ldc, s, K, tile);   // kbytes: B's row
+        TRY(check_grid(p));
+        p.mx_sa = scale_a;
+        p.mx_sb = scale_b;
+        p.bias = bias;
+        return launch([&] { return launch_mx48(tile, bias != nullptr, (int)b_layout, p, (hipStream_t)stream); });
+    }
     int tile = pick_tile_mx84(s);
     if (packed && is_skinny_tile(tile))   // the small-M kernel reads the row-major B only
         tile = DMA128_TILE;

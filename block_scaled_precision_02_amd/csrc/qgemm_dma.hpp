@@ -92,6 +92,7 @@ template <> struct DmaTraits<PATH_MX8> { static constexpr int NSUB = 1; };  // c
 template <> struct DmaTraits<PATH_MX4> { static constexpr int NSUB = 2; };  // chunk 2h+S
 template <> struct DmaTraits<PATH_F8B> { static constexpr int NSUB = 1; };  // chunks h, 2+h
 template <> struct DmaTraits<PATH_MX84> { static constexpr int NSUB = 1; }; // A chunks h, 2+h; B chunk h of 32 B
+template <> struct DmaTraits<PATH_MX48> { static constexpr int NSUB = 1; }; // A chunk h of 32 B; B chunks h, 2+h
 template <> struct DmaTraits<PATH_MX6> { static constexpr int NSUB = 1; };  // 24 bytes at 24h of a 48-byte row
 template <> struct DmaTraits<PATH_MX6E3> { static constexpr int NSUB = 1; };
 
@@ -149,15 +150,17 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     constexpr int NSUB = DmaTraits<PATH>::NSUB;
     constexpr bool F6 = (PATH == PATH_MX6 || PATH == PATH_MX6E3);   // 6-bit operands: 48-byte stages in 64-byte lines
-    constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4 || PATH == PATH_MX84 || F6);
+    constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4 || PATH == PATH_MX84 || PATH == PATH_MX48 || F6);
     constexpr bool B4 = (PATH == PATH_MX84);              // e2m1 B under e4m3 A: 32-byte B stage rows
+    constexpr bool A4 = (PATH == PATH_MX48);              // e2m1 A under e4m3 B: 32-byte A stage rows
     constexpr bool BS = (PATH == PATH_F8B);               // blockscale FP8
     constexpr bool SCL = MX || BS;                        // scale chunks staged through LDS
     static_assert(!BS || BROWS == 128, "blockscale B scales cover 128 rows");
     static_assert(BROWS == 1 || (BN % BROWS == 0 || BROWS == 32), "B scale rows must align with the tile");
     // bytes per row of one ring slot (FP6: a line, 64 bytes as for 8 bits)
-    constexpr int ASTAGE = DSTAGE;
+    constexpr int ASTAGE = A4 ? DSTAGE / 2 : DSTAGE;
     constexpr int BSTAGE = B4 ? DSTAGE / 2 : DSTAGE;
+    constexpr int AROWS_PER_FETCH = 1024 / ASTAGE;       // rows one 1 KB A fetch covers
     constexpr int BROWS_PER_FETCH = 1024 / BSTAGE;       // rows one 1 KB B fetch covers
     constexpr int STAGE_BYTES = BM * ASTAGE + BN * BSTAGE;
     // The 192x192 tile of the unscaled paths keeps six stages (three pairs,
@@ -195,10 +198,11 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr int NSCW = NWT / (G * NW);                  // per wave and round
     constexpr int SCL_BYTES = SCL ? 2 * (WIDE ? WIDE_BUF : SCL_BUF) : 0;
     constexpr int NQ = TM * TN;
-    constexpr int RPF = (PATH == PATH_F8 || PATH == PATH_MX8 || PATH == PATH_F8B || PATH == PATH_MX84) ? 2 : 1;
-    constexpr int RPF_B = B4 ? 1 : RPF;
-    constexpr int NDSR = TM * RPF + TN * RPF_B;           // fragment reads per sub-step
-    constexpr int DMA_A = BM / 16 / NW, DMA_B = BN / BROWS_PER_FETCH / NW; // fetches per wave per stage
+    constexpr int RPF = (PATH == PATH_F8 || PATH == PATH_MX8 || PATH == PATH_F8B || PATH == PATH_MX84 ||
+                         PATH == PATH_MX48) ? 2 : 1;
+    constexpr int RPF_A = A4 ? 1 : RPF, RPF_B = B4 ? 1 : RPF;
+    constexpr int NDSR = TM * RPF_A + TN * RPF_B;         // fragment reads per sub-step
+    constexpr int DMA_A = BM / AROWS_PER_FETCH / NW, DMA_B = BN / BROWS_PER_FETCH / NW; // fetches per wave per stage
     constexpr int NDMA = DMA_A + DMA_B;                   // fetches per wave per stage (FP6: per line)
     // Pair fetches (the eight-wave 256x256 tile of INT8, and of e2m1 with
     // 1x32 B scales -- with 32x32 ones it would spill): one
@@ -229,7 +233,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // (region B of the stage 4 back) except for MX, whose region B is busy
     // with scale reads.
     constexpr bool SPLIT = !SCL;
-    static_assert((DMA_A * 16 * NW == BM && DMA_B * BROWS_PER_FETCH * NW == BN),
+    static_assert((DMA_A * AROWS_PER_FETCH * NW == BM && DMA_B * BROWS_PER_FETCH * NW == BN),
                   "tile rows must be a whole number of fetches per wave");
     static_assert(BM <= SA_ROWS && (BROWS == 1 ? BN <= SB_ROWS : BN / 32 <= SB_ROWS), "scale rows per buffer");
     using Frag = typename PathTraits<PATH>::Frag;
@@ -239,7 +243,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // scale buffers; the mixed path's smaller B stages leave less than the
     // 256x256 stash needs, so its block is sized up to that
     constexpr int STASH_NEED = NW * TM * 32 * pow2_at_least(TN * 32 * 2 / 16) * 16;
-    constexpr int BODY = (B4 || F6) ? (OPND_BYTES + SCL_BYTES > STASH_NEED ? OPND_BYTES + SCL_BYTES : STASH_NEED)
+    constexpr int BODY = (B4 || A4 || F6) ? (OPND_BYTES + SCL_BYTES > STASH_NEED ? OPND_BYTES + SCL_BYTES : STASH_NEED)
                                     : OPND_BYTES + SCL_BYTES;
     constexpr int PRM_OFF = BODY;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[BODY + (PRM ? PRM_BYTES : 0)];
@@ -263,7 +267,8 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     const int nst = F6 ? p.K / 64 : p.kbytes / DSTAGE;
     const int nfetch = F6 ? (p.kbytes + DSTAGE - 1) / DSTAGE : nst;
     const uint8_t *const a_base = p.A + (int64_t)m0 * p.lda;
-    const uint32_t a_range = (uint32_t)((rows_a - 1) * p.lda + p.kbytes);
+    const int kbytes_a = A4 ? p.kbytes / 2 : p.kbytes;   // (p.kbytes: the e4m3 operand's row)
+    const uint32_t a_range = (uint32_t)((rows_a - 1) * p.lda + kbytes_a);
     // B row-major, or prepacked: 16-row groups of 1 KB blocks (32-row groups
     // for the mixed path's 32-byte B rows), block t of a group holding its
     // rows' K piece t already in this kernel's LDS order, so that a fetch
@@ -283,9 +288,17 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     unsigned a_off[DMA_A], b_off[DMA_B];
 #pragma unroll
     for (int j = 0; j < DMA_A; ++j) {
-        const int r = 16 * (DMA_A * wave + j) + (lane >> 2);
-        const int c = (lane & 3) ^ ((r >> 2) & 3);
-        a_off[j] = r < rows_a ? (unsigned)(r * p.lda + 16 * c) : OOB;
+        if constexpr (A4) {
+            // 32 rows of 32 bytes (as the mixed path's B): lane i takes row
+            // i/2, the chunk of slot i%2
+            const int r4 = AROWS_PER_FETCH * (DMA_A * wave + j) + (lane >> 1);
+            const int c4 = (lane & 1) ^ ((r4 >> 3) & 1);
+            a_off[j] = r4 < rows_a ? (unsigned)(r4 * p.lda + 16 * c4) : OOB;
+        } else {
+            const int r = 16 * (DMA_A * wave + j) + (lane >> 2);
+            const int c = (lane & 3) ^ ((r >> 2) & 3);
+            a_off[j] = r < rows_a ? (unsigned)(r * p.lda + 16 * c) : OOB;
+        }
     }
 #pragma unroll
     for (int j = 0; j < DMA_B; ++j) {
@@ -358,19 +371,19 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // Stage (FP6: line) t goes to slot t % 4, its A rows (part 0) and B rows
     // (part 1) fetched separately.
     auto fetch_part = [&](int t, auto partc) {
-        const unsigned kb = (unsigned)(t * DSTAGE), kbb = (unsigned)t * bstep;
+        const unsigned kb = (unsigned)(t * ASTAGE), kbb = (unsigned)t * bstep;
         const bool live = t < nfetch;
         uint8_t *slot = &lds[(t & 3) * STAGE_BYTES];
         if constexpr (decltype(partc)::value == 0) {
             const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base, live ? a_range : 0u);
 #pragma unroll
             for (int j = 0; j < DMA_A; ++j)
-                dma16(ra, a_off[j] + kb, slot + (DMA_A * wave + j) * 16 * DSTAGE);
+                dma16(ra, a_off[j] + kb, slot + (DMA_A * wave + j) * 1024);
         } else {
             const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base, live ? b_range : 0u);
 #pragma unroll
             for (int j = 0; j < DMA_B; ++j)
-                dma16(rb, b_off[j] + kbb, slot + BM * DSTAGE + (DMA_B * wave + j) * 1024);
+                dma16(rb, b_off[j] + kbb, slot + BM * ASTAGE + (DMA_B * wave + j) * 1024);
         }
     };
 
@@ -382,10 +395,10 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         uint8_t *slot = &lds[(t & 3) * STAGE_BYTES];
         if constexpr (decltype(partc)::value == 0) {
             const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base, live ? a_range : 0u);
-            dma16(ra, a_off[j] + (unsigned)(t * DSTAGE), slot + (DMA_A * wave + j) * 16 * DSTAGE);
+            dma16(ra, a_off[j] + (unsigned)(t * ASTAGE), slot + (DMA_A * wave + j) * 1024);
         } else {
             const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base, live ? b_range : 0u);
-            dma16(rb, b_off[j] + (unsigned)t * bstep, slot + BM * DSTAGE + (DMA_B * wave + j) * 1024);
+            dma16(rb, b_off[j] + (unsigned)t * bstep, slot + BM * ASTAGE + (DMA_B * wave + j) * 1024);
         }
     };
 
@@ -555,14 +568,20 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             else
                 fa[SET][k - TN] = f6_frag(slotc, s, P0(), (unsigned)(wm * TM * 32), std::integral_constant<int, k - TN>());
         } else if constexpr (k == 0) {
-            fa[SET][0] = dma_frag<PATH, S, HALF>(ta, arow, h);
+            if constexpr (A4)
+                fa[SET][0] = dma_frag_b32(ta, arow, h);
+            else
+                fa[SET][0] = dma_frag<PATH, S, HALF>(ta, arow, h);
         } else if constexpr (k <= TN) {
             if constexpr (B4)
                 fb[SET][k - 1] = dma_frag_b32(tb, brow + 32 * (k - 1), h);
             else
                 fb[SET][k - 1] = dma_frag<PATH, S, HALF>(tb, brow + 32 * (k - 1), h);
         } else {
-            fa[SET][k - TN] = dma_frag<PATH, S, HALF>(ta, arow + 32 * (k - TN), h);
+            if constexpr (A4)
+                fa[SET][k - TN] = dma_frag_b32(ta, arow + 32 * (k - TN), h);
+            else
+                fa[SET][k - TN] = dma_frag<PATH, S, HALF>(ta, arow + 32 * (k - TN), h);
         }
     };
 
@@ -932,7 +951,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     }
     wait_vmcnt<0>();   // nothing may still be landing in LDS once it holds the output
 
-    store_tile<PATH, WM, WN, TM, TN, BIAS, OUT, ((B4 || F6) ? BODY : OPND_BYTES), PRM>(p, acc, &lds[0], &lds[PRM_OFF], m0, n0,
+    store_tile<PATH, WM, WN, TM, TN, BIAS, OUT, ((B4 || A4 || F6) ? BODY : OPND_BYTES), PRM>(p, acc, &lds[0], &lds[PRM_OFF], m0, n0,
                                                                             rows_a, rows_b);
 }
 

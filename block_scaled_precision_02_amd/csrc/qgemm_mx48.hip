@@ -1,0 +1,34 @@
+// Mixed MX variants with the formats the other way round: e2m1 A with e4m3 B,
+// ue8m0 scales per 32 K elements on both (v_mfma_scale_f32_32x32x64_f8f6f4
+// with an FP8 first operand and an FP4 second), run by the LDS-fetch kernel
+// only: tiles 4, 5 and 7 (the 192x192 tile's A rows are not a whole number of
+// 32-row fetches per wave); small M takes tile 7.
+#include "qgemm_launch.hpp"
+
+namespace qgemm {
+template <bool BIAS, int BROWS>
+static hipError_t mx48_tile(int tile, const Params &p, hipStream_t s)
+{
+    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(tile_threads(tile));
+    switch (tile) {
+    case DMA_TILE:
+        hipLaunchKernelGGL((qgemm_dma_kernel<PATH_MX48, 2, 4, 4, BIAS, BROWS, OUT_BF16>), grid, block, 0, s, p);
+        break;
+    case DMA8_TILE:
+        hipLaunchKernelGGL((qgemm_dma_kernel<PATH_MX48, 4, 4, 2, BIAS, BROWS, OUT_BF16>), grid, block, 0, s, p);
+        break;
+    case DMA128_TILE:
+        hipLaunchKernelGGL((qgemm_dma_kernel<PATH_MX48, 2, 2, 2, BIAS, BROWS, OUT_BF16>), grid, block, 0, s, p);
+        break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_mx48(int tile, bool bias, int brows, const Params &p, hipStream_t s)
+{
+    if (brows == 1)
+        return bias ? mx48_tile<true, 1>(tile, p, s) : mx48_tile<false, 1>(tile, p, s);
+    return bias ? mx48_tile<true, 32>(tile, p, s) : mx48_tile<false, 32>(tile, p, s);
+}
+}  // namespace qgemm

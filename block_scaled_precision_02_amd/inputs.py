@@ -26,6 +26,8 @@ rotating input set):
   mx_a8w4    MX with e4m3 A (activations) and e2m1 B (weights), M=N=K=8192
              (seed 107): A as mxfp8's A, B as mxfp4's B, 1x32 scales on both
              ([M,K/32], [N,K/32]); no bias.
+  mx_a4w8    the same pairing the other way round (seed 110): e2m1 A as
+             mxfp4's A, e4m3 B as mxfp8's with 1x32 scales.
   mxfp6      MX e2m3 (OCP FP6) M=N=K=8192 (seed 108): as mxfp4 with the
              6-bit E2M3 element (emax 2: X = floor(log2(amax)) - 2), four
              codes per three bytes (element k in bits 6k..6k+5 of the row,
@@ -56,6 +58,7 @@ WORKLOADS = {
     "i8_qkv": ("i8", 30000, 21504, 5376, 105, True, None, None),
     "f8_block": ("f8b", 16384, 7168, 2048, 106, False, None, 128),
     "mx_a8w4": ("mx", 8192, 8192, 8192, 107, False, "e4m3/e2m1", 1),
+    "mx_a4w8": ("mx", 8192, 8192, 8192, 110, False, "e2m1/e4m3", 1),
     "mxfp6": ("mx", 8192, 8192, 8192, 108, False, "e2m3", 1),
     "mxfp6_e3m2": ("mx", 8192, 8192, 8192, 109, False, "e3m2", 1),
 }

@@ -26,8 +26,8 @@
  *                      ROCm/FlyDSL PR #990 "[fp4_gemm_4wave] MXFP4 GEMM perf
  *                      optimize").
  *   qgemm_mx_mixed     MX with e4m3 A (activations) and e2m1 B (weights),
- *                      each operand under its own format and the same
- *                      ue8m0 per-32 scale rule.
+ *                      or e2m1 A with e4m3 B, each operand under its own
+ *                      format and the same ue8m0 per-32 scale rule.
  *
  * Prepacked variants of each GEMM take a B already laid out in the order the
  * kernels' LDS stages use (qgemm_prepack_b, qgemm_prepack_b32).
@@ -175,14 +175,17 @@ qgemm_status qgemm_mx(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const 
 
 /* MX GEMM with a format per operand: fmt_a for A, fmt_b for B, otherwise as
  * qgemm_mx (one ue8m0 scale per 32 elements along K for each operand, the
- * scale layouts of qgemm_mx).  Equal formats are qgemm_mx.  Of the mixed
- * pairs, e4m3 A (activations) with e2m1 B (weights) is supported:
- *   A        [M, K] e4m3fn codes, row stride lda_bytes (>= K)
- *   B        [N, K] e2m1, two per byte (even k in the low nibble), row stride
+ * scale layouts of qgemm_mx).  Equal formats are qgemm_mx.  Both mixed pairs
+ * of e4m3 and e2m1 are supported:
+ *   e4m3 A (activations), e2m1 B (weights):
+ *     A      [M, K] e4m3fn codes, row stride lda_bytes (>= K)
+ *     B      [N, K] e2m1, two per byte (even k in the low nibble), row stride
  *            ldb_bytes (>= K/2)
- * It needs K a multiple of 128 (QGEMM_ERR_BAD_SHAPE) and 8-byte aligned
- * scale arrays (QGEMM_ERR_BAD_LAYOUT); e2m1 A with e4m3 B returns
- * QGEMM_ERR_BAD_FORMAT.  Numerics as qgemm_mx. */
+ *   e2m1 A, e4m3 B: the same with the operands' formats swapped (lda_bytes
+ *            >= K/2, ldb_bytes >= K); every M runs an LDS-fetch tile (4, 5
+ *            or 7; no small-M form).
+ * Either needs K a multiple of 128 (QGEMM_ERR_BAD_SHAPE) and 8-byte aligned
+ * scale arrays (QGEMM_ERR_BAD_LAYOUT).  Numerics as qgemm_mx. */
 qgemm_status qgemm_mx_mixed(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *A, int64_t lda_bytes,
                             const void *B, int64_t ldb_bytes, const uint8_t *scale_a, const uint8_t *scale_b,
                             qgemm_mx_bscale b_layout, const uint16_t *bias, uint16_t *C, int64_t ldc,
@@ -197,8 +200,8 @@ qgemm_status qgemm_mx_mixed(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *
  * slot p being row 32R + p/2, chunk (p mod 2) XOR ((p/16) mod 2); rows past N
  * are zeros -- the order the mixed GEMM's B stages take in LDS.
  * qgemm_prepacked_b32_bytes returns -1 for a bad size.  qgemm_mx_mixed_prepacked
- * is qgemm_mx_mixed (e4m3 A with e2m1 B only; equal formats return
- * QGEMM_ERR_BAD_FORMAT) with Bp in place of (B, ldb) and K a multiple of 256
+ * is qgemm_mx_mixed (e4m3 A with e2m1 B only; equal formats and e2m1 A
+ * return QGEMM_ERR_BAD_FORMAT) with Bp in place of (B, ldb) and K a multiple of 256
  * (the packer's rows); results equal qgemm_mx_mixed's on the same tile;
  * M <= 16 runs the 128x128 tile. */
 int64_t qgemm_prepacked_b32_bytes(int64_t N, int64_t row_bytes);
@@ -328,7 +331,8 @@ const char *qgemm_status_string(qgemm_status status);
  * tile 10 when its grid of 256x128 tiles fills the 256 CUs at least once,
  * else tile 7), 5 MX e4m3 A with e2m1 B (tile 8 for M <= 16, else tile 4
  * where the table picks 256x256, else 7), 6 / 7 MX with 6-bit E2M3 / E3M2
- * elements (tile 4 where the table picks 256x256, else 7; no small-M tile).
+ * elements (tile 4 where the table picks 256x256, else 7; no small-M tile),
+ * 8 MX e2m1 A with e4m3 B (as 6 / 7).
  * Returns the tile id, or -1 for a bad path:
  *   0: 256x256, 4 waves, operands staged through registers
  *   1: 128x128    2: 256x256 with 8 waves, staged through registers
@@ -343,8 +347,8 @@ const char *qgemm_status_string(qgemm_status status);
  * Tiles 4-7 need K bytes a multiple of 64 (whole stages; a last round of
  * fewer than four is masked) and MX scale rows of whole dwords (K % 128),
  * with scale arrays aligned to 16 (e2m1) or 8 (e4m3) bytes; where these
- * hold, the table's 256x256 choice runs as tile 4 (INT8, mixed and 6-bit MX)
- * or 5 (the others), 192x192 as tile 6 and 128x128 as tile 7.  Calls with M <= 64 take tile 8
+ * hold, the table's 256x256 choice runs as tile 4 (mixed and 6-bit MX, and
+ * INT8 on a prepacked B) or 5 (the others), 192x192 as tile 6 and 128x128 as tile 7.  Calls with M <= 64 take tile 8
  * (M <= 16) or 9 (INT8 and FP8 only: MX takes the small-M kernel up to
  * M = 16). */
 int qgemm_select_tile(int path, int64_t M, int64_t N, int64_t K);

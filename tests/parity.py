@@ -145,7 +145,7 @@ def path_of(d):
     if d["kind"] in PATH_OF:
         return PATH_OF[d["kind"]]
     if "/" in (d["fmt"] or ""):
-        return 5
+        return 5 if d["fmt"] == "e4m3/e2m1" else 8
     return {"e4m3": 2, "e2m1": 3, "e2m3": 6, "e3m2": 7}[d["fmt"]]
 
 

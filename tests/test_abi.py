@@ -159,7 +159,7 @@ def test_tile_table():
     # round (LDS-fetch form when K fits, register-staged otherwise)
     assert L.qgemm_select_tile(1, 4096, 2112, 7168) == 6
     assert L.qgemm_select_tile(1, 4096, 2112, 7200) == 3
-    assert L.qgemm_select_tile(8, 64, 64, 64) == -1
+    assert L.qgemm_select_tile(9, 64, 64, 64) == -1
     # e4m3 MX with K % 128 == 64: the scale rows are whole dwords but a round's
     # last scale word would cover one stage of data and one past K, which the
     # masked round cannot split -- the register-staged tile (one rule for every
@@ -344,7 +344,9 @@ def mx2(fa=0, fb=1, A=FAKE, lda=512, B=FAKE2, ldb=256, sa=FAKE3, sb=FAKE3, layou
 @pytest.mark.parametrize("kw,status", [
     (dict(fa=2), q.QGEMM_ERR_BAD_FORMAT),
     (dict(fb=7), q.QGEMM_ERR_BAD_FORMAT),
-    (dict(fa=1, fb=0), q.QGEMM_ERR_BAD_FORMAT),                 # e2m1 A with e4m3 B
+    (dict(fa=1, fb=0), q.QGEMM_ERR_BAD_LAYOUT),                 # e2m1 A x e4m3 B: B row is K = 512 bytes
+    (dict(fa=1, fb=0, lda=128, ldb=512), q.QGEMM_ERR_BAD_LAYOUT),  # ... and A row K/2 = 256
+    (dict(fa=1, fb=0, lda=256, ldb=512, K=576), q.QGEMM_ERR_BAD_SHAPE),
     (dict(layout=16), q.QGEMM_ERR_BAD_FORMAT),
     (dict(K=576, lda=576, ldb=288), q.QGEMM_ERR_BAD_SHAPE),      # K % 128
     (dict(A=None), q.QGEMM_ERR_NULL_POINTER),
@@ -364,6 +366,13 @@ def test_mx_mixed_checks_pass_before_the_device_check(monkeypatch):
     assert q.select_tile(5, 8192, 8192, 8192) == 4
     assert q.select_tile(5, 16, 8192, 8192) == 8           # small M: the small-M kernel
     assert q.select_tile(5, 17, 8192, 8192) == 7           # the table: 64 tiles of 128 beat 32 of 256
+    # e2m1 A x e4m3 B: the LDS-fetch kernel at every M (no small-M form)
+    assert mx2(fa=1, fb=0, lda=256, ldb=512) == q.QGEMM_ERR_UNSUPPORTED_DEVICE
+    assert mx2(fa=1, fb=0, lda=256, ldb=512, N=0) == q.QGEMM_OK
+    assert q.select_tile(8, 8192, 8192, 8192) == 4
+    assert q.select_tile(8, 16, 8192, 8192) == 7
+    assert q.select_tile(8, 17, 8192, 8192) == 7
+    assert q.select_tile(9, 64, 64, 64) == -1
 
 
 def test_blockscale_prepacked_rejects_and_passes(monkeypatch):
@@ -397,6 +406,7 @@ def test_prepacked_b32_sizes_and_rejects(monkeypatch):
     assert L.qgemm_prepack_b32(FAKE, 128, 33, 128, None, None) == q.QGEMM_ERR_NULL_POINTER
     m = L.qgemm_mx_mixed_prepacked
     assert m(0, 0, FAKE, 512, FAKE2, FAKE3, FAKE3, 1, None, FAKE, 64, 64, 64, 512, None) == q.QGEMM_ERR_BAD_FORMAT
+    assert m(1, 0, FAKE, 256, FAKE2, FAKE3, FAKE3, 1, None, FAKE, 64, 64, 64, 512, None) == q.QGEMM_ERR_BAD_FORMAT
     assert m(0, 1, FAKE, 512, None, FAKE3, FAKE3, 1, None, FAKE, 64, 64, 64, 512, None) == q.QGEMM_ERR_NULL_POINTER
     assert m(0, 1, FAKE, 512, FAKE2 + 8, FAKE3, FAKE3, 1, None, FAKE, 64, 64, 64, 512, None) == q.QGEMM_ERR_BAD_LAYOUT
     monkeypatch.setenv("QGEMM_FAKE_ARCH", "gfx1201")
@@ -439,6 +449,8 @@ def test_injected_launch_error_leaves_everything_untouched(monkeypatch):
                                   None),
         "mixed": lambda: L.qgemm_mx_mixed(0, 1, P(a), K, P(b), K // 2, P(s32), P(s32b), 1, None, P(c), N, M, N, K,
                                           None),
+        "mixed_a4": lambda: L.qgemm_mx_mixed(1, 0, P(a), K // 2, P(b), K, P(s32), P(s32b), 32, None, P(c), N, M, N,
+                                             K, None),
     }
     for name, call in calls.items():
         assert call() == q.QGEMM_ERR_HIP, name

@@ -70,7 +70,8 @@ def _run(d, At, Bt):
     if d["kind"] == "f8b":
         return q.qgemm_f8_blockscale(At, Bt, sa, sb, bias)
     if "/" in d["fmt"]:
-        return q.qgemm_mx_mixed(q.QGEMM_MX_E4M3, q.QGEMM_MX_E2M1, At, Bt, sa, sb, d["b_rows_per_scale"], bias)
+        fa, fb = (q.QGEMM_MX_E4M3 if f == "e4m3" else q.QGEMM_MX_E2M1 for f in d["fmt"].split("/"))
+        return q.qgemm_mx_mixed(fa, fb, At, Bt, sa, sb, d["b_rows_per_scale"], bias)
     fmt = q.QGEMM_MX_E4M3 if d["fmt"] == "e4m3" else q.QGEMM_MX_E2M1
     return q.qgemm_mx(fmt, At, Bt, sa, sb, d["b_rows_per_scale"], bias)
 
@@ -144,6 +145,12 @@ def test_partial_round_blockscale(K, tile):
 @pytest.mark.parametrize("K", [128, 384, 640])
 def test_partial_round_mixed(K, tile):
     _check("mx_a8w4", 200, 300, K, tile)
+
+
+@pytest.mark.parametrize("tile", [4, 5, 7])
+@pytest.mark.parametrize("K", [128, 384, 640])
+def test_partial_round_mixed_e2m1_a(K, tile):
+    _check("mx_a4w8", 200, 300, K, tile)
 
 
 def test_partial_round_full_size_mxfp8():

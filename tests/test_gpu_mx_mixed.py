@@ -1,5 +1,6 @@
-"""GPU parity of the mixed-format MX GEMM (qgemm_mx_mixed: e4m3 A x e2m1 B)
-against the CPU oracle (orc_mx2) on the same seeded inputs, through the C ABI.
+"""GPU parity of the mixed-format MX GEMM (qgemm_mx_mixed: e4m3 A x e2m1 B,
+and e2m1 A x e4m3 B) against the CPU oracle (orc_mx2) on the same seeded
+inputs, through the C ABI.
 
 Bar: per element |gpu - oracle| <= 1e-2 * sum_k |A~ B~| + 1 bf16 ulp, cosine
 >= 0.99999.  Every LDS-fetch tile it runs on (4, 5, 7), both B-scale
@@ -36,8 +37,8 @@ def _gpu_only():
     q.force_tile(-1)
 
 
-def _make(M, N, K, brows=1, bias=False):
-    d = inputs.make("mx_a8w4", M=M, N=N, K=K, bias=bias)
+def _make(M, N, K, brows=1, bias=False, name="mx_a8w4"):
+    d = inputs.make(name, M=M, N=N, K=K, bias=bias)
     if brows == 32:
         # 32x32 B scales: one code per 32 rows of B (the recipe's 1x32 codes of the group's first row)
         d["scale_b"] = np.ascontiguousarray(d["scale_b"][::32])
@@ -104,7 +105,7 @@ def test_mx84_rejects():
     s = torch.full((4, 18), 127, dtype=torch.uint8, device="cuda")
     with pytest.raises(ValueError):      # K = 576 is not a multiple of 128
         q.qgemm_mx_mixed(q.QGEMM_MX_E4M3, q.QGEMM_MX_E2M1, A8, B4, s, s, 1)
-    with pytest.raises(ValueError):      # e2m1 A with e4m3 B
+    with pytest.raises(ValueError):      # e2m1 A with e4m3 B, the same K
         q.qgemm_mx_mixed(q.QGEMM_MX_E2M1, q.QGEMM_MX_E4M3, B4, A8, s, s, 1)
 
 
@@ -150,3 +151,56 @@ def test_mx84_small_m_kernel(M, N, K, tile, brows):
     after = parity.bits(buf)
     assert np.array_equal(after[:M, N:], before[:M, N:]), "wrote past N"
     assert np.array_equal(after[M:], before[M:]), "wrote past M"
+
+
+# ---- e2m1 A x e4m3 B (the LDS-fetch tiles 4, 5, 7 at every M)
+
+SHAPES = [(256, 256, 512), (33, 70, 512), (300, 520, 1024), (1, 1, 512), (257, 300, 1536), (300, 264, 256),
+          (256, 512, 768), (130, 200, 1792), (16, 300, 640)]
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("brows", [1, 32])
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_mx48_small(M, N, K, brows, tile):
+    q.force_tile(tile)
+    _check(_make(M, N, K, brows, name="mx_a4w8"), f"mx48 brows={brows} tile={tile}")
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("brows", [1, 32])
+def test_mx48_bias_and_random_scales(tile, brows):
+    q.force_tile(tile)
+    d = _make(320, 288, 2048, brows, bias=True, name="mx_a4w8")
+    rng = np.random.default_rng(11 + brows)
+    d["scale_a"] = rng.integers(112, 142, d["scale_a"].shape, dtype=np.uint8)
+    d["scale_b"] = rng.integers(112, 142, d["scale_b"].shape, dtype=np.uint8)
+    _check(d, f"mx48 random scales brows={brows} tile={tile}")
+
+
+@pytest.mark.parametrize("tile", TILES + [-1])
+@pytest.mark.parametrize("M,N,K", [(17, 31, 512), (100, 200, 1024), (1000, 129, 2048), (5, 300, 384)])
+def test_mx48_edges_canaries(M, N, K, tile):
+    q.force_tile(tile)
+    d = _make(M, N, K, bias=True, name="mx_a4w8")
+    ldc = N + (-N) % 8 + 8
+    buf = torch.full((M + 3, ldc), float("nan"), dtype=torch.bfloat16, device="cuda")
+    before = parity.bits(buf)
+    _check(d, f"mx48 canaries tile={tile}", out=buf[:M, :N])
+    after = parity.bits(buf)
+    assert np.array_equal(after[:M, N:], before[:M, N:]), "wrote past N"
+    assert np.array_equal(after[M:], before[M:]), "wrote past M"
+
+
+@pytest.mark.parametrize("tile", [-1, 5, 7])
+def test_mx48_full_workload_sampled(tile):
+    """8192^3 e2m1 A x e4m3 B, launched as the benchmark launches it, into a
+    NaN-filled C: every output written; the first and last row of every tile
+    band and random rows against the oracle."""
+    q.force_tile(tile)
+    d = inputs.make("mx_a4w8")
+    _say(f"[parity] full mx_a4w8 tile {tile}")
+    out = parity.gpu_run(d, out=parity.nan_out(d["M"], d["N"]))
+    worst, cos, _ = parity.check_full_grid(d, out, tile, "full mx_a4w8",
+                                           _sample_rows(d["M"], 16, np.random.default_rng(4)))
+    _say(f"[parity] full mx_a4w8: worst err/bound {worst:.3g} cos {cos:.8f}")

@@ -37,7 +37,7 @@ def _gpu_only():
 def _shape(rng, name):
     M = int(rng.choice([int(rng.integers(1, 17)), int(rng.integers(17, 65)), int(rng.integers(65, 520))]))
     N = int(rng.integers(1, 520))
-    if name in ("f8_block", "mx_a8w4", "mxfp6", "mxfp6_e3m2"):
+    if name in ("f8_block", "mx_a8w4", "mx_a4w8", "mxfp6", "mxfp6_e3m2"):
         K = 128 * int(rng.integers(1, 13))                 # these paths: K a multiple of 128
     else:
         # any multiple of 32 (e2m1 K = 32 * odd: 16-byte row ends, the
@@ -56,7 +56,7 @@ def _make(name, M, N, K, bias, rng):
     return d
 
 
-NAMES = ["i8_small", "f8_ptpc", "mxfp8", "mxfp4", "f8_block", "mx_a8w4", "mxfp6", "mxfp6_e3m2"]
+NAMES = ["i8_small", "f8_ptpc", "mxfp8", "mxfp4", "f8_block", "mx_a8w4", "mx_a4w8", "mxfp6", "mxfp6_e3m2"]
 
 
 @pytest.mark.parametrize("name", NAMES)

@@ -66,6 +66,7 @@ CASES = [
     ("mxfp4", 260, 300, 1280, [0, 1, 4, 5, 6, 7]),
     ("f8_block", 280, 300, 640, [7, 10]),
     ("mx_a8w4", 200, 300, 640, [4, 5, 7]),
+    ("mx_a4w8", 200, 300, 640, [4, 5, 7]),
     ("mxfp6", 200, 300, 640, [4, 7]),
     ("mxfp6_e3m2", 130, 260, 1024, [4, 7]),
 ]

@@ -28,3 +28,4 @@ def test_path_of():
     assert parity.path_of({"kind": "mx", "fmt": "e2m1"}) == 3
     assert parity.path_of({"kind": "f8b", "fmt": None}) == 4
     assert parity.path_of({"kind": "mx", "fmt": "e4m3/e2m1"}) == 5
+    assert parity.path_of({"kind": "mx", "fmt": "e2m1/e4m3"}) == 8
