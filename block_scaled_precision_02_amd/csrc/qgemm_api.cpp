@@ -278,23 +278,30 @@ qgemm_status launch(F &&f)
 
 // The LDS-fetch kernels (tiles 4-7) run tiles whose K is a whole number of
 // their 64-byte stages (a last round of fewer than four is masked).  For MX,
-// a round reads 16 bytes of each scale row from byte 16u (e2m1) or 8u (e4m3):
-// scale rows of whole dwords (K % 128), so that each such fetch is dword
-// aligned, and the caller's scale arrays aligned to 16 / 8 bytes (svec: the
+// a round reads 16 bytes of each scale row from byte 16u (e2m1) or 8u (e4m3),
+// from the row's start rounded down to a dword (a whole dword unless K % 128
+// == 64), and the caller's scale arrays aligned to 16 / 8 bytes (svec: the
 // caller's check).
 //
 // The masked last round keeps word 0 of a round's scale chunk live and
-// replaces later words past K; a word covers 4 / (words per round) stages, so
-// the stage count must be a whole number of words -- K % 128 for every
-// e4m3-scaled path (two stages per word) and e2m1 (K % 128 keeps K bytes a
-// whole number of 64-byte stages, one stage per word).  dma_k_ok is the one
-// place that rule lives; the MX, blockscale, mixed and 6-bit paths all take it.
+// replaces later words past K; a word covers 4 / (words per round) stages.
+// e2m1 (one stage per word) needs K % 128 for whole 64-byte stages, the
+// blockscale and 6-bit paths K % 128 by their blocks and rows.  The
+// e4m3-staged MX paths (e4m3, and both mixed pairings: 64 K elements a stage,
+// two stages per word) take any K % 64: at K % 128 == 64 their scale rows
+// start 2 bytes into a dword on every other row and the last live word may
+// be half past K, which the LDS-fetch kernel's SU form handles (fetches from the
+// dword-aligned start, half-word masking).  dma_k_ok is the one place that
+// rule lives; every LDS-fetch path takes it.
 bool dma_k_ok(int path, int64_t K)
 {
     switch (path) {
     case 0:
     case 1: return K % 64 == 0;    // int8 / e4m3 bytes: whole 64-byte stages
-    default: return K % 128 == 0;  // scaled paths: whole scale words per round
+    case 2:                        // e4m3 MX
+    case 5:                        // mixed MX, e4m3 A x e2m1 B
+    case 8: return K % 64 == 0;    // mixed MX, e2m1 A x e4m3 B
+    default: return K % 128 == 0;  // e2m1, blockscale, 6-bit: whole scale words per round
     }
 }
 
@@ -737,7 +744,7 @@ static qgemm_status mx_mixed_common(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, cons
     TRY(check_shape(s, false));
     if (!dma_k_ok(5, K) || (packed && K % 256))
         return fail(QGEMM_ERR_BAD_SHAPE, "K=%lld: %s needs K a multiple of %d", (long long)K, pair,
-                    packed ? 256 : 128);
+                    packed ? 256 : 64);
     if (M == 0 || N == 0)
         return QGEMM_OK;
     TRY(check_operand("A", A, lda_bytes, a4 ? K / 2 : K));

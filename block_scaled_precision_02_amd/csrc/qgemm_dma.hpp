@@ -142,7 +142,10 @@ __device__ __forceinline__ typename PathTraits<PATH>::Frag dma_frag(const uint8_
 
 // WN = 2: 4 waves (one per SIMD) of 128x128; WN = 4: 8 waves (two per
 // SIMD, so one can issue MFMAs while the other waits) of 128x64.
-template <int PATH, int WN, int TM, int TN, bool BIAS, int BROWS, int OUT>
+// SU (the e4m3-staged MX paths at K % 128 == 64): scale rows of K/32 bytes,
+// every other one starting 2 bytes into a dword.  (One kernel template: the
+// body moved into a device function called from two kernels spilled.)
+template <int PATH, int WN, int TM, int TN, bool BIAS, int BROWS, int OUT, bool SU = false>
 __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
 {
     constexpr int WM = 2;
@@ -193,9 +196,14 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr int WIDE_BUF = (SAW + SBW) * RW;
     constexpr bool PRM = OUT == OUT_BF16 && (!SCL || BIAS);
     constexpr int NWA = SAW / WRPF, NWT = NWA + SBW / WRPF;   // fetches per refill: A rows, all
-    constexpr bool WIDE = MX && BROWS == 1 && SAW % WRPF == 0 && SBW % WRPF == 0 && NWT % (G * NW) == 0 &&
+    constexpr bool WIDE = !SU && MX && BROWS == 1 && SAW % WRPF == 0 && SBW % WRPF == 0 && NWT % (G * NW) == 0 &&
                           NSLOT * STAGE_BYTES + 2 * WIDE_BUF + (PRM ? PRM_BYTES : 0) <= 160 * 1024;
     constexpr int NSCW = NWT / (G * NW);                  // per wave and round
+    // Unaligned scale rows (SU): every chunk is fetched from its row's
+    // dword-aligned start rounded down, m = 2 bytes early on the rows where
+    // the row starts 2 bytes into a dword; the narrow chunk's 16 bytes still
+    // hold the round's 8 from byte m, which the reader shifts out.
+    static_assert(!SU || (MX && !F6 && RB == 8 && !WIDE), "unaligned scale rows: e4m3-staged MX, narrow chunks");
     constexpr int SCL_BYTES = SCL ? 2 * (WIDE ? WIDE_BUF : SCL_BUF) : 0;
     constexpr int NQ = TM * TN;
     constexpr int RPF = (PATH == PATH_F8 || PATH == PATH_MX8 || PATH == PATH_F8B || PATH == PATH_MX84 ||
@@ -408,14 +416,20 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     __amdgpu_buffer_rsrc_t rsa, rsb;
     unsigned sa_fo = OOB, sb_fo = OOB;
     if constexpr (SCL) {
-        rsa = make_rsrc(p.mx_sa + (int64_t)m0 * p.kblocks, (uint32_t)(rows_a * p.kblocks));
+        // Ranges in whole dwords: a dword the range ends inside reads as
+        // zero, and under SU (K/32 = 4n + 2) an odd row count ends the tile's
+        // last scale row half way into one.  Such a range ends the array
+        // (the last tile of A, or of B's scale rows), and the dword's other
+        // 2 bytes lie in the same page; they land past the row's K/32 scales,
+        // where the round's masking replaces them.
+        rsa = make_rsrc(p.mx_sa + (int64_t)m0 * p.kblocks, (uint32_t)((rows_a * p.kblocks + 3) & ~3));
         const int srows_b = (rows_b + BROWS - 1) / BROWS;
-        rsb = make_rsrc(p.mx_sb + (int64_t)(n0 / BROWS) * p.kblocks, (uint32_t)(srows_b * p.kblocks));
+        rsb = make_rsrc(p.mx_sb + (int64_t)(n0 / BROWS) * p.kblocks, (uint32_t)((srows_b * p.kblocks + 3) & ~3));
         const int sw = NW == 8 ? (wave & 3) : wave;               // scale row group of this wave
         const int ra_row = 64 * sw + lane;                         // A scale row of this lane
-        sa_fo = ra_row < rows_a ? (unsigned)(ra_row * p.kblocks) : OOB;
+        sa_fo = ra_row < rows_a ? (unsigned)(ra_row * p.kblocks) & ~3u : OOB;
         const int rb_row = BROWS == 1 ? 64 * sw + lane : lane;     // 32 / 128 rows: rows 0..63, fetched alike by every wave
-        sb_fo = rb_row < srows_b ? (unsigned)(rb_row * p.kblocks) : OOB;
+        sb_fo = rb_row < srows_b ? (unsigned)(rb_row * p.kblocks) & ~3u : OOB;
     }
     // Wide: half e (0, 1) of a refill is global fetches g = e * NWT/2 + NSCW *
     // wave + k, k < NSCW; fetch g < NWA covers A scale rows WRPF*g .. +WRPF-1,
@@ -600,8 +614,13 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
                                        : &lds[OPND_BYTES + (r & 1) * SCL_BUF];
             constexpr int SP = WIDE ? RW : 16;                // row pitch
             constexpr int SBOFF = WIDE ? SAW * RW : SA_ROWS * 16;
-            auto rd = [&](const uint8_t *row_base, unsigned (&w)[SCW]) {
-                if constexpr (SCW == 4) {
+            // (SU: the row's 8 bytes start at byte m of its chunk)
+            auto rd = [&](const uint8_t *row_base, unsigned (&w)[SCW], unsigned m) {
+                if constexpr (SU) {
+                    const u32x4 v = *(const u32x4 *)row_base;
+                    w[0] = __builtin_amdgcn_alignbyte(v[1], v[0], m);
+                    w[1] = __builtin_amdgcn_alignbyte(v[2], v[1], m);
+                } else if constexpr (SCW == 4) {
                     const u32x4 v = *(const u32x4 *)row_base;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) w[q] = v[q];
@@ -611,13 +630,15 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
                     w[1] = v[1];
                 }
             };
+            // a row's offset in its dword (0 unless SU; rows 32 apart share it)
+            const unsigned ma = SU ? (unsigned)(arow * p.kblocks) & 3u : 0u;
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                rd(sbuf + (arow + 32 * i) * SP, cra[i]);
+                rd(sbuf + (arow + 32 * i) * SP, cra[i], ma);
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int row = BROWS == 1 ? brow + 32 * j : (wn * TN * 32 + 32 * j) / BROWS;
-                rd(sbuf + SBOFF + row * SP, crb[j]);
+                rd(sbuf + SBOFF + row * SP, crb[j], SU ? (unsigned)(row * p.kblocks) & 3u : 0u);
             }
         }
     };
@@ -627,18 +648,33 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             // row's scales or zeros: make them finite and neutral -- scale
             // 2^0 under zero data for MX, a fold factor of 0 for blockscale.
             // Word 0 is always live (a round starts below K), and each word
-            // covers 4 / SCW whole stages: the host admits only K with a whole
-            // number of words (dma_k_ok: K % 128 on every scaled path), so a
-            // word is either wholly past K or wholly before it.
+            // covers 4 / SCW whole stages: outside SU the host admits only K
+            // with a whole number of words (K % 128), so a word is either
+            // wholly past K or wholly before it; SU splits words.
             constexpr unsigned NEUTRAL = BS ? 0u : 0x7F7F7F7Fu;
             static_assert(4 % SCW == 0, "a scale word covers whole stages");
+            if constexpr (SU) {
+                // K % 128 == 64: the round's last live word may hold one
+                // stage of data (bytes 0, 1) and one past K (bytes 2, 3)
 #pragma unroll
-            for (int w = 1; w < SCW; ++w) {
-                const bool past = t + w * (4 / SCW) >= nst;
+                for (int w = 0; w < SCW; ++w) {
+                    const bool past = t + 2 * w >= nst, past_hi = t + 2 * w + 1 >= nst;
+                    const unsigned keep = past ? 0u : past_hi ? 0xFFFFu : ~0u;
+                    const unsigned fill = NEUTRAL & ~keep;
 #pragma unroll
-                for (int i = 0; i < TM; ++i) cra[i][w] = past ? NEUTRAL : cra[i][w];
+                    for (int i = 0; i < TM; ++i) cra[i][w] = (cra[i][w] & keep) | fill;
 #pragma unroll
-                for (int j = 0; j < TN; ++j) crb[j][w] = past ? NEUTRAL : crb[j][w];
+                    for (int j = 0; j < TN; ++j) crb[j][w] = (crb[j][w] & keep) | fill;
+                }
+            } else {
+#pragma unroll
+                for (int w = 1; w < SCW; ++w) {
+                    const bool past = t + w * (4 / SCW) >= nst;
+#pragma unroll
+                    for (int i = 0; i < TM; ++i) cra[i][w] = past ? NEUTRAL : cra[i][w];
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) crb[j][w] = past ? NEUTRAL : crb[j][w];
+                }
             }
         }
     };
@@ -821,7 +857,9 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         // row's last byte in a half-live line: they are not multiplied.  The
         // other paths multiply zeros there.  (K % 128 == 0: the stage count
         // is even, so the first two stages of a round are always live.)
-        // (P6: the loop runs in steps of six stages; those past K are skipped.)
+        // (P6: the loop runs in steps of six stages; those past K are skipped.
+        // SU, whose odd stage count leaves a last round of one or three
+        // stages, multiplies zeros: branching there spills the 8-wave tile.)
         const bool mul = F6 ? (J < 2 || t < nst) : P6 ? t < nst : true;
         // ---- region A
         {
@@ -934,8 +972,8 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     };
 
     // The host guarantees a whole number of stages (kbytes % 64 == 0; for the
-    // scaled paths, of the stages that one scale word covers; FP6: K % 128 ==
-    // 0).  Fetches run three stages (FP6: two to three lines) ahead, into
+    // scaled paths, of the stages that one scale word covers, except under
+    // SU, where the last live word may be half past K; FP6: K % 128 == 0).  Fetches run three stages (FP6: two to three lines) ahead, into
     // stages past K that are never multiplied or, in a partial last round,
     // multiplied as zeros (FP6: skipped).
     if constexpr (P6) {

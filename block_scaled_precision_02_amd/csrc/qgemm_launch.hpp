@@ -12,7 +12,9 @@ namespace qgemm {
 //   2 -> 256x256, 2x4 waves of 128x64 (2 waves per SIMD, 128 accumulators)
 //   3 -> 192x192, 2x2 waves of 96x96 (144 accumulators)
 //   4 -> 256x256 as tile 0, operands fetched straight into LDS (qgemm_dma.hpp);
-//        needs K bytes % 256 == 0 and, for MX, K/32 % 16 == 0 with aligned scales
+//        needs K bytes % 64 == 0 and, for the scaled paths, K % 128 == 0 (the
+//        e4m3-staged MX paths: K % 64, the SU form at K % 128 == 64)
+//        with aligned scales
 //   5 -> 256x256 fetched straight into LDS as tile 4, 2x4 waves of 128x64 (two
 //        waves per SIMD); same requirements
 //   6 -> 192x192 fetched straight into LDS, 2x2 waves of 96x96; same requirements
@@ -51,6 +53,34 @@ hipError_t launch_variant(const Params &p, hipStream_t s)
     return hipGetLastError();
 }
 
+// The e4m3-staged MX paths at K % 128 == 64 (scale rows of K/32 bytes, every
+// other one starting 2 bytes into a dword): tiles 4, 5, 7, and 6 for e4m3.
+template <int PATH, bool BIAS, int BROWS, int OUT = OUT_BF16>
+hipError_t launch_dma_su(int tile, const Params &p, hipStream_t s)
+{
+    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(tile_threads(tile));
+    switch (tile) {
+    case DMA_TILE:
+        hipLaunchKernelGGL((qgemm_dma_kernel<PATH, 2, 4, 4, BIAS, BROWS, OUT, true>), grid, block, 0, s, p);
+        break;
+    case DMA8_TILE:
+        hipLaunchKernelGGL((qgemm_dma_kernel<PATH, 4, 4, 2, BIAS, BROWS, OUT, true>), grid, block, 0, s, p);
+        break;
+    case DMA192_TILE:
+        if constexpr (PATH == PATH_MX8) {
+            hipLaunchKernelGGL((qgemm_dma_kernel<PATH, 2, 3, 3, BIAS, BROWS, OUT, true>), grid, block, 0, s, p);
+            break;
+        } else {
+            return hipErrorInvalidValue;
+        }
+    case DMA128_TILE:
+        hipLaunchKernelGGL((qgemm_dma_kernel<PATH, 2, 2, 2, BIAS, BROWS, OUT, true>), grid, block, 0, s, p);
+        break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 template <int PATH, bool BIAS, int BROWS, bool SVEC, int OUT>
 hipError_t launch_tile(int tile, const Params &p, hipStream_t s)
 {
@@ -69,6 +99,10 @@ hipError_t launch_tile(int tile, const Params &p, hipStream_t s)
         }
         {
             const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(tile_threads(tile));
+            if constexpr (PATH == PATH_MX8) {
+                if (p.kblocks % 4 != 0)   // K % 128 == 64: scale rows off dword boundaries
+                    return launch_dma_su<PATH, BIAS, BROWS, OUT>(tile, p, s);
+            }
             if (tile == DMA_TILE)
                 hipLaunchKernelGGL((qgemm_dma_kernel<PATH, 2, 4, 4, BIAS, BROWS, OUT>), grid, block, 0, s, p);
             else if (tile == DMA8_TILE)

@@ -160,12 +160,12 @@ def test_tile_table():
     assert L.qgemm_select_tile(1, 4096, 2112, 7168) == 6
     assert L.qgemm_select_tile(1, 4096, 2112, 7200) == 3
     assert L.qgemm_select_tile(9, 64, 64, 64) == -1
-    # e4m3 MX with K % 128 == 64: the scale rows are whole dwords but a round's
-    # last scale word would cover one stage of data and one past K, which the
-    # masked round cannot split -- the register-staged tile (one rule for every
-    # scaled path: K % 128)
-    assert L.qgemm_select_tile(2, 16384, 7168, 2112) == 0
-    assert L.qgemm_select_tile(3, 8192, 8192, 8256) == 0        # e2m1, K % 128 == 64 as well
+    # e4m3 MX with K % 128 == 64 (K/32 = 66: scale rows 2 bytes off a dword
+    # on every other row, a last round of one or three stages): the LDS-fetch
+    # kernel's unaligned-scale-row form; e2m1 at K % 128 == 64 has half a
+    # 64-byte stage left over -- the register-staged tile
+    assert L.qgemm_select_tile(2, 16384, 7168, 2112) == 5
+    assert L.qgemm_select_tile(3, 8192, 8192, 8256) == 0        # e2m1, K % 128 == 64
     # 6-bit MX: the LDS-fetch kernel only -- 256x256 (the four-wave tile 4) or 128x128 (7)
     assert L.qgemm_select_tile(6, 8192, 8192, 8192) == 4
     assert L.qgemm_select_tile(7, 8192, 8192, 8192) == 4
@@ -346,9 +346,9 @@ def mx2(fa=0, fb=1, A=FAKE, lda=512, B=FAKE2, ldb=256, sa=FAKE3, sb=FAKE3, layou
     (dict(fb=7), q.QGEMM_ERR_BAD_FORMAT),
     (dict(fa=1, fb=0), q.QGEMM_ERR_BAD_LAYOUT),                 # e2m1 A x e4m3 B: B row is K = 512 bytes
     (dict(fa=1, fb=0, lda=128, ldb=512), q.QGEMM_ERR_BAD_LAYOUT),  # ... and A row K/2 = 256
-    (dict(fa=1, fb=0, lda=256, ldb=512, K=576), q.QGEMM_ERR_BAD_SHAPE),
+    (dict(fa=1, fb=0, lda=288, ldb=544, K=544), q.QGEMM_ERR_BAD_SHAPE),
     (dict(layout=16), q.QGEMM_ERR_BAD_FORMAT),
-    (dict(K=576, lda=576, ldb=288), q.QGEMM_ERR_BAD_SHAPE),      # K % 128
+    (dict(K=544, lda=544, ldb=272), q.QGEMM_ERR_BAD_SHAPE),      # K % 64
     (dict(A=None), q.QGEMM_ERR_NULL_POINTER),
     (dict(sb=None), q.QGEMM_ERR_NULL_POINTER),
     (dict(ldb=128), q.QGEMM_ERR_BAD_LAYOUT),                     # e2m1 B row is K/2 = 256 bytes

@@ -76,23 +76,23 @@ def _run(d, At, Bt):
     return q.qgemm_mx(fmt, At, Bt, sa, sb, d["b_rows_per_scale"], bias)
 
 
-def _poison_scales(d):
-    """Every scale of the odd A scale rows and odd B scale rows is non-finite;
+def _poison_scales(d, keep=0):
+    """Every scale of the A and B scale rows of parity 1 - keep is non-finite;
     returns the output rows and columns whose scales are all finite."""
     M, N = d["M"], d["N"]
     if d["kind"] in ("i8", "f8"):
         return np.arange(M), np.arange(N)        # scales applied per row in the epilogue
     sa, sb = d["scale_a"].copy(), d["scale_b"].copy()
     bad = np.float32(np.inf) if d["kind"] == "f8b" else np.uint8(255)
-    sa[1::2, :] = bad        # every word of a neighbouring row, so each masked word position is checked
-    sb[1::2, :] = bad
+    sa[1 - keep::2, :] = bad  # every word of a neighbouring row, so each masked word position is checked
+    sb[1 - keep::2, :] = bad
     d["scale_a"], d["scale_b"] = sa, sb
     group = 128 if d["kind"] == "f8b" else d["b_rows_per_scale"]
     cols = np.arange(N)
-    return np.arange(0, M, 2), cols[(cols // group) % 2 == 0]
+    return np.arange(keep, M, 2), cols[(cols // group) % 2 == keep]
 
 
-def _check(name, M, N, K, tile, brows=None, bias=True):
+def _check(name, M, N, K, tile, brows=None, bias=True, keep=0):
     q.force_tile(tile)
     d = inputs.make(name, M=M, N=N, K=K, bias=bias)
     if brows == 1 and d["kind"] == "mx" and d["b_rows_per_scale"] != 1:
@@ -100,7 +100,7 @@ def _check(name, M, N, K, tile, brows=None, bias=True):
         xb = rng.standard_normal((N, K)).astype(np.float32)
         d["B"], d["scale_b"] = inputs.mx_quantise(xb, d["fmt"], 1)
         d["b_rows_per_scale"] = 1
-    rows, cols = _poison_scales(d)
+    rows, cols = _poison_scales(d, keep)
     pa, pb = _poison_bytes(d)
     _say(f"[ktail] {name} {M}x{N}x{K} tile={tile} brows={d['b_rows_per_scale']}")
     out = _run(d, _padded(d["A"], pa), _padded(d["B"], pb))
@@ -151,6 +151,40 @@ def test_partial_round_mixed(K, tile):
 @pytest.mark.parametrize("K", [128, 384, 640])
 def test_partial_round_mixed_e2m1_a(K, tile):
     _check("mx_a4w8", 200, 300, K, tile)
+
+
+# K % 128 == 64 on the e4m3-staged MX paths: scale rows of K/32 = 4n + 2
+# bytes (every other row starts 2 bytes into a dword), a last round of one or
+# three stages whose last scale word is half past K.  Both row parities are
+# checked against poisoned neighbours.
+@pytest.mark.parametrize("keep", [0, 1])
+@pytest.mark.parametrize("tile", DMA_TILES)
+@pytest.mark.parametrize("brows", [1, 32])
+@pytest.mark.parametrize("K", [64, 192, 320, 1216])
+@pytest.mark.parametrize("M,N", [(200, 300), (201, 289)])   # odd: the last scale row ends mid-dword
+def test_k64_mxfp8(M, N, K, brows, tile, keep):
+    _check("mxfp8", M, N, K, tile, brows=brows, keep=keep)
+
+
+@pytest.mark.parametrize("keep", [0, 1])
+@pytest.mark.parametrize("tile", [4, 5, 7])
+@pytest.mark.parametrize("name", ["mx_a8w4", "mx_a4w8"])
+@pytest.mark.parametrize("K", [64, 192, 704])
+@pytest.mark.parametrize("M,N", [(200, 300), (201, 289)])
+def test_k64_mixed(name, M, N, K, tile, keep):
+    _check(name, M, N, K, tile, keep=keep)
+
+
+def test_k64_full_size_mxfp8():
+    """16384 x 7168 x 2112 (K/32 = 66, 33 stages) in the launch the benchmark
+    uses for MXFP8, into a NaN-filled C, on sampled whole rows of both
+    parities."""
+    d = inputs.make("mxfp8", K=2112)
+    assert q.select_tile(2, d["M"], d["N"], d["K"]) == 5
+    _say(f"[ktail] full mxfp8 {d['M']}x{d['N']}x{d['K']}")
+    out = parity.gpu_run(d, out=parity.nan_out(d["M"], d["N"]))
+    rng = np.random.default_rng(5)
+    parity.check_full_grid(d, out, -1, "k64 full mxfp8", rng.choice(d["M"], 16, replace=False))
 
 
 def test_partial_round_full_size_mxfp8():

@@ -59,7 +59,8 @@ def _check(d, what, out=None):
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("brows", [1, 32])
 @pytest.mark.parametrize("M,N,K", [(256, 256, 512), (33, 70, 512), (300, 520, 1024), (1, 1, 512), (257, 300, 1536),
-                                   (300, 264, 256), (256, 512, 768), (130, 200, 1792)])
+                                   (300, 264, 256), (256, 512, 768), (130, 200, 1792),
+                                   (300, 264, 192), (257, 300, 704), (64, 130, 64), (130, 257, 1216)])
 def test_mx84_small(M, N, K, brows, tile):
     q.force_tile(tile)
     _check(_make(M, N, K, brows), f"mx84 brows={brows} tile={tile}")
@@ -100,10 +101,10 @@ def test_mx84_equal_formats_are_qgemm_mx():
 
 
 def test_mx84_rejects():
-    A8 = torch.zeros((4, 576), dtype=torch.uint8, device="cuda")
-    B4 = torch.zeros((4, 288), dtype=torch.uint8, device="cuda")
-    s = torch.full((4, 18), 127, dtype=torch.uint8, device="cuda")
-    with pytest.raises(ValueError):      # K = 576 is not a multiple of 128
+    A8 = torch.zeros((4, 544), dtype=torch.uint8, device="cuda")
+    B4 = torch.zeros((4, 272), dtype=torch.uint8, device="cuda")
+    s = torch.full((4, 17), 127, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):      # K = 544 is not a multiple of 64
         q.qgemm_mx_mixed(q.QGEMM_MX_E4M3, q.QGEMM_MX_E2M1, A8, B4, s, s, 1)
     with pytest.raises(ValueError):      # e2m1 A with e4m3 B, the same K
         q.qgemm_mx_mixed(q.QGEMM_MX_E2M1, q.QGEMM_MX_E4M3, B4, A8, s, s, 1)
@@ -131,7 +132,7 @@ def test_mx84_full_workload_sampled(tile):
 
 
 SMALL_M = [(1, 7168, 2048, 8), (5, 200, 256, 8), (16, 300, 1792, 8), (1, 1, 512, 8), (33, 130, 512, 9),
-           (64, 264, 768, 9)]
+           (64, 264, 768, 9), (5, 200, 320, 8), (33, 130, 704, 9)]
 
 
 @pytest.mark.parametrize("brows", [1, 32])
@@ -156,7 +157,9 @@ def test_mx84_small_m_kernel(M, N, K, tile, brows):
 # ---- e2m1 A x e4m3 B (the LDS-fetch tiles 4, 5, 7 at every M)
 
 SHAPES = [(256, 256, 512), (33, 70, 512), (300, 520, 1024), (1, 1, 512), (257, 300, 1536), (300, 264, 256),
-          (256, 512, 768), (130, 200, 1792), (16, 300, 640)]
+          (256, 512, 768), (130, 200, 1792), (16, 300, 640),
+          # K % 128 == 64: scale rows off dword boundaries, a half-live last scale word
+          (300, 264, 192), (257, 300, 704), (64, 130, 64), (130, 257, 1216)]
 
 
 @pytest.mark.parametrize("tile", TILES)

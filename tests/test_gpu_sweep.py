@@ -37,8 +37,10 @@ def _gpu_only():
 def _shape(rng, name):
     M = int(rng.choice([int(rng.integers(1, 17)), int(rng.integers(17, 65)), int(rng.integers(65, 520))]))
     N = int(rng.integers(1, 520))
-    if name in ("f8_block", "mx_a8w4", "mx_a4w8", "mxfp6", "mxfp6_e3m2"):
+    if name in ("f8_block", "mxfp6", "mxfp6_e3m2"):
         K = 128 * int(rng.integers(1, 13))                 # these paths: K a multiple of 128
+    elif name in ("mx_a8w4", "mx_a4w8"):
+        K = 64 * int(rng.integers(1, 25))                  # mixed MX: K a multiple of 64
     else:
         # any multiple of 32 (e2m1 K = 32 * odd: 16-byte row ends, the
         # register-staged and small-M tails)

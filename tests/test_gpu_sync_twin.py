@@ -67,6 +67,9 @@ CASES = [
     ("f8_block", 280, 300, 640, [7, 10]),
     ("mx_a8w4", 200, 300, 640, [4, 5, 7]),
     ("mx_a4w8", 200, 300, 640, [4, 5, 7]),
+    ("mxfp8", 200, 300, 704, [4, 5, 6, 7]),                       # K % 128 == 64
+    ("mx_a8w4", 130, 260, 448, [4, 5, 7]),
+    ("mx_a4w8", 130, 260, 448, [4, 5, 7]),
     ("mxfp6", 200, 300, 640, [4, 7]),
     ("mxfp6_e3m2", 130, 260, 1024, [4, 7]),
 ]
