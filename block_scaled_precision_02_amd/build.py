@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqgemm.so")
-SOURCES = ["qgemm_api.cpp", "qgemm_i8.hip", "qgemm_f8.hip", "qgemm_mx8.hip", "qgemm_mx4.hip", "qgemm_f8b.hip", "qgemm_mx84.hip", "qgemm_mx48.hip", "qgemm_mx6.hip",
+SOURCES = ["qgemm_api.cpp", "qgemm_i8.hip", "qgemm_f8.hip", "qgemm_mx8.hip", "qgemm_mx4.hip", "qgemm_f8b.hip", "qgemm_mx84.hip", "qgemm_mx48.hip", "qgemm_mx4h.hip", "qgemm_mx6.hip",
            "qgemm_quant.hip", "qgemm_pack.hip"]
 # Per-source extra flags.  The blockscale kernel folds its MFMA partial sums
 # into the totals with VALU FMAs every 128 K elements; keeping the MFMA

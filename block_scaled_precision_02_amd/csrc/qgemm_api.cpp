@@ -407,6 +407,21 @@ int pick_tile_mx48(Shape s)
     return select_tile_impl(2, s.M, s.N) == 0 ? DMA_TILE : DMA128_TILE;
 }
 
+// e2m1 MX at K % 128 == 64 (K/32 = 4n + 2): the LDS-fetch kernel in
+// 64-element stages -- the eight-wave tile 5 where the table picks 256x256
+// (one MI355X, 8192x8192x8256: 0.505 ms against 0.551 on tile 4 and 0.799 on
+// the register-staged tile), else 7 (forced: 4, 5, 7) -- unless the call
+// takes the small-M kernel (M <= 16, or forced 8 / 9) or a forced
+// register-staged tile: then -1, the e2m1 path's own choice.
+int pick_tile_mx4h(Shape s)
+{
+    if (g_forced_tile == DMA_TILE || g_forced_tile == DMA8_TILE || g_forced_tile == DMA128_TILE)
+        return g_forced_tile;
+    if (g_forced_tile >= 0 || s.M <= SKINNY_MAX_M_MX)
+        return -1;
+    return select_tile_impl(3, s.M, s.N) == 0 ? DMA8_TILE : DMA128_TILE;
+}
+
 // 6-bit MX: the four-wave 256x256 tile where the 256x256 grid fills the
 // chip, else 128x128 (the only two FP6 tiles built).
 int pick_tile_mx6(Shape s)
@@ -481,7 +496,9 @@ int qgemm_select_tile(int path, int64_t M, int64_t N, int64_t K)
     const int64_t kbytes = path == 3 ? K / 2 : K;
     const int prev = g_forced_tile;
     g_forced_tile = -1;
-    const int t = pick_tile(path, Shape{M, N, K}, kbytes, true, true);   // scales assumed aligned, bf16 out
+    int t = (path == 3 && K % 128 == 64) ? pick_tile_mx4h(Shape{M, N, K}) : -1;
+    if (t < 0)
+        t = pick_tile(path, Shape{M, N, K}, kbytes, true, true);   // scales assumed aligned, bf16 out
     g_forced_tile = prev;
     return t;
 }
@@ -706,6 +723,17 @@ static qgemm_status mx_common(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes
         return fail(QGEMM_ERR_BAD_LAYOUT, "a prepacked MX B needs K/32 a multiple of 16 (e2m1) or 8 (e4m3) and scale "
                                           "arrays aligned to 16 (e2m1) or 8 (e4m3) bytes");
     TRY(check_device());
+    if (fmt == QGEMM_MX_E2M1 && !packed && K % 128 == 64 && aligned(scale_a, 8) && aligned(scale_b, 8)) {
+        const int t4 = pick_tile_mx4h(s);
+        if (t4 >= 0) {
+            Params p = base_params(A, lda_bytes, B, ldb_bytes, C, ldc, s, K, t4);   // kbytes: K, as for e4m3
+            TRY(check_grid(p));
+            p.mx_sa = scale_a;
+            p.mx_sb = scale_b;
+            p.bias = bias;
+            return launch([&] { return launch_mx4h(t4, bias != nullptr, (int)b_layout, p, (hipStream_t)stream); });
+        }
+    }
     const int tile = packed ? pick_tile_packed(path, s, row_bytes, true) : pick_tile(path, s, row_bytes, svec16, true);
     Params p = base_params(A, lda_bytes, B, packed ? row_bytes : ldb_bytes, C, ldc, s, row_bytes, tile);
     p.b_packed = packed;

@@ -93,6 +93,7 @@ template <> struct DmaTraits<PATH_MX4> { static constexpr int NSUB = 2; };  // c
 template <> struct DmaTraits<PATH_F8B> { static constexpr int NSUB = 1; };  // chunks h, 2+h
 template <> struct DmaTraits<PATH_MX84> { static constexpr int NSUB = 1; }; // A chunks h, 2+h; B chunk h of 32 B
 template <> struct DmaTraits<PATH_MX48> { static constexpr int NSUB = 1; }; // A chunk h of 32 B; B chunks h, 2+h
+template <> struct DmaTraits<PATH_MX4H> { static constexpr int NSUB = 1; }; // A and B chunk h of 32 B
 template <> struct DmaTraits<PATH_MX6> { static constexpr int NSUB = 1; };  // 24 bytes at 24h of a 48-byte row
 template <> struct DmaTraits<PATH_MX6E3> { static constexpr int NSUB = 1; };
 
@@ -153,9 +154,12 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     constexpr int NSUB = DmaTraits<PATH>::NSUB;
     constexpr bool F6 = (PATH == PATH_MX6 || PATH == PATH_MX6E3);   // 6-bit operands: 48-byte stages in 64-byte lines
-    constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4 || PATH == PATH_MX84 || PATH == PATH_MX48 || F6);
-    constexpr bool B4 = (PATH == PATH_MX84);              // e2m1 B under e4m3 A: 32-byte B stage rows
-    constexpr bool A4 = (PATH == PATH_MX48);              // e2m1 A under e4m3 B: 32-byte A stage rows
+    constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4 || PATH == PATH_MX84 || PATH == PATH_MX48 ||
+                         PATH == PATH_MX4H || F6);
+    // 32-byte stage rows (64 e2m1 elements): B under e4m3 A, A under e4m3 B,
+    // both for e2m1 in 64-element stages
+    constexpr bool B4 = (PATH == PATH_MX84 || PATH == PATH_MX4H);
+    constexpr bool A4 = (PATH == PATH_MX48 || PATH == PATH_MX4H);
     constexpr bool BS = (PATH == PATH_F8B);               // blockscale FP8
     constexpr bool SCL = MX || BS;                        // scale chunks staged through LDS
     static_assert(!BS || BROWS == 128, "blockscale B scales cover 128 rows");
@@ -207,7 +211,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr int SCL_BYTES = SCL ? 2 * (WIDE ? WIDE_BUF : SCL_BUF) : 0;
     constexpr int NQ = TM * TN;
     constexpr int RPF = (PATH == PATH_F8 || PATH == PATH_MX8 || PATH == PATH_F8B || PATH == PATH_MX84 ||
-                         PATH == PATH_MX48) ? 2 : 1;
+                         PATH == PATH_MX48 || PATH == PATH_MX4H) ? 2 : 1;
     constexpr int RPF_A = A4 ? 1 : RPF, RPF_B = B4 ? 1 : RPF;
     constexpr int NDSR = TM * RPF_A + TN * RPF_B;         // fragment reads per sub-step
     constexpr int DMA_A = BM / AROWS_PER_FETCH / NW, DMA_B = BN / BROWS_PER_FETCH / NW; // fetches per wave per stage
@@ -275,7 +279,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     const int nst = F6 ? p.K / 64 : p.kbytes / DSTAGE;
     const int nfetch = F6 ? (p.kbytes + DSTAGE - 1) / DSTAGE : nst;
     const uint8_t *const a_base = p.A + (int64_t)m0 * p.lda;
-    const int kbytes_a = A4 ? p.kbytes / 2 : p.kbytes;   // (p.kbytes: the e4m3 operand's row)
+    const int kbytes_a = A4 ? p.kbytes / 2 : p.kbytes;   // (A4 / B4: p.kbytes is K, a byte per element)
     const uint32_t a_range = (uint32_t)((rows_a - 1) * p.lda + kbytes_a);
     // B row-major, or prepacked: 16-row groups of 1 KB blocks (32-row groups
     // for the mixed path's 32-byte B rows), block t of a group holding its

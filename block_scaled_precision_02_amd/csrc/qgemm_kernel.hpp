@@ -56,8 +56,11 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // codes per three bytes, lowest bits first); LDS-fetch kernel only.
 // PATH_MX48: MX with e2m1 A and e4m3 B (the mixed path with the operands'
 // formats the other way round); LDS-fetch kernel only.
+// PATH_MX4H: MX e2m1 on both operands in stages of 64 K elements (32-byte
+// stage rows, as the mixed paths' e2m1 operand), for K % 128 == 64, where
+// PATH_MX4's 64-byte stages would leave half a stage; LDS-fetch kernel only.
 enum Path { PATH_I8 = 0, PATH_F8 = 1, PATH_MX8 = 2, PATH_MX4 = 3, PATH_F8B = 4, PATH_MX84 = 5, PATH_MX6 = 6,
-            PATH_MX6E3 = 7, PATH_MX48 = 8 };
+            PATH_MX6E3 = 7, PATH_MX48 = 8, PATH_MX4H = 9 };
 enum OutKind { OUT_BF16 = 0, OUT_I32 = 1 };
 
 // Kernel arguments (one struct, passed by value).
@@ -169,6 +172,7 @@ template <> struct PathTraits<PATH_MX4> { static constexpr int NSUB = 4; using F
 template <> struct PathTraits<PATH_F8B> { static constexpr int NSUB = 2; using Frag = i32x8; };
 template <> struct PathTraits<PATH_MX84> { static constexpr int NSUB = 2; using Frag = i32x8; };
 template <> struct PathTraits<PATH_MX48> { static constexpr int NSUB = 2; using Frag = i32x8; };
+template <> struct PathTraits<PATH_MX4H> { static constexpr int NSUB = 2; using Frag = i32x8; };
 template <> struct PathTraits<PATH_MX6> { static constexpr int NSUB = 1; using Frag = i32x8; };
 template <> struct PathTraits<PATH_MX6E3> { static constexpr int NSUB = 1; using Frag = i32x8; };
 
@@ -221,6 +225,9 @@ __device__ __forceinline__ void mfma(typename AccT<PATH>::T &acc,
     } else if constexpr (PATH == PATH_MX84) {
         // first operand (B) e2m1: cbsz = 4; second (A) e4m3: blgp = 0
         acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, acc, 4, 0, S, (int)sc_b, S, (int)sc_a);
+    } else if constexpr (PATH == PATH_MX4H) {
+        // both operands e2m1: cbsz = blgp = 4
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, acc, 4, 4, S, (int)sc_b, S, (int)sc_a);
     } else if constexpr (PATH == PATH_MX48) {
         // first operand (B) e4m3: cbsz = 0; second (A) e2m1: blgp = 4
         acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, acc, 0, 4, S, (int)sc_b, S, (int)sc_a);
@@ -308,7 +315,7 @@ __device__ __forceinline__ void store_tile(const Params &p, Acc (&acc)[TM][TN], 
     // MX and blockscale apply their scales inside the K loop: the epilogue
     // only adds the bias and rounds
     constexpr bool MX = (PATH == PATH_MX8 || PATH == PATH_MX4 || PATH == PATH_F8B || PATH == PATH_MX84 ||
-                         PATH == PATH_MX48 || PATH == PATH_MX6 || PATH == PATH_MX6E3);
+                         PATH == PATH_MX48 || PATH == PATH_MX4H || PATH == PATH_MX6 || PATH == PATH_MX6E3);
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;

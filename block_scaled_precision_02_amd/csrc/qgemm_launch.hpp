@@ -144,6 +144,8 @@ hipError_t launch_f8b(int tile, bool bias, const Params &p, hipStream_t s);
 hipError_t launch_mx84(int tile, bool bias, int brows, const Params &p, hipStream_t s);
 // MX with e2m1 A and e4m3 B: tiles 4, 5, 7 (same requirements as MX on them).
 hipError_t launch_mx48(int tile, bool bias, int brows, const Params &p, hipStream_t s);
+// MX e2m1 at K % 128 == 64 in 64-element stages: tiles 4, 5, 7 (K/32 % 4 == 2).
+hipError_t launch_mx4h(int tile, bool bias, int brows, const Params &p, hipStream_t s);
 // MX with 6-bit elements (E2M3, or E3M2 when e3m2): tiles 4, 5, 7 (K % 128 == 0
 // and 8-byte aligned scale arrays, as e4m3 MX on them).
 hipError_t launch_mx6(int tile, bool e3m2, bool bias, int brows, const Params &p, hipStream_t s);

@@ -167,9 +167,10 @@ qgemm_status qgemm_f8_blockscale(const uint8_t *A, int64_t lda, const uint8_t *B
  * then f = acc, [+ bias], bf16 round-nearest-even.  Scale code 255 is NaN.
  * The 6-bit formats need K a multiple of 128 (QGEMM_ERR_BAD_SHAPE) and 8-byte
  * aligned scale arrays (QGEMM_ERR_BAD_LAYOUT); qgemm_mx_prepacked does not take
- * them (QGEMM_ERR_BAD_FORMAT).  e4m3 takes any K a multiple of 32: the
- * LDS-fetch tiles where K % 64 == 0 (K % 128 == 64 included), else the
- * register-staged tile. */
+ * them (QGEMM_ERR_BAD_FORMAT).  e4m3 and e2m1 take any K a multiple of 32:
+ * e4m3 runs the LDS-fetch tiles where K % 64 == 0, e2m1 where K % 128 == 0
+ * and, in stages of 64 elements (tiles 4, 5, 7), where K % 128 == 64 with
+ * 8-byte aligned scale arrays; other K run the register-staged tile. */
 qgemm_status qgemm_mx(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const void *B,
                       int64_t ldb_bytes, const uint8_t *scale_a, const uint8_t *scale_b,
                       qgemm_mx_bscale b_layout, const uint16_t *bias, uint16_t *C, int64_t ldc,
@@ -329,7 +330,8 @@ const char *qgemm_status_string(qgemm_status status);
 
 /* Tile variant the host-side table picks for a problem (pure host logic, no
  * HIP call; for MX, assuming 16-byte-aligned scale arrays).  path: 0 int8,
- * 1 fp8, 2 MX e4m3, 3 MX e2m1, 4 fp8 blockscale (tile 8 for M <= 16, else
+ * 1 fp8, 2 MX e4m3, 3 MX e2m1 (at K % 128 == 64 and M > 16: tile 5 where
+ * the table picks 256x256, else 7), 4 fp8 blockscale (tile 8 for M <= 16, else
  * tile 10 when its grid of 256x128 tiles fills the 256 CUs at least once,
  * else tile 7), 5 MX e4m3 A with e2m1 B (tile 8 for M <= 16, else tile 4
  * where the table picks 256x256, else 7), 6 / 7 MX with 6-bit E2M3 / E3M2

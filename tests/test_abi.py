@@ -162,10 +162,13 @@ def test_tile_table():
     assert L.qgemm_select_tile(9, 64, 64, 64) == -1
     # e4m3 MX with K % 128 == 64 (K/32 = 66: scale rows 2 bytes off a dword
     # on every other row, a last round of one or three stages): the LDS-fetch
-    # kernel's unaligned-scale-row form; e2m1 at K % 128 == 64 has half a
-    # 64-byte stage left over -- the register-staged tile
+    # kernel's unaligned-scale-row form; e2m1 at K % 128 == 64 (half a 64-byte
+    # stage left over) runs in 64-element stages on tile 5 or 7
     assert L.qgemm_select_tile(2, 16384, 7168, 2112) == 5
-    assert L.qgemm_select_tile(3, 8192, 8192, 8256) == 0        # e2m1, K % 128 == 64
+    assert L.qgemm_select_tile(3, 8192, 8192, 8256) == 5        # e2m1, K % 128 == 64
+    assert L.qgemm_select_tile(3, 1024, 1024, 2880) == 7        # 16 tiles of 256: the table's 128
+    assert L.qgemm_select_tile(3, 16, 8192, 2880) == 8          # small M: the small-M kernel
+    assert L.qgemm_select_tile(3, 8192, 8192, 8224) == 0        # K % 128 == 32: register-staged
     # 6-bit MX: the LDS-fetch kernel only -- 256x256 (the four-wave tile 4) or 128x128 (7)
     assert L.qgemm_select_tile(6, 8192, 8192, 8192) == 4
     assert L.qgemm_select_tile(7, 8192, 8192, 8192) == 4

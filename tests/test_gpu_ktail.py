@@ -175,6 +175,27 @@ def test_k64_mixed(name, M, N, K, tile, keep):
     _check(name, M, N, K, tile, keep=keep)
 
 
+@pytest.mark.parametrize("keep", [0, 1])
+@pytest.mark.parametrize("tile", [4, 5, 7])
+@pytest.mark.parametrize("K", [64, 192, 320, 1216])
+@pytest.mark.parametrize("M,N", [(200, 300), (201, 289)])
+def test_k64_mxfp4(M, N, K, tile, keep):
+    """e2m1 at K % 128 == 64: both operands in 64-element stages (32-byte rows,
+    the row's last 32 bytes a stage of their own)."""
+    _check("mxfp4", M, N, K, tile, keep=keep)
+
+
+def test_k64_full_size_mxfp4():
+    """8192 x 8192 x 8256 e2m1 (129 stages of 64 elements) in the table's
+    launch, into a NaN-filled C, on the band rows and sampled rows."""
+    d = inputs.make("mxfp4", K=8256)
+    assert q.select_tile(3, d["M"], d["N"], d["K"]) == 5
+    _say(f"[ktail] full mxfp4 {d['M']}x{d['N']}x{d['K']}")
+    out = parity.gpu_run(d, out=parity.nan_out(d["M"], d["N"]))
+    rng = np.random.default_rng(6)
+    parity.check_full_grid(d, out, -1, "k64 full mxfp4", rng.choice(d["M"], 8, replace=False))
+
+
 def test_k64_full_size_mxfp8():
     """16384 x 7168 x 2112 (K/32 = 66, 33 stages) in the launch the benchmark
     uses for MXFP8, into a NaN-filled C, on sampled whole rows of both

@@ -260,6 +260,32 @@ def test_dma_kernel_other_b_layout_and_random_scales(name, tile):
             assert np.array_equal(got, first), f"launch {it} differs"
 
 
+@pytest.mark.parametrize("tile", [-1, 4, 5, 7])
+@pytest.mark.parametrize("brows", [1, 32])
+@pytest.mark.parametrize("K", [1088, 2880])
+def test_mx4_k64_stages_random_scales(K, brows, tile):
+    """e2m1 at K % 128 == 64 (64-element stages, scale rows of K/32 = 4n + 2
+    bytes): both B-scale layouts, random scale codes, bias, repeated launches
+    bit-identical."""
+    rng = np.random.default_rng(K + brows)
+    d = inputs.make("mxfp4", M=300, N=264, K=K, bias=True)
+    if brows == 32:
+        cb, sb = inputs.mx_quantise(rng.standard_normal((264, K)).astype(np.float32), "e2m1", 32)
+        d = dict(d, B=inputs.pack_e2m1(cb), scale_b=sb, b_rows_per_scale=32)
+    d["scale_a"] = rng.integers(118, 136, d["scale_a"].shape, dtype=np.uint8)
+    q.force_tile(tile)
+    _say(f"[parity] mx4 K={K} brows={brows} tile={tile}")
+    ref, absdot, _ = parity.oracle_run(d)
+    first = None
+    for it in range(3):
+        got = parity.bits(parity.gpu_run(d))
+        if first is None:
+            parity.compare(d, got, ref, absdot, f"mx4 K={K} brows={brows} tile={tile}")
+            first = got
+        else:
+            assert np.array_equal(got, first), f"launch {it} differs"
+
+
 @pytest.mark.parametrize("tile", [4, 5, 6, 7])
 def test_dma_tile_falls_back_when_k_does_not_fit(tile):
     d = inputs.make("i8_small", M=100, N=70, K=96)

@@ -70,6 +70,7 @@ CASES = [
     ("mxfp8", 200, 300, 704, [4, 5, 6, 7]),                       # K % 128 == 64
     ("mx_a8w4", 130, 260, 448, [4, 5, 7]),
     ("mx_a4w8", 130, 260, 448, [4, 5, 7]),
+    ("mxfp4", 130, 260, 704, [4, 5, 7]),                          # e2m1 in 64-element stages
     ("mxfp6", 200, 300, 640, [4, 7]),
     ("mxfp6_e3m2", 130, 260, 1024, [4, 7]),
 ]
