@@ -918,9 +918,17 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
                             : PAIR ? ((J & 1) ? 0 : NPF) + ((J == 0 || J == 1) ? NSCD : 0)
                             : F6   ? (J == 1 ? 1 : 2) * NDMA + (J == 3 ? 0 : NSCD)
                                    : 2 * NDMA + ((J == 0 || J == 1) ? NSCD : 0);
+        // Pairs: region B of an even stage reads the second half of the pair
+        // the previous (odd) stage waited for, and issues nothing; every
+        // refill goes out in region B of an odd stage, after that stage's
+        // barrier, into the slot whose last reads (region A of the same odd
+        // stage) precede it.  So only odd stages wait and synchronise.
+        constexpr bool SYNC = !(PAIR && (J & 1) == 0);
         twin_sync();
-        wait_vmcnt<AFTER>();
-        lds_barrier();
+        if constexpr (SYNC) {
+            wait_vmcnt<AFTER>();
+            lds_barrier();
+        }
         __builtin_amdgcn_sched_barrier(0);
         // ---- region B
         {
