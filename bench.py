@@ -183,7 +183,7 @@ def upload(d):
 
 KERNEL_SOURCES = "block_scaled_precision_02_amd/csrc"
 # workloads whose FETCH_SIZE / WRITE_SIZE runs profiles/traffic.json holds
-TRAFFIC_WORKLOADS = ["i8_qkv", "mxfp4", "f8_ptpc", "mxfp8", "mxfp6", "f8_block", "mx_a8w4"]
+TRAFFIC_WORKLOADS = ["i8_qkv", "mxfp4", "f8_ptpc", "mxfp8", "mxfp6", "f8_block", "mx_a8w4", "mx_a4w8"]
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
