@@ -236,6 +236,17 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr bool PAIR = ((PATH == PATH_I8 || (PATH == PATH_MX4 && BROWS == 1)) && WN == 4 && TM == 4 && TN == 2) || P6;
     constexpr int DPA = BM / 8 / NW, DPB = BN / 8 / NW;   // pair fetches per wave: A, B
     constexpr int NPF = PAIR ? DPA + DPB : 0;
+    // INT8 four-slot pair ring: a pair's fetches go out in two halves, the
+    // first in region B of the odd stage whose barrier freed its slot, the
+    // second in region A of the even stage after it, so that the data unit
+    // takes them over two regions instead of one burst (its queue, full,
+    // stalls every wave that issues a load); the pair is waited for one stage
+    // later.  (One MI355X, alternating: INT8 30000x21504x5376 2.890 -> 2.852
+    // ms, and 3.052 -> 2.998 ms on a slower box; e2m1 8192^3 0.2675 -> 0.2690
+    // ms, and unchanged with only the pair issued at J = 1 split, so it keeps
+    // whole pairs.)
+    constexpr bool PH = PAIR && !P6 && PATH == PATH_I8;
+    static_assert(!PH || NPF % 2 == 0, "pair fetches split in two halves");
     static_assert(!PAIR || (DPA * 8 * NW == BM && DPB * 8 * NW == BN), "pair fetches: whole 8-row groups");
     static_assert(!P6 || !SCL, "six-slot ring: unscaled paths only (the scale rounds are four stages)");
     // scale fetches per wave per chunk: 4 waves fetch A and B scale rows,
@@ -801,12 +812,13 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // (issue order is what the wait counts: no reordering across stages)
     fetch_scales(0);
     if constexpr (PAIR) {
-        // pairs 0 and 1 (stages 0..3; P6: pairs 0..2); wait for pair 0
-#pragma unroll
-        for (int k = 0; k < (P6 ? 3 : 2); ++k) {
+        // pairs 0 and 1 (stages 0..3; P6: pairs 0..2; PH: pair 1's first half,
+        // its second goes out in stage 0); wait for pair 0
+        static_for<0, P6 ? 3 : 2>([&](auto kc) {
+            constexpr int k = decltype(kc)::value;
             __builtin_amdgcn_sched_barrier(0);
-            static_for<0, NPF>([&](auto vc) { fetch_pair(k, vc); });
-        }
+            static_for<0, (PH && k == 1) ? NPF / 2 : NPF>([&](auto vc) { fetch_pair(k, vc); });
+        });
     } else {
 #pragma unroll
         for (int t = 0; t < (F6 ? 4 : 3); ++t) {
@@ -820,7 +832,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     }
     __builtin_amdgcn_sched_barrier(0);
     twin_sync();
-    wait_vmcnt<PAIR ? (P6 ? 2 : 1) * NPF : (F6 ? 3 : 2) * NDMA + (SPLIT ? DMA_A : 0)>();
+    wait_vmcnt<PAIR ? (P6 ? 2 * NPF : PH ? NPF / 2 : NPF) : (F6 ? 3 : 2) * NDMA + (SPLIT ? DMA_A : 0)>();
     lds_barrier();
     // stage 0's first fragments (one sub-step per stage: those its first
     // half of MFMAs uses; its region A reads the rest)
@@ -870,7 +882,10 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             constexpr int NA = (NSUB == 2) ? NQ : NQ / 2;
             constexpr int NSC = (J == 0) ? NSCD : 0;
             constexpr int VA = SPLIT ? 0 : DMA_A;
-            constexpr int V = NSC + ((F6 || PAIR) ? 0 : VA + DMA_B);   // fetches: scale chunk, A rows, B rows
+            // pairs (four-slot ring): the second half of the pair whose first
+            // half the odd stage before issued
+            constexpr int NPH = (PH && (J & 1) == 0) ? NPF / 2 : 0;
+            constexpr int V = NPH + NSC + ((F6 || PAIR) ? 0 : VA + DMA_B);   // fetches: pair half, scale chunk, A rows, B rows
             constexpr int R = (NSUB == 2) ? NIT : NIT - EARLY;
             constexpr int NR = NA > 2 ? NA - 2 : 1;        // reads go out before the last two MFMAs
             static_for<0, NA>([&](auto qc) {
@@ -889,12 +904,14 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
                     fold(std::integral_constant<int, Q - 1>());
                 static_for<V * Q / NA, V * (Q + 1) / NA>([&](auto vc) {
                     constexpr int v = decltype(vc)::value;
-                    if constexpr (v < NSC)
+                    if constexpr (v < NPH)
+                        fetch_pair((t + 2) >> 1, std::integral_constant<int, NPF / 2 + v>());
+                    else if constexpr (v < NPH + NSC)
                         fetch_scales((t >> 2) + 1);
-                    else if constexpr (v < NSC + VA)
-                        fetch_one(t + 3, I0(), std::integral_constant<int, v - NSC>());
+                    else if constexpr (v < NPH + NSC + VA)
+                        fetch_one(t + 3, I0(), std::integral_constant<int, v - NPH - NSC>());
                     else
-                        fetch_one(t + 3, I1(), std::integral_constant<int, v - NSC - VA>());
+                        fetch_one(t + 3, I1(), std::integral_constant<int, v - NPH - NSC - VA>());
                 });
                 if constexpr (FENCE)
                     __builtin_amdgcn_sched_barrier(0);
@@ -909,11 +926,12 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         // lines 3v+2, 3v+3 and the chunk went out), 3v+2 (J = 1: line 3v+3 and
         // the chunk), 3v+2 again (J = 2), or line 3v+3 and the chunk (J = 3:
         // then lines 3v+4, 3v+5).
-        // Pairs (issued in region B of odd stages: pair (t+3)/2 at stage t):
-        // stage t+1 of an even t is the second half of a pair followed by one
-        // more pair; of an odd t, the first half of the last pair issued.
-        // P6: stage t+1 is followed by two more pairs at an even t, one at an
-        // odd t.
+        // Pairs (pair (t+3)/2's first half in region B of an odd stage t, its
+        // second half in region A of stage t+1): only odd stages wait, for
+        // pair (t+1)/2, whose second half went out before stage t-1's scale
+        // chunk -- the one load that may still be in flight.  (Even stages:
+        // the count below is unused.)  P6: stage t+1 is followed by two more
+        // pairs at an even t, one at an odd t.
         constexpr int AFTER = P6 ? ((J & 1) ? 1 : 2) * NPF
                             : PAIR ? ((J & 1) ? 0 : NPF) + ((J == 0 || J == 1) ? NSCD : 0)
                             : F6   ? (J == 1 ? 1 : 2) * NDMA + (J == 3 ? 0 : NSCD)
@@ -936,7 +954,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             constexpr int QB = (NSUB == 2) ? 0 : NQ / 2;   // first MFMA of the region
             // FP6: the line whose slot the barrier just freed (line 3v + J - 1,
             // last read by stage t) is refilled with line 3v + J + 3
-            constexpr int V = PAIR ? ((J & 1) ? NPF : 0) : F6 ? (J == 0 ? 0 : NDMA) : SPLIT ? DMA_A : 0;
+            constexpr int V = PAIR ? ((J & 1) ? (PH ? NPF / 2 : NPF) : 0) : F6 ? (J == 0 ? 0 : NDMA) : SPLIT ? DMA_A : 0;
             constexpr bool CHUNK = SCL && JN == 0;         // stage t+1 starts a round
             constexpr int R = EARLY;
             constexpr int NR = NB > 2 ? NB - 2 : 1;
