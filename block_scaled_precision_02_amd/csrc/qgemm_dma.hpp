@@ -97,11 +97,19 @@ template <> struct DmaTraits<PATH_MX4H> { static constexpr int NSUB = 1; }; // A
 template <> struct DmaTraits<PATH_MX6> { static constexpr int NSUB = 1; };  // 24 bytes at 24h of a 48-byte row
 template <> struct DmaTraits<PATH_MX6E3> { static constexpr int NSUB = 1; };
 
-// B fragment of the mixed path: lane half h's 16 bytes (32 e2m1 elements) of
-// a 32-byte staged B row; VGPRs 4-7 unused.
+// Fragment of a 32-byte staged e2m1 row (the mixed paths' e2m1 operand):
+// lane half h's 16 bytes (32 elements); VGPRs 4-7 unused.  HALF < 0: the
+// one-stage layout (chunk c of row r at slot c ^ ((r >> 3) & 1) of 32 bytes);
+// else stage HALF of a pair: 64-byte rows holding the pair's two stages,
+// logical chunk q = 2 * HALF + c at slot q ^ ((r >> 2) & 3), so that 16 lanes
+// on 16 consecutive rows at one chunk cover 16 different 16-byte slots of
+// 256 bytes of banks.
+template <int HALF = -1>
 __device__ __forceinline__ i32x8 dma_frag_b32(const uint8_t *tile, int row, int h)
 {
-    const i32x4 lo = *(const i32x4 *)(tile + row * 32 + ((h ^ ((row >> 3) & 1)) << 4));
+    const int off = HALF < 0 ? row * 32 + ((h ^ ((row >> 3) & 1)) << 4)
+                             : row * 64 + (((2 * HALF + h) ^ ((row >> 2) & 3)) << 4);
+    const i32x4 lo = *(const i32x4 *)(tile + off);
     return i32x8{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
 }
 
@@ -233,8 +241,20 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // 256x256x512 on 128x128 5.4 -> 6.1 us).
     // With six slots (P6) the pairs sit in three double slots, pair k in
     // k % 3, and pair m+3 goes out at stage 2m+1, four stages before use.
-    constexpr bool PAIR = ((PATH == PATH_I8 || (PATH == PATH_MX4 && BROWS == 1)) && WN == 4 && TM == 4 && TN == 2) || P6;
-    constexpr int DPA = BM / 8 / NW, DPB = BN / 8 / NW;   // pair fetches per wave: A, B
+    // The mixed and 64-element-stage e2m1 paths pair their 256x256 tiles as
+    // well: e4m3 rows as above, 32-byte e2m1 rows as 16 rows x 64 bytes per
+    // instruction (two stages of a row: one whole 64-byte segment instead of
+    // half of one).  One MI355X, alternating: e4m3 x e2m1 8192^3 0.4227 ->
+    // 0.4100 ms, e2m1 x e4m3 0.4416 -> 0.4130, e2m1 8192x8192x8256 (tile 5)
+    // 0.5079 -> 0.4283; with a prepacked B, already whole lines, the shorter
+    // prefetch costs 0.3903 -> 0.4026 ms.  (The eight-wave e4m3 x e2m1 tile
+    // with 32x32 B scales would spill: one-stage fetches there.)
+    constexpr bool PAIR4 = (PATH == PATH_MX84 || PATH == PATH_MX48 || PATH == PATH_MX4H) && TM == 4 &&
+                           ((WN == 4 && TN == 2 && !(PATH == PATH_MX84 && BROWS == 32)) || (WN == 2 && TN == 4));
+    constexpr bool PAIR = ((PATH == PATH_I8 || (PATH == PATH_MX4 && BROWS == 1)) && WN == 4 && TM == 4 && TN == 2) ||
+                          P6 || PAIR4;
+    constexpr int PRA = A4 ? 16 : 8, PRB = B4 ? 16 : 8;    // rows per pair fetch instruction: A, B
+    constexpr int DPA = BM / PRA / NW, DPB = BN / PRB / NW;   // pair fetches per wave: A, B
     constexpr int NPF = PAIR ? DPA + DPB : 0;
     // INT8 four-slot pair ring: a pair's fetches go out in two halves, the
     // first in region B of the odd stage whose barrier freed its slot, the
@@ -247,7 +267,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // whole pairs.)
     constexpr bool PH = PAIR && !P6 && PATH == PATH_I8;
     static_assert(!PH || NPF % 2 == 0, "pair fetches split in two halves");
-    static_assert(!PAIR || (DPA * 8 * NW == BM && DPB * 8 * NW == BN), "pair fetches: whole 8-row groups");
+    static_assert(!PAIR || (DPA * PRA * NW == BM && DPB * PRB * NW == BN), "pair fetches: whole row groups");
     static_assert(!P6 || !SCL, "six-slot ring: unscaled paths only (the scale rounds are four stages)");
     // scale fetches per wave per chunk: 4 waves fetch A and B scale rows,
     // 8 waves split them (waves 0-3 A, 4-7 B)
@@ -348,17 +368,41 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // q = (i & 7) ^ ((r >> 1) & 7) whose slot is i%8.  Bit 2 of q (chunks 4..7:
     // the pair's second stage) is bit 2 of i xor bit 0 of g: a pair whose
     // second stage is past K sends those lanes out of range.
+    // 32-byte rows (A4 / B4): wave w's j-th pair fetch covers rows
+    // 16*(D*w + j) .. +15; lane i takes row r = 16g + i/4 and the logical
+    // chunk q = (i & 3) ^ ((r >> 2) & 3) (slot i%4 of the row's 64 bytes);
+    // q >= 2 (the pair's second stage) exactly when bit 1 of i differs from
+    // bit 5, whatever the group.
     unsigned pa_off[PAIR ? DPA : 1], pb_off[PAIR ? DPB : 1];
     const bool p_lb2 = (lane >> 2) & 1;
+    const bool p_hi4 = ((lane >> 1) & 1) != ((lane >> 5) & 1);
     if constexpr (PAIR) {
 #pragma unroll
         for (int j = 0; j < DPA; ++j) {
-            const int r = 8 * (DPA * wave + j) + (lane >> 3);
-            const int q = (lane & 7) ^ ((r >> 1) & 7);
-            pa_off[j] = r < rows_a ? (unsigned)(r * p.lda + 16 * q) : OOB;
+            if constexpr (A4) {
+                const int r = 16 * (DPA * wave + j) + (lane >> 2);
+                const int q = (lane & 3) ^ ((r >> 2) & 3);
+                pa_off[j] = r < rows_a ? (unsigned)(r * p.lda + 16 * q) : OOB;
+            } else {
+                const int r = 8 * (DPA * wave + j) + (lane >> 3);
+                const int q = (lane & 7) ^ ((r >> 1) & 7);
+                pa_off[j] = r < rows_a ? (unsigned)(r * p.lda + 16 * q) : OOB;
+            }
         }
 #pragma unroll
         for (int j = 0; j < DPB; ++j) {
+          if constexpr (B4) {
+            const int r = 16 * (DPB * wave + j) + (lane >> 2);
+            const int q = (lane & 3) ^ ((r >> 2) & 3);
+            // prepacked (32-row groups of 1 KB blocks, block t = stage t of
+            // the group's rows, slot p = row p/2, chunk (p & 1) ^ ((p >> 4) & 1)):
+            // chunk q of pair 0 is chunk q % 2 of row r in block q / 2
+            const int rr = r % 32, c = q & 1;
+            const unsigned packed = (unsigned)((r / 32) * gbytes + (q >> 1) * 1024 +
+                                               16 * (2 * rr + (c ^ ((rr >> 3) & 1))));
+            const bool ok = p.b_packed ? 32 * (r / 32) < rows_b : r < rows_b;
+            pb_off[j] = ok ? (p.b_packed ? packed : (unsigned)(r * p.ldb + 16 * q)) : OOB;
+          } else {
             const int r = 8 * (DPB * wave + j) + (lane >> 3);
             const int q = (lane & 7) ^ ((r >> 1) & 7);
             // prepacked B (16-row groups of 1 KB blocks, block t = stage t of
@@ -372,23 +416,26 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             // one-stage map fetches whole groups)
             const bool ok = p.b_packed ? 16 * (r / 16) < rows_b : r < rows_b;
             pb_off[j] = ok ? (p.b_packed ? packed : (unsigned)(r * p.ldb + 16 * q)) : OOB;
+          }
         }
     }
-    const unsigned pbstep = p.b_packed ? 2048u : 128u;    // B bytes per pair along K
+    const unsigned pbstep = p.b_packed ? 2048u : 2u * BSTAGE;   // B bytes per pair along K
     // The v-th pair fetch of pair k (A fetches, then B).
     auto fetch_pair = [&](int k, auto vc) {
         constexpr int v = decltype(vc)::value;
         const bool live = 2 * k < nst, live_hi = 2 * k + 1 < nst;   // uniform
         uint8_t *ds = &lds[(P6 ? k % 3 : k & 1) * 2 * STAGE_BYTES];
         const int g = v < DPA ? DPA * wave + v : DPB * wave + (v - DPA);   // fetch group (uniform)
-        const bool hi = p_lb2 != (bool)(g & 1);
+        const bool hi8 = p_lb2 != (bool)(g & 1);
         if constexpr (v < DPA) {
-            const unsigned o = (!live_hi && hi) ? OOB : pa_off[v] + (unsigned)(128 * k);
+            const bool hi = A4 ? p_hi4 : hi8;
+            const unsigned o = (!live_hi && hi) ? OOB : pa_off[v] + (unsigned)(2 * ASTAGE * k);
             dma16(make_rsrc(a_base, live ? a_range : 0u), o, ds + (DPA * wave + v) * 1024);
         } else {
             constexpr int j = v - DPA;
+            const bool hi = B4 ? p_hi4 : hi8;
             const unsigned o = (!live_hi && hi) ? OOB : pb_off[j] + pbstep * (unsigned)k;
-            dma16(make_rsrc(b_base, live ? b_range : 0u), o, ds + BM * 128 + (DPB * wave + j) * 1024);
+            dma16(make_rsrc(b_base, live ? b_range : 0u), o, ds + BM * 2 * ASTAGE + (DPB * wave + j) * 1024);
         }
     };
     // Stage (FP6: line) t goes to slot t % 4, its A rows (part 0) and B rows
@@ -586,7 +633,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         // pair layout: slot SLOT is half SLOT % 2 of double slot SLOT / 2
         constexpr int HALF = PAIR ? (SLOT & 1) : -1;
         const uint8_t *ta = PAIR ? &lds[(SLOT >> 1) * 2 * STAGE_BYTES] : &lds[SLOT * STAGE_BYTES];
-        const uint8_t *tb = ta + BM * (PAIR ? 128 : ASTAGE);
+        const uint8_t *tb = ta + BM * (PAIR ? 2 * ASTAGE : ASTAGE);
         if constexpr (F6) {
             using P0 = std::integral_constant<int, 0>;
             using PB = std::integral_constant<int, BM * DSTAGE>;
@@ -598,17 +645,17 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
                 fa[SET][k - TN] = f6_frag(slotc, s, P0(), (unsigned)(wm * TM * 32), std::integral_constant<int, k - TN>());
         } else if constexpr (k == 0) {
             if constexpr (A4)
-                fa[SET][0] = dma_frag_b32(ta, arow, h);
+                fa[SET][0] = dma_frag_b32<HALF>(ta, arow, h);
             else
                 fa[SET][0] = dma_frag<PATH, S, HALF>(ta, arow, h);
         } else if constexpr (k <= TN) {
             if constexpr (B4)
-                fb[SET][k - 1] = dma_frag_b32(tb, brow + 32 * (k - 1), h);
+                fb[SET][k - 1] = dma_frag_b32<HALF>(tb, brow + 32 * (k - 1), h);
             else
                 fb[SET][k - 1] = dma_frag<PATH, S, HALF>(tb, brow + 32 * (k - 1), h);
         } else {
             if constexpr (A4)
-                fa[SET][k - TN] = dma_frag_b32(ta, arow + 32 * (k - TN), h);
+                fa[SET][k - TN] = dma_frag_b32<HALF>(ta, arow + 32 * (k - TN), h);
             else
                 fa[SET][k - TN] = dma_frag<PATH, S, HALF>(ta, arow + 32 * (k - TN), h);
         }
