@@ -514,37 +514,46 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
                 sw_dst[e * NSCW + k] = a ? 1024 * g : SAW * RW + 1024 * (g - NWA);
             }
     }
-    // Round u's scale fetch: narrow, round u+1's 16-byte chunk of every row;
-    // wide, half u % 2 of refill u/2 + 1.
-    auto fetch_scales = [&](int u) {
+    // Fetch u of the scales (u = r + 1, issued in round r: narrow, round
+    // r+1's 16-byte chunk of every row; wide, half r % 2 of refill r/2 + 1):
+    // the k-th of the NSCD instructions a wave issues for it, which the
+    // regions spread between the MFMAs -- narrow, the wave's A rows (k = 0)
+    // and B rows (k = 1) with four waves, its A or B rows with eight; wide,
+    // the k-th of the wave's fetches of that half.
+    auto fetch_scale_one = [&](int u, auto kc) {
+        constexpr int k = decltype(kc)::value;
         if constexpr (WIDE) {
-            // round 2v-2 (u = 2v-1) fetches half 0 of refill v, round 2v-1
-            // (u = 2v) half 1; the prologue (u = 0) fetches refill 0 whole
-            const int v = (u + 1) >> 1;
+            const int v = (u + 1) >> 1, e = (u - 1) & 1;
             uint8_t *base = &lds[OPND_BYTES + (v & 1) * WIDE_BUF];
-            if (u == 0) {
-#pragma unroll
-                for (int k = 0; k < 2 * NSCW; ++k)
-                    dma16(sw_a[k] ? rsa : rsb, sw_off[k], base + sw_dst[k]);
-            } else {
-                const int e = (u - 1) & 1;
-#pragma unroll
-                for (int k = 0; k < NSCW; ++k)
-                    dma16(sw_a[e * NSCW + k] ? rsa : rsb, sw_off[e * NSCW + k] + (unsigned)(RW * v),
-                          base + sw_dst[e * NSCW + k]);
-            }
+            dma16(sw_a[e * NSCW + k] ? rsa : rsb, sw_off[e * NSCW + k] + (unsigned)(RW * v), base + sw_dst[e * NSCW + k]);
         } else if constexpr (SCL) {
             uint8_t *base = &lds[OPND_BYTES + (u & 1) * SCL_BUF];
             // four stages of scales: 16 bytes (e2m1) or 8 bytes (e4m3, blockscale) per row
             const unsigned kb = (unsigned)((PATH == PATH_MX4 ? 16 : 8) * u);
             if constexpr (NW == 4) {
-                dma16(rsa, sa_fo + kb, base + 64 * 16 * wave);
-                dma16(rsb, sb_fo + kb, base + SA_ROWS * 16 + (BROWS == 1 ? 64 * 16 * wave : 0));
+                if constexpr (k == 0)
+                    dma16(rsa, sa_fo + kb, base + 64 * 16 * wave);
+                else
+                    dma16(rsb, sb_fo + kb, base + SA_ROWS * 16 + (BROWS == 1 ? 64 * 16 * wave : 0));
             } else if (wave < 4) {
                 dma16(rsa, sa_fo + kb, base + 64 * 16 * wave);
             } else {
                 dma16(rsb, sb_fo + kb, base + SA_ROWS * 16 + (BROWS == 1 ? 64 * 16 * (wave - 4) : 0));
             }
+        }
+    };
+    // The prologue's scale fetches: round 0's chunk (narrow); refill 0 whole,
+    // both halves (wide).  Round r's own fetches (u = r + 1: narrow, round
+    // r+1's chunk; wide, half r % 2 of refill r/2 + 1, so that round 2v-2
+    // fetches half 0 of refill v and round 2v-1 half 1) go out one
+    // instruction at a time between the MFMAs.
+    auto fetch_scales0 = [&]() {
+        if constexpr (WIDE) {
+#pragma unroll
+            for (int k = 0; k < 2 * NSCW; ++k)
+                dma16(sw_a[k] ? rsa : rsb, sw_off[k], &lds[OPND_BYTES] + sw_dst[k]);
+        } else if constexpr (SCL) {
+            static_for<0, NSCD>([&](auto kc) { fetch_scale_one(0, kc); });
         }
     };
 
@@ -857,7 +866,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     // (issue order is what the wait counts: no reordering across stages)
-    fetch_scales(0);
+    fetch_scales0();
     if constexpr (PAIR) {
         // pairs 0 and 1 (stages 0..3; P6: pairs 0..2; PH: pair 1's first half,
         // its second goes out in stage 0); wait for pair 0
@@ -959,7 +968,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
                     if constexpr (v < NPH)
                         fetch_pair((t + 2) >> 1, std::integral_constant<int, NPF / 2 + v>());
                     else if constexpr (v < NPH + NSC)
-                        fetch_scales((t >> 2) + 1);
+                        fetch_scale_one((t >> 2) + 1, std::integral_constant<int, v - NPH>());
                     else if constexpr (v < NPH + NSC + VA)
                         fetch_one(t + 3, I0(), std::integral_constant<int, v - NPH - NSC>());
                     else
@@ -1034,7 +1043,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
                     else if constexpr (PAIR && (J & 1))
                         fetch_pair((t + 3) >> 1, vc);
                     else if constexpr (PAIR)
-                        fetch_scales((t >> 2) + 1);
+                        fetch_scale_one((t >> 2) + 1, vc);
                     else if constexpr (!F6)
                         fetch_one(t + 4, I0(), vc);
                     else if constexpr (v < DMA_A)
