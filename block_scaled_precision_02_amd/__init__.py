@@ -79,8 +79,8 @@ def lib():
 
 def declare(L):
     """Declare the argument and return types of every exported function on a
-    loaded copy of the library (this build's, or another build of the same
-    sources) and return it."""
+    loaded copy of the library (libqgemm.so, or the conservative-sync twin
+    built from the same sources) and return it."""
     st = ctypes.c_int
     L.qgemm_i8_rowwise.restype = st
     L.qgemm_i8_rowwise.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
