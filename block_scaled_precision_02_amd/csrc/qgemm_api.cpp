@@ -280,7 +280,7 @@ qgemm_status launch(F &&f)
 // their 64-byte stages (a last round of fewer than four is masked).  For MX,
 // a round reads 16 bytes of each scale row from byte 16u (e2m1) or 8u (e4m3),
 // from the row's start rounded down to a dword (a whole dword unless K % 128
-// == 64), and the caller's scale arrays aligned to 16 / 8 bytes (svec: the
+// != 0), and the caller's scale arrays aligned to 16 / 8 bytes (svec: the
 // caller's check).
 //
 // The masked last round keeps word 0 of a round's scale chunk live and
@@ -288,11 +288,13 @@ qgemm_status launch(F &&f)
 // e2m1 (one stage per word) needs K % 128 for whole 64-byte stages, the
 // blockscale and 6-bit paths K % 128 by their blocks and rows.  The
 // e4m3-staged MX paths (e4m3, and both mixed pairings: 64 K elements a stage,
-// two stages per word) take any K % 64: at K % 128 == 64 their scale rows
-// start 2 bytes into a dword on every other row and the last live word may
-// be half past K, which the LDS-fetch kernel's SU form handles (fetches from the
-// dword-aligned start, half-word masking).  dma_k_ok is the one place that
-// rule lives; every LDS-fetch path takes it.
+// two stages per word) take any K % 32: at K % 128 != 0 their scale rows
+// start off dword boundaries, the last live word may end part way past K
+// and, at K % 64 == 32, the last stage half way, which the LDS-fetch
+// kernel's SU form handles (fetches from the start rounded down to a dword,
+// byte masking of the scale words, the half stage's other chunks fetched as
+// zeros).  dma_k_ok is the one place that rule lives; every LDS-fetch path
+// takes it.
 bool dma_k_ok(int path, int64_t K)
 {
     switch (path) {
@@ -300,16 +302,17 @@ bool dma_k_ok(int path, int64_t K)
     case 1: return K % 64 == 0;    // int8 / e4m3 bytes: whole 64-byte stages
     case 2:                        // e4m3 MX
     case 5:                        // mixed MX, e4m3 A x e2m1 B
-    case 8: return K % 64 == 0;    // mixed MX, e2m1 A x e4m3 B
+    case 8: return K % 32 == 0;    // mixed MX, e2m1 A x e4m3 B
     default: return K % 128 == 0;  // e2m1, blockscale, 6-bit: whole scale words per round
     }
 }
 
 bool dma_eligible(int path, int64_t kbytes, int64_t K, bool svec)
 {
-    if (path == 2 || path == 3)
-        return svec && kbytes % 64 == 0 && dma_k_ok(path, K);
-    return kbytes % 64 == 0 && dma_k_ok(path, K);
+    if ((path == 2 || path == 3) && !svec)
+        return false;
+    const bool e4m3_staged = path == 2 || path == 5 || path == 8;   // K % 32: the SU form
+    return (e4m3_staged || kbytes % 64 == 0) && dma_k_ok(path, K);
 }
 
 // When K fits, the table's tile edge runs in an LDS-fetch kernel: 256 as the
@@ -407,8 +410,8 @@ int pick_tile_mx48(Shape s)
     return select_tile_impl(2, s.M, s.N) == 0 ? DMA_TILE : DMA128_TILE;
 }
 
-// e2m1 MX at K % 128 == 64 (K/32 = 4n + 2): the LDS-fetch kernel in
-// 64-element stages -- the eight-wave tile 5 where the table picks 256x256
+// e2m1 MX at K % 128 != 0 (K/32 not a multiple of 4): the LDS-fetch kernel
+// in 64-element stages -- the eight-wave tile 5 where the table picks 256x256
 // (one MI355X, 8192x8192x8256: 0.505 ms against 0.551 on tile 4 and 0.799 on
 // the register-staged tile), else 7 (forced: 4, 5, 7) -- unless the call
 // takes the small-M kernel (M <= 16, or forced 8 / 9) or a forced
@@ -496,7 +499,7 @@ int qgemm_select_tile(int path, int64_t M, int64_t N, int64_t K)
     const int64_t kbytes = path == 3 ? K / 2 : K;
     const int prev = g_forced_tile;
     g_forced_tile = -1;
-    int t = (path == 3 && K % 128 == 64) ? pick_tile_mx4h(Shape{M, N, K}) : -1;
+    int t = (path == 3 && K % 128 != 0) ? pick_tile_mx4h(Shape{M, N, K}) : -1;
     if (t < 0)
         t = pick_tile(path, Shape{M, N, K}, kbytes, true, true);   // scales assumed aligned, bf16 out
     g_forced_tile = prev;
@@ -715,15 +718,17 @@ static qgemm_status mx_common(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes
     // and the scale arrays themselves start aligned.  The LDS-fetch kernel
     // reads 16 (e2m1) or 8 (e4m3) bytes of each scale row per round: the
     // arrays must be aligned to that.
+    // sdma: the scales fit the LDS-fetch kernel (e4m3 at any K/32: its SU
+    // form; the register-staged tile then loads scale bytes)
     const int wb = (fmt == QGEMM_MX_E2M1) ? 4 : 2;
     const bool svec = ((K / 32) % wb == 0) && aligned(scale_a, wb) && aligned(scale_b, wb);
     const unsigned chunk_align = (fmt == QGEMM_MX_E2M1) ? 16 : 8;
-    const bool svec16 = svec && aligned(scale_a, chunk_align) && aligned(scale_b, chunk_align);
-    if (packed && (row_bytes % 256 || !dma_eligible(path, row_bytes, K, svec16)))
+    const bool sdma = (svec || fmt == QGEMM_MX_E4M3) && aligned(scale_a, chunk_align) && aligned(scale_b, chunk_align);
+    if (packed && (row_bytes % 256 || !dma_eligible(path, row_bytes, K, sdma)))
         return fail(QGEMM_ERR_BAD_LAYOUT, "a prepacked MX B needs K/32 a multiple of 16 (e2m1) or 8 (e4m3) and scale "
                                           "arrays aligned to 16 (e2m1) or 8 (e4m3) bytes");
     TRY(check_device());
-    if (fmt == QGEMM_MX_E2M1 && !packed && K % 128 == 64 && aligned(scale_a, 8) && aligned(scale_b, 8)) {
+    if (fmt == QGEMM_MX_E2M1 && !packed && K % 128 != 0 && aligned(scale_a, 8) && aligned(scale_b, 8)) {
         const int t4 = pick_tile_mx4h(s);
         if (t4 >= 0) {
             Params p = base_params(A, lda_bytes, B, ldb_bytes, C, ldc, s, K, t4);   // kbytes: K, as for e4m3
@@ -734,7 +739,7 @@ static qgemm_status mx_common(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes
             return launch([&] { return launch_mx4h(t4, bias != nullptr, (int)b_layout, p, (hipStream_t)stream); });
         }
     }
-    const int tile = packed ? pick_tile_packed(path, s, row_bytes, true) : pick_tile(path, s, row_bytes, svec16, true);
+    const int tile = packed ? pick_tile_packed(path, s, row_bytes, true) : pick_tile(path, s, row_bytes, sdma, true);
     Params p = base_params(A, lda_bytes, B, packed ? row_bytes : ldb_bytes, C, ldc, s, row_bytes, tile);
     p.b_packed = packed;
     TRY(check_grid(p));
@@ -772,7 +777,7 @@ static qgemm_status mx_mixed_common(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, cons
     TRY(check_shape(s, false));
     if (!dma_k_ok(5, K) || (packed && K % 256))
         return fail(QGEMM_ERR_BAD_SHAPE, "K=%lld: %s needs K a multiple of %d", (long long)K, pair,
-                    packed ? 256 : 64);
+                    packed ? 256 : 32);
     if (M == 0 || N == 0)
         return QGEMM_OK;
     TRY(check_operand("A", A, lda_bytes, a4 ? K / 2 : K));

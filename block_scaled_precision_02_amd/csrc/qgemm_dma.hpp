@@ -48,9 +48,11 @@
 //
 // Requirements (checked on the host, which otherwise uses qgemm_kernel):
 // K bytes a whole number of stages (64 bytes), and for the scaled paths scale
-// rows of whole dwords (K % 128).  A last round of fewer than four stages
-// fetches the rest through descriptors of empty range (zeros) and replaces
-// their scale words by neutral ones.  Rows past M / N are fetched from out of
+// rows of whole dwords (K % 128) -- except in the SU form of the e4m3-staged
+// MX paths, which takes any K % 32 (a last half stage, scale rows off dword
+// boundaries).  A last round of fewer than four stages fetches the rest
+// through descriptors of empty range (zeros) and replaces their scale words
+// by neutral ones.  Rows past M / N are fetched from out of
 // range offsets; whatever lands in LDS for them only reaches output rows and
 // columns that are never stored.
 #pragma once
@@ -151,9 +153,10 @@ __device__ __forceinline__ typename PathTraits<PATH>::Frag dma_frag(const uint8_
 
 // WN = 2: 4 waves (one per SIMD) of 128x128; WN = 4: 8 waves (two per
 // SIMD, so one can issue MFMAs while the other waits) of 128x64.
-// SU (the e4m3-staged MX paths at K % 128 == 64): scale rows of K/32 bytes,
-// every other one starting 2 bytes into a dword.  (One kernel template: the
-// body moved into a device function called from two kernels spilled.)
+// SU (the e4m3-staged MX paths at K % 128 != 0): scale rows of K/32 bytes
+// that start off dword boundaries, and at K % 64 == 32 a last stage of 32 K
+// elements.  (One kernel template: the body moved into a device function
+// called from two kernels spilled.)
 template <int PATH, int WN, int TM, int TN, bool BIAS, int BROWS, int OUT, bool SU = false>
 __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
 {
@@ -212,9 +215,9 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
                           NSLOT * STAGE_BYTES + 2 * WIDE_BUF + (PRM ? PRM_BYTES : 0) <= 160 * 1024;
     constexpr int NSCW = NWT / (G * NW);                  // per wave and round
     // Unaligned scale rows (SU): every chunk is fetched from its row's
-    // dword-aligned start rounded down, m = 2 bytes early on the rows where
-    // the row starts 2 bytes into a dword; the narrow chunk's 16 bytes still
-    // hold the round's 8 from byte m, which the reader shifts out.
+    // start rounded down to a dword, m = 1..3 bytes early on the rows that
+    // start inside one; the narrow chunk's 16 bytes still hold the round's 8
+    // from byte m, which the reader shifts out.
     static_assert(!SU || (MX && !F6 && RB == 8 && !WIDE), "unaligned scale rows: e4m3-staged MX, narrow chunks");
     constexpr int SCL_BYTES = SCL ? 2 * (WIDE ? WIDE_BUF : SCL_BUF) : 0;
     constexpr int NQ = TM * TN;
@@ -302,12 +305,13 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     const int m0 = tm * BM, n0 = tn * BN;
     const int rows_a = min(BM, p.M - m0), rows_b = min(BN, p.N - n0);
 
-    // K is a whole number of stages; the last round may hold fewer than four.
-    // Its stages at or past K are fetched through descriptors of empty range
-    // (zeros land in LDS, whatever the offset), so their MFMAs add nothing.
-    // FP6: nst counts the 48-byte stages that the MFMAs take, nfetch the
-    // 64-byte lines that hold them (the last one possibly half past K).
-    const int nst = F6 ? p.K / 64 : p.kbytes / DSTAGE;
+    // K is a whole number of stages (SU: possibly ending in half a stage);
+    // the last round may hold fewer than four.  Its stages at or past K are
+    // fetched through descriptors of empty range (zeros land in LDS, whatever
+    // the offset), so their MFMAs add nothing.  FP6: nst counts the 48-byte
+    // stages that the MFMAs take, nfetch the 64-byte lines that hold them
+    // (the last one possibly half past K).
+    const int nst = F6 ? p.K / 64 : SU ? (p.kbytes + DSTAGE - 1) / DSTAGE : p.kbytes / DSTAGE;
     const int nfetch = F6 ? (p.kbytes + DSTAGE - 1) / DSTAGE : nst;
     const uint8_t *const a_base = p.A + (int64_t)m0 * p.lda;
     const int kbytes_a = A4 ? p.kbytes / 2 : p.kbytes;   // (A4 / B4: p.kbytes is K, a byte per element)
@@ -420,6 +424,24 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         }
     }
     const unsigned pbstep = p.b_packed ? 2048u : 2u * BSTAGE;   // B bytes per pair along K
+    // SU with K % 64 == 32: the last stage holds 32 K elements -- the first
+    // 32 bytes of a 64-byte stage row, the first 16 of a 32-byte one.  A
+    // fetch whose lane's 16-byte chunk starts at or past its row's K bytes
+    // goes out of range (zeros).  The chunk's column (bytes from the start of
+    // the stage, or of the pair) is one per lane for every fetch of a map:
+    // (i & 3) ^ ((i >> 4) & 3) chunks for one-stage 64-byte rows and pair
+    // 32-byte rows, (i & 1) ^ ((i >> 4) & 1) for one-stage 32-byte rows, and
+    // for pair 64-byte rows (i & 7) ^ ((i >> 4) & 3), bit 2 flipped in odd
+    // groups -- the maps above with their row terms worked out.
+    const int col64 = 16 * ((lane & 3) ^ ((lane >> 4) & 3));
+    const int col32 = 16 * ((lane & 1) ^ ((lane >> 4) & 1));
+    const int colp = 16 * ((lane & 7) ^ ((lane >> 4) & 3));
+    auto kcut = [&](unsigned o, int col, int k0, int row_bytes) -> unsigned {
+        if constexpr (SU)
+            return col < row_bytes - k0 ? o : OOB;
+        else
+            return o;
+    };
     // The v-th pair fetch of pair k (A fetches, then B).
     auto fetch_pair = [&](int k, auto vc) {
         constexpr int v = decltype(vc)::value;
@@ -429,12 +451,17 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         const bool hi8 = p_lb2 != (bool)(g & 1);
         if constexpr (v < DPA) {
             const bool hi = A4 ? p_hi4 : hi8;
-            const unsigned o = (!live_hi && hi) ? OOB : pa_off[v] + (unsigned)(2 * ASTAGE * k);
+            const int k0 = 2 * ASTAGE * k;
+            const unsigned o = SU ? kcut(pa_off[v] + (unsigned)k0, A4 ? col64 : colp ^ ((g & 1) << 6), k0, kbytes_a)
+                                  : (!live_hi && hi) ? OOB : pa_off[v] + (unsigned)k0;
             dma16(make_rsrc(a_base, live ? a_range : 0u), o, ds + (DPA * wave + v) * 1024);
         } else {
             constexpr int j = v - DPA;
             const bool hi = B4 ? p_hi4 : hi8;
-            const unsigned o = (!live_hi && hi) ? OOB : pb_off[j] + pbstep * (unsigned)k;
+            // (SU: B row-major, a pair 2 * BSTAGE bytes of the row)
+            const int k0 = (int)pbstep * k;
+            const unsigned o = SU ? kcut(pb_off[j] + (unsigned)k0, B4 ? col64 : colp ^ ((g & 1) << 6), k0, kbytes_b)
+                                  : (!live_hi && hi) ? OOB : pb_off[j] + (unsigned)k0;
             dma16(make_rsrc(b_base, live ? b_range : 0u), o, ds + BM * 2 * ASTAGE + (DPB * wave + j) * 1024);
         }
     };
@@ -448,12 +475,14 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base, live ? a_range : 0u);
 #pragma unroll
             for (int j = 0; j < DMA_A; ++j)
-                dma16(ra, a_off[j] + kb, slot + (DMA_A * wave + j) * 1024);
+                dma16(ra, kcut(a_off[j] + kb, A4 ? col32 : col64, (int)kb, kbytes_a),
+                      slot + (DMA_A * wave + j) * 1024);
         } else {
             const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base, live ? b_range : 0u);
 #pragma unroll
             for (int j = 0; j < DMA_B; ++j)
-                dma16(rb, b_off[j] + kbb, slot + BM * ASTAGE + (DMA_B * wave + j) * 1024);
+                dma16(rb, kcut(b_off[j] + kbb, B4 ? col32 : col64, (int)kbb, kbytes_b),
+                      slot + BM * ASTAGE + (DMA_B * wave + j) * 1024);
         }
     };
 
@@ -465,10 +494,13 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
         uint8_t *slot = &lds[(t & 3) * STAGE_BYTES];
         if constexpr (decltype(partc)::value == 0) {
             const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base, live ? a_range : 0u);
-            dma16(ra, a_off[j] + (unsigned)(t * ASTAGE), slot + (DMA_A * wave + j) * 1024);
+            const int k0 = t * ASTAGE;
+            dma16(ra, kcut(a_off[j] + (unsigned)k0, A4 ? col32 : col64, k0, kbytes_a), slot + (DMA_A * wave + j) * 1024);
         } else {
             const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base, live ? b_range : 0u);
-            dma16(rb, b_off[j] + (unsigned)t * bstep, slot + BM * ASTAGE + (DMA_B * wave + j) * 1024);
+            const int k0 = (int)bstep * t;
+            dma16(rb, kcut(b_off[j] + (unsigned)k0, B4 ? col32 : col64, k0, kbytes_b),
+                  slot + BM * ASTAGE + (DMA_B * wave + j) * 1024);
         }
     };
 
@@ -479,11 +511,11 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     unsigned sa_fo = OOB, sb_fo = OOB;
     if constexpr (SCL) {
         // Ranges in whole dwords: a dword the range ends inside reads as
-        // zero, and under SU (K/32 = 4n + 2) an odd row count ends the tile's
-        // last scale row half way into one.  Such a range ends the array
-        // (the last tile of A, or of B's scale rows), and the dword's other
-        // 2 bytes lie in the same page; they land past the row's K/32 scales,
-        // where the round's masking replaces them.
+        // zero, and under SU (K/32 not a multiple of 4) the tile's last
+        // scale row may end inside one.  Such a range ends the array (the
+        // last tile of A, or of B's scale rows), and the dword's other bytes
+        // lie in the same page; they land past the row's K/32 scales, where
+        // the round's masking replaces them.
         rsa = make_rsrc(p.mx_sa + (int64_t)m0 * p.kblocks, (uint32_t)((rows_a * p.kblocks + 3) & ~3));
         const int srows_b = (rows_b + BROWS - 1) / BROWS;
         rsb = make_rsrc(p.mx_sb + (int64_t)(n0 / BROWS) * p.kblocks, (uint32_t)((srows_b * p.kblocks + 3) & ~3));
@@ -725,12 +757,13 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             constexpr unsigned NEUTRAL = BS ? 0u : 0x7F7F7F7Fu;
             static_assert(4 % SCW == 0, "a scale word covers whole stages");
             if constexpr (SU) {
-                // K % 128 == 64: the round's last live word may hold one
-                // stage of data (bytes 0, 1) and one past K (bytes 2, 3)
+                // K/32 not a multiple of 4: the round's last live word ends
+                // in K/32 mod 4 live bytes (byte b of word w: K block
+                // 2t + 4w + b); its other bytes are past K
 #pragma unroll
                 for (int w = 0; w < SCW; ++w) {
-                    const bool past = t + 2 * w >= nst, past_hi = t + 2 * w + 1 >= nst;
-                    const unsigned keep = past ? 0u : past_hi ? 0xFFFFu : ~0u;
+                    const int live = p.kblocks - 2 * t - 4 * w;   // uniform
+                    const unsigned keep = live >= 4 ? ~0u : live <= 0 ? 0u : (1u << (8 * live)) - 1u;
                     const unsigned fill = NEUTRAL & ~keep;
 #pragma unroll
                     for (int i = 0; i < TM; ++i) cra[i][w] = (cra[i][w] & keep) | fill;
@@ -1067,9 +1100,11 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     };
 
     // The host guarantees a whole number of stages (kbytes % 64 == 0; for the
-    // scaled paths, of the stages that one scale word covers, except under
-    // SU, where the last live word may be half past K; FP6: K % 128 == 0).  Fetches run three stages (FP6: two to three lines) ahead, into
-    // stages past K that are never multiplied or, in a partial last round,
+    // scaled paths, of the stages that one scale word covers; FP6: K % 128 ==
+    // 0), except under SU, where the last stage may end half way (its other
+    // half fetched as zeros) and the last live word part way past K.
+    // Fetches run three stages (FP6: two to three lines) ahead, into stages
+    // past K that are never multiplied or, in a partial last round,
     // multiplied as zeros (FP6: skipped).
     if constexpr (P6) {
         for (int t = 0; t < nst; t += 6)

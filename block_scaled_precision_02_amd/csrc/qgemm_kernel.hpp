@@ -57,8 +57,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // PATH_MX48: MX with e2m1 A and e4m3 B (the mixed path with the operands'
 // formats the other way round); LDS-fetch kernel only.
 // PATH_MX4H: MX e2m1 on both operands in stages of 64 K elements (32-byte
-// stage rows, as the mixed paths' e2m1 operand), for K % 128 == 64, where
-// PATH_MX4's 64-byte stages would leave half a stage; LDS-fetch kernel only.
+// stage rows, as the mixed paths' e2m1 operand), for K % 128 != 0, where
+// PATH_MX4's 64-byte stages would leave part of a stage; LDS-fetch kernel
+// only.
 enum Path { PATH_I8 = 0, PATH_F8 = 1, PATH_MX8 = 2, PATH_MX4 = 3, PATH_F8B = 4, PATH_MX84 = 5, PATH_MX6 = 6,
             PATH_MX6E3 = 7, PATH_MX48 = 8, PATH_MX4H = 9 };
 enum OutKind { OUT_BF16 = 0, OUT_I32 = 1 };

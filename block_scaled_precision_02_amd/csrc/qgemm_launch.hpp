@@ -13,7 +13,7 @@ namespace qgemm {
 //   3 -> 192x192, 2x2 waves of 96x96 (144 accumulators)
 //   4 -> 256x256 as tile 0, operands fetched straight into LDS (qgemm_dma.hpp);
 //        needs K bytes % 64 == 0 and, for the scaled paths, K % 128 == 0 (the
-//        e4m3-staged MX paths: K % 64, the SU form at K % 128 == 64)
+//        e4m3-staged MX paths: K % 32, the SU form at K % 128 != 0)
 //        with aligned scales
 //   5 -> 256x256 fetched straight into LDS as tile 4, 2x4 waves of 128x64 (two
 //        waves per SIMD); same requirements
@@ -53,8 +53,9 @@ hipError_t launch_variant(const Params &p, hipStream_t s)
     return hipGetLastError();
 }
 
-// The e4m3-staged MX paths at K % 128 == 64 (scale rows of K/32 bytes, every
-// other one starting 2 bytes into a dword): tiles 4, 5, 7, and 6 for e4m3.
+// The e4m3-staged MX paths at K % 128 != 0 (scale rows of K/32 bytes off
+// dword boundaries; at K % 64 == 32 a last half stage): tiles 4, 5, 7, and 6
+// for e4m3.
 template <int PATH, bool BIAS, int BROWS, int OUT = OUT_BF16>
 hipError_t launch_dma_su(int tile, const Params &p, hipStream_t s)
 {
@@ -93,16 +94,16 @@ hipError_t launch_tile(int tile, const Params &p, hipStream_t s)
     case DMA8_TILE:
     case DMA192_TILE:
     case DMA128_TILE:
+        if constexpr (PATH == PATH_MX8) {
+            if (p.kblocks % 4 != 0)   // K % 128 != 0: scale rows off dword boundaries (any K/32)
+                return launch_dma_su<PATH, BIAS, BROWS, OUT>(tile, p, s);
+        }
         if constexpr (PATH == PATH_MX8 || PATH == PATH_MX4) {
             if (!SVEC)
                 return hipErrorInvalidValue;
         }
         {
             const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(tile_threads(tile));
-            if constexpr (PATH == PATH_MX8) {
-                if (p.kblocks % 4 != 0)   // K % 128 == 64: scale rows off dword boundaries
-                    return launch_dma_su<PATH, BIAS, BROWS, OUT>(tile, p, s);
-            }
             if (tile == DMA_TILE)
                 hipLaunchKernelGGL((qgemm_dma_kernel<PATH, 2, 4, 4, BIAS, BROWS, OUT>), grid, block, 0, s, p);
             else if (tile == DMA8_TILE)
@@ -144,7 +145,7 @@ hipError_t launch_f8b(int tile, bool bias, const Params &p, hipStream_t s);
 hipError_t launch_mx84(int tile, bool bias, int brows, const Params &p, hipStream_t s);
 // MX with e2m1 A and e4m3 B: tiles 4, 5, 7 (same requirements as MX on them).
 hipError_t launch_mx48(int tile, bool bias, int brows, const Params &p, hipStream_t s);
-// MX e2m1 at K % 128 == 64 in 64-element stages: tiles 4, 5, 7 (K/32 % 4 == 2).
+// MX e2m1 at K % 128 != 0 in 64-element stages: tiles 4, 5, 7 (K/32 % 4 != 0).
 hipError_t launch_mx4h(int tile, bool bias, int brows, const Params &p, hipStream_t s);
 // MX with 6-bit elements (E2M3, or E3M2 when e3m2): tiles 4, 5, 7 (K % 128 == 0
 // and 8-byte aligned scale arrays, as e4m3 MX on them).

@@ -1,7 +1,8 @@
-// MX e2m1 at K % 128 == 64: both operands staged 64 K elements (32 bytes a
-// row) at a time, as the mixed paths stage their e2m1 operand, so that K/64
-// stages are whole (the e2m1 kernel's 64-byte stages would leave half of
-// one); scale rows of K/32 = 4n + 2 bytes take the unaligned-scale-row form.
+// MX e2m1 at K % 128 != 0: both operands staged 64 K elements (32 bytes a
+// row) at a time, as the mixed paths stage their e2m1 operand (the e2m1
+// kernel's 64-byte stages would leave part of one); scale rows of K/32 bytes
+// off dword boundaries, and at K % 64 == 32 a last half stage, take the SU
+// form.
 // Tiles 4, 5 and 7 (the 192x192 tile's rows are not a whole number of
 // 32-row fetches per wave).
 #include "qgemm_launch.hpp"

@@ -9,7 +9,7 @@ namespace qgemm {
 template <bool BIAS, int BROWS>
 static hipError_t mx84_tile(int tile, const Params &p, hipStream_t s)
 {
-    if (is_dma_tile(tile) && p.kblocks % 4 != 0)   // K % 128 == 64
+    if (is_dma_tile(tile) && p.kblocks % 4 != 0)   // K % 128 != 0
         return launch_dma_su<PATH_MX84, BIAS, BROWS>(tile, p, s);
     const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(tile_threads(tile));
     switch (tile) {

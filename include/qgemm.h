@@ -167,10 +167,10 @@ qgemm_status qgemm_f8_blockscale(const uint8_t *A, int64_t lda, const uint8_t *B
  * then f = acc, [+ bias], bf16 round-nearest-even.  Scale code 255 is NaN.
  * The 6-bit formats need K a multiple of 128 (QGEMM_ERR_BAD_SHAPE) and 8-byte
  * aligned scale arrays (QGEMM_ERR_BAD_LAYOUT); qgemm_mx_prepacked does not take
- * them (QGEMM_ERR_BAD_FORMAT).  e4m3 and e2m1 take any K a multiple of 32:
- * e4m3 runs the LDS-fetch tiles where K % 64 == 0, e2m1 where K % 128 == 0
- * and, in stages of 64 elements (tiles 4, 5, 7), where K % 128 == 64 with
- * 8-byte aligned scale arrays; other K run the register-staged tile. */
+ * them (QGEMM_ERR_BAD_FORMAT).  e4m3 and e2m1 take any K a multiple of 32,
+ * and run the LDS-fetch tiles with 8-byte aligned scale arrays: e4m3 at any
+ * such K, e2m1 where K % 128 == 0 and, in stages of 64 elements (tiles 4, 5,
+ * 7; M > 16), at the other K; otherwise the register-staged tile. */
 qgemm_status qgemm_mx(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const void *B,
                       int64_t ldb_bytes, const uint8_t *scale_a, const uint8_t *scale_b,
                       qgemm_mx_bscale b_layout, const uint16_t *bias, uint16_t *C, int64_t ldc,
@@ -187,7 +187,7 @@ qgemm_status qgemm_mx(qgemm_mx_fmt fmt, const void *A, int64_t lda_bytes, const 
  *   e2m1 A, e4m3 B: the same with the operands' formats swapped (lda_bytes
  *            >= K/2, ldb_bytes >= K); every M runs an LDS-fetch tile (4, 5
  *            or 7; no small-M form).
- * Either needs K a multiple of 64 (QGEMM_ERR_BAD_SHAPE) and 8-byte aligned
+ * Either needs K a multiple of 32 (QGEMM_ERR_BAD_SHAPE) and 8-byte aligned
  * scale arrays (QGEMM_ERR_BAD_LAYOUT).  Numerics as qgemm_mx. */
 qgemm_status qgemm_mx_mixed(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *A, int64_t lda_bytes,
                             const void *B, int64_t ldb_bytes, const uint8_t *scale_a, const uint8_t *scale_b,
@@ -330,7 +330,7 @@ const char *qgemm_status_string(qgemm_status status);
 
 /* Tile variant the host-side table picks for a problem (pure host logic, no
  * HIP call; for MX, assuming 16-byte-aligned scale arrays).  path: 0 int8,
- * 1 fp8, 2 MX e4m3, 3 MX e2m1 (at K % 128 == 64 and M > 16: tile 5 where
+ * 1 fp8, 2 MX e4m3, 3 MX e2m1 (at K % 128 != 0 and M > 16: tile 5 where
  * the table picks 256x256, else 7), 4 fp8 blockscale (tile 8 for M <= 16, else
  * tile 10 when its grid of 256x128 tiles fills the 256 CUs at least once,
  * else tile 7), 5 MX e4m3 A with e2m1 B (tile 8 for M <= 16, else tile 4
@@ -350,9 +350,8 @@ const char *qgemm_status_string(qgemm_status status);
  *  10: 256 rows x 128 columns, fp8 blockscale only
  * Tiles 4-7 need K bytes a multiple of 64 (whole stages; a last round of
  * fewer than four is masked) and, for e2m1 MX, K % 128 (e4m3 MX and the mixed
- * pairs: K % 64), with scale arrays aligned to 16 (e2m1) or 8 (e4m3) bytes;
- * where these
- * hold, the table's 256x256 choice runs as tile 4 (mixed and 6-bit MX, and
+ * pairs: any K % 32, e2m1 at K % 128 != 0 as above), with scale arrays
+ * aligned to 16 (e2m1) or 8 (e4m3) bytes; where these hold, the table's 256x256 choice runs as tile 4 (mixed and 6-bit MX, and
  * INT8 on a prepacked B) or 5 (the others), 192x192 as tile 6 and 128x128 as tile 7.  Calls with M <= 64 take tile 8
  * (M <= 16) or 9 (INT8 and FP8 only: MX takes the small-M kernel up to
  * M = 16). */

@@ -151,10 +151,10 @@ def test_tile_table():
     assert L.qgemm_select_tile(0, 30000, 21504, 5440) == 5      # 85 stages: a partial last round
     assert L.qgemm_select_tile(3, 8192, 8192, 8192) == 5        # 1024 tiles = 4 rounds
     assert L.qgemm_select_tile(2, 16384, 7168, 2048) == 5       # 1792 tiles = 7 rounds
-    assert L.qgemm_select_tile(2, 16384, 7168, 2016) == 0       # K/32 = 63: scale rows not whole dwords
+    assert L.qgemm_select_tile(2, 16384, 7168, 2016) == 5       # K/32 = 63: the unaligned-scale-row form
     assert L.qgemm_select_tile(2, 16384, 7168, 2176) == 5       # K/32 = 68: a partial last round
     assert L.qgemm_select_tile(3, 8192, 8192, 8320) == 5        # e2m1, 65 stages
-    assert L.qgemm_select_tile(2, 16384, 7168, 2080) == 0       # K/32 = 65
+    assert L.qgemm_select_tile(2, 16384, 7168, 2080) == 5       # K/32 = 65: a last half stage
     # 144 tiles of 256x256 leave 112 CUs idle; 242 tiles of 192x192 fill one
     # round (LDS-fetch form when K fits, register-staged otherwise)
     assert L.qgemm_select_tile(1, 4096, 2112, 7168) == 6
@@ -168,7 +168,8 @@ def test_tile_table():
     assert L.qgemm_select_tile(3, 8192, 8192, 8256) == 5        # e2m1, K % 128 == 64
     assert L.qgemm_select_tile(3, 1024, 1024, 2880) == 7        # 16 tiles of 256: the table's 128
     assert L.qgemm_select_tile(3, 16, 8192, 2880) == 8          # small M: the small-M kernel
-    assert L.qgemm_select_tile(3, 8192, 8192, 8224) == 0        # K % 128 == 32: register-staged
+    assert L.qgemm_select_tile(3, 8192, 8192, 8224) == 5        # K % 128 == 32: 64-element stages too
+    assert L.qgemm_select_tile(3, 1024, 1024, 2912) == 7        # K % 128 == 96
     # 6-bit MX: the LDS-fetch kernel only -- 256x256 (the four-wave tile 4) or 128x128 (7)
     assert L.qgemm_select_tile(6, 8192, 8192, 8192) == 4
     assert L.qgemm_select_tile(7, 8192, 8192, 8192) == 4
@@ -349,9 +350,9 @@ def mx2(fa=0, fb=1, A=FAKE, lda=512, B=FAKE2, ldb=256, sa=FAKE3, sb=FAKE3, layou
     (dict(fb=7), q.QGEMM_ERR_BAD_FORMAT),
     (dict(fa=1, fb=0), q.QGEMM_ERR_BAD_LAYOUT),                 # e2m1 A x e4m3 B: B row is K = 512 bytes
     (dict(fa=1, fb=0, lda=128, ldb=512), q.QGEMM_ERR_BAD_LAYOUT),  # ... and A row K/2 = 256
-    (dict(fa=1, fb=0, lda=288, ldb=544, K=544), q.QGEMM_ERR_BAD_SHAPE),
+    (dict(fa=1, fb=0, lda=272, ldb=528, K=528), q.QGEMM_ERR_BAD_SHAPE),   # K % 32
     (dict(layout=16), q.QGEMM_ERR_BAD_FORMAT),
-    (dict(K=544, lda=544, ldb=272), q.QGEMM_ERR_BAD_SHAPE),      # K % 64
+    (dict(K=528, lda=528, ldb=272), q.QGEMM_ERR_BAD_SHAPE),      # K % 32
     (dict(A=None), q.QGEMM_ERR_NULL_POINTER),
     (dict(sb=None), q.QGEMM_ERR_NULL_POINTER),
     (dict(ldb=128), q.QGEMM_ERR_BAD_LAYOUT),                     # e2m1 B row is K/2 = 256 bytes
@@ -372,6 +373,9 @@ def test_mx_mixed_checks_pass_before_the_device_check(monkeypatch):
     # e2m1 A x e4m3 B: the LDS-fetch kernel at every M (no small-M form)
     assert mx2(fa=1, fb=0, lda=256, ldb=512) == q.QGEMM_ERR_UNSUPPORTED_DEVICE
     assert mx2(fa=1, fb=0, lda=256, ldb=512, N=0) == q.QGEMM_OK
+    # any K a multiple of 32, both pairings
+    assert mx2(K=544, lda=544, ldb=272) == q.QGEMM_ERR_UNSUPPORTED_DEVICE
+    assert mx2(fa=1, fb=0, lda=272, ldb=544, K=544) == q.QGEMM_ERR_UNSUPPORTED_DEVICE
     assert q.select_tile(8, 8192, 8192, 8192) == 4
     assert q.select_tile(8, 16, 8192, 8192) == 7
     assert q.select_tile(8, 17, 8192, 8192) == 7

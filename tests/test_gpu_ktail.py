@@ -208,6 +208,71 @@ def test_k64_full_size_mxfp8():
     parity.check_full_grid(d, out, -1, "k64 full mxfp8", rng.choice(d["M"], 16, replace=False))
 
 
+# K % 64 == 32 (K/32 odd) on the e4m3-staged MX paths and e2m1: the last
+# stage holds 32 K elements (its other chunks are fetched as zeros), scale
+# rows start 1-3 bytes into a dword and the last live scale word ends one or
+# three bytes into the row's end; against poisoned operand padding and
+# poisoned neighbouring scale rows.
+@pytest.mark.parametrize("keep", [0, 1])
+@pytest.mark.parametrize("tile", DMA_TILES)
+@pytest.mark.parametrize("brows", [1, 32])
+@pytest.mark.parametrize("K", [32, 96, 224, 288, 1120])
+@pytest.mark.parametrize("M,N", [(200, 300), (201, 289)])
+def test_k32_mxfp8(M, N, K, brows, tile, keep):
+    _check("mxfp8", M, N, K, tile, brows=brows, keep=keep)
+
+
+@pytest.mark.parametrize("keep", [0, 1])
+@pytest.mark.parametrize("tile", [4, 5, 7])
+@pytest.mark.parametrize("name", ["mx_a8w4", "mx_a4w8"])
+@pytest.mark.parametrize("K", [32, 96, 224, 736])
+@pytest.mark.parametrize("M,N", [(200, 300), (201, 289)])
+def test_k32_mixed(name, M, N, K, tile, keep):
+    _check(name, M, N, K, tile, keep=keep)
+
+
+@pytest.mark.parametrize("tile", [8, 9])
+@pytest.mark.parametrize("K", [32, 96, 224, 736])
+@pytest.mark.parametrize("M", [1, 13])
+def test_k32_mixed_small_m(M, K, tile):
+    """e4m3 x e2m1 at K % 64 == 32 in the small-M kernel (16-byte e2m1 row
+    ends fetched as zeros past K)."""
+    _check("mx_a8w4", M, 300, K, tile)
+
+
+@pytest.mark.parametrize("keep", [0, 1])
+@pytest.mark.parametrize("tile", [4, 5, 7])
+@pytest.mark.parametrize("K", [32, 96, 160, 224, 1184])
+@pytest.mark.parametrize("M,N", [(200, 300), (201, 289)])
+def test_k32_mxfp4(M, N, K, tile, keep):
+    """e2m1 at K % 128 == 32 or 96: 64-element stages, the last one 16 bytes
+    of each row."""
+    _check("mxfp4", M, N, K, tile, keep=keep)
+
+
+def test_k32_full_size_mxfp8():
+    """16384 x 7168 x 2080 (K/32 = 65: 32.5 stages) in the launch the
+    benchmark uses for MXFP8, into a NaN-filled C, on the band rows and
+    sampled rows."""
+    d = inputs.make("mxfp8", K=2080)
+    assert q.select_tile(2, d["M"], d["N"], d["K"]) == 5
+    _say(f"[ktail] full mxfp8 {d['M']}x{d['N']}x{d['K']}")
+    out = parity.gpu_run(d, out=parity.nan_out(d["M"], d["N"]))
+    rng = np.random.default_rng(7)
+    parity.check_full_grid(d, out, -1, "k32 full mxfp8", rng.choice(d["M"], 16, replace=False))
+
+
+def test_k32_full_size_mxfp4():
+    """8192 x 8192 x 8224 e2m1 (128.5 stages of 64 elements) in the table's
+    launch, into a NaN-filled C, on the band rows and sampled rows."""
+    d = inputs.make("mxfp4", K=8224)
+    assert q.select_tile(3, d["M"], d["N"], d["K"]) == 5
+    _say(f"[ktail] full mxfp4 {d['M']}x{d['N']}x{d['K']}")
+    out = parity.gpu_run(d, out=parity.nan_out(d["M"], d["N"]))
+    rng = np.random.default_rng(8)
+    parity.check_full_grid(d, out, -1, "k32 full mxfp4", rng.choice(d["M"], 8, replace=False))
+
+
 def test_partial_round_full_size_mxfp8():
     """16384 x 7168 x 2176 (K/32 = 68: a last round of two stages) in the
     launch the benchmark uses for MXFP8, on sampled whole rows."""

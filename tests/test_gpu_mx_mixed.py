@@ -101,10 +101,10 @@ def test_mx84_equal_formats_are_qgemm_mx():
 
 
 def test_mx84_rejects():
-    A8 = torch.zeros((4, 544), dtype=torch.uint8, device="cuda")
-    B4 = torch.zeros((4, 272), dtype=torch.uint8, device="cuda")
-    s = torch.full((4, 17), 127, dtype=torch.uint8, device="cuda")
-    with pytest.raises(ValueError):      # K = 544 is not a multiple of 64
+    A8 = torch.zeros((4, 528), dtype=torch.uint8, device="cuda")
+    B4 = torch.zeros((4, 264), dtype=torch.uint8, device="cuda")
+    s = torch.full((4, 16), 127, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):      # K = 528 is not a multiple of 32
         q.qgemm_mx_mixed(q.QGEMM_MX_E4M3, q.QGEMM_MX_E2M1, A8, B4, s, s, 1)
     with pytest.raises(ValueError):      # e2m1 A with e4m3 B, the same K
         q.qgemm_mx_mixed(q.QGEMM_MX_E2M1, q.QGEMM_MX_E4M3, B4, A8, s, s, 1)

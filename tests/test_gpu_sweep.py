@@ -39,11 +39,9 @@ def _shape(rng, name):
     N = int(rng.integers(1, 520))
     if name in ("f8_block", "mxfp6", "mxfp6_e3m2"):
         K = 128 * int(rng.integers(1, 13))                 # these paths: K a multiple of 128
-    elif name in ("mx_a8w4", "mx_a4w8"):
-        K = 64 * int(rng.integers(1, 25))                  # mixed MX: K a multiple of 64
     else:
-        # any multiple of 32 (e2m1 K = 32 * odd: 16-byte row ends, the
-        # register-staged and small-M tails)
+        # any multiple of 32 (K = 32 * odd: a last half stage, 16-byte
+        # e2m1 row ends)
         K = 32 * int(rng.integers(1, 49))
     return M, N, K
 
