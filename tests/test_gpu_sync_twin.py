@@ -71,6 +71,9 @@ CASES = [
     ("mx_a8w4", 130, 260, 448, [4, 5, 7]),
     ("mx_a4w8", 130, 260, 448, [4, 5, 7]),
     ("mxfp4", 130, 260, 704, [4, 5, 7]),                          # e2m1 in 64-element stages
+    ("mxfp8", 201, 289, 736, [4, 5, 6, 7]),                       # K % 64 == 32: a last half stage
+    ("mx_a4w8", 130, 260, 480, [4, 5, 7]),
+    ("mxfp4", 130, 260, 736, [4, 5, 7]),
     ("mxfp6", 200, 300, 640, [4, 7]),
     ("mxfp6_e3m2", 130, 260, 1024, [4, 7]),
 ]
