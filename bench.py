@@ -108,11 +108,11 @@ class Launcher:
         for s in sets:
             bias = None if s["bias"] is None else s["bias"].data_ptr()
             if prepacked and "/" in (d["fmt"] or ""):
-                if d["fmt"] != "e4m3/e2m1":
-                    raise SystemExit("a prepacked B is taken with e4m3 A and e2m1 B only")
-                pb = q.qgemm_prepack_b32(s["B"]).data
+                # e2m1 B: the 32-row packer; e4m3 B (under e2m1 A): the 16-row one
+                a4 = d["fmt"] == "e2m1/e4m3"
+                pb = (q.qgemm_prepack_b(s["B"]) if a4 else q.qgemm_prepack_b32(s["B"])).data
                 s["Bp"] = pb
-                a = (0, 1, s["A"].data_ptr(), s["A"].stride(0), pb.data_ptr(), s["scale_a"].data_ptr(),
+                a = ((1, 0) if a4 else (0, 1)) + (s["A"].data_ptr(), s["A"].stride(0), pb.data_ptr(), s["scale_a"].data_ptr(),
                      s["scale_b"].data_ptr(), d["b_rows_per_scale"], bias, out.data_ptr(), self.ldc, d["M"], N, d["K"],
                      self.stream)
                 self.args.append((self.L.qgemm_mx_mixed_prepacked, a))

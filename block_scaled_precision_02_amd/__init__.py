@@ -554,16 +554,26 @@ def qgemm_prepack_b32(B, out=None, stream=None):
 
 
 def qgemm_mx_mixed_prepacked(fmt_a, fmt_b, A, Bp, scale_a, scale_b, b_layout, bias=None, out=None, stream=None):
-    """The mixed MX GEMM (e4m3 A, e2m1 B) with B from qgemm_prepack_b32 -> bf16 [M, N]."""
+    """The mixed MX GEMM with a prepacked B -> bf16 [M, N]: e4m3 A [M, K] with
+    an e2m1 B from qgemm_prepack_b32, or e2m1 A [M, K/2] with an e4m3 B from
+    qgemm_prepack_b."""
     torch = _torch()
-    lda = _operand(A, "A", (torch.uint8, torch.float8_e4m3fn))
-    M, K = A.shape
-    if fmt_a != QGEMM_MX_E4M3 or fmt_b != QGEMM_MX_E2M1:
-        raise ValueError("the prepacked mixed GEMM takes e4m3 A and e2m1 B")
-    if not isinstance(Bp, PackedB) or Bp.group_rows != 32:
-        raise ValueError("Bp must be a PackedB from qgemm_prepack_b32")
-    if Bp.row_bytes != K // 2:
-        raise ValueError(f"Bp was packed from rows of {Bp.row_bytes} bytes; K/2 = {K // 2}")
+    if (fmt_a, fmt_b) == (QGEMM_MX_E4M3, QGEMM_MX_E2M1):
+        lda = _operand(A, "A", (torch.uint8, torch.float8_e4m3fn))
+        M, K = A.shape
+        if not isinstance(Bp, PackedB) or Bp.group_rows != 32:
+            raise ValueError("Bp must be a PackedB from qgemm_prepack_b32")
+        if Bp.row_bytes != K // 2:
+            raise ValueError(f"Bp was packed from rows of {Bp.row_bytes} bytes; K/2 = {K // 2}")
+    elif (fmt_a, fmt_b) == (QGEMM_MX_E2M1, QGEMM_MX_E4M3):
+        lda = _operand(A, "A", (torch.uint8,))
+        M, K = A.shape[0], 2 * A.shape[1]
+        if not isinstance(Bp, PackedB) or Bp.group_rows != 16:
+            raise ValueError("Bp must be a PackedB from qgemm_prepack_b")
+        if Bp.row_bytes != K:
+            raise ValueError(f"Bp was packed from rows of {Bp.row_bytes} bytes; K = {K}")
+    else:
+        raise ValueError("the prepacked mixed GEMM takes e4m3 A with e2m1 B or e2m1 A with e4m3 B")
     N = Bp.N
     sdt = (torch.uint8,) + ((torch.float8_e8m0fnu,) if hasattr(torch, "float8_e8m0fnu") else ())
     brows = -(-N // b_layout) if b_layout in (1, 32) else N

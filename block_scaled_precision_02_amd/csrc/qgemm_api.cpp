@@ -768,8 +768,6 @@ static qgemm_status mx_mixed_common(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, cons
                          false);
     }
     const bool a4 = fmt_a == QGEMM_MX_E2M1;   // e2m1 A with e4m3 B
-    if (a4 && packed)
-        return fail(QGEMM_ERR_BAD_FORMAT, "e2m1 A with e4m3 B: prepacked B is not supported (use qgemm_mx_mixed)");
     if (b_layout != QGEMM_MX_BSCALE_1x32 && b_layout != QGEMM_MX_BSCALE_32x32)
         return fail(QGEMM_ERR_BAD_FORMAT, "unknown B-scale layout %d", (int)b_layout);
     const char *pair = a4 ? "e2m1 x e4m3" : "e4m3 x e2m1";
@@ -782,6 +780,8 @@ static qgemm_status mx_mixed_common(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, cons
         return QGEMM_OK;
     TRY(check_operand("A", A, lda_bytes, a4 ? K / 2 : K));
     if (packed) {
+        // e4m3 B: qgemm_prepack_b's 16-row groups of K-byte rows; e2m1 B:
+        // qgemm_prepack_b32's 32-row groups of K/2-byte rows
         if (!B)
             return fail(QGEMM_ERR_NULL_POINTER, "Bp is NULL");
         if (!aligned(B, 16))
@@ -800,7 +800,8 @@ static qgemm_status mx_mixed_common(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, cons
     TRY(check_device());
     if (a4) {
         const int tile = pick_tile_mx48(s);
-        Params p = base_params(A, lda_bytes, B, ldb_bytes, C, ldc, s, K, tile);   // kbytes: B's row
+        Params p = base_params(A, lda_bytes, B, packed ? K : ldb_bytes, C, ldc, s, K, tile);   // kbytes: B's row
+        p.b_packed = packed;
         TRY(check_grid(p));
         p.mx_sa = scale_a;
         p.mx_sb = scale_b;

@@ -203,10 +203,12 @@ qgemm_status qgemm_mx_mixed(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *
  * slot p being row 32R + p/2, chunk (p mod 2) XOR ((p/16) mod 2); rows past N
  * are zeros -- the order the mixed GEMM's B stages take in LDS.
  * qgemm_prepacked_b32_bytes returns -1 for a bad size.  qgemm_mx_mixed_prepacked
- * is qgemm_mx_mixed (e4m3 A with e2m1 B only; equal formats and e2m1 A
- * return QGEMM_ERR_BAD_FORMAT) with Bp in place of (B, ldb) and K a multiple of 256
- * (the packer's rows); results equal qgemm_mx_mixed's on the same tile;
- * M <= 16 runs the 128x128 tile. */
+ * is qgemm_mx_mixed with Bp in place of (B, ldb) and K a multiple of 256 (the
+ * packer's rows): for e4m3 A, Bp is an e2m1 B [N, K/2] packed by
+ * qgemm_prepack_b32 (M <= 16 runs the 128x128 tile); for e2m1 A, an e4m3 B
+ * [N, K] packed by qgemm_prepack_b (qgemm_prepack_b's layout, below).  Equal
+ * formats return QGEMM_ERR_BAD_FORMAT.  Results equal qgemm_mx_mixed's on the
+ * same tile. */
 int64_t qgemm_prepacked_b32_bytes(int64_t N, int64_t row_bytes);
 qgemm_status qgemm_prepack_b32(const void *B, int64_t ldb, int64_t N, int64_t row_bytes, void *Bp, void *stream);
 qgemm_status qgemm_mx_mixed_prepacked(qgemm_mx_fmt fmt_a, qgemm_mx_fmt fmt_b, const void *A, int64_t lda_bytes,

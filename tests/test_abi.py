@@ -413,11 +413,15 @@ def test_prepacked_b32_sizes_and_rejects(monkeypatch):
     assert L.qgemm_prepack_b32(FAKE, 128, 33, 128, None, None) == q.QGEMM_ERR_NULL_POINTER
     m = L.qgemm_mx_mixed_prepacked
     assert m(0, 0, FAKE, 512, FAKE2, FAKE3, FAKE3, 1, None, FAKE, 64, 64, 64, 512, None) == q.QGEMM_ERR_BAD_FORMAT
-    assert m(1, 0, FAKE, 256, FAKE2, FAKE3, FAKE3, 1, None, FAKE, 64, 64, 64, 512, None) == q.QGEMM_ERR_BAD_FORMAT
+    assert m(1, 1, FAKE, 256, FAKE2, FAKE3, FAKE3, 1, None, FAKE, 64, 64, 64, 512, None) == q.QGEMM_ERR_BAD_FORMAT
+    assert m(1, 0, FAKE, 128, FAKE2, FAKE3, FAKE3, 1, None, FAKE, 64, 64, 64, 512, None) == q.QGEMM_ERR_BAD_LAYOUT
+    assert m(1, 0, FAKE, 256, FAKE2, FAKE3, FAKE3, 1, None, FAKE, 64, 64, 64, 320, None) == q.QGEMM_ERR_BAD_SHAPE
     assert m(0, 1, FAKE, 512, None, FAKE3, FAKE3, 1, None, FAKE, 64, 64, 64, 512, None) == q.QGEMM_ERR_NULL_POINTER
     assert m(0, 1, FAKE, 512, FAKE2 + 8, FAKE3, FAKE3, 1, None, FAKE, 64, 64, 64, 512, None) == q.QGEMM_ERR_BAD_LAYOUT
     monkeypatch.setenv("QGEMM_FAKE_ARCH", "gfx1201")
     assert m(0, 1, FAKE, 512, FAKE2, FAKE3, FAKE3, 1, None, FAKE, 64, 64, 64, 512, None) == q.QGEMM_ERR_UNSUPPORTED_DEVICE
+    # e2m1 A with an e4m3 B from qgemm_prepack_b (A rows K/2 bytes)
+    assert m(1, 0, FAKE, 256, FAKE2, FAKE3, FAKE3, 1, None, FAKE, 64, 64, 64, 512, None) == q.QGEMM_ERR_UNSUPPORTED_DEVICE
 
 
 def _aligned(n, fill):

@@ -144,20 +144,26 @@ def test_prepack_b32_bit_exact(orc, N, row):
 
 
 def _run_mixed_packed(d, out=None):
+    """e4m3 A with an e2m1 B from the 32-row packer, or e2m1 A with an e4m3 B
+    from the 16-row one."""
     bias = None if d["bias"] is None else parity.dev(d["bias"].view(np.int16))
-    pb = q.qgemm_prepack_b32(parity.dev(d["B"]))
-    return q.qgemm_mx_mixed_prepacked(q.QGEMM_MX_E4M3, q.QGEMM_MX_E2M1, parity.dev(d["A"]), pb,
+    a4 = d["fmt"] == "e2m1/e4m3"
+    pb = q.qgemm_prepack_b(parity.dev(d["B"])) if a4 else q.qgemm_prepack_b32(parity.dev(d["B"]))
+    fa, fb = (q.QGEMM_MX_E2M1, q.QGEMM_MX_E4M3) if a4 else (q.QGEMM_MX_E4M3, q.QGEMM_MX_E2M1)
+    return q.qgemm_mx_mixed_prepacked(fa, fb, parity.dev(d["A"]), pb,
                                       parity.dev(d["scale_a"]), parity.dev(d["scale_b"]), d["b_rows_per_scale"],
                                       bias, out=out)
 
 
 @pytest.mark.parametrize("tile", [-1, 4, 5, 7])
+@pytest.mark.parametrize("name", ["mx_a8w4", "mx_a4w8"])
 @pytest.mark.parametrize("M,N,K", [(1, 1, 256), (17, 33, 512), (255, 257, 1024), (300, 520, 2048), (64, 300, 768)])
-def test_prepacked_mixed_edges(M, N, K, tile):
-    """The mixed GEMM on a prepacked e2m1 B: ragged M / N, canaries; bit for bit
-    equal to the same tile on the row-major B (M <= 16 runs the 128x128 tile)."""
-    d = inputs.make("mx_a8w4", M=M, N=N, K=K, bias=(M % 2 == 1))
-    _say(f"[prepacked] mx_a8w4 {M}x{N}x{K} tile {tile}")
+def test_prepacked_mixed_edges(name, M, N, K, tile):
+    """The mixed GEMMs on a prepacked B (e2m1 under e4m3 A, e4m3 under e2m1
+    A): ragged M / N, canaries; bit for bit equal to the same tile on the
+    row-major B (e4m3 A: M <= 16 runs the 128x128 tile)."""
+    d = inputs.make(name, M=M, N=N, K=K, bias=(M % 2 == 1))
+    _say(f"[prepacked] {name} {M}x{N}x{K} tile {tile}")
     q.force_tile(tile)
     ldc = N + (-N) % 8 + 8
     buf = torch.full((M + 3, ldc), float("nan"), dtype=torch.bfloat16, device="cuda")
@@ -165,17 +171,19 @@ def test_prepacked_mixed_edges(M, N, K, tile):
     _run_mixed_packed(d, out=buf[:M, :N])
     after = parity.bits(buf)
     ref, absdot, _ = parity.oracle_run(d)
-    parity.compare(d, after[:M, :N], ref, absdot, f"prepacked mx_a8w4 {M}x{N}x{K} tile {tile}")
+    parity.compare(d, after[:M, :N], ref, absdot, f"prepacked {name} {M}x{N}x{K} tile {tile}")
     assert np.array_equal(after[:M, N:], before[:M, N:]), "wrote past N"
     assert np.array_equal(after[M:], before[M:]), "wrote past M"
-    q.force_tile(7 if (tile == -1 and M <= 16) else tile)
+    q.force_tile(7 if (tile == -1 and M <= 16 and name == "mx_a8w4") else tile)
     plain = parity.bits(parity.gpu_run(d))
     assert np.array_equal(after[:M, :N], plain), "prepacked and row-major B differ"
 
 
-def test_prepacked_mixed_full_workload_sampled():
-    d = inputs.make("mx_a8w4")
+@pytest.mark.parametrize("name", ["mx_a8w4", "mx_a4w8"])
+def test_prepacked_mixed_full_workload_sampled(name):
+    d = inputs.make(name)
     q.force_tile(-1)
+    _say(f"[prepacked] full {name}")
     out = _run_mixed_packed(d, out=parity.nan_out(d["M"], d["N"]))
-    parity.check_full_grid(d, out, -1, "prepacked full mx_a8w4",
+    parity.check_full_grid(d, out, -1, f"prepacked full {name}",
                            np.random.default_rng(3).choice(d["M"], 8, replace=False))
