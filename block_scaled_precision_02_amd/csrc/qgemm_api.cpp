@@ -246,7 +246,7 @@ Params base_params(const void *A, int64_t lda, const void *B, int64_t ldb, void 
     // round: MXFP4 8192^3, 201 MB, 0.272 -> 0.262 ms), non-temporal otherwise
     // (where C would only push the operands out: INT8 30000x21504x5376 2.84
     // vs 2.93 ms, MXFP8 16384x7168x2048 0.236 vs 0.240 ms; one MI355X, same
-    // box alternating).
+    // machine alternating).
     const double footprint = (double)s.M * (double)s.N * 2.0 + (double)(s.M + s.N) * (double)kbytes;
     p.c_cached = footprint <= MALL_BYTES ? 1 : 0;
     return p;
@@ -316,7 +316,7 @@ bool dma_eligible(int path, int64_t kbytes, int64_t K, bool svec)
 }
 
 // When K fits, the table's tile edge runs in an LDS-fetch kernel: 256 as the
-// eight-wave kernel (one MI355X, same box: INT8 30000x21504x5376 2155 TOPS vs
+// eight-wave kernel (one MI355X, same machine: INT8 30000x21504x5376 2155 TOPS vs
 // 2130 for the four-wave LDS-fetch kernel and ~2100 for register staging;
 // MXFP4 8192^3 3756 vs 3668 TFLOPS; MXFP8 16384x7168x2048 1940 vs 1933), 192
 // and 128 as their four-wave LDS-fetch forms.
@@ -329,7 +329,7 @@ bool dma_eligible(int path, int64_t kbytes, int64_t K, bool svec)
 constexpr int64_t SKINNY_MAX_M = 64, SKINNY_MAX_M_MX = 16;
 
 // The LDS-fetch form of the 256x256 edge: the eight-wave kernel, whose INT8
-// and e2m1 forms fetch two stages of a row per request (one MI355X, same box
+// and e2m1 forms fetch two stages of a row per request (one MI355X, same machine
 // alternating: INT8 30000x21504x5376 2.909 ms on tile 5 vs 3.031 ms on the
 // four-wave tile 4; MXFP4 8192^3 0.304 vs 0.332 ms; MXFP8 16384x7168x2048
 // 0.248 vs 0.255 ms) -- except INT8 with a prepacked B, whose whole-line
@@ -395,7 +395,7 @@ int pick_tile_mx84(Shape s)
     if (s.M <= SKINNY_MAX_M_MX)
         return SKINNY16_TILE;
     // the four-wave 256x256 tile, where the 16-byte wide scale refills apply
-    // (8192^3 on one box, alternating: 0.445 vs 0.477 ms for the eight-wave
+    // (8192^3 on one machine, alternating: 0.445 vs 0.477 ms for the eight-wave
     // tile 5)
     return select_tile_impl(2, s.M, s.N) == 0 ? DMA_TILE : DMA128_TILE;
 }

@@ -265,7 +265,7 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // takes them over two regions instead of one burst (its queue, full,
     // stalls every wave that issues a load); the pair is waited for one stage
     // later.  (One MI355X, alternating: INT8 30000x21504x5376 2.890 -> 2.852
-    // ms, and 3.052 -> 2.998 ms on a slower box; e2m1 8192^3 0.2675 -> 0.2690
+    // ms, and 3.052 -> 2.998 ms on a slower machine; e2m1 8192^3 0.2675 -> 0.2690
     // ms, and unchanged with only the pair issued at J = 1 split, so it keeps
     // whole pairs.)
     constexpr bool PH = PAIR && !P6 && PATH == PATH_I8;
