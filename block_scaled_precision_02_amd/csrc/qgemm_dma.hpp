@@ -1117,10 +1117,108 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
             stage(t + 3, std::integral_constant<int, 3>());
         }
     }
-    wait_vmcnt<0>();   // nothing may still be landing in LDS once it holds the output
+    // Successor prefetch (e2m1 MX).  Once a round of tiles is running, the
+    // tile that starts next on this XCD is the one of workgroup blockIdx + NXT
+    // (the dispatcher hands workgroups to the 8 XCDs round-robin and, within
+    // an XCD, in order to whichever CU frees up; NXT = 8 XCDs x 32 CUs x the
+    // workgroups a CU holds).  Its prologue waits for the first stage of its
+    // A and B rows and its first scale refill, which at that point come from
+    // beyond L2.  So, with the K loop done, every workgroup loads one dword of
+    // the first 128-byte line of each of the next tile's A, B and scale rows
+    // (prepacked B: of the first two 1 KB blocks of each row group) into
+    // registers: the lines come into the XCD's L2 while this tile's epilogue
+    // runs.  The loads are range-checked like every fetch and their values
+    // are never used.  They are the last loads before the wait below, which
+    // therefore lets exactly them stay in flight.  The launch arguments they
+    // need are read again through an opaque copy of the argument pointer, so
+    // that the K loop does not keep them in registers.  (One MI355X each,
+    // alternating: MXFP4 8192^3 0.2617 -> 0.2594 ms on one machine, level on
+    // another, prepacked B 0.2617 -> 0.2588; INT8 30000x21504x5376 2.798 ->
+    // 2.808, e4m3 x e2m1 8192^3 0.4095 -> 0.4121, MXFP8 level: those paths
+    // do not prefetch.)
+    constexpr bool SUCC = PATH == PATH_MX4;
+    constexpr int NT = 64 * NW;
+    constexpr int WPC = sizeof(lds) > 80 * 1024 ? 1 : 2;           // workgroups per CU (LDS)
+    constexpr int NXT = 8 * 32 * WPC;
+    constexpr int NPA = SUCC ? (BM + BN + NT - 1) / NT : 0;        // operand lines per lane
+    constexpr int NPS = SUCC ? (BM + BN + NT - 1) / NT : 0;        // scale lines per lane
+    unsigned pf[NPA + NPS + 1];
+    typedef const Params __attribute__((address_space(4))) *KargP;
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!SUCC) {
+        wait_vmcnt<0>();   // nothing may still be landing in LDS once it holds the output
+    } else {
+        KargP kp = (KargP)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(kp));
+        const int tms = kp->tiles_m, tns = kp->tiles_n;
+        const int nb = (int)blockIdx.x + NXT;
+        if (nb < tms * tns) {
+            int sm, sn;
+            tile_of_index(tms, tns, kp->group_m, nb, sm, sn);
+            const int m1 = sm * BM, n1 = sn * BN;
+            const int ra = min(BM, kp->M - m1), rb = min(BN, kp->N - n1);
+            const int64_t lda = kp->lda, ldb = kp->ldb;
+            const __amdgpu_buffer_rsrc_t pa =
+                make_rsrc(kp->A + (int64_t)m1 * lda, (uint32_t)((ra - 1) * lda + kbytes_a));
+            const bool packed = kp->b_packed;
+            const __amdgpu_buffer_rsrc_t pb =
+                packed ? make_rsrc(kp->B + (int64_t)(n1 / PGR) * gbytes, (uint32_t)(((rb + PGR - 1) / PGR) * gbytes))
+                       : make_rsrc(kp->B + (int64_t)n1 * ldb, (uint32_t)((rb - 1) * ldb + kbytes_b));
+#pragma unroll
+            for (int q = 0; q < NPA; ++q) {
+                const int idx0 = q * NT + 64 * wave;                 // uniform: BM is a multiple of 64
+                const int idx = idx0 + lane;
+                if (idx0 < BM) {
+                    pf[q] = __builtin_amdgcn_raw_buffer_load_b32(pa, idx < ra ? (unsigned)(idx * lda) : OOB, 0, 0);
+                } else {
+                    const int b = idx - BM;
+                    unsigned off;
+                    if (packed) {
+                        // 16 lines of each group's first 2 KB
+                        const int g = b >> 4;
+                        off = (g < (BN + PGR - 1) / PGR && PGR * g < rb) ? (unsigned)(g * gbytes + 128 * (b & 15))
+                                                                         : OOB;
+                    } else {
+                        off = (b < BN && b < rb) ? (unsigned)(b * ldb) : OOB;
+                    }
+                    pf[q] = __builtin_amdgcn_raw_buffer_load_b32(pb, off, 0, 0);
+                }
+            }
+            const int kbl = kp->kblocks;
+            const int srb = (rb + BROWS - 1) / BROWS;
+            const __amdgpu_buffer_rsrc_t qa =
+                make_rsrc(kp->mx_sa + (int64_t)m1 * kbl, (uint32_t)((ra * kbl + 3) & ~3));
+            const __amdgpu_buffer_rsrc_t qb =
+                make_rsrc(kp->mx_sb + (int64_t)(n1 / BROWS) * kbl, (uint32_t)((srb * kbl + 3) & ~3));
+#pragma unroll
+            for (int q = 0; q < NPS; ++q) {
+                const int idx0 = q * NT + 64 * wave;
+                const int idx = idx0 + lane;
+                if (idx0 < BM)
+                    pf[NPA + q] = __builtin_amdgcn_raw_buffer_load_b32(
+                        qa, idx < ra ? (unsigned)(idx * kbl) & ~3u : OOB, 0, 0);
+                else
+                    pf[NPA + q] = __builtin_amdgcn_raw_buffer_load_b32(
+                        qb, idx - BM < srb ? (unsigned)((idx - BM) * kbl) & ~3u : OOB, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<NPA + NPS>();   // every fetch into LDS has landed; only the prefetch is in flight
+        } else {
+#pragma unroll
+            for (int q = 0; q < NPA + NPS; ++q) pf[q] = 0;
+            wait_vmcnt<0>();   // nothing may still be landing in LDS once it holds the output
+        }
+    }
 
     store_tile<PATH, WM, WN, TM, TN, BIAS, OUT, ((B4 || A4 || F6) ? BODY : OPND_BYTES), PRM>(p, acc, &lds[0], &lds[PRM_OFF], m0, n0,
                                                                             rows_a, rows_b);
+    // (the prefetched values, consumed here so that the loads stay: the wait
+    // for them falls after the output stores)
+    if constexpr (SUCC) {
+#pragma unroll
+        for (int q = 0; q < NPA + NPS; ++q)
+            asm volatile("" : : "v"(pf[q]));
+    }
 }
 
 }  // namespace qgemm

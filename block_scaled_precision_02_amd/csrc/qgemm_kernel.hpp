@@ -148,21 +148,24 @@ __device__ __forceinline__ int lds_off(int r, int c)
 // Workgroup -> output tile.  Workgroups are handed to the 8 XCDs round-robin;
 // renumber so each XCD gets a contiguous run of the grouped order (tiles
 // that share A and B panels then share that XCD's L2), then walk the tiles
-// in groups of group_m tile rows.
-__device__ __forceinline__ void tile_of(const Params &p, int &tm, int &tn)
+// in groups of group_m tile rows.  (tile_of_index: the tile of workgroup i.)
+__device__ __forceinline__ void tile_of_index(int tiles_m, int tiles_n, int group_m, int i, int &tm, int &tn)
 {
-    const int G = p.tiles_m * p.tiles_n;
-    const int i = blockIdx.x;
+    const int G = tiles_m * tiles_n;
     const int xcd = i & 7, local = i >> 3;
     const int per = G >> 3, rem = G & 7;
     const int pid = xcd * per + (xcd < rem ? xcd : rem) + local;
-    const int width = p.group_m * p.tiles_n;
+    const int width = group_m * tiles_n;
     const int group = pid / width;
-    const int first_m = group * p.group_m;
-    const int gsz = min(p.tiles_m - first_m, p.group_m);
+    const int first_m = group * group_m;
+    const int gsz = min(tiles_m - first_m, group_m);
     const int in = pid - group * width;
     tm = first_m + in % gsz;
     tn = in / gsz;
+}
+__device__ __forceinline__ void tile_of(const Params &p, int &tm, int &tn)
+{
+    tile_of_index(p.tiles_m, p.tiles_n, p.group_m, (int)blockIdx.x, tm, tn);
 }
 
 template <int PATH> struct PathTraits;
