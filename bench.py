@@ -267,10 +267,13 @@ def write_traffic(prof_dir, workloads, out_path=TRAFFIC_JSON):
 
 def cpu_baseline(d, target_s):
     """The oracle, as it is, on whole rows of the same workload: a few rows
-    first to calibrate, then enough rows for about target_s seconds."""
+    first to calibrate, then enough rows for about target_s seconds.  The
+    calibration takes two rows per oracle thread, so that it runs on all of
+    them as the timed sample does (two rows alone ran on two threads, and the
+    sample came out several times shorter than target_s)."""
     import oracle
     from tests import parity
-    rows = np.arange(min(2, d["M"]))
+    rows = np.arange(min(2 * oracle.num_threads(), d["M"]))
     t0 = time.perf_counter()
     parity.oracle_run(d, rows=rows)
     t1 = time.perf_counter() - t0
