@@ -1,7 +1,7 @@
-"""GPU parity of the e2m1 MX LDS-fetch kernels on grids of more than one round
-of tiles, where each workgroup, once its K loop is done, loads the first
-lines of the A, B and scale rows of the tile that starts after it on its XCD
-(a prefetch into L2 whose values are never used).
+"""GPU parity of the e2m1 MX, 6-bit MX and blockscale FP8 LDS-fetch kernels on
+grids of more than one round of tiles, where each workgroup, once its K loop
+is done, loads the first lines of the A, B and scale rows of the tile that
+starts after it on its XCD (a prefetch into L2 whose values are never used).
 
 The cases put ragged M and N edges into the grid, so that some workgroups
 prefetch for an edge tile, and cover plain and prepacked B, 1x32 and 32x32 B
@@ -96,3 +96,28 @@ def test_multi_round_bias_and_repeat(M, N, K, tile):
     out = _run(d, False, out)
     parity.check_full_grid(d, out, tile, f"successor bias {M}x{N}x{K} tile={tile} (second launch)")
     assert np.array_equal(parity.bits(out), first), "two launches on the same inputs differ"
+
+
+def _run_other(d, packed, out):
+    bias = None if d["bias"] is None else parity.dev(d["bias"].view(np.int16))
+    A, sa, sb = parity.dev(d["A"]), parity.dev(d["scale_a"]), parity.dev(d["scale_b"])
+    if packed:
+        pb = q.qgemm_prepack_b(parity.dev(d["B"]))
+        return q.qgemm_f8_blockscale_prepacked(A, pb, sa, sb, bias, out=out)
+    return parity.gpu_run(d, out=out)
+
+
+# Blockscale FP8 (256x128 and 128x128 tiles) and both 6-bit MX formats
+# (256x256 on four waves, 128x128) prefetch as well.
+@pytest.mark.parametrize("name,tile,packed", [
+    ("f8_block", -1, False), ("f8_block", 10, False), ("f8_block", 7, False), ("f8_block", 10, True),
+    ("mxfp6", -1, False), ("mxfp6", 4, False), ("mxfp6", 7, False),
+    ("mxfp6_e3m2", 4, False), ("mxfp6_e3m2", 7, False),
+])
+def test_multi_round_ragged_grid_other_paths(name, tile, packed):
+    M, N, K = SHAPE
+    d = inputs.make(name, M=M, N=N, K=K)
+    _say(f"[successor] {name} {M}x{N}x{K} tile={tile} packed={packed}")
+    q.force_tile(tile)
+    out = _run_other(d, packed, parity.nan_out(M, N))
+    parity.check_full_grid(d, out, tile, f"successor {name} tile={tile} packed={packed}")
