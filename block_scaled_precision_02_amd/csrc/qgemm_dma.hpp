@@ -1143,7 +1143,8 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     constexpr int WPC = sizeof(lds) > 80 * 1024 ? 1 : 2;           // workgroups per CU (LDS)
     constexpr int NXT = 8 * 32 * WPC;
     constexpr int NPA = SUCC ? (BM + BN + NT - 1) / NT : 0;        // operand lines per lane
-    constexpr int NPS = SUCC ? (BM + BN + NT - 1) / NT : 0;        // scale lines per lane
+    constexpr int NPS = SUCC && SCL ? (BM + BN + NT - 1) / NT : 0; // scale lines per lane (MX / blockscale only:
+                                                                   // other paths have no scale rows, and null pointers)
     unsigned pf[NPA + NPS + 1];
     typedef const Params __attribute__((address_space(4))) *KargP;
     __builtin_amdgcn_sched_barrier(0);
@@ -1186,22 +1187,24 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
                     pf[q] = __builtin_amdgcn_raw_buffer_load_b32(pb, off, 0, 0);
                 }
             }
-            const int kbl = kp->kblocks;
-            const int srb = (rb + BROWS - 1) / BROWS;
-            const __amdgpu_buffer_rsrc_t qa =
-                make_rsrc(kp->mx_sa + (int64_t)m1 * kbl, (uint32_t)((ra * kbl + 3) & ~3));
-            const __amdgpu_buffer_rsrc_t qb =
-                make_rsrc(kp->mx_sb + (int64_t)(n1 / BROWS) * kbl, (uint32_t)((srb * kbl + 3) & ~3));
+            if constexpr (NPS > 0) {
+                const int kbl = kp->kblocks;
+                const int srb = (rb + BROWS - 1) / BROWS;
+                const __amdgpu_buffer_rsrc_t qa =
+                    make_rsrc(kp->mx_sa + (int64_t)m1 * kbl, (uint32_t)((ra * kbl + 3) & ~3));
+                const __amdgpu_buffer_rsrc_t qb =
+                    make_rsrc(kp->mx_sb + (int64_t)(n1 / BROWS) * kbl, (uint32_t)((srb * kbl + 3) & ~3));
 #pragma unroll
-            for (int q = 0; q < NPS; ++q) {
-                const int idx0 = q * NT + 64 * wave;
-                const int idx = idx0 + lane;
-                if (idx0 < BM)
-                    pf[NPA + q] = __builtin_amdgcn_raw_buffer_load_b32(
-                        qa, idx < ra ? (unsigned)(idx * kbl) & ~3u : OOB, 0, 0);
-                else
-                    pf[NPA + q] = __builtin_amdgcn_raw_buffer_load_b32(
-                        qb, idx - BM < srb ? (unsigned)((idx - BM) * kbl) & ~3u : OOB, 0, 0);
+                for (int q = 0; q < NPS; ++q) {
+                    const int idx0 = q * NT + 64 * wave;
+                    const int idx = idx0 + lane;
+                    if (idx0 < BM)
+                        pf[NPA + q] = __builtin_amdgcn_raw_buffer_load_b32(
+                            qa, idx < ra ? (unsigned)(idx * kbl) & ~3u : OOB, 0, 0);
+                    else
+                        pf[NPA + q] = __builtin_amdgcn_raw_buffer_load_b32(
+                            qb, idx - BM < srb ? (unsigned)((idx - BM) * kbl) & ~3u : OOB, 0, 0);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
             wait_vmcnt<NPA + NPS>();   // every fetch into LDS has landed; only the prefetch is in flight
