@@ -1121,23 +1121,25 @@ __global__ void __launch_bounds__(128 * WN, 1) qgemm_dma_kernel(const Params p)
     // of tiles is running, the tile that starts next on this XCD is the one of
     // workgroup blockIdx + NXT (the dispatcher hands workgroups to the 8 XCDs
     // round-robin and, within an XCD, in order to whichever CU frees up;
-    // NXT = 8 XCDs x 32 CUs x the workgroups a CU holds).  Its prologue waits for the first stage of its
-    // A and B rows and its first scale refill, which at that point come from
-    // beyond L2.  So, with the K loop done, every workgroup loads one dword of
-    // the first 128-byte line of each of the next tile's A, B and scale rows
-    // (prepacked B: of the first two 1 KB blocks of each row group) into
-    // registers: the lines come into the XCD's L2 while this tile's epilogue
-    // runs.  The loads are range-checked like every fetch and their values
-    // are never used.  They are the last loads before the wait below, which
-    // therefore lets exactly them stay in flight.  The launch arguments they
-    // need are read again through an opaque copy of the argument pointer, so
-    // that the K loop does not keep them in registers.  (One MI355X each,
-    // alternating: MXFP4 8192^3 0.2617 -> 0.2594 ms on one machine, level on
-    // another, prepacked B 0.2617 -> 0.2588; blockscale 16384x7168x2048
-    // 0.3200 -> 0.3152; MXFP6 8192^3 0.3947 -> 0.3937.  INT8 30000x21504x5376
-    // 2.798 -> 2.808, e4m3 x e2m1 8192^3 0.4095 -> 0.4121, e2m1 in 64-element
-    // stages 8192x8192x8256 0.4261 -> 0.4267, MXFP8 level: those paths do not
-    // prefetch.)
+    // NXT = 8 XCDs x 32 CUs x the workgroups a CU holds).  Its prologue waits
+    // for the first stage of its A and B rows and its first scale refill,
+    // which at that point come from beyond L2.  So, with the K loop done,
+    // every workgroup loads one dword of the first 128-byte line of each of
+    // the next tile's A, B and scale rows (prepacked B: of the first two 1 KB
+    // blocks of each row group) into registers: the lines come into the XCD's
+    // L2 while this tile's epilogue runs.  The loads are range-checked like
+    // every fetch and their values are never used.  They are the last loads
+    // before the wait below, which therefore lets exactly them stay in
+    // flight.  The launch arguments they need are read again through an
+    // opaque copy of the kernarg segment pointer (the one explicit argument,
+    // Params, sits at offset 0 of that segment, as the code-object ABI lays
+    // explicit arguments out first), so that the K loop does not keep them in
+    // registers.  (One MI355X each, alternating: MXFP4 8192^3 0.2617 -> 0.2594
+    // ms on one machine, level on another, prepacked B 0.2617 -> 0.2588;
+    // blockscale 16384x7168x2048 0.3200 -> 0.3152; MXFP6 8192^3 0.3947 ->
+    // 0.3937.  INT8 30000x21504x5376 2.817 -> 2.837, e2m1 in 64-element stages
+    // 8192x8192x8256 0.4261 -> 0.4267, MXFP8 and e4m3 x e2m1 level: those
+    // paths do not prefetch.)
     constexpr bool SUCC = PATH == PATH_MX4 || F6 || BS;
     constexpr int NT = 64 * NW;
     constexpr int WPC = sizeof(lds) > 80 * 1024 ? 1 : 2;           // workgroups per CU (LDS)
